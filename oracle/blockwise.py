@@ -1,0 +1,64 @@
+"""Blockwise ("fine-grained") FP8 quantisation, DeepSeek-V3 style (oracle).
+
+aifind.ru, "DeepSeek-V3: a revolutionary high-performance language model with
+low training cost", section "Low-precision training: FP8 Framework" and the
+caption of its figure (a): activations are scaled per 1x128 tile (one row,
+128 columns), weights per 128x128 block, each tile/block with its own scale.
+
+Readings (the page gives tile shapes only): the scale is an fp32 number
+s = fl32(amax / 448) computed by IEEE float32 division (s = 1 when amax = 0);
+elements are q = E4M3(fl32(v / s)) with the division again in float32, then
+rounded to nearest even and saturated at 448 (because s is rounded, the amax
+element can land just above 448).  A weight block's amax covers all
+128 x 128 entries.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .codecs import e4m3_decode, e4m3_encode
+
+TILE = 128
+
+
+def _scale_and_quantize(v32: np.ndarray, amax32: np.ndarray):
+    """v32, amax32 float32 (amax broadcastable); returns (q, s float32)."""
+    s = (amax32 / np.float32(448.0)).astype(np.float32)      # IEEE fp32 division
+    s = np.where(amax32 == 0, np.float32(1.0), s).astype(np.float32)
+    y = (v32 / s).astype(np.float32)                          # IEEE fp32 division
+    return e4m3_encode(y.astype(np.float64)), s
+
+
+def bw_quantize_act_1x128(x_bits):
+    """bf16 [R, C] -> (q uint8 [R, C], s float32 [R, C/128]), one scale per 1x128 tile."""
+    x_bits = np.asarray(x_bits, dtype=np.uint16)
+    R, C = x_bits.shape
+    if C % TILE:
+        raise ValueError("C must be a multiple of 128")
+    v = (x_bits.astype(np.uint32) << 16).view(np.float32).reshape(R, C // TILE, TILE)
+    amax = np.max(np.abs(v), axis=2, keepdims=True)
+    q, s = _scale_and_quantize(v, amax)
+    return q.reshape(R, C), s.reshape(R, C // TILE)
+
+
+def bw_quantize_weight_128x128(w_bits):
+    """bf16 [R, C] (R = G*N) -> (q uint8 [R, C], s float32 [R/128, C/128])."""
+    w_bits = np.asarray(w_bits, dtype=np.uint16)
+    R, C = w_bits.shape
+    if R % TILE or C % TILE:
+        raise ValueError("R and C must be multiples of 128")
+    v = (w_bits.astype(np.uint32) << 16).view(np.float32).reshape(R // TILE, TILE, C // TILE, TILE)
+    amax = np.max(np.abs(v), axis=(1, 3), keepdims=True)
+    q, s = _scale_and_quantize(v, amax)
+    return q.reshape(R, C), s.reshape(R // TILE, C // TILE)
+
+
+def bw_dequantize_act(q, s) -> np.ndarray:
+    q = np.asarray(q)
+    return e4m3_decode(q) * np.repeat(np.asarray(s, dtype=np.float64), TILE, axis=-1)
+
+
+def bw_dequantize_weight(q, s) -> np.ndarray:
+    q = np.asarray(q)
+    s = np.asarray(s, dtype=np.float64)
+    return e4m3_decode(q) * np.repeat(np.repeat(s, TILE, axis=0), TILE, axis=1)

@@ -1,0 +1,126 @@
+"""MX (microscaling) quantisation of bf16 tensors to E4M3 + E8M0 (oracle).
+
+opensourcebeat.com, "Enabling up to 41 % faster pre-training: MXFP8 and
+DeepEP ...", FAQ "What is MXFP8?": each block of 32 elements shares one
+exponent.  The block always runs along the contraction axis of the GEMM that
+consumes the copy (reading of the pages, which show only the forward pass):
+
+* row-wise   -- blocks of 32 consecutive elements of a row (X and W for the
+  forward GEMM, dY for dgrad);
+* column-wise -- blocks of 32 consecutive rows of one column, restarting at
+  every expert's first row (dY and X for wgrad, W for dgrad).  A group's last
+  block may hold fewer than 32 rows; its amax covers the real rows only.
+
+Steps for one block v_1..v_n (n <= 32), in order:
+
+1. amax = max |v_i| over the block.
+2. shared exponent e = floor(log2 amax) - 8, where 8 = floor(log2 448) is the
+   largest E4M3 exponent (the OCP MX v1.0 rule); e = -127 when amax = 0;
+   e is clamped to [-127, 127]; the scale byte is e + 127.
+3. q_i = E4M3(v_i * 2^-e), rounded to nearest even and saturated at 448.
+   The product is exact (power-of-two scaling of a bf16 value).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .codecs import bf16_bits_to_f64, e4m3_decode, e4m3_encode
+
+BLOCK = 32
+E4M3_EMAX = 8
+
+
+def mx_block_exponent(amax) -> np.ndarray:
+    """Shared exponent of blocks with the given amax (step 2 above)."""
+    amax = np.asarray(amax, dtype=np.float64)
+    _, ex = np.frexp(amax)               # amax = f * 2^ex, f in [0.5, 1): floor(log2 amax) = ex - 1
+    e = (ex - 1) - E4M3_EMAX
+    e = np.where(amax == 0.0, -127, e)
+    return np.clip(e, -127, 127).astype(np.int64)
+
+
+def _quantize_blocks(v: np.ndarray, axis: int):
+    """Quantise float64 values whose blocks run along `axis` (each block whole)."""
+    amax = np.max(np.abs(v), axis=axis, keepdims=True)
+    e = mx_block_exponent(amax)
+    q = e4m3_encode(np.ldexp(v, -e))
+    return q, (e + 127).astype(np.uint8)
+
+
+def mx_quantize_rowwise(x_bits):
+    """bf16 [R, C] -> (q uint8 [R, C], s uint8 [R, C/32]); blocks along each row."""
+    x_bits = np.asarray(x_bits, dtype=np.uint16)
+    R, C = x_bits.shape
+    if C % BLOCK:
+        raise ValueError("C must be a multiple of 32")
+    v = bf16_bits_to_f64(x_bits).reshape(R, C // BLOCK, BLOCK)
+    q, s = _quantize_blocks(v, axis=2)
+    return q.reshape(R, C), s.reshape(R, C // BLOCK)
+
+
+def mx_colwise_ld_min(M: int, G: int) -> int:
+    """Smallest admissible leading dimension of the column-wise layout.
+
+    Group g needs 32*ceil(m_g/32) <= m_g + 31 columns, so 32*ceil((M+31G)/32)
+    columns hold any split of M rows into G groups.
+    """
+    return 32 * (-(-(M + 31 * G) // 32))
+
+
+def mx_group_columns(offs):
+    """First column of each group in the column-wise layout: 32 * sum_{h<g} ceil(m_h/32)."""
+    offs = np.asarray(offs, dtype=np.int64)
+    nb = -(-np.diff(offs) // BLOCK)
+    start = np.zeros(len(nb) + 1, dtype=np.int64)
+    np.cumsum(nb, out=start[1:])
+    return BLOCK * start[:-1], nb
+
+
+def mx_quantize_colwise(x_bits, offs, ld: int):
+    """bf16 [R, C] quantised with blocks down the rows of each group.
+
+    ``offs=None`` means a single group of all R rows (then ld >= 32*ceil(R/32)).
+    W [G*N, K] for dgrad uses it: with N a multiple of 32 no block straddles
+    two experts, so one group gives the per-expert blocking.
+
+    Returns qT uint8 [C, ld] and sT uint8 [C, ld/32].  Group g occupies
+    columns [c_g, c_g + m_g) with c_g = 32 * sum_{h<g} ceil(m_h/32); every
+    other byte (the <= 31 pad columns after each group and the tail) is 0x00,
+    and so is every scale byte that belongs to no block.
+    """
+    x_bits = np.asarray(x_bits, dtype=np.uint16)
+    R, C = x_bits.shape
+    if offs is None:                      # one group spanning all rows
+        offs = np.array([0, R], dtype=np.int64)
+        need = BLOCK * (-(-R // BLOCK))
+    else:
+        offs = np.asarray(offs, dtype=np.int64)
+        need = mx_colwise_ld_min(R, len(offs) - 1)
+    if offs[0] != 0 or offs[-1] != R or np.any(np.diff(offs) < 0):
+        raise ValueError("bad offsets")
+    if ld % BLOCK or ld < need:
+        raise ValueError("bad ld")
+    qT = np.zeros((C, ld), dtype=np.uint8)
+    sT = np.zeros((C, ld // BLOCK), dtype=np.uint8)
+    col0, nb = mx_group_columns(offs)
+    for g in range(len(offs) - 1):
+        r0, r1 = int(offs[g]), int(offs[g + 1])
+        for b in range(int(nb[g])):
+            a = r0 + BLOCK * b
+            z = min(a + BLOCK, r1)
+            v = bf16_bits_to_f64(x_bits[a:z, :])          # [n, C], block along rows
+            q, s = _quantize_blocks(v, axis=0)
+            c = int(col0[g]) + BLOCK * b
+            qT[:, c:c + (z - a)] = q.T
+            sT[:, c // BLOCK] = s[0]
+    return qT, sT
+
+
+def mx_dequantize(q, s) -> np.ndarray:
+    """Exact value of an MX array whose 32-blocks run along the last axis."""
+    q = np.asarray(q)
+    s = np.asarray(s).astype(np.int64)
+    if q.shape[-1] != s.shape[-1] * BLOCK:
+        raise ValueError("shape mismatch")
+    scale = np.ldexp(1.0, s - 127)
+    return e4m3_decode(q) * np.repeat(scale, BLOCK, axis=-1)

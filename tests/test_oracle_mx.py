@@ -1,0 +1,209 @@
+"""Pins for the oracle's MX quantisers: hand-derived worked examples, an
+exhaustive bf16 sweep through an independent bit-level derivation of the scale,
+and the invariants the MX block rule implies."""
+import json
+import os
+
+import numpy as np
+
+from oracle import (bf16_bits_to_f64, e4m3_decode, e4m3_encode_bruteforce, mx_colwise_ld_min,
+                    mx_dequantize, mx_quantize_colwise, mx_quantize_rowwise, mx_group_columns)
+from workloads import f32_to_bf16_bits
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden", "mx_worked_examples.json")
+
+
+def _block(bits_hex):
+    b = np.zeros((1, 32), dtype=np.uint16)
+    for i, h in enumerate(bits_hex):
+        b[0, i] = int(h, 16)
+    return b
+
+
+def test_rowwise_worked_examples():
+    g = json.load(open(GOLD))
+    for ex in g["rowwise_blocks"]:
+        q, s = mx_quantize_rowwise(_block(ex["bf16"]))
+        want = np.zeros(32, dtype=np.uint8)
+        for i, c in enumerate(ex["codes"]):
+            want[i] = int(c, 16)
+        assert s[0, 0] == int(ex["scale"], 16), ex["why"]
+        assert np.array_equal(q[0], want), ex["why"]
+
+
+def test_colwise_worked_example():
+    ex = json.load(open(GOLD))["colwise_example"]
+    offs = np.array(ex["offs"])
+    assert mx_colwise_ld_min(40, 3) == ex["ld"]
+    x = np.zeros((40, 32), dtype=np.float32)
+    x[0:3, 0] = [1, 2, 3]
+    x[3:35, 0] = 0.5
+    x[35:40, 0] = [4, -4, 4, -4, 1]
+    qT, sT = mx_quantize_colwise(f32_to_bf16_bits(x), offs, ex["ld"])
+    want = np.zeros(ex["ld"], dtype=np.uint8)
+    for k, c in ex["col0_q_nonzero"].items():
+        if "-" in k:
+            a, b = map(int, k.split("-"))
+            want[a:b + 1] = int(c, 16)
+        else:
+            want[int(k)] = int(c, 16)
+    assert np.array_equal(qT[0], want)
+    assert list(sT[0]) == ex["col0_scales"]
+    assert not qT[1:].any() and not sT[1:].any()
+
+
+def _scale_exponent_from_bits(bits):
+    """floor(log2 |v|) - 8 from the bf16 bit fields, clamped (independent of frexp)."""
+    mag = bits & 0x7FFF
+    E = mag >> 7
+    m = mag & 0x7F
+    if mag == 0:
+        return -127
+    if E == 0:
+        fl = (int(m).bit_length() - 1) - 133      # subnormal: m * 2^-133
+    else:
+        fl = int(E) - 127
+    return max(-127, min(127, fl - 8))
+
+
+def test_exhaustive_bf16_as_block_max():
+    """Every finite bf16 pattern p as the block maximum: scale byte and code of p."""
+    bits = np.array([b for b in range(65536) if ((b >> 7) & 0xFF) != 0xFF], dtype=np.uint16)
+    blocks = np.zeros((len(bits), 32), dtype=np.uint16)
+    blocks[:, 0] = bits
+    q, s = mx_quantize_rowwise(blocks)
+    exp = np.array([_scale_exponent_from_bits(int(b)) for b in bits])
+    assert np.array_equal(s[:, 0].astype(np.int64), exp + 127)
+    y = bf16_bits_to_f64(bits) * np.ldexp(1.0, -exp)
+    sample = np.random.default_rng(0).choice(len(bits), 6000, replace=False)
+    assert np.array_equal(q[sample, 0], e4m3_encode_bruteforce(y[sample]))
+    # the block max always lands in [256, 512) unless the exponent was clamped
+    v = np.abs(bf16_bits_to_f64(bits))
+    scaled = v * np.ldexp(1.0, -exp)
+    unclamped = (v > 0) & (exp > -127)
+    assert np.all((scaled[unclamped] >= 256) & (scaled[unclamped] < 512))
+
+
+def test_exhaustive_bf16_as_non_max_element():
+    """Every finite bf16 pattern below a fixed amax: code = brute-force E4M3 of v * 2^-e."""
+    bits = np.array([b for b in range(65536) if ((b >> 7) & 0xFF) != 0xFF], dtype=np.uint16)
+    v = bf16_bits_to_f64(bits)
+    for amax in (1.0, 3.0, 2.0 ** -100, 2.0 ** 60):
+        keep = np.abs(v) <= amax
+        b = bits[keep]
+        blocks = np.zeros((len(b), 32), dtype=np.uint16)
+        blocks[:, 0] = b
+        blocks[:, 1] = f32_to_bf16_bits(np.array([amax], dtype=np.float32))[0]
+        q, s = mx_quantize_rowwise(blocks)
+        e = int(np.floor(np.log2(amax))) - 8
+        assert np.all(s[:, 0] == e + 127)
+        y = v[keep] * 2.0 ** -e
+        sample = np.random.default_rng(1).choice(len(b), 3000, replace=False)
+        assert np.array_equal(q[sample, 0], e4m3_encode_bruteforce(y[sample]))
+
+
+def _rand_bf16(rng, shape, std=1.0):
+    return f32_to_bf16_bits((rng.standard_normal(shape) * std).astype(np.float32))
+
+
+def test_power_of_two_exactness():
+    rng = np.random.default_rng(2)
+    codes = rng.integers(0, 0x7F, size=(500, 32))
+    codes[:, 0] = rng.integers(0x78, 0x7F, size=500)        # one element in [256, 448]
+    sign = rng.integers(0, 2, size=(500, 32)) * 0x80
+    t = rng.integers(-100, 100, size=(500, 1))
+    v = e4m3_decode(codes | sign) * np.ldexp(1.0, t)
+    bits = f32_to_bf16_bits(v.astype(np.float32))
+    assert np.array_equal(bf16_bits_to_f64(bits), v)            # exact in bf16
+    q, s = mx_quantize_rowwise(bits)
+    assert np.array_equal(s[:, 0].astype(np.int64), t[:, 0] + 127)
+    assert np.array_equal(mx_dequantize(q, s), v)
+
+
+def test_shift_invariance():
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((400, 64)).astype(np.float32)
+    q0, s0 = mx_quantize_rowwise(f32_to_bf16_bits(x))
+    for j in (-40, -3, 1, 17, 60):
+        xs = (x.astype(np.float64) * 2.0 ** j).astype(np.float32)
+        q1, s1 = mx_quantize_rowwise(f32_to_bf16_bits(xs))
+        assert np.array_equal(q0, q1)
+        assert np.array_equal(s1.astype(np.int64), s0.astype(np.int64) + j)
+
+
+def test_idempotence():
+    rng = np.random.default_rng(4)
+    x = _rand_bf16(rng, (2000, 128))
+    x[rng.random(x.shape) < 0.01] = f32_to_bf16_bits(np.array([300.0], np.float32))[0]
+    q, s = mx_quantize_rowwise(x)
+    d = mx_dequantize(q, s)
+    bits = f32_to_bf16_bits(d.astype(np.float32))
+    assert np.array_equal(bf16_bits_to_f64(bits), d)
+    q2, s2 = mx_quantize_rowwise(bits)
+    assert np.array_equal(q, q2) and np.array_equal(s, s2)
+
+
+def test_zero_and_signed_zero_blocks():
+    x = np.zeros((2, 64), dtype=np.uint16)
+    x[1, :] = 0x8000
+    q, s = mx_quantize_rowwise(x)
+    assert not s.any()
+    assert not q[0].any() and np.all(q[1] == 0x80)
+
+
+def test_ld_min_for_the_workload_shapes():
+    assert [mx_colwise_ld_min(M, G) for M, G in ((1024, 4), (49152, 64), (65536, 8), (32768, 16))] == \
+        [1152, 51136, 65792, 33280]
+
+
+def test_colwise_equals_rowwise_of_transposed_groups():
+    """Column-wise quantisation of a group whose size is a multiple of 32 equals the
+    row-wise quantisation of that group's transpose, placed at its start column."""
+    rng = np.random.default_rng(5)
+    sizes = [64, 0, 32, 96, 0]
+    offs = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    M, C = int(offs[-1]), 96
+    x = _rand_bf16(rng, (M, C))
+    ld = mx_colwise_ld_min(M, len(sizes))
+    qT, sT = mx_quantize_colwise(x, offs, ld)
+    col0, nb = mx_group_columns(offs)
+    for g, m in enumerate(sizes):
+        if m == 0:
+            continue
+        r0 = int(offs[g])
+        qr, sr = mx_quantize_rowwise(np.ascontiguousarray(x[r0:r0 + m].T))
+        c = int(col0[g])
+        assert np.array_equal(qT[:, c:c + m], qr)
+        assert np.array_equal(sT[:, c // 32:c // 32 + m // 32], sr)
+    assert not qT[:, M:].any() and not sT[:, M // 32:].any()
+
+
+def test_colwise_ragged_groups_short_tail_and_pads():
+    rng = np.random.default_rng(6)
+    sizes = [17, 0, 33, 1, 70]
+    offs = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    M, C = int(offs[-1]), 64
+    x = _rand_bf16(rng, (M, C))
+    ld = mx_colwise_ld_min(M, len(sizes))
+    qT, sT = mx_quantize_colwise(x, offs, ld)
+    col0, nb = mx_group_columns(offs)
+    assert list(col0) == [0, 32, 32, 96, 128] and list(nb) == [1, 0, 2, 1, 3]
+    v = bf16_bits_to_f64(x)
+    used = np.zeros(ld, dtype=bool)
+    for g, m in enumerate(sizes):
+        r0, c0 = int(offs[g]), int(col0[g])
+        used[c0:c0 + m] = True
+        for b in range(int(nb[g])):
+            rows = slice(r0 + 32 * b, min(r0 + 32 * b + 32, r0 + m))
+            amax = np.abs(v[rows]).max(axis=0)                       # per column, real rows only
+            e = np.floor(np.log2(amax)).astype(np.int64) - 8
+            assert np.array_equal(sT[:, c0 // 32 + b].astype(np.int64), e + 127)
+    assert not qT[:, ~used].any()
+    # dequantised values are within half an E4M3 step of the input, or below it by
+    # the saturation error (< 1/8: a scaled block max lies in [256, 512) and saturates at 448)
+    d = mx_dequantize(qT, sT)
+    for g, m in enumerate(sizes):
+        r0, c0 = int(offs[g]), int(col0[g])
+        if m:
+            err = np.abs(d[:, c0:c0 + m] - v[r0:r0 + m].T)
+            assert np.all(err <= np.abs(v[r0:r0 + m].T) * 2 ** -3 + 2.0 ** -9 * np.abs(v).max())
