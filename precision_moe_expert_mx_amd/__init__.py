@@ -1,0 +1,251 @@
+"""Python binding of libmxmoe (MXFP8 quantisers and dropless grouped GEMMs for MI355X / gfx950).
+
+Argument marshalling only: every step runs in the HIP library.  Tensors are torch tensors on the
+current HIP device (bf16 inputs may be given as torch.bfloat16 or as uint16/int16 bit patterns);
+outputs are allocated with torch when not passed in.  Calls are asynchronous on torch's current
+stream unless `stream` (a torch.cuda.Stream or a raw hipStream_t integer) is given.
+
+The library must be built (``python -m precision_moe_expert_mx_amd.build``); importing this package
+without it raises, and there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+__all__ = [
+    "LIB_PATH", "MxMoeError", "lib", "abi_version", "FEED_FP8",
+    "mx_colwise_ld_min", "mx_quantize_rowwise", "mx_quantize_colwise",
+    "mx_grouped_gemm_fwd", "mx_grouped_gemm_dgrad", "mx_grouped_gemm_wgrad",
+    "fp8bw_quantize_act_1x128", "fp8bw_quantize_weight_128x128",
+    "fp8bw_grouped_gemm_fwd", "fp8bw_grouped_gemm_dgrad", "mxmoe_check_offsets",
+    "EXPORTED_SYMBOLS",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmxmoe.so")
+
+MXMOE_F32, MXMOE_BF16 = 0, 1
+FEED_FP8 = 0x100          # OR-ed into a GEMM's output dtype: full-rate FP8 MFMA feed
+_STATUS = {0: "OK", 1: "ERR_NULL", 2: "ERR_SHAPE", 3: "ERR_ALIGN", 4: "ERR_DTYPE", 5: "ERR_OFFSETS",
+           6: "ERR_HIP", 7: "ERR_UNSUPPORTED"}
+
+_p = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_i32 = ctypes.c_int32
+
+# name -> (restype, argtypes); mirrors include/mxmoe.h
+_SIGS = {
+    "mxmoe_abi_version": (ctypes.c_int, []),
+    "mxmoe_last_error": (ctypes.c_char_p, []),
+    "mx_colwise_ld_min": (_i64, [_i64, _i32]),
+    "mx_quantize_rowwise": (ctypes.c_int, [_p, _i64, _i64, _p, _p, _p]),
+    "mx_quantize_colwise": (ctypes.c_int, [_p, _i64, _i64, _p, _i32, _p, _p, _i64, _p]),
+    "mx_grouped_gemm_fwd": (ctypes.c_int, [_p, _p, _p, _p, _p, _i32, _i64, _i64, _i64, _p, ctypes.c_int, _p]),
+    "mx_grouped_gemm_dgrad": (ctypes.c_int, [_p, _p, _p, _p, _i64, _p, _i32, _i64, _i64, _i64, _p, ctypes.c_int, _p]),
+    "mx_grouped_gemm_wgrad": (ctypes.c_int, [_p, _p, _p, _p, _i64, _p, _i32, _i64, _i64, _i64, _p, ctypes.c_int, _p]),
+    "fp8bw_quantize_act_1x128": (ctypes.c_int, [_p, _i64, _i64, _p, _p, _p]),
+    "fp8bw_quantize_weight_128x128": (ctypes.c_int, [_p, _i64, _i64, _p, _p, _p]),
+    "fp8bw_grouped_gemm_fwd": (ctypes.c_int, [_p, _p, _p, _p, _p, _i32, _i64, _i64, _i64, _p, ctypes.c_int, _p]),
+    "fp8bw_grouped_gemm_dgrad": (ctypes.c_int, [_p, _p, _p, _p, _p, _i32, _i64, _i64, _i64, _p, ctypes.c_int, _p]),
+    "mxmoe_check_offsets": (ctypes.c_int, [_p, _i32, _i64, _p]),
+}
+EXPORTED_SYMBOLS = tuple(_SIGS)
+
+
+class MxMoeError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn}: {_STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libmxmoe (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with `python -m precision_moe_expert_mx_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise MxMoeError(fn, status, lib().mxmoe_last_error().decode(errors="replace"))
+
+
+def abi_version() -> int:
+    return lib().mxmoe_abi_version()
+
+
+def mx_colwise_ld_min(M: int, G: int) -> int:
+    return lib().mx_colwise_ld_min(int(M), int(G))
+
+
+# ---------------------------------------------------------------- torch plumbing
+def _torch():
+    import torch
+    return torch
+
+
+def _stream_handle(stream) -> Optional[int]:
+    torch = _torch()
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _bf16_bits(x):
+    torch = _torch()
+    if x.dtype == torch.bfloat16 or x.dtype in (torch.int16, torch.uint16):
+        return x
+    raise TypeError(f"expected bfloat16 (or its 16-bit pattern), got {x.dtype}")
+
+
+def _empty(shape, dtype, like):
+    return _torch().empty(shape, dtype=dtype, device=like.device)
+
+
+def _out_dtype(dt: str, fast: bool = False):
+    torch = _torch()
+    flag = FEED_FP8 if fast else 0
+    if dt == "f32":
+        return torch.float32, MXMOE_F32 | flag
+    if dt == "bf16":
+        return torch.bfloat16, MXMOE_BF16 | flag
+    raise ValueError(dt)
+
+
+# ---------------------------------------------------------------- MX quantisers
+def mx_quantize_rowwise(x, q=None, s=None, stream=None) -> Tuple[object, object]:
+    """x bf16 [R, C] -> (q uint8 [R, C], s uint8 [R, C/32])."""
+    torch = _torch()
+    x = _bf16_bits(x)
+    R, C = x.shape
+    q = _empty((R, C), torch.uint8, x) if q is None else q
+    s = _empty((R, C // 32), torch.uint8, x) if s is None else s
+    _check("mx_quantize_rowwise", lib().mx_quantize_rowwise(_ptr(x), R, C, _ptr(q), _ptr(s), _stream_handle(stream)))
+    return q, s
+
+
+def mx_quantize_colwise(x, offs=None, G: int = 1, ld: Optional[int] = None, qT=None, sT=None, stream=None):
+    """x bf16 [R, C] -> (qT uint8 [C, ld], sT uint8 [C, ld/32]); offs int32 [G+1] device or None."""
+    torch = _torch()
+    x = _bf16_bits(x)
+    R, C = x.shape
+    if offs is not None:
+        G = offs.numel() - 1
+    if ld is None:
+        ld = mx_colwise_ld_min(R, G) if offs is not None else 32 * ((R + 31) // 32)
+    qT = _empty((C, ld), torch.uint8, x) if qT is None else qT
+    sT = _empty((C, ld // 32), torch.uint8, x) if sT is None else sT
+    _check("mx_quantize_colwise", lib().mx_quantize_colwise(_ptr(x), R, C, _ptr(offs), G, _ptr(qT), _ptr(sT), ld,
+                                                            _stream_handle(stream)))
+    return qT, sT
+
+
+# ---------------------------------------------------------------- MX grouped GEMMs
+def mx_grouped_gemm_fwd(qx, sx, qw, sw, offs, N: int, out_dtype: str = "f32", y=None, stream=None, fast: bool = False):
+    """Y [M, N] = per-expert X_g W_g^T from row-wise MX operands (qw: [G*N, K])."""
+    M, K = qx.shape
+    G = offs.numel() - 1
+    tdt, cdt = _out_dtype(out_dtype, fast)
+    y = _empty((M, N), tdt, qx) if y is None else y
+    _check("mx_grouped_gemm_fwd", lib().mx_grouped_gemm_fwd(_ptr(qx), _ptr(sx), _ptr(qw), _ptr(sw), _ptr(offs), G, M,
+                                                            N, K, _ptr(y), cdt, _stream_handle(stream)))
+    return y
+
+
+def mx_grouped_gemm_dgrad(qdy, sdy, qwT, swT, offs, K: int, out_dtype: str = "f32", dx=None, stream=None, fast: bool = False):
+    """dX [M, K] = per-expert dY_g W_g from row-wise dY and column-wise W ([K, ldw])."""
+    M, N = qdy.shape
+    G = offs.numel() - 1
+    ldw = qwT.shape[1]
+    tdt, cdt = _out_dtype(out_dtype, fast)
+    dx = _empty((M, K), tdt, qdy) if dx is None else dx
+    _check("mx_grouped_gemm_dgrad", lib().mx_grouped_gemm_dgrad(_ptr(qdy), _ptr(sdy), _ptr(qwT), _ptr(swT), ldw,
+                                                                _ptr(offs), G, M, N, K, _ptr(dx), cdt,
+                                                                _stream_handle(stream)))
+    return dx
+
+
+def mx_grouped_gemm_wgrad(qdyT, sdyT, qxT, sxT, offs, M: int, out_dtype: str = "f32", dw=None, stream=None, fast: bool = False):
+    """dW [G, N, K] = per-expert dY_g^T X_g from column-wise dY ([N, ld]) and X ([K, ld])."""
+    N, ld = qdyT.shape
+    K = qxT.shape[0]
+    G = offs.numel() - 1
+    tdt, cdt = _out_dtype(out_dtype, fast)
+    dw = _empty((G, N, K), tdt, qdyT) if dw is None else dw
+    _check("mx_grouped_gemm_wgrad", lib().mx_grouped_gemm_wgrad(_ptr(qdyT), _ptr(sdyT), _ptr(qxT), _ptr(sxT), ld,
+                                                                _ptr(offs), G, M, N, K, _ptr(dw), cdt,
+                                                                _stream_handle(stream)))
+    return dw
+
+
+# ---------------------------------------------------------------- blockwise FP8
+def fp8bw_quantize_act_1x128(x, q=None, s=None, stream=None):
+    torch = _torch()
+    x = _bf16_bits(x)
+    R, C = x.shape
+    q = _empty((R, C), torch.uint8, x) if q is None else q
+    s = _empty((R, C // 128), torch.float32, x) if s is None else s
+    _check("fp8bw_quantize_act_1x128", lib().fp8bw_quantize_act_1x128(_ptr(x), R, C, _ptr(q), _ptr(s),
+                                                                      _stream_handle(stream)))
+    return q, s
+
+
+def fp8bw_quantize_weight_128x128(w, q=None, s=None, stream=None):
+    torch = _torch()
+    w = _bf16_bits(w)
+    R, C = w.shape
+    q = _empty((R, C), torch.uint8, w) if q is None else q
+    s = _empty((R // 128, C // 128), torch.float32, w) if s is None else s
+    _check("fp8bw_quantize_weight_128x128", lib().fp8bw_quantize_weight_128x128(_ptr(w), R, C, _ptr(q), _ptr(s),
+                                                                                _stream_handle(stream)))
+    return q, s
+
+
+def fp8bw_grouped_gemm_fwd(qx, sx, qw, sw, offs, N: int, out_dtype: str = "f32", y=None, stream=None, fast: bool = False):
+    M, K = qx.shape
+    G = offs.numel() - 1
+    tdt, cdt = _out_dtype(out_dtype, fast)
+    y = _empty((M, N), tdt, qx) if y is None else y
+    _check("fp8bw_grouped_gemm_fwd", lib().fp8bw_grouped_gemm_fwd(_ptr(qx), _ptr(sx), _ptr(qw), _ptr(sw), _ptr(offs),
+                                                                  G, M, N, K, _ptr(y), cdt, _stream_handle(stream)))
+    return y
+
+
+def fp8bw_grouped_gemm_dgrad(qdy, sdy, qw, sw, offs, K: int, out_dtype: str = "f32", dx=None, stream=None, fast: bool = False):
+    M, N = qdy.shape
+    G = offs.numel() - 1
+    tdt, cdt = _out_dtype(out_dtype, fast)
+    dx = _empty((M, K), tdt, qdy) if dx is None else dx
+    _check("fp8bw_grouped_gemm_dgrad", lib().fp8bw_grouped_gemm_dgrad(_ptr(qdy), _ptr(sdy), _ptr(qw), _ptr(sw),
+                                                                      _ptr(offs), G, M, N, K, _ptr(dx), cdt,
+                                                                      _stream_handle(stream)))
+    return dx
+
+
+def mxmoe_check_offsets(offs, M: int, stream=None) -> None:
+    G = offs.numel() - 1
+    _check("mxmoe_check_offsets", lib().mxmoe_check_offsets(_ptr(offs), G, M, _stream_handle(stream)))

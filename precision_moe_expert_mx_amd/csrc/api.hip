@@ -1,0 +1,267 @@
+// C ABI of the MXFP8 expert-GEMM library: host-side argument validation (before any HIP call),
+// device check, dispatch to the kernels.  See include/mxmoe.h for the contract of each entry point.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <mutex>
+#include <vector>
+
+#include "common.h"
+
+using namespace mxmoe;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+mxmoe_status fail(mxmoe_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+mxmoe_status ok() {
+  g_err[0] = '\0';
+  return MXMOE_OK;
+}
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+// gfx950 check, cached per device ordinal (0 = unknown, 1 = gfx950, 2 = other)
+std::mutex g_dev_mu;
+std::vector<int> g_dev_ok;
+
+mxmoe_status check_device() {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MXMOE_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+  {
+    std::lock_guard<std::mutex> lk(g_dev_mu);
+    if ((int)g_dev_ok.size() > dev && g_dev_ok[dev] != 0)
+      return g_dev_ok[dev] == 1 ? MXMOE_OK : fail(MXMOE_ERR_UNSUPPORTED, "device %d is not gfx950", dev);
+  }
+  hipDeviceProp_t prop;
+  e = hipGetDeviceProperties(&prop, dev);
+  if (e != hipSuccess) return fail(MXMOE_ERR_HIP, "hipGetDeviceProperties failed: %s", hipGetErrorString(e));
+  const bool is950 = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  {
+    std::lock_guard<std::mutex> lk(g_dev_mu);
+    if ((int)g_dev_ok.size() <= dev) g_dev_ok.resize(dev + 1, 0);
+    g_dev_ok[dev] = is950 ? 1 : 2;
+  }
+  return is950 ? MXMOE_OK : fail(MXMOE_ERR_UNSUPPORTED, "device %d (%s) is not gfx950", dev, prop.gcnArchName);
+}
+
+mxmoe_status launched(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(MXMOE_ERR_HIP, "%s: launch failed: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+constexpr int32_t kMaxG = 1024;
+
+mxmoe_status check_gemm_common(const char* fn, const int32_t* offs, int32_t G, int64_t M, int64_t N, int64_t K,
+                               const void* out, int dt) {
+  if (G < 1 || G > kMaxG) return fail(MXMOE_ERR_SHAPE, "%s: G = %d outside [1, %d]", fn, (int)G, (int)kMaxG);
+  if (M < 0 || N <= 0 || K <= 0) return fail(MXMOE_ERR_SHAPE, "%s: bad sizes M=%lld N=%lld K=%lld", fn,
+                                             (long long)M, (long long)N, (long long)K);
+  if (N % 128 || K % 128) return fail(MXMOE_ERR_SHAPE, "%s: N and K must be multiples of 128 (N=%lld K=%lld)", fn,
+                                      (long long)N, (long long)K);
+  if (M > INT32_MAX) return fail(MXMOE_ERR_SHAPE, "%s: M too large", fn);
+  const int base = dt & ~MXMOE_FEED_FP8;
+  if (base != MXMOE_F32 && base != MXMOE_BF16) return fail(MXMOE_ERR_DTYPE, "%s: unknown output dtype %d", fn, dt);
+  if (!offs) return fail(MXMOE_ERR_NULL, "%s: offs is NULL", fn);
+  if (!out) return fail(MXMOE_ERR_NULL, "%s: output is NULL", fn);
+  if (!aligned(offs, 4)) return fail(MXMOE_ERR_ALIGN, "%s: offs not 4-byte aligned", fn);
+  if (!aligned(out, 16)) return fail(MXMOE_ERR_ALIGN, "%s: output not 16-byte aligned", fn);
+  return MXMOE_OK;
+}
+
+mxmoe_status check_ptr(const char* fn, const char* name, const void* p, uintptr_t al) {
+  if (!p) return fail(MXMOE_ERR_NULL, "%s: %s is NULL", fn, name);
+  if (!aligned(p, al)) return fail(MXMOE_ERR_ALIGN, "%s: %s not %d-byte aligned", fn, name, (int)al);
+  return MXMOE_OK;
+}
+
+#define TRY(x)                          \
+  do {                                  \
+    mxmoe_status _s = (x);              \
+    if (_s != MXMOE_OK) return _s;      \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+int mxmoe_abi_version(void) { return MXMOE_ABI_VERSION; }
+
+const char* mxmoe_last_error(void) { return g_err; }
+
+int64_t mx_colwise_ld_min(int64_t M, int32_t G) {
+  if (M < 0 || G < 1) return -1;
+  return 32 * ((M + 31 * (int64_t)G + 31) / 32);
+}
+
+mxmoe_status mx_quantize_rowwise(const void* x, int64_t R, int64_t C, uint8_t* q, uint8_t* s, void* stream) {
+  const char* fn = "mx_quantize_rowwise";
+  if (R < 0 || C <= 0 || C % 32) return fail(MXMOE_ERR_SHAPE, "%s: need R >= 0, C > 0, C %% 32 == 0 (R=%lld C=%lld)",
+                                            fn, (long long)R, (long long)C);
+  if (R == 0) return ok();
+  TRY(check_ptr(fn, "x", x, 16));
+  TRY(check_ptr(fn, "q", q, 16));
+  TRY(check_ptr(fn, "s", s, 4));
+  TRY(check_device());
+  return launched(launch_mx_rowwise((const uint16_t*)x, R, C, q, s, (hipStream_t)stream), fn);
+}
+
+mxmoe_status mx_quantize_colwise(const void* x, int64_t R, int64_t C, const int32_t* offs, int32_t G, uint8_t* qT,
+                                 uint8_t* sT, int64_t ld, void* stream) {
+  const char* fn = "mx_quantize_colwise";
+  if (R < 0 || C <= 0 || C % 32) return fail(MXMOE_ERR_SHAPE, "%s: need R >= 0, C > 0, C %% 32 == 0 (R=%lld C=%lld)",
+                                            fn, (long long)R, (long long)C);
+  if (R > INT32_MAX) return fail(MXMOE_ERR_SHAPE, "%s: R too large", fn);
+  if (offs && (G < 1 || G > kMaxG)) return fail(MXMOE_ERR_SHAPE, "%s: G = %d outside [1, %d]", fn, (int)G, (int)kMaxG);
+  if (ld <= 0 || ld % 32) return fail(MXMOE_ERR_ALIGN, "%s: ld must be a positive multiple of 32 (ld=%lld)", fn,
+                                      (long long)ld);
+  const int64_t need = offs ? mx_colwise_ld_min(R, G) : 32 * ((R + 31) / 32);
+  if (ld < need) return fail(MXMOE_ERR_SHAPE, "%s: ld=%lld < required %lld", fn, (long long)ld, (long long)need);
+  if (R > 0) TRY(check_ptr(fn, "x", x, 16));
+  if (offs && !aligned(offs, 4)) return fail(MXMOE_ERR_ALIGN, "%s: offs not 4-byte aligned", fn);
+  TRY(check_ptr(fn, "qT", qT, 16));
+  TRY(check_ptr(fn, "sT", sT, 4));
+  TRY(check_device());
+  return launched(launch_mx_colwise((const uint16_t*)x, R, C, offs, G, qT, sT, ld, (hipStream_t)stream), fn);
+}
+
+static mxmoe_status mx_gemm_common(int mode, const char* fn, const uint8_t* a, const uint8_t* sa, const uint8_t* b,
+                                   const uint8_t* sb, int64_t ldb_cols, const int32_t* offs, int32_t G, int64_t M,
+                                   int64_t N, int64_t K, void* out, int dt, void* stream) {
+  TRY(check_gemm_common(fn, offs, G, M, N, K, out, dt));
+  TRY(check_ptr(fn, "A operand", a, 16));
+  TRY(check_ptr(fn, "A scales", sa, 4));
+  TRY(check_ptr(fn, "B operand", b, 16));
+  TRY(check_ptr(fn, "B scales", sb, 4));
+  GemmArgs p;
+  memset(&p, 0, sizeof p);
+  p.a = a; p.sa = sa; p.b = b; p.sb = sb; p.offs = offs; p.out = out;
+  p.M = M; p.N = N; p.K = K; p.G = G;
+  p.out_bf16 = (dt & ~MXMOE_FEED_FP8) == MXMOE_BF16;
+  p.feed = (dt & MXMOE_FEED_FP8) ? kFeedFast : kFeedPrecise;
+  if (mode == kFwd) {
+    p.lda = K; p.ldsa = K / 32; p.ldb = K; p.ldsb = K / 32;
+  } else if (mode == kDgrad) {
+    p.lda = N; p.ldsa = N / 32; p.ldb = ldb_cols; p.ldsb = ldb_cols / 32;
+  } else {
+    p.lda = ldb_cols; p.ldsa = ldb_cols / 32; p.ldb = ldb_cols; p.ldsb = ldb_cols / 32;
+  }
+  if (mode != kWgrad && M == 0) return ok();
+  TRY(check_device());
+  return launched(launch_mx_gemm(mode, p, (hipStream_t)stream), fn);
+}
+
+mxmoe_status mx_grouped_gemm_fwd(const uint8_t* qx, const uint8_t* sx, const uint8_t* qw, const uint8_t* sw,
+                                 const int32_t* offs, int32_t G, int64_t M, int64_t N, int64_t K, void* y,
+                                 mxmoe_dtype ydt, void* stream) {
+  return mx_gemm_common(kFwd, "mx_grouped_gemm_fwd", qx, sx, qw, sw, 0, offs, G, M, N, K, y, (int)ydt, stream);
+}
+
+mxmoe_status mx_grouped_gemm_dgrad(const uint8_t* qdy, const uint8_t* sdy, const uint8_t* qwT, const uint8_t* swT,
+                                   int64_t ldw, const int32_t* offs, int32_t G, int64_t M, int64_t N, int64_t K,
+                                   void* dx, mxmoe_dtype dxdt, void* stream) {
+  const char* fn = "mx_grouped_gemm_dgrad";
+  if (ldw % 32 || ldw < (int64_t)G * N)
+    return fail(MXMOE_ERR_SHAPE, "%s: ldw=%lld must be a multiple of 32 and >= G*N=%lld", fn, (long long)ldw,
+                (long long)G * N);
+  return mx_gemm_common(kDgrad, fn, qdy, sdy, qwT, swT, ldw, offs, G, M, N, K, dx, (int)dxdt, stream);
+}
+
+mxmoe_status mx_grouped_gemm_wgrad(const uint8_t* qdyT, const uint8_t* sdyT, const uint8_t* qxT, const uint8_t* sxT,
+                                   int64_t ld, const int32_t* offs, int32_t G, int64_t M, int64_t N, int64_t K,
+                                   void* dw, mxmoe_dtype dwdt, void* stream) {
+  const char* fn = "mx_grouped_gemm_wgrad";
+  if (G >= 1 && M >= 0 && (ld % 32 || ld < mx_colwise_ld_min(M, G)))
+    return fail(MXMOE_ERR_SHAPE, "%s: ld=%lld must be a multiple of 32 and >= mx_colwise_ld_min(M, G)=%lld", fn,
+                (long long)ld, (long long)mx_colwise_ld_min(M, G));
+  return mx_gemm_common(kWgrad, fn, qdyT, sdyT, qxT, sxT, ld, offs, G, M, N, K, dw, (int)dwdt, stream);
+}
+
+mxmoe_status fp8bw_quantize_act_1x128(const void* x, int64_t R, int64_t C, uint8_t* q, float* s, void* stream) {
+  const char* fn = "fp8bw_quantize_act_1x128";
+  if (R < 0 || C <= 0 || C % 128) return fail(MXMOE_ERR_SHAPE, "%s: need R >= 0, C > 0, C %% 128 == 0", fn);
+  if (R == 0) return ok();
+  TRY(check_ptr(fn, "x", x, 16));
+  TRY(check_ptr(fn, "q", q, 16));
+  TRY(check_ptr(fn, "s", s, 4));
+  TRY(check_device());
+  return launched(launch_bw_act((const uint16_t*)x, R, C, q, s, (hipStream_t)stream), fn);
+}
+
+mxmoe_status fp8bw_quantize_weight_128x128(const void* w, int64_t R, int64_t C, uint8_t* q, float* s, void* stream) {
+  const char* fn = "fp8bw_quantize_weight_128x128";
+  if (R < 0 || C <= 0 || R % 128 || C % 128)
+    return fail(MXMOE_ERR_SHAPE, "%s: need R %% 128 == 0, C > 0, C %% 128 == 0", fn);
+  if (R / 128 > 65535 || C / 128 > INT32_MAX) return fail(MXMOE_ERR_SHAPE, "%s: too many blocks", fn);
+  if (R == 0) return ok();
+  TRY(check_ptr(fn, "w", w, 16));
+  TRY(check_ptr(fn, "q", q, 16));
+  TRY(check_ptr(fn, "s", s, 4));
+  TRY(check_device());
+  return launched(launch_bw_weight((const uint16_t*)w, R, C, q, s, (hipStream_t)stream), fn);
+}
+
+static mxmoe_status bw_gemm_common(int mode, const char* fn, const uint8_t* a, const float* sa, const uint8_t* b,
+                                   const float* sb, const int32_t* offs, int32_t G, int64_t M, int64_t N, int64_t K,
+                                   void* out, int dt, void* stream) {
+  TRY(check_gemm_common(fn, offs, G, M, N, K, out, dt));
+  TRY(check_ptr(fn, "A operand", a, 16));
+  TRY(check_ptr(fn, "A scales", sa, 4));
+  TRY(check_ptr(fn, "B operand", b, 16));
+  TRY(check_ptr(fn, "B scales", sb, 4));
+  GemmArgs p;
+  memset(&p, 0, sizeof p);
+  p.a = a; p.sa = sa; p.b = b; p.sb = sb; p.offs = offs; p.out = out;
+  p.M = M; p.N = N; p.K = K; p.G = G;
+  p.out_bf16 = (dt & ~MXMOE_FEED_FP8) == MXMOE_BF16;
+  p.feed = (dt & MXMOE_FEED_FP8) ? kFeedFast : kFeedPrecise;
+  if (mode == kFwd) {
+    p.lda = K; p.ldsa = K / 128; p.ldb = K; p.ldsb = K / 128;
+  } else {
+    p.lda = N; p.ldsa = N / 128; p.ldb = K; p.ldsb = K / 128;
+  }
+  if (M == 0) return ok();
+  TRY(check_device());
+  return launched(launch_bw_gemm(mode, p, (hipStream_t)stream), fn);
+}
+
+mxmoe_status fp8bw_grouped_gemm_fwd(const uint8_t* qx, const float* sx, const uint8_t* qw, const float* sw,
+                                    const int32_t* offs, int32_t G, int64_t M, int64_t N, int64_t K, void* y,
+                                    mxmoe_dtype ydt, void* stream) {
+  return bw_gemm_common(kFwd, "fp8bw_grouped_gemm_fwd", qx, sx, qw, sw, offs, G, M, N, K, y, (int)ydt, stream);
+}
+
+mxmoe_status fp8bw_grouped_gemm_dgrad(const uint8_t* qdy, const float* sdy, const uint8_t* qw, const float* sw,
+                                      const int32_t* offs, int32_t G, int64_t M, int64_t N, int64_t K, void* dx,
+                                      mxmoe_dtype dxdt, void* stream) {
+  return bw_gemm_common(kDgrad, "fp8bw_grouped_gemm_dgrad", qdy, sdy, qw, sw, offs, G, M, N, K, dx, (int)dxdt,
+                        stream);
+}
+
+mxmoe_status mxmoe_check_offsets(const int32_t* offs, int32_t G, int64_t M, void* stream) {
+  const char* fn = "mxmoe_check_offsets";
+  if (G < 1) return fail(MXMOE_ERR_SHAPE, "%s: G < 1", fn);
+  if (M < 0) return fail(MXMOE_ERR_SHAPE, "%s: M < 0", fn);
+  TRY(check_ptr(fn, "offs", offs, 4));
+  std::vector<int32_t> h((size_t)G + 1);
+  hipError_t e = hipMemcpyAsync(h.data(), offs, h.size() * sizeof(int32_t), hipMemcpyDeviceToHost, (hipStream_t)stream);
+  if (e == hipSuccess) e = hipStreamSynchronize((hipStream_t)stream);
+  if (e != hipSuccess) return fail(MXMOE_ERR_HIP, "%s: copy failed: %s", fn, hipGetErrorString(e));
+  if (h[0] != 0) return fail(MXMOE_ERR_OFFSETS, "%s: offs[0] = %d, expected 0", fn, h[0]);
+  for (int32_t g = 0; g < G; ++g)
+    if (h[g + 1] < h[g]) return fail(MXMOE_ERR_OFFSETS, "%s: offs[%d] = %d < offs[%d] = %d", fn, g + 1, h[g + 1], g, h[g]);
+  if ((int64_t)h[G] != M) return fail(MXMOE_ERR_OFFSETS, "%s: offs[G] = %d, expected M = %lld", fn, h[G], (long long)M);
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,103 @@
+// Shared device helpers and internal launch declarations of the MXFP8 expert-GEMM library (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/mxmoe.h"
+
+namespace mxmoe {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v2i __attribute__((ext_vector_type(2)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef short v2s __attribute__((ext_vector_type(2)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
+// GEMM operand feeds: bf16-widened operands on the bf16 MFMA (fp32-accurate sums), or the
+// full-rate block-scaled FP8 MFMA (sums truncated per 8-element run, see gemm.hip).
+enum GemmFeed { kFeedPrecise = 0, kFeedFast = 1 };
+
+// ---- MX scale helpers (E8M0 shared exponent of a 32-block) -------------------------------------
+// The magnitude bits of a finite bf16 value order like the value itself, so amax is an integer max
+// over (bits & 0x7FFF).  floor(log2 v) of that magnitude: exponent field - 127 for normals, and for
+// subnormals (m * 2^-133) the index of m's leading bit - 133.
+__device__ __forceinline__ int bf16_floor_log2(uint32_t mag) {
+  uint32_t e = mag >> 7;
+  if (e != 0) return (int)e - 127;
+  // subnormal (mag != 0 assumed by caller): 31 - clz(m) is the leading-bit index of m
+  return (31 - __builtin_clz(mag)) - 133;
+}
+
+// Shared exponent e (already clamped) for a block with magnitude bits `amax_bits`.
+__device__ __forceinline__ int mx_exponent(uint32_t amax_bits) {
+  if (amax_bits == 0) return -127;
+  int e = bf16_floor_log2(amax_bits) - 8;
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
+// bf16 bit pattern of 448 * 2^e (the largest magnitude that does not saturate), e in [-127, 119].
+__device__ __forceinline__ uint32_t mx_clamp_bits(int e) { return ((uint32_t)(e + 135) << 7) | 0x60u; }
+
+// Convert two bf16 (one dword, low half first) to two E4M3 bytes placed in the low or high
+// half-word of `old`.  The magnitude is first clamped to 448 * 2^e so values that would round
+// above 448 saturate (the hardware conversion returns NaN on overflow); the conversion divides by
+// the power of two whose exponent field is `scale_bits` (only the exponent is used) and rounds to
+// nearest even, keeping the sign.
+template <bool HI>
+__device__ __forceinline__ uint32_t cvt2_e4m3(uint32_t old, uint32_t w, uint32_t clamp_pk, float scale) {
+  typedef unsigned short v2us __attribute__((ext_vector_type(2)));
+  v2us mag = __builtin_bit_cast(v2us, w & 0x7FFF7FFFu);
+  v2us lim = __builtin_bit_cast(v2us, clamp_pk);
+  uint32_t c = __builtin_bit_cast(uint32_t, __builtin_elementwise_min(mag, lim)) | (w & 0x80008000u);
+  v2s o = __builtin_bit_cast(v2s, old);
+  o = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(o, __builtin_bit_cast(v2bf, c), scale, HI);
+  return __builtin_bit_cast(uint32_t, o);
+}
+
+// Four bf16 (two dwords) -> four E4M3 bytes.
+__device__ __forceinline__ uint32_t cvt4_e4m3(uint32_t w0, uint32_t w1, uint32_t clamp_pk, float scale) {
+  uint32_t r = cvt2_e4m3<false>(0u, w0, clamp_pk, scale);
+  return cvt2_e4m3<true>(r, w1, clamp_pk, scale);
+}
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Device-side clamp of an offset read from memory into [0, M].
+__device__ __forceinline__ int64_t clamp_off(int64_t v, int64_t M) { return v < 0 ? 0 : (v > M ? M : v); }
+
+// ---- internal launchers (defined in the .hip files; arguments already validated) ---------------
+hipError_t launch_mx_rowwise(const uint16_t* x, int64_t R, int64_t C, uint8_t* q, uint8_t* s, hipStream_t st);
+hipError_t launch_mx_colwise(const uint16_t* x, int64_t R, int64_t C, const int32_t* offs, int32_t G,
+                             uint8_t* qT, uint8_t* sT, int64_t ld, hipStream_t st);
+hipError_t launch_bw_act(const uint16_t* x, int64_t R, int64_t C, uint8_t* q, float* s, hipStream_t st);
+hipError_t launch_bw_weight(const uint16_t* w, int64_t R, int64_t C, uint8_t* q, float* s, hipStream_t st);
+
+enum GemmMode { kFwd = 0, kDgrad = 1, kWgrad = 2 };
+
+struct GemmArgs {
+  const uint8_t* a;   // A operand rows (E4M3), contraction contiguous
+  const void* sa;     // A scales: uint8 E8M0 per 32 (MX) or float per 128 (blockwise)
+  const uint8_t* b;   // B operand rows
+  const void* sb;     // B scales
+  const int32_t* offs;
+  void* out;
+  int64_t lda, ldsa;  // A row stride in bytes / scale row stride in elements
+  int64_t ldb, ldsb;
+  int64_t M, N, K;    // problem sizes as in the ABI
+  int32_t G;
+  int32_t out_bf16;
+  int32_t feed;       // GemmFeed
+};
+
+hipError_t launch_mx_gemm(int mode, const GemmArgs& a, hipStream_t st);
+hipError_t launch_bw_gemm(int mode, const GemmArgs& a, hipStream_t st);
+
+}  // namespace mxmoe

@@ -1,0 +1,431 @@
+// Dropless grouped GEMM for MoE experts on gfx950 block-scaled FP8 MFMA.
+//
+// All experts run in one launch, each on its real number of rows (iitak.ru, "NVIDIA sped up
+// training of mixture-of-experts models on JAX tenfold": no capacity padding, no dropped tokens).
+// The work of every expert is cut into 128x128 output tiles; the launch enumerates the tiles of
+// all experts from the device-resident group offsets, so an expert with no rows contributes no
+// tile (forward / dgrad) and one with a handful of rows contributes one partial tile.
+//
+// Generic form computed by one workgroup (tile (mt, nt) of expert g):
+//   out[i, j] = sum_t A[row_a(i), col0_a + t] * B[row_b(j), col0_b + t],   t < L_g
+// with per-32 E8M0 scales (MX) or per-128 fp32 scales (blockwise), where
+//   forward: A = X rows of expert g, B = W_g rows, L = K            (Y = X W^T)
+//   dgrad:   A = dY rows of expert g, B = column-wise W (rows = k, columns gN..gN+N), L = N
+//   wgrad:   A = column-wise dY (rows = n), B = column-wise X (rows = k), both from column c_g,
+//            L = 32 ceil(m_g / 32) (pads are zero)
+//
+// Main loop: BK = 128 contraction bytes per step; global -> registers (prefetch of the next step)
+// -> LDS (16-byte chunks XOR-swizzled by row) -> MFMA operands.  Each of the four waves owns a
+// 64x64 quarter of the tile as 4x4 v_mfma_scale_f32_16x16x128_f8f6f4 (fp32 accumulators).
+//
+// MFMA operand layout (measured on gfx950): lane l feeds row/column (l % 16); its 32 operand bytes
+// are contraction elements [16 g, 16 g + 16) and [64 + 16 g, 64 + 16 g + 16) with g = l / 16, i.e.
+// 16-byte chunks g and 4 + g of the 128-byte row; its scale byte is the E8M0 of 32-block g.
+//
+// Two operand feeds (same tiling, same LDS staging of the FP8 bytes):
+//  * precise (default): each 32-block is widened to bf16 with its E8M0 scale folded in (exact) and
+//    multiplied on v_mfma_f32_16x16x32_bf16, whose sums are fp32-accurate;
+//  * fast (opt-in): v_mfma_scale_f32_16x16x128_f8f6f4 at twice the rate.  Measured on gfx950, it
+//    truncates the products of each run of 8 consecutive operand bytes to a 14-bit window below the
+//    run's largest product, so its error is bounded by about 7 * 2^-13 times the largest product of
+//    each run rather than by fp32 rounding.
+#include "common.h"
+
+namespace mxmoe {
+
+constexpr int BM = 128, BN = 128, BK = 128;
+constexpr int kThreads = 256;
+constexpr int kMaxGroups = 1024;
+
+struct TileInfo {
+  int g;          // expert
+  int mt, nt;     // tile coordinates inside the expert
+  int64_t row0;   // first global row of A for this expert (forward / dgrad)
+  int rows;       // valid rows of this tile (forward / dgrad)
+  int nblk;       // wgrad: number of 32-blocks in the contraction
+  int64_t col0;   // wgrad: first column of the expert in the column-wise layout
+  bool valid;
+};
+
+// Tiles are enumerated expert by expert; inside an expert the output-column tile runs fastest so
+// that consecutive workgroups share A rows.  Wave 0 computes the per-expert tile counts and their
+// prefix sums in LDS, then every thread binary-searches its tile.
+__device__ TileInfo decode_tile(int mode, const GemmArgs& p, int32_t* pre, int64_t* rowstart) {
+  const int G = p.G;
+  const int64_t M = p.M;
+  const int nt_count = (int)((mode == kFwd ? p.N : p.K) / BN);
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    int32_t carry = 0;
+    for (int g0 = 0; g0 <= G; g0 += 64) {
+      int g = g0 + lane;
+      int32_t cnt = 0;
+      int64_t o0 = 0;
+      if (g <= G) {
+        o0 = clamp_off(p.offs[g], M);
+        rowstart[g] = o0;
+      }
+      if (g < G) {
+        int64_t o1 = clamp_off(p.offs[g + 1], M);
+        int64_t m = o1 > o0 ? o1 - o0 : 0;
+        if (mode == kWgrad) cnt = (int32_t)((m + 31) / 32);   // contraction blocks (prefix -> c_g)
+        else cnt = (int32_t)((m + BM - 1) / BM) * nt_count;
+      }
+      int32_t incl = cnt;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        int32_t t = __shfl_up(incl, d, 64);
+        if (lane >= d) incl += t;
+      }
+      if (g <= G) pre[g] = carry + incl - cnt;
+      carry += __shfl(incl, 63, 64);
+    }
+  }
+  __syncthreads();
+  TileInfo ti;
+  ti.valid = false;
+  ti.nblk = 0;
+  ti.col0 = 0;
+  ti.rows = 0;
+  ti.row0 = 0;
+  const int64_t t = blockIdx.x;
+  if (mode == kWgrad) {
+    const int per_g = (int)(p.N / BM) * (int)(p.K / BN);
+    const int g = (int)(t / per_g);
+    if (g >= G) return ti;
+    const int lt = (int)(t % per_g);
+    const int ntc = (int)(p.K / BN);
+    ti.g = g;
+    ti.mt = lt / ntc;
+    ti.nt = lt % ntc;
+    ti.col0 = 32 * (int64_t)pre[g];
+    int64_t o0 = rowstart[g], o1 = rowstart[g + 1];
+    ti.nblk = o1 > o0 ? (int)((o1 - o0 + 31) / 32) : 0;
+    ti.row0 = o0;
+    ti.rows = (int)(o1 > o0 ? o1 - o0 : 0);   // contraction length m_g
+    ti.valid = true;
+    return ti;
+  }
+  if (t >= pre[G]) return ti;
+  int lo = 0, hi = G - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (pre[mid] <= t) lo = mid; else hi = mid - 1;
+  }
+  const int g = lo;
+  const int lt = (int)(t - pre[g]);
+  ti.g = g;
+  ti.mt = lt / nt_count;
+  ti.nt = lt % nt_count;
+  ti.row0 = rowstart[g] + (int64_t)ti.mt * BM;
+  int64_t left = rowstart[g + 1] - ti.row0;
+  ti.rows = (int)(left < BM ? left : BM);
+  ti.valid = ti.rows > 0;
+  return ti;
+}
+
+// LDS byte offset of 16-byte chunk c of tile row r (8 chunks per 128-byte row).
+__device__ __forceinline__ int lds_off(int r, int c) { return r * BK + ((c ^ (r & 7)) << 4); }
+
+// Eight E4M3 bytes -> eight bf16 multiplied by the power of two whose exponent field is that of
+// `scale` (the E8M0 byte shifted into a float's exponent); exact for every product of the GEMMs.
+__device__ __forceinline__ v8bf widen8(uint2 w, float scale) {
+  const v2bf a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, scale, false);
+  const v2bf b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, scale, true);
+  const v2bf c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, scale, false);
+  const v2bf d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, scale, true);
+  return v8bf{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+template <int MODE, bool BW, int FEED>
+__device__ __forceinline__ void gemm_tile(const GemmArgs& p, const TileInfo& ti, uint8_t* ldsA, uint8_t* ldsB,
+                                          uint32_t* ldsSA, uint32_t* ldsSB) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  // blockwise dgrad reads the forward weight operand [G*N, K] transposed (rows = n, columns = k)
+  constexpr bool BT = BW && MODE == kDgrad;
+
+  // ---- per-tile operand geometry ------------------------------------------------------------
+  // A rows: forward/dgrad -> token rows (clamped to the expert's last row); wgrad -> n rows
+  // B rows: forward -> gN + j; dgrad -> k rows of W^c (column offset gN); wgrad -> k rows (col c_g)
+  int64_t a_col0 = 0, b_col0 = 0;
+  int64_t L;   // contraction length in bytes (multiple of 128 for forward/dgrad)
+  if (MODE == kFwd) L = p.K;
+  else if (MODE == kDgrad) L = p.N;
+  else L = 32 * (int64_t)ti.nblk;
+  if (MODE == kDgrad) b_col0 = (int64_t)ti.g * p.N;
+  int nblk = ti.nblk;
+  if (MODE == kWgrad) {
+    a_col0 = ti.col0;
+    b_col0 = ti.col0;
+    // offsets that are not monotone could place an expert past the leading dimension: clip
+    const int64_t room = p.lda > a_col0 ? (p.lda - a_col0) / 32 : 0;
+    if (nblk > room) nblk = (int)room;
+    L = 32 * (int64_t)nblk;
+  }
+  const int nsteps = (int)((L + BK - 1) / BK);
+
+  // global load assignment: chunk id c = tid + 256 j (j = 0..3): row c / 8, chunk c % 8
+  const int ld_row = tid >> 3, ld_ch = tid & 7;
+  const uint8_t* a_ptr[4];
+  const uint8_t* b_ptr[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    int r = ld_row + 32 * j;
+    int64_t arow;
+    if (MODE == kWgrad) arow = (int64_t)ti.mt * BM + r;
+    else arow = ti.row0 + (r < ti.rows ? r : ti.rows - 1);
+    a_ptr[j] = p.a + arow * p.lda + a_col0 + ld_ch * 16;
+    if (BT) {
+      b_ptr[j] = p.b + ((int64_t)ti.g * p.N + r) * p.ldb + (int64_t)ti.nt * BN + ld_ch * 16;
+    } else {
+      int64_t brow;
+      if (MODE == kFwd) brow = (int64_t)ti.g * p.N + (int64_t)ti.nt * BN + r;
+      else brow = (int64_t)ti.nt * BN + r;
+      b_ptr[j] = p.b + brow * p.ldb + b_col0 + ld_ch * 16;
+    }
+  }
+  // scale rows: threads 0..127 -> A row tid, 128..255 -> B row tid-128
+  const bool s_is_a = tid < 128;
+  const int s_r = tid & 127;
+  int64_t s_row;
+  if (s_is_a) {
+    if (MODE == kWgrad) s_row = (int64_t)ti.mt * BM + s_r;
+    else s_row = ti.row0 + (s_r < ti.rows ? s_r : ti.rows - 1);
+  } else {
+    if (MODE == kFwd) s_row = (int64_t)ti.g * p.N + (int64_t)ti.nt * BN + s_r;
+    else s_row = (int64_t)ti.nt * BN + s_r;
+  }
+  const int64_t s_ld = s_is_a ? p.ldsa : p.ldsb;
+  const int64_t s_col0 = (s_is_a ? a_col0 : b_col0) / (BW ? 128 : 32);
+
+  uint4 ra[4], rb[4];
+  uint32_t rs = 0;
+
+  auto load_step = [&](int ks) {
+    const int64_t koff = (int64_t)ks * BK;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      bool ok = true;
+      if (MODE == kWgrad) ok = (koff + ld_ch * 16) < L;     // chunk inside the expert's blocks
+      ra[j] = ok ? *(const uint4*)(a_ptr[j] + koff) : make_uint4(0, 0, 0, 0);
+      rb[j] = ok ? *(const uint4*)(b_ptr[j] + (BT ? koff * p.ldb : koff)) : make_uint4(0, 0, 0, 0);
+    }
+    if (BW) {
+      const float* sp = (const float*)(s_is_a ? p.sa : p.sb);
+      if (s_is_a) rs = __float_as_uint(sp[s_row * s_ld + s_col0 + ks]);
+    } else {
+      const uint8_t* sp = (const uint8_t*)(s_is_a ? p.sa : p.sb) + s_row * s_ld + s_col0 + (int64_t)ks * 4;
+      uint32_t v = 0;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        bool ok = true;
+        if (MODE == kWgrad) ok = (int64_t)ks * 4 + b < nblk;
+        if (ok) v |= (uint32_t)sp[b] << (8 * b);
+      }
+      rs = v;
+    }
+  };
+  auto store_step = [&]() {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      int r = ld_row + 32 * j;
+      *(uint4*)(ldsA + lds_off(r, ld_ch)) = ra[j];
+      if (BT) {
+        // byte i of the chunk is element (n = r, k = 16 ld_ch + i): store it at row k, column n
+        const uint32_t w4[4] = {rb[j].x, rb[j].y, rb[j].z, rb[j].w};
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          ldsB[lds_off(16 * ld_ch + i, r >> 4) + (r & 15)] = (uint8_t)(w4[i >> 2] >> (8 * (i & 3)));
+      } else {
+        *(uint4*)(ldsB + lds_off(r, ld_ch)) = rb[j];
+      }
+    }
+    if (s_is_a) ldsSA[s_r] = rs;
+    else if (!BW) ldsSB[s_r] = rs;
+  };
+
+  v4f acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  const int fr = lane & 15, fg = lane >> 4;
+  if (nsteps > 0) load_step(0);
+  for (int ks = 0; ks < nsteps; ++ks) {
+    store_step();
+    __syncthreads();
+    if (ks + 1 < nsteps) load_step(ks + 1);
+
+    // blockwise: fp32 weight-block scale of this step (one per 128x128 block)
+    float sbw = 0.f;
+    float rsc[4][4];
+    if (BW) {
+      const float* sw = (const float*)p.sb;
+      if (MODE == kFwd) sbw = sw[(((int64_t)ti.g * p.N + (int64_t)ti.nt * BN) / 128) * p.ldsb + ks];
+      else sbw = sw[(((int64_t)ti.g * p.N) / 128 + ks) * p.ldsb + ti.nt];
+      // promotion factors of the lane's four output rows per A fragment
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          rsc[i][q] = __uint_as_float(ldsSA[wm * 64 + i * 16 + 4 * fg + q]) * sbw;
+    }
+
+    if (FEED == kFeedPrecise) {
+      // four bf16 MFMAs of K = 32 per step, one per 32-block: lane group fg supplies bytes
+      // [8 fg, 8 fg + 8) of the block, widened to bf16 with the block's E8M0 scale folded in
+      // (exact), so every product is exact and the MFMA sums them at fp32 precision
+      v4f part[4][4];
+      if (BW) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) part[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        v8bf af[4], bfr[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = wm * 64 + i * 16 + fr;
+          const uint2 w = *(const uint2*)(ldsA + lds_off(r, 2 * kb + (fg >> 1)) + 8 * (fg & 1));
+          const float sc = BW ? 1.0f : __uint_as_float(((ldsSA[r] >> (8 * kb)) & 0xFFu) << 23);
+          af[i] = widen8(w, sc);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int r = wn * 64 + j * 16 + fr;
+          const uint2 w = *(const uint2*)(ldsB + lds_off(r, 2 * kb + (fg >> 1)) + 8 * (fg & 1));
+          const float sc = BW ? 1.0f : __uint_as_float(((ldsSB[r] >> (8 * kb)) & 0xFFu) << 23);
+          bfr[j] = widen8(w, sc);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            if (BW) part[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], part[i][j], 0, 0, 0);
+            else acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+          }
+      }
+      if (BW) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) acc[i][j][q] = __builtin_fmaf(part[i][j][q], rsc[i][q], acc[i][j][q]);
+      }
+    } else {
+      // full-rate block-scaled FP8 MFMA, K = 128 per instruction
+      int sa[4], sb[4];
+      v8i af[4], bf[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = wm * 64 + i * 16 + fr;
+        v4i lo = *(const v4i*)(ldsA + lds_off(r, fg));
+        v4i hi = *(const v4i*)(ldsA + lds_off(r, 4 + fg));
+        af[i] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        sa[i] = BW ? 127 : (int)((ldsSA[r] >> (8 * fg)) & 0xFFu);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = wn * 64 + i * 16 + fr;
+        v4i lo = *(const v4i*)(ldsB + lds_off(r, fg));
+        v4i hi = *(const v4i*)(ldsB + lds_off(r, 4 + fg));
+        bf[i] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        sb[i] = BW ? 127 : (int)((ldsSB[r] >> (8 * fg)) & 0xFFu);
+      }
+      if (BW) {
+        // promotion: unscaled partial over this 128-slice, then fp32 FMA with the two scales
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const v4f part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[i], bf[j], v4f{0.f, 0.f, 0.f, 0.f},
+                                                                              0, 0, 0, 127, 0, 127);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) acc[i][j][q] = __builtin_fmaf(part[q], rsc[i][q], acc[i][j][q]);
+          }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[i], bf[j], acc[i][j], 0, 0, 0, sa[i], 0,
+                                                                         sb[j]);
+      }
+    }
+    __syncthreads();
+  }
+
+  // ---- epilogue: lane holds rows 4*(l/16)+q of each 16x16 sub-tile, column l%16 --------------
+  const int64_t nout = (MODE == kFwd) ? p.N : p.K;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r = wm * 64 + i * 16 + 4 * fg + q;
+        const int c = wn * 64 + j * 16 + fr;
+        int64_t idx;
+        if (MODE == kWgrad) {
+          idx = ((int64_t)ti.g * p.N + (int64_t)ti.mt * BM + r) * p.K + (int64_t)ti.nt * BN + c;
+        } else {
+          if (r >= ti.rows) continue;
+          idx = (ti.row0 + r) * nout + (int64_t)ti.nt * BN + c;
+        }
+        const float v = acc[i][j][q];
+        if (p.out_bf16) ((uint16_t*)p.out)[idx] = (uint16_t)f32_to_bf16_bits(v);
+        else ((float*)p.out)[idx] = v;
+      }
+}
+
+template <int MODE, bool BW, int FEED>
+__global__ __launch_bounds__(kThreads, 2) void grouped_gemm_kernel(GemmArgs p) {
+  __shared__ int32_t pre[kMaxGroups + 1];
+  __shared__ int64_t rowstart[kMaxGroups + 1];
+  __shared__ __attribute__((aligned(16))) uint8_t ldsA[BM * BK];
+  __shared__ __attribute__((aligned(16))) uint8_t ldsB[BN * BK];
+  __shared__ uint32_t ldsSA[BM];
+  __shared__ uint32_t ldsSB[BN];
+  const TileInfo ti = decode_tile(MODE, p, pre, rowstart);
+  if (!ti.valid) return;   // uniform across the workgroup
+  gemm_tile<MODE, BW, FEED>(p, ti, ldsA, ldsB, ldsSA, ldsSB);
+}
+
+static int64_t tile_upper_bound(int mode, const GemmArgs& p) {
+  if (mode == kWgrad) return (int64_t)p.G * (p.N / BM) * (p.K / BN);
+  const int64_t ntc = (mode == kFwd ? p.N : p.K) / BN;
+  return ((p.M + BM - 1) / BM + p.G) * ntc;   // sum_g ceil(m_g/BM) <= ceil(M/BM) + G
+}
+
+template <int MODE, bool BW>
+static void launch_feed(const GemmArgs& p, dim3 grid, dim3 block, hipStream_t st) {
+  if (p.feed == kFeedFast) hipLaunchKernelGGL((grouped_gemm_kernel<MODE, BW, kFeedFast>), grid, block, 0, st, p);
+  else hipLaunchKernelGGL((grouped_gemm_kernel<MODE, BW, kFeedPrecise>), grid, block, 0, st, p);
+}
+
+hipError_t launch_mx_gemm(int mode, const GemmArgs& p, hipStream_t st) {
+  const int64_t tiles = tile_upper_bound(mode, p);
+  if (tiles == 0) return hipSuccess;
+  dim3 grid((unsigned)tiles), block(kThreads);
+  if (mode == kFwd) launch_feed<kFwd, false>(p, grid, block, st);
+  else if (mode == kDgrad) launch_feed<kDgrad, false>(p, grid, block, st);
+  else launch_feed<kWgrad, false>(p, grid, block, st);
+  return hipGetLastError();
+}
+
+hipError_t launch_bw_gemm(int mode, const GemmArgs& p, hipStream_t st) {
+  const int64_t tiles = tile_upper_bound(mode, p);
+  if (tiles == 0) return hipSuccess;
+  dim3 grid((unsigned)tiles), block(kThreads);
+  if (mode == kFwd) launch_feed<kFwd, true>(p, grid, block, st);
+  else launch_feed<kDgrad, true>(p, grid, block, st);
+  return hipGetLastError();
+}
+
+}  // namespace mxmoe

@@ -1,0 +1,99 @@
+// Blockwise ("fine-grained") FP8 quantisers for gfx950: E4M3 elements with one fp32 scale per
+// 1x128 activation tile or per 128x128 weight block (aifind.ru DeepSeek-V3 article, section
+// "Low-precision training: FP8 Framework").  Scale s = fl32(amax / 448) by IEEE division (1 for an
+// all-zero tile); elements E4M3(fl32(v / s)), nearest even.  |v / s| <= 448 (1 + 2^-23)^2 < 464,
+// so the hardware conversion (which rounds to nearest even) never overflows and no clamp is needed.
+#include "common.h"
+
+namespace mxmoe {
+
+__device__ __forceinline__ uint32_t cvt4_f32_e4m3(float a, float b, float c, float d) {
+  int r = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  r = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, r, true);
+  return (uint32_t)r;
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Quantise 8 bf16 (one uint4) with scale s -> 8 bytes.
+__device__ __forceinline__ uint2 bw_convert8(const uint4& v, float s) {
+  uint2 o;
+  o.x = cvt4_f32_e4m3(__fdiv_rn(bf16_lo(v.x), s), __fdiv_rn(bf16_hi(v.x), s),
+                      __fdiv_rn(bf16_lo(v.y), s), __fdiv_rn(bf16_hi(v.y), s));
+  o.y = cvt4_f32_e4m3(__fdiv_rn(bf16_lo(v.z), s), __fdiv_rn(bf16_hi(v.z), s),
+                      __fdiv_rn(bf16_lo(v.w), s), __fdiv_rn(bf16_hi(v.w), s));
+  return o;
+}
+
+__device__ __forceinline__ uint32_t magmax8(const uint4& v) {
+  uint32_t a = max(max(v.x & 0x7FFFu, (v.x >> 16) & 0x7FFFu), max(v.y & 0x7FFFu, (v.y >> 16) & 0x7FFFu));
+  uint32_t b = max(max(v.z & 0x7FFFu, (v.z >> 16) & 0x7FFFu), max(v.w & 0x7FFFu, (v.w >> 16) & 0x7FFFu));
+  return max(a, b);
+}
+
+__device__ __forceinline__ float bw_scale_from_amax_bits(uint32_t m) {
+  float amax = __uint_as_float(m << 16);
+  return m == 0 ? 1.0f : __fdiv_rn(amax, 448.0f);
+}
+
+// 1x128 activation tiles: 16 lanes per tile (16 bytes each), reduced with xor shuffles inside the 16.
+__global__ __launch_bounds__(256) void bw_act_kernel(const uint4* __restrict__ x, int64_t nchunks,
+                                                     uint2* __restrict__ q, float* __restrict__ s) {
+  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  uint4 v = i < nchunks ? x[i] : make_uint4(0, 0, 0, 0);
+  uint32_t m = magmax8(v);
+#pragma unroll
+  for (int d = 1; d < 16; d <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, d, 64));
+  float sc = bw_scale_from_amax_bits(m);
+  if (i < nchunks) {
+    q[i] = bw_convert8(v, sc);
+    if ((threadIdx.x & 15) == 0) s[i >> 4] = sc;
+  }
+}
+
+// 128x128 weight blocks: one workgroup of 256 lanes per block; lane t owns rows (t/16) + 16 i,
+// 16-byte column chunk t%16, i = 0..7 (64 values in registers), amax reduced through LDS.
+__global__ __launch_bounds__(256) void bw_weight_kernel(const uint16_t* __restrict__ w, int64_t C,
+                                                        uint8_t* __restrict__ q, float* __restrict__ s) {
+  __shared__ uint32_t red[4];
+  const int64_t br = blockIdx.y, bcn = blockIdx.x;
+  const int t = threadIdx.x;
+  const int r = t >> 4, ch = t & 15;
+  uint4 v[8];
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    int64_t row = br * 128 + r + 16 * i;
+    v[i] = *(const uint4*)(w + row * C + bcn * 128 + ch * 8);
+    m = max(m, magmax8(v[i]));
+  }
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, d, 64));
+  if ((t & 63) == 0) red[t >> 6] = m;
+  __syncthreads();
+  m = max(max(red[0], red[1]), max(red[2], red[3]));
+  float sc = bw_scale_from_amax_bits(m);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    int64_t row = br * 128 + r + 16 * i;
+    *(uint2*)(q + row * C + bcn * 128 + ch * 8) = bw_convert8(v[i], sc);
+  }
+  if (t == 0) s[br * (C / 128) + bcn] = sc;
+}
+
+hipError_t launch_bw_act(const uint16_t* x, int64_t R, int64_t C, uint8_t* q, float* s, hipStream_t st) {
+  int64_t nchunks = R * C / 8;
+  if (nchunks == 0) return hipSuccess;
+  hipLaunchKernelGGL(bw_act_kernel, dim3((unsigned)((nchunks + 255) / 256)), dim3(256), 0, st,
+                     (const uint4*)x, nchunks, (uint2*)q, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_bw_weight(const uint16_t* w, int64_t R, int64_t C, uint8_t* q, float* s, hipStream_t st) {
+  if (R == 0 || C == 0) return hipSuccess;
+  hipLaunchKernelGGL(bw_weight_kernel, dim3((unsigned)(C / 128), (unsigned)(R / 128)), dim3(256), 0, st, w, C, q, s);
+  return hipGetLastError();
+}
+
+}  // namespace mxmoe

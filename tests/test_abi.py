@@ -1,0 +1,106 @@
+"""The C-ABI library loads, exports every entry point declared in include/mxmoe.h, and rejects bad
+arguments on the host (no GPU needed: validation happens before any HIP call)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mxmoe.h")
+
+
+def _lib():
+    import precision_moe_expert_mx_amd as m
+    if not os.path.exists(m.LIB_PATH):
+        pytest.skip("libmxmoe.so not built (run __graft_entry__.build())")
+    return m, m.lib()
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z][a-z0-9_]*)\s*\(", text)) - {"defined"})
+
+
+def test_header_declarations_match_binding():
+    import precision_moe_expert_mx_amd as m
+    assert _declared() == sorted(m.EXPORTED_SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol():
+    m, L = _lib()
+    for name in _declared():
+        assert hasattr(L, name), name
+    assert m.abi_version() == 1
+
+
+def test_host_helpers():
+    m, L = _lib()
+    assert [m.mx_colwise_ld_min(M, G) for M, G in ((1024, 4), (49152, 64), (65536, 8), (32768, 16))] == \
+        [1152, 51136, 65792, 33280]
+    assert m.mx_colwise_ld_min(-1, 4) == -1 and m.mx_colwise_ld_min(10, 0) == -1
+
+
+A16 = 0x10000      # fake, 16-byte aligned device addresses: never dereferenced on error paths
+A16b = 0x20000
+BAD = 0x10001
+
+
+def _status(L, fn, *args):
+    st = getattr(L, fn)(*args)
+    return st, L.mxmoe_last_error().decode()
+
+
+def test_quantiser_argument_errors():
+    _, L = _lib()
+    st, msg = _status(L, "mx_quantize_rowwise", A16, 4, 33, A16, A16, None)
+    assert st == 2 and "32" in msg
+    assert _status(L, "mx_quantize_rowwise", A16, -1, 32, A16, A16, None)[0] == 2
+    assert _status(L, "mx_quantize_rowwise", None, 4, 64, A16, A16, None)[0] == 1
+    assert _status(L, "mx_quantize_rowwise", BAD, 4, 64, A16, A16, None)[0] == 3
+    assert _status(L, "mx_quantize_rowwise", A16, 0, 64, None, None, None) == (0, "")   # empty: no-op
+    # column-wise: ld too small / not a multiple of 32 / G out of range
+    assert _status(L, "mx_quantize_colwise", A16, 100, 64, A16, 4, A16, A16, 96, None)[0] == 2
+    assert _status(L, "mx_quantize_colwise", A16, 100, 64, A16, 4, A16, A16, 250, None)[0] == 3
+    assert _status(L, "mx_quantize_colwise", A16, 100, 64, A16, 0, A16, A16, 256, None)[0] == 2
+    assert _status(L, "mx_quantize_colwise", A16, 100, 64, None, 0, A16, A16, 96, None)[0] == 2    # needs 128
+    assert _status(L, "mx_quantize_colwise", A16, 100, 64, None, 0, None, A16, 128, None)[0] == 1
+    # blockwise
+    assert _status(L, "fp8bw_quantize_act_1x128", A16, 4, 96, A16, A16, None)[0] == 2
+    assert _status(L, "fp8bw_quantize_weight_128x128", A16, 100, 128, A16, A16, None)[0] == 2
+
+
+def test_gemm_argument_errors():
+    _, L = _lib()
+    ok_args = (A16, A16, A16b, A16b, A16, 4, 1024, 512, 256, A16, 0, None)
+    # N not a multiple of 128
+    a = list(ok_args); a[7] = 500
+    assert _status(L, "mx_grouped_gemm_fwd", *a)[0] == 2
+    a = list(ok_args); a[5] = 0
+    assert _status(L, "mx_grouped_gemm_fwd", *a)[0] == 2           # G < 1
+    a = list(ok_args); a[10] = 7
+    assert _status(L, "mx_grouped_gemm_fwd", *a)[0] == 4           # dtype
+    a = list(ok_args); a[4] = None
+    assert _status(L, "mx_grouped_gemm_fwd", *a)[0] == 1           # offsets
+    a = list(ok_args); a[9] = BAD
+    assert _status(L, "mx_grouped_gemm_fwd", *a)[0] == 3           # output alignment
+    a = list(ok_args); a[6] = 0
+    assert _status(L, "mx_grouped_gemm_fwd", *a) == (0, "")       # M == 0: no-op
+    # dgrad: ldw < G*N
+    st, msg = _status(L, "mx_grouped_gemm_dgrad", A16, A16, A16b, A16b, 1024, A16, 4, 1024, 512, 256, A16, 0, None)
+    assert st == 2 and "ldw" in msg
+    # wgrad: ld < mx_colwise_ld_min
+    st, msg = _status(L, "mx_grouped_gemm_wgrad", A16, A16, A16b, A16b, 1024, A16, 4, 1024, 512, 256, A16, 0, None)
+    assert st == 2 and "ld" in msg
+    # blockwise
+    a = list(ok_args); a[8] = 200
+    assert _status(L, "fp8bw_grouped_gemm_fwd", *a)[0] == 2
+    assert _status(L, "mxmoe_check_offsets", A16, 0, 10, None)[0] == 2
+
+
+def test_binding_refuses_cpu_tensors():
+    m, _ = _lib()
+    import torch
+    with pytest.raises(ValueError):
+        m.mx_quantize_rowwise(torch.zeros((4, 32), dtype=torch.bfloat16))

@@ -1,0 +1,226 @@
+"""GPU parity of the grouped GEMMs against the float64 oracle:
+|gpu - ref| <= 1e-5 * sum_k |a_k b_k| per element (bf16 outputs: plus half a bf16 ulp)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import dev, host, random_bf16, require_gpu
+from workloads import make_workload, random_offsets, routing_offsets
+
+pytestmark = pytest.mark.gpu
+
+
+class Layer:
+    """Host inputs of one expert layer plus the MX operands the oracle quantises itself."""
+
+    def __init__(self, offs, x, w, dy, N, K):
+        self.offs, self.x, self.w, self.dy, self.N, self.K = np.asarray(offs, np.int32), x, w, dy, N, K
+        self.G = len(self.offs) - 1
+        self.M = int(self.offs[-1])
+
+
+def _rand_layer(rng, sizes, N, K, w_std=0.05, outliers=0.0):
+    offs = routing_offsets(sizes)
+    M, G = int(offs[-1]), len(sizes)
+    return Layer(offs, random_bf16(rng, (M, K), outlier_frac=outliers), random_bf16(rng, (G * N, K), w_std),
+                 random_bf16(rng, (M, N), outlier_frac=outliers), N, K)
+
+
+# Full-rate FP8 feed: the MFMA truncates each 8-product run to 14 bits below the run's largest product,
+# so |err| <= 7 * 2^-13 * sum_runs max|p| + fp32 rounding <= 2^-10 * sum |a b| (derived from the
+# measured arithmetic of the instruction; the precise feed meets the 1e-5 bound).
+FAST_REL = 2.0 ** -10
+
+
+def _check(got, ref, bound, dt, what, rel=oracle.gemm.REL_TOL):
+    ok, worst, idx = oracle.check_gemm(got, ref, bound, dt, rel=rel)
+    assert ok, f"{what}: worst |err|/tol = {worst:.3g} at flat index {idx} (got {got.reshape(-1)[idx]!r}, " \
+               f"ref {ref.reshape(-1)[idx]!r}, bound {bound.reshape(-1)[idx]!r})"
+    return worst
+
+
+def _gpu_out(t):
+    a = host(t)
+    if t.dtype == torch.bfloat16:
+        return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return a.astype(np.float64)
+
+
+def run_layer(m, L, dt="f32", rows=None, wgrad_groups=None, n_idx=None, k_idx=None, check=("fwd", "dgrad", "wgrad"),
+              fast=False):
+    """Quantise on the GPU (bit-exactness is covered elsewhere), run the GEMMs, compare with the oracle
+    evaluated on the GPU's own quantised operands (copied back)."""
+    offs_d = dev(L.offs)
+    x, w, dy = dev(L.x), dev(L.w), dev(L.dy)
+    rel = FAST_REL if fast else oracle.gemm.REL_TOL
+    worst = {}
+    if "fwd" in check:
+        qx, sx = m.mx_quantize_rowwise(x)
+        qw, sw = m.mx_quantize_rowwise(w)
+        y = m.mx_grouped_gemm_fwd(qx, sx, qw, sw, offs_d, L.N, dt, fast=fast)
+        hq = [host(t) for t in (qx, sx, qw, sw)]
+        ref, bnd = oracle.mx_gemm_fwd(*hq, L.offs, L.N, rows=rows)
+        got = _gpu_out(y)[rows] if rows is not None else _gpu_out(y)
+        worst["fwd"] = _check(got, ref, bnd, dt, "fwd", rel)
+    if "dgrad" in check:
+        qdy, sdy = m.mx_quantize_rowwise(dy)
+        qwT, swT = m.mx_quantize_colwise(w, None, ld=L.G * L.N)
+        dx = m.mx_grouped_gemm_dgrad(qdy, sdy, qwT, swT, offs_d, L.K, dt, fast=fast)
+        hq = [host(t) for t in (qdy, sdy, qwT, swT)]
+        ref, bnd = oracle.mx_gemm_dgrad(*hq, L.offs, L.N, L.K, rows=rows)
+        got = _gpu_out(dx)[rows] if rows is not None else _gpu_out(dx)
+        worst["dgrad"] = _check(got, ref, bnd, dt, "dgrad", rel)
+    if "wgrad" in check:
+        ld = oracle.mx_colwise_ld_min(L.M, L.G)
+        qdyT, sdyT = m.mx_quantize_colwise(dy, offs_d, ld=ld)
+        qxT, sxT = m.mx_quantize_colwise(x, offs_d, ld=ld)
+        dw = m.mx_grouped_gemm_wgrad(qdyT, sdyT, qxT, sxT, offs_d, L.M, dt, fast=fast)
+        hq = [host(t) for t in (qdyT, sdyT, qxT, sxT)]
+        ref, bnd = oracle.mx_gemm_wgrad(*hq, L.offs, L.N, L.K, groups=wgrad_groups, n_idx=n_idx, k_idx=k_idx)
+        got = _gpu_out(dw)
+        if wgrad_groups is not None:
+            got = got[np.asarray(wgrad_groups)]
+        if n_idx is not None:
+            got = got[:, np.asarray(n_idx)]
+        if k_idx is not None:
+            got = got[:, :, np.asarray(k_idx)]
+        worst["wgrad"] = _check(got, ref, bnd, dt, "wgrad", rel)
+    return worst
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_tiny_workload_all_three(dt):
+    m = require_gpu()
+    lay = make_workload("tiny").layers[0]
+    w = run_layer(m, Layer(lay.offs, lay.x, lay.w.reshape(-1, lay.K), lay.dy, lay.N, lay.K), dt)
+    print("worst err/tol", w)
+
+
+def test_ragged_groups_short_contractions():
+    """Short contractions; experts of 0, 1, 17, 33, 129 rows."""
+    m = require_gpu()
+    rng = np.random.default_rng(30)
+    L = _rand_layer(rng, [0, 1, 17, 0, 33, 129, 5], 256, 384, outliers=0.002)
+    print(run_layer(m, L))
+
+
+def test_ragged_groups_long_contractions():
+    """Long contractions (K = 2048 forward, N = 1024 dgrad)."""
+    m = require_gpu()
+    rng = np.random.default_rng(31)
+    L = _rand_layer(rng, [3, 0, 130, 257, 64], 1024, 2048)
+    print(run_layer(m, L, check=("fwd", "dgrad")))
+
+
+def test_wgrad_mixed_expert_sizes():
+    """Experts of very different sizes in one launch (wgrad contraction length varies per expert)."""
+    m = require_gpu()
+    rng = np.random.default_rng(32)
+    L = _rand_layer(rng, [1500, 0, 17, 1024, 1023, 2100], 256, 256)
+    print(run_layer(m, L, check=("wgrad",)))
+
+
+def test_single_group_and_empty_batch():
+    m = require_gpu()
+    rng = np.random.default_rng(33)
+    print(run_layer(m, _rand_layer(rng, [200], 128, 1024)))
+    # M = 0: forward / dgrad are no-ops, wgrad writes zeros
+    L = _rand_layer(rng, [0, 0], 128, 256)
+    dw = torch.full((2, 128, 256), 7.0, device="cuda")
+    ld = oracle.mx_colwise_ld_min(0, 2)
+    qT = torch.zeros((128, ld), dtype=torch.uint8, device="cuda")
+    sT = torch.zeros((128, ld // 32), dtype=torch.uint8, device="cuda")
+    qX = torch.zeros((256, ld), dtype=torch.uint8, device="cuda")
+    sX = torch.zeros((256, ld // 32), dtype=torch.uint8, device="cuda")
+    m.mx_grouped_gemm_wgrad(qT, sT, qX, sX, dev(L.offs), 0, "f32", dw=dw)
+    torch.cuda.synchronize()
+    assert not dw.any()
+
+
+def test_determinism_and_no_out_of_bounds_writes():
+    m = require_gpu()
+    rng = np.random.default_rng(34)
+    L = _rand_layer(rng, [7, 300, 0, 45], 256, 1024)
+    offs = dev(L.offs)
+    qx, sx = m.mx_quantize_rowwise(dev(L.x))
+    qw, sw = m.mx_quantize_rowwise(dev(L.w))
+    guard = 4096
+    buf = torch.full((L.M * L.N + 2 * guard,), -3.0, device="cuda")
+    y = buf[guard:guard + L.M * L.N].view(L.M, L.N)
+    m.mx_grouped_gemm_fwd(qx, sx, qw, sw, offs, L.N, y=y)
+    y1 = y.clone()
+    m.mx_grouped_gemm_fwd(qx, sx, qw, sw, offs, L.N, y=y)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y1)
+    assert torch.all(buf[:guard] == -3.0) and torch.all(buf[guard + L.M * L.N:] == -3.0)
+
+
+@pytest.mark.parametrize("fast", [False, True])
+def test_tiny_and_ragged_fast_feed(fast):
+    """The full-rate FP8 feed within its derived bound (and the precise feed within 1e-5)."""
+    m = require_gpu()
+    lay = make_workload("tiny").layers[0]
+    print(run_layer(m, Layer(lay.offs, lay.x, lay.w.reshape(-1, lay.K), lay.dy, lay.N, lay.K), fast=fast))
+    rng = np.random.default_rng(38)
+    print(run_layer(m, _rand_layer(rng, [0, 1, 17, 300, 1100], 256, 1024, outliers=0.002), fast=fast))
+
+
+@pytest.mark.parametrize("name", ["dsv3_16b", "dsv3_671b_shard", "llama4_scout"])
+def test_full_size_sampled(name):
+    """Full-size layers in the launch configuration the benchmark times; the oracle checks sampled
+    rows (forward, dgrad) and sampled (expert, n, k) entries (wgrad), every expert included."""
+    m = require_gpu()
+    wl = make_workload(name)
+    rng = np.random.default_rng(35)
+    for lay in wl.layers:
+        offs = lay.offs.astype(np.int64)
+        rows = []
+        for g in range(lay.G):
+            if offs[g + 1] > offs[g]:
+                rows += [offs[g], offs[g + 1] - 1] + list(rng.integers(offs[g], offs[g + 1], size=6))
+        rows = np.unique(np.array(rows, np.int64))
+        L = Layer(lay.offs, lay.x, lay.w.reshape(-1, lay.K), lay.dy, lay.N, lay.K)
+        n_idx = np.unique(np.concatenate([[0, lay.N - 1], rng.choice(lay.N, 24, replace=False)]))
+        k_idx = np.unique(np.concatenate([[0, lay.K - 1], rng.choice(lay.K, 24, replace=False)]))
+        w = run_layer(m, L, "bf16" if lay.name == "gate_up" else "f32", rows=rows, n_idx=n_idx, k_idx=k_idx)
+        print(name, lay.name, w)
+        torch.cuda.empty_cache()
+
+
+def test_blockwise_gemms():
+    m = require_gpu()
+    rng = np.random.default_rng(36)
+    for sizes, N, K in (([0, 5, 130, 1, 60], 256, 1024), ([40, 0, 200], 1024, 256)):
+        L = _rand_layer(rng, sizes, N, K, w_std=0.02, outliers=0.001)
+        offs = dev(L.offs)
+        qx, sx = m.fp8bw_quantize_act_1x128(dev(L.x))
+        qw, sw = m.fp8bw_quantize_weight_128x128(dev(L.w))
+        y = m.fp8bw_grouped_gemm_fwd(qx, sx, qw, sw, offs, N)
+        ref, bnd = oracle.bw_gemm_fwd(host(qx), host(sx), host(qw), host(sw), L.offs, N)
+        print("bw fwd", _check(_gpu_out(y), ref, bnd, "f32", "bw fwd"))
+        qd, sd = m.fp8bw_quantize_act_1x128(dev(L.dy))
+        dx = m.fp8bw_grouped_gemm_dgrad(qd, sd, qw, sw, offs, K)
+        ref, bnd = oracle.bw_gemm_dgrad(host(qd), host(sd), host(qw), host(sw), L.offs, N, K)
+        print("bw dgrad", _check(_gpu_out(dx), ref, bnd, "f32", "bw dgrad"))
+
+
+def test_blockwise_full_size_sampled():
+    """The blockwise recipe on the DeepSeek-V3-16B layer tensors (sampled rows)."""
+    m = require_gpu()
+    wl = make_workload("dsv3_16b_blockwise")
+    rng = np.random.default_rng(37)
+    for lay in wl.layers:
+        offs_d = dev(lay.offs)
+        rows = np.unique(rng.choice(lay.M, 64, replace=False))
+        qx, sx = m.fp8bw_quantize_act_1x128(dev(lay.x))
+        qw, sw = m.fp8bw_quantize_weight_128x128(dev(lay.w.reshape(-1, lay.K)))
+        y = m.fp8bw_grouped_gemm_fwd(qx, sx, qw, sw, offs_d, lay.N)
+        hqw, hsw = host(qw), host(sw)
+        ref, bnd = oracle.bw_gemm_fwd(host(qx), host(sx), hqw, hsw, lay.offs, lay.N, rows=rows)
+        print(lay.name, "bw fwd", _check(_gpu_out(y)[rows], ref, bnd, "f32", "bw fwd"))
+        qd, sd = m.fp8bw_quantize_act_1x128(dev(lay.dy))
+        dx = m.fp8bw_grouped_gemm_dgrad(qd, sd, qw, sw, offs_d, lay.K)
+        ref, bnd = oracle.bw_gemm_dgrad(host(qd), host(sd), hqw, hsw, lay.offs, lay.N, lay.K, rows=rows)
+        print(lay.name, "bw dgrad", _check(_gpu_out(dx)[rows], ref, bnd, "f32", "bw dgrad"))
+        torch.cuda.empty_cache()
