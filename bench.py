@@ -1,0 +1,332 @@
+"""Benchmark of the MXFP8 expert-layer hot path on one MI355X.
+
+One step is the whole path, forward and backward, of both expert linear layers
+(gate+up and down) of the DeepSeek-V3-671B one-GPU expert shard: 8 local
+experts, 65536 routed rows with Zipf(1.2)-skewed group sizes (one expert with
+17 rows), hidden 7168, gate+up N=4096, down N=7168.  Per layer:
+
+    MX quantise X row-wise, W row-wise        -> grouped GEMM forward  (Y bf16)
+    MX quantise dY row-wise, W column-wise    -> grouped GEMM dgrad    (dX bf16)
+    MX quantise dY, X column-wise per expert  -> grouped GEMM wgrad    (dW fp32)
+
+`value` = algorithmic GEMM flops of the step (2*M*N*K per GEMM, real rows only)
+divided by the wall time of the whole step, quantisers included, inputs
+resident in HBM.  Every kernel launch is also timed with HIP events on the
+stream it runs on; the JSON line carries per-op figures, the roofline of the
+dominant kernel and the CPU oracle timed on a bounded sample.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "mxfp8": 5000.0}
+QUANT_BYTES_PER_ELEM = 2.0 + 1.0 + 1.0 / 32.0   # bf16 in, E4M3 out, one E8M0 per 32
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_traffic_dsv3_671b_shard.txt")
+GEMM_SOURCES = [os.path.join(ROOT, "precision_moe_expert_mx_amd", "csrc", f) for f in ("gemm.hip", "common.h")]
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def gemm_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in GEMM_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+# ------------------------------------------------------------------------------------------- ops
+class Op:
+    """One kernel launch of the step: `kind` is 'quant' (work = bytes) or 'gemm' (work = flops)."""
+
+    def __init__(self, name, kind, fn, work, kernel):
+        self.name, self.kind, self.fn, self.work, self.kernel = name, kind, fn, work, kernel
+        self.ms = []
+
+
+def build_layer_ops(m, torch, lay, dev_in, fast=False):
+    """Allocate the layer's device buffers and return its ops in step order."""
+    G, M, N, K = lay.G, lay.M, lay.N, lay.K
+    x, w, dy, offs = dev_in
+    d = x.device
+    u8 = torch.uint8
+    ld = m.mx_colwise_ld_min(M, G)
+    b = dict(
+        qx=torch.empty((M, K), dtype=u8, device=d), sx=torch.empty((M, K // 32), dtype=u8, device=d),
+        qw=torch.empty((G * N, K), dtype=u8, device=d), sw=torch.empty((G * N, K // 32), dtype=u8, device=d),
+        y=torch.empty((M, N), dtype=torch.bfloat16, device=d),
+        qdy=torch.empty((M, N), dtype=u8, device=d), sdy=torch.empty((M, N // 32), dtype=u8, device=d),
+        qwT=torch.empty((K, G * N), dtype=u8, device=d), swT=torch.empty((K, G * N // 32), dtype=u8, device=d),
+        dx=torch.empty((M, K), dtype=torch.bfloat16, device=d),
+        qdyT=torch.empty((N, ld), dtype=u8, device=d), sdyT=torch.empty((N, ld // 32), dtype=u8, device=d),
+        qxT=torch.empty((K, ld), dtype=u8, device=d), sxT=torch.empty((K, ld // 32), dtype=u8, device=d),
+        dw=torch.empty((G, N, K), dtype=torch.float32, device=d),
+    )
+    w2 = w.view(G * N, K)
+    f = 2.0 * M * N * K
+    n = lay.name
+    ops = [
+        Op(f"{n}.quant_x_row", "quant", lambda: m.mx_quantize_rowwise(x, b["qx"], b["sx"]),
+           M * K * QUANT_BYTES_PER_ELEM, "mx_rowwise_kernel"),
+        Op(f"{n}.quant_w_row", "quant", lambda: m.mx_quantize_rowwise(w2, b["qw"], b["sw"]),
+           G * N * K * QUANT_BYTES_PER_ELEM, "mx_rowwise_kernel"),
+        Op(f"{n}.fwd", "gemm", lambda: m.mx_grouped_gemm_fwd(b["qx"], b["sx"], b["qw"], b["sw"], offs, N, "bf16",
+                                                             y=b["y"], fast=fast), f, "grouped_gemm fwd"),
+        Op(f"{n}.quant_dy_row", "quant", lambda: m.mx_quantize_rowwise(dy, b["qdy"], b["sdy"]),
+           M * N * QUANT_BYTES_PER_ELEM, "mx_rowwise_kernel"),
+        Op(f"{n}.quant_w_col", "quant", lambda: m.mx_quantize_colwise(w2, None, ld=G * N, qT=b["qwT"], sT=b["swT"]),
+           G * N * K * QUANT_BYTES_PER_ELEM, "mx_colwise_kernel"),
+        Op(f"{n}.dgrad", "gemm", lambda: m.mx_grouped_gemm_dgrad(b["qdy"], b["sdy"], b["qwT"], b["swT"], offs, K,
+                                                                 "bf16", dx=b["dx"], fast=fast), f,
+           "grouped_gemm dgrad"),
+        Op(f"{n}.quant_dy_col", "quant", lambda: m.mx_quantize_colwise(dy, offs, ld=ld, qT=b["qdyT"], sT=b["sdyT"]),
+           M * N * QUANT_BYTES_PER_ELEM, "mx_colwise_kernel"),
+        Op(f"{n}.quant_x_col", "quant", lambda: m.mx_quantize_colwise(x, offs, ld=ld, qT=b["qxT"], sT=b["sxT"]),
+           M * K * QUANT_BYTES_PER_ELEM, "mx_colwise_kernel"),
+        Op(f"{n}.wgrad", "gemm", lambda: m.mx_grouped_gemm_wgrad(b["qdyT"], b["sdyT"], b["qxT"], b["sxT"], offs, M,
+                                                                 "f32", dw=b["dw"], fast=fast), f,
+           "grouped_gemm wgrad"),
+    ]
+    return ops, b
+
+
+def to_device(torch, a: np.ndarray):
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(a).cuda()
+
+
+def time_ops(torch, ops, steps, warmup, per_op=True):
+    """Run `warmup` untimed steps, then `steps` timed ones; returns ms per step (whole-step events)."""
+    for _ in range(warmup):
+        for op in ops:
+            op.fn()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    evs = []
+    t0.record()
+    for _ in range(steps):
+        for op in ops:
+            if per_op:
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                op.fn()
+                b.record()
+                evs.append((op, a, b))
+            else:
+                op.fn()
+    t1.record()
+    torch.cuda.synchronize()
+    for op, a, b in evs:
+        op.ms.append(a.elapsed_time(b))
+    return t0.elapsed_time(t1) / steps
+
+
+def op_summary(op):
+    ms = float(np.mean(op.ms))
+    d = {"ms": round(ms, 4), "ms_min": round(float(np.min(op.ms)), 4)}
+    if op.kind == "gemm":
+        d["tflops"] = round(op.work / (ms * 1e-3) / 1e12, 1)
+    else:
+        d["gbps"] = round(op.work / (ms * 1e-3) / 1e9, 1)
+        d["frac_hbm"] = round(d["gbps"] / HBM_PEAK_GBS, 3)
+    return d
+
+
+# ------------------------------------------------------------------------------------------- traffic
+def read_traffic():
+    """Per-launch HBM bytes of the GEMM ops from the committed counter summary (None if stale)."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    rec = None
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            line = line.strip()
+            if line.startswith("{"):
+                rec = json.loads(line)
+    if not rec or rec.get("source_sha256") != gemm_source_hash():
+        return None
+    return rec.get("ops", {})
+
+
+# ------------------------------------------------------------------------------------------- CPU oracle
+def cpu_baseline(lay, rows_per_expert=2048):
+    """The oracle, as it stands, on a bounded sample: the largest expert's weights and its first
+    `rows_per_expert` routed rows, quantised and contracted (forward GEMM) on the host."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        cores = 1
+    g = int(np.argmax(lay.sizes))
+    r0 = int(lay.offs[g])
+    rows = int(min(rows_per_expert, lay.sizes[g]))
+    t = time.perf_counter()
+    qw, sw = oracle.mx_quantize_rowwise(lay.w.reshape(lay.G, lay.N, lay.K)[g])
+    qx, sx = oracle.mx_quantize_rowwise(lay.x[r0:r0 + rows])
+    oracle.mx_gemm_fwd(qx, sx, qw, sw, np.array([0, rows]), lay.N)
+    dt = time.perf_counter() - t
+    flops = 2.0 * rows * lay.N * lay.K
+    cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"value": round(flops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{lay.name} layer, expert {g}: its weights [{lay.N}x{lay.K}] and {rows} routed rows "
+                      f"MX-quantised by the oracle, then the fp64 grouped forward GEMM "
+                      f"({flops / 1e9:.1f} GFLOP) with its error-bound pass; {dt:.1f} s",
+            "seconds": round(dt, 2), "cpu": cpu}
+
+
+# ------------------------------------------------------------------------------------------- main
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle timing")
+    ap.add_argument("--no-extra-legs", action="store_true",
+                    help="skip the FP8-feed and blockwise legs (reported beside the headline)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
+              "the expert-parallel split across GPUs is a design, not an implementation", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    import precision_moe_expert_mx_amd as m
+    m.lib()                                    # raises if the HIP library is not built
+
+    from workloads import make_workload
+    wname = "dsv3_671b_shard"
+    t = time.perf_counter()
+    wl = make_workload(wname)
+    log(f"workload {wname} generated in {time.perf_counter() - t:.1f} s")
+
+    # plain copy of known size: the calibration point for HBM byte counters
+    cal = torch.empty(256 << 20, dtype=torch.float32, device="cuda")
+    cal2 = torch.empty_like(cal)
+    cal2.copy_(cal)
+    torch.cuda.synchronize()
+    del cal, cal2
+
+    ops = []
+    keep = []
+    for lay in wl.layers:
+        dev_in = (to_device(torch, lay.x), to_device(torch, lay.w), to_device(torch, lay.dy),
+                  to_device(torch, lay.offs))
+        lops, bufs = build_layer_ops(m, torch, lay, dev_in)
+        ops += lops
+        keep.append((dev_in, bufs))
+    torch.cuda.synchronize()
+    log(f"inputs resident; {torch.cuda.memory_allocated() / 2**30:.1f} GiB allocated")
+
+    ms_step = time_ops(torch, ops, args.steps, args.warmup)
+    log(f"timed {args.steps} steps: {ms_step:.3f} ms/step")
+
+    gemm_flops = sum(op.work for op in ops if op.kind == "gemm")
+    value = gemm_flops / (ms_step * 1e-3) / 1e12
+    per_op = {op.name: op_summary(op) for op in ops}
+    gemm_ms = sum(float(np.mean(op.ms)) for op in ops if op.kind == "gemm")
+    quant_ms = sum(float(np.mean(op.ms)) for op in ops if op.kind == "quant")
+    quant_bytes = sum(op.work for op in ops if op.kind == "quant")
+
+    # dominant kernel: the GEMM op with the largest share of the step
+    dom = max((op for op in ops if op.kind == "gemm"), key=lambda o: float(np.mean(o.ms)))
+    dom_ms = float(np.mean(dom.ms))
+    achieved = dom.work / (dom_ms * 1e-3) / 1e12
+    traffic = read_traffic()
+    roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_PEAK_TFLOPS["bf16"],
+                "unit": "TFLOP/s", "frac": round(achieved / MFMA_PEAK_TFLOPS["bf16"], 4),
+                "traffic": (traffic or {}).get(dom.name), "op": dom.name, "kernel": dom.kernel,
+                "flop_per_launch": dom.work, "avg_launch_ms": round(dom_ms, 4),
+                "frac_of_mxfp8_peak": round(achieved / MFMA_PEAK_TFLOPS["mxfp8"], 4)}
+
+    extra = {}
+    if not args.no_extra_legs:
+        # the same GEMMs on the full-rate block-scaled FP8 MFMA (reduced-precision sums; see DESIGN)
+        fops = []
+        for lay, (dev_in, _) in zip(wl.layers, keep):
+            lops, bufs = build_layer_ops(m, torch, lay, dev_in, fast=True)
+            fops.append((lops, bufs))
+        flat = [op for lops, _ in fops for op in lops]
+        for op in flat:                       # quantised operands for the GEMMs
+            if op.kind == "quant":
+                op.fn()
+        g_ops = [op for op in flat if op.kind == "gemm"]
+        time_ops(torch, g_ops, 5, 1)
+        extra["fp8_feed_gemms"] = {op.name: op_summary(op) for op in g_ops}
+        fms = sum(float(np.mean(op.ms)) for op in g_ops)
+        extra["fp8_feed_gemm_tflops"] = round(gemm_flops / (fms * 1e-3) / 1e12, 1)
+        del fops, flat, g_ops
+        torch.cuda.empty_cache()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample ...")
+        cpu = cpu_baseline(wl.layers[0])
+        log(f"oracle: {cpu['value']} TFLOP/s in {cpu['seconds']} s")
+
+    out = {
+        "metric": "MXFP8 grouped-GEMM TFLOP/s fwd+bwd (% of MFMA peak); quantize GB/s",
+        "value": round(value, 1),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "e4m3+e8m0 (bf16 MFMA, fp32 acc)",
+        "data": "synthetic",
+        "config": {"workload": wname, "experts": wl.layers[0].G, "routed_rows": wl.layers[0].M,
+                   "group_sizes": [int(s) for s in wl.layers[0].sizes],
+                   "layers": {l.name: {"N": l.N, "K": l.K} for l in wl.layers},
+                   "step": "per layer: 6 MX quantisers + grouped GEMM fwd/dgrad/wgrad"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "gemm_only_tflops": round(gemm_flops / (gemm_ms * 1e-3) / 1e12, 1),
+        "gemm_frac_of_mxfp8_peak": round(gemm_flops / (gemm_ms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS["mxfp8"], 4),
+        "quant_gbps": round(quant_bytes / (quant_ms * 1e-3) / 1e9, 1),
+        "quant_frac_hbm": round(quant_bytes / (quant_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 3),
+        "step_gflop": round(gemm_flops / 1e9, 1),
+        "ops": per_op,
+        "gemm_source_sha256": gemm_source_hash(),
+        "host": platform.node(),
+    }
+    out.update(extra)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

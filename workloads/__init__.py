@@ -23,10 +23,15 @@ Shapes and distributions stand in for the workloads the pages describe
               gate+up (N=16384, K=5120) and down (N=5120, K=8192); N(0,1).
 
 Floats are drawn as float32 and rounded to bfloat16 with round-to-nearest-even
-on the bit pattern; tensors are returned as uint16 bit arrays.
+on the bit pattern; tensors are returned as uint16 bit arrays.  Large tensors
+are drawn in fixed chunks of 2^22 elements, each from its own child of the
+workload's SeedSequence, and filled by a thread pool: the bytes depend only on
+the seed, never on the number of threads.
 """
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field
 from typing import Dict, List, Optional
 
@@ -36,15 +41,44 @@ __all__ = ["Layer", "Workload", "f32_to_bf16_bits", "make_workload", "WORKLOADS"
            "routing_offsets", "make_layer", "random_offsets"]
 
 
+CHUNK = 1 << 22          # elements per independently seeded chunk
+
+
+def _threads() -> int:
+    # the host share of one GPU is at most 16 cores
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def _parallel(fn, n: int) -> None:
+    if n <= 1:
+        for i in range(n):
+            fn(i)
+        return
+    with ThreadPoolExecutor(max_workers=min(_threads(), n)) as ex:
+        list(ex.map(fn, range(n)))
+
+
+def _round_chunk(src: np.ndarray, dst: np.ndarray) -> None:
+    if not np.all(np.isfinite(src)):
+        raise ValueError("non-finite input")
+    u = src.view(np.uint32)
+    r = u >> 16
+    r &= 1
+    r += u
+    r += np.uint32(0x7FFF)
+    r >>= 16
+    dst[...] = r
+
+
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """Round float32 to bfloat16 (nearest, ties to even) and return the uint16 bits."""
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32)
-    if not np.all(np.isfinite(x)):
-        raise ValueError("non-finite input")
-    lsb = (u >> 16) & 1
-    r = (u + np.uint32(0x7FFF) + lsb) >> 16
-    return r.astype(np.uint16)
+    out = np.empty(x.shape, dtype=np.uint16)
+    xf, of = x.reshape(-1), out.reshape(-1)
+    n = xf.size
+    _parallel(lambda i: _round_chunk(xf[i * CHUNK:(i + 1) * CHUNK], of[i * CHUNK:(i + 1) * CHUNK]),
+              -(-n // CHUNK))
+    return out
 
 
 @dataclass
@@ -79,10 +113,21 @@ class Workload:
     description: str = ""
 
 
-def _normal(rng: np.random.Generator, shape, std: float = 1.0) -> np.ndarray:
-    out = rng.standard_normal(size=shape, dtype=np.float32)
-    if std != 1.0:
-        out *= np.float32(std)
+def _normal(seq: np.random.SeedSequence, shape, std: float = 1.0) -> np.ndarray:
+    """float32 N(0, std^2) of the given shape, chunk i drawn from child i of `seq`."""
+    out = np.empty(shape, dtype=np.float32)
+    flat = out.reshape(-1)
+    n = flat.size
+    nchunks = -(-n // CHUNK)
+    kids = seq.spawn(nchunks)
+
+    def fill(i):
+        part = flat[i * CHUNK:(i + 1) * CHUNK]
+        np.random.Generator(np.random.PCG64(kids[i])).standard_normal(out=part, dtype=np.float32)
+        if std != 1.0:
+            part *= np.float32(std)
+
+    _parallel(fill, nchunks)
     return out
 
 
@@ -147,17 +192,23 @@ def _sizes_dirichlet(rng, rows=32768, experts=16, alpha=5.0):
 
 def make_layer(rng, name, sizes, N, K, x_std=1.0, w_std=1.0, dy_std=1.0,
                outliers: Optional[str] = None, outlier_frac=1e-3) -> Layer:
+    """One layer's tensors; `rng` supplies the layer's seed and the outlier positions."""
     offs = routing_offsets(sizes)
     G = len(sizes)
     M = int(offs[-1])
-    x = _normal(rng, (M, K), x_std)
-    w = _normal(rng, (G, N, K), w_std)
-    dy = _normal(rng, (M, N), dy_std)
+    seq = np.random.SeedSequence(int(rng.integers(0, 2 ** 63)))
+    sx, sw, sdy = seq.spawn(3)
+    x = _normal(sx, (M, K), x_std)
+    w = _normal(sw, (G, N, K), w_std)
+    dy = _normal(sdy, (M, N), dy_std)
     if outliers is not None:
         for a in (x, w, dy):
             _outliers(rng, a, outlier_frac, outliers)
-    return Layer(name, G, M, N, K, offs,
-                 f32_to_bf16_bits(x), f32_to_bf16_bits(w), f32_to_bf16_bits(dy))
+    xb = f32_to_bf16_bits(x)
+    del x
+    wb = f32_to_bf16_bits(w)
+    del w
+    return Layer(name, G, M, N, K, offs, xb, wb, f32_to_bf16_bits(dy))
 
 
 def random_offsets(rng, M: int, G: int, empty_frac: float = 0.25) -> np.ndarray:
