@@ -10,7 +10,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmxmoe.so")
-SOURCES = ["api.hip", "quant_mx.hip", "quant_bw.hip", "gemm.hip"]
+SOURCES = ["api.hip", "quant_mx.hip", "quant_bw.hip", "gemm_bw.hip", "gemm_mx.hip"]
 ARCH = "gfx950"
 
 
@@ -25,7 +25,7 @@ def build(verbose: bool = False) -> str:
     """Compile every source for gfx950 and link libmxmoe.so; returns its path."""
     tmp = LIB + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
-           "-Wall", "-Wno-unused-function",
+           "-Wall", "-Wno-unused-function", "-Wno-inline-asm",
            # no packed-fp32 VALU ops in device code
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
            "-o", tmp] + [os.path.join(CSRC, s) for s in SOURCES]

@@ -95,6 +95,7 @@ struct GemmArgs {
   int32_t G;
   int32_t out_bf16;
   int32_t feed;       // GemmFeed
+  int32_t scale_dword;  // MX: every row's four scale bytes of a stage form one aligned dword
 };
 
 hipError_t launch_mx_gemm(int mode, const GemmArgs& a, hipStream_t st);

@@ -409,16 +409,6 @@ static void launch_feed(const GemmArgs& p, dim3 grid, dim3 block, hipStream_t st
   else hipLaunchKernelGGL((grouped_gemm_kernel<MODE, BW, kFeedPrecise>), grid, block, 0, st, p);
 }
 
-hipError_t launch_mx_gemm(int mode, const GemmArgs& p, hipStream_t st) {
-  const int64_t tiles = tile_upper_bound(mode, p);
-  if (tiles == 0) return hipSuccess;
-  dim3 grid((unsigned)tiles), block(kThreads);
-  if (mode == kFwd) launch_feed<kFwd, false>(p, grid, block, st);
-  else if (mode == kDgrad) launch_feed<kDgrad, false>(p, grid, block, st);
-  else launch_feed<kWgrad, false>(p, grid, block, st);
-  return hipGetLastError();
-}
-
 hipError_t launch_bw_gemm(int mode, const GemmArgs& p, hipStream_t st) {
   const int64_t tiles = tile_upper_bound(mode, p);
   if (tiles == 0) return hipSuccess;

@@ -1,0 +1,489 @@
+// MX grouped GEMM of a dropless MoE expert layer on gfx950: forward, dgrad and wgrad in one launch
+// each, every expert on its real number of rows (iitak.ru, "NVIDIA sped up training of
+// mixture-of-experts models on JAX tenfold": one call for all experts, real token counts, no capacity
+// padding, no dropped tokens; opensourcebeat.com MXFP8/DeepEP article, section "Two-sided attack":
+// MXFP8 applied to the grouped GEMMs of the expert layers).
+//
+// Generic form computed by one workgroup, output tile (mt, nt) of expert g:
+//   out[i, j] = sum_t A[row_a(i), col0 + t] * B[row_b(j), col0_b + t],   t < L_g
+// with a per-32 E8M0 scale on each operand, where
+//   forward: A = X rows of expert g, B = W_g rows (gN + n), L = K           (Y = X W^T)
+//   dgrad:   A = dY rows of expert g, B = column-wise W (rows k, columns gN..gN+N), L = N
+//   wgrad:   A = column-wise dY (rows n), B = column-wise X (rows k), both from column c_g,
+//            L = 32 ceil(m_g / 32); the zero pad columns of the layout contribute nothing
+//
+// Tiling: 256 x 256 output tile per workgroup of 8 waves (2 along A rows x 4 along B rows, 128 x 64
+// outputs per wave).  The contraction advances 128 bytes (four MX blocks) per stage.  Operand bytes
+// and scale bytes go global -> LDS by direct-to-LDS loads (no register staging), two stages in LDS:
+// the loads of stage s+1 are issued right after the barrier that publishes stage s, and land while
+// stage s is multiplied.  LDS rows are 128 bytes with 16-byte chunks XOR-swizzled by row.
+//
+// Operand feeds (same tiling and LDS staging):
+//  * precise (default): each lane reads 16 consecutive bytes of one MX block, widens them exactly to
+//    bf16 with the block's power-of-two scale folded in (v_cvt_scalef32_pk_bf16_fp8), and feeds two
+//    v_mfma_f32_32x32x16_bf16; every product is exact and the MFMA sums at fp32 precision.  A and B
+//    use the same assignment of contraction elements to MFMA k-slots, so the sum is unchanged.
+//  * fast (opt-in): v_mfma_scale_f32_16x16x128_f8f6f4 at twice the bf16 rate, scales applied by the
+//    instruction.  Lane l feeds row l % 16, 16-byte chunks g and 4 + g of the 128-byte row
+//    (g = l / 16) and the E8M0 byte of block g.  Its sums are truncated per run of products (see
+//    include/mxmoe.h).
+//
+// Scheduling: the tile list of the launch is built on the device from the group offsets (prefix sums
+// in LDS); forward / dgrad enumerate ceil(m_g / 256) row tiles per expert, so an expert without rows
+// has no tile and a 17-row expert one; wgrad has ceil(N/256) x ceil(K/256) tiles for every expert
+// (zeros for an empty one), experts taken largest first.  Inside an expert tiles are rasterised in
+// columns of four A tiles; consecutive chunks of 8 tiles go to the same XCD (workgroups are
+// dispatched round-robin over the 8 XCDs) so that tiles sharing operands share an L2.
+#include "common.h"
+
+namespace mxmoe {
+namespace {
+
+constexpr int BM = 256;                          // A rows per tile
+constexpr int BN = 256;                          // B rows per tile (output columns)
+constexpr int BK = 128;                          // contraction elements (bytes) per stage
+constexpr int NT = 512;                          // threads per workgroup
+constexpr int kStageA = BM * BK;                 // 32 KiB
+constexpr int kStage = kStageA + BN * BK;        // 64 KiB
+constexpr int kScaleStage = (BM + BN) * 4;       // four E8M0 bytes per operand row
+constexpr int kLds = 2 * kStage + 2 * kScaleStage;
+constexpr int kMaxG = 1024;
+constexpr int kXcd = 8;
+constexpr int kChunk = 8;
+constexpr int kGroupM = 4;
+constexpr int kLptMaxG = 256;                    // wgrad orders experts by size up to this G
+#ifndef MXMOE_LDS_SWZ
+#define MXMOE_LDS_SWZ(r) (((r) >> 1) & 7)
+#endif
+
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+struct Tile {
+  int g, mt, nt;
+  int64_t row0;   // forward / dgrad: first A row of the tile
+  int rows;       // forward / dgrad: valid A rows (1..256)
+  int64_t col0;   // wgrad: first column of the expert in the column-wise layout
+  int nblk;       // wgrad: 32-blocks in the expert's contraction
+};
+
+// LDS rows of 128 bytes; 16-byte chunk c of row r sits at chunk position c ^ swz(r), so that the
+// lanes of one 16-byte LDS read (consecutive rows, same logical chunk) hit distinct banks.
+__device__ __forceinline__ int swz(int r) { return MXMOE_LDS_SWZ(r); }
+__device__ __forceinline__ int lds_off(int r, int c) { return r * BK + ((c ^ swz(r)) << 4); }
+
+__device__ __forceinline__ int cdiv(int64_t a, int b) { return (int)((a + b - 1) / b); }
+
+// Tile list of the launch and this workgroup's tile.  Scratch arrays live at the start of the LDS
+// (before the first operand load overwrites them).  Returns false when the workgroup has no tile.
+template <int MODE>
+__device__ bool decode_tile(const GemmArgs& p, char* lds, Tile& t) {
+  int32_t* s_rs = (int32_t*)lds;             // clamped offsets [G+1]
+  int32_t* s_pre = s_rs + (kMaxG + 1);       // tile prefix over the processing order [G+1]
+  int32_t* s_cb = s_pre + (kMaxG + 1);       // wgrad: first 32-block of each expert [G+1]
+  int32_t* s_ord = s_cb + (kMaxG + 1);       // processing order [G]
+  const int G = p.G;
+  const int tid = threadIdx.x;
+  const int64_t M = p.M;
+  for (int g = tid; g <= G; g += NT) s_rs[g] = (int32_t)clamp_off(p.offs[g], M);
+  __syncthreads();
+  const bool lpt = MODE == kWgrad && G <= kLptMaxG;
+  for (int g = tid; g < G; g += NT) {
+    int pos = g;
+    if (lpt) {
+      const int mg = max(s_rs[g + 1] - s_rs[g], 0);
+      pos = 0;
+      for (int h = 0; h < G; ++h) {
+        const int mh = max(s_rs[h + 1] - s_rs[h], 0);
+        pos += (mh > mg) || (mh == mg && h < g);
+      }
+    }
+    s_ord[pos] = g;
+  }
+  __syncthreads();
+  const int ntc = cdiv(MODE == kFwd ? p.N : p.K, BN);
+  const int mtc_w = cdiv(p.N, BM);
+  const int lane = tid & 63;
+  if (tid < 64 || (MODE == kWgrad && tid < 128)) {
+    const bool tiles = tid < 64;
+    int carry = 0;
+    for (int base = 0; base < G; base += 64) {
+      const int q = base + lane;
+      int c = 0;
+      if (q < G) {
+        if (tiles) {
+          const int g = s_ord[q];
+          if (MODE == kWgrad) c = mtc_w * ntc;
+          else c = cdiv(max(s_rs[g + 1] - s_rs[g], 0), BM) * ntc;
+        } else {
+          c = cdiv(max(s_rs[q + 1] - s_rs[q], 0), 32);
+        }
+      }
+      int incl = c;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int v = __shfl_up(incl, d, 64);
+        if (lane >= d) incl += v;
+      }
+      if (q < G) (tiles ? s_pre : s_cb)[q] = carry + incl - c;
+      carry += __shfl(incl, 63, 64);
+    }
+    if (lane == 0) (tiles ? s_pre : s_cb)[G] = carry;
+  }
+  __syncthreads();
+
+  // workgroup -> logical tile: chunks of kChunk consecutive tiles per XCD visit
+  const int b = blockIdx.x;
+  const int x = b % kXcd, q = b / kXcd;
+  const int lt_all = ((q / kChunk) * kXcd + x) * kChunk + (q % kChunk);
+  if (lt_all >= s_pre[G]) return false;
+  int lo = 0, hi = G - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (s_pre[mid] <= lt_all) lo = mid; else hi = mid - 1;
+  }
+  const int g = s_ord[lo];
+  const int lt = lt_all - s_pre[lo];
+  const int m_g = max(s_rs[g + 1] - s_rs[g], 0);
+  const int mtc = MODE == kWgrad ? mtc_w : cdiv(m_g, BM);
+  const int span = kGroupM * ntc;
+  const int sg = lt / span;
+  const int fm = sg * kGroupM;
+  const int gsz = min(mtc - fm, kGroupM);
+  const int r = lt - sg * span;
+  t.g = g;
+  t.mt = fm + r % gsz;
+  t.nt = r / gsz;
+  t.row0 = s_rs[g] + (int64_t)t.mt * BM;
+  t.rows = (int)min((int64_t)BM, (int64_t)s_rs[g + 1] - t.row0);
+  t.col0 = 32 * (int64_t)s_cb[g];
+  t.nblk = cdiv(m_g, 32);
+  if (MODE == kWgrad) {
+    // offsets that are not monotone could place an expert past the leading dimension: clip
+    const int64_t room = p.lda > t.col0 ? (p.lda - t.col0) / 32 : 0;
+    if (t.nblk > room) t.nblk = (int)room;
+  }
+  return true;
+}
+
+// Eight E4M3 bytes -> eight bf16 multiplied by 2^(e-127), e the E8M0 byte whose bits sit in the
+// exponent field of `scale`; exact for every product the GEMMs form.
+__device__ __forceinline__ v8bf widen8(uint32_t w0, uint32_t w1, float scale) {
+  const v2bf a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, scale, false);
+  const v2bf b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, scale, true);
+  const v2bf c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, scale, false);
+  const v2bf d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, scale, true);
+  return v8bf{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+__device__ __forceinline__ float e8m0_as_scale(uint32_t word, int b) {
+  return __uint_as_float(((word >> (8 * b)) & 0xFFu) << 23);
+}
+
+// Direct global -> LDS loads.  Lane l writes its bytes at LDS address m0 + size * l, m0 being the
+// wave-uniform base.  Issued from inline assembly so that the compiler does not treat them as LDS
+// stores it must wait for before every later LDS read: the kernel orders them itself (stage_barrier).
+// Nothing else in these kernels uses m0.
+__device__ __forceinline__ uint32_t lds_addr(const char* p) { return (uint32_t)(uintptr_t)p; }
+
+__device__ __forceinline__ void dma16(const uint8_t* g, const char* lds_wave_base) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+               :: "s"(__builtin_amdgcn_readfirstlane(lds_addr(lds_wave_base))), "v"(g) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const uint8_t* g, const char* lds_wave_base) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off"
+               :: "s"(__builtin_amdgcn_readfirstlane(lds_addr(lds_wave_base))), "v"(g) : "memory", "m0");
+}
+
+// Wait for this wave's outstanding loads and LDS operations, then the workgroup barrier.  The memory
+// clobber keeps the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void stage_barrier() {
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+template <int MODE, int FEED, bool SDW>
+__device__ __forceinline__ void run_tile(const GemmArgs& p, const Tile& t, char* lds) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6;
+
+  // ---- operand geometry ----------------------------------------------------------------------
+  int64_t L;
+  if (MODE == kFwd) L = p.K;
+  else if (MODE == kDgrad) L = p.N;
+  else L = 32 * (int64_t)t.nblk;
+  const int nsteps = (int)((L + BK - 1) / BK);
+  const int64_t a_col0 = MODE == kWgrad ? t.col0 : 0;
+  const int64_t b_col0 = MODE == kWgrad ? t.col0 : (MODE == kDgrad ? (int64_t)t.g * p.N : 0);
+  const int64_t a_rows_lim = MODE == kWgrad ? p.N : 0;     // wgrad: A rows are n
+  const int64_t b_rows_lim = MODE == kFwd ? p.N : p.K;
+
+  auto a_row = [&](int r) -> int64_t {
+    if (MODE == kWgrad) return min((int64_t)t.mt * BM + r, a_rows_lim - 1);
+    return t.row0 + min(r, t.rows - 1);
+  };
+  auto b_row = [&](int r) -> int64_t {
+    const int64_t n = min((int64_t)t.nt * BN + r, b_rows_lim - 1);
+    return MODE == kFwd ? (int64_t)t.g * p.N + n : n;
+  };
+
+  // data loads: wave w moves rows [32w, 32w + 32) of A and of B, 8 rows (1 KiB) per instruction;
+  // lane l lands in row 32w + 8j + l/8 at chunk position l%8, which holds logical chunk
+  // (l%8) ^ swz(row)
+  const int drow = 32 * w + (lane >> 3);
+  int dchunk[4];
+  const uint8_t* a_src[4];
+  const uint8_t* b_src[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    dchunk[j] = (lane & 7) ^ swz(drow + 8 * j);
+    a_src[j] = p.a + a_row(drow + 8 * j) * p.lda + a_col0 + 16 * dchunk[j];
+    b_src[j] = p.b + b_row(drow + 8 * j) * p.ldb + b_col0 + 16 * dchunk[j];
+  }
+  // scale loads: four E8M0 bytes per row and stage, landing as one dword per row.  When the four
+  // bytes are an aligned dword in memory (forward, dgrad), waves 0-3 move A rows [64w, 64w + 64) and
+  // waves 4-7 the B rows with one direct-to-LDS dword load per lane.  Otherwise (wgrad: experts start
+  // at arbitrary 32-blocks) thread t gathers the bytes of row t % 256 of A (t < 256) or B into a
+  // register one stage ahead and stores the dword to LDS.
+  const uint8_t* sa = (const uint8_t*)p.sa;
+  const uint8_t* sb = (const uint8_t*)p.sb;
+  const int64_t sa_col0 = a_col0 / 32, sb_col0 = b_col0 / 32;
+  const uint8_t* s_src;
+  if (SDW) {
+    const int r = 64 * (w & 3) + lane;
+    s_src = w < 4 ? sa + a_row(r) * p.ldsa + sa_col0 : sb + b_row(r) * p.ldsb + sb_col0;
+  } else {
+    const int r = tid & 255;
+    s_src = tid < 256 ? sa + a_row(r) * p.ldsa + sa_col0 : sb + b_row(r) * p.ldsb + sb_col0;
+  }
+  // Bytes [4ks, 4ks + nv) of the thread's scale row (nv < 4 only in the last wgrad stage; the rest
+  // read as 0): two aligned dword loads funnel-shifted together.  The first word holds byte 0; the
+  // second is read only when it holds a wanted byte (else the first is read again), so no load
+  // touches a word without a byte of the row.  The words are combined only when stored, one stage
+  // later, so that no wait for them sits between the loads of a stage.
+  auto scale_geom = [&](int ks, int& nv, int& sh) -> const uint32_t* {
+    nv = MODE == kWgrad ? min(4, t.nblk - 4 * ks) : 4;
+    const uintptr_t ai = (uintptr_t)(s_src + 4 * ks);
+    sh = (int)(ai & 3);
+    return (const uint32_t*)(ai & ~(uintptr_t)3);
+  };
+  auto gather_scales = [&](int ks, uint32_t& lo, uint32_t& hi) {
+    int nv, sh;
+    typedef const __attribute__((address_space(1))) uint32_t* gptr;
+    const gptr w0 = (gptr)scale_geom(ks, nv, sh);
+    lo = *w0;
+    hi = *(sh + nv > 4 ? w0 + 1 : w0);
+  };
+  auto put_scales = [&](int ks, uint32_t lo, uint32_t hi) {
+    int nv, sh;
+    scale_geom(ks, nv, sh);
+    uint32_t v = __builtin_amdgcn_alignbyte(hi, lo, (uint32_t)sh);
+    if (nv < 4) v &= (1u << (8 * nv)) - 1u;
+    *(uint32_t*)(lds + 2 * kStage + (ks & 1) * kScaleStage + (tid < 256 ? 0 : BM * 4) + 4 * (tid & 255)) = v;
+  };
+
+  auto issue = [&](int ks) {
+    char* st = lds + (ks & 1) * kStage;
+    char* ss = lds + 2 * kStage + (ks & 1) * kScaleStage;
+    const int64_t koff = (int64_t)ks * BK;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      // wgrad: chunks past the expert's blocks are not loaded (zeroed after landing)
+      if (MODE != kWgrad || koff + 16 * dchunk[j] < L) {
+        dma16(a_src[j] + koff, st + (32 * w + 8 * j) * BK);
+        dma16(b_src[j] + koff, st + kStageA + (32 * w + 8 * j) * BK);
+      }
+    }
+    if (SDW) dma4(s_src + 4 * ks, ss + (w < 4 ? 0 : BM * 4) + 256 * (w & 3));
+  };
+
+  // ---- accumulators ----------------------------------------------------------------------------
+  const int wm = w >> 2, wn = w & 3;
+  constexpr int NI = FEED == kFeedPrecise ? 4 : 8;      // A fragments (32 or 16 rows)
+  constexpr int NJ = FEED == kFeedPrecise ? 2 : 4;      // B fragments
+  constexpr int NR = FEED == kFeedPrecise ? 16 : 4;     // accumulator registers per fragment pair
+  typedef float vacc __attribute__((ext_vector_type(NR)));
+  vacc acc[NI][NJ];
+#pragma unroll
+  for (int i = 0; i < NI; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int r = 0; r < NR; ++r) acc[i][j][r] = 0.f;
+
+  uint32_t s_lo = 0, s_hi = 0;                     // register-staged scale words of the next stage
+  if (nsteps > 0) {
+    issue(0);
+    if (!SDW) {
+      gather_scales(0, s_lo, s_hi);
+      put_scales(0, s_lo, s_hi);
+      if (nsteps > 1) gather_scales(1, s_lo, s_hi);
+    }
+  }
+  for (int ks = 0; ks < nsteps; ++ks) {
+    stage_barrier();                               // stage ks landed; stage ks-1 fully read
+    if (ks + 1 < nsteps) {
+      // the staged scale words arrived before the barrier; store them before issuing the next
+      // stage's loads so that no wait on those loads is needed here
+      if (!SDW) put_scales(ks + 1, s_lo, s_hi);
+      issue(ks + 1);
+      if (!SDW && ks + 2 < nsteps) gather_scales(ks + 2, s_lo, s_hi);
+    }
+    char* st = lds + (ks & 1) * kStage;
+    const uint32_t* SA = (const uint32_t*)(lds + 2 * kStage + (ks & 1) * kScaleStage);
+    const uint32_t* SB = SA + BM;
+    if (MODE == kWgrad && ks == nsteps - 1 && (t.nblk & 3)) {
+      // the last stage holds 1-3 valid blocks: zero the unloaded chunks of every row (their scale
+      // bytes were gathered as 0)
+      const int r = tid & 255;
+      char* row = st + (tid < 256 ? 0 : kStageA) + r * BK;
+      for (int bb = t.nblk & 3; bb < 4; ++bb) {
+        *(uint4*)(row + (((2 * bb) ^ swz(r)) << 4)) = make_uint4(0, 0, 0, 0);
+        *(uint4*)(row + (((2 * bb + 1) ^ swz(r)) << 4)) = make_uint4(0, 0, 0, 0);
+      }
+      stage_barrier();
+    }
+    const char* A = st;
+    const char* B = st + kStageA;
+
+    if constexpr (FEED == kFeedPrecise) {
+      const int lr = lane & 31, h = lane >> 5;
+      uint32_t sa_w[NI], sb_w[NJ];
+#pragma unroll
+      for (int i = 0; i < NI; ++i) sa_w[i] = SA[128 * wm + 32 * i + lr];
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) sb_w[j] = SB[64 * wn + 32 * j + lr];
+#pragma unroll
+      for (int bb = 0; bb < 4; ++bb) {
+        v8bf alo[NI], ahi[NI], blo[NJ], bhi[NJ];
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+          const int r = 128 * wm + 32 * i + lr;
+          const uint4 v = *(const uint4*)(A + lds_off(r, 2 * bb + h));
+          const float sc = e8m0_as_scale(sa_w[i], bb);
+          alo[i] = widen8(v.x, v.y, sc);
+          ahi[i] = widen8(v.z, v.w, sc);
+        }
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          const int r = 64 * wn + 32 * j + lr;
+          const uint4 v = *(const uint4*)(B + lds_off(r, 2 * bb + h));
+          const float sc = e8m0_as_scale(sb_w[j], bb);
+          blo[j] = widen8(v.x, v.y, sc);
+          bhi[j] = widen8(v.z, v.w, sc);
+        }
+#pragma unroll
+        for (int i = 0; i < NI; ++i)
+#pragma unroll
+          for (int j = 0; j < NJ; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo[i], blo[j], acc[i][j], 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < NI; ++i)
+#pragma unroll
+          for (int j = 0; j < NJ; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi[i], bhi[j], acc[i][j], 0, 0, 0);
+      }
+    } else {
+      const int fr = lane & 15, fg = lane >> 4;
+      v8i bf[NJ];
+      int sbv[NJ];
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int r = 64 * wn + 16 * j + fr;
+        const v4i lo = *(const v4i*)(B + lds_off(r, fg));
+        const v4i hi = *(const v4i*)(B + lds_off(r, 4 + fg));
+        bf[j] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        sbv[j] = (int)((SB[r] >> (8 * fg)) & 0xFFu);
+      }
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int r = 128 * wm + 16 * i + fr;
+        const v4i lo = *(const v4i*)(A + lds_off(r, fg));
+        const v4i hi = *(const v4i*)(A + lds_off(r, 4 + fg));
+        const v8i af = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        const int sav = (int)((SA[r] >> (8 * fg)) & 0xFFu);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bf[j], acc[i][j], 0, 0, 0, sav, 0, sbv[j]);
+      }
+    }
+  }
+
+  // ---- epilogue --------------------------------------------------------------------------------
+  const int64_t nout = MODE == kFwd ? p.N : p.K;
+#pragma unroll
+  for (int i = 0; i < NI; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        int rl, cl;
+        if constexpr (FEED == kFeedPrecise) {
+          // 32x32 accumulator: lane l holds column l%32, rows 8(r/4) + 4(l/32) + r%4
+          rl = 128 * wm + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          cl = 64 * wn + 32 * j + (lane & 31);
+        } else {
+          // 16x16 accumulator: lane l holds column l%16, rows 4(l/16) + r
+          rl = 128 * wm + 16 * i + 4 * (lane >> 4) + r;
+          cl = 64 * wn + 16 * j + (lane & 15);
+        }
+        const int64_t col = (int64_t)t.nt * BN + cl;
+        int64_t idx;
+        if (MODE == kWgrad) {
+          const int64_t n = (int64_t)t.mt * BM + rl;
+          if (n >= p.N || col >= p.K) continue;
+          idx = ((int64_t)t.g * p.N + n) * p.K + col;
+        } else {
+          if (rl >= t.rows || col >= nout) continue;
+          idx = (t.row0 + rl) * nout + col;
+        }
+        const float v = acc[i][j][r];
+        if (p.out_bf16) ((uint16_t*)p.out)[idx] = (uint16_t)f32_to_bf16_bits(v);
+        else ((float*)p.out)[idx] = v;
+      }
+}
+
+template <int MODE, int FEED, bool SDW>
+__global__ __launch_bounds__(NT, 1) void mx_grouped_gemm_kernel(GemmArgs p) {
+  __shared__ __attribute__((aligned(16))) char lds[kLds];
+  Tile t;
+  if (!decode_tile<MODE>(p, lds, t)) return;     // uniform across the workgroup
+  __syncthreads();                               // scheduler scratch is reused for operands
+  run_tile<MODE, FEED, SDW>(p, t, lds);
+}
+
+static_assert(4 * (kMaxG + 1) * 4 <= kStage, "scheduler scratch must fit in the first stage");
+
+int64_t tile_count_bound(int mode, const GemmArgs& p) {
+  if (mode == kWgrad) return (int64_t)p.G * ((p.N + BM - 1) / BM) * ((p.K + BN - 1) / BN);
+  const int64_t ntc = ((mode == kFwd ? p.N : p.K) + BN - 1) / BN;
+  return ((p.M + BM - 1) / BM + p.G) * ntc;     // sum_g ceil(m_g / BM) <= ceil(M / BM) + G
+}
+
+template <int MODE, bool SDW>
+void launch_mode(const GemmArgs& p, dim3 grid, hipStream_t st) {
+  if (p.feed == kFeedFast)
+    hipLaunchKernelGGL((mx_grouped_gemm_kernel<MODE, kFeedFast, SDW>), grid, dim3(NT), 0, st, p);
+  else
+    hipLaunchKernelGGL((mx_grouped_gemm_kernel<MODE, kFeedPrecise, SDW>), grid, dim3(NT), 0, st, p);
+}
+
+}  // namespace
+
+hipError_t launch_mx_gemm(int mode, const GemmArgs& args, hipStream_t st) {
+  GemmArgs p = args;
+  const int64_t tiles = tile_count_bound(mode, p);
+  if (tiles == 0) return hipSuccess;
+  const int64_t per = (int64_t)kXcd * kChunk;
+  const int64_t grid = (tiles + per - 1) / per * per;
+  if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
+  // four scale bytes of a row and stage are one aligned dword when every scale row and column
+  // offset is a multiple of 4 bytes (wgrad expert columns start at arbitrary 32-blocks)
+  p.scale_dword = mode != kWgrad && p.ldsa % 4 == 0 && p.ldsb % 4 == 0 && (p.N / 32) % 4 == 0;
+  const dim3 g((unsigned)grid);
+  if (mode == kFwd) launch_mode<kFwd, true>(p, g, st);
+  else if (mode == kDgrad && p.scale_dword) launch_mode<kDgrad, true>(p, g, st);
+  else if (mode == kDgrad) launch_mode<kDgrad, false>(p, g, st);
+  else launch_mode<kWgrad, false>(p, g, st);
+  return hipGetLastError();
+}
+
+}  // namespace mxmoe
