@@ -82,6 +82,9 @@ def build_layer_ops(m, torch, lay, dev_in, fast=False):
     w2 = w.view(G * N, K)
     f = 2.0 * M * N * K
     n = lay.name
+    mxb = 1.0 + 1.0 / 32.0          # E4M3 byte plus its share of an E8M0 scale
+    gemm_bytes = {"fwd": (M * K + G * N * K) * mxb + M * N * 2, "dgrad": (M * N + G * N * K) * mxb + M * K * 2,
+                  "wgrad": (M * N + M * K) * mxb + G * N * K * 4}
     ops = [
         Op(f"{n}.quant_x_row", "quant", lambda: m.mx_quantize_rowwise(x, b["qx"], b["sx"]),
            M * K * QUANT_BYTES_PER_ELEM, "mx_rowwise_kernel"),
@@ -104,6 +107,9 @@ def build_layer_ops(m, torch, lay, dev_in, fast=False):
                                                                  "f32", dw=b["dw"], fast=fast), f,
            "grouped_gemm wgrad"),
     ]
+    for op in ops:
+        if op.kind == "gemm":
+            op.bytes = gemm_bytes[op.name.split(".")[1]]
     return ops, b
 
 
@@ -168,6 +174,42 @@ def read_traffic():
     return rec.get("ops", {})
 
 
+def pmc_summary(fetch_csv: str, write_csv: str, out_path: str, cmds) -> None:
+    """Per-launch HBM bytes of the six GEMM launches of a step from two rocprofv3 counter runs of this
+    script (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each scaled by what the same counter
+    reads for the 1 GiB device copy the script performs before timing."""
+    import csv
+    names = [f"{l}.{k}" for l in ("gate_up", "down") for k in ("fwd", "dgrad", "wgrad")]
+    res = {}
+    factors = {}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        per_disp = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            d = per_disp.setdefault(int(r["Dispatch_Id"]), {"name": r["Kernel_Name"], "v": 0.0})
+            d["v"] += float(r["Counter_Value"])
+        disp = [per_disp[k] for k in sorted(per_disp)]
+        copies = [d["v"] for d in disp if "copyBuffer" in d["name"]]
+        cal_kib = max(copies)
+        factors[counter] = (1 << 30) / (cal_kib * 1024.0)
+        gemms = [d["v"] for d in disp if "mx_grouped_gemm" in d["name"]]
+        for i, v in enumerate(gemms):
+            res.setdefault(names[i % 6], {}).setdefault(counter, []).append(v * 1024.0 * factors[counter])
+    ops = {n: round(float(np.mean(c["FETCH_SIZE"])) + float(np.mean(c["WRITE_SIZE"])))
+           for n, c in res.items()}
+    rec = {"source_sha256": gemm_source_hash(), "calibration": factors, "ops": ops,
+           "fetch": {n: round(float(np.mean(c["FETCH_SIZE"]))) for n, c in res.items()},
+           "write": {n: round(float(np.mean(c["WRITE_SIZE"]))) for n, c in res.items()}}
+    with open(out_path, "w") as f:
+        f.write("# HBM traffic per launch of the six grouped-GEMM launches of one step (DeepSeek-V3-671B expert shard)\n")
+        f.write("# bytes = counter KiB * 1024 * (2^30 / counter KiB of the 1 GiB device copy); commands (repository root):\n")
+        for c in cmds:
+            f.write(f"#   {c}\n")
+        f.write(json.dumps(rec) + "\n")
+    print(json.dumps(rec))
+
+
 # ------------------------------------------------------------------------------------------- CPU oracle
 def cpu_baseline(lay, rows_per_expert=2048):
     """The oracle, as it stands, on a bounded sample: the largest expert's weights and its first
@@ -203,6 +245,69 @@ def cpu_baseline(lay, rows_per_expert=2048):
             "seconds": round(dt, 2), "cpu": cpu}
 
 
+# ------------------------------------------------------------------------------------------- blockwise
+def blockwise_leg(m, torch, steps=5, sample_rows=256):
+    """DeepSeek-style blockwise FP8 (1x128 activation tiles, 128x128 weight blocks, fp32 scales,
+    promotion every 128) against MXFP8 on the same DeepSeek-V3-16B expert-layer tensors: forward and
+    dgrad, each recipe with its own quantisers.  Accuracy: relative Frobenius error of each recipe's
+    fp32 Y and dX against an fp64 product of the original bf16 tensors, on sampled rows."""
+    from workloads import make_workload
+    wl = make_workload("dsv3_16b_blockwise")
+    out = {"workload": "dsv3_16b (64 experts, 49152 routed rows)", "layers": {}}
+    rng = np.random.default_rng(7)
+    for lay in wl.layers:
+        G, M, N, K = lay.G, lay.M, lay.N, lay.K
+        x, w, dy = to_device(torch, lay.x), to_device(torch, lay.w).view(G * N, K), to_device(torch, lay.dy)
+        offs = to_device(torch, lay.offs)
+        f = 2.0 * M * N * K
+        rec = {}
+        # blockwise
+        bq = {}
+        ops_bw = [
+            Op("quant_x", "quant", lambda: bq.update(x=m.fp8bw_quantize_act_1x128(x)), M * K * QUANT_BYTES_PER_ELEM, ""),
+            Op("quant_w", "quant", lambda: bq.update(w=m.fp8bw_quantize_weight_128x128(w)), G * N * K * QUANT_BYTES_PER_ELEM, ""),
+            Op("fwd", "gemm", lambda: bq.update(y=m.fp8bw_grouped_gemm_fwd(*bq["x"], *bq["w"], offs, N, "f32")), f, ""),
+            Op("quant_dy", "quant", lambda: bq.update(dy=m.fp8bw_quantize_act_1x128(dy)), M * N * QUANT_BYTES_PER_ELEM, ""),
+            Op("dgrad", "gemm", lambda: bq.update(dx=m.fp8bw_grouped_gemm_dgrad(*bq["dy"], *bq["w"], offs, K, "f32")), f, ""),
+        ]
+        mq = {}
+        ld = G * N
+        ops_mx = [
+            Op("quant_x", "quant", lambda: mq.update(x=m.mx_quantize_rowwise(x)), M * K * QUANT_BYTES_PER_ELEM, ""),
+            Op("quant_w", "quant", lambda: mq.update(w=m.mx_quantize_rowwise(w)), G * N * K * QUANT_BYTES_PER_ELEM, ""),
+            Op("fwd", "gemm", lambda: mq.update(y=m.mx_grouped_gemm_fwd(*mq["x"], *mq["w"], offs, N, "f32")), f, ""),
+            Op("quant_dy", "quant", lambda: mq.update(dy=m.mx_quantize_rowwise(dy)), M * N * QUANT_BYTES_PER_ELEM, ""),
+            Op("quant_w_col", "quant", lambda: mq.update(wc=m.mx_quantize_colwise(w, None, ld=ld)), G * N * K * QUANT_BYTES_PER_ELEM, ""),
+            Op("dgrad", "gemm", lambda: mq.update(dx=m.mx_grouped_gemm_dgrad(*mq["dy"], *mq["wc"], offs, K, "f32")), f, ""),
+        ]
+        for name, ops_ in (("blockwise", ops_bw), ("mxfp8", ops_mx)):
+            ms = time_ops(torch, ops_, steps, 1)
+            gm = sum(float(np.mean(o.ms)) for o in ops_ if o.kind == "gemm")
+            rec[name] = {"ms_fwd_dgrad_with_quant": round(ms, 4),
+                         "gemm_tflops": round(2 * f / (gm * 1e-3) / 1e12, 1),
+                         "ops": {o.name: op_summary(o) for o in ops_}}
+        # accuracy on sampled rows against fp64 products of the bf16 inputs
+        rows = np.sort(rng.choice(M, sample_rows, replace=False))
+        grp = np.searchsorted(lay.offs.astype(np.int64), rows, side="right") - 1
+        xb = bf16_to_f64(lay.x[rows]); dyb = bf16_to_f64(lay.dy[rows])
+        wf = lay.w.reshape(G, N, K)
+        y_ref = np.stack([xb[i] @ bf16_to_f64(wf[g]).T for i, g in enumerate(grp)])
+        dx_ref = np.stack([dyb[i] @ bf16_to_f64(wf[g]) for i, g in enumerate(grp)])
+        for name, q in (("blockwise", bq), ("mxfp8", mq)):
+            yg = q["y"][torch.from_numpy(rows).cuda()].double().cpu().numpy()
+            dxg = q["dx"][torch.from_numpy(rows).cuda()].double().cpu().numpy()
+            rec[name]["rel_fro_err_y"] = float(np.linalg.norm(yg - y_ref) / np.linalg.norm(y_ref))
+            rec[name]["rel_fro_err_dx"] = float(np.linalg.norm(dxg - dx_ref) / np.linalg.norm(dx_ref))
+        out["layers"][lay.name] = rec
+        del x, w, dy, bq, mq, ops_bw, ops_mx
+        torch.cuda.empty_cache()
+    return out
+
+
+def bf16_to_f64(a: np.ndarray) -> np.ndarray:
+    return (np.asarray(a, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
 # ------------------------------------------------------------------------------------------- main
 def main():
     ap = argparse.ArgumentParser()
@@ -212,7 +317,18 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle timing")
     ap.add_argument("--no-extra-legs", action="store_true",
                     help="skip the FP8-feed and blockwise legs (reported beside the headline)")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write the GEMM traffic summary from two rocprofv3 counter runs of this script")
     args = ap.parse_args()
+
+    if args.pmc_summary:
+        cmds = [f"rocprofv3 --pmc {c} --output-format csv -d gpurun_out/pmc_{c.lower()} -o p -- "
+                "python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-extra-legs"
+                for c in ("FETCH_SIZE", "WRITE_SIZE")]
+        cmds.append("python3 bench.py --pmc-summary gpurun_out/pmc_fetch_size/p_counter_collection.csv "
+                    "gpurun_out/pmc_write_size/p_counter_collection.csv")
+        pmc_summary(args.pmc_summary[0], args.pmc_summary[1], TRAFFIC_FILE, cmds)
+        return
 
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
@@ -268,12 +384,14 @@ def main():
     roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_PEAK_TFLOPS["bf16"],
                 "unit": "TFLOP/s", "frac": round(achieved / MFMA_PEAK_TFLOPS["bf16"], 4),
                 "traffic": (traffic or {}).get(dom.name), "op": dom.name, "kernel": dom.kernel,
-                "flop_per_launch": dom.work, "avg_launch_ms": round(dom_ms, 4),
+                "flop_per_launch": dom.work, "algorithmic_bytes_per_launch": round(dom.bytes),
+                "avg_launch_ms": round(dom_ms, 4),
                 "frac_of_mxfp8_peak": round(achieved / MFMA_PEAK_TFLOPS["mxfp8"], 4)}
 
     extra = {}
     if not args.no_extra_legs:
-        # the same GEMMs on the full-rate block-scaled FP8 MFMA (reduced-precision sums; see DESIGN)
+        # the same GEMMs on the full-rate block-scaled FP8 MFMA, whose sums are truncated per run of
+        # 8 products: reported beside the headline, never as it
         fops = []
         for lay, (dev_in, _) in zip(wl.layers, keep):
             lops, bufs = build_layer_ops(m, torch, lay, dev_in, fast=True)
@@ -289,6 +407,9 @@ def main():
         extra["fp8_feed_gemm_tflops"] = round(gemm_flops / (fms * 1e-3) / 1e12, 1)
         del fops, flat, g_ops
         torch.cuda.empty_cache()
+        del keep, ops
+        torch.cuda.empty_cache()
+        extra["blockwise_vs_mx"] = blockwise_leg(m, torch)
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -224,3 +224,58 @@ def test_blockwise_full_size_sampled():
         ref, bnd = oracle.bw_gemm_dgrad(host(qd), host(sd), hqw, hsw, lay.offs, lay.N, lay.K, rows=rows)
         print(lay.name, "bw dgrad", _check(_gpu_out(dx)[rows], ref, bnd, "f32", "bw dgrad"))
         torch.cuda.empty_cache()
+
+
+def test_precise_feed_keeps_small_products_of_a_run():
+    """A product 2^17 times smaller than the largest one of its 8-element contraction run is summed
+    exactly by the precise feed (the block-scaled FP8 MFMA keeps only about 14 bits below the run's
+    largest product).  The sums are exact in fp32, so the result must equal the oracle bit for bit."""
+    m = require_gpu()
+    K, N = 128, 256
+    offs = np.array([0, 1], np.int32)
+    qw = np.full((N, K), 0x38, np.uint8)                 # 1.0
+    sw = np.full((N, K // 32), 127, np.uint8)
+    cases = []
+    for j in (1, 3, 7, 8, 40, 127):
+        qx = np.zeros((1, K), np.uint8)
+        qx[0, 0], qx[0, j] = 0x78, 0x01                  # 256 and 2^-9
+        cases.append(qx)
+    qx = np.zeros((1, K), np.uint8)
+    qx[0, 0], qx[0, 1:8] = 0x78, 0x1F                    # 256 and seven times 0.1171875
+    cases.append(qx)
+    sx = np.full((1, K // 32), 127, np.uint8)
+    for qx in cases:
+        y = m.mx_grouped_gemm_fwd(dev(qx), dev(sx), dev(qw), dev(sw), dev(offs), N, "f32")
+        ref, _ = oracle.mx_gemm_fwd(qx, sx, qw, sw, offs, N)
+        assert np.array_equal(_gpu_out(y), ref), (np.flatnonzero(qx[0]), _gpu_out(y)[0, 0], ref[0, 0])
+
+
+def _block_scaled_bf16(rng, shape, block_axis, span=40):
+    """N(0,1) values whose 32-element blocks along `block_axis` are each scaled by 2^u, u ~ U{-span..span}."""
+    from workloads import f32_to_bf16_bits
+    x = rng.standard_normal(shape).astype(np.float32)
+    if block_axis == 1:
+        u = rng.integers(-span, span + 1, size=(shape[0], shape[1] // 32))
+        x *= np.repeat(np.exp2(u), 32, axis=1).astype(np.float32)
+    else:
+        u = rng.integers(-span, span + 1, size=(-(-shape[0] // 32), shape[1]))
+        x *= np.repeat(np.exp2(u), 32, axis=0)[:shape[0]].astype(np.float32)
+    return f32_to_bf16_bits(x)
+
+
+@pytest.mark.parametrize("fast", [False, True])
+def test_per_block_scales_over_a_wide_range(fast):
+    """Every 32-block carries its own scale (2^-40 .. 2^40 relative): a scale paired with the wrong
+    block would miss the oracle by orders of magnitude.  Blocks vary along the contraction axis of
+    each GEMM (row-wise copies along K / N, column-wise copies down the token rows)."""
+    m = require_gpu()
+    rng = np.random.default_rng(40)
+    sizes, N, K = [33, 0, 290, 5, 64], 256, 512
+    offs = routing_offsets(sizes)
+    M, G = int(offs[-1]), len(sizes)
+    L = Layer(offs, _block_scaled_bf16(rng, (M, K), 1), _block_scaled_bf16(rng, (G * N, K), 1),
+              _block_scaled_bf16(rng, (M, N), 1), N, K)
+    print(run_layer(m, L, check=("fwd",), fast=fast))
+    L = Layer(offs, _block_scaled_bf16(rng, (M, K), 0), _block_scaled_bf16(rng, (G * N, K), 0),
+              _block_scaled_bf16(rng, (M, N), 0), N, K)
+    print(run_layer(m, L, check=("dgrad", "wgrad"), fast=fast))
