@@ -39,10 +39,25 @@
 namespace mxmoe {
 namespace {
 
+#ifndef MXMOE_WAVES_M
+#define MXMOE_WAVES_M 2
+#endif
+#ifndef MXMOE_WAVES_N
+#define MXMOE_WAVES_N 4
+#endif
 constexpr int BM = 256;                          // A rows per tile
 constexpr int BN = 256;                          // B rows per tile (output columns)
 constexpr int BK = 128;                          // contraction elements (bytes) per stage
-constexpr int NT = 512;                          // threads per workgroup
+constexpr int kWavesM = MXMOE_WAVES_M;           // waves along the A rows of the tile
+constexpr int kWavesN = MXMOE_WAVES_N;           // waves along the B rows
+constexpr int kWaves = kWavesM * kWavesN;
+constexpr int NT = 64 * kWaves;                  // threads per workgroup
+constexpr int WM = BM / kWavesM;                 // outputs per wave along A rows
+constexpr int WN = BN / kWavesN;                 // outputs per wave along B rows
+constexpr int kLoadRows = BM / kWaves;           // A (and B) rows each wave loads per stage
+constexpr int kScaleLoads = 2 * BM / 64 / kWaves;  // dword scale loads (64 rows each) per wave
+constexpr int kScaleRows = 2 * BM / NT;          // scale rows each thread gathers (register path)
+static_assert(BM == BN && kLoadRows % 8 == 0 && kScaleLoads >= 1 && kScaleRows >= 1, "tile / wave layout");
 constexpr int kStageA = BM * BK;                 // 32 KiB
 constexpr int kStage = kStageA + BN * BK;        // 64 KiB
 constexpr int kScaleStage = (BM + BN) * 4;       // four E8M0 bytes per operand row
@@ -225,59 +240,65 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const Tile& t, char*
     return MODE == kFwd ? (int64_t)t.g * p.N + n : n;
   };
 
-  // data loads: wave w moves rows [32w, 32w + 32) of A and of B, 8 rows (1 KiB) per instruction;
-  // lane l lands in row 32w + 8j + l/8 at chunk position l%8, which holds logical chunk
+  // data loads: wave w moves rows [R w, R w + R) of A and of B (R = kLoadRows), 8 rows (1 KiB) per
+  // instruction; lane l lands in row R w + 8j + l/8 at chunk position l%8, which holds logical chunk
   // (l%8) ^ swz(row)
-  const int drow = 32 * w + (lane >> 3);
-  int dchunk[4];
-  const uint8_t* a_src[4];
-  const uint8_t* b_src[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    dchunk[j] = (lane & 7) ^ swz(drow + 8 * j);
-    a_src[j] = p.a + a_row(drow + 8 * j) * p.lda + a_col0 + 16 * dchunk[j];
-    b_src[j] = p.b + b_row(drow + 8 * j) * p.ldb + b_col0 + 16 * dchunk[j];
-  }
-  // scale loads: four E8M0 bytes per row and stage, landing as one dword per row.  When the four
-  // bytes are an aligned dword in memory (forward, dgrad), waves 0-3 move A rows [64w, 64w + 64) and
-  // waves 4-7 the B rows with one direct-to-LDS dword load per lane.  Otherwise (wgrad: experts start
-  // at arbitrary 32-blocks) thread t gathers the bytes of row t % 256 of A (t < 256) or B into a
-  // register one stage ahead and stores the dword to LDS.
+  constexpr int ND = kLoadRows / 8;
+  const int drow = kLoadRows * w + (lane >> 3);
+  // source addresses are formed at issue time (few VALU operations per load) rather than kept in
+  // registers, which the accumulators need
+  auto dchunk = [&](int j) { return (lane & 7) ^ swz(drow + 8 * j); };
+  auto a_src = [&](int j) { return p.a + a_row(drow + 8 * j) * p.lda + a_col0 + 16 * dchunk(j); };
+  auto b_src = [&](int j) { return p.b + b_row(drow + 8 * j) * p.ldb + b_col0 + 16 * dchunk(j); };
+  // scale loads: four E8M0 bytes per row and stage, landing as one dword per row (A rows then B
+  // rows).  When the four bytes are an aligned dword in memory (forward, dgrad), the 512 rows move
+  // as 8 direct-to-LDS dword loads of 64 rows (u < 4: A rows [64u, 64u + 64), else B rows), spread
+  // over the waves.  Otherwise (wgrad: experts start at arbitrary 32-blocks) thread t gathers rows
+  // q = t + NT j (q < 256: A row q, else B row q - 256) into registers one stage ahead and stores
+  // the dwords to LDS.
   const uint8_t* sa = (const uint8_t*)p.sa;
   const uint8_t* sb = (const uint8_t*)p.sb;
   const int64_t sa_col0 = a_col0 / 32, sb_col0 = b_col0 / 32;
-  const uint8_t* s_src;
-  if (SDW) {
-    const int r = 64 * (w & 3) + lane;
-    s_src = w < 4 ? sa + a_row(r) * p.ldsa + sa_col0 : sb + b_row(r) * p.ldsb + sb_col0;
-  } else {
-    const int r = tid & 255;
-    s_src = tid < 256 ? sa + a_row(r) * p.ldsa + sa_col0 : sb + b_row(r) * p.ldsb + sb_col0;
+  constexpr int NS = SDW ? kScaleLoads : kScaleRows;
+  const uint8_t* s_src[NS];
+#pragma unroll
+  for (int j = 0; j < NS; ++j) {
+    int q;
+    if (SDW) q = 64 * (kScaleLoads * w + j) + lane;
+    else q = tid + NT * j;
+    const int r = q & 255;
+    s_src[j] = q < 256 ? sa + a_row(r) * p.ldsa + sa_col0 : sb + b_row(r) * p.ldsb + sb_col0;
   }
-  // Bytes [4ks, 4ks + nv) of the thread's scale row (nv < 4 only in the last wgrad stage; the rest
-  // read as 0): two aligned dword loads funnel-shifted together.  The first word holds byte 0; the
-  // second is read only when it holds a wanted byte (else the first is read again), so no load
-  // touches a word without a byte of the row.  The words are combined only when stored, one stage
-  // later, so that no wait for them sits between the loads of a stage.
-  auto scale_geom = [&](int ks, int& nv, int& sh) -> const uint32_t* {
+  // Bytes [4ks, 4ks + nv) of a scale row (nv < 4 only in the last wgrad stage; the rest read as 0):
+  // two aligned dword loads funnel-shifted together.  The first word holds byte 0; the second is
+  // read only when it holds a wanted byte (else the first is read again), so no load touches a word
+  // without a byte of the row.  The words are combined only when stored, one stage later, so that no
+  // wait for them sits between the loads of a stage.
+  auto scale_geom = [&](int j, int ks, int& nv, int& sh) -> const uint32_t* {
     nv = MODE == kWgrad ? min(4, t.nblk - 4 * ks) : 4;
-    const uintptr_t ai = (uintptr_t)(s_src + 4 * ks);
+    const uintptr_t ai = (uintptr_t)(s_src[j] + 4 * ks);
     sh = (int)(ai & 3);
     return (const uint32_t*)(ai & ~(uintptr_t)3);
   };
-  auto gather_scales = [&](int ks, uint32_t& lo, uint32_t& hi) {
-    int nv, sh;
-    typedef const __attribute__((address_space(1))) uint32_t* gptr;
-    const gptr w0 = (gptr)scale_geom(ks, nv, sh);
-    lo = *w0;
-    hi = *(sh + nv > 4 ? w0 + 1 : w0);
+  auto gather_scales = [&](int ks, uint32_t* lo, uint32_t* hi) {
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      int nv, sh;
+      typedef const __attribute__((address_space(1))) uint32_t* gptr;
+      const gptr w0 = (gptr)scale_geom(j, ks, nv, sh);
+      lo[j] = *w0;
+      hi[j] = *(sh + nv > 4 ? w0 + 1 : w0);
+    }
   };
-  auto put_scales = [&](int ks, uint32_t lo, uint32_t hi) {
-    int nv, sh;
-    scale_geom(ks, nv, sh);
-    uint32_t v = __builtin_amdgcn_alignbyte(hi, lo, (uint32_t)sh);
-    if (nv < 4) v &= (1u << (8 * nv)) - 1u;
-    *(uint32_t*)(lds + 2 * kStage + (ks & 1) * kScaleStage + (tid < 256 ? 0 : BM * 4) + 4 * (tid & 255)) = v;
+  auto put_scales = [&](int ks, const uint32_t* lo, const uint32_t* hi) {
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      int nv, sh;
+      scale_geom(j, ks, nv, sh);
+      uint32_t v = __builtin_amdgcn_alignbyte(hi[j], lo[j], (uint32_t)sh);
+      if (nv < 4) v &= (1u << (8 * nv)) - 1u;
+      *(uint32_t*)(lds + 2 * kStage + (ks & 1) * kScaleStage + 4 * (tid + NT * j)) = v;
+    }
   };
 
   auto issue = [&](int ks) {
@@ -285,20 +306,23 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const Tile& t, char*
     char* ss = lds + 2 * kStage + (ks & 1) * kScaleStage;
     const int64_t koff = (int64_t)ks * BK;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < ND; ++j) {
       // wgrad: chunks past the expert's blocks are not loaded (zeroed after landing)
-      if (MODE != kWgrad || koff + 16 * dchunk[j] < L) {
-        dma16(a_src[j] + koff, st + (32 * w + 8 * j) * BK);
-        dma16(b_src[j] + koff, st + kStageA + (32 * w + 8 * j) * BK);
+      if (MODE != kWgrad || koff + 16 * dchunk(j) < L) {
+        dma16(a_src(j) + koff, st + (kLoadRows * w + 8 * j) * BK);
+        dma16(b_src(j) + koff, st + kStageA + (kLoadRows * w + 8 * j) * BK);
       }
     }
-    if (SDW) dma4(s_src + 4 * ks, ss + (w < 4 ? 0 : BM * 4) + 256 * (w & 3));
+    if (SDW) {
+#pragma unroll
+      for (int j = 0; j < NS; ++j) dma4(s_src[j] + 4 * ks, ss + 256 * (kScaleLoads * w + j));
+    }
   };
 
   // ---- accumulators ----------------------------------------------------------------------------
-  const int wm = w >> 2, wn = w & 3;
-  constexpr int NI = FEED == kFeedPrecise ? 4 : 8;      // A fragments (32 or 16 rows)
-  constexpr int NJ = FEED == kFeedPrecise ? 2 : 4;      // B fragments
+  const int wm = w / kWavesN, wn = w % kWavesN;
+  constexpr int NI = FEED == kFeedPrecise ? WM / 32 : WM / 16;   // A fragments (32 or 16 rows)
+  constexpr int NJ = FEED == kFeedPrecise ? WN / 32 : WN / 16;   // B fragments
   constexpr int NR = FEED == kFeedPrecise ? 16 : 4;     // accumulator registers per fragment pair
   typedef float vacc __attribute__((ext_vector_type(NR)));
   vacc acc[NI][NJ];
@@ -309,7 +333,7 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const Tile& t, char*
 #pragma unroll
       for (int r = 0; r < NR; ++r) acc[i][j][r] = 0.f;
 
-  uint32_t s_lo = 0, s_hi = 0;                     // register-staged scale words of the next stage
+  uint32_t s_lo[NS], s_hi[NS];                    // register-staged scale words of the next stage
   if (nsteps > 0) {
     issue(0);
     if (!SDW) {
@@ -333,11 +357,13 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const Tile& t, char*
     if (MODE == kWgrad && ks == nsteps - 1 && (t.nblk & 3)) {
       // the last stage holds 1-3 valid blocks: zero the unloaded chunks of every row (their scale
       // bytes were gathered as 0)
-      const int r = tid & 255;
-      char* row = st + (tid < 256 ? 0 : kStageA) + r * BK;
-      for (int bb = t.nblk & 3; bb < 4; ++bb) {
-        *(uint4*)(row + (((2 * bb) ^ swz(r)) << 4)) = make_uint4(0, 0, 0, 0);
-        *(uint4*)(row + (((2 * bb + 1) ^ swz(r)) << 4)) = make_uint4(0, 0, 0, 0);
+      for (int q = tid; q < BM + BN; q += NT) {
+        const int r = q & 255;
+        char* row = st + (q < BM ? 0 : kStageA) + r * BK;
+        for (int bb = t.nblk & 3; bb < 4; ++bb) {
+          *(uint4*)(row + (((2 * bb) ^ swz(r)) << 4)) = make_uint4(0, 0, 0, 0);
+          *(uint4*)(row + (((2 * bb + 1) ^ swz(r)) << 4)) = make_uint4(0, 0, 0, 0);
+        }
       }
       stage_barrier();
     }
@@ -348,15 +374,15 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const Tile& t, char*
       const int lr = lane & 31, h = lane >> 5;
       uint32_t sa_w[NI], sb_w[NJ];
 #pragma unroll
-      for (int i = 0; i < NI; ++i) sa_w[i] = SA[128 * wm + 32 * i + lr];
+      for (int i = 0; i < NI; ++i) sa_w[i] = SA[WM * wm + 32 * i + lr];
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) sb_w[j] = SB[64 * wn + 32 * j + lr];
+      for (int j = 0; j < NJ; ++j) sb_w[j] = SB[WN * wn + 32 * j + lr];
 #pragma unroll
       for (int bb = 0; bb < 4; ++bb) {
         v8bf alo[NI], ahi[NI], blo[NJ], bhi[NJ];
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
-          const int r = 128 * wm + 32 * i + lr;
+          const int r = WM * wm + 32 * i + lr;
           const uint4 v = *(const uint4*)(A + lds_off(r, 2 * bb + h));
           const float sc = e8m0_as_scale(sa_w[i], bb);
           alo[i] = widen8(v.x, v.y, sc);
@@ -364,7 +390,7 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const Tile& t, char*
         }
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
-          const int r = 64 * wn + 32 * j + lr;
+          const int r = WN * wn + 32 * j + lr;
           const uint4 v = *(const uint4*)(B + lds_off(r, 2 * bb + h));
           const float sc = e8m0_as_scale(sb_w[j], bb);
           blo[j] = widen8(v.x, v.y, sc);
@@ -387,7 +413,7 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const Tile& t, char*
       int sbv[NJ];
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
-        const int r = 64 * wn + 16 * j + fr;
+        const int r = WN * wn + 16 * j + fr;
         const v4i lo = *(const v4i*)(B + lds_off(r, fg));
         const v4i hi = *(const v4i*)(B + lds_off(r, 4 + fg));
         bf[j] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
@@ -395,7 +421,7 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const Tile& t, char*
       }
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
-        const int r = 128 * wm + 16 * i + fr;
+        const int r = WM * wm + 16 * i + fr;
         const v4i lo = *(const v4i*)(A + lds_off(r, fg));
         const v4i hi = *(const v4i*)(A + lds_off(r, 4 + fg));
         const v8i af = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
@@ -408,37 +434,35 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const Tile& t, char*
   }
 
   // ---- epilogue --------------------------------------------------------------------------------
+  // Output row of tile row rl: forward / dgrad row0 + rl of [M, nout]; wgrad n = mt*BM + rl of dW_g
+  // [N, K].  Every lane keeps one base address (its first row and column); the offsets of its other
+  // elements are the same for all lanes, so they cost scalar arithmetic only.
   const int64_t nout = MODE == kFwd ? p.N : p.K;
+  const int64_t row_lim = MODE == kWgrad ? p.N - (int64_t)t.mt * BM : t.rows;   // valid tile rows
+  const int64_t col_lim = nout - (int64_t)t.nt * BN;                               // valid tile columns
+  const int64_t out_row0 = MODE == kWgrad ? (int64_t)t.g * p.N + (int64_t)t.mt * BM : t.row0;
+  // 32x32 accumulator: lane l holds column l%32 and rows 8(r/4) + 4(l/32) + r%4;
+  // 16x16 accumulator: lane l holds column l%16 and rows 4(l/16) + r
+  const int lr0 = FEED == kFeedPrecise ? WM * wm + 4 * (lane >> 5) : WM * wm + 4 * (lane >> 4);
+  const int lc0 = FEED == kFeedPrecise ? WN * wn + (lane & 31) : WN * wn + (lane & 15);
+  const int64_t base = (out_row0 + lr0) * nout + (int64_t)t.nt * BN + lc0;
+  constexpr int FI = FEED == kFeedPrecise ? 32 : 16;     // fragment rows / columns
 #pragma unroll
   for (int i = 0; i < NI; ++i)
 #pragma unroll
-    for (int j = 0; j < NJ; ++j)
+    for (int r = 0; r < NR; ++r) {
+      const int ro = FI * i + (FEED == kFeedPrecise ? 8 * (r >> 2) + (r & 3) : r);   // uniform
+      if (lr0 + ro >= row_lim) continue;
+      const int64_t rbase = base + (int64_t)ro * nout;
 #pragma unroll
-      for (int r = 0; r < NR; ++r) {
-        int rl, cl;
-        if constexpr (FEED == kFeedPrecise) {
-          // 32x32 accumulator: lane l holds column l%32, rows 8(r/4) + 4(l/32) + r%4
-          rl = 128 * wm + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-          cl = 64 * wn + 32 * j + (lane & 31);
-        } else {
-          // 16x16 accumulator: lane l holds column l%16, rows 4(l/16) + r
-          rl = 128 * wm + 16 * i + 4 * (lane >> 4) + r;
-          cl = 64 * wn + 16 * j + (lane & 15);
-        }
-        const int64_t col = (int64_t)t.nt * BN + cl;
-        int64_t idx;
-        if (MODE == kWgrad) {
-          const int64_t n = (int64_t)t.mt * BM + rl;
-          if (n >= p.N || col >= p.K) continue;
-          idx = ((int64_t)t.g * p.N + n) * p.K + col;
-        } else {
-          if (rl >= t.rows || col >= nout) continue;
-          idx = (t.row0 + rl) * nout + col;
-        }
+      for (int j = 0; j < NJ; ++j) {
+        if (lc0 + FI * j >= col_lim) continue;
+        const int64_t idx = rbase + FI * j;
         const float v = acc[i][j][r];
         if (p.out_bf16) ((uint16_t*)p.out)[idx] = (uint16_t)f32_to_bf16_bits(v);
         else ((float*)p.out)[idx] = v;
       }
+    }
 }
 
 template <int MODE, int FEED, bool SDW>
