@@ -400,12 +400,12 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const Tile& t, char*
         for (int i = 0; i < NI; ++i)
 #pragma unroll
           for (int j = 0; j < NJ; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo[i], blo[j], acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(blo[j], alo[i], acc[i][j], 0, 0, 0);
 #pragma unroll
         for (int i = 0; i < NI; ++i)
 #pragma unroll
           for (int j = 0; j < NJ; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi[i], bhi[j], acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bhi[j], ahi[i], acc[i][j], 0, 0, 0);
       }
     } else {
       const int fr = lane & 15, fg = lane >> 4;
@@ -428,41 +428,47 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const Tile& t, char*
         const int sav = (int)((SA[r] >> (8 * fg)) & 0xFFu);
 #pragma unroll
         for (int j = 0; j < NJ; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bf[j], acc[i][j], 0, 0, 0, sav, 0, sbv[j]);
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[j], af, acc[i][j], 0, 0, 0, sbv[j], 0, sav);
       }
     }
   }
 
   // ---- epilogue --------------------------------------------------------------------------------
-  // Output row of tile row rl: forward / dgrad row0 + rl of [M, nout]; wgrad n = mt*BM + rl of dW_g
-  // [N, K].  Every lane keeps one base address (its first row and column); the offsets of its other
-  // elements are the same for all lanes, so they cost scalar arithmetic only.
+  // The MFMAs take the B fragment as their first operand, so each accumulator holds a tile transposed:
+  // lane l has output row (fragment row) l % 32 (l % 16 for the 16x16 shape) and, per group of four
+  // registers, four consecutive output columns, written with one 8-byte (bf16) or 16-byte (fp32)
+  // store.  Output row of tile row rl: forward / dgrad row0 + rl of [M, nout]; wgrad n = mt*BM + rl
+  // of dW_g [N, K].  N and K are multiples of 128, so no group of four columns straddles the edge.
   const int64_t nout = MODE == kFwd ? p.N : p.K;
-  const int64_t row_lim = MODE == kWgrad ? p.N - (int64_t)t.mt * BM : t.rows;   // valid tile rows
-  const int64_t col_lim = nout - (int64_t)t.nt * BN;                               // valid tile columns
+  const int row_lim = (int)min((int64_t)BM, MODE == kWgrad ? p.N - (int64_t)t.mt * BM : (int64_t)t.rows);
+  const int col_lim = (int)min((int64_t)BN, nout - (int64_t)t.nt * BN);
   const int64_t out_row0 = MODE == kWgrad ? (int64_t)t.g * p.N + (int64_t)t.mt * BM : t.row0;
-  // 32x32 accumulator: lane l holds column l%32 and rows 8(r/4) + 4(l/32) + r%4;
-  // 16x16 accumulator: lane l holds column l%16 and rows 4(l/16) + r
-  const int lr0 = FEED == kFeedPrecise ? WM * wm + 4 * (lane >> 5) : WM * wm + 4 * (lane >> 4);
-  const int lc0 = FEED == kFeedPrecise ? WN * wn + (lane & 31) : WN * wn + (lane & 15);
-  const int64_t base = (out_row0 + lr0) * nout + (int64_t)t.nt * BN + lc0;
   constexpr int FI = FEED == kFeedPrecise ? 32 : 16;     // fragment rows / columns
+  const int lrow = WM * wm + lane % FI;
+  const int lcol = WN * wn + 4 * (lane / FI);
+  const int64_t base = (out_row0 + lrow) * nout + (int64_t)t.nt * BN + lcol;
 #pragma unroll
-  for (int i = 0; i < NI; ++i)
+  for (int i = 0; i < NI; ++i) {
+    if (lrow + FI * i >= row_lim) continue;
+    const int64_t rbase = base + (int64_t)(FI * i) * nout;
 #pragma unroll
-    for (int r = 0; r < NR; ++r) {
-      const int ro = FI * i + (FEED == kFeedPrecise ? 8 * (r >> 2) + (r & 3) : r);   // uniform
-      if (lr0 + ro >= row_lim) continue;
-      const int64_t rbase = base + (int64_t)ro * nout;
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        if (lc0 + FI * j >= col_lim) continue;
-        const int64_t idx = rbase + FI * j;
-        const float v = acc[i][j][r];
-        if (p.out_bf16) ((uint16_t*)p.out)[idx] = (uint16_t)f32_to_bf16_bits(v);
-        else ((float*)p.out)[idx] = v;
+      for (int q = 0; q < NR / 4; ++q) {
+        const int co = FI * j + 8 * q;                     // 32x32: register group q covers columns 8q + 4h .. + 3
+        if (lcol + co >= col_lim) continue;
+        const int64_t idx = rbase + co;
+        const float v0 = acc[i][j][4 * q], v1 = acc[i][j][4 * q + 1];
+        const float v2 = acc[i][j][4 * q + 2], v3 = acc[i][j][4 * q + 3];
+        if (p.out_bf16) {
+          const uint2 w = make_uint2(f32_to_bf16_bits(v0) | (f32_to_bf16_bits(v1) << 16),
+                                     f32_to_bf16_bits(v2) | (f32_to_bf16_bits(v3) << 16));
+          *(uint2*)((uint16_t*)p.out + idx) = w;
+        } else {
+          *(float4*)((float*)p.out + idx) = make_float4(v0, v1, v2, v3);
+        }
       }
-    }
+  }
 }
 
 template <int MODE, int FEED, bool SDW>
