@@ -265,10 +265,12 @@ def blockwise_leg(m, torch, steps=5, sample_rows=256):
         bq = {}
         ops_bw = [
             Op("quant_x", "quant", lambda: bq.update(x=m.fp8bw_quantize_act_1x128(x)), M * K * QUANT_BYTES_PER_ELEM, ""),
-            Op("quant_w", "quant", lambda: bq.update(w=m.fp8bw_quantize_weight_128x128(w)), G * N * K * QUANT_BYTES_PER_ELEM, ""),
-            Op("fwd", "gemm", lambda: bq.update(y=m.fp8bw_grouped_gemm_fwd(*bq["x"], *bq["w"], offs, N, "f32")), f, ""),
+            Op("quant_w", "quant", lambda: bq.update(w=m.fp8bw_quantize_weight_128x128(w, transposed=True)),
+               G * N * K * (QUANT_BYTES_PER_ELEM + 1), ""),
+            Op("fwd", "gemm", lambda: bq.update(y=m.fp8bw_grouped_gemm_fwd(*bq["x"], *bq["w"][:2], offs, N, "f32")), f, ""),
             Op("quant_dy", "quant", lambda: bq.update(dy=m.fp8bw_quantize_act_1x128(dy)), M * N * QUANT_BYTES_PER_ELEM, ""),
-            Op("dgrad", "gemm", lambda: bq.update(dx=m.fp8bw_grouped_gemm_dgrad(*bq["dy"], *bq["w"], offs, K, "f32")), f, ""),
+            Op("dgrad", "gemm", lambda: bq.update(dx=m.fp8bw_grouped_gemm_dgrad(*bq["dy"], bq["w"][2], bq["w"][1], offs, K,
+                                                                                 "f32")), f, ""),
         ]
         mq = {}
         ld = G * N

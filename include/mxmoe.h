@@ -152,9 +152,11 @@ mxmoe_status fp8bw_quantize_act_1x128(const void* x_bf16, int64_t R, int64_t C,
                                       uint8_t* q, float* s, void* stream);
 
 /* fp8bw_quantize_weight_128x128: w bf16 [R, C] (R = G*N) -> q [R, C],
- * s f32 [R/128, C/128] (amax over each 128x128 block).  R % 128 == 0, C % 128 == 0. */
+ * s f32 [R/128, C/128] (amax over each 128x128 block).  R % 128 == 0, C % 128 == 0.
+ * qT, if not NULL, also receives the codes transposed, qT [C, R] (qT[c, r] = q[r, c]): the weight
+ * operand of fp8bw_grouped_gemm_dgrad, which contracts over the rows of W (same block scales). */
 mxmoe_status fp8bw_quantize_weight_128x128(const void* w_bf16, int64_t R, int64_t C,
-                                           uint8_t* q, float* s, void* stream);
+                                           uint8_t* q, float* s, uint8_t* qT, void* stream);
 
 /* fp8bw_grouped_gemm_fwd: Y[r, n] = sum_kb sx[r, kb] sw[(gN+n)/128, kb] *
  *                                   sum_{k in kb} qx[r, k] qw[gN+n, k]
@@ -167,11 +169,12 @@ mxmoe_status fp8bw_grouped_gemm_fwd(const uint8_t* qx, const float* sx,
                                     void* y, mxmoe_dtype ydt, void* stream);
 
 /* fp8bw_grouped_gemm_dgrad: dX[r, k] = sum_nb sdy[r, nb] sw[gN/128 + nb, k/128] *
- *                                      sum_{n in nb} qdy[r, n] qw[gN+n, k]
- * qdy/sdy from fp8bw_quantize_act_1x128(dY [M, N]) (1x128 along N); qw/sw are
- * the forward weight operands, read transposed.  dx [M, K]. */
+ *                                      sum_{n in nb} qdy[r, n] qwT[k, gN+n]
+ * qdy/sdy from fp8bw_quantize_act_1x128(dY [M, N]) (1x128 along N); qwT [K, G*N] is the transposed
+ * weight copy from fp8bw_quantize_weight_128x128 and sw its (forward-layout) block scales: the
+ * 128x128 weight blocks of the forward pass, read transposed.  dx [M, K]. */
 mxmoe_status fp8bw_grouped_gemm_dgrad(const uint8_t* qdy, const float* sdy,
-                                      const uint8_t* qw, const float* sw,
+                                      const uint8_t* qwT, const float* sw,
                                       const int32_t* offs, int32_t G, int64_t M, int64_t N, int64_t K,
                                       void* dx, mxmoe_dtype dxdt, void* stream);
 

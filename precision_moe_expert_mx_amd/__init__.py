@@ -45,7 +45,7 @@ _SIGS = {
     "mx_grouped_gemm_dgrad": (ctypes.c_int, [_p, _p, _p, _p, _i64, _p, _i32, _i64, _i64, _i64, _p, ctypes.c_int, _p]),
     "mx_grouped_gemm_wgrad": (ctypes.c_int, [_p, _p, _p, _p, _i64, _p, _i32, _i64, _i64, _i64, _p, ctypes.c_int, _p]),
     "fp8bw_quantize_act_1x128": (ctypes.c_int, [_p, _i64, _i64, _p, _p, _p]),
-    "fp8bw_quantize_weight_128x128": (ctypes.c_int, [_p, _i64, _i64, _p, _p, _p]),
+    "fp8bw_quantize_weight_128x128": (ctypes.c_int, [_p, _i64, _i64, _p, _p, _p, _p]),
     "fp8bw_grouped_gemm_fwd": (ctypes.c_int, [_p, _p, _p, _p, _p, _i32, _i64, _i64, _i64, _p, ctypes.c_int, _p]),
     "fp8bw_grouped_gemm_dgrad": (ctypes.c_int, [_p, _p, _p, _p, _p, _i32, _i64, _i64, _i64, _p, ctypes.c_int, _p]),
     "mxmoe_check_offsets": (ctypes.c_int, [_p, _i32, _i64, _p]),
@@ -214,15 +214,19 @@ def fp8bw_quantize_act_1x128(x, q=None, s=None, stream=None):
     return q, s
 
 
-def fp8bw_quantize_weight_128x128(w, q=None, s=None, stream=None):
+def fp8bw_quantize_weight_128x128(w, q=None, s=None, qT=None, transposed: bool = False, stream=None):
+    """w bf16 [R, C] -> (q [R, C], s f32 [R/128, C/128]) or, with transposed=True (or qT given),
+    (q, s, qT [C, R]) where qT is the dgrad operand."""
     torch = _torch()
     w = _bf16_bits(w)
     R, C = w.shape
     q = _empty((R, C), torch.uint8, w) if q is None else q
     s = _empty((R // 128, C // 128), torch.float32, w) if s is None else s
+    if transposed and qT is None:
+        qT = _empty((C, R), torch.uint8, w)
     _check("fp8bw_quantize_weight_128x128", lib().fp8bw_quantize_weight_128x128(_ptr(w), R, C, _ptr(q), _ptr(s),
-                                                                                _stream_handle(stream)))
-    return q, s
+                                                                                _ptr(qT), _stream_handle(stream)))
+    return (q, s) if qT is None else (q, s, qT)
 
 
 def fp8bw_grouped_gemm_fwd(qx, sx, qw, sw, offs, N: int, out_dtype: str = "f32", y=None, stream=None, fast: bool = False):
@@ -235,12 +239,14 @@ def fp8bw_grouped_gemm_fwd(qx, sx, qw, sw, offs, N: int, out_dtype: str = "f32",
     return y
 
 
-def fp8bw_grouped_gemm_dgrad(qdy, sdy, qw, sw, offs, K: int, out_dtype: str = "f32", dx=None, stream=None, fast: bool = False):
+def fp8bw_grouped_gemm_dgrad(qdy, sdy, qwT, sw, offs, K: int, out_dtype: str = "f32", dx=None, stream=None,
+                             fast: bool = False):
+    """dX [M, K] from blockwise dY (1x128 along N) and the transposed weight copy qwT [K, G*N]."""
     M, N = qdy.shape
     G = offs.numel() - 1
     tdt, cdt = _out_dtype(out_dtype, fast)
     dx = _empty((M, K), tdt, qdy) if dx is None else dx
-    _check("fp8bw_grouped_gemm_dgrad", lib().fp8bw_grouped_gemm_dgrad(_ptr(qdy), _ptr(sdy), _ptr(qw), _ptr(sw),
+    _check("fp8bw_grouped_gemm_dgrad", lib().fp8bw_grouped_gemm_dgrad(_ptr(qdy), _ptr(sdy), _ptr(qwT), _ptr(sw),
                                                                       _ptr(offs), G, M, N, K, _ptr(dx), cdt,
                                                                       _stream_handle(stream)))
     return dx

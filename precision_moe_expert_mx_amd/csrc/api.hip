@@ -198,7 +198,8 @@ mxmoe_status fp8bw_quantize_act_1x128(const void* x, int64_t R, int64_t C, uint8
   return launched(launch_bw_act((const uint16_t*)x, R, C, q, s, (hipStream_t)stream), fn);
 }
 
-mxmoe_status fp8bw_quantize_weight_128x128(const void* w, int64_t R, int64_t C, uint8_t* q, float* s, void* stream) {
+mxmoe_status fp8bw_quantize_weight_128x128(const void* w, int64_t R, int64_t C, uint8_t* q, float* s, uint8_t* qT,
+                                           void* stream) {
   const char* fn = "fp8bw_quantize_weight_128x128";
   if (R < 0 || C <= 0 || R % 128 || C % 128)
     return fail(MXMOE_ERR_SHAPE, "%s: need R %% 128 == 0, C > 0, C %% 128 == 0", fn);
@@ -207,8 +208,9 @@ mxmoe_status fp8bw_quantize_weight_128x128(const void* w, int64_t R, int64_t C, 
   TRY(check_ptr(fn, "w", w, 16));
   TRY(check_ptr(fn, "q", q, 16));
   TRY(check_ptr(fn, "s", s, 4));
+  if (qT) TRY(check_ptr(fn, "qT", qT, 16));
   TRY(check_device());
-  return launched(launch_bw_weight((const uint16_t*)w, R, C, q, s, (hipStream_t)stream), fn);
+  return launched(launch_bw_weight((const uint16_t*)w, R, C, q, s, qT, (hipStream_t)stream), fn);
 }
 
 static mxmoe_status bw_gemm_common(int mode, const char* fn, const uint8_t* a, const float* sa, const uint8_t* b,
@@ -228,7 +230,8 @@ static mxmoe_status bw_gemm_common(int mode, const char* fn, const uint8_t* a, c
   if (mode == kFwd) {
     p.lda = K; p.ldsa = K / 128; p.ldb = K; p.ldsb = K / 128;
   } else {
-    p.lda = N; p.ldsa = N / 128; p.ldb = K; p.ldsb = K / 128;
+    // dgrad: B is the transposed weight copy [K, G*N]; scales keep the forward layout
+    p.lda = N; p.ldsa = N / 128; p.ldb = (int64_t)G * N; p.ldsb = K / 128;
   }
   if (M == 0) return ok();
   TRY(check_device());
@@ -241,10 +244,10 @@ mxmoe_status fp8bw_grouped_gemm_fwd(const uint8_t* qx, const float* sx, const ui
   return bw_gemm_common(kFwd, "fp8bw_grouped_gemm_fwd", qx, sx, qw, sw, offs, G, M, N, K, y, (int)ydt, stream);
 }
 
-mxmoe_status fp8bw_grouped_gemm_dgrad(const uint8_t* qdy, const float* sdy, const uint8_t* qw, const float* sw,
+mxmoe_status fp8bw_grouped_gemm_dgrad(const uint8_t* qdy, const float* sdy, const uint8_t* qwT, const float* sw,
                                       const int32_t* offs, int32_t G, int64_t M, int64_t N, int64_t K, void* dx,
                                       mxmoe_dtype dxdt, void* stream) {
-  return bw_gemm_common(kDgrad, "fp8bw_grouped_gemm_dgrad", qdy, sdy, qw, sw, offs, G, M, N, K, dx, (int)dxdt,
+  return bw_gemm_common(kDgrad, "fp8bw_grouped_gemm_dgrad", qdy, sdy, qwT, sw, offs, G, M, N, K, dx, (int)dxdt,
                         stream);
 }
 

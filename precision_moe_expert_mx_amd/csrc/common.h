@@ -78,7 +78,8 @@ hipError_t launch_mx_rowwise(const uint16_t* x, int64_t R, int64_t C, uint8_t* q
 hipError_t launch_mx_colwise(const uint16_t* x, int64_t R, int64_t C, const int32_t* offs, int32_t G,
                              uint8_t* qT, uint8_t* sT, int64_t ld, hipStream_t st);
 hipError_t launch_bw_act(const uint16_t* x, int64_t R, int64_t C, uint8_t* q, float* s, hipStream_t st);
-hipError_t launch_bw_weight(const uint16_t* w, int64_t R, int64_t C, uint8_t* q, float* s, hipStream_t st);
+hipError_t launch_bw_weight(const uint16_t* w, int64_t R, int64_t C, uint8_t* q, float* s, uint8_t* qT,
+                            hipStream_t st);
 
 enum GemmMode { kFwd = 0, kDgrad = 1, kWgrad = 2 };
 

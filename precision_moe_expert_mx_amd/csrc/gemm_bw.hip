@@ -143,8 +143,6 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const TileInfo& ti,
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  // blockwise dgrad reads the forward weight operand [G*N, K] transposed (rows = n, columns = k)
-  constexpr bool BT = BW && MODE == kDgrad;
 
   // ---- per-tile operand geometry ------------------------------------------------------------
   // A rows: forward/dgrad -> token rows (clamped to the expert's last row); wgrad -> n rows
@@ -177,14 +175,10 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const TileInfo& ti,
     if (MODE == kWgrad) arow = (int64_t)ti.mt * BM + r;
     else arow = ti.row0 + (r < ti.rows ? r : ti.rows - 1);
     a_ptr[j] = p.a + arow * p.lda + a_col0 + ld_ch * 16;
-    if (BT) {
-      b_ptr[j] = p.b + ((int64_t)ti.g * p.N + r) * p.ldb + (int64_t)ti.nt * BN + ld_ch * 16;
-    } else {
-      int64_t brow;
-      if (MODE == kFwd) brow = (int64_t)ti.g * p.N + (int64_t)ti.nt * BN + r;
-      else brow = (int64_t)ti.nt * BN + r;
-      b_ptr[j] = p.b + brow * p.ldb + b_col0 + ld_ch * 16;
-    }
+    int64_t brow;
+    if (MODE == kFwd) brow = (int64_t)ti.g * p.N + (int64_t)ti.nt * BN + r;
+    else brow = (int64_t)ti.nt * BN + r;
+    b_ptr[j] = p.b + brow * p.ldb + b_col0 + ld_ch * 16;
   }
   // scale rows: threads 0..127 -> A row tid, 128..255 -> B row tid-128
   const bool s_is_a = tid < 128;
@@ -210,7 +204,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const TileInfo& ti,
       bool ok = true;
       if (MODE == kWgrad) ok = (koff + ld_ch * 16) < L;     // chunk inside the expert's blocks
       ra[j] = ok ? *(const uint4*)(a_ptr[j] + koff) : make_uint4(0, 0, 0, 0);
-      rb[j] = ok ? *(const uint4*)(b_ptr[j] + (BT ? koff * p.ldb : koff)) : make_uint4(0, 0, 0, 0);
+      rb[j] = ok ? *(const uint4*)(b_ptr[j] + koff) : make_uint4(0, 0, 0, 0);
     }
     if (BW) {
       const float* sp = (const float*)(s_is_a ? p.sa : p.sb);
@@ -232,15 +226,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const TileInfo& ti,
     for (int j = 0; j < 4; ++j) {
       int r = ld_row + 32 * j;
       *(uint4*)(ldsA + lds_off(r, ld_ch)) = ra[j];
-      if (BT) {
-        // byte i of the chunk is element (n = r, k = 16 ld_ch + i): store it at row k, column n
-        const uint32_t w4[4] = {rb[j].x, rb[j].y, rb[j].z, rb[j].w};
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          ldsB[lds_off(16 * ld_ch + i, r >> 4) + (r & 15)] = (uint8_t)(w4[i >> 2] >> (8 * (i & 3)));
-      } else {
-        *(uint4*)(ldsB + lds_off(r, ld_ch)) = rb[j];
-      }
+      *(uint4*)(ldsB + lds_off(r, ld_ch)) = rb[j];
     }
     if (s_is_a) ldsSA[s_r] = rs;
     else if (!BW) ldsSB[s_r] = rs;

@@ -53,10 +53,16 @@ __global__ __launch_bounds__(256) void bw_act_kernel(const uint4* __restrict__ x
 }
 
 // 128x128 weight blocks: one workgroup of 256 lanes per block; lane t owns rows (t/16) + 16 i,
-// 16-byte column chunk t%16, i = 0..7 (64 values in registers), amax reduced through LDS.
-__global__ __launch_bounds__(256) void bw_weight_kernel(const uint16_t* __restrict__ w, int64_t C,
-                                                        uint8_t* __restrict__ q, float* __restrict__ s) {
+// 16-byte column chunk t%16, i = 0..7 (64 values in registers), amax reduced through LDS.  When qT is
+// given, the block's codes also go through an LDS tile and out transposed (qT [C, R], 128-byte rows),
+// the operand layout of the dgrad GEMM, which contracts over the rows.
+constexpr int kBwTPitch = 128 + 16;     // LDS bytes per transposed row (padded against bank conflicts)
+
+__global__ __launch_bounds__(256) void bw_weight_kernel(const uint16_t* __restrict__ w, int64_t R, int64_t C,
+                                                        uint8_t* __restrict__ q, float* __restrict__ s,
+                                                        uint8_t* __restrict__ qT) {
   __shared__ uint32_t red[4];
+  __shared__ __attribute__((aligned(16))) uint8_t tile[128 * kBwTPitch];
   const int64_t br = blockIdx.y, bcn = blockIdx.x;
   const int t = threadIdx.x;
   const int r = t >> 4, ch = t & 15;
@@ -76,10 +82,29 @@ __global__ __launch_bounds__(256) void bw_weight_kernel(const uint16_t* __restri
   float sc = bw_scale_from_amax_bits(m);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    int64_t row = br * 128 + r + 16 * i;
-    *(uint2*)(q + row * C + bcn * 128 + ch * 8) = bw_convert8(v[i], sc);
+    const int rr = r + 16 * i;
+    const int64_t row = br * 128 + rr;
+    const uint2 o = bw_convert8(v[i], sc);
+    *(uint2*)(q + row * C + bcn * 128 + ch * 8) = o;
+    if (qT) {
+      // element (row rr, column 8 ch + b) of the block goes to transposed row 8 ch + b, column rr
+      const uint32_t wd[2] = {o.x, o.y};
+#pragma unroll
+      for (int b = 0; b < 8; ++b) tile[(8 * ch + b) * kBwTPitch + rr] = (uint8_t)(wd[b >> 2] >> (8 * (b & 3)));
+    }
   }
   if (t == 0) s[br * (C / 128) + bcn] = sc;
+  if (qT) {
+    __syncthreads();
+    // transposed row k (= block column) holds the block's 128 rows: 8 lanes x 16 bytes per row
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int idx = it * 256 + t;
+      const int k = idx >> 3, piece = idx & 7;
+      const uint4 val = *(const uint4*)(tile + k * kBwTPitch + 16 * piece);
+      *(uint4*)(qT + (bcn * 128 + k) * R + br * 128 + 16 * piece) = val;
+    }
+  }
 }
 
 hipError_t launch_bw_act(const uint16_t* x, int64_t R, int64_t C, uint8_t* q, float* s, hipStream_t st) {
@@ -90,9 +115,10 @@ hipError_t launch_bw_act(const uint16_t* x, int64_t R, int64_t C, uint8_t* q, fl
   return hipGetLastError();
 }
 
-hipError_t launch_bw_weight(const uint16_t* w, int64_t R, int64_t C, uint8_t* q, float* s, hipStream_t st) {
+hipError_t launch_bw_weight(const uint16_t* w, int64_t R, int64_t C, uint8_t* q, float* s, uint8_t* qT, hipStream_t st) {
   if (R == 0 || C == 0) return hipSuccess;
-  hipLaunchKernelGGL(bw_weight_kernel, dim3((unsigned)(C / 128), (unsigned)(R / 128)), dim3(256), 0, st, w, C, q, s);
+  hipLaunchKernelGGL(bw_weight_kernel, dim3((unsigned)(C / 128), (unsigned)(R / 128)), dim3(256), 0, st, w, R, C, q, s,
+                     qT);
   return hipGetLastError();
 }
 

@@ -68,7 +68,8 @@ def test_quantiser_argument_errors():
     assert _status(L, "mx_quantize_colwise", A16, 100, 64, None, 0, None, A16, 128, None)[0] == 1
     # blockwise
     assert _status(L, "fp8bw_quantize_act_1x128", A16, 4, 96, A16, A16, None)[0] == 2
-    assert _status(L, "fp8bw_quantize_weight_128x128", A16, 100, 128, A16, A16, None)[0] == 2
+    assert _status(L, "fp8bw_quantize_weight_128x128", A16, 100, 128, A16, A16, None, None)[0] == 2
+    assert _status(L, "fp8bw_quantize_weight_128x128", A16, 128, 128, A16, A16, BAD, None)[0] == 3
 
 
 def test_gemm_argument_errors():

@@ -195,12 +195,12 @@ def test_blockwise_gemms():
         L = _rand_layer(rng, sizes, N, K, w_std=0.02, outliers=0.001)
         offs = dev(L.offs)
         qx, sx = m.fp8bw_quantize_act_1x128(dev(L.x))
-        qw, sw = m.fp8bw_quantize_weight_128x128(dev(L.w))
+        qw, sw, qwT = m.fp8bw_quantize_weight_128x128(dev(L.w), transposed=True)
         y = m.fp8bw_grouped_gemm_fwd(qx, sx, qw, sw, offs, N)
         ref, bnd = oracle.bw_gemm_fwd(host(qx), host(sx), host(qw), host(sw), L.offs, N)
         print("bw fwd", _check(_gpu_out(y), ref, bnd, "f32", "bw fwd"))
         qd, sd = m.fp8bw_quantize_act_1x128(dev(L.dy))
-        dx = m.fp8bw_grouped_gemm_dgrad(qd, sd, qw, sw, offs, K)
+        dx = m.fp8bw_grouped_gemm_dgrad(qd, sd, qwT, sw, offs, K)
         ref, bnd = oracle.bw_gemm_dgrad(host(qd), host(sd), host(qw), host(sw), L.offs, N, K)
         print("bw dgrad", _check(_gpu_out(dx), ref, bnd, "f32", "bw dgrad"))
 
@@ -214,13 +214,13 @@ def test_blockwise_full_size_sampled():
         offs_d = dev(lay.offs)
         rows = np.unique(rng.choice(lay.M, 64, replace=False))
         qx, sx = m.fp8bw_quantize_act_1x128(dev(lay.x))
-        qw, sw = m.fp8bw_quantize_weight_128x128(dev(lay.w.reshape(-1, lay.K)))
+        qw, sw, qwT = m.fp8bw_quantize_weight_128x128(dev(lay.w.reshape(-1, lay.K)), transposed=True)
         y = m.fp8bw_grouped_gemm_fwd(qx, sx, qw, sw, offs_d, lay.N)
         hqw, hsw = host(qw), host(sw)
         ref, bnd = oracle.bw_gemm_fwd(host(qx), host(sx), hqw, hsw, lay.offs, lay.N, rows=rows)
         print(lay.name, "bw fwd", _check(_gpu_out(y)[rows], ref, bnd, "f32", "bw fwd"))
         qd, sd = m.fp8bw_quantize_act_1x128(dev(lay.dy))
-        dx = m.fp8bw_grouped_gemm_dgrad(qd, sd, qw, sw, offs_d, lay.K)
+        dx = m.fp8bw_grouped_gemm_dgrad(qd, sd, qwT, sw, offs_d, lay.K)
         ref, bnd = oracle.bw_gemm_dgrad(host(qd), host(sd), hqw, hsw, lay.offs, lay.N, lay.K, rows=rows)
         print(lay.name, "bw dgrad", _check(_gpu_out(dx)[rows], ref, bnd, "f32", "bw dgrad"))
         torch.cuda.empty_cache()

@@ -124,6 +124,10 @@ def test_blockwise_quantisers():
         qo, so = oracle.bw_quantize_weight_128x128(w)
         assert np.array_equal(host(s), so)
         assert np.array_equal(host(q), qo)
+        # with the transposed copy: same codes and scales, plus qT == q^T
+        q2, s2, qT = m.fp8bw_quantize_weight_128x128(dev(w), transposed=True)
+        assert np.array_equal(host(s2), so) and np.array_equal(host(q2), qo)
+        assert np.array_equal(host(qT), qo.T)
 
 
 def test_quantisers_full_size_sampled():
