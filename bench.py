@@ -36,6 +36,7 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "mxfp8": 5000.0}
 QUANT_BYTES_PER_ELEM = 2.0 + 1.0 + 1.0 / 32.0   # bf16 in, E4M3 out, one E8M0 per 32
+DUAL_BYTES_PER_ELEM = 2.0 + 2.0 * (1.0 + 1.0 / 32.0)   # bf16 in once, both MX layouts out
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_traffic_dsv3_671b_shard.txt")
 GEMM_SOURCES = [os.path.join(ROOT, "precision_moe_expert_mx_amd", "csrc", f) for f in ("gemm_mx.hip", "common.h")]
 
@@ -61,8 +62,11 @@ class Op:
         self.ms = []
 
 
-def build_layer_ops(m, torch, lay, dev_in, fast=False):
-    """Allocate the layer's device buffers and return its ops in step order."""
+def build_layer_ops(m, torch, lay, dev_in, fast=False, fused=True):
+    """Allocate the layer's device buffers and return its ops in step order.
+
+    fused: X, W and dY each get both MX layouts from one dual-layout launch (3 quantiser launches
+    per layer); otherwise six separate row-wise / column-wise launches."""
     G, M, N, K = lay.G, lay.M, lay.N, lay.K
     x, w, dy, offs = dev_in
     d = x.device
@@ -85,28 +89,48 @@ def build_layer_ops(m, torch, lay, dev_in, fast=False):
     mxb = 1.0 + 1.0 / 32.0          # E4M3 byte plus its share of an E8M0 scale
     gemm_bytes = {"fwd": (M * K + G * N * K) * mxb + M * N * 2, "dgrad": (M * N + G * N * K) * mxb + M * K * 2,
                   "wgrad": (M * N + M * K) * mxb + G * N * K * 4}
-    ops = [
-        Op(f"{n}.quant_x_row", "quant", lambda: m.mx_quantize_rowwise(x, b["qx"], b["sx"]),
-           M * K * QUANT_BYTES_PER_ELEM, "mx_rowwise_kernel"),
-        Op(f"{n}.quant_w_row", "quant", lambda: m.mx_quantize_rowwise(w2, b["qw"], b["sw"]),
-           G * N * K * QUANT_BYTES_PER_ELEM, "mx_rowwise_kernel"),
-        Op(f"{n}.fwd", "gemm", lambda: m.mx_grouped_gemm_fwd(b["qx"], b["sx"], b["qw"], b["sw"], offs, N, "bf16",
-                                                             y=b["y"], fast=fast), f, "grouped_gemm fwd"),
-        Op(f"{n}.quant_dy_row", "quant", lambda: m.mx_quantize_rowwise(dy, b["qdy"], b["sdy"]),
-           M * N * QUANT_BYTES_PER_ELEM, "mx_rowwise_kernel"),
-        Op(f"{n}.quant_w_col", "quant", lambda: m.mx_quantize_colwise(w2, None, ld=G * N, qT=b["qwT"], sT=b["swT"]),
-           G * N * K * QUANT_BYTES_PER_ELEM, "mx_colwise_kernel"),
-        Op(f"{n}.dgrad", "gemm", lambda: m.mx_grouped_gemm_dgrad(b["qdy"], b["sdy"], b["qwT"], b["swT"], offs, K,
-                                                                 "bf16", dx=b["dx"], fast=fast), f,
-           "grouped_gemm dgrad"),
-        Op(f"{n}.quant_dy_col", "quant", lambda: m.mx_quantize_colwise(dy, offs, ld=ld, qT=b["qdyT"], sT=b["sdyT"]),
-           M * N * QUANT_BYTES_PER_ELEM, "mx_colwise_kernel"),
-        Op(f"{n}.quant_x_col", "quant", lambda: m.mx_quantize_colwise(x, offs, ld=ld, qT=b["qxT"], sT=b["sxT"]),
-           M * K * QUANT_BYTES_PER_ELEM, "mx_colwise_kernel"),
-        Op(f"{n}.wgrad", "gemm", lambda: m.mx_grouped_gemm_wgrad(b["qdyT"], b["sdyT"], b["qxT"], b["sxT"], offs, M,
-                                                                 "f32", dw=b["dw"], fast=fast), f,
-           "grouped_gemm wgrad"),
-    ]
+    fwd = Op(f"{n}.fwd", "gemm", lambda: m.mx_grouped_gemm_fwd(b["qx"], b["sx"], b["qw"], b["sw"], offs, N, "bf16",
+                                                              y=b["y"], fast=fast), f, "grouped_gemm fwd")
+    dgrad = Op(f"{n}.dgrad", "gemm", lambda: m.mx_grouped_gemm_dgrad(b["qdy"], b["sdy"], b["qwT"], b["swT"], offs, K,
+                                                                      "bf16", dx=b["dx"], fast=fast), f,
+               "grouped_gemm dgrad")
+    wgrad = Op(f"{n}.wgrad", "gemm", lambda: m.mx_grouped_gemm_wgrad(b["qdyT"], b["sdyT"], b["qxT"], b["sxT"], offs, M,
+                                                                      "f32", dw=b["dw"], fast=fast), f,
+               "grouped_gemm wgrad")
+    if fused:
+        ops = [
+            Op(f"{n}.quant_x_dual", "quant",
+               lambda: m.mx_quantize_dual(x, offs, ld=ld, q=b["qx"], s=b["sx"], qT=b["qxT"], sT=b["sxT"]),
+               M * K * DUAL_BYTES_PER_ELEM, "mx_colwise_kernel<true, false>"),
+            Op(f"{n}.quant_w_dual", "quant",
+               lambda: m.mx_quantize_dual(w2, None, ld=G * N, q=b["qw"], s=b["sw"], qT=b["qwT"], sT=b["swT"]),
+               G * N * K * DUAL_BYTES_PER_ELEM, "mx_colwise_kernel<true, false>"),
+            fwd,
+            Op(f"{n}.quant_dy_dual", "quant",
+               lambda: m.mx_quantize_dual(dy, offs, ld=ld, q=b["qdy"], s=b["sdy"], qT=b["qdyT"], sT=b["sdyT"]),
+               M * N * DUAL_BYTES_PER_ELEM, "mx_colwise_kernel<true, false>"),
+            dgrad,
+            wgrad,
+        ]
+    else:
+        ops = [
+            Op(f"{n}.quant_x_row", "quant", lambda: m.mx_quantize_rowwise(x, b["qx"], b["sx"]),
+               M * K * QUANT_BYTES_PER_ELEM, "mx_rowwise_kernel"),
+            Op(f"{n}.quant_w_row", "quant", lambda: m.mx_quantize_rowwise(w2, b["qw"], b["sw"]),
+               G * N * K * QUANT_BYTES_PER_ELEM, "mx_rowwise_kernel"),
+            fwd,
+            Op(f"{n}.quant_dy_row", "quant", lambda: m.mx_quantize_rowwise(dy, b["qdy"], b["sdy"]),
+               M * N * QUANT_BYTES_PER_ELEM, "mx_rowwise_kernel"),
+            Op(f"{n}.quant_w_col", "quant",
+               lambda: m.mx_quantize_colwise(w2, None, ld=G * N, qT=b["qwT"], sT=b["swT"]),
+               G * N * K * QUANT_BYTES_PER_ELEM, "mx_colwise_kernel<false, false>"),
+            dgrad,
+            Op(f"{n}.quant_dy_col", "quant", lambda: m.mx_quantize_colwise(dy, offs, ld=ld, qT=b["qdyT"], sT=b["sdyT"]),
+               M * N * QUANT_BYTES_PER_ELEM, "mx_colwise_kernel<false, false>"),
+            Op(f"{n}.quant_x_col", "quant", lambda: m.mx_quantize_colwise(x, offs, ld=ld, qT=b["qxT"], sT=b["sxT"]),
+               M * K * QUANT_BYTES_PER_ELEM, "mx_colwise_kernel<false, false>"),
+            wgrad,
+        ]
     for op in ops:
         if op.kind == "gemm":
             op.bytes = gemm_bytes[op.name.split(".")[1]]
@@ -355,6 +379,14 @@ def main():
     cal2 = torch.empty_like(cal)
     cal2.copy_(cal)
     torch.cuda.synchronize()
+    # its rate (1 GiB read + 1 GiB written) is the practical HBM ceiling the quantisers are compared to
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        cal2.copy_(cal)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_gbps = 2 * 5 * (1 << 30) / (e0.elapsed_time(e1) * 1e-3) / 1e9
     del cal, cal2
 
     ops = []
@@ -390,7 +422,7 @@ def main():
                 "avg_launch_ms": round(dom_ms, 4),
                 "frac_of_mxfp8_peak": round(achieved / MFMA_PEAK_TFLOPS["mxfp8"], 4)}
 
-    extra = {}
+    extra = {"device_copy_gbps": round(copy_gbps, 1), "quant_frac_of_copy": round(quant_bytes / (quant_ms * 1e-3) / 1e9 / copy_gbps, 3)}
     if not args.no_extra_legs:
         # the same GEMMs on the full-rate block-scaled FP8 MFMA, whose sums are truncated per run of
         # 8 products: reported beside the headline, never as it
@@ -408,6 +440,19 @@ def main():
         fms = sum(float(np.mean(op.ms)) for op in g_ops)
         extra["fp8_feed_gemm_tflops"] = round(gemm_flops / (fms * 1e-3) / 1e12, 1)
         del fops, flat, g_ops
+        torch.cuda.empty_cache()
+        # the six separate row-wise / column-wise launches per layer that the dual-layout launches
+        # replace (same outputs)
+        sops = []
+        for lay, (dev_in, _) in zip(wl.layers, keep):
+            lops, bufs = build_layer_ops(m, torch, lay, dev_in, fused=False)
+            sops.append((lops, bufs))
+        q_ops = [op for lops, _ in sops for op in lops if op.kind == "quant"]
+        time_ops(torch, q_ops, 5, 1)
+        sep_ms = sum(float(np.mean(op.ms)) for op in q_ops)
+        extra["separate_quantisers"] = {"ms_per_step": round(sep_ms, 4), "dual_ms_per_step": round(quant_ms, 4),
+                                        "ops": {op.name: op_summary(op) for op in q_ops}}
+        del sops, q_ops
         torch.cuda.empty_cache()
         del keep, ops
         torch.cuda.empty_cache()
@@ -435,7 +480,7 @@ def main():
         "config": {"workload": wname, "experts": wl.layers[0].G, "routed_rows": wl.layers[0].M,
                    "group_sizes": [int(s) for s in wl.layers[0].sizes],
                    "layers": {l.name: {"N": l.N, "K": l.K} for l in wl.layers},
-                   "step": "per layer: 6 MX quantisers + grouped GEMM fwd/dgrad/wgrad"},
+                   "step": "per layer: X, W, dY each quantised to both MX layouts in one launch + grouped GEMM fwd/dgrad/wgrad"},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "gemm_only_tflops": round(gemm_flops / (gemm_ms * 1e-3) / 1e12, 1),

@@ -98,6 +98,25 @@ mxmoe_status mx_quantize_colwise(const void* x_bf16, int64_t R, int64_t C,
                                  const int32_t* offs, int32_t G,
                                  uint8_t* qT, uint8_t* sT, int64_t ld, void* stream);
 
+/* mx_quantize_dual: both layouts of one tensor from a single read of it (the
+ * input side of a layer's forward and backward needs X, dY and W both
+ * row-wise and column-wise; one pass moves 2 + 2 + 2/32 bytes per element
+ * instead of 2 * (2 + 1 + 1/32)).  Results are byte-identical to
+ * mx_quantize_rowwise(x') into q [R, C] / s [R, C/32] plus
+ * mx_quantize_colwise(x', offs, G, ld) into qT / sT, where x' [R, C] is:
+ *   - row_idx == NULL: x itself (R_src ignored);
+ *   - otherwise the routed rows x'[r] = x[row_idx[r]] of x [R_src, C] (the
+ *     token permute of a dropless MoE layer folded into the quantiser; indices
+ *     are read on the device and clamped into [0, R_src)).
+ * With offs, every row in [0, offs[G]) is written row-wise; offs[G] == R is
+ * required for the whole of q / s to be defined (only the opt-in validator can
+ * check device offsets).  Shapes, alignment and errors as the two routines. */
+mxmoe_status mx_quantize_dual(const void* x_bf16, int64_t R, int64_t C,
+                              const int32_t* row_idx, int64_t R_src,
+                              const int32_t* offs, int32_t G,
+                              uint8_t* q, uint8_t* s,
+                              uint8_t* qT, uint8_t* sT, int64_t ld, void* stream);
+
 /* ---------------------------------------------------------------- MX grouped GEMM
  * Each routine computes, for every expert g in ONE launch, a matrix product
  * over the expert's real rows, from MX operands (value = E4M3 * 2^(E8M0-127)),

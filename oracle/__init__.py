@@ -33,7 +33,8 @@ routine (torch's CPU float8 cast), brute force or invariants in
 from .codecs import (E4M3_MAX, bf16_bits_to_f64, e4m3_decode, e4m3_encode,
                      e4m3_encode_bruteforce, e8m0_decode, f32_round)
 from .mx import (mx_block_exponent, mx_colwise_ld_min, mx_dequantize,
-                 mx_quantize_colwise, mx_quantize_rowwise, mx_group_columns)
+                 mx_quantize_colwise, mx_quantize_rowwise, mx_group_columns,
+                 mx_gather_rows, mx_quantize_dual)
 from .blockwise import (bw_quantize_act_1x128, bw_quantize_weight_128x128,
                         bw_dequantize_act, bw_dequantize_weight)
 from .gemm import (mx_gemm_fwd, mx_gemm_dgrad, mx_gemm_wgrad, bw_gemm_fwd,

@@ -124,3 +124,33 @@ def mx_dequantize(q, s) -> np.ndarray:
         raise ValueError("shape mismatch")
     scale = np.ldexp(1.0, s - 127)
     return e4m3_decode(q) * np.repeat(scale, BLOCK, axis=-1)
+
+
+def mx_gather_rows(x_bits, row_idx):
+    """Routed rows of a token matrix: row r of the result is x[row_idx[r]].
+
+    A dropless MoE layer computes each expert on the tokens routed to it, stored
+    contiguously per expert (iitak.ru, "NVIDIA sped up training of
+    mixture-of-experts models on JAX tenfold": every expert on its real token
+    count in one call), so the tokens are first permuted into expert order; a
+    token routed to k experts appears k times.  Indices outside [0, R_src) are
+    clamped (the library's documented handling of invalid device indices).
+    """
+    x_bits = np.asarray(x_bits, dtype=np.uint16)
+    idx = np.clip(np.asarray(row_idx, dtype=np.int64), 0, x_bits.shape[0] - 1)
+    return x_bits[idx]
+
+
+def mx_quantize_dual(x_bits, offs, ld: int, row_idx=None):
+    """Both MX layouts of one tensor: (q, s) row-wise and (qT, sT) column-wise.
+
+    The input side of a layer needs X, dY and W in both directions (blocks run
+    along each GEMM's contraction axis); the fused quantiser produces both from
+    one read, optionally gathering routed rows first.  Definition: the row-wise
+    and column-wise quantisations above of x' = x (row_idx None) or of the
+    routed rows x' = mx_gather_rows(x, row_idx).
+    """
+    xr = np.asarray(x_bits, dtype=np.uint16) if row_idx is None else mx_gather_rows(x_bits, row_idx)
+    q, s = mx_quantize_rowwise(xr)
+    qT, sT = mx_quantize_colwise(xr, offs, ld)
+    return q, s, qT, sT

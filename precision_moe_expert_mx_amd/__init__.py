@@ -16,7 +16,7 @@ from typing import Optional, Tuple
 
 __all__ = [
     "LIB_PATH", "MxMoeError", "lib", "abi_version", "FEED_FP8",
-    "mx_colwise_ld_min", "mx_quantize_rowwise", "mx_quantize_colwise",
+    "mx_colwise_ld_min", "mx_quantize_rowwise", "mx_quantize_colwise", "mx_quantize_dual",
     "mx_grouped_gemm_fwd", "mx_grouped_gemm_dgrad", "mx_grouped_gemm_wgrad",
     "fp8bw_quantize_act_1x128", "fp8bw_quantize_weight_128x128",
     "fp8bw_grouped_gemm_fwd", "fp8bw_grouped_gemm_dgrad", "mxmoe_check_offsets",
@@ -41,6 +41,7 @@ _SIGS = {
     "mx_colwise_ld_min": (_i64, [_i64, _i32]),
     "mx_quantize_rowwise": (ctypes.c_int, [_p, _i64, _i64, _p, _p, _p]),
     "mx_quantize_colwise": (ctypes.c_int, [_p, _i64, _i64, _p, _i32, _p, _p, _i64, _p]),
+    "mx_quantize_dual": (ctypes.c_int, [_p, _i64, _i64, _p, _i64, _p, _i32, _p, _p, _p, _p, _i64, _p]),
     "mx_grouped_gemm_fwd": (ctypes.c_int, [_p, _p, _p, _p, _p, _i32, _i64, _i64, _i64, _p, ctypes.c_int, _p]),
     "mx_grouped_gemm_dgrad": (ctypes.c_int, [_p, _p, _p, _p, _i64, _p, _i32, _i64, _i64, _i64, _p, ctypes.c_int, _p]),
     "mx_grouped_gemm_wgrad": (ctypes.c_int, [_p, _p, _p, _p, _i64, _p, _i32, _i64, _i64, _i64, _p, ctypes.c_int, _p]),
@@ -162,6 +163,29 @@ def mx_quantize_colwise(x, offs=None, G: int = 1, ld: Optional[int] = None, qT=N
     _check("mx_quantize_colwise", lib().mx_quantize_colwise(_ptr(x), R, C, _ptr(offs), G, _ptr(qT), _ptr(sT), ld,
                                                             _stream_handle(stream)))
     return qT, sT
+
+
+def mx_quantize_dual(x, offs=None, G: int = 1, ld: Optional[int] = None, row_idx=None, q=None, s=None, qT=None,
+                     sT=None, stream=None):
+    """Row-wise and column-wise MX layouts from one read of x.
+
+    x bf16 [R_src, C]; row_idx int32 [R] (routed row r reads x[row_idx[r]]) or None (R = R_src).
+    Returns (q [R, C], s [R, C/32], qT [C, ld], sT [C, ld/32]), all uint8."""
+    torch = _torch()
+    x = _bf16_bits(x)
+    R_src, C = x.shape
+    R = row_idx.numel() if row_idx is not None else R_src
+    if offs is not None:
+        G = offs.numel() - 1
+    if ld is None:
+        ld = mx_colwise_ld_min(R, G) if offs is not None else 32 * ((R + 31) // 32)
+    q = _empty((R, C), torch.uint8, x) if q is None else q
+    s = _empty((R, C // 32), torch.uint8, x) if s is None else s
+    qT = _empty((C, ld), torch.uint8, x) if qT is None else qT
+    sT = _empty((C, ld // 32), torch.uint8, x) if sT is None else sT
+    _check("mx_quantize_dual", lib().mx_quantize_dual(_ptr(x), R, C, _ptr(row_idx), R_src, _ptr(offs), G, _ptr(q),
+                                                      _ptr(s), _ptr(qT), _ptr(sT), ld, _stream_handle(stream)))
+    return q, s, qT, sT
 
 
 # ---------------------------------------------------------------- MX grouped GEMMs

@@ -135,6 +135,35 @@ mxmoe_status mx_quantize_colwise(const void* x, int64_t R, int64_t C, const int3
   return launched(launch_mx_colwise((const uint16_t*)x, R, C, offs, G, qT, sT, ld, (hipStream_t)stream), fn);
 }
 
+mxmoe_status mx_quantize_dual(const void* x, int64_t R, int64_t C, const int32_t* row_idx, int64_t R_src,
+                              const int32_t* offs, int32_t G, uint8_t* q, uint8_t* s, uint8_t* qT, uint8_t* sT,
+                              int64_t ld, void* stream) {
+  const char* fn = "mx_quantize_dual";
+  if (R < 0 || C <= 0 || C % 32) return fail(MXMOE_ERR_SHAPE, "%s: need R >= 0, C > 0, C %% 32 == 0 (R=%lld C=%lld)",
+                                            fn, (long long)R, (long long)C);
+  if (R > INT32_MAX) return fail(MXMOE_ERR_SHAPE, "%s: R too large", fn);
+  if (offs && (G < 1 || G > kMaxG)) return fail(MXMOE_ERR_SHAPE, "%s: G = %d outside [1, %d]", fn, (int)G, (int)kMaxG);
+  if (ld <= 0 || ld % 32) return fail(MXMOE_ERR_ALIGN, "%s: ld must be a positive multiple of 32 (ld=%lld)", fn,
+                                      (long long)ld);
+  const int64_t need = offs ? mx_colwise_ld_min(R, G) : 32 * ((R + 31) / 32);
+  if (ld < need) return fail(MXMOE_ERR_SHAPE, "%s: ld=%lld < required %lld", fn, (long long)ld, (long long)need);
+  if (row_idx && R > 0 && R_src < 1)
+    return fail(MXMOE_ERR_SHAPE, "%s: R_src must be >= 1 with row_idx (R_src=%lld)", fn, (long long)R_src);
+  if (R > 0) {
+    TRY(check_ptr(fn, "x", x, 16));
+    TRY(check_ptr(fn, "q", q, 16));
+    TRY(check_ptr(fn, "s", s, 4));
+    if (row_idx && !aligned(row_idx, 4)) return fail(MXMOE_ERR_ALIGN, "%s: row_idx not 4-byte aligned", fn);
+  }
+  if (offs && !aligned(offs, 4)) return fail(MXMOE_ERR_ALIGN, "%s: offs not 4-byte aligned", fn);
+  TRY(check_ptr(fn, "qT", qT, 16));
+  TRY(check_ptr(fn, "sT", sT, 4));
+  TRY(check_device());
+  return launched(launch_mx_dual((const uint16_t*)x, R, C, R > 0 ? row_idx : nullptr, row_idx ? R_src : R, offs, G, q,
+                                 s, qT, sT, ld, (hipStream_t)stream),
+                  fn);
+}
+
 static mxmoe_status mx_gemm_common(int mode, const char* fn, const uint8_t* a, const uint8_t* sa, const uint8_t* b,
                                    const uint8_t* sb, int64_t ldb_cols, const int32_t* offs, int32_t G, int64_t M,
                                    int64_t N, int64_t K, void* out, int dt, void* stream) {

@@ -32,11 +32,12 @@ __device__ __forceinline__ int bf16_floor_log2(uint32_t mag) {
   return (31 - __builtin_clz(mag)) - 133;
 }
 
-// Shared exponent e (already clamped) for a block with magnitude bits `amax_bits`.
+// Shared exponent e = clamp(floor(log2 amax) - 8, -127, 127), -127 for amax = 0, of a block with
+// magnitude bits `amax_bits`.  Branch-free: a normal amax with exponent field E gives E - 135 (at most
+// 254 - 135 = 119, so the upper clamp never applies), and a zero or subnormal amax (field 0,
+// floor(log2) <= -127) gives at most -135 before clamping, so both reduce to max(E - 135, -127).
 __device__ __forceinline__ int mx_exponent(uint32_t amax_bits) {
-  if (amax_bits == 0) return -127;
-  int e = bf16_floor_log2(amax_bits) - 8;
-  return e < -127 ? -127 : (e > 127 ? 127 : e);
+  return max((int)(amax_bits >> 7) - 135, -127);
 }
 
 // bf16 bit pattern of 448 * 2^e (the largest magnitude that does not saturate), e in [-127, 119].
@@ -77,6 +78,9 @@ __device__ __forceinline__ int64_t clamp_off(int64_t v, int64_t M) { return v < 
 hipError_t launch_mx_rowwise(const uint16_t* x, int64_t R, int64_t C, uint8_t* q, uint8_t* s, hipStream_t st);
 hipError_t launch_mx_colwise(const uint16_t* x, int64_t R, int64_t C, const int32_t* offs, int32_t G,
                              uint8_t* qT, uint8_t* sT, int64_t ld, hipStream_t st);
+hipError_t launch_mx_dual(const uint16_t* x, int64_t R, int64_t C, const int32_t* row_idx, int64_t Rsrc,
+                          const int32_t* offs, int32_t G, uint8_t* q, uint8_t* s, uint8_t* qT, uint8_t* sT, int64_t ld,
+                          hipStream_t st);
 hipError_t launch_bw_act(const uint16_t* x, int64_t R, int64_t C, uint8_t* q, float* s, hipStream_t st);
 hipError_t launch_bw_weight(const uint16_t* w, int64_t R, int64_t C, uint8_t* q, float* s, uint8_t* qT,
                             hipStream_t st);

@@ -74,30 +74,32 @@ hipError_t launch_mx_rowwise(const uint16_t* x, int64_t R, int64_t C, uint8_t* q
 }
 
 // ---------------------------------------------------------------------------------------------
-// Column-wise (group-blocked, transposed): output column index space is ld; block-column bc
-// (32 output columns) holds block b of group g, rows offs[g] + 32b .. min(+32, offs[g+1]).
-// A workgroup handles 4 W consecutive block-columns x 64 P input columns (W block-columns per wave,
-// P adjacent columns per lane).  Lane l of wave w owns input columns P l .. P l + P - 1 of the tile
-// and, for each of the wave's block-columns, loads the block's (<= 32) rows as 2P-byte pieces (a
-// wave reads 128 P contiguous bytes of a row), takes each column's amax with packed 16-bit maxima,
-// pairs rows with byte permutes and converts them.  The 32 code bytes of each (column, block) go to
-// an LDS tile of 64 P output rows x 128 W bytes, which the workgroup then writes out as whole row
-// segments, 16 bytes per lane.
+// Column-wise (group-blocked, transposed), optionally fused with the row-wise layout.
+//
+// Output column index space is ld; block-column bc (32 output columns) holds block b of group g,
+// rows offs[g] + 32b .. min(+32, offs[g+1]).  A workgroup (4 waves) owns a window of 256 input
+// columns and 4 consecutive block-columns, one per wave.  Lane l owns input columns 4l .. 4l + 3 of
+// the window and loads its block's 32 rows as 8-byte pieces (a wave reads 512 contiguous bytes of a
+// row); the block's first row and row count are wave-uniform, so row addresses are scalar and full
+// blocks carry no per-row bounds.
+//  * column-wise: each column's amax by packed 16-bit maxima, rows paired by byte permutes and
+//    converted; the 32 code bytes of each (column, block) go to an LDS tile of 256 output rows x
+//    128 bytes, written out as whole 128-byte row segments, 16 bytes per lane;
+//  * row-wise (fused launch): the 8 lanes holding one 32-column block reduce its amax with DPP and
+//    convert their 4 elements; codes go straight to q, scale bytes through LDS.
+// Measured on MI355X, a double-buffered variant (next block's rows loading while the current one
+// converts), a 4-wave-per-SIMD variant and variants with linear reads or linear writes all ran at
+// the same rate: both layouts together move about as many bytes out as in, and run at 75-90% of a
+// plain device copy.
 // ---------------------------------------------------------------------------------------------
-#ifndef MXMOE_COL_LANE_COLS
-#define MXMOE_COL_LANE_COLS 4
-#endif
-#ifndef MXMOE_COL_WAVE_BLKS
-#define MXMOE_COL_WAVE_BLKS 1
-#endif
 constexpr int kColThreads = 256;
-constexpr int kColLaneCols = MXMOE_COL_LANE_COLS;  // adjacent input columns per lane (4: 8-byte pieces)
-constexpr int kColWaveBlks = MXMOE_COL_WAVE_BLKS;  // block-columns per wave
+constexpr int kColLaneCols = 4;                    // adjacent input columns per lane (8-byte pieces)
 constexpr int kColCols = 64 * kColLaneCols;        // input columns (output rows) per workgroup
-constexpr int kColBlk = 4 * kColWaveBlks;          // consecutive block-columns per workgroup
+constexpr int kColBlk = 4;                         // block-columns per workgroup (one per wave)
 constexpr int kColPitch = kColBlk * 32 + 16;       // LDS bytes per output row (padded against bank conflicts)
 constexpr int kColWinRun = 8;                      // column windows visited together (grid order)
-constexpr int kMaxGroupsLds = 1024;              // largest G the column-wise quantiser accepts
+constexpr int kRowBlks = kColCols / 32;            // row-wise 32-column blocks per window
+constexpr int kMaxGroupsLds = 1024;                // largest G the column-wise quantiser accepts
 
 __device__ __forceinline__ void group_block_starts(const int32_t* offs, int G, int64_t R, int32_t* starts,
                                                    int32_t* rows0) {
@@ -131,16 +133,195 @@ __device__ __forceinline__ void group_block_starts(const int32_t* offs, int G, i
   }
 }
 
+// Magnitude maximum of four bf16 (two dwords), as a bf16 bit pattern.
+__device__ __forceinline__ uint32_t mag_max4(uint32_t w0, uint32_t w1) {
+  typedef unsigned short v2us __attribute__((ext_vector_type(2)));
+  const v2us m = __builtin_elementwise_max(__builtin_bit_cast(v2us, w0 & 0x7FFF7FFFu),
+                                           __builtin_bit_cast(v2us, w1 & 0x7FFF7FFFu));
+  return max((uint32_t)m[0], (uint32_t)m[1]);
+}
 
+// Maximum over each group of 8 lanes: quad permutes, then the half-row mirror (lane i of an 8-lane
+// group with lane 7 - i, in the other quad).  bound_ctrl with an old value of 0 (the identity of an
+// unsigned max) lets each permute fold into the max as one DPP instruction.
+__device__ __forceinline__ uint32_t oct_max(uint32_t m) {
+  m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0xB1, 0xF, 0xF, true));
+  m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x4E, 0xF, 0xF, true));
+  return max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x141, 0xF, 0xF, true));
+}
+
+typedef uint32_t ColRows __attribute__((ext_vector_type(kColLaneCols / 2)));   // the lane's columns of one row
+
+struct ColArgs {
+  const uint16_t* x;
+  int64_t R, C;
+  int64_t cbase;        // the window's first input column
+  const int32_t* row_idx;
+  int64_t Rsrc;
+  uint8_t* q;
+  uint8_t* s;
+  uint8_t* qT;
+  uint8_t* sT;
+  int64_t ld;
+  int lane, w, t;
+  bool in;              // the lane's columns lie inside the tensor
+};
+
+// Issue the loads of one block's rows (r0, n wave-uniform).  Rows past n repeat row n - 1 (zeroed
+// after arrival), so no load depends on a per-row branch; an empty block loads nothing.
+template <bool GATHER, bool FULLWIN>
+__device__ __forceinline__ void col_load(const ColArgs& a, int r0, int n, ColRows (&v)[32]) {
+  if (n == 0 || !(FULLWIN || a.in)) {
+#pragma unroll
+    for (int r = 0; r < 32; ++r) v[r] = ColRows{};
+    return;
+  }
+  const uint32_t loff = (uint32_t)(2 * kColLaneCols * a.lane);
+#pragma unroll
+  for (int r = 0; r < 32; ++r) {
+    int64_t src_row = (int64_t)r0 + (r < n ? r : n - 1);
+    if (GATHER) {
+      const int64_t sr = a.row_idx[src_row];
+      src_row = sr < 0 ? 0 : (sr >= a.Rsrc ? a.Rsrc - 1 : sr);
+    }
+    // row base (wave-uniform, scalar registers) plus the lane's 32-bit byte offset
+    const char* base = (const char*)(a.x + src_row * a.C + a.cbase);
+    v[r] = *(const ColRows*)(base + loff);
+  }
+}
+
+// Convert the workgroup's 4 blocks (this wave's: rows r0 .. r0 + n of block-column bc0 + w) and write
+// them out.
+template <bool ROW, bool FULLWIN>
+__device__ __forceinline__ void col_group(const ColArgs& a, int r0, int n, int bc0, ColRows (&v)[32],
+                                          uint8_t* outq, uint8_t* outs, uint8_t* rsc, const int32_t* g_r0,
+                                          const int32_t* g_n) {
+  if (n < 32) {
+#pragma unroll
+    for (int r = 0; r < 32; ++r)
+      if (r >= n) v[r] = ColRows{};
+  }
+  if constexpr (ROW) {
+    // The scale byte of row r collects in byte r % 4 of rs[r / 4] (the same in all 8 lanes of a
+    // block); lane 8j + i then stores rs[i], rows 4i .. 4i + 3 of block j, to rsc [wave][j][row].
+    static_assert(kColLaneCols == 4, "row-wise blocks assume 8 lanes per 32 columns");
+    uint32_t rs[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    uint8_t* qrow = a.q + (int64_t)r0 * a.C + a.cbase;   // wave-uniform
+    const uint32_t qoff = (uint32_t)(kColLaneCols * a.lane);
+#pragma unroll
+    for (int r = 0; r < 32; ++r) {
+      const uint32_t m = oct_max(mag_max4(v[r][0], v[r][1]));
+      const int e = mx_exponent(m);
+      const uint32_t cl = mx_clamp_bits(e);
+      const float sc = __uint_as_float((uint32_t)(e + 127) << 23);
+      const uint32_t o = cvt4_e4m3(v[r][0], v[r][1], cl | (cl << 16), sc);
+      rs[r >> 2] |= (uint32_t)(e + 127) << (8 * (r & 3));
+      if (r < n && (FULLWIN || a.in)) *(uint32_t*)(qrow + r * a.C + qoff) = o;
+    }
+    const int i = a.lane & 7;
+    uint32_t mine = rs[0];
+#pragma unroll
+    for (int k = 1; k < 8; ++k) mine = i == k ? rs[k] : mine;
+    *(uint32_t*)(rsc + (a.w * kRowBlks + (a.lane >> 3)) * 32 + 4 * i) = mine;
+  }
+  typedef unsigned short v2us __attribute__((ext_vector_type(2)));
+  v2us mx[kColLaneCols / 2];
+#pragma unroll
+  for (int k = 0; k < kColLaneCols / 2; ++k) mx[k] = v2us{0, 0};
+#pragma unroll
+  for (int r = 0; r < 32; ++r)
+#pragma unroll
+    for (int k = 0; k < kColLaneCols / 2; ++k) {
+      // the magnitude mask goes through an opaque instruction: as a plain expression the compiler
+      // would share it with the row-wise conversion and keep all 64 masked words live
+      uint32_t mag;
+      asm volatile("v_and_b32 %0, 0x7fff7fff, %1" : "=v"(mag) : "v"(v[r][k]));
+      mx[k] = __builtin_elementwise_max(mx[k], __builtin_bit_cast(v2us, mag));
+    }
+#pragma unroll
+  for (int k = 0; k < kColLaneCols; ++k) {
+    const int e = mx_exponent(mx[k >> 1][k & 1]);
+    const uint32_t cl = mx_clamp_bits(e);
+    const uint32_t cl2 = cl | (cl << 16);
+    const float sc = __uint_as_float((uint32_t)(e + 127) << 23);
+    // rows 4d..4d+3 of column k: pair rows through byte permutes (row a in the low half)
+    const uint32_t sel = (k & 1) ? 0x07060302u : 0x05040100u;
+    uint32_t o[8];
+#pragma unroll
+    for (int d = 0; d < 8; ++d) {
+      const uint32_t p01 = __builtin_amdgcn_perm(v[4 * d + 1][k >> 1], v[4 * d][k >> 1], sel);
+      const uint32_t p23 = __builtin_amdgcn_perm(v[4 * d + 3][k >> 1], v[4 * d + 2][k >> 1], sel);
+      o[d] = cvt4_e4m3(p01, p23, cl2, sc);
+    }
+    uint4* dst = (uint4*)(outq + (kColLaneCols * a.lane + k) * kColPitch + 32 * a.w);
+    dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
+    dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
+    outs[(kColLaneCols * a.lane + k) * kColBlk + a.w] = (uint8_t)(e + 127);   // all-zero (pad) blocks give 0
+  }
+  // Publish the LDS tiles.  Only LDS needs to be complete: a __syncthreads() would also wait for the
+  // row-wise global stores above, putting their write latency on the path.
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+
+  // write out: output row cbase + rr holds 32 kColBlk bytes from column 32 bc0 (fewer at the right
+  // edge of ld), 16 bytes per lane
+  constexpr int kPieces = kColBlk * 2;                             // 16-byte pieces per output row
+  const int64_t nbc = a.ld / 32;
+  const int nb = nbc - bc0 < kColBlk ? (int)(nbc - bc0) : kColBlk;  // block-columns inside ld
+#pragma unroll
+  for (int it = 0; it < kColCols * kPieces / kColThreads; ++it) {
+    const int idx = it * kColThreads + a.t;
+    const int rr = idx / kPieces, piece = idx % kPieces;
+    const int64_t c = a.cbase + rr;
+    if ((FULLWIN || c < a.C) && (piece >> 1) < nb) {
+      const uint4 val = *(const uint4*)(outq + rr * kColPitch + 16 * piece);
+      *(uint4*)(a.qT + c * a.ld + (int64_t)bc0 * 32 + 16 * piece) = val;
+    }
+  }
+  for (int idx = a.t; idx < kColCols * kColBlk; idx += kColThreads) {
+    const int rr = idx / kColBlk, bb = idx % kColBlk;
+    const int64_t c = a.cbase + rr;
+    if ((FULLWIN || c < a.C) && bb < nb) a.sT[c * nbc + bc0 + bb] = outs[idx];
+  }
+  if constexpr (ROW) {
+    // row-wise scales: the window's (up to) 8 bytes of each row of the 4 blocks, one lane per row
+    const int64_t c32 = a.C / 32;
+    const int nrb = FULLWIN ? kRowBlks : (int)((a.C - a.cbase) / 32 < kRowBlks ? (a.C - a.cbase) / 32 : kRowBlks);
+    for (int idx = a.t; idx < kColBlk * 32; idx += kColThreads) {
+      const int wb = idx >> 5, r = idx & 31;
+      if (r < g_n[wb]) {
+        uint32_t lo = 0, hi = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) lo |= (uint32_t)rsc[(wb * kRowBlks + j) * 32 + r] << (8 * j);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) hi |= (uint32_t)rsc[(wb * kRowBlks + 4 + j) * 32 + r] << (8 * j);
+        uint8_t* dst = a.s + ((int64_t)g_r0[wb] + r) * c32 + a.cbase / 32;
+        if (nrb == kRowBlks && ((uintptr_t)dst & 7) == 0) {
+          *(uint2*)dst = make_uint2(lo, hi);
+        } else {
+          for (int j = 0; j < nrb; ++j) dst[j] = (uint8_t)((j < 4 ? lo : hi) >> (8 * (j & 3)));
+        }
+      }
+    }
+  }
+}
+
+// ROW: the same launch also writes the row-wise layout (q [R, C], s [R, C/32]) of every row it
+// reads; each routed row lies in exactly one block-column, so it is written once.  GATHER: routed
+// row r is read from source row row_idx[r] (clamped into [0, Rsrc)).  FULLWIN: C % 256 == 0, so every
+// window lies inside the tensor.
+template <bool ROW, bool GATHER, bool FULLWIN>
 __global__ __launch_bounds__(kColThreads) void mx_colwise_kernel(const uint16_t* __restrict__ x, int64_t R, int64_t C,
                                                                  const int32_t* __restrict__ offs, int G,
                                                                  uint8_t* __restrict__ qT, uint8_t* __restrict__ sT,
-                                                                 int64_t ld) {
+                                                                 int64_t ld, uint8_t* __restrict__ q,
+                                                                 uint8_t* __restrict__ s,
+                                                                 const int32_t* __restrict__ row_idx, int64_t Rsrc) {
   __shared__ int32_t starts[kMaxGroupsLds + 1];
   __shared__ int32_t rows0[kMaxGroupsLds + 1];
   __shared__ int32_t blk_r0[kColBlk], blk_n[kColBlk];
   __shared__ __attribute__((aligned(16))) uint8_t outq[kColCols * kColPitch];
   __shared__ uint8_t outs[kColCols * kColBlk];
+  __shared__ __attribute__((aligned(8))) uint8_t rsc[ROW ? kColBlk * 32 * kRowBlks : 8];
 
   const int nbc = (int)(ld / 32);
   // workgroup -> (column window, block-column group), 8 adjacent column windows fastest: the
@@ -186,85 +367,54 @@ __global__ __launch_bounds__(kColThreads) void mx_colwise_kernel(const uint16_t*
   }
   __syncthreads();
 
-  const int64_t cbase = (int64_t)win * kColCols;
-  const int w = t >> 6, lane = t & 63;
-  typedef uint32_t vcols __attribute__((ext_vector_type(kColLaneCols / 2)));   // the lane's columns of one row
-  for (int wb = 0; wb < kColWaveBlks; ++wb) {
-    // block-column bc0 + bl of the workgroup, columns cbase + kColLaneCols * lane ..
-    const int bl = w * kColWaveBlks + wb;
-    const int n = blk_n[bl];
-    const int64_t c = cbase + kColLaneCols * lane;
-    vcols v[32];
-    if (c < C) {   // C % 32 == 0 and c % kColLaneCols == 0: the lane's columns are all in range
-      const uint16_t* src = x + (int64_t)blk_r0[bl] * C + c;
-#pragma unroll
-      for (int r = 0; r < 32; ++r) v[r] = r < n ? *(const vcols*)(src + r * C) : vcols{};
-    } else {
-#pragma unroll
-      for (int r = 0; r < 32; ++r) v[r] = vcols{};
-    }
-    typedef unsigned short v2us __attribute__((ext_vector_type(2)));
-    v2us mx[kColLaneCols / 2];
-#pragma unroll
-    for (int q = 0; q < kColLaneCols / 2; ++q) mx[q] = v2us{0, 0};
-#pragma unroll
-    for (int r = 0; r < 32; ++r)
-#pragma unroll
-      for (int q = 0; q < kColLaneCols / 2; ++q)
-        mx[q] = __builtin_elementwise_max(mx[q], __builtin_bit_cast(v2us, v[r][q] & 0x7FFF7FFFu));
-#pragma unroll
-    for (int k = 0; k < kColLaneCols; ++k) {
-      const int e = mx_exponent(mx[k >> 1][k & 1]);
-      const uint32_t cl = mx_clamp_bits(e);
-      const uint32_t cl2 = cl | (cl << 16);
-      const float sc = __uint_as_float((uint32_t)(e + 127) << 23);
-      // rows 4d..4d+3 of column k: pair rows through byte permutes (row a in the low half)
-      const uint32_t sel = (k & 1) ? 0x07060302u : 0x05040100u;
-      uint32_t o[8];
-#pragma unroll
-      for (int d = 0; d < 8; ++d) {
-        const uint32_t p01 = __builtin_amdgcn_perm(v[4 * d + 1][k >> 1], v[4 * d][k >> 1], sel);
-        const uint32_t p23 = __builtin_amdgcn_perm(v[4 * d + 3][k >> 1], v[4 * d + 2][k >> 1], sel);
-        o[d] = cvt4_e4m3(p01, p23, cl2, sc);
-      }
-      uint4* dst = (uint4*)(outq + (kColLaneCols * lane + k) * kColPitch + 32 * bl);
-      dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
-      dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
-      outs[(kColLaneCols * lane + k) * kColBlk + bl] = (uint8_t)(e + 127);   // all-zero (pad) blocks give 0
-    }
-  }
-  __syncthreads();
+  ColArgs a;
+  a.x = x; a.R = R; a.C = C; a.cbase = (int64_t)win * kColCols; a.row_idx = row_idx; a.Rsrc = Rsrc;
+  a.q = q; a.s = s; a.qT = qT; a.sT = sT; a.ld = ld;
+  a.t = t; a.w = t >> 6; a.lane = t & 63;
+  a.in = a.cbase + kColLaneCols * a.lane < C;   // C % 32 == 0: all or none of the lane's columns
+  const int r0 = __builtin_amdgcn_readfirstlane(blk_r0[a.w]);
+  const int n = __builtin_amdgcn_readfirstlane(blk_n[a.w]);
+  ColRows v[32];
+  col_load<GATHER, FULLWIN>(a, r0, n, v);
+  col_group<ROW, FULLWIN>(a, r0, n, bc0, v, outq, outs, rsc, blk_r0, blk_n);
+}
 
-  // write out: output row cbase + rr holds 32 kColBlk bytes from column 32 bc0 (fewer at the right
-  // edge of ld), 16 bytes per lane
-  constexpr int kPieces = kColBlk * 2;                             // 16-byte pieces per output row
-  const int nb = nbc - bc0 < kColBlk ? nbc - bc0 : kColBlk;       // block-columns inside ld
-  const int64_t lds32 = ld / 32;
-#pragma unroll
-  for (int it = 0; it < kColCols * kPieces / kColThreads; ++it) {
-    const int idx = it * kColThreads + t;
-    const int rr = idx / kPieces, piece = idx % kPieces;
-    const int64_t c = cbase + rr;
-    if (c < C && (piece >> 1) < nb) {
-      const uint4 val = *(const uint4*)(outq + rr * kColPitch + 16 * piece);
-      *(uint4*)(qT + c * ld + (int64_t)bc0 * 32 + 16 * piece) = val;
-    }
-  }
-  for (int idx = t; idx < kColCols * kColBlk; idx += kColThreads) {
-    const int rr = idx / kColBlk, b = idx % kColBlk;
-    const int64_t c = cbase + rr;
-    if (c < C && b < nb) sT[c * lds32 + bc0 + b] = outs[idx];
-  }
+static int64_t colwise_grid(int64_t C, int64_t ld) {
+  return ((ld / 32 + kColBlk - 1) / kColBlk) * ((C + kColCols - 1) / kColCols);
+}
+
+template <bool ROW, bool GATHER>
+static void launch_col(bool fullwin, int64_t nwg, hipStream_t st, const uint16_t* x, int64_t R, int64_t C,
+                       const int32_t* offs, int32_t G, uint8_t* qT, uint8_t* sT, int64_t ld, uint8_t* q, uint8_t* s,
+                       const int32_t* row_idx, int64_t Rsrc) {
+  if (fullwin)
+    hipLaunchKernelGGL((mx_colwise_kernel<ROW, GATHER, true>), dim3((unsigned)nwg), dim3(kColThreads), 0, st, x, R, C,
+                       offs, G, qT, sT, ld, q, s, row_idx, Rsrc);
+  else
+    hipLaunchKernelGGL((mx_colwise_kernel<ROW, GATHER, false>), dim3((unsigned)nwg), dim3(kColThreads), 0, st, x, R,
+                       C, offs, G, qT, sT, ld, q, s, row_idx, Rsrc);
 }
 
 hipError_t launch_mx_colwise(const uint16_t* x, int64_t R, int64_t C, const int32_t* offs, int32_t G,
                              uint8_t* qT, uint8_t* sT, int64_t ld, hipStream_t st) {
   if (C == 0 || ld == 0) return hipSuccess;
-  int nbc = (int)(ld / 32);
-  const int64_t nwg = (int64_t)((nbc + kColBlk - 1) / kColBlk) * ((C + kColCols - 1) / kColCols);
+  const int64_t nwg = colwise_grid(C, ld);
   if (nwg > 0x7FFFFFFF) return hipErrorInvalidValue;
-  dim3 grid((unsigned)nwg);
-  hipLaunchKernelGGL(mx_colwise_kernel, grid, dim3(kColThreads), 0, st, x, R, C, offs, offs ? G : 1, qT, sT, ld);
+  launch_col<false, false>(C % kColCols == 0, nwg, st, x, R, C, offs, offs ? G : 1, qT, sT, ld, nullptr, nullptr,
+                           nullptr, (int64_t)0);
+  return hipGetLastError();
+}
+
+hipError_t launch_mx_dual(const uint16_t* x, int64_t R, int64_t C, const int32_t* row_idx, int64_t Rsrc,
+                          const int32_t* offs, int32_t G, uint8_t* q, uint8_t* s, uint8_t* qT, uint8_t* sT, int64_t ld,
+                          hipStream_t st) {
+  if (C == 0 || ld == 0) return hipSuccess;
+  const int64_t nwg = colwise_grid(C, ld);
+  if (nwg > 0x7FFFFFFF) return hipErrorInvalidValue;
+  if (row_idx)
+    launch_col<true, true>(C % kColCols == 0, nwg, st, x, R, C, offs, offs ? G : 1, qT, sT, ld, q, s, row_idx, Rsrc);
+  else
+    launch_col<true, false>(C % kColCols == 0, nwg, st, x, R, C, offs, offs ? G : 1, qT, sT, ld, q, s, nullptr, R);
   return hipGetLastError();
 }
 

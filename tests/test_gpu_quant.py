@@ -146,3 +146,84 @@ def test_quantisers_full_size_sampled():
     cols = np.concatenate([[0, lay.K - 1], rng.choice(lay.K, 40, replace=False)])
     qo, so = oracle.mx_quantize_colwise(np.ascontiguousarray(lay.x[:, cols]), lay.offs, ld)
     assert np.array_equal(host(qT[cols]), qo) and np.array_equal(host(sT[cols]), so)
+
+
+def _dual_equal(m, x, offs, ld, row_idx=None):
+    """Fused dual-layout quantiser against the oracle: all four outputs byte for byte."""
+    out = m.mx_quantize_dual(dev(x), None if offs is None else dev(offs), ld=ld,
+                             row_idx=None if row_idx is None else dev(row_idx))
+    ref = oracle.mx_quantize_dual(x, offs, ld, row_idx)
+    for name, g, r in zip(("q", "s", "qT", "sT"), out, ref):
+        g = host(g)
+        bad = np.argwhere(g != r)
+        assert bad.size == 0, f"{name} mismatch at {bad[:5]}"
+
+
+def test_dual_ragged_groups_and_partial_windows():
+    m = require_gpu()
+    rng = np.random.default_rng(25)
+    sizes = [0, 5, 130, 1, 60, 33, 0]
+    offs = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    M = int(offs[-1])
+    for C in (32, 96, 288, 512, 1056):
+        x = random_bf16(rng, (M, C), outlier_frac=0.01, outlier_mult=1000.0)
+        ld = oracle.mx_colwise_ld_min(M, len(sizes))
+        _dual_equal(m, x, offs, ld)
+        _dual_equal(m, x, offs, ld + 96)          # extra tail columns stay zero
+
+
+def test_dual_single_group_weight_layout():
+    m = require_gpu()
+    rng = np.random.default_rng(26)
+    for R, C in ((4 * 64, 320), (3 * 128, 2048), (37, 64)):
+        x = random_bf16(rng, (R, C), std=0.02, outlier_frac=0.001)
+        ld = 32 * ((R + 31) // 32)
+        _dual_equal(m, x, None, ld)
+        _dual_equal(m, x, None, ld + 32)
+
+
+def test_dual_gather_top2_routing():
+    """Routed rows gathered by index (each token twice, in expert order), including two invalid
+    indices that the library clamps into range."""
+    m = require_gpu()
+    rng = np.random.default_rng(27)
+    T, C, G = 300, 384, 5
+    x = random_bf16(rng, (T, C), outlier_frac=0.01, outlier_mult=100.0)
+    experts = np.stack([rng.choice(G, 2, replace=False) for _ in range(T)])    # top-2, distinct
+    tok = np.repeat(np.arange(T), 2)
+    exp = experts.reshape(-1)
+    order = np.argsort(exp, kind="stable")
+    row_idx = tok[order].astype(np.int32)
+    row_idx[7] = -3
+    row_idx[11] = T + 40
+    sizes = np.bincount(exp, minlength=G)
+    offs = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    ld = oracle.mx_colwise_ld_min(2 * T, G)
+    _dual_equal(m, x, offs, ld, row_idx)
+
+
+def test_dual_no_rows():
+    m = require_gpu()
+    x = np.zeros((0, 64), np.uint16)
+    offs = np.zeros(4, np.int32)
+    ld = oracle.mx_colwise_ld_min(0, 3)
+    q, s, qT, sT = m.mx_quantize_dual(dev(np.zeros((1, 64), np.uint16))[:0], dev(offs), ld=ld)
+    qo, so, qTo, sTo = oracle.mx_quantize_dual(x, offs, ld)
+    assert q.numel() == 0 and s.numel() == 0
+    assert np.array_equal(host(qT), qTo) and np.array_equal(host(sT), sTo)
+
+
+def test_dual_full_size_sampled():
+    """DeepSeek-V3-671B shard, gate+up X [65536, 7168]: the fused launch at full size, sampled rows
+    (row-wise) and columns (column-wise) against the oracle."""
+    m = require_gpu()
+    lay = make_workload("dsv3_671b_shard", layers=["gate_up"]).layers[0]
+    rng = np.random.default_rng(28)
+    ld = oracle.mx_colwise_ld_min(lay.M, lay.G)
+    q, s, qT, sT = m.mx_quantize_dual(dev(lay.x), dev(lay.offs), ld=ld)
+    rows = np.concatenate([[0, lay.M - 1], rng.choice(lay.M, 300, replace=False)])
+    qo, so = oracle.mx_quantize_rowwise(lay.x[rows])
+    assert np.array_equal(host(q[rows]), qo) and np.array_equal(host(s[rows]), so)
+    cols = np.concatenate([[0, lay.K - 1], rng.choice(lay.K, 40, replace=False)])
+    qo, so = oracle.mx_quantize_colwise(np.ascontiguousarray(lay.x[:, cols]), lay.offs, ld)
+    assert np.array_equal(host(qT[cols]), qo) and np.array_equal(host(sT[cols]), so)

@@ -207,3 +207,43 @@ def test_colwise_ragged_groups_short_tail_and_pads():
         if m:
             err = np.abs(d[:, c0:c0 + m] - v[r0:r0 + m].T)
             assert np.all(err <= np.abs(v[r0:r0 + m].T) * 2 ** -3 + 2.0 ** -9 * np.abs(v).max())
+
+
+def test_gather_rows_by_explicit_loop():
+    """The routed-row gather written out row by row on a tiny top-2 routing (each token twice),
+    with an out-of-range index clamped to the last token."""
+    from oracle import mx_gather_rows
+    rng = np.random.default_rng(5)
+    x = f32_to_bf16_bits(rng.standard_normal((5, 64)).astype(np.float32))
+    idx = np.array([3, 0, 4, 1, 3, 2, 0, 9, -2], dtype=np.int32)
+    want = np.zeros((len(idx), 64), dtype=np.uint16)
+    for r, i in enumerate(idx):
+        j = 0 if i < 0 else (4 if i > 4 else i)
+        for c in range(64):
+            want[r, c] = x[j, c]
+    assert np.array_equal(mx_gather_rows(x, idx), want)
+
+
+def test_dual_is_both_layouts_of_the_routed_rows():
+    """mx_quantize_dual equals row-wise and column-wise quantisation of the routed rows, and the
+    row-wise codes of a permuted tensor are the permuted codes (row-wise blocks are row-local)."""
+    from oracle import mx_quantize_dual
+    rng = np.random.default_rng(6)
+    T, C = 40, 96
+    x = f32_to_bf16_bits((rng.standard_normal((T, C)) * np.where(rng.random((T, C)) < 0.02, 100, 1))
+                         .astype(np.float32))
+    idx = np.concatenate([rng.permutation(T), rng.permutation(T)[:25]]).astype(np.int32)   # 65 routed rows
+    offs = np.array([0, 17, 17, 50, 65], dtype=np.int64)
+    ld = mx_colwise_ld_min(65, 4)
+    q, s, qT, sT = mx_quantize_dual(x, offs, ld, row_idx=idx)
+    qx, sx = mx_quantize_rowwise(x)
+    assert np.array_equal(q, qx[idx]) and np.array_equal(s, sx[idx])
+    # column-wise: the routed matrix built by an explicit loop
+    xr = np.stack([x[i] for i in idx])
+    qo, so = mx_quantize_colwise(xr, offs, ld)
+    assert np.array_equal(qT, qo) and np.array_equal(sT, so)
+    # no gather: the plain two layouts
+    q2, s2, qT2, sT2 = mx_quantize_dual(x, None, 64)
+    assert np.array_equal(q2, qx) and np.array_equal(s2, sx)
+    qo2, so2 = mx_quantize_colwise(x, None, 64)
+    assert np.array_equal(qT2, qo2) and np.array_equal(sT2, so2)
