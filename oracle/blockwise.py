@@ -62,3 +62,53 @@ def bw_dequantize_weight(q, s) -> np.ndarray:
     q = np.asarray(q)
     s = np.asarray(s, dtype=np.float64)
     return e4m3_decode(q) * np.repeat(np.repeat(s, TILE, axis=0), TILE, axis=1)
+
+
+def bw_colwise_ld_min(M: int, G: int) -> int:
+    """Smallest leading dimension of the column-wise blockwise layout: group g needs
+    128*ceil(m_g/128) <= m_g + 127 columns, so 128*ceil((M + 127 G)/128) hold any split."""
+    return TILE * (-(-(M + (TILE - 1) * G) // TILE))
+
+
+def bw_group_columns(offs):
+    """First column of each group in the column-wise blockwise layout and its block count:
+    c_g = 128 * sum_{h<g} ceil(m_h/128)."""
+    offs = np.asarray(offs, dtype=np.int64)
+    nb = -(-np.diff(offs) // TILE)
+    start = np.zeros(len(nb) + 1, dtype=np.int64)
+    np.cumsum(nb, out=start[1:])
+    return TILE * start[:-1], nb
+
+
+def bw_quantize_colwise_128(x_bits, offs, ld: int):
+    """bf16 [R, C] quantised in 128-row blocks of one column, restarting at every group's first
+    row -- the weight-gradient operands of the blockwise recipe, whose contraction runs over the
+    tokens of one expert (reading: the page shows only the forward pass; the backward pass quantises
+    along its own contraction axis, like the MX copies).
+
+    Returns qT uint8 [C, ld] and sT float32 [C, ld/128].  Group g occupies columns
+    [c_g, c_g + m_g) (see bw_group_columns); a group's last block may hold fewer than 128 rows and
+    its amax covers the real rows only.  Pad and tail bytes are 0x00; scale slots of no block are 0.
+    """
+    x_bits = np.asarray(x_bits, dtype=np.uint16)
+    R, C = x_bits.shape
+    offs = np.asarray(offs, dtype=np.int64)
+    if offs[0] != 0 or offs[-1] != R or np.any(np.diff(offs) < 0):
+        raise ValueError("bad offsets")
+    if ld % TILE or ld < bw_colwise_ld_min(R, len(offs) - 1):
+        raise ValueError("bad ld")
+    qT = np.zeros((C, ld), dtype=np.uint8)
+    sT = np.zeros((C, ld // TILE), dtype=np.float32)
+    col0, nb = bw_group_columns(offs)
+    for g in range(len(offs) - 1):
+        r0, r1 = int(offs[g]), int(offs[g + 1])
+        for b in range(int(nb[g])):
+            a = r0 + TILE * b
+            z = min(a + TILE, r1)
+            v = (x_bits[a:z].astype(np.uint32) << 16).view(np.float32)     # [n, C]
+            amax = np.max(np.abs(v), axis=0, keepdims=True)
+            q, sc = _scale_and_quantize(v, amax)
+            c = int(col0[g]) + TILE * b
+            qT[:, c:c + (z - a)] = q.T
+            sT[:, c // TILE] = sc[0]
+    return qT, sT

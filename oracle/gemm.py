@@ -17,7 +17,9 @@ DQ() is the exact value of a quantised operand.
             column-wise, blocks along N)
 * wgrad   : dW_g[n,k] = sum_{j < m_g} DQ(dY^c)[n, c_g + j] DQ(X^c)[k, c_g + j]
             (column-wise copies, group g starting at column c_g; dW_g = 0 for an
-            empty group)
+            empty group).  Blockwise: the same sum promoted per 128-token block,
+            each block's partial multiplied by the dY row scale and the X row scale
+            of that block.
 
 Blockwise recipe (aifind.ru DeepSeek-V3 article, section "Low-precision
 training: FP8 Framework"): the FP8 products over each 128-element slice of the
@@ -38,7 +40,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .blockwise import TILE
+from .blockwise import TILE, bw_group_columns
 from .codecs import e4m3_decode
 from .mx import BLOCK, mx_dequantize, mx_group_columns
 
@@ -169,6 +171,34 @@ def bw_gemm_dgrad(qdy, sdy, qw, sw, offs, N, K, rows=None):
         sb = np.repeat(sw64[g * N // TILE:(g + 1) * N // TILE].T, TILE, axis=0)   # [K, N/128]
         return qb, sb
     return _bw_rows(qdy, sdy, offs, rows, b_of, K)
+
+
+def bw_gemm_wgrad(qdyT, sdyT, qxT, sxT, offs, N, K, groups=None, n_idx=None, k_idx=None):
+    """Blockwise weight gradient: dW_g[n,k] = sum_b sdyT[n, b] sxT[k, b] sum_{j in block b} qdyT[n, j] qxT[k, j]
+    over group g's 128-token blocks b (columns from bw_group_columns; pads hold zero codes).
+
+    Returns (dW [len(groups), len(n_idx), len(k_idx)], bound) in float64.
+    """
+    qdyT, qxT = np.asarray(qdyT), np.asarray(qxT)
+    sdyT, sxT = np.asarray(sdyT, dtype=np.float64), np.asarray(sxT, dtype=np.float64)
+    offs = np.asarray(offs, dtype=np.int64)
+    G = len(offs) - 1
+    groups = np.arange(G) if groups is None else np.asarray(groups)
+    n_idx = np.arange(N) if n_idx is None else np.asarray(n_idx)
+    k_idx = np.arange(K) if k_idx is None else np.asarray(k_idx)
+    col0, nb = bw_group_columns(offs)
+    out = np.zeros((len(groups), len(n_idx), len(k_idx)))
+    bound = np.zeros_like(out)
+    for i, g in enumerate(groups):
+        c0 = int(col0[g])
+        for b in range(int(nb[g])):
+            cs = slice(c0 + TILE * b, c0 + TILE * (b + 1))
+            A = e4m3_decode(qdyT[n_idx, cs])
+            B = e4m3_decode(qxT[k_idx, cs])
+            scale = sdyT[n_idx, c0 // TILE + b][:, None] * sxT[k_idx, c0 // TILE + b][None, :]
+            out[i] += scale * (A @ B.T)
+            bound[i] += np.abs(scale) * (np.abs(A) @ np.abs(B).T)
+    return out, bound
 
 
 def _ulp_bf16(x):

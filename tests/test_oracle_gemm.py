@@ -221,3 +221,74 @@ def test_tolerance_checker():
     # bf16: half a bf16 ulp of (|ref| + tol) on top of the fp32 bound
     t = gemm_tolerance(np.array([1000.0]), np.array([1000.0]), "bf16")
     assert np.isclose(t[0], 1e-2 + 0.5 * 4.0)
+
+
+def test_blockwise_colwise_is_act_quantiser_of_transposed_groups():
+    """The 128-row column-wise blockwise quantiser of group g equals the (separately pinned) 1x128
+    activation quantiser applied to the group's rows transposed and zero-padded to a multiple of
+    128: zeros neither raise an amax nor change a code, and an all-zero pad tile is not stored."""
+    from oracle import bw_colwise_ld_min, bw_group_columns, bw_quantize_colwise_128
+    rng = np.random.default_rng(19)
+    sizes, C = [0, 5, 130, 1, 300, 128, 0], 256
+    offs = routing_offsets(sizes)
+    M, G = int(offs[-1]), len(sizes)
+    v = rng.standard_normal((M, C)) * np.where(rng.random((M, C)) < 0.01, 100.0, 1.0)
+    x = f32_to_bf16_bits(v.astype(np.float32))
+    ld = bw_colwise_ld_min(M, G) + 128
+    qT, sT = bw_quantize_colwise_128(x, offs, ld)
+    col0, nb = bw_group_columns(offs)
+    assert ld == 128 * (-(-(M + 127 * G) // 128)) + 128
+    used = np.zeros(ld, bool)
+    for g in range(G):
+        r0, r1 = int(offs[g]), int(offs[g + 1])
+        m = r1 - r0
+        if m == 0:
+            assert nb[g] == 0
+            continue
+        pad = np.zeros((128 * int(nb[g]), C), np.uint16)
+        pad[:m] = x[r0:r1]
+        qa, sa = bw_quantize_act_1x128(np.ascontiguousarray(pad.T))      # [C, 128 nb]
+        c0 = int(col0[g])
+        assert np.array_equal(qT[:, c0:c0 + m], qa[:, :m])
+        assert np.array_equal(sT[:, c0 // 128:c0 // 128 + int(nb[g])], sa)
+        used[c0:c0 + m] = True
+    assert not qT[:, ~used].any()                      # pads and the tail are zero
+    assert not sT[:, int(np.sum(nb)):].any()           # scale slots of no block are zero
+
+
+def test_blockwise_wgrad_bruteforce_and_dense():
+    """Blockwise wgrad against fsum triple loops with per-block promotion (tiny shapes), and for a
+    single group against np.matmul of the dequantised column-wise operands."""
+    from oracle import bw_colwise_ld_min, bw_gemm_wgrad, bw_group_columns, bw_quantize_colwise_128
+    rng = np.random.default_rng(20)
+    sizes, N, K = [3, 0, 130], 128, 128
+    offs = routing_offsets(sizes)
+    M, G = int(offs[-1]), len(sizes)
+    ld = bw_colwise_ld_min(M, G)
+    qd, sd = bw_quantize_colwise_128(_bf(rng, (M, N)), offs, ld)
+    qx, sx = bw_quantize_colwise_128(_bf(rng, (M, K)), offs, ld)
+    dw, bnd = bw_gemm_wgrad(qd, sd, qx, sx, offs, N, K)
+    assert not dw[1].any() and not bnd[1].any()        # empty expert: zero gradient
+    A, B = e4m3_decode(qd), e4m3_decode(qx)
+    col0, nb = bw_group_columns(offs)
+    for g in (0, 2):
+        c0, m = int(col0[g]), sizes[g]
+        for n in range(0, N, 17):
+            for k in range(0, K, 23):
+                terms = []
+                for b in range(int(nb[g])):
+                    js = range(c0 + 128 * b, min(c0 + 128 * b + 128, c0 + m))
+                    part = math.fsum(float(A[n, j]) * float(B[k, j]) for j in js)
+                    terms.append(float(sd[n, c0 // 128 + b]) * float(sx[k, c0 // 128 + b]) * part)
+                assert math.isclose(dw[g, n, k], math.fsum(terms), rel_tol=1e-12, abs_tol=1e-300)
+    # one group of 256 tokens: the dense product of the dequantised operands
+    offs1 = np.array([0, 256])
+    ld1 = bw_colwise_ld_min(256, 1)
+    qd1, sd1 = bw_quantize_colwise_128(_bf(rng, (256, N)), offs1, ld1)
+    qx1, sx1 = bw_quantize_colwise_128(_bf(rng, (256, K)), offs1, ld1)
+    dw1, bnd1 = bw_gemm_wgrad(qd1, sd1, qx1, sx1, offs1, N, K)
+    Dd = e4m3_decode(qd1[:, :256]) * np.repeat(sd1[:, :2].astype(np.float64), 128, axis=1)
+    Dx = e4m3_decode(qx1[:, :256]) * np.repeat(sx1[:, :2].astype(np.float64), 128, axis=1)
+    # products of two fp32 scales and two E4M3 codes need up to 56 bits, so both sides round in
+    # float64: compare relative to sum |a b|
+    assert np.all(np.abs(dw1[0] - np.matmul(Dd, Dx.T)) <= 1e-12 * bnd1[0])
