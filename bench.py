@@ -271,10 +271,11 @@ def cpu_baseline(lay, rows_per_expert=2048):
 
 # ------------------------------------------------------------------------------------------- blockwise
 def blockwise_leg(m, torch, steps=5, sample_rows=256):
-    """DeepSeek-style blockwise FP8 (1x128 activation tiles, 128x128 weight blocks, fp32 scales,
-    promotion every 128) against MXFP8 on the same DeepSeek-V3-16B expert-layer tensors: forward and
-    dgrad, each recipe with its own quantisers.  Accuracy: relative Frobenius error of each recipe's
-    fp32 Y and dX against an fp64 product of the original bf16 tensors, on sampled rows."""
+    """DeepSeek-style blockwise FP8 (1x128 activation tiles, 128x128 weight blocks, 128-token blocks
+    for the weight gradient, fp32 scales, promotion every 128) against MXFP8 on the same
+    DeepSeek-V3-16B expert-layer tensors: forward, dgrad and wgrad, each recipe with its own
+    quantisers.  Accuracy: relative Frobenius error of each recipe's fp32 Y, dX (sampled rows) and dW
+    (two experts, sampled n and k) against fp64 products of the original bf16 tensors."""
     from workloads import make_workload
     wl = make_workload("dsv3_16b_blockwise")
     out = {"workload": "dsv3_16b (64 experts, 49152 routed rows)", "layers": {}}
@@ -287,6 +288,7 @@ def blockwise_leg(m, torch, steps=5, sample_rows=256):
         rec = {}
         # blockwise
         bq = {}
+        ldb = m.fp8bw_colwise_ld_min(M, G)
         ops_bw = [
             Op("quant_x", "quant", lambda: bq.update(x=m.fp8bw_quantize_act_1x128(x)), M * K * QUANT_BYTES_PER_ELEM, ""),
             Op("quant_w", "quant", lambda: bq.update(w=m.fp8bw_quantize_weight_128x128(w, transposed=True)),
@@ -295,9 +297,16 @@ def blockwise_leg(m, torch, steps=5, sample_rows=256):
             Op("quant_dy", "quant", lambda: bq.update(dy=m.fp8bw_quantize_act_1x128(dy)), M * N * QUANT_BYTES_PER_ELEM, ""),
             Op("dgrad", "gemm", lambda: bq.update(dx=m.fp8bw_grouped_gemm_dgrad(*bq["dy"], bq["w"][2], bq["w"][1], offs, K,
                                                                                  "f32")), f, ""),
+            Op("quant_dy_col", "quant", lambda: bq.update(dyc=m.fp8bw_quantize_colwise_128(dy, offs, ld=ldb)),
+               M * N * QUANT_BYTES_PER_ELEM, ""),
+            Op("quant_x_col", "quant", lambda: bq.update(xc=m.fp8bw_quantize_colwise_128(x, offs, ld=ldb)),
+               M * K * QUANT_BYTES_PER_ELEM, ""),
+            Op("wgrad", "gemm", lambda: bq.update(dw=m.fp8bw_grouped_gemm_wgrad(*bq["dyc"], *bq["xc"], offs, M, "f32")),
+               f, ""),
         ]
         mq = {}
         ld = G * N
+        ldm = m.mx_colwise_ld_min(M, G)
         ops_mx = [
             Op("quant_x", "quant", lambda: mq.update(x=m.mx_quantize_rowwise(x)), M * K * QUANT_BYTES_PER_ELEM, ""),
             Op("quant_w", "quant", lambda: mq.update(w=m.mx_quantize_rowwise(w)), G * N * K * QUANT_BYTES_PER_ELEM, ""),
@@ -305,12 +314,18 @@ def blockwise_leg(m, torch, steps=5, sample_rows=256):
             Op("quant_dy", "quant", lambda: mq.update(dy=m.mx_quantize_rowwise(dy)), M * N * QUANT_BYTES_PER_ELEM, ""),
             Op("quant_w_col", "quant", lambda: mq.update(wc=m.mx_quantize_colwise(w, None, ld=ld)), G * N * K * QUANT_BYTES_PER_ELEM, ""),
             Op("dgrad", "gemm", lambda: mq.update(dx=m.mx_grouped_gemm_dgrad(*mq["dy"], *mq["wc"], offs, K, "f32")), f, ""),
+            Op("quant_dy_col", "quant", lambda: mq.update(dyc=m.mx_quantize_colwise(dy, offs, ld=ldm)),
+               M * N * QUANT_BYTES_PER_ELEM, ""),
+            Op("quant_x_col", "quant", lambda: mq.update(xc=m.mx_quantize_colwise(x, offs, ld=ldm)),
+               M * K * QUANT_BYTES_PER_ELEM, ""),
+            Op("wgrad", "gemm", lambda: mq.update(dw=m.mx_grouped_gemm_wgrad(*mq["dyc"], *mq["xc"], offs, M, "f32")),
+               f, ""),
         ]
         for name, ops_ in (("blockwise", ops_bw), ("mxfp8", ops_mx)):
             ms = time_ops(torch, ops_, steps, 1)
             gm = sum(float(np.mean(o.ms)) for o in ops_ if o.kind == "gemm")
-            rec[name] = {"ms_fwd_dgrad_with_quant": round(ms, 4),
-                         "gemm_tflops": round(2 * f / (gm * 1e-3) / 1e12, 1),
+            rec[name] = {"ms_fwd_bwd_with_quant": round(ms, 4),
+                         "gemm_tflops": round(3 * f / (gm * 1e-3) / 1e12, 1),
                          "ops": {o.name: op_summary(o) for o in ops_}}
         # accuracy on sampled rows against fp64 products of the bf16 inputs
         rows = np.sort(rng.choice(M, sample_rows, replace=False))
@@ -324,6 +339,20 @@ def blockwise_leg(m, torch, steps=5, sample_rows=256):
             dxg = q["dx"][torch.from_numpy(rows).cuda()].double().cpu().numpy()
             rec[name]["rel_fro_err_y"] = float(np.linalg.norm(yg - y_ref) / np.linalg.norm(y_ref))
             rec[name]["rel_fro_err_dx"] = float(np.linalg.norm(dxg - dx_ref) / np.linalg.norm(dx_ref))
+        # weight gradient of two sampled experts on sampled (n, k)
+        sizes = np.diff(lay.offs.astype(np.int64))
+        gs = [int(np.argmax(sizes)), int(rng.choice(np.flatnonzero(sizes > 0)))]
+        n_idx = np.sort(rng.choice(N, 64, replace=False))
+        k_idx = np.sort(rng.choice(K, 64, replace=False))
+        for name, q in (("blockwise", bq), ("mxfp8", mq)):
+            num = den = 0.0
+            for g in gs:
+                r0, r1 = int(lay.offs[g]), int(lay.offs[g + 1])
+                ref = bf16_to_f64(lay.dy[r0:r1][:, n_idx]).T @ bf16_to_f64(lay.x[r0:r1][:, k_idx])
+                got = q["dw"][g][torch.from_numpy(n_idx).cuda()][:, torch.from_numpy(k_idx).cuda()].double().cpu().numpy()
+                num += float(np.sum((got - ref) ** 2))
+                den += float(np.sum(ref ** 2))
+            rec[name]["rel_fro_err_dw"] = float(np.sqrt(num / den))
         out["layers"][lay.name] = rec
         del x, w, dy, bq, mq, ops_bw, ops_mx
         torch.cuda.empty_cache()

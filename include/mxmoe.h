@@ -197,6 +197,36 @@ mxmoe_status fp8bw_grouped_gemm_dgrad(const uint8_t* qdy, const float* sdy,
                                       const int32_t* offs, int32_t G, int64_t M, int64_t N, int64_t K,
                                       void* dx, mxmoe_dtype dxdt, void* stream);
 
+/* fp8bw_colwise_ld_min: smallest leading dimension of the column-wise blockwise
+ * layout for M rows in G groups, 128 * ceil((M + 127 G) / 128) (-1 for M < 0 or
+ * G < 1).  Host-only arithmetic. */
+int64_t fp8bw_colwise_ld_min(int64_t M, int32_t G);
+
+/* fp8bw_quantize_colwise_128: x bf16 [R, C] -> qT E4M3 [C, ld], sT f32 [C, ld/128].
+ * The weight-gradient operands of the blockwise recipe (a reading: the page shows
+ * the forward pass only; the backward pass quantises along its own contraction
+ * axis, the tokens of one expert): blocks of 128 consecutive rows of one column,
+ * restarting at each group's first row, scale s = fl32(amax / 448) (1 for an
+ * all-zero block), codes E4M3(fl32(v / s)).  Group g occupies columns
+ * [c_g, c_g + m_g), c_g = 128 * sum_{h<g} ceil(m_h/128); a group's last block may
+ * be short (amax over real rows); pad and tail bytes are 0x00 and scale slots of
+ * no block are 0.  offs == NULL means one group of R rows (ld >= 128*ceil(R/128));
+ * otherwise ld >= fp8bw_colwise_ld_min(R, G).  ld % 128 == 0, C % 128 == 0. */
+mxmoe_status fp8bw_quantize_colwise_128(const void* x_bf16, int64_t R, int64_t C,
+                                        const int32_t* offs, int32_t G,
+                                        uint8_t* qT, float* sT, int64_t ld, void* stream);
+
+/* fp8bw_grouped_gemm_wgrad: dW[g, n, k] = sum_b sdyT[n, c_g/128 + b] sxT[k, c_g/128 + b] *
+ *                                         sum_{j in block b} qdyT[n, j] qxT[k, j]
+ * over expert g's 128-token blocks b (each block's FP8 partial promoted with its two
+ * fp32 scales).  qdyT/sdyT = fp8bw_quantize_colwise_128(dY [M, N], offs, ld),
+ * qxT/sxT = fp8bw_quantize_colwise_128(X [M, K], offs, ld) with the same ld;
+ * dw [G, N, K] (dwdt); dW_g = 0 for an empty expert, written (also for M == 0). */
+mxmoe_status fp8bw_grouped_gemm_wgrad(const uint8_t* qdyT, const float* sdyT,
+                                      const uint8_t* qxT, const float* sxT, int64_t ld,
+                                      const int32_t* offs, int32_t G, int64_t M, int64_t N, int64_t K,
+                                      void* dw, mxmoe_dtype dwdt, void* stream);
+
 /* Opt-in offsets validator: copies offs to the host (synchronising `stream`)
  * and checks offs[0] == 0, non-decreasing, offs[G] == M.  Returns
  * MXMOE_ERR_OFFSETS with a message naming the first bad index. */

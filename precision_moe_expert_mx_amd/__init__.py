@@ -20,6 +20,7 @@ __all__ = [
     "mx_grouped_gemm_fwd", "mx_grouped_gemm_dgrad", "mx_grouped_gemm_wgrad",
     "fp8bw_quantize_act_1x128", "fp8bw_quantize_weight_128x128",
     "fp8bw_grouped_gemm_fwd", "fp8bw_grouped_gemm_dgrad", "mxmoe_check_offsets",
+    "fp8bw_colwise_ld_min", "fp8bw_quantize_colwise_128", "fp8bw_grouped_gemm_wgrad",
     "EXPORTED_SYMBOLS",
 ]
 
@@ -49,6 +50,10 @@ _SIGS = {
     "fp8bw_quantize_weight_128x128": (ctypes.c_int, [_p, _i64, _i64, _p, _p, _p, _p]),
     "fp8bw_grouped_gemm_fwd": (ctypes.c_int, [_p, _p, _p, _p, _p, _i32, _i64, _i64, _i64, _p, ctypes.c_int, _p]),
     "fp8bw_grouped_gemm_dgrad": (ctypes.c_int, [_p, _p, _p, _p, _p, _i32, _i64, _i64, _i64, _p, ctypes.c_int, _p]),
+    "fp8bw_colwise_ld_min": (_i64, [_i64, _i32]),
+    "fp8bw_quantize_colwise_128": (ctypes.c_int, [_p, _i64, _i64, _p, _i32, _p, _p, _i64, _p]),
+    "fp8bw_grouped_gemm_wgrad": (ctypes.c_int, [_p, _p, _p, _p, _i64, _p, _i32, _i64, _i64, _i64, _p, ctypes.c_int,
+                                                _p]),
     "mxmoe_check_offsets": (ctypes.c_int, [_p, _i32, _i64, _p]),
 }
 EXPORTED_SYMBOLS = tuple(_SIGS)
@@ -274,6 +279,41 @@ def fp8bw_grouped_gemm_dgrad(qdy, sdy, qwT, sw, offs, K: int, out_dtype: str = "
                                                                       _ptr(offs), G, M, N, K, _ptr(dx), cdt,
                                                                       _stream_handle(stream)))
     return dx
+
+
+def fp8bw_colwise_ld_min(M: int, G: int) -> int:
+    """Smallest leading dimension of the column-wise blockwise layout (host arithmetic)."""
+    return int(lib().fp8bw_colwise_ld_min(M, G))
+
+
+def fp8bw_quantize_colwise_128(x, offs=None, G: int = 1, ld: Optional[int] = None, qT=None, sT=None, stream=None):
+    """x bf16 [R, C] -> (qT uint8 [C, ld], sT float32 [C, ld/128]): 128-row blocks restarting per group."""
+    torch = _torch()
+    x = _bf16_bits(x)
+    R, C = x.shape
+    if offs is not None:
+        G = offs.numel() - 1
+    if ld is None:
+        ld = fp8bw_colwise_ld_min(R, G) if offs is not None else 128 * ((R + 127) // 128)
+    qT = _empty((C, ld), torch.uint8, x) if qT is None else qT
+    sT = _empty((C, ld // 128), torch.float32, x) if sT is None else sT
+    _check("fp8bw_quantize_colwise_128", lib().fp8bw_quantize_colwise_128(_ptr(x), R, C, _ptr(offs), G, _ptr(qT),
+                                                                          _ptr(sT), ld, _stream_handle(stream)))
+    return qT, sT
+
+
+def fp8bw_grouped_gemm_wgrad(qdyT, sdyT, qxT, sxT, offs, M: int, out_dtype: str = "f32", dw=None, stream=None,
+                             fast: bool = False):
+    """dW [G, N, K] from the column-wise blockwise copies of dY [N, ld] and X [K, ld]."""
+    N, ld = qdyT.shape
+    K = qxT.shape[0]
+    G = offs.numel() - 1
+    tdt, cdt = _out_dtype(out_dtype, fast)
+    dw = _empty((G, N, K), tdt, qdyT) if dw is None else dw
+    _check("fp8bw_grouped_gemm_wgrad", lib().fp8bw_grouped_gemm_wgrad(_ptr(qdyT), _ptr(sdyT), _ptr(qxT), _ptr(sxT), ld,
+                                                                      _ptr(offs), G, M, N, K, _ptr(dw), cdt,
+                                                                      _stream_handle(stream)))
+    return dw
 
 
 def mxmoe_check_offsets(offs, M: int, stream=None) -> None:

@@ -242,9 +242,33 @@ mxmoe_status fp8bw_quantize_weight_128x128(const void* w, int64_t R, int64_t C, 
   return launched(launch_bw_weight((const uint16_t*)w, R, C, q, s, qT, (hipStream_t)stream), fn);
 }
 
+int64_t fp8bw_colwise_ld_min(int64_t M, int32_t G) {
+  if (M < 0 || G < 1) return -1;
+  return 128 * ((M + 127 * (int64_t)G + 127) / 128);
+}
+
+mxmoe_status fp8bw_quantize_colwise_128(const void* x, int64_t R, int64_t C, const int32_t* offs, int32_t G,
+                                        uint8_t* qT, float* sT, int64_t ld, void* stream) {
+  const char* fn = "fp8bw_quantize_colwise_128";
+  if (R < 0 || C <= 0 || C % 128) return fail(MXMOE_ERR_SHAPE, "%s: need R >= 0, C > 0, C %% 128 == 0 (R=%lld C=%lld)",
+                                             fn, (long long)R, (long long)C);
+  if (R > INT32_MAX) return fail(MXMOE_ERR_SHAPE, "%s: R too large", fn);
+  if (offs && (G < 1 || G > kMaxG)) return fail(MXMOE_ERR_SHAPE, "%s: G = %d outside [1, %d]", fn, (int)G, (int)kMaxG);
+  if (ld <= 0 || ld % 128) return fail(MXMOE_ERR_ALIGN, "%s: ld must be a positive multiple of 128 (ld=%lld)", fn,
+                                       (long long)ld);
+  const int64_t need = offs ? fp8bw_colwise_ld_min(R, G) : 128 * ((R + 127) / 128);
+  if (ld < need) return fail(MXMOE_ERR_SHAPE, "%s: ld=%lld < required %lld", fn, (long long)ld, (long long)need);
+  if (R > 0) TRY(check_ptr(fn, "x", x, 16));
+  if (offs && !aligned(offs, 4)) return fail(MXMOE_ERR_ALIGN, "%s: offs not 4-byte aligned", fn);
+  TRY(check_ptr(fn, "qT", qT, 16));
+  TRY(check_ptr(fn, "sT", sT, 4));
+  TRY(check_device());
+  return launched(launch_bw_colwise((const uint16_t*)x, R, C, offs, G, qT, sT, ld, (hipStream_t)stream), fn);
+}
+
 static mxmoe_status bw_gemm_common(int mode, const char* fn, const uint8_t* a, const float* sa, const uint8_t* b,
                                    const float* sb, const int32_t* offs, int32_t G, int64_t M, int64_t N, int64_t K,
-                                   void* out, int dt, void* stream) {
+                                   void* out, int dt, void* stream, int64_t ld = 0) {
   TRY(check_gemm_common(fn, offs, G, M, N, K, out, dt));
   TRY(check_ptr(fn, "A operand", a, 16));
   TRY(check_ptr(fn, "A scales", sa, 4));
@@ -258,11 +282,14 @@ static mxmoe_status bw_gemm_common(int mode, const char* fn, const uint8_t* a, c
   p.feed = (dt & MXMOE_FEED_FP8) ? kFeedFast : kFeedPrecise;
   if (mode == kFwd) {
     p.lda = K; p.ldsa = K / 128; p.ldb = K; p.ldsb = K / 128;
-  } else {
+  } else if (mode == kDgrad) {
     // dgrad: B is the transposed weight copy [K, G*N]; scales keep the forward layout
     p.lda = N; p.ldsa = N / 128; p.ldb = (int64_t)G * N; p.ldsb = K / 128;
+  } else {
+    // wgrad: both operands column-wise with leading dimension ld, one fp32 scale per 128 columns
+    p.lda = ld; p.ldsa = ld / 128; p.ldb = ld; p.ldsb = ld / 128;
   }
-  if (M == 0) return ok();
+  if (mode != kWgrad && M == 0) return ok();
   TRY(check_device());
   return launched(launch_bw_gemm(mode, p, (hipStream_t)stream), fn);
 }
@@ -271,6 +298,16 @@ mxmoe_status fp8bw_grouped_gemm_fwd(const uint8_t* qx, const float* sx, const ui
                                     const int32_t* offs, int32_t G, int64_t M, int64_t N, int64_t K, void* y,
                                     mxmoe_dtype ydt, void* stream) {
   return bw_gemm_common(kFwd, "fp8bw_grouped_gemm_fwd", qx, sx, qw, sw, offs, G, M, N, K, y, (int)ydt, stream);
+}
+
+mxmoe_status fp8bw_grouped_gemm_wgrad(const uint8_t* qdyT, const float* sdyT, const uint8_t* qxT, const float* sxT,
+                                      int64_t ld, const int32_t* offs, int32_t G, int64_t M, int64_t N, int64_t K,
+                                      void* dw, mxmoe_dtype dwdt, void* stream) {
+  const char* fn = "fp8bw_grouped_gemm_wgrad";
+  if (G >= 1 && M >= 0 && (ld % 128 || ld < fp8bw_colwise_ld_min(M, G)))
+    return fail(MXMOE_ERR_SHAPE, "%s: ld=%lld must be a multiple of 128 and >= fp8bw_colwise_ld_min(M, G)=%lld", fn,
+                (long long)ld, (long long)fp8bw_colwise_ld_min(M, G));
+  return bw_gemm_common(kWgrad, fn, qdyT, sdyT, qxT, sxT, offs, G, M, N, K, dw, (int)dwdt, stream, ld);
 }
 
 mxmoe_status fp8bw_grouped_gemm_dgrad(const uint8_t* qdy, const float* sdy, const uint8_t* qwT, const float* sw,

@@ -74,6 +74,63 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
 // Device-side clamp of an offset read from memory into [0, M].
 __device__ __forceinline__ int64_t clamp_off(int64_t v, int64_t M) { return v < 0 ? 0 : (v > M ? M : v); }
 
+// Column-wise layouts place group g's blocks of BLK rows from block-column starts[g] =
+// sum_{h<g} ceil(m_h / BLK).  Wave 0 of the workgroup scans the clamped offsets 64 groups per step and
+// writes starts[0..G] and rows0[g] = offs[g] (offs NULL: one group of R rows).  The caller
+// synchronises before reading them.
+template <int BLK>
+__device__ __forceinline__ void group_block_starts(const int32_t* offs, int G, int64_t R, int32_t* starts,
+                                                   int32_t* rows0) {
+  if (threadIdx.x < 64) {
+    int lane = threadIdx.x;
+    int32_t carry = 0;
+    for (int g0 = 0; g0 <= G; g0 += 64) {
+      int g = g0 + lane;
+      int32_t nb = 0;
+      int64_t o0 = 0;
+      if (g <= G) {
+        o0 = offs ? clamp_off(offs[g], R) : (g == 0 ? 0 : R);
+        rows0[g] = (int32_t)o0;
+      }
+      if (g < G) {
+        int64_t o1 = offs ? clamp_off(offs[g + 1], R) : R;
+        int64_t m = o1 > o0 ? o1 - o0 : 0;
+        nb = (int32_t)((m + BLK - 1) / BLK);
+      }
+      // inclusive scan of nb across the wave
+      int32_t incl = nb;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        int32_t t = __shfl_up(incl, d, 64);
+        if (lane >= d) incl += t;
+      }
+      if (g <= G) starts[g] = carry + incl - nb;    // exclusive
+      carry += __shfl(incl, 63, 64);
+    }
+  }
+}
+
+// Block-column bc of a column-wise layout (see group_block_starts): first row r0 and row count n
+// (<= BLK) of the block it holds, n = 0 for pad / tail block-columns.
+template <int BLK>
+__device__ __forceinline__ void block_rows(int bc, int nbc, int G, const int32_t* starts, const int32_t* rows0,
+                                           int32_t& r0, int32_t& n) {
+  r0 = 0;
+  n = 0;
+  if (bc < nbc && bc < starts[G]) {
+    // last group g with starts[g] <= bc (empty groups share their start with the next group)
+    int lo = 0, hi = G - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (starts[mid] <= bc) lo = mid; else hi = mid - 1;
+    }
+    const int64_t g0 = rows0[lo], g1 = rows0[lo + 1];
+    r0 = (int32_t)(g0 + (int64_t)BLK * (bc - starts[lo]));
+    const int64_t left = g1 - r0;
+    n = (int32_t)(left < BLK ? left : BLK);
+  }
+}
+
 // ---- internal launchers (defined in the .hip files; arguments already validated) ---------------
 hipError_t launch_mx_rowwise(const uint16_t* x, int64_t R, int64_t C, uint8_t* q, uint8_t* s, hipStream_t st);
 hipError_t launch_mx_colwise(const uint16_t* x, int64_t R, int64_t C, const int32_t* offs, int32_t G,
@@ -81,6 +138,8 @@ hipError_t launch_mx_colwise(const uint16_t* x, int64_t R, int64_t C, const int3
 hipError_t launch_mx_dual(const uint16_t* x, int64_t R, int64_t C, const int32_t* row_idx, int64_t Rsrc,
                           const int32_t* offs, int32_t G, uint8_t* q, uint8_t* s, uint8_t* qT, uint8_t* sT, int64_t ld,
                           hipStream_t st);
+hipError_t launch_bw_colwise(const uint16_t* x, int64_t R, int64_t C, const int32_t* offs, int32_t G, uint8_t* qT,
+                             float* sT, int64_t ld, hipStream_t st);
 hipError_t launch_bw_act(const uint16_t* x, int64_t R, int64_t C, uint8_t* q, float* s, hipStream_t st);
 hipError_t launch_bw_weight(const uint16_t* w, int64_t R, int64_t C, uint8_t* q, float* s, uint8_t* qT,
                             hipStream_t st);

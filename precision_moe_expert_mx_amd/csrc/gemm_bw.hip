@@ -12,7 +12,8 @@
 //   forward: A = X rows of expert g, B = W_g rows, L = K            (Y = X W^T)
 //   dgrad:   A = dY rows of expert g, B = column-wise W (rows = k, columns gN..gN+N), L = N
 //   wgrad:   A = column-wise dY (rows = n), B = column-wise X (rows = k), both from column c_g,
-//            L = 32 ceil(m_g / 32) (pads are zero)
+//            L = 128 ceil(m_g / 128) (pads are zero); blockwise only: 128-token blocks restarting at
+//            each expert, an fp32 scale per (row, block) on both operands, promoted per block
 //
 // Main loop: BK = 128 contraction bytes per step; global -> registers (prefetch of the next step)
 // -> LDS (16-byte chunks XOR-swizzled by row) -> MFMA operands.  Each of the four waves owns a
@@ -42,7 +43,7 @@ struct TileInfo {
   int mt, nt;     // tile coordinates inside the expert
   int64_t row0;   // first global row of A for this expert (forward / dgrad)
   int rows;       // valid rows of this tile (forward / dgrad)
-  int nblk;       // wgrad: number of 32-blocks in the contraction
+  int nblk;       // wgrad: number of contraction blocks (32 rows MX, 128 rows blockwise)
   int64_t col0;   // wgrad: first column of the expert in the column-wise layout
   bool valid;
 };
@@ -50,7 +51,7 @@ struct TileInfo {
 // Tiles are enumerated expert by expert; inside an expert the output-column tile runs fastest so
 // that consecutive workgroups share A rows.  Wave 0 computes the per-expert tile counts and their
 // prefix sums in LDS, then every thread binary-searches its tile.
-__device__ TileInfo decode_tile(int mode, const GemmArgs& p, int32_t* pre, int64_t* rowstart) {
+__device__ TileInfo decode_tile(int mode, int wblk, const GemmArgs& p, int32_t* pre, int64_t* rowstart) {
   const int G = p.G;
   const int64_t M = p.M;
   const int nt_count = (int)((mode == kFwd ? p.N : p.K) / BN);
@@ -68,7 +69,7 @@ __device__ TileInfo decode_tile(int mode, const GemmArgs& p, int32_t* pre, int64
       if (g < G) {
         int64_t o1 = clamp_off(p.offs[g + 1], M);
         int64_t m = o1 > o0 ? o1 - o0 : 0;
-        if (mode == kWgrad) cnt = (int32_t)((m + 31) / 32);   // contraction blocks (prefix -> c_g)
+        if (mode == kWgrad) cnt = (int32_t)((m + wblk - 1) / wblk);   // contraction blocks (prefix -> c_g)
         else cnt = (int32_t)((m + BM - 1) / BM) * nt_count;
       }
       int32_t incl = cnt;
@@ -98,9 +99,9 @@ __device__ TileInfo decode_tile(int mode, const GemmArgs& p, int32_t* pre, int64
     ti.g = g;
     ti.mt = lt / ntc;
     ti.nt = lt % ntc;
-    ti.col0 = 32 * (int64_t)pre[g];
+    ti.col0 = (int64_t)wblk * pre[g];
     int64_t o0 = rowstart[g], o1 = rowstart[g + 1];
-    ti.nblk = o1 > o0 ? (int)((o1 - o0 + 31) / 32) : 0;
+    ti.nblk = o1 > o0 ? (int)((o1 - o0 + wblk - 1) / wblk) : 0;
     ti.row0 = o0;
     ti.rows = (int)(o1 > o0 ? o1 - o0 : 0);   // contraction length m_g
     ti.valid = true;
@@ -148,19 +149,20 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const TileInfo& ti,
   // A rows: forward/dgrad -> token rows (clamped to the expert's last row); wgrad -> n rows
   // B rows: forward -> gN + j; dgrad -> k rows of W^c (column offset gN); wgrad -> k rows (col c_g)
   int64_t a_col0 = 0, b_col0 = 0;
+  constexpr int WBLK = BW ? 128 : 32;   // wgrad contraction block
   int64_t L;   // contraction length in bytes (multiple of 128 for forward/dgrad)
   if (MODE == kFwd) L = p.K;
   else if (MODE == kDgrad) L = p.N;
-  else L = 32 * (int64_t)ti.nblk;
+  else L = (int64_t)WBLK * ti.nblk;
   if (MODE == kDgrad) b_col0 = (int64_t)ti.g * p.N;
   int nblk = ti.nblk;
   if (MODE == kWgrad) {
     a_col0 = ti.col0;
     b_col0 = ti.col0;
     // offsets that are not monotone could place an expert past the leading dimension: clip
-    const int64_t room = p.lda > a_col0 ? (p.lda - a_col0) / 32 : 0;
+    const int64_t room = p.lda > a_col0 ? (p.lda - a_col0) / WBLK : 0;
     if (nblk > room) nblk = (int)room;
-    L = 32 * (int64_t)nblk;
+    L = (int64_t)WBLK * nblk;
   }
   const int nsteps = (int)((L + BK - 1) / BK);
 
@@ -207,8 +209,9 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const TileInfo& ti,
       rb[j] = ok ? *(const uint4*)(b_ptr[j] + koff) : make_uint4(0, 0, 0, 0);
     }
     if (BW) {
+      // A row scales; wgrad also B row scales (forward / dgrad read the B block scale per tile)
       const float* sp = (const float*)(s_is_a ? p.sa : p.sb);
-      if (s_is_a) rs = __float_as_uint(sp[s_row * s_ld + s_col0 + ks]);
+      if (s_is_a || MODE == kWgrad) rs = __float_as_uint(sp[s_row * s_ld + s_col0 + ks]);
     } else {
       const uint8_t* sp = (const uint8_t*)(s_is_a ? p.sa : p.sb) + s_row * s_ld + s_col0 + (int64_t)ks * 4;
       uint32_t v = 0;
@@ -229,7 +232,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const TileInfo& ti,
       *(uint4*)(ldsB + lds_off(r, ld_ch)) = rb[j];
     }
     if (s_is_a) ldsSA[s_r] = rs;
-    else if (!BW) ldsSB[s_r] = rs;
+    else if (!BW || MODE == kWgrad) ldsSB[s_r] = rs;
   };
 
   v4f acc[4][4];
@@ -246,18 +249,21 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const TileInfo& ti,
     if (ks + 1 < nsteps) load_step(ks + 1);
 
     // blockwise: fp32 weight-block scale of this step (one per 128x128 block)
-    float sbw = 0.f;
-    float rsc[4][4];
+    float sbw = 1.f;
+    float rsc[4][4], csc[4];
     if (BW) {
       const float* sw = (const float*)p.sb;
       if (MODE == kFwd) sbw = sw[(((int64_t)ti.g * p.N + (int64_t)ti.nt * BN) / 128) * p.ldsb + ks];
-      else sbw = sw[(((int64_t)ti.g * p.N) / 128 + ks) * p.ldsb + ti.nt];
-      // promotion factors of the lane's four output rows per A fragment
+      else if (MODE == kDgrad) sbw = sw[(((int64_t)ti.g * p.N) / 128 + ks) * p.ldsb + ti.nt];
+      // promotion factors of the lane's four output rows per A fragment (times the weight-block scale)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int q = 0; q < 4; ++q)
           rsc[i][q] = __uint_as_float(ldsSA[wm * 64 + i * 16 + 4 * fg + q]) * sbw;
+      // wgrad: the lane's output column of each B fragment has its own scale (the X row scale)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) csc[j] = MODE == kWgrad ? __uint_as_float(ldsSB[wn * 64 + j * 16 + fr]) : 1.f;
     }
 
     if (FEED == kFeedPrecise) {
@@ -302,7 +308,10 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const TileInfo& ti,
 #pragma unroll
           for (int j = 0; j < 4; ++j)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) acc[i][j][q] = __builtin_fmaf(part[i][j][q], rsc[i][q], acc[i][j][q]);
+            for (int q = 0; q < 4; ++q) {
+              const float f = MODE == kWgrad ? rsc[i][q] * csc[j] : rsc[i][q];
+              acc[i][j][q] = __builtin_fmaf(part[i][j][q], f, acc[i][j][q]);
+            }
       }
     } else {
       // full-rate block-scaled FP8 MFMA, K = 128 per instruction
@@ -333,7 +342,10 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const TileInfo& ti,
             const v4f part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[i], bf[j], v4f{0.f, 0.f, 0.f, 0.f},
                                                                               0, 0, 0, 127, 0, 127);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) acc[i][j][q] = __builtin_fmaf(part[q], rsc[i][q], acc[i][j][q]);
+            for (int q = 0; q < 4; ++q) {
+              const float f = MODE == kWgrad ? rsc[i][q] * csc[j] : rsc[i][q];
+              acc[i][j][q] = __builtin_fmaf(part[q], f, acc[i][j][q]);
+            }
           }
       } else {
 #pragma unroll
@@ -378,7 +390,7 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_kernel(GemmArgs p) {
   __shared__ __attribute__((aligned(16))) uint8_t ldsB[BN * BK];
   __shared__ uint32_t ldsSA[BM];
   __shared__ uint32_t ldsSB[BN];
-  const TileInfo ti = decode_tile(MODE, p, pre, rowstart);
+  const TileInfo ti = decode_tile(MODE, BW ? 128 : 32, p, pre, rowstart);
   if (!ti.valid) return;   // uniform across the workgroup
   gemm_tile<MODE, BW, FEED>(p, ti, ldsA, ldsB, ldsSA, ldsSB);
 }
@@ -400,7 +412,8 @@ hipError_t launch_bw_gemm(int mode, const GemmArgs& p, hipStream_t st) {
   if (tiles == 0) return hipSuccess;
   dim3 grid((unsigned)tiles), block(kThreads);
   if (mode == kFwd) launch_feed<kFwd, true>(p, grid, block, st);
-  else launch_feed<kDgrad, true>(p, grid, block, st);
+  else if (mode == kDgrad) launch_feed<kDgrad, true>(p, grid, block, st);
+  else launch_feed<kWgrad, true>(p, grid, block, st);
   return hipGetLastError();
 }
 

@@ -122,4 +122,118 @@ hipError_t launch_bw_weight(const uint16_t* w, int64_t R, int64_t C, uint8_t* q,
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------------------------
+// Column-wise blockwise quantiser (the weight-gradient operands of the blockwise recipe): blocks of
+// 128 consecutive rows of one column, restarting at every expert's first row, one fp32 scale per
+// (column, block).  Output qT [C, ld], sT [C, ld/128]: expert g's rows at columns
+// [128 starts[g], 128 starts[g] + m_g), a short last block padded with zero codes, block-columns of
+// no expert all zero (codes and scale).
+//
+// A workgroup (256 lanes) takes one block-column and a window of 128 input columns: the block's rows
+// come into LDS as 16-byte row pieces; lane t then owns columns 2 (t % 64), +1 and rows
+// 32 (t / 64) .. +31, reduces its column pair's amax (combined over the four row quarters through
+// LDS), converts, and leaves 32 code bytes per column in an LDS output tile that is written out as
+// 128-byte rows of qT.
+// ---------------------------------------------------------------------------------------------
+constexpr int kBwColPitch = 128 + 16;   // LDS bytes per output (qT) row, padded against bank conflicts
+constexpr int kBwMaxGroupsLds = 1024;
+
+__global__ __launch_bounds__(256) void bw_colwise_kernel(const uint16_t* __restrict__ x, int64_t R, int64_t C,
+                                                         const int32_t* __restrict__ offs, int G,
+                                                         uint8_t* __restrict__ qT, float* __restrict__ sT,
+                                                         int64_t ld) {
+  __shared__ int32_t starts[kBwMaxGroupsLds + 1];
+  __shared__ int32_t rows0[kBwMaxGroupsLds + 1];
+  __shared__ __attribute__((aligned(16))) uint8_t tile[128 * 256];        // 128 rows x 128 bf16
+  __shared__ __attribute__((aligned(16))) uint8_t outq[128 * kBwColPitch];
+  __shared__ uint32_t red[4][64];
+  __shared__ int32_t blk[2];
+
+  const int nwin = (int)(C / 128);
+  const int win = blockIdx.x % nwin;
+  const int bc = blockIdx.x / nwin;
+  const int nbc = (int)(ld / 128);
+  const int t = threadIdx.x;
+  group_block_starts<128>(offs, G, R, starts, rows0);
+  __syncthreads();
+  if (t == 0) {
+    int32_t r0, n;
+    block_rows<128>(bc, nbc, G, starts, rows0, r0, n);
+    blk[0] = r0;
+    blk[1] = n;
+  }
+  __syncthreads();
+  const int r0 = blk[0], n = blk[1];
+  const int64_t cbase = (int64_t)win * 128;
+
+  // the block's rows (zeros past n) into LDS: 16 pieces of 16 bytes per row
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int c = t + 256 * i;
+    const int row = c >> 4, ch = c & 15;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (row < n) v = *(const uint4*)(x + ((int64_t)r0 + row) * C + cbase + 8 * ch);
+    *(uint4*)(tile + row * 256 + 16 * ch) = v;
+  }
+  __syncthreads();
+
+  const int cp = t & 63, qq = t >> 6;
+  uint32_t w[32];
+  uint32_t m0 = 0, m1 = 0;
+#pragma unroll
+  for (int r = 0; r < 32; ++r) {
+    w[r] = *(const uint32_t*)(tile + (32 * qq + r) * 256 + 4 * cp);
+    m0 = max(m0, w[r] & 0x7FFFu);
+    m1 = max(m1, (w[r] >> 16) & 0x7FFFu);
+  }
+  red[qq][cp] = m0 | (m1 << 16);
+  __syncthreads();
+  uint32_t a0 = 0, a1 = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    a0 = max(a0, red[k][cp] & 0xFFFFu);
+    a1 = max(a1, red[k][cp] >> 16);
+  }
+  const float s0 = bw_scale_from_amax_bits(a0), s1 = bw_scale_from_amax_bits(a1);
+  uint32_t o0[8], o1[8];
+#pragma unroll
+  for (int d = 0; d < 8; ++d) {
+    o0[d] = cvt4_f32_e4m3(__fdiv_rn(bf16_lo(w[4 * d]), s0), __fdiv_rn(bf16_lo(w[4 * d + 1]), s0),
+                          __fdiv_rn(bf16_lo(w[4 * d + 2]), s0), __fdiv_rn(bf16_lo(w[4 * d + 3]), s0));
+    o1[d] = cvt4_f32_e4m3(__fdiv_rn(bf16_hi(w[4 * d]), s1), __fdiv_rn(bf16_hi(w[4 * d + 1]), s1),
+                          __fdiv_rn(bf16_hi(w[4 * d + 2]), s1), __fdiv_rn(bf16_hi(w[4 * d + 3]), s1));
+  }
+  uint4* d0 = (uint4*)(outq + (2 * cp) * kBwColPitch + 32 * qq);
+  uint4* d1 = (uint4*)(outq + (2 * cp + 1) * kBwColPitch + 32 * qq);
+  d0[0] = make_uint4(o0[0], o0[1], o0[2], o0[3]);
+  d0[1] = make_uint4(o0[4], o0[5], o0[6], o0[7]);
+  d1[0] = make_uint4(o1[0], o1[1], o1[2], o1[3]);
+  d1[1] = make_uint4(o1[4], o1[5], o1[6], o1[7]);
+  if (qq == 0) {
+    // a block-column of no expert keeps scale 0; a real all-zero block gets 1
+    const int64_t srow = (int64_t)nbc;
+    sT[(cbase + 2 * cp) * srow + bc] = n > 0 ? s0 : 0.0f;
+    sT[(cbase + 2 * cp + 1) * srow + bc] = n > 0 ? s1 : 0.0f;
+  }
+  __syncthreads();
+  // qT rows cbase .. cbase + 127, bytes [128 bc, 128 bc + 128): 8 lanes x 16 bytes per row
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = t + 256 * i;
+    const int row = c >> 3, piece = c & 7;
+    *(uint4*)(qT + (cbase + row) * ld + (int64_t)bc * 128 + 16 * piece) =
+        *(const uint4*)(outq + row * kBwColPitch + 16 * piece);
+  }
+}
+
+hipError_t launch_bw_colwise(const uint16_t* x, int64_t R, int64_t C, const int32_t* offs, int32_t G, uint8_t* qT,
+                             float* sT, int64_t ld, hipStream_t st) {
+  const int64_t nwg = (ld / 128) * (C / 128);
+  if (nwg == 0) return hipSuccess;
+  if (nwg > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(bw_colwise_kernel, dim3((unsigned)nwg), dim3(256), 0, st, x, R, C, offs, offs ? G : 1, qT, sT,
+                     ld);
+  return hipGetLastError();
+}
+
 }  // namespace mxmoe

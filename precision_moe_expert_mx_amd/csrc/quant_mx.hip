@@ -101,38 +101,6 @@ constexpr int kColWinRun = 8;                      // column windows visited tog
 constexpr int kRowBlks = kColCols / 32;            // row-wise 32-column blocks per window
 constexpr int kMaxGroupsLds = 1024;                // largest G the column-wise quantiser accepts
 
-__device__ __forceinline__ void group_block_starts(const int32_t* offs, int G, int64_t R, int32_t* starts,
-                                                   int32_t* rows0) {
-  // starts[g] = sum_{h<g} ceil(m_h/32) for g = 0..G (wave 0 scans 64 groups per step); rows0[g] = offs[g]
-  if (threadIdx.x < 64) {
-    int lane = threadIdx.x;
-    int32_t carry = 0;
-    for (int g0 = 0; g0 <= G; g0 += 64) {
-      int g = g0 + lane;
-      int32_t nb = 0;
-      int64_t o0 = 0;
-      if (g <= G) {
-        o0 = offs ? clamp_off(offs[g], R) : (g == 0 ? 0 : R);
-        rows0[g] = (int32_t)o0;
-      }
-      if (g < G) {
-        int64_t o1 = offs ? clamp_off(offs[g + 1], R) : R;
-        int64_t m = o1 > o0 ? o1 - o0 : 0;
-        nb = (int32_t)((m + 31) / 32);
-      }
-      // inclusive scan of nb across the wave
-      int32_t incl = nb;
-#pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        int32_t t = __shfl_up(incl, d, 64);
-        if (lane >= d) incl += t;
-      }
-      if (g <= G) starts[g] = carry + incl - nb;    // exclusive
-      carry += __shfl(incl, 63, 64);
-    }
-  }
-}
-
 // Magnitude maximum of four bf16 (two dwords), as a bf16 bit pattern.
 __device__ __forceinline__ uint32_t mag_max4(uint32_t w0, uint32_t w1) {
   typedef unsigned short v2us __attribute__((ext_vector_type(2)));
@@ -337,25 +305,14 @@ __global__ __launch_bounds__(kColThreads) void mx_colwise_kernel(const uint16_t*
   const int bc0 = (inchunk / cw_here) * kColBlk;
   const int t = threadIdx.x;
   if (offs) {
-    group_block_starts(offs, G, R, starts, rows0);
+    group_block_starts<32>(offs, G, R, starts, rows0);
     __syncthreads();
   }
   if (t < kColBlk) {
     const int bc = bc0 + t;
     int32_t r0 = 0, n = 0;
     if (offs) {
-      if (bc < nbc && bc < starts[G]) {
-        // last group g with starts[g] <= bc (empty groups share their start with the next group)
-        int lo = 0, hi = G - 1;
-        while (lo < hi) {
-          const int mid = (lo + hi + 1) >> 1;
-          if (starts[mid] <= bc) lo = mid; else hi = mid - 1;
-        }
-        const int64_t g0 = rows0[lo], g1 = rows0[lo + 1];
-        r0 = (int32_t)(g0 + 32 * (int64_t)(bc - starts[lo]));
-        const int64_t left = g1 - r0;
-        n = (int32_t)(left < 32 ? left : 32);
-      }
+      block_rows<32>(bc, nbc, G, starts, rows0, r0, n);
     } else if (bc < nbc) {
       // one group of R rows
       r0 = 32 * bc;

@@ -40,6 +40,9 @@ def test_host_helpers():
     assert [m.mx_colwise_ld_min(M, G) for M, G in ((1024, 4), (49152, 64), (65536, 8), (32768, 16))] == \
         [1152, 51136, 65792, 33280]
     assert m.mx_colwise_ld_min(-1, 4) == -1 and m.mx_colwise_ld_min(10, 0) == -1
+    assert [m.fp8bw_colwise_ld_min(M, G) for M, G in ((1024, 4), (49152, 64), (65536, 8))] == \
+        [1536, 57344, 66560]
+    assert m.fp8bw_colwise_ld_min(-1, 4) == -1 and m.fp8bw_colwise_ld_min(10, 0) == -1
 
 
 A16 = 0x10000      # fake, 16-byte aligned device addresses: never dereferenced on error paths
@@ -70,6 +73,11 @@ def test_quantiser_argument_errors():
     assert _status(L, "fp8bw_quantize_act_1x128", A16, 4, 96, A16, A16, None)[0] == 2
     assert _status(L, "fp8bw_quantize_weight_128x128", A16, 100, 128, A16, A16, None, None)[0] == 2
     assert _status(L, "fp8bw_quantize_weight_128x128", A16, 128, 128, A16, A16, BAD, None)[0] == 3
+    # blockwise column-wise: C % 128, ld % 128, ld too small
+    assert _status(L, "fp8bw_quantize_colwise_128", A16, 100, 96, A16, 4, A16, A16, 640, None)[0] == 2
+    assert _status(L, "fp8bw_quantize_colwise_128", A16, 100, 128, A16, 4, A16, A16, 600, None)[0] == 3
+    assert _status(L, "fp8bw_quantize_colwise_128", A16, 100, 128, A16, 4, A16, A16, 512, None)[0] == 2
+    assert _status(L, "fp8bw_quantize_colwise_128", A16, 200, 128, None, 0, A16, A16, 128, None)[0] == 2   # one group
 
 
 def test_gemm_argument_errors():
@@ -98,6 +106,11 @@ def test_gemm_argument_errors():
     a = list(ok_args); a[8] = 200
     assert _status(L, "fp8bw_grouped_gemm_fwd", *a)[0] == 2
     assert _status(L, "mxmoe_check_offsets", A16, 0, 10, None)[0] == 2
+    # blockwise wgrad: ld not a multiple of 128 / below fp8bw_colwise_ld_min
+    st, msg = _status(L, "fp8bw_grouped_gemm_wgrad", A16, A16, A16b, A16b, 1184, A16, 4, 1024, 512, 256, A16, 0, None)
+    assert st == 2 and "ld" in msg
+    assert _status(L, "fp8bw_grouped_gemm_wgrad", A16, A16, A16b, A16b, 1408, A16, 4, 1024, 512, 256, A16, 0,
+                   None)[0] == 2
 
 
 def test_binding_refuses_cpu_tensors():

@@ -279,3 +279,47 @@ def test_per_block_scales_over_a_wide_range(fast):
     L = Layer(offs, _block_scaled_bf16(rng, (M, K), 0), _block_scaled_bf16(rng, (G * N, K), 0),
               _block_scaled_bf16(rng, (M, N), 0), N, K)
     print(run_layer(m, L, check=("dgrad", "wgrad"), fast=fast))
+
+
+def _bw_wgrad_case(m, L, dt, groups=None, n_idx=None, k_idx=None):
+    ld = oracle.bw_colwise_ld_min(L.M, L.G)
+    offs = dev(L.offs)
+    qd, sd = m.fp8bw_quantize_colwise_128(dev(L.dy), offs, ld=ld)
+    qx, sx = m.fp8bw_quantize_colwise_128(dev(L.x), offs, ld=ld)
+    dw = m.fp8bw_grouped_gemm_wgrad(qd, sd, qx, sx, offs, L.M, dt)
+    ref, bnd = oracle.bw_gemm_wgrad(host(qd), host(sd), host(qx), host(sx), L.offs, L.N, L.K,
+                                    groups=groups, n_idx=n_idx, k_idx=k_idx)
+    got = _gpu_out(dw)
+    if groups is not None:
+        got = got[np.ix_(groups, n_idx, k_idx)]
+    return _check(got, ref, bnd, dt, f"bw wgrad {dt}")
+
+
+def test_blockwise_wgrad():
+    """Blockwise wgrad (128-token blocks promoted with the dY and X row scales) on ragged experts,
+    including empty ones (zero gradient written), fp32 and bf16 outputs."""
+    m = require_gpu()
+    rng = np.random.default_rng(38)
+    for sizes, N, K in (([0, 5, 130, 1, 300], 256, 384), ([129, 0, 0, 17], 128, 256)):
+        L = _rand_layer(rng, sizes, N, K, outliers=0.001)
+        for dt in ("f32", "bf16"):
+            print("bw wgrad", sizes, dt, _bw_wgrad_case(m, L, dt))
+    # no routed rows at all: every dW_g is written as zero
+    ld = oracle.bw_colwise_ld_min(0, 2)
+    offs = dev(np.zeros(3, np.int32))
+    qd, sd = m.fp8bw_quantize_colwise_128(dev(np.zeros((1, 128), np.uint16))[:0], offs, ld=ld)
+    dw = m.fp8bw_grouped_gemm_wgrad(qd, sd, qd, sd, offs, 0, "f32", dw=torch.full((2, 128, 128), 7.0, device="cuda"))
+    assert not host(dw).any()
+
+
+def test_blockwise_wgrad_full_size_sampled():
+    """DeepSeek-V3-16B layer tensors (64 experts): the full launches, sampled experts and n / k."""
+    m = require_gpu()
+    wl = make_workload("dsv3_16b_blockwise")
+    rng = np.random.default_rng(39)
+    for lay in wl.layers:
+        groups = np.unique(np.concatenate([[0, lay.G - 1], rng.choice(lay.G, 4, replace=False)]))
+        n_idx = np.unique(np.concatenate([[0, lay.N - 1], rng.choice(lay.N, 24, replace=False)]))
+        k_idx = np.unique(np.concatenate([[0, lay.K - 1], rng.choice(lay.K, 24, replace=False)]))
+        print(lay.name, "bw wgrad", _bw_wgrad_case(m, lay, "f32", groups, n_idx, k_idx))
+        torch.cuda.empty_cache()

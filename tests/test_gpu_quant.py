@@ -227,3 +227,27 @@ def test_dual_full_size_sampled():
     cols = np.concatenate([[0, lay.K - 1], rng.choice(lay.K, 40, replace=False)])
     qo, so = oracle.mx_quantize_colwise(np.ascontiguousarray(lay.x[:, cols]), lay.offs, ld)
     assert np.array_equal(host(qT[cols]), qo) and np.array_equal(host(sT[cols]), so)
+
+
+def test_blockwise_colwise_ragged_groups():
+    """128-token column-wise blockwise copies (the blockwise wgrad operands): codes and fp32 scales
+    bit-exact, ragged experts (empty, 1, 5, 130, 300 rows), extra tail columns, one group."""
+    m = require_gpu()
+    rng = np.random.default_rng(29)
+    sizes = [0, 5, 130, 1, 300, 128, 0]
+    offs = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    M = int(offs[-1])
+    for C in (128, 384):
+        x = random_bf16(rng, (M, C), outlier_frac=0.01, outlier_mult=1000.0)
+        x[5:135, :128] = 0                      # an all-zero block: scale 1, zero codes
+        for extra in (0, 128):
+            ld = oracle.bw_colwise_ld_min(M, len(sizes)) + extra
+            qT, sT = m.fp8bw_quantize_colwise_128(dev(x), dev(offs), ld=ld)
+            qo, so = oracle.bw_quantize_colwise_128(x, offs, ld)
+            assert np.array_equal(host(sT), so), f"scale mismatch at {np.argwhere(host(sT) != so)[:5]}"
+            assert np.array_equal(host(qT), qo), f"code mismatch at {np.argwhere(host(qT) != qo)[:5]}"
+    x = random_bf16(rng, (300, 256))
+    ld1 = oracle.bw_colwise_ld_min(300, 1)           # 512: admissible for the oracle's offsets form too
+    qT, sT = m.fp8bw_quantize_colwise_128(dev(x), None, ld=ld1)
+    qo, so = oracle.bw_quantize_colwise_128(x, np.array([0, 300]), ld1)
+    assert np.array_equal(host(qT), qo) and np.array_equal(host(sT), so)
