@@ -129,11 +129,11 @@ hipError_t launch_bw_weight(const uint16_t* w, int64_t R, int64_t C, uint8_t* q,
 // [128 starts[g], 128 starts[g] + m_g), a short last block padded with zero codes, block-columns of
 // no expert all zero (codes and scale).
 //
-// A workgroup (256 lanes) takes one block-column and a window of 128 input columns: the block's rows
-// come into LDS as 16-byte row pieces; lane t then owns columns 2 (t % 64), +1 and rows
-// 32 (t / 64) .. +31, reduces its column pair's amax (combined over the four row quarters through
-// LDS), converts, and leaves 32 code bytes per column in an LDS output tile that is written out as
-// 128-byte rows of qT.
+// A workgroup (256 lanes) takes one block-column and a window of 128 input columns.  Lane t owns
+// columns 2 (t % 64), +1 and rows 32 (t / 64) .. +31 of the block, loaded straight into registers as
+// one dword per row (a wave reads 256 contiguous bytes of a row); the column pair's amax is combined
+// over the four row quarters through LDS, and the lane's 32 code bytes per column go to an LDS
+// output tile that is written out as 128-byte rows of qT.
 // ---------------------------------------------------------------------------------------------
 constexpr int kBwColPitch = 128 + 16;   // LDS bytes per output (qT) row, padded against bank conflicts
 constexpr int kBwMaxGroupsLds = 1024;
@@ -144,7 +144,6 @@ __global__ __launch_bounds__(256) void bw_colwise_kernel(const uint16_t* __restr
                                                          int64_t ld) {
   __shared__ int32_t starts[kBwMaxGroupsLds + 1];
   __shared__ int32_t rows0[kBwMaxGroupsLds + 1];
-  __shared__ __attribute__((aligned(16))) uint8_t tile[128 * 256];        // 128 rows x 128 bf16
   __shared__ __attribute__((aligned(16))) uint8_t outq[128 * kBwColPitch];
   __shared__ uint32_t red[4][64];
   __shared__ int32_t blk[2];
@@ -166,23 +165,16 @@ __global__ __launch_bounds__(256) void bw_colwise_kernel(const uint16_t* __restr
   const int r0 = blk[0], n = blk[1];
   const int64_t cbase = (int64_t)win * 128;
 
-  // the block's rows (zeros past n) into LDS: 16 pieces of 16 bytes per row
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int c = t + 256 * i;
-    const int row = c >> 4, ch = c & 15;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (row < n) v = *(const uint4*)(x + ((int64_t)r0 + row) * C + cbase + 8 * ch);
-    *(uint4*)(tile + row * 256 + 16 * ch) = v;
-  }
-  __syncthreads();
-
   const int cp = t & 63, qq = t >> 6;
+  // the lane's column pair in rows 32 qq .. 32 qq + 31 of the block (zeros past n); row addresses are
+  // wave-uniform
   uint32_t w[32];
   uint32_t m0 = 0, m1 = 0;
+  const int nq = n - 32 * qq;       // rows of this quarter inside the block
+  const uint16_t* src = x + ((int64_t)r0 + 32 * qq) * C + cbase + 2 * cp;
 #pragma unroll
   for (int r = 0; r < 32; ++r) {
-    w[r] = *(const uint32_t*)(tile + (32 * qq + r) * 256 + 4 * cp);
+    w[r] = r < nq ? *(const uint32_t*)(src + (int64_t)r * C) : 0u;
     m0 = max(m0, w[r] & 0x7FFFu);
     m1 = max(m1, (w[r] >> 16) & 0x7FFFu);
   }
