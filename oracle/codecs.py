@@ -97,3 +97,75 @@ def e8m0_decode(b) -> np.ndarray:
     """Value of E8M0 scale bytes: 2^(b - 127) for b in [0, 254]; 0xFF is NaN."""
     b = np.asarray(b).astype(np.int64)
     return np.where(b == 0xFF, np.nan, np.ldexp(1.0, (b - 127).astype(np.int64)))
+
+
+# ----------------------------------------------------------------------------------------- E2M1 (FP4)
+# OCP MX v1.0, FP4 element "E2M1": sign, 2 exponent bits (bias 1), 1 mantissa bit; no infinity or NaN;
+# largest magnitude 6.  The pages only announce a 4-bit format as the next step (iitak.ru article,
+# closing section); MXFP4 is that format on the MX scale of E8M0 per 32 elements.
+E2M1_MAX = 6.0
+
+
+def e2m1_decode(codes) -> np.ndarray:
+    """Value of E2M1 codes (0..15):
+      E == 0 : (-1)^s * m * 0.5             (0x0 / 0x8 are +-0, 0x1 = 0.5)
+      E >  0 : (-1)^s * (1 + m/2) * 2^(E-1)  (1, 1.5, 2, 3, 4, 6)
+    """
+    c = np.asarray(codes).astype(np.int64)
+    s = (c >> 3) & 1
+    e = (c >> 1) & 0x3
+    m = c & 0x1
+    mag = np.where(e == 0, m * 0.5, (1.0 + m / 2.0) * np.exp2(e - 1.0))
+    return np.where(s == 1, -mag, mag)
+
+
+_POS4 = e2m1_decode(np.arange(8))
+
+
+def e2m1_encode(y) -> np.ndarray:
+    """Round finite reals to E2M1: nearest, ties to even, saturating at +-6 (same readings as E4M3:
+    the pages are silent).  Below 2^(e+1) with e >= 0 the representable magnitudes are the multiples
+    of 2^(e-1), so |y| is divided by that quantum, rounded half-to-even and multiplied back."""
+    y = np.asarray(y, dtype=np.float64)
+    if not np.all(np.isfinite(y)):
+        raise ValueError("e2m1_encode: non-finite input is outside the contract")
+    a = np.abs(y)
+    _, ex = np.frexp(a)
+    e = np.maximum(ex - 1, 0)
+    quantum = np.ldexp(1.0, e - 1)
+    r = np.minimum(np.rint(a / quantum) * quantum, E2M1_MAX)
+    code = np.searchsorted(_POS4, r)
+    if not np.array_equal(_POS4[np.minimum(code, 7)], r):
+        raise AssertionError("e2m1_encode: rounded value not representable")
+    sign = np.where(np.signbit(y), 0x8, 0)
+    return (code | sign).astype(np.uint8)
+
+
+def e2m1_encode_bruteforce(y) -> np.ndarray:
+    """Independent encoder: the nearest of the 8 magnitudes (|y| clamped to 6), ties to the code with
+    an even mantissa bit."""
+    y = np.asarray(y, dtype=np.float64).reshape(-1)
+    out = np.empty(y.shape, dtype=np.uint8)
+    for i, v in enumerate(y):
+        a = min(abs(float(v)), E2M1_MAX)
+        d = np.abs(_POS4 - a)
+        best = [c for c in np.flatnonzero(d == d.min())]
+        if len(best) > 1:
+            best = [c for c in best if (c & 1) == 0]
+        out[i] = int(best[0]) | (0x8 if np.signbit(v) else 0)
+    return out
+
+
+def fp4_pack(codes) -> np.ndarray:
+    """Pack E2M1 codes along the last axis, two per byte: element 2i in the low nibble, 2i+1 in the
+    high nibble (a layout choice: OCP MX leaves packing to the implementation)."""
+    c = np.asarray(codes, dtype=np.uint8)
+    return (c[..., 0::2] | (c[..., 1::2] << 4)).astype(np.uint8)
+
+
+def fp4_unpack(packed) -> np.ndarray:
+    p = np.asarray(packed, dtype=np.uint8)
+    out = np.empty(p.shape[:-1] + (2 * p.shape[-1],), dtype=np.uint8)
+    out[..., 0::2] = p & 0xF
+    out[..., 1::2] = p >> 4
+    return out

@@ -42,7 +42,7 @@ import numpy as np
 
 from .blockwise import TILE, bw_group_columns
 from .codecs import e4m3_decode
-from .mx import BLOCK, mx_dequantize, mx_group_columns
+from .mx import BLOCK, mx_dequantize, mx_group_columns, mxfp4_dequantize
 
 CHUNK = 4096
 REL_TOL = 1e-5
@@ -117,6 +117,50 @@ def mx_gemm_wgrad(qdyT, sdyT, qxT, sxT, offs, N, K, groups=None, n_idx=None, k_i
         sl = slice(c0 // BLOCK, c0 // BLOCK + nblk)
         A = mx_dequantize(qdyT[n_idx, c0:c0 + BLOCK * nblk], sdyT[n_idx, sl])[:, :m]
         B = mx_dequantize(qxT[k_idx, c0:c0 + BLOCK * nblk], sxT[k_idx, sl])[:, :m]
+        out[i] = A @ B.T
+        bound[i] = np.abs(A) @ np.abs(B).T
+    return out, bound
+
+
+# ---------------------------------------------------------------------------------- MXFP4 GEMMs
+# The same three products over MXFP4 operands (E2M1 codes packed two per byte along the contraction
+# axis, E8M0 per 32): packed column c covers elements 2c and 2c + 1.
+
+def mxfp4_gemm_fwd(qx, sx, qw, sw, offs, N, rows=None):
+    qx, sx, qw, sw = map(np.asarray, (qx, sx, qw, sw))
+    return _grouped_rows(
+        qx, sx, offs, rows,
+        lambda g: mxfp4_dequantize(qw[g * N:(g + 1) * N], sw[g * N:(g + 1) * N]),
+        N, lambda r: mxfp4_dequantize(qx[r], sx[r]))
+
+
+def mxfp4_gemm_dgrad(qdy, sdy, qwT, swT, offs, N, K, rows=None):
+    qdy, sdy, qwT, swT = map(np.asarray, (qdy, sdy, qwT, swT))
+    def b_of(g):
+        c = g * N
+        return mxfp4_dequantize(qwT[:K, c // 2:(c + N) // 2], swT[:K, c // BLOCK:(c + N) // BLOCK])
+    return _grouped_rows(qdy, sdy, offs, rows, b_of, K, lambda r: mxfp4_dequantize(qdy[r], sdy[r]))
+
+
+def mxfp4_gemm_wgrad(qdyT, sdyT, qxT, sxT, offs, N, K, groups=None, n_idx=None, k_idx=None):
+    qdyT, sdyT, qxT, sxT = map(np.asarray, (qdyT, sdyT, qxT, sxT))
+    offs = np.asarray(offs, dtype=np.int64)
+    G = len(offs) - 1
+    groups = np.arange(G) if groups is None else np.asarray(groups)
+    n_idx = np.arange(N) if n_idx is None else np.asarray(n_idx)
+    k_idx = np.arange(K) if k_idx is None else np.asarray(k_idx)
+    col0, nb = mx_group_columns(offs)
+    out = np.zeros((len(groups), len(n_idx), len(k_idx)))
+    bound = np.zeros_like(out)
+    for i, g in enumerate(groups):
+        m = int(offs[g + 1] - offs[g])
+        if m == 0:
+            continue
+        c0, nblk = int(col0[g]), int(nb[g])
+        sl = slice(c0 // BLOCK, c0 // BLOCK + nblk)
+        bs = slice(c0 // 2, (c0 + BLOCK * nblk) // 2)
+        A = mxfp4_dequantize(qdyT[n_idx, bs], sdyT[n_idx, sl])[:, :m]
+        B = mxfp4_dequantize(qxT[k_idx, bs], sxT[k_idx, sl])[:, :m]
         out[i] = A @ B.T
         bound[i] = np.abs(A) @ np.abs(B).T
     return out, bound

@@ -24,26 +24,29 @@ from __future__ import annotations
 
 import numpy as np
 
-from .codecs import bf16_bits_to_f64, e4m3_decode, e4m3_encode
+from .codecs import bf16_bits_to_f64, e2m1_decode, e2m1_encode, e4m3_decode, e4m3_encode, fp4_pack, fp4_unpack
 
 BLOCK = 32
 E4M3_EMAX = 8
+E2M1_EMAX = 2          # largest exponent of an E2M1 element: 6 = 1.5 * 2^2
 
 
-def mx_block_exponent(amax) -> np.ndarray:
-    """Shared exponent of blocks with the given amax (step 2 above)."""
+def mx_block_exponent(amax, emax: int = E4M3_EMAX) -> np.ndarray:
+    """Shared exponent of blocks with the given amax (step 2 above; emax is the element format's
+    largest exponent: 8 for E4M3, 2 for E2M1)."""
     amax = np.asarray(amax, dtype=np.float64)
     _, ex = np.frexp(amax)               # amax = f * 2^ex, f in [0.5, 1): floor(log2 amax) = ex - 1
-    e = (ex - 1) - E4M3_EMAX
+    e = (ex - 1) - emax
     e = np.where(amax == 0.0, -127, e)
     return np.clip(e, -127, 127).astype(np.int64)
 
 
-def _quantize_blocks(v: np.ndarray, axis: int):
-    """Quantise float64 values whose blocks run along `axis` (each block whole)."""
+def _quantize_blocks(v: np.ndarray, axis: int, fp4: bool = False):
+    """Quantise float64 values whose blocks run along `axis` (each block whole); E4M3 codes, or
+    E2M1 codes (unpacked, one per byte) with fp4."""
     amax = np.max(np.abs(v), axis=axis, keepdims=True)
-    e = mx_block_exponent(amax)
-    q = e4m3_encode(np.ldexp(v, -e))
+    e = mx_block_exponent(amax, E2M1_EMAX if fp4 else E4M3_EMAX)
+    q = (e2m1_encode if fp4 else e4m3_encode)(np.ldexp(v, -e))
     return q, (e + 127).astype(np.uint8)
 
 
@@ -154,3 +157,57 @@ def mx_quantize_dual(x_bits, offs, ld: int, row_idx=None):
     q, s = mx_quantize_rowwise(xr)
     qT, sT = mx_quantize_colwise(xr, offs, ld)
     return q, s, qT, sT
+
+
+# ------------------------------------------------------------------------------------------- MXFP4
+# The same block rule with E2M1 elements (OCP MX v1.0 "MXFP4"): e = floor(log2 amax) - 2, codes
+# E2M1(v * 2^-e) to nearest even, saturating at 6; two codes per byte (see codecs.fp4_pack).
+
+def mxfp4_quantize_rowwise(x_bits):
+    """bf16 [R, C] -> (q uint8 [R, C/2] packed E2M1, s uint8 [R, C/32])."""
+    x_bits = np.asarray(x_bits, dtype=np.uint16)
+    R, C = x_bits.shape
+    if C % BLOCK:
+        raise ValueError("C must be a multiple of 32")
+    v = bf16_bits_to_f64(x_bits).reshape(R, C // BLOCK, BLOCK)
+    q, s = _quantize_blocks(v, axis=2, fp4=True)
+    return fp4_pack(q.reshape(R, C)), s.reshape(R, C // BLOCK)
+
+
+def mxfp4_quantize_colwise(x_bits, offs, ld: int):
+    """Column-wise MXFP4 copy in the layout of mx_quantize_colwise, codes packed along ld:
+    qT uint8 [C, ld/2], sT uint8 [C, ld/32]; pads and the tail are zero."""
+    x_bits = np.asarray(x_bits, dtype=np.uint16)
+    R, C = x_bits.shape
+    if offs is None:
+        offs = np.array([0, R], dtype=np.int64)
+        need = BLOCK * (-(-R // BLOCK))
+    else:
+        offs = np.asarray(offs, dtype=np.int64)
+        need = mx_colwise_ld_min(R, len(offs) - 1)
+    if offs[0] != 0 or offs[-1] != R or np.any(np.diff(offs) < 0):
+        raise ValueError("bad offsets")
+    if ld % BLOCK or ld < need:
+        raise ValueError("bad ld")
+    codes = np.zeros((C, ld), dtype=np.uint8)
+    sT = np.zeros((C, ld // BLOCK), dtype=np.uint8)
+    col0, nb = mx_group_columns(offs)
+    for g in range(len(offs) - 1):
+        r0, r1 = int(offs[g]), int(offs[g + 1])
+        for b in range(int(nb[g])):
+            a = r0 + BLOCK * b
+            z = min(a + BLOCK, r1)
+            q, s = _quantize_blocks(bf16_bits_to_f64(x_bits[a:z, :]), axis=0, fp4=True)
+            c = int(col0[g]) + BLOCK * b
+            codes[:, c:c + (z - a)] = q.T
+            sT[:, c // BLOCK] = s[0]
+    return fp4_pack(codes), sT
+
+
+def mxfp4_dequantize(q, s) -> np.ndarray:
+    """Exact value of a packed MXFP4 array whose 32-blocks run along the last axis."""
+    v = e2m1_decode(fp4_unpack(q))
+    s = np.asarray(s).astype(np.int64)
+    if v.shape[-1] != s.shape[-1] * BLOCK:
+        raise ValueError("shape mismatch")
+    return v * np.repeat(np.ldexp(1.0, s - 127), BLOCK, axis=-1)
