@@ -34,7 +34,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
-MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "mxfp8": 5000.0}
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "mxfp8": 5000.0, "mxfp4": 10100.0}
 QUANT_BYTES_PER_ELEM = 2.0 + 1.0 + 1.0 / 32.0   # bf16 in, E4M3 out, one E8M0 per 32
 DUAL_BYTES_PER_ELEM = 2.0 + 2.0 * (1.0 + 1.0 / 32.0)   # bf16 in once, both MX layouts out
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_traffic_dsv3_671b_shard.txt")
@@ -270,6 +270,68 @@ def cpu_baseline(lay, rows_per_expert=2048):
 
 
 # ------------------------------------------------------------------------------------------- blockwise
+def mxfp4_leg(m, torch, wl, keep, steps=5, sample_rows=64):
+    """MXFP4 (E2M1 elements, E8M0 per 32, block-scaled FP4 MFMA) on the same expert-shard step: per
+    layer the six quantisers (row-wise X, W, dY; column-wise W, dY, X) and the three grouped GEMMs,
+    with the step's device inputs.  Accuracy: relative Frobenius error of Y and dX against an fp64
+    product of the original bf16 tensors on sampled rows."""
+    ops = []
+    bufs = []
+    fp4_bytes = 2.0 + 0.5 + 1.0 / 32.0            # bf16 in, half a byte out, one scale per 32
+    for lay, (dev_in, _) in zip(wl.layers, keep):
+        G, M, N, K = lay.G, lay.M, lay.N, lay.K
+        x, w, dy, offs = dev_in
+        w2 = w.view(G * N, K)
+        ld = m.mx_colwise_ld_min(M, G)
+        q = {}
+        bufs.append(q)
+        f = 2.0 * M * N * K
+        n = lay.name
+
+        def add(name, kind, fn, work):
+            ops.append(Op(f"{n}.{name}", kind, fn, work, ""))
+        add("quant_x", "quant", lambda q=q, x=x: q.update(x=m.mxfp4_quantize_rowwise(x)), M * K * fp4_bytes)
+        add("quant_w", "quant", lambda q=q, w2=w2: q.update(w=m.mxfp4_quantize_rowwise(w2)), G * N * K * fp4_bytes)
+        add("fwd", "gemm", lambda q=q, offs=offs, N=N: q.update(y=m.mxfp4_grouped_gemm_fwd(*q["x"], *q["w"], offs, N,
+                                                                                         "bf16")), f)
+        add("quant_dy", "quant", lambda q=q, dy=dy: q.update(dy=m.mxfp4_quantize_rowwise(dy)), M * N * fp4_bytes)
+        add("quant_w_col", "quant", lambda q=q, w2=w2, G=G, N=N: q.update(wc=m.mxfp4_quantize_colwise(w2, None,
+                                                                                                     ld=G * N)),
+            G * N * K * fp4_bytes)
+        add("dgrad", "gemm", lambda q=q, offs=offs, K=K: q.update(dx=m.mxfp4_grouped_gemm_dgrad(*q["dy"], *q["wc"], offs,
+                                                                                              K, "bf16")), f)
+        add("quant_dy_col", "quant", lambda q=q, dy=dy, offs=offs, ld=ld: q.update(dyc=m.mxfp4_quantize_colwise(
+            dy, offs, ld=ld)), M * N * fp4_bytes)
+        add("quant_x_col", "quant", lambda q=q, x=x, offs=offs, ld=ld: q.update(xc=m.mxfp4_quantize_colwise(
+            x, offs, ld=ld)), M * K * fp4_bytes)
+        add("wgrad", "gemm", lambda q=q, offs=offs, M=M: q.update(dw=m.mxfp4_grouped_gemm_wgrad(*q["dyc"], *q["xc"],
+                                                                                               offs, M, "f32")), f)
+    ms = time_ops(torch, ops, steps, 1)
+    flops = sum(o.work for o in ops if o.kind == "gemm")
+    gm = sum(float(np.mean(o.ms)) for o in ops if o.kind == "gemm")
+    out = {"ms_per_step": round(ms, 4), "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+           "gemm_tflops": round(flops / (gm * 1e-3) / 1e12, 1),
+           "gemm_frac_of_fp4_peak": round(flops / (gm * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS["mxfp4"], 4),
+           "ops": {o.name: op_summary(o) for o in ops}}
+    # accuracy of the gate+up layer on sampled rows
+    lay, q = wl.layers[0], bufs[0]
+    rng = np.random.default_rng(8)
+    rows = np.sort(rng.choice(lay.M, sample_rows, replace=False))
+    grp = np.searchsorted(lay.offs.astype(np.int64), rows, side="right") - 1
+    xb, dyb = bf16_to_f64(lay.x[rows]), bf16_to_f64(lay.dy[rows])
+    wf = lay.w.reshape(lay.G, lay.N, lay.K)
+    y_ref = np.stack([xb[i] @ bf16_to_f64(wf[g]).T for i, g in enumerate(grp)])
+    dx_ref = np.stack([dyb[i] @ bf16_to_f64(wf[g]) for i, g in enumerate(grp)])
+    ridx = torch.from_numpy(rows).cuda()
+    yg = q["y"][ridx].double().cpu().numpy()
+    dxg = q["dx"][ridx].double().cpu().numpy()
+    out["rel_fro_err_y"] = float(np.linalg.norm(yg - y_ref) / np.linalg.norm(y_ref))
+    out["rel_fro_err_dx"] = float(np.linalg.norm(dxg - dx_ref) / np.linalg.norm(dx_ref))
+    del ops, bufs
+    torch.cuda.empty_cache()
+    return out
+
+
 def blockwise_leg(m, torch, steps=5, sample_rows=256):
     """DeepSeek-style blockwise FP8 (1x128 activation tiles, 128x128 weight blocks, 128-token blocks
     for the weight gradient, fp32 scales, promotion every 128) against MXFP8 on the same
@@ -483,6 +545,7 @@ def main():
                                         "ops": {op.name: op_summary(op) for op in q_ops}}
         del sops, q_ops
         torch.cuda.empty_cache()
+        extra["mxfp4_step"] = mxfp4_leg(m, torch, wl, keep)
         del keep, ops
         torch.cuda.empty_cache()
         extra["blockwise_vs_mx"] = blockwise_leg(m, torch)

@@ -160,6 +160,40 @@ mxmoe_status mx_grouped_gemm_wgrad(const uint8_t* qdyT, const uint8_t* sdyT,
                                    const int32_t* offs, int32_t G, int64_t M, int64_t N, int64_t K,
                                    void* dw, mxmoe_dtype dwdt, void* stream);
 
+/* ---------------------------------------------------------------- MXFP4
+ * The MX scheme with E2M1 elements (OCP MX v1.0 "MXFP4": sign, 2 exponent bits,
+ * 1 mantissa bit, magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6): the pages announce a
+ * 4-bit format as the next step after MXFP8; on gfx950 the block-scaled MFMA runs
+ * it at twice the FP8 rate.  Scale e = floor(log2 amax) - 2 clamped to
+ * [-127, 127] (byte e + 127), codes E2M1(v * 2^-e) to nearest even, saturating
+ * at 6.  Codes are packed two per byte along the contraction axis, element 2i in
+ * the low nibble of byte i.  Layouts, offsets and errors as the E4M3 routines
+ * with byte counts halved: row-wise q [R, C/2], column-wise qT [C, ld/2]. */
+mxmoe_status mxfp4_quantize_rowwise(const void* x_bf16, int64_t R, int64_t C,
+                                    uint8_t* q, uint8_t* s, void* stream);
+mxmoe_status mxfp4_quantize_colwise(const void* x_bf16, int64_t R, int64_t C,
+                                    const int32_t* offs, int32_t G,
+                                    uint8_t* qT, uint8_t* sT, int64_t ld, void* stream);
+
+/* MXFP4 grouped GEMMs: the same products as mx_grouped_gemm_* over packed E2M1
+ * operands (from the mxfp4 quantisers; ldw and ld count elements, as for E4M3).
+ * They always use the block-scaled MFMA (E2M1 format): every E2M1 product is a
+ * multiple of 1/4 below 36 times its pair of scales, which the instruction sums
+ * exactly, so |err| <= 1e-5 * sum_k |a_k b_k| as for the precise E4M3 feed.
+ * N % 256 == 0 and K % 256 == 0. */
+mxmoe_status mxfp4_grouped_gemm_fwd(const uint8_t* qx, const uint8_t* sx,
+                                    const uint8_t* qw, const uint8_t* sw,
+                                    const int32_t* offs, int32_t G, int64_t M, int64_t N, int64_t K,
+                                    void* y, mxmoe_dtype ydt, void* stream);
+mxmoe_status mxfp4_grouped_gemm_dgrad(const uint8_t* qdy, const uint8_t* sdy,
+                                      const uint8_t* qwT, const uint8_t* swT, int64_t ldw,
+                                      const int32_t* offs, int32_t G, int64_t M, int64_t N, int64_t K,
+                                      void* dx, mxmoe_dtype dxdt, void* stream);
+mxmoe_status mxfp4_grouped_gemm_wgrad(const uint8_t* qdyT, const uint8_t* sdyT,
+                                      const uint8_t* qxT, const uint8_t* sxT, int64_t ld,
+                                      const int32_t* offs, int32_t G, int64_t M, int64_t N, int64_t K,
+                                      void* dw, mxmoe_dtype dwdt, void* stream);
+
 /* ---------------------------------------------------------------- blockwise FP8
  * The GEMMs take the same operand-feed flag and have the same accuracy as the
  * MX GEMMs.  Scale rule (a reading): s = fl32(amax / 448) by IEEE fp32 division, s = 1 for

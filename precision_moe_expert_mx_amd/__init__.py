@@ -21,6 +21,8 @@ __all__ = [
     "fp8bw_quantize_act_1x128", "fp8bw_quantize_weight_128x128",
     "fp8bw_grouped_gemm_fwd", "fp8bw_grouped_gemm_dgrad", "mxmoe_check_offsets",
     "fp8bw_colwise_ld_min", "fp8bw_quantize_colwise_128", "fp8bw_grouped_gemm_wgrad",
+    "mxfp4_quantize_rowwise", "mxfp4_quantize_colwise", "mxfp4_grouped_gemm_fwd", "mxfp4_grouped_gemm_dgrad",
+    "mxfp4_grouped_gemm_wgrad",
     "EXPORTED_SYMBOLS",
 ]
 
@@ -51,6 +53,13 @@ _SIGS = {
     "fp8bw_grouped_gemm_fwd": (ctypes.c_int, [_p, _p, _p, _p, _p, _i32, _i64, _i64, _i64, _p, ctypes.c_int, _p]),
     "fp8bw_grouped_gemm_dgrad": (ctypes.c_int, [_p, _p, _p, _p, _p, _i32, _i64, _i64, _i64, _p, ctypes.c_int, _p]),
     "fp8bw_colwise_ld_min": (_i64, [_i64, _i32]),
+    "mxfp4_quantize_rowwise": (ctypes.c_int, [_p, _i64, _i64, _p, _p, _p]),
+    "mxfp4_quantize_colwise": (ctypes.c_int, [_p, _i64, _i64, _p, _i32, _p, _p, _i64, _p]),
+    "mxfp4_grouped_gemm_fwd": (ctypes.c_int, [_p, _p, _p, _p, _p, _i32, _i64, _i64, _i64, _p, ctypes.c_int, _p]),
+    "mxfp4_grouped_gemm_dgrad": (ctypes.c_int, [_p, _p, _p, _p, _i64, _p, _i32, _i64, _i64, _i64, _p, ctypes.c_int,
+                                                _p]),
+    "mxfp4_grouped_gemm_wgrad": (ctypes.c_int, [_p, _p, _p, _p, _i64, _p, _i32, _i64, _i64, _i64, _p, ctypes.c_int,
+                                                _p]),
     "fp8bw_quantize_colwise_128": (ctypes.c_int, [_p, _i64, _i64, _p, _i32, _p, _p, _i64, _p]),
     "fp8bw_grouped_gemm_wgrad": (ctypes.c_int, [_p, _p, _p, _p, _i64, _p, _i32, _i64, _i64, _i64, _p, ctypes.c_int,
                                                 _p]),
@@ -228,6 +237,72 @@ def mx_grouped_gemm_wgrad(qdyT, sdyT, qxT, sxT, offs, M: int, out_dtype: str = "
     _check("mx_grouped_gemm_wgrad", lib().mx_grouped_gemm_wgrad(_ptr(qdyT), _ptr(sdyT), _ptr(qxT), _ptr(sxT), ld,
                                                                 _ptr(offs), G, M, N, K, _ptr(dw), cdt,
                                                                 _stream_handle(stream)))
+    return dw
+
+
+# ---------------------------------------------------------------- MXFP4
+def mxfp4_quantize_rowwise(x, q=None, s=None, stream=None):
+    """x bf16 [R, C] -> (q uint8 [R, C/2] packed E2M1, s uint8 [R, C/32])."""
+    torch = _torch()
+    x = _bf16_bits(x)
+    R, C = x.shape
+    q = _empty((R, C // 2), torch.uint8, x) if q is None else q
+    s = _empty((R, C // 32), torch.uint8, x) if s is None else s
+    _check("mxfp4_quantize_rowwise", lib().mxfp4_quantize_rowwise(_ptr(x), R, C, _ptr(q), _ptr(s),
+                                                                  _stream_handle(stream)))
+    return q, s
+
+
+def mxfp4_quantize_colwise(x, offs=None, G: int = 1, ld: Optional[int] = None, qT=None, sT=None, stream=None):
+    """x bf16 [R, C] -> (qT uint8 [C, ld/2] packed E2M1, sT uint8 [C, ld/32])."""
+    torch = _torch()
+    x = _bf16_bits(x)
+    R, C = x.shape
+    if offs is not None:
+        G = offs.numel() - 1
+    if ld is None:
+        ld = mx_colwise_ld_min(R, G) if offs is not None else 32 * ((R + 31) // 32)
+    qT = _empty((C, ld // 2), torch.uint8, x) if qT is None else qT
+    sT = _empty((C, ld // 32), torch.uint8, x) if sT is None else sT
+    _check("mxfp4_quantize_colwise", lib().mxfp4_quantize_colwise(_ptr(x), R, C, _ptr(offs), G, _ptr(qT), _ptr(sT),
+                                                                  ld, _stream_handle(stream)))
+    return qT, sT
+
+
+def mxfp4_grouped_gemm_fwd(qx, sx, qw, sw, offs, N: int, out_dtype: str = "f32", y=None, stream=None):
+    """Y [M, N] from row-wise MXFP4 X (qx [M, K/2]) and W (qw [G*N, K/2])."""
+    M, K = qx.shape[0], 2 * qx.shape[1]
+    G = offs.numel() - 1
+    tdt, cdt = _out_dtype(out_dtype)
+    y = _empty((M, N), tdt, qx) if y is None else y
+    _check("mxfp4_grouped_gemm_fwd", lib().mxfp4_grouped_gemm_fwd(_ptr(qx), _ptr(sx), _ptr(qw), _ptr(sw), _ptr(offs),
+                                                                  G, M, N, K, _ptr(y), cdt, _stream_handle(stream)))
+    return y
+
+
+def mxfp4_grouped_gemm_dgrad(qdy, sdy, qwT, swT, offs, K: int, out_dtype: str = "f32", dx=None, stream=None):
+    """dX [M, K] from row-wise MXFP4 dY (qdy [M, N/2]) and column-wise W (qwT [K, ldw/2])."""
+    M, N = qdy.shape[0], 2 * qdy.shape[1]
+    ldw = 2 * qwT.shape[1]
+    G = offs.numel() - 1
+    tdt, cdt = _out_dtype(out_dtype)
+    dx = _empty((M, K), tdt, qdy) if dx is None else dx
+    _check("mxfp4_grouped_gemm_dgrad", lib().mxfp4_grouped_gemm_dgrad(_ptr(qdy), _ptr(sdy), _ptr(qwT), _ptr(swT), ldw,
+                                                                      _ptr(offs), G, M, N, K, _ptr(dx), cdt,
+                                                                      _stream_handle(stream)))
+    return dx
+
+
+def mxfp4_grouped_gemm_wgrad(qdyT, sdyT, qxT, sxT, offs, M: int, out_dtype: str = "f32", dw=None, stream=None):
+    """dW [G, N, K] from column-wise MXFP4 dY (qdyT [N, ld/2]) and X (qxT [K, ld/2])."""
+    N, ld = qdyT.shape[0], 2 * qdyT.shape[1]
+    K = qxT.shape[0]
+    G = offs.numel() - 1
+    tdt, cdt = _out_dtype(out_dtype)
+    dw = _empty((G, N, K), tdt, qdyT) if dw is None else dw
+    _check("mxfp4_grouped_gemm_wgrad", lib().mxfp4_grouped_gemm_wgrad(_ptr(qdyT), _ptr(sdyT), _ptr(qxT), _ptr(sxT), ld,
+                                                                      _ptr(offs), G, M, N, K, _ptr(dw), cdt,
+                                                                      _stream_handle(stream)))
     return dw
 
 

@@ -166,8 +166,11 @@ mxmoe_status mx_quantize_dual(const void* x, int64_t R, int64_t C, const int32_t
 
 static mxmoe_status mx_gemm_common(int mode, const char* fn, const uint8_t* a, const uint8_t* sa, const uint8_t* b,
                                    const uint8_t* sb, int64_t ldb_cols, const int32_t* offs, int32_t G, int64_t M,
-                                   int64_t N, int64_t K, void* out, int dt, void* stream) {
+                                   int64_t N, int64_t K, void* out, int dt, void* stream, bool fp4 = false) {
   TRY(check_gemm_common(fn, offs, G, M, N, K, out, dt));
+  if (fp4 && (N % 256 || K % 256))
+    return fail(MXMOE_ERR_SHAPE, "%s: MXFP4 needs N and K multiples of 256 (N=%lld K=%lld)", fn, (long long)N,
+                (long long)K);
   TRY(check_ptr(fn, "A operand", a, 16));
   TRY(check_ptr(fn, "A scales", sa, 4));
   TRY(check_ptr(fn, "B operand", b, 16));
@@ -178,12 +181,16 @@ static mxmoe_status mx_gemm_common(int mode, const char* fn, const uint8_t* a, c
   p.M = M; p.N = N; p.K = K; p.G = G;
   p.out_bf16 = (dt & ~MXMOE_FEED_FP8) == MXMOE_BF16;
   p.feed = (dt & MXMOE_FEED_FP8) ? kFeedFast : kFeedPrecise;
+  // operand leading dimensions in bytes (E2M1: two elements per byte), scale ones in blocks
+  const int epb = fp4 ? 2 : 1;
+  p.fp4 = fp4;
+  if (fp4) p.feed = kFeedFast;
   if (mode == kFwd) {
-    p.lda = K; p.ldsa = K / 32; p.ldb = K; p.ldsb = K / 32;
+    p.lda = K / epb; p.ldsa = K / 32; p.ldb = K / epb; p.ldsb = K / 32;
   } else if (mode == kDgrad) {
-    p.lda = N; p.ldsa = N / 32; p.ldb = ldb_cols; p.ldsb = ldb_cols / 32;
+    p.lda = N / epb; p.ldsa = N / 32; p.ldb = ldb_cols / epb; p.ldsb = ldb_cols / 32;
   } else {
-    p.lda = ldb_cols; p.ldsa = ldb_cols / 32; p.ldb = ldb_cols; p.ldsb = ldb_cols / 32;
+    p.lda = ldb_cols / epb; p.ldsa = ldb_cols / 32; p.ldb = ldb_cols / epb; p.ldsb = ldb_cols / 32;
   }
   if (mode != kWgrad && M == 0) return ok();
   TRY(check_device());
@@ -214,6 +221,64 @@ mxmoe_status mx_grouped_gemm_wgrad(const uint8_t* qdyT, const uint8_t* sdyT, con
     return fail(MXMOE_ERR_SHAPE, "%s: ld=%lld must be a multiple of 32 and >= mx_colwise_ld_min(M, G)=%lld", fn,
                 (long long)ld, (long long)mx_colwise_ld_min(M, G));
   return mx_gemm_common(kWgrad, fn, qdyT, sdyT, qxT, sxT, ld, offs, G, M, N, K, dw, (int)dwdt, stream);
+}
+
+mxmoe_status mxfp4_quantize_rowwise(const void* x, int64_t R, int64_t C, uint8_t* q, uint8_t* s, void* stream) {
+  const char* fn = "mxfp4_quantize_rowwise";
+  if (R < 0 || C <= 0 || C % 32) return fail(MXMOE_ERR_SHAPE, "%s: need R >= 0, C > 0, C %% 32 == 0 (R=%lld C=%lld)",
+                                            fn, (long long)R, (long long)C);
+  if (R == 0) return ok();
+  TRY(check_ptr(fn, "x", x, 16));
+  TRY(check_ptr(fn, "q", q, 16));
+  TRY(check_ptr(fn, "s", s, 4));
+  TRY(check_device());
+  return launched(launch_mxfp4_rowwise((const uint16_t*)x, R, C, q, s, (hipStream_t)stream), fn);
+}
+
+mxmoe_status mxfp4_quantize_colwise(const void* x, int64_t R, int64_t C, const int32_t* offs, int32_t G, uint8_t* qT,
+                                    uint8_t* sT, int64_t ld, void* stream) {
+  const char* fn = "mxfp4_quantize_colwise";
+  if (R < 0 || C <= 0 || C % 32) return fail(MXMOE_ERR_SHAPE, "%s: need R >= 0, C > 0, C %% 32 == 0 (R=%lld C=%lld)",
+                                            fn, (long long)R, (long long)C);
+  if (R > INT32_MAX) return fail(MXMOE_ERR_SHAPE, "%s: R too large", fn);
+  if (offs && (G < 1 || G > kMaxG)) return fail(MXMOE_ERR_SHAPE, "%s: G = %d outside [1, %d]", fn, (int)G, (int)kMaxG);
+  if (ld <= 0 || ld % 32) return fail(MXMOE_ERR_ALIGN, "%s: ld must be a positive multiple of 32 (ld=%lld)", fn,
+                                      (long long)ld);
+  const int64_t need = offs ? mx_colwise_ld_min(R, G) : 32 * ((R + 31) / 32);
+  if (ld < need) return fail(MXMOE_ERR_SHAPE, "%s: ld=%lld < required %lld", fn, (long long)ld, (long long)need);
+  if (R > 0) TRY(check_ptr(fn, "x", x, 16));
+  if (offs && !aligned(offs, 4)) return fail(MXMOE_ERR_ALIGN, "%s: offs not 4-byte aligned", fn);
+  TRY(check_ptr(fn, "qT", qT, 16));
+  TRY(check_ptr(fn, "sT", sT, 4));
+  TRY(check_device());
+  return launched(launch_mxfp4_colwise((const uint16_t*)x, R, C, offs, G, qT, sT, ld, (hipStream_t)stream), fn);
+}
+
+mxmoe_status mxfp4_grouped_gemm_fwd(const uint8_t* qx, const uint8_t* sx, const uint8_t* qw, const uint8_t* sw,
+                                    const int32_t* offs, int32_t G, int64_t M, int64_t N, int64_t K, void* y,
+                                    mxmoe_dtype ydt, void* stream) {
+  return mx_gemm_common(kFwd, "mxfp4_grouped_gemm_fwd", qx, sx, qw, sw, 0, offs, G, M, N, K, y, (int)ydt, stream,
+                        true);
+}
+
+mxmoe_status mxfp4_grouped_gemm_dgrad(const uint8_t* qdy, const uint8_t* sdy, const uint8_t* qwT, const uint8_t* swT,
+                                      int64_t ldw, const int32_t* offs, int32_t G, int64_t M, int64_t N, int64_t K,
+                                      void* dx, mxmoe_dtype dxdt, void* stream) {
+  const char* fn = "mxfp4_grouped_gemm_dgrad";
+  if (ldw % 32 || ldw < (int64_t)G * N)
+    return fail(MXMOE_ERR_SHAPE, "%s: ldw=%lld must be a multiple of 32 and >= G*N=%lld", fn, (long long)ldw,
+                (long long)G * N);
+  return mx_gemm_common(kDgrad, fn, qdy, sdy, qwT, swT, ldw, offs, G, M, N, K, dx, (int)dxdt, stream, true);
+}
+
+mxmoe_status mxfp4_grouped_gemm_wgrad(const uint8_t* qdyT, const uint8_t* sdyT, const uint8_t* qxT,
+                                      const uint8_t* sxT, int64_t ld, const int32_t* offs, int32_t G, int64_t M,
+                                      int64_t N, int64_t K, void* dw, mxmoe_dtype dwdt, void* stream) {
+  const char* fn = "mxfp4_grouped_gemm_wgrad";
+  if (G >= 1 && M >= 0 && (ld % 32 || ld < mx_colwise_ld_min(M, G)))
+    return fail(MXMOE_ERR_SHAPE, "%s: ld=%lld must be a multiple of 32 and >= mx_colwise_ld_min(M, G)=%lld", fn,
+                (long long)ld, (long long)mx_colwise_ld_min(M, G));
+  return mx_gemm_common(kWgrad, fn, qdyT, sdyT, qxT, sxT, ld, offs, G, M, N, K, dw, (int)dwdt, stream, true);
 }
 
 mxmoe_status fp8bw_quantize_act_1x128(const void* x, int64_t R, int64_t C, uint8_t* q, float* s, void* stream) {

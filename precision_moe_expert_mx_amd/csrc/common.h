@@ -40,6 +40,23 @@ __device__ __forceinline__ int mx_exponent(uint32_t amax_bits) {
   return max((int)(amax_bits >> 7) - 135, -127);
 }
 
+// The same rule for E2M1 elements (largest exponent 2): max(E - 129, -127).
+__device__ __forceinline__ int mxfp4_exponent(uint32_t amax_bits) {
+  return max((int)(amax_bits >> 7) - 129, -127);
+}
+
+// Eight bf16 (four dwords, element order) -> eight E2M1 codes packed two per byte, element 2i in the
+// low nibble of byte i.  The conversion divides by the power of two whose exponent field is that of
+// `scale`, rounds to nearest even and saturates at 6 (checked on gfx950 against every finite bf16
+// at several scales), so no clamp is needed.
+__device__ __forceinline__ uint32_t cvt8_e2m1(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3, float scale) {
+  typedef __bf16 v2bf_ __attribute__((ext_vector_type(2)));
+  uint32_t o = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(0u, __builtin_bit_cast(v2bf_, w0), scale, 0);
+  o = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(o, __builtin_bit_cast(v2bf_, w1), scale, 1);
+  o = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(o, __builtin_bit_cast(v2bf_, w2), scale, 2);
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(o, __builtin_bit_cast(v2bf_, w3), scale, 3);
+}
+
 // bf16 bit pattern of 448 * 2^e (the largest magnitude that does not saturate), e in [-127, 119].
 __device__ __forceinline__ uint32_t mx_clamp_bits(int e) { return ((uint32_t)(e + 135) << 7) | 0x60u; }
 
@@ -135,6 +152,9 @@ __device__ __forceinline__ void block_rows(int bc, int nbc, int G, const int32_t
 hipError_t launch_mx_rowwise(const uint16_t* x, int64_t R, int64_t C, uint8_t* q, uint8_t* s, hipStream_t st);
 hipError_t launch_mx_colwise(const uint16_t* x, int64_t R, int64_t C, const int32_t* offs, int32_t G,
                              uint8_t* qT, uint8_t* sT, int64_t ld, hipStream_t st);
+hipError_t launch_mxfp4_rowwise(const uint16_t* x, int64_t R, int64_t C, uint8_t* q, uint8_t* s, hipStream_t st);
+hipError_t launch_mxfp4_colwise(const uint16_t* x, int64_t R, int64_t C, const int32_t* offs, int32_t G,
+                                uint8_t* qT, uint8_t* sT, int64_t ld, hipStream_t st);
 hipError_t launch_mx_dual(const uint16_t* x, int64_t R, int64_t C, const int32_t* row_idx, int64_t Rsrc,
                           const int32_t* offs, int32_t G, uint8_t* q, uint8_t* s, uint8_t* qT, uint8_t* sT, int64_t ld,
                           hipStream_t st);
@@ -159,7 +179,8 @@ struct GemmArgs {
   int32_t G;
   int32_t out_bf16;
   int32_t feed;       // GemmFeed
-  int32_t scale_dword;  // MX: every row's four scale bytes of a stage form one aligned dword
+  int32_t scale_dword;  // MX: every row's scale bytes of a stage form aligned dwords
+  int32_t fp4;          // MX operands are E2M1 (two per byte; leading dimensions in bytes)
 };
 
 hipError_t launch_mx_gemm(int mode, const GemmArgs& a, hipStream_t st);

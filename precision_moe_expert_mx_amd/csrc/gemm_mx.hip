@@ -28,6 +28,13 @@
 //    (g = l / 16) and the E8M0 byte of block g.  Its sums are truncated per run of products (see
 //    include/mxmoe.h).
 //
+// MXFP4 (E2M1 codes two per byte, E8M0 per 32): the same tiling with 128 bytes = 256 elements
+// (eight blocks) per stage on the fast feed only, two v_mfma_scale_f32_16x16x128_f8f6f4 k-steps per
+// fragment pair and stage with the E2M1 operand format; lane l feeds row l % 16 with the 16 bytes of
+// block g (k-step 0) and 4 + g (k-step 1), g = l / 16, and that block's scale (measured on gfx950).
+// E2M1 products span at most 2^-2 .. 36 times the pair's scales, inside the instruction's summation
+// window, so its sums are exact up to fp32 accumulation.
+//
 // Scheduling: the tile list of the launch is built on the device from the group offsets (prefix sums
 // in LDS); forward / dgrad enumerate ceil(m_g / 256) row tiles per expert, so an expert without rows
 // has no tile and a 17-row expert one; wgrad has ceil(N/256) x ceil(K/256) tiles for every expert
@@ -60,8 +67,9 @@ constexpr int kScaleRows = 2 * BM / NT;          // scale rows each thread gathe
 static_assert(BM == BN && kLoadRows % 8 == 0 && kScaleLoads >= 1 && kScaleRows >= 1, "tile / wave layout");
 constexpr int kStageA = BM * BK;                 // 32 KiB
 constexpr int kStage = kStageA + BN * BK;        // 64 KiB
-constexpr int kScaleStage = (BM + BN) * 4;       // four E8M0 bytes per operand row
-constexpr int kLds = 2 * kStage + 2 * kScaleStage;
+constexpr int kScaleStage = (BM + BN) * 4;       // four E8M0 bytes per operand row (E4M3)
+constexpr int kScaleStage4 = (BM + BN) * 8;      // eight E8M0 bytes per operand row (E2M1), two dword planes
+constexpr int kLds = 2 * kStage + 2 * kScaleStage4;
 constexpr int kMaxG = 1024;
 constexpr int kXcd = 8;
 constexpr int kChunk = 8;
@@ -173,8 +181,10 @@ __device__ bool decode_tile(const GemmArgs& p, char* lds, Tile& t) {
   t.col0 = 32 * (int64_t)s_cb[g];
   t.nblk = cdiv(m_g, 32);
   if (MODE == kWgrad) {
-    // offsets that are not monotone could place an expert past the leading dimension: clip
-    const int64_t room = p.lda > t.col0 ? (p.lda - t.col0) / 32 : 0;
+    // offsets that are not monotone could place an expert past the leading dimension: clip (lda is
+    // in bytes; an E2M1 block is 16 bytes)
+    const int64_t ld_el = p.fp4 ? 2 * p.lda : p.lda;
+    const int64_t room = ld_el > t.col0 ? (ld_el - t.col0) / 32 : 0;
     if (t.nblk > room) t.nblk = (int)room;
   }
   return true;
@@ -215,19 +225,25 @@ __device__ __forceinline__ void stage_barrier() {
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-template <int MODE, int FEED, bool SDW>
+template <int MODE, int FEED, bool SDW, bool FP4>
 __device__ __forceinline__ void run_tile(const GemmArgs& p, const Tile& t, char* lds) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
+  static_assert(!FP4 || FEED == kFeedFast, "E2M1 operands use the block-scaled MFMA");
+  // E2M1: two elements per byte, so a 128-byte stage holds eight 32-blocks
+  constexpr int EPB = FP4 ? 2 : 1;            // elements per byte
+  constexpr int SPS = FP4 ? 8 : 4;            // scale bytes per row and stage
+  constexpr int kSStage = FP4 ? kScaleStage4 : kScaleStage;
 
-  // ---- operand geometry ----------------------------------------------------------------------
+  // ---- operand geometry (contraction offsets in bytes; scale offsets in 32-blocks) ------------
   int64_t L;
-  if (MODE == kFwd) L = p.K;
-  else if (MODE == kDgrad) L = p.N;
-  else L = 32 * (int64_t)t.nblk;
+  if (MODE == kFwd) L = p.K / EPB;
+  else if (MODE == kDgrad) L = p.N / EPB;
+  else L = 32 / EPB * (int64_t)t.nblk;
   const int nsteps = (int)((L + BK - 1) / BK);
-  const int64_t a_col0 = MODE == kWgrad ? t.col0 : 0;
-  const int64_t b_col0 = MODE == kWgrad ? t.col0 : (MODE == kDgrad ? (int64_t)t.g * p.N : 0);
+  const int64_t a_el0 = MODE == kWgrad ? t.col0 : 0;     // first contraction element
+  const int64_t b_el0 = MODE == kWgrad ? t.col0 : (MODE == kDgrad ? (int64_t)t.g * p.N : 0);
+  const int64_t a_col0 = a_el0 / EPB, b_col0 = b_el0 / EPB;
   const int64_t a_rows_lim = MODE == kWgrad ? p.N : 0;     // wgrad: A rows are n
   const int64_t b_rows_lim = MODE == kFwd ? p.N : p.K;
 
@@ -258,7 +274,7 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const Tile& t, char*
   // the dwords to LDS.
   const uint8_t* sa = (const uint8_t*)p.sa;
   const uint8_t* sb = (const uint8_t*)p.sb;
-  const int64_t sa_col0 = a_col0 / 32, sb_col0 = b_col0 / 32;
+  const int64_t sa_col0 = a_el0 / 32, sb_col0 = b_el0 / 32;
   constexpr int NS = SDW ? kScaleLoads : kScaleRows;
   const uint8_t* s_src[NS];
 #pragma unroll
@@ -269,41 +285,49 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const Tile& t, char*
     const int r = q & 255;
     s_src[j] = q < 256 ? sa + a_row(r) * p.ldsa + sa_col0 : sb + b_row(r) * p.ldsb + sb_col0;
   }
-  // Bytes [4ks, 4ks + nv) of a scale row (nv < 4 only in the last wgrad stage; the rest read as 0):
-  // two aligned dword loads funnel-shifted together.  The first word holds byte 0; the second is
-  // read only when it holds a wanted byte (else the first is read again), so no load touches a word
-  // without a byte of the row.  The words are combined only when stored, one stage later, so that no
-  // wait for them sits between the loads of a stage.
+  // Scale bytes [SPS ks, SPS ks + nv) of a row (nv < SPS only in the last wgrad stage; the rest read
+  // as 0) land as SPS / 4 dwords, dword d of every row in plane d of the stage's scale area.  Register
+  // path: aligned dword loads funnel-shifted together; word k is read only when it holds a wanted
+  // byte (else the previous word is read again), so no load touches a word without a byte of the
+  // row.  The words are combined only when stored, one stage later, so that no wait for them sits
+  // between the loads of a stage.
+  constexpr int P = SPS / 4;                  // dword planes
   auto scale_geom = [&](int j, int ks, int& nv, int& sh) -> const uint32_t* {
-    nv = MODE == kWgrad ? min(4, t.nblk - 4 * ks) : 4;
-    const uintptr_t ai = (uintptr_t)(s_src[j] + 4 * ks);
+    nv = MODE == kWgrad ? min(SPS, t.nblk - SPS * ks) : SPS;
+    const uintptr_t ai = (uintptr_t)(s_src[j] + SPS * ks);
     sh = (int)(ai & 3);
     return (const uint32_t*)(ai & ~(uintptr_t)3);
   };
-  auto gather_scales = [&](int ks, uint32_t* lo, uint32_t* hi) {
+  auto gather_scales = [&](int ks, uint32_t (*sw)[P + 1]) {
 #pragma unroll
     for (int j = 0; j < NS; ++j) {
       int nv, sh;
       typedef const __attribute__((address_space(1))) uint32_t* gptr;
       const gptr w0 = (gptr)scale_geom(j, ks, nv, sh);
-      lo[j] = *w0;
-      hi[j] = *(sh + nv > 4 ? w0 + 1 : w0);
+      sw[j][0] = w0[0];
+#pragma unroll
+      for (int k = 1; k <= P; ++k) sw[j][k] = w0[4 * k < sh + nv ? k : k - 1];
     }
   };
-  auto put_scales = [&](int ks, const uint32_t* lo, const uint32_t* hi) {
+  auto put_scales = [&](int ks, const uint32_t (*sw)[P + 1]) {
 #pragma unroll
     for (int j = 0; j < NS; ++j) {
       int nv, sh;
       scale_geom(j, ks, nv, sh);
-      uint32_t v = __builtin_amdgcn_alignbyte(hi[j], lo[j], (uint32_t)sh);
-      if (nv < 4) v &= (1u << (8 * nv)) - 1u;
-      *(uint32_t*)(lds + 2 * kStage + (ks & 1) * kScaleStage + 4 * (tid + NT * j)) = v;
+#pragma unroll
+      for (int d = 0; d < P; ++d) {
+        uint32_t v = __builtin_amdgcn_alignbyte(sw[j][d + 1], sw[j][d], (uint32_t)sh);
+        const int keep = nv - 4 * d;            // valid bytes of this dword
+        if (keep <= 0) v = 0;
+        else if (keep < 4) v &= (1u << (8 * keep)) - 1u;
+        *(uint32_t*)(lds + 2 * kStage + (ks & 1) * kSStage + 2048 * d + 4 * (tid + NT * j)) = v;
+      }
     }
   };
 
   auto issue = [&](int ks) {
     char* st = lds + (ks & 1) * kStage;
-    char* ss = lds + 2 * kStage + (ks & 1) * kScaleStage;
+    char* ss = lds + 2 * kStage + (ks & 1) * kSStage;
     const int64_t koff = (int64_t)ks * BK;
 #pragma unroll
     for (int j = 0; j < ND; ++j) {
@@ -315,7 +339,10 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const Tile& t, char*
     }
     if (SDW) {
 #pragma unroll
-      for (int j = 0; j < NS; ++j) dma4(s_src[j] + 4 * ks, ss + 256 * (kScaleLoads * w + j));
+      for (int j = 0; j < NS; ++j)
+#pragma unroll
+        for (int d = 0; d < P; ++d)
+          dma4(s_src[j] + SPS * ks + 4 * d, ss + 2048 * d + 256 * (kScaleLoads * w + j));
     }
   };
 
@@ -333,37 +360,36 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const Tile& t, char*
 #pragma unroll
       for (int r = 0; r < NR; ++r) acc[i][j][r] = 0.f;
 
-  uint32_t s_lo[NS], s_hi[NS];                    // register-staged scale words of the next stage
+  uint32_t s_w[NS][P + 1];                       // register-staged scale words of the next stage
   if (nsteps > 0) {
     issue(0);
     if (!SDW) {
-      gather_scales(0, s_lo, s_hi);
-      put_scales(0, s_lo, s_hi);
-      if (nsteps > 1) gather_scales(1, s_lo, s_hi);
+      gather_scales(0, s_w);
+      put_scales(0, s_w);
+      if (nsteps > 1) gather_scales(1, s_w);
     }
   }
+  constexpr int BPS = SPS;                        // 32-blocks per stage
+  constexpr int CPB = 8 / BPS;                    // 16-byte chunks per block
   for (int ks = 0; ks < nsteps; ++ks) {
     stage_barrier();                               // stage ks landed; stage ks-1 fully read
     if (ks + 1 < nsteps) {
       // the staged scale words arrived before the barrier; store them before issuing the next
       // stage's loads so that no wait on those loads is needed here
-      if (!SDW) put_scales(ks + 1, s_lo, s_hi);
+      if (!SDW) put_scales(ks + 1, s_w);
       issue(ks + 1);
-      if (!SDW && ks + 2 < nsteps) gather_scales(ks + 2, s_lo, s_hi);
+      if (!SDW && ks + 2 < nsteps) gather_scales(ks + 2, s_w);
     }
     char* st = lds + (ks & 1) * kStage;
-    const uint32_t* SA = (const uint32_t*)(lds + 2 * kStage + (ks & 1) * kScaleStage);
+    const uint32_t* SA = (const uint32_t*)(lds + 2 * kStage + (ks & 1) * kSStage);
     const uint32_t* SB = SA + BM;
-    if (MODE == kWgrad && ks == nsteps - 1 && (t.nblk & 3)) {
-      // the last stage holds 1-3 valid blocks: zero the unloaded chunks of every row (their scale
-      // bytes were gathered as 0)
+    if (MODE == kWgrad && ks == nsteps - 1 && (t.nblk % BPS)) {
+      // the last stage holds fewer blocks: zero the unloaded chunks of every row (their scale bytes
+      // were gathered as 0)
       for (int q = tid; q < BM + BN; q += NT) {
         const int r = q & 255;
         char* row = st + (q < BM ? 0 : kStageA) + r * BK;
-        for (int bb = t.nblk & 3; bb < 4; ++bb) {
-          *(uint4*)(row + (((2 * bb) ^ swz(r)) << 4)) = make_uint4(0, 0, 0, 0);
-          *(uint4*)(row + (((2 * bb + 1) ^ swz(r)) << 4)) = make_uint4(0, 0, 0, 0);
-        }
+        for (int c = CPB * (t.nblk % BPS); c < 8; ++c) *(uint4*)(row + ((c ^ swz(r)) << 4)) = make_uint4(0, 0, 0, 0);
       }
       stage_barrier();
     }
@@ -406,6 +432,32 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const Tile& t, char*
 #pragma unroll
           for (int j = 0; j < NJ; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bhi[j], ahi[i], acc[i][j], 0, 0, 0);
+      }
+    } else if constexpr (FP4) {
+      // two k-steps of 128 E2M1 elements: lane group fg feeds block 4 ks2 + fg (16 bytes, the upper
+      // half of the operand registers unused) with its scale byte from plane ks2
+      const int fr = lane & 15, fg = lane >> 4;
+#pragma unroll
+      for (int ks2 = 0; ks2 < 2; ++ks2) {
+        v8i bf[NJ];
+        int sbv[NJ];
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          const int r = WN * wn + 16 * j + fr;
+          const v4i c = *(const v4i*)(B + lds_off(r, 4 * ks2 + fg));
+          bf[j] = v8i{c[0], c[1], c[2], c[3], 0, 0, 0, 0};
+          sbv[j] = (int)((SB[512 * ks2 + r] >> (8 * fg)) & 0xFFu);
+        }
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+          const int r = WM * wm + 16 * i + fr;
+          const v4i c = *(const v4i*)(A + lds_off(r, 4 * ks2 + fg));
+          const v8i af = v8i{c[0], c[1], c[2], c[3], 0, 0, 0, 0};
+          const int sav = (int)((SA[512 * ks2 + r] >> (8 * fg)) & 0xFFu);
+#pragma unroll
+          for (int j = 0; j < NJ; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[j], af, acc[i][j], 4, 4, 0, sbv[j], 0, sav);
+        }
       }
     } else {
       const int fr = lane & 15, fg = lane >> 4;
@@ -471,13 +523,13 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const Tile& t, char*
   }
 }
 
-template <int MODE, int FEED, bool SDW>
+template <int MODE, int FEED, bool SDW, bool FP4 = false>
 __global__ __launch_bounds__(NT, 1) void mx_grouped_gemm_kernel(GemmArgs p) {
   __shared__ __attribute__((aligned(16))) char lds[kLds];
   Tile t;
   if (!decode_tile<MODE>(p, lds, t)) return;     // uniform across the workgroup
   __syncthreads();                               // scheduler scratch is reused for operands
-  run_tile<MODE, FEED, SDW>(p, t, lds);
+  run_tile<MODE, FEED, SDW, FP4>(p, t, lds);
 }
 
 static_assert(4 * (kMaxG + 1) * 4 <= kStage, "scheduler scratch must fit in the first stage");
@@ -490,7 +542,9 @@ int64_t tile_count_bound(int mode, const GemmArgs& p) {
 
 template <int MODE, bool SDW>
 void launch_mode(const GemmArgs& p, dim3 grid, hipStream_t st) {
-  if (p.feed == kFeedFast)
+  if (p.fp4)
+    hipLaunchKernelGGL((mx_grouped_gemm_kernel<MODE, kFeedFast, SDW, true>), grid, dim3(NT), 0, st, p);
+  else if (p.feed == kFeedFast)
     hipLaunchKernelGGL((mx_grouped_gemm_kernel<MODE, kFeedFast, SDW>), grid, dim3(NT), 0, st, p);
   else
     hipLaunchKernelGGL((mx_grouped_gemm_kernel<MODE, kFeedPrecise, SDW>), grid, dim3(NT), 0, st, p);
@@ -505,8 +559,8 @@ hipError_t launch_mx_gemm(int mode, const GemmArgs& args, hipStream_t st) {
   const int64_t per = (int64_t)kXcd * kChunk;
   const int64_t grid = (tiles + per - 1) / per * per;
   if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
-  // four scale bytes of a row and stage are one aligned dword when every scale row and column
-  // offset is a multiple of 4 bytes (wgrad expert columns start at arbitrary 32-blocks)
+  // the scale bytes of a row and stage are aligned dwords when every scale row and column offset is
+  // a multiple of 4 bytes (wgrad expert columns start at arbitrary 32-blocks)
   p.scale_dword = mode != kWgrad && p.ldsa % 4 == 0 && p.ldsb % 4 == 0 && (p.N / 32) % 4 == 0;
   const dim3 g((unsigned)grid);
   if (mode == kFwd) launch_mode<kFwd, true>(p, g, st);

@@ -73,6 +73,40 @@ hipError_t launch_mx_rowwise(const uint16_t* x, int64_t R, int64_t C, uint8_t* q
   return hipGetLastError();
 }
 
+// MXFP4 row-wise: the same lane layout; each lane's 8 elements become 4 bytes (two E2M1 per byte).
+__global__ __launch_bounds__(kRowThreads) void mxfp4_rowwise_kernel(const uint4* __restrict__ x, int64_t nchunks,
+                                                                     uint32_t* __restrict__ q, uint8_t* __restrict__ s) {
+  const int64_t base = (int64_t)blockIdx.x * (kRowThreads * kRowUnroll) + threadIdx.x;
+  uint4 v[kRowUnroll];
+#pragma unroll
+  for (int j = 0; j < kRowUnroll; ++j) {
+    int64_t i = base + (int64_t)j * kRowThreads;
+    v[j] = i < nchunks ? x[i] : make_uint4(0, 0, 0, 0);
+  }
+#pragma unroll
+  for (int j = 0; j < kRowUnroll; ++j) {
+    int64_t i = base + (int64_t)j * kRowThreads;
+    const uint32_t m = quad_max(mag_max8(v[j]));
+    const int e = mxfp4_exponent(m);
+    const float sc = __uint_as_float((uint32_t)(e + 127) << 23);
+    const uint32_t o = cvt8_e2m1(v[j].x, v[j].y, v[j].z, v[j].w, sc);
+    if (i < nchunks) {
+      q[i] = o;
+      if ((threadIdx.x & 3) == 0) s[i >> 2] = (uint8_t)(e + 127);
+    }
+  }
+}
+
+hipError_t launch_mxfp4_rowwise(const uint16_t* x, int64_t R, int64_t C, uint8_t* q, uint8_t* s, hipStream_t st) {
+  int64_t nchunks = R * C / 8;
+  if (nchunks == 0) return hipSuccess;
+  int64_t per = (int64_t)kRowThreads * kRowUnroll;
+  int64_t blocks = (nchunks + per - 1) / per;
+  hipLaunchKernelGGL(mxfp4_rowwise_kernel, dim3((unsigned)blocks), dim3(kRowThreads), 0, st, (const uint4*)x, nchunks,
+                     (uint32_t*)q, s);
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------------------------------------
 // Column-wise (group-blocked, transposed), optionally fused with the row-wise layout.
 //
@@ -160,7 +194,7 @@ __device__ __forceinline__ void col_load(const ColArgs& a, int r0, int n, ColRow
 
 // Convert the workgroup's 4 blocks (this wave's: rows r0 .. r0 + n of block-column bc0 + w) and write
 // them out.
-template <bool ROW, bool FULLWIN>
+template <bool ROW, bool FULLWIN, bool FP4>
 __device__ __forceinline__ void col_group(const ColArgs& a, int r0, int n, int bc0, ColRows (&v)[32],
                                           uint8_t* outq, uint8_t* outs, uint8_t* rsc, const int32_t* g_r0,
                                           const int32_t* g_n) {
@@ -206,43 +240,63 @@ __device__ __forceinline__ void col_group(const ColArgs& a, int r0, int n, int b
       asm volatile("v_and_b32 %0, 0x7fff7fff, %1" : "=v"(mag) : "v"(v[r][k]));
       mx[k] = __builtin_elementwise_max(mx[k], __builtin_bit_cast(v2us, mag));
     }
+  // LDS bytes per output row: 32 code bytes per block (E4M3), 16 (E2M1, two per byte), plus padding
+  constexpr int kPitch = FP4 ? kColBlk * 16 + 16 : kColPitch;
+  constexpr int kBlkBytes = FP4 ? 16 : 32;
 #pragma unroll
   for (int k = 0; k < kColLaneCols; ++k) {
-    const int e = mx_exponent(mx[k >> 1][k & 1]);
-    const uint32_t cl = mx_clamp_bits(e);
-    const uint32_t cl2 = cl | (cl << 16);
+    const int e = FP4 ? mxfp4_exponent(mx[k >> 1][k & 1]) : mx_exponent(mx[k >> 1][k & 1]);
     const float sc = __uint_as_float((uint32_t)(e + 127) << 23);
-    // rows 4d..4d+3 of column k: pair rows through byte permutes (row a in the low half)
+    // pair rows of column k through byte permutes (the lower row in the low half)
     const uint32_t sel = (k & 1) ? 0x07060302u : 0x05040100u;
-    uint32_t o[8];
+    if constexpr (FP4) {
+      // rows 8d .. 8d + 7 of column k -> one dword of E2M1 codes
+      uint32_t o[4];
 #pragma unroll
-    for (int d = 0; d < 8; ++d) {
-      const uint32_t p01 = __builtin_amdgcn_perm(v[4 * d + 1][k >> 1], v[4 * d][k >> 1], sel);
-      const uint32_t p23 = __builtin_amdgcn_perm(v[4 * d + 3][k >> 1], v[4 * d + 2][k >> 1], sel);
-      o[d] = cvt4_e4m3(p01, p23, cl2, sc);
+      for (int d = 0; d < 4; ++d) {
+        uint32_t pr[4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+          pr[p] = __builtin_amdgcn_perm(v[8 * d + 2 * p + 1][k >> 1], v[8 * d + 2 * p][k >> 1], sel);
+        o[d] = cvt8_e2m1(pr[0], pr[1], pr[2], pr[3], sc);
+      }
+      *(uint4*)(outq + (kColLaneCols * a.lane + k) * kPitch + kBlkBytes * a.w) = make_uint4(o[0], o[1], o[2], o[3]);
+    } else {
+      const uint32_t cl = mx_clamp_bits(e);
+      const uint32_t cl2 = cl | (cl << 16);
+      // rows 4d..4d+3 of column k
+      uint32_t o[8];
+#pragma unroll
+      for (int d = 0; d < 8; ++d) {
+        const uint32_t p01 = __builtin_amdgcn_perm(v[4 * d + 1][k >> 1], v[4 * d][k >> 1], sel);
+        const uint32_t p23 = __builtin_amdgcn_perm(v[4 * d + 3][k >> 1], v[4 * d + 2][k >> 1], sel);
+        o[d] = cvt4_e4m3(p01, p23, cl2, sc);
+      }
+      uint4* dst = (uint4*)(outq + (kColLaneCols * a.lane + k) * kPitch + kBlkBytes * a.w);
+      dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
+      dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
     }
-    uint4* dst = (uint4*)(outq + (kColLaneCols * a.lane + k) * kColPitch + 32 * a.w);
-    dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
-    dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
     outs[(kColLaneCols * a.lane + k) * kColBlk + a.w] = (uint8_t)(e + 127);   // all-zero (pad) blocks give 0
   }
   // Publish the LDS tiles.  Only LDS needs to be complete: a __syncthreads() would also wait for the
   // row-wise global stores above, putting their write latency on the path.
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
-  // write out: output row cbase + rr holds 32 kColBlk bytes from column 32 bc0 (fewer at the right
-  // edge of ld), 16 bytes per lane
-  constexpr int kPieces = kColBlk * 2;                             // 16-byte pieces per output row
+  // write out: output row cbase + rr holds kBlkBytes kColBlk bytes from block-column bc0 (fewer at the
+  // right edge of ld), 16 bytes per lane
+  constexpr int kPieces = kColBlk * kBlkBytes / 16;                // 16-byte pieces per output row
+  constexpr int kPiecesPerBlk = kBlkBytes / 16;
   const int64_t nbc = a.ld / 32;
+  const int64_t row_bytes = FP4 ? a.ld / 2 : a.ld;
   const int nb = nbc - bc0 < kColBlk ? (int)(nbc - bc0) : kColBlk;  // block-columns inside ld
 #pragma unroll
   for (int it = 0; it < kColCols * kPieces / kColThreads; ++it) {
     const int idx = it * kColThreads + a.t;
     const int rr = idx / kPieces, piece = idx % kPieces;
     const int64_t c = a.cbase + rr;
-    if ((FULLWIN || c < a.C) && (piece >> 1) < nb) {
-      const uint4 val = *(const uint4*)(outq + rr * kColPitch + 16 * piece);
-      *(uint4*)(a.qT + c * a.ld + (int64_t)bc0 * 32 + 16 * piece) = val;
+    if ((FULLWIN || c < a.C) && (piece / kPiecesPerBlk) < nb) {
+      const uint4 val = *(const uint4*)(outq + rr * kPitch + 16 * piece);
+      *(uint4*)(a.qT + c * row_bytes + (int64_t)bc0 * kBlkBytes + 16 * piece) = val;
     }
   }
   for (int idx = a.t; idx < kColCols * kColBlk; idx += kColThreads) {
@@ -277,7 +331,7 @@ __device__ __forceinline__ void col_group(const ColArgs& a, int r0, int n, int b
 // reads; each routed row lies in exactly one block-column, so it is written once.  GATHER: routed
 // row r is read from source row row_idx[r] (clamped into [0, Rsrc)).  FULLWIN: C % 256 == 0, so every
 // window lies inside the tensor.
-template <bool ROW, bool GATHER, bool FULLWIN>
+template <bool ROW, bool GATHER, bool FULLWIN, bool FP4>
 __global__ __launch_bounds__(kColThreads) void mx_colwise_kernel(const uint16_t* __restrict__ x, int64_t R, int64_t C,
                                                                  const int32_t* __restrict__ offs, int G,
                                                                  uint8_t* __restrict__ qT, uint8_t* __restrict__ sT,
@@ -333,23 +387,23 @@ __global__ __launch_bounds__(kColThreads) void mx_colwise_kernel(const uint16_t*
   const int n = __builtin_amdgcn_readfirstlane(blk_n[a.w]);
   ColRows v[32];
   col_load<GATHER, FULLWIN>(a, r0, n, v);
-  col_group<ROW, FULLWIN>(a, r0, n, bc0, v, outq, outs, rsc, blk_r0, blk_n);
+  col_group<ROW, FULLWIN, FP4>(a, r0, n, bc0, v, outq, outs, rsc, blk_r0, blk_n);
 }
 
 static int64_t colwise_grid(int64_t C, int64_t ld) {
   return ((ld / 32 + kColBlk - 1) / kColBlk) * ((C + kColCols - 1) / kColCols);
 }
 
-template <bool ROW, bool GATHER>
+template <bool ROW, bool GATHER, bool FP4 = false>
 static void launch_col(bool fullwin, int64_t nwg, hipStream_t st, const uint16_t* x, int64_t R, int64_t C,
                        const int32_t* offs, int32_t G, uint8_t* qT, uint8_t* sT, int64_t ld, uint8_t* q, uint8_t* s,
                        const int32_t* row_idx, int64_t Rsrc) {
   if (fullwin)
-    hipLaunchKernelGGL((mx_colwise_kernel<ROW, GATHER, true>), dim3((unsigned)nwg), dim3(kColThreads), 0, st, x, R, C,
-                       offs, G, qT, sT, ld, q, s, row_idx, Rsrc);
-  else
-    hipLaunchKernelGGL((mx_colwise_kernel<ROW, GATHER, false>), dim3((unsigned)nwg), dim3(kColThreads), 0, st, x, R,
+    hipLaunchKernelGGL((mx_colwise_kernel<ROW, GATHER, true, FP4>), dim3((unsigned)nwg), dim3(kColThreads), 0, st, x, R,
                        C, offs, G, qT, sT, ld, q, s, row_idx, Rsrc);
+  else
+    hipLaunchKernelGGL((mx_colwise_kernel<ROW, GATHER, false, FP4>), dim3((unsigned)nwg), dim3(kColThreads), 0, st, x,
+                       R, C, offs, G, qT, sT, ld, q, s, row_idx, Rsrc);
 }
 
 hipError_t launch_mx_colwise(const uint16_t* x, int64_t R, int64_t C, const int32_t* offs, int32_t G,
@@ -359,6 +413,16 @@ hipError_t launch_mx_colwise(const uint16_t* x, int64_t R, int64_t C, const int3
   if (nwg > 0x7FFFFFFF) return hipErrorInvalidValue;
   launch_col<false, false>(C % kColCols == 0, nwg, st, x, R, C, offs, offs ? G : 1, qT, sT, ld, nullptr, nullptr,
                            nullptr, (int64_t)0);
+  return hipGetLastError();
+}
+
+hipError_t launch_mxfp4_colwise(const uint16_t* x, int64_t R, int64_t C, const int32_t* offs, int32_t G,
+                                uint8_t* qT, uint8_t* sT, int64_t ld, hipStream_t st) {
+  if (C == 0 || ld == 0) return hipSuccess;
+  const int64_t nwg = colwise_grid(C, ld);
+  if (nwg > 0x7FFFFFFF) return hipErrorInvalidValue;
+  launch_col<false, false, true>(C % kColCols == 0, nwg, st, x, R, C, offs, offs ? G : 1, qT, sT, ld, nullptr,
+                                 nullptr, nullptr, (int64_t)0);
   return hipGetLastError();
 }
 
