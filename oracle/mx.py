@@ -211,3 +211,27 @@ def mxfp4_dequantize(q, s) -> np.ndarray:
     if v.shape[-1] != s.shape[-1] * BLOCK:
         raise ValueError("shape mismatch")
     return v * np.repeat(np.ldexp(1.0, s - 127), BLOCK, axis=-1)
+
+
+# ---------------------------------------------------------------- gated activation + quantisation
+def mx_quantize_rowwise_values(v):
+    """MX-quantise exact real values (float64 [R, C], e.g. float32 results widened) row-wise: the same
+    block rule as mx_quantize_rowwise, whose input is bf16 bit patterns."""
+    v = np.asarray(v, dtype=np.float64)
+    if not np.all(np.isfinite(v)):
+        raise ValueError("non-finite input is outside the contract")
+    R, C = v.shape
+    if C % BLOCK:
+        raise ValueError("C must be a multiple of 32")
+    q, s = _quantize_blocks(v.reshape(R, C // BLOCK, BLOCK), axis=2)
+    return q.reshape(R, C), s.reshape(R, C // BLOCK)
+
+
+def swiglu(gate, up):
+    """Gated activation of an expert's gate+up output: silu(gate) * up, silu(z) = z / (1 + e^-z).
+
+    Reading: the pages name no activation; SwiGLU is the gated unit of the DeepSeek-V3 and Llama-4
+    expert MLPs the configurations come from.  The gate+up GEMM's output columns [0, H) are the gate
+    and [H, 2H) the up projection of each expert."""
+    g = np.asarray(gate, dtype=np.float64)
+    return g / (1.0 + np.exp(-g)) * np.asarray(up, dtype=np.float64)

@@ -247,3 +247,32 @@ def test_dual_is_both_layouts_of_the_routed_rows():
     assert np.array_equal(q2, qx) and np.array_equal(s2, sx)
     qo2, so2 = mx_quantize_colwise(x, None, 64)
     assert np.array_equal(qT2, qo2) and np.array_equal(sT2, so2)
+
+
+def test_swiglu_against_torch_and_closed_forms():
+    """silu(g) * u against torch's CPU silu (a library routine), and its closed forms."""
+    import torch
+    from oracle import swiglu
+    rng = np.random.default_rng(7)
+    g = rng.standard_normal(5000) * 6
+    u = rng.standard_normal(5000)
+    want = (torch.nn.functional.silu(torch.from_numpy(g)) * torch.from_numpy(u)).numpy()
+    assert np.allclose(swiglu(g, u), want, rtol=1e-14, atol=1e-300)
+    assert swiglu(0.0, 3.0) == 0.0 and swiglu(1.0, 1.0) == 1.0 / (1.0 + np.exp(-1.0))
+    assert swiglu(60.0, 2.0) == 120.0 and abs(swiglu(-60.0, 2.0) + 120.0 * np.exp(-60.0)) < 1e-36
+
+
+def test_quantise_values_matches_bf16_path():
+    """The value quantiser equals the bf16-pattern quantiser on bf16-representable inputs, and on
+    float32 values it follows the same rule (exponent from the float32 amax)."""
+    from oracle import mx_quantize_rowwise_values
+    rng = np.random.default_rng(8)
+    x = f32_to_bf16_bits((rng.standard_normal((64, 96)) * np.where(rng.random((64, 96)) < 0.02, 100, 1))
+                         .astype(np.float32))
+    q1, s1 = mx_quantize_rowwise(x)
+    q2, s2 = mx_quantize_rowwise_values(bf16_bits_to_f64(x))
+    assert np.array_equal(q1, q2) and np.array_equal(s1, s2)
+    v = rng.standard_normal((8, 32)).astype(np.float32).astype(np.float64)
+    v[0, 0] = 3.0 * 2.0 ** 20                       # amax with exponent field 127 + 21
+    q, s = mx_quantize_rowwise_values(v)
+    assert s[0, 0] == 127 + 21 - 8
