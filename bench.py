@@ -332,6 +332,39 @@ def mxfp4_leg(m, torch, wl, keep, steps=5, sample_rows=64):
     return out
 
 
+def swiglu_leg(m, torch, lay, dev_in, steps=10):
+    """The gate+up forward with SwiGLU and the MX quantisation of H in the GEMM epilogue, against the
+    same outputs produced unfused: the forward GEMM writing bf16 Y, the activation by torch
+    elementwise ops (a comparison path only), and the row-wise MX quantiser on bf16 H."""
+    G, M, N, K = lay.G, lay.M, lay.N, lay.K
+    H = N // 2
+    x, w, _, offs = dev_in
+    w2 = w.view(G * N, K)
+    qx, sx = m.mx_quantize_rowwise(x)
+    qw, sw = m.mx_quantize_rowwise(w2)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    qh = torch.empty((M, H), dtype=torch.uint8, device=x.device)
+    sh = torch.empty((M, H // 32), dtype=torch.uint8, device=x.device)
+    f = 2.0 * M * N * K
+    fused = [Op("fused", "gemm", lambda: m.mx_grouped_gemm_fwd_swiglu(qx, sx, qw, sw, offs, N, y=y, qh=qh, sh=sh), f,
+                "")]
+    hb = {}
+    unfused = [
+        Op("fwd", "gemm", lambda: m.mx_grouped_gemm_fwd(qx, sx, qw, sw, offs, N, "bf16", y=y), f, ""),
+        Op("act", "quant", lambda: hb.update(h=(torch.nn.functional.silu(y[:, :H].float()) * y[:, H:].float())
+                                             .to(torch.bfloat16)), M * N * 2 + M * H * 2, ""),
+        Op("quant_h", "quant", lambda: m.mx_quantize_rowwise(hb["h"], qh, sh), M * H * QUANT_BYTES_PER_ELEM, ""),
+    ]
+    ms_f = time_ops(torch, fused, steps, 2)
+    ms_u = time_ops(torch, unfused, steps, 2)
+    out = {"layer": lay.name, "fused_ms": round(ms_f, 4), "unfused_ms": round(ms_u, 4),
+           "fused_tflops": round(f / (ms_f * 1e-3) / 1e12, 1),
+           "unfused_ops": {o.name: op_summary(o) for o in unfused}}
+    del y, qh, sh, hb
+    torch.cuda.empty_cache()
+    return out
+
+
 def blockwise_leg(m, torch, steps=5, sample_rows=256):
     """DeepSeek-style blockwise FP8 (1x128 activation tiles, 128x128 weight blocks, 128-token blocks
     for the weight gradient, fp32 scales, promotion every 128) against MXFP8 on the same
@@ -546,6 +579,7 @@ def main():
         del sops, q_ops
         torch.cuda.empty_cache()
         extra["mxfp4_step"] = mxfp4_leg(m, torch, wl, keep)
+        extra["swiglu_fused_forward"] = swiglu_leg(m, torch, wl.layers[0], keep[0][0])
         del keep, ops
         torch.cuda.empty_cache()
         extra["blockwise_vs_mx"] = blockwise_leg(m, torch)

@@ -141,6 +141,21 @@ mxmoe_status mx_grouped_gemm_fwd(const uint8_t* qx, const uint8_t* sx,
                                  const int32_t* offs, int32_t G, int64_t M, int64_t N, int64_t K,
                                  void* y, mxmoe_dtype ydt, void* stream);
 
+/* fwd with the gated activation fused into the epilogue (the output side of an expert MLP):
+ * W [G*N, K] holds each expert's gate rows [g N, g N + H) and up rows [g N + H, (g+1) N), N = 2H.
+ *   y  bf16 [M, N]: the pre-activations Y = X W_g^T (kept for the backward pass);
+ *   qh [M, H], sh [M, H/32]: H = silu(gate) * up, silu(z) = z / (1 + e^-z), formed in fp32 from the
+ *      GEMM's fp32 sums (hardware exponential and reciprocal: a few ulp relative) and MX-quantised
+ *      row-wise (the forward operand of the down GEMM) without H
+ *      ever reaching memory in a wider format (a reading: the pages name no activation; SwiGLU is
+ *      the gated unit of the DeepSeek-V3 / Llama-4 expert MLPs);
+ *   h  f32 [M, H] or NULL: H as formed before quantisation (for checking).
+ * Precise feed; N % 256 == 0; qx/sx, qw/sw and offs as for mx_grouped_gemm_fwd. */
+mxmoe_status mx_grouped_gemm_fwd_swiglu(const uint8_t* qx, const uint8_t* sx,
+                                        const uint8_t* qw, const uint8_t* sw,
+                                        const int32_t* offs, int32_t G, int64_t M, int64_t N, int64_t K,
+                                        void* y, uint8_t* qh, uint8_t* sh, float* h, void* stream);
+
 /* dgrad: dX[r, k] = sum_n dY[r, n] W[g*N + n, k]        for r in group g
  *        qdy/sdy = mx_quantize_rowwise(dY [M, N]);
  *        qwT/swT = mx_quantize_colwise(W [G*N, K], offs = NULL) with leading

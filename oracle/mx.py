@@ -234,4 +234,5 @@ def swiglu(gate, up):
     expert MLPs the configurations come from.  The gate+up GEMM's output columns [0, H) are the gate
     and [H, 2H) the up projection of each expert."""
     g = np.asarray(gate, dtype=np.float64)
-    return g / (1.0 + np.exp(-g)) * np.asarray(up, dtype=np.float64)
+    with np.errstate(over="ignore"):            # e^-g overflows to inf for g < -709: silu -> -0
+        return g / (1.0 + np.exp(-g)) * np.asarray(up, dtype=np.float64)

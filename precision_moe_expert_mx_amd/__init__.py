@@ -17,7 +17,7 @@ from typing import Optional, Tuple
 __all__ = [
     "LIB_PATH", "MxMoeError", "lib", "abi_version", "FEED_FP8",
     "mx_colwise_ld_min", "mx_quantize_rowwise", "mx_quantize_colwise", "mx_quantize_dual",
-    "mx_grouped_gemm_fwd", "mx_grouped_gemm_dgrad", "mx_grouped_gemm_wgrad",
+    "mx_grouped_gemm_fwd", "mx_grouped_gemm_dgrad", "mx_grouped_gemm_wgrad", "mx_grouped_gemm_fwd_swiglu",
     "fp8bw_quantize_act_1x128", "fp8bw_quantize_weight_128x128",
     "fp8bw_grouped_gemm_fwd", "fp8bw_grouped_gemm_dgrad", "mxmoe_check_offsets",
     "fp8bw_colwise_ld_min", "fp8bw_quantize_colwise_128", "fp8bw_grouped_gemm_wgrad",
@@ -46,6 +46,7 @@ _SIGS = {
     "mx_quantize_colwise": (ctypes.c_int, [_p, _i64, _i64, _p, _i32, _p, _p, _i64, _p]),
     "mx_quantize_dual": (ctypes.c_int, [_p, _i64, _i64, _p, _i64, _p, _i32, _p, _p, _p, _p, _i64, _p]),
     "mx_grouped_gemm_fwd": (ctypes.c_int, [_p, _p, _p, _p, _p, _i32, _i64, _i64, _i64, _p, ctypes.c_int, _p]),
+    "mx_grouped_gemm_fwd_swiglu": (ctypes.c_int, [_p, _p, _p, _p, _p, _i32, _i64, _i64, _i64, _p, _p, _p, _p, _p]),
     "mx_grouped_gemm_dgrad": (ctypes.c_int, [_p, _p, _p, _p, _i64, _p, _i32, _i64, _i64, _i64, _p, ctypes.c_int, _p]),
     "mx_grouped_gemm_wgrad": (ctypes.c_int, [_p, _p, _p, _p, _i64, _p, _i32, _i64, _i64, _i64, _p, ctypes.c_int, _p]),
     "fp8bw_quantize_act_1x128": (ctypes.c_int, [_p, _i64, _i64, _p, _p, _p]),
@@ -212,6 +213,26 @@ def mx_grouped_gemm_fwd(qx, sx, qw, sw, offs, N: int, out_dtype: str = "f32", y=
     _check("mx_grouped_gemm_fwd", lib().mx_grouped_gemm_fwd(_ptr(qx), _ptr(sx), _ptr(qw), _ptr(sw), _ptr(offs), G, M,
                                                             N, K, _ptr(y), cdt, _stream_handle(stream)))
     return y
+
+
+def mx_grouped_gemm_fwd_swiglu(qx, sx, qw, sw, offs, N: int, y=None, qh=None, sh=None, h=None,
+                               with_h: bool = False, stream=None):
+    """Forward of the gate+up GEMM (W rows: gate then up of each expert, N = 2H) with SwiGLU and the
+    row-wise MX quantisation of H in the epilogue.  Returns (y bf16 [M, N], qh [M, H], sh [M, H/32])
+    and, with with_h (or h given), H in fp32 [M, H] as a fourth item."""
+    torch = _torch()
+    M, K = qx.shape
+    G = offs.numel() - 1
+    H = N // 2
+    y = _empty((M, N), torch.bfloat16, qx) if y is None else y
+    qh = _empty((M, H), torch.uint8, qx) if qh is None else qh
+    sh = _empty((M, H // 32), torch.uint8, qx) if sh is None else sh
+    if with_h and h is None:
+        h = _empty((M, H), torch.float32, qx)
+    _check("mx_grouped_gemm_fwd_swiglu", lib().mx_grouped_gemm_fwd_swiglu(
+        _ptr(qx), _ptr(sx), _ptr(qw), _ptr(sw), _ptr(offs), G, M, N, K, _ptr(y), _ptr(qh), _ptr(sh), _ptr(h),
+        _stream_handle(stream)))
+    return (y, qh, sh) if h is None else (y, qh, sh, h)
 
 
 def mx_grouped_gemm_dgrad(qdy, sdy, qwT, swT, offs, K: int, out_dtype: str = "f32", dx=None, stream=None, fast: bool = False):

@@ -203,6 +203,32 @@ mxmoe_status mx_grouped_gemm_fwd(const uint8_t* qx, const uint8_t* sx, const uin
   return mx_gemm_common(kFwd, "mx_grouped_gemm_fwd", qx, sx, qw, sw, 0, offs, G, M, N, K, y, (int)ydt, stream);
 }
 
+mxmoe_status mx_grouped_gemm_fwd_swiglu(const uint8_t* qx, const uint8_t* sx, const uint8_t* qw, const uint8_t* sw,
+                                        const int32_t* offs, int32_t G, int64_t M, int64_t N, int64_t K, void* y,
+                                        uint8_t* qh, uint8_t* sh, float* h, void* stream) {
+  const char* fn = "mx_grouped_gemm_fwd_swiglu";
+  TRY(check_gemm_common(fn, offs, G, M, N, K, y, MXMOE_BF16));
+  if (N % 256) return fail(MXMOE_ERR_SHAPE, "%s: N = 2H must be a multiple of 256 (N=%lld)", fn, (long long)N);
+  TRY(check_ptr(fn, "A operand", qx, 16));
+  TRY(check_ptr(fn, "A scales", sx, 4));
+  TRY(check_ptr(fn, "B operand", qw, 16));
+  TRY(check_ptr(fn, "B scales", sw, 4));
+  TRY(check_ptr(fn, "qh", qh, 16));
+  TRY(check_ptr(fn, "sh", sh, 4));
+  if (h && !aligned(h, 16)) return fail(MXMOE_ERR_ALIGN, "%s: h not 16-byte aligned", fn);
+  GemmArgs p;
+  memset(&p, 0, sizeof p);
+  p.a = qx; p.sa = sx; p.b = qw; p.sb = sw; p.offs = offs; p.out = y;
+  p.M = M; p.N = N; p.K = K; p.G = G;
+  p.out_bf16 = 1;
+  p.feed = kFeedPrecise;
+  p.lda = K; p.ldsa = K / 32; p.ldb = K; p.ldsb = K / 32;
+  p.act_q = qh; p.act_s = sh; p.act_dbg = h;
+  if (M == 0) return ok();
+  TRY(check_device());
+  return launched(launch_mx_gemm(kFwd, p, (hipStream_t)stream), fn);
+}
+
 mxmoe_status mx_grouped_gemm_dgrad(const uint8_t* qdy, const uint8_t* sdy, const uint8_t* qwT, const uint8_t* swT,
                                    int64_t ldw, const int32_t* offs, int32_t G, int64_t M, int64_t N, int64_t K,
                                    void* dx, mxmoe_dtype dxdt, void* stream) {

@@ -76,6 +76,17 @@ __device__ __forceinline__ uint32_t cvt2_e4m3(uint32_t old, uint32_t w, uint32_t
   return __builtin_bit_cast(uint32_t, o);
 }
 
+// Four fp32 values -> four E4M3 bytes with the power-of-two scale `scale`; magnitudes are first
+// clamped to lim = 448 * scale so that values rounding above 448 saturate.
+__device__ __forceinline__ uint32_t cvt4_f32_e4m3_scaled(float a, float b, float c, float d, float lim, float scale) {
+  const float ca = copysignf(fminf(fabsf(a), lim), a), cb = copysignf(fminf(fabsf(b), lim), b);
+  const float cc = copysignf(fminf(fabsf(c), lim), c), cd = copysignf(fminf(fabsf(d), lim), d);
+  v2s o = v2s{0, 0};
+  o = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(o, ca, cb, scale, false);
+  o = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(o, cc, cd, scale, true);
+  return __builtin_bit_cast(uint32_t, o);
+}
+
 // Four bf16 (two dwords) -> four E4M3 bytes.
 __device__ __forceinline__ uint32_t cvt4_e4m3(uint32_t w0, uint32_t w1, uint32_t clamp_pk, float scale) {
   uint32_t r = cvt2_e4m3<false>(0u, w0, clamp_pk, scale);
@@ -181,6 +192,12 @@ struct GemmArgs {
   int32_t feed;       // GemmFeed
   int32_t scale_dword;  // MX: every row's scale bytes of a stage form aligned dwords
   int32_t fp4;          // MX operands are E2M1 (two per byte; leading dimensions in bytes)
+  // forward with the gated activation in the epilogue: out = Y bf16 [M, 2H] (gate | up), plus
+  // H = silu(gate) * up MX-quantised row-wise into act_q [M, H] / act_s [M, H/32], and H in fp32 into
+  // act_dbg [M, H] when not NULL
+  uint8_t* act_q;
+  uint8_t* act_s;
+  float* act_dbg;
 };
 
 hipError_t launch_mx_gemm(int mode, const GemmArgs& a, hipStream_t st);

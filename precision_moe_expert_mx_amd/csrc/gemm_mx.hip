@@ -225,7 +225,89 @@ __device__ __forceinline__ void stage_barrier() {
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-template <int MODE, int FEED, bool SDW, bool FP4>
+// Gated forward epilogue (precise feed, 32x32 fragments, 8 waves 2 x 4).  Waves wn = 0, 1 hold the
+// gate columns of the tile's 128 hidden units, waves 2, 3 the up columns of the same units.  Every
+// wave writes its pre-activations as bf16 to Y (gate at column u, up at H + u); the up waves hand
+// their fp32 values to the gate waves through LDS, which form H = silu(gate) * up in fp32 and
+// MX-quantise it row-wise: a row's 32-column block is one fragment, split between lanes l and l ^ 32.
+template <typename Acc>
+__device__ __forceinline__ void act_epilogue(const GemmArgs& p, const Tile& t, char* lds, Acc (&acc)[WM / 32][WN / 32]) {
+  constexpr int NI = WM / 32, NJ = WN / 32;
+  constexpr int kUpPitch = BN / 2 + 4;            // floats per LDS row (padded against bank conflicts)
+  static_assert(BM * kUpPitch * 4 <= kLds, "up tile must fit in LDS");
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int wm = w / kWavesN, wn = w % kWavesN;
+  const int64_t H = p.N / 2;
+  const bool up_wave = wn >= kWavesN / 2;
+  const int ucol0 = WN * (wn % (kWavesN / 2)) + 4 * (lane / 32);    // tile-local hidden column of fragment 0
+  const int64_t hcol0 = (int64_t)t.nt * (BN / 2) + ucol0;          // global hidden column
+  const int row_lim = t.rows;
+  const int lrow = WM * wm + lane % 32;
+  float* up = (float*)lds;
+
+  // pre-activations (bf16) and the up values to LDS
+  stage_barrier();                                  // every wave is done with the last stage
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int r = lrow + 32 * i;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int c = ucol0 + 32 * j + 8 * q;
+        const float v0 = acc[i][j][4 * q], v1 = acc[i][j][4 * q + 1], v2 = acc[i][j][4 * q + 2], v3 = acc[i][j][4 * q + 3];
+        if (up_wave) *(float4*)(up + r * kUpPitch + c) = make_float4(v0, v1, v2, v3);
+        if (r < row_lim) {
+          const int64_t yc = (up_wave ? H : 0) + (int64_t)t.nt * (BN / 2) + c;
+          const uint2 wv = make_uint2(f32_to_bf16_bits(v0) | (f32_to_bf16_bits(v1) << 16),
+                                      f32_to_bf16_bits(v2) | (f32_to_bf16_bits(v3) << 16));
+          *(uint2*)((uint16_t*)p.out + (t.row0 + r) * p.N + yc) = wv;
+        }
+      }
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  if (up_wave) return;
+
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int r = lrow + 32 * i;
+    const int64_t grow = t.row0 + r;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      float h[16];
+      uint32_t amax = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 u = *(const float4*)(up + r * kUpPitch + ucol0 + 32 * j + 8 * q);
+        const float uu[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float g = acc[i][j][4 * q + k];
+          // silu with the hardware exponential and reciprocal (a few ulp; g -> -inf gives -0)
+          h[4 * q + k] = g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * uu[k];
+          amax = max(amax, __float_as_uint(h[4 * q + k]) & 0x7FFFFFFFu);
+        }
+      }
+      amax = max(amax, (uint32_t)__shfl_xor((int)amax, 32, 64));
+      // shared exponent of the block: floor(log2 amax) - 8 from the fp32 exponent field, clamped
+      const int e = max((int)(amax >> 23) - 135, -127);
+      const float sc = __uint_as_float((uint32_t)(e + 127) << 23);
+      const float lim = __uint_as_float(((uint32_t)(e + 135) << 23) | 0x600000u);   // 448 * 2^e
+      if (r >= row_lim) continue;
+      const int64_t hc = hcol0 + 32 * j;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t code = cvt4_f32_e4m3_scaled(h[4 * q], h[4 * q + 1], h[4 * q + 2], h[4 * q + 3], lim, sc);
+        *(uint32_t*)(p.act_q + grow * H + hc + 8 * q) = code;
+        if (p.act_dbg)
+          *(float4*)(p.act_dbg + grow * H + hc + 8 * q) = make_float4(h[4 * q], h[4 * q + 1], h[4 * q + 2], h[4 * q + 3]);
+      }
+      if (lane < 32) p.act_s[grow * (H / 32) + (hc - 4 * (lane / 32)) / 32] = (uint8_t)(e + 127);
+    }
+  }
+}
+
+template <int MODE, int FEED, bool SDW, bool FP4, bool ACT>
 __device__ __forceinline__ void run_tile(const GemmArgs& p, const Tile& t, char* lds) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
@@ -252,6 +334,12 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const Tile& t, char*
     return t.row0 + min(r, t.rows - 1);
   };
   auto b_row = [&](int r) -> int64_t {
+    if (ACT) {
+      // gated forward: tile columns [0, 128) are gate rows 128 nt .., [128, 256) the up rows of the
+      // same hidden units (N = 2H, up rows start at H)
+      const int64_t n = (r < BN / 2 ? 0 : p.N / 2 - BN / 2) + (int64_t)t.nt * (BN / 2) + r;
+      return (int64_t)t.g * p.N + n;
+    }
     const int64_t n = min((int64_t)t.nt * BN + r, b_rows_lim - 1);
     return MODE == kFwd ? (int64_t)t.g * p.N + n : n;
   };
@@ -485,6 +573,12 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const Tile& t, char*
     }
   }
 
+  if constexpr (ACT) {
+    static_assert(MODE == kFwd && FEED == kFeedPrecise && !FP4, "gated epilogue: precise forward only");
+    act_epilogue(p, t, lds, acc);
+    return;
+  }
+
   // ---- epilogue --------------------------------------------------------------------------------
   // The MFMAs take the B fragment as their first operand, so each accumulator holds a tile transposed:
   // lane l has output row (fragment row) l % 32 (l % 16 for the 16x16 shape) and, per group of four
@@ -523,13 +617,13 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const Tile& t, char*
   }
 }
 
-template <int MODE, int FEED, bool SDW, bool FP4 = false>
+template <int MODE, int FEED, bool SDW, bool FP4 = false, bool ACT = false>
 __global__ __launch_bounds__(NT, 1) void mx_grouped_gemm_kernel(GemmArgs p) {
   __shared__ __attribute__((aligned(16))) char lds[kLds];
   Tile t;
   if (!decode_tile<MODE>(p, lds, t)) return;     // uniform across the workgroup
   __syncthreads();                               // scheduler scratch is reused for operands
-  run_tile<MODE, FEED, SDW, FP4>(p, t, lds);
+  run_tile<MODE, FEED, SDW, FP4, ACT>(p, t, lds);
 }
 
 static_assert(4 * (kMaxG + 1) * 4 <= kStage, "scheduler scratch must fit in the first stage");
@@ -563,7 +657,10 @@ hipError_t launch_mx_gemm(int mode, const GemmArgs& args, hipStream_t st) {
   // a multiple of 4 bytes (wgrad expert columns start at arbitrary 32-blocks)
   p.scale_dword = mode != kWgrad && p.ldsa % 4 == 0 && p.ldsb % 4 == 0 && (p.N / 32) % 4 == 0;
   const dim3 g((unsigned)grid);
-  if (mode == kFwd) launch_mode<kFwd, true>(p, g, st);
+  if (mode == kFwd && p.act_q) {
+    if (!p.scale_dword) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((mx_grouped_gemm_kernel<kFwd, kFeedPrecise, true, false, true>), g, dim3(NT), 0, st, p);
+  } else if (mode == kFwd) launch_mode<kFwd, true>(p, g, st);
   else if (mode == kDgrad && p.scale_dword) launch_mode<kDgrad, true>(p, g, st);
   else if (mode == kDgrad) launch_mode<kDgrad, false>(p, g, st);
   else launch_mode<kWgrad, false>(p, g, st);

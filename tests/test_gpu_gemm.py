@@ -323,3 +323,51 @@ def test_blockwise_wgrad_full_size_sampled():
         k_idx = np.unique(np.concatenate([[0, lay.K - 1], rng.choice(lay.K, 24, replace=False)]))
         print(lay.name, "bw wgrad", _bw_wgrad_case(m, lay, "f32", groups, n_idx, k_idx))
         torch.cuda.empty_cache()
+
+
+def _swiglu_case(m, L, rows=None):
+    """Fused gate+up forward: Y against the oracle forward; the kernel's fp32 H against fp64 SwiGLU of
+    the oracle's Y within the propagated GEMM bound; qh / sh bit-exact against the oracle's MX
+    quantisation of that same fp32 H."""
+    offs = dev(L.offs)
+    qx, sx = m.mx_quantize_rowwise(dev(L.x))
+    qw, sw = m.mx_quantize_rowwise(dev(L.w))
+    y, qh, sh, h = m.mx_grouped_gemm_fwd_swiglu(qx, sx, qw, sw, offs, L.N, with_h=True)
+    H = L.N // 2
+    ref, bnd = oracle.mx_gemm_fwd(host(qx), host(sx), host(qw), host(sw), L.offs, L.N, rows=rows)
+    sel = slice(None) if rows is None else rows
+    worst_y = _check(_gpu_out(y)[sel], ref, bnd, "bf16", "swiglu y")
+    hg = host(h)[sel].astype(np.float64)
+    g, u = ref[:, :H], ref[:, H:]
+    tol_g = oracle.gemm.REL_TOL * bnd[:, :H] + 2.0 ** -24 * np.abs(g)
+    tol_u = oracle.gemm.REL_TOL * bnd[:, H:] + 2.0 ** -24 * np.abs(u)
+    href = oracle.swiglu(g, u)
+    with np.errstate(over="ignore"):
+        silu = g / (1.0 + np.exp(-g))
+    tol_h = 1.1 * tol_g * np.abs(u) + np.abs(silu) * tol_u + 4e-6 * np.abs(href) + 1e-30
+    err = np.abs(hg - href)
+    assert np.all(err <= tol_h), f"H: worst err/tol {np.max(err / tol_h):.3g}"
+    qo, so = oracle.mx_quantize_rowwise_values(hg)
+    assert np.array_equal(host(sh)[sel], so), "H scales differ from the oracle's quantisation of the kernel's H"
+    bad = np.argwhere(host(qh)[sel] != qo)
+    assert bad.size == 0, f"H codes differ at {bad[:5]}"
+    return worst_y, float(np.max(err / tol_h))
+
+
+def test_swiglu_fused_forward():
+    m = require_gpu()
+    rng = np.random.default_rng(45)
+    for sizes, N, K in (([0, 5, 130, 1, 300], 512, 256), ([257, 0, 17], 256, 384)):
+        L = _rand_layer(rng, sizes, N, K, w_std=0.05, outliers=0.001)
+        print("swiglu", sizes, _swiglu_case(m, L))
+
+
+def test_swiglu_fused_forward_full_size_sampled():
+    """DeepSeek-V3-671B shard gate+up (N = 2H = 4096, K = 7168), sampled rows."""
+    m = require_gpu()
+    lay = make_workload("dsv3_671b_shard", layers=["gate_up"]).layers[0]
+    rng = np.random.default_rng(46)
+    rows = np.unique(np.concatenate([[0, lay.M - 1], rng.choice(lay.M, 48, replace=False)]))
+    L = Layer(lay.offs, lay.x, lay.w.reshape(-1, lay.K), lay.dy, lay.N, lay.K)
+    print("swiglu full", _swiglu_case(m, L, rows=rows))
+    torch.cuda.empty_cache()
