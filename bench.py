@@ -183,27 +183,44 @@ def op_summary(op):
 
 
 # ------------------------------------------------------------------------------------------- traffic
-def read_traffic():
-    """Per-launch HBM bytes of the GEMM ops from the committed counter summary (None if stale)."""
-    if not os.path.exists(TRAFFIC_FILE):
+# Per-launch HBM bytes of the step's launches come from two rocprofv3 counter runs of this script
+# (FETCH_SIZE, then WRITE_SIZE); each summary carries a hash of the sources of the kernels it
+# covers and is ignored once they change.
+QUANT_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "quant_traffic_dsv3_671b_shard.txt")
+QUANT_SOURCES = [os.path.join(ROOT, "precision_moe_expert_mx_amd", "csrc", f) for f in ("quant_mx.hip", "common.h")]
+GEMM_NAMES = [f"{l}.{k}" for l in ("gate_up", "down") for k in ("fwd", "dgrad", "wgrad")]
+QUANT_NAMES = [f"{l}.quant_{t}_dual" for l in ("gate_up", "down") for t in ("x", "w", "dy")]
+
+
+def quant_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in QUANT_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(path=TRAFFIC_FILE, src_hash=None):
+    """Per-launch HBM bytes of the step's ops from a committed counter summary (None if stale)."""
+    if not os.path.exists(path):
         return None
     rec = None
-    with open(TRAFFIC_FILE) as f:
+    with open(path) as f:
         for line in f:
             line = line.strip()
             if line.startswith("{"):
                 rec = json.loads(line)
-    if not rec or rec.get("source_sha256") != gemm_source_hash():
+    if not rec or rec.get("source_sha256") != (src_hash or gemm_source_hash()):
         return None
     return rec.get("ops", {})
 
 
-def pmc_summary(fetch_csv: str, write_csv: str, out_path: str, cmds) -> None:
-    """Per-launch HBM bytes of the six GEMM launches of a step from two rocprofv3 counter runs of this
-    script (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each scaled by what the same counter
-    reads for the 1 GiB device copy the script performs before timing."""
+def pmc_summary(fetch_csv: str, write_csv: str, cmds) -> None:
+    """Per-launch HBM bytes of the six GEMM launches and the six dual-layout quantiser launches of a
+    step from two rocprofv3 counter runs of this script (FETCH_SIZE, then WRITE_SIZE, KiB per
+    dispatch), each scaled by what the same counter reads for the 1 GiB device copy the script
+    performs before timing."""
     import csv
-    names = [f"{l}.{k}" for l in ("gate_up", "down") for k in ("fwd", "dgrad", "wgrad")]
     res = {}
     factors = {}
     for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
@@ -217,21 +234,24 @@ def pmc_summary(fetch_csv: str, write_csv: str, out_path: str, cmds) -> None:
         copies = [d["v"] for d in disp if "copyBuffer" in d["name"]]
         cal_kib = max(copies)
         factors[counter] = (1 << 30) / (cal_kib * 1024.0)
-        gemms = [d["v"] for d in disp if "mx_grouped_gemm" in d["name"]]
-        for i, v in enumerate(gemms):
-            res.setdefault(names[i % 6], {}).setdefault(counter, []).append(v * 1024.0 * factors[counter])
-    ops = {n: round(float(np.mean(c["FETCH_SIZE"])) + float(np.mean(c["WRITE_SIZE"])))
-           for n, c in res.items()}
-    rec = {"source_sha256": gemm_source_hash(), "calibration": factors, "ops": ops,
-           "fetch": {n: round(float(np.mean(c["FETCH_SIZE"]))) for n, c in res.items()},
-           "write": {n: round(float(np.mean(c["WRITE_SIZE"]))) for n, c in res.items()}}
-    with open(out_path, "w") as f:
-        f.write("# HBM traffic per launch of the six grouped-GEMM launches of one step (DeepSeek-V3-671B expert shard)\n")
-        f.write("# bytes = counter KiB * 1024 * (2^30 / counter KiB of the 1 GiB device copy); commands (repository root):\n")
-        for c in cmds:
-            f.write(f"#   {c}\n")
-        f.write(json.dumps(rec) + "\n")
-    print(json.dumps(rec))
+        for key, names in (("mx_grouped_gemm", GEMM_NAMES), ("mx_colwise_kernel", QUANT_NAMES)):
+            launches = [d["v"] for d in disp if key in d["name"]]
+            for i, v in enumerate(launches):
+                res.setdefault(names[i % len(names)], {}).setdefault(counter, []).append(v * 1024.0 * factors[counter])
+    for path, names, src, what in ((TRAFFIC_FILE, GEMM_NAMES, gemm_source_hash(), "grouped-GEMM"),
+                                   (QUANT_TRAFFIC_FILE, QUANT_NAMES, quant_source_hash(), "dual-layout MX quantiser")):
+        sel = {n: res[n] for n in names if n in res}
+        rec = {"source_sha256": src, "calibration": factors,
+               "ops": {n: round(float(np.mean(c["FETCH_SIZE"])) + float(np.mean(c["WRITE_SIZE"]))) for n, c in sel.items()},
+               "fetch": {n: round(float(np.mean(c["FETCH_SIZE"]))) for n, c in sel.items()},
+               "write": {n: round(float(np.mean(c["WRITE_SIZE"]))) for n, c in sel.items()}}
+        with open(path, "w") as f:
+            f.write(f"# HBM traffic per launch of the six {what} launches of one step (DeepSeek-V3-671B expert shard)\n")
+            f.write("# bytes = counter KiB * 1024 * (2^30 / counter KiB of the 1 GiB device copy); commands (repository root):\n")
+            for c in cmds:
+                f.write(f"#   {c}\n")
+            f.write(json.dumps(rec) + "\n")
+        print(json.dumps(rec))
 
 
 # ------------------------------------------------------------------------------------------- CPU oracle
@@ -468,7 +488,7 @@ def main():
     ap.add_argument("--no-extra-legs", action="store_true",
                     help="skip the FP8-feed and blockwise legs (reported beside the headline)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
-                    help="write the GEMM traffic summary from two rocprofv3 counter runs of this script")
+                    help="write the GEMM and quantiser traffic summaries from two rocprofv3 counter runs of this script")
     args = ap.parse_args()
 
     if args.pmc_summary:
@@ -477,7 +497,7 @@ def main():
                 for c in ("FETCH_SIZE", "WRITE_SIZE")]
         cmds.append("python3 bench.py --pmc-summary gpurun_out/pmc_fetch_size/p_counter_collection.csv "
                     "gpurun_out/pmc_write_size/p_counter_collection.csv")
-        pmc_summary(args.pmc_summary[0], args.pmc_summary[1], TRAFFIC_FILE, cmds)
+        pmc_summary(args.pmc_summary[0], args.pmc_summary[1], cmds)
         return
 
     if args.gpus != 1:
@@ -503,7 +523,7 @@ def main():
     cal2 = torch.empty_like(cal)
     cal2.copy_(cal)
     torch.cuda.synchronize()
-    # its rate (1 GiB read + 1 GiB written) is the practical HBM ceiling the quantisers are compared to
+    # its rate (1 GiB read + 1 GiB written) is reported beside the quantisers' rate
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(5):
@@ -545,6 +565,16 @@ def main():
                 "flop_per_launch": dom.work, "algorithmic_bytes_per_launch": round(dom.bytes),
                 "avg_launch_ms": round(dom_ms, 4),
                 "frac_of_mxfp8_peak": round(achieved / MFMA_PEAK_TFLOPS["mxfp8"], 4)}
+
+    # the HBM-bound side: the longest dual-layout quantiser launch against the HBM peak
+    qdom = max((op for op in ops if op.kind == "quant"), key=lambda o: float(np.mean(o.ms)))
+    qdom_ms = float(np.mean(qdom.ms))
+    qach = qdom.work / (qdom_ms * 1e-3) / 1e9
+    qtraffic = read_traffic(QUANT_TRAFFIC_FILE, quant_source_hash())
+    quant_roofline = {"bound": "hbm", "achieved": round(qach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                      "frac": round(qach / HBM_PEAK_GBS, 4), "traffic": (qtraffic or {}).get(qdom.name),
+                      "op": qdom.name, "kernel": qdom.kernel, "algorithmic_bytes_per_launch": round(qdom.work),
+                      "avg_launch_ms": round(qdom_ms, 4)}
 
     extra = {"device_copy_gbps": round(copy_gbps, 1), "quant_frac_of_copy": round(quant_bytes / (quant_ms * 1e-3) / 1e9 / copy_gbps, 3)}
     if not args.no_extra_legs:
@@ -609,6 +639,7 @@ def main():
                    "step": "per layer: X, W, dY each quantised to both MX layouts in one launch + grouped GEMM fwd/dgrad/wgrad"},
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "quant_roofline": quant_roofline,
         "gemm_only_tflops": round(gemm_flops / (gemm_ms * 1e-3) / 1e12, 1),
         "gemm_frac_of_mxfp8_peak": round(gemm_flops / (gemm_ms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS["mxfp8"], 4),
         "quant_gbps": round(quant_bytes / (quant_ms * 1e-3) / 1e9, 1),
