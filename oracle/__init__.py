@@ -39,7 +39,7 @@ from .mx import (mx_block_exponent, mx_colwise_ld_min, mx_dequantize,
                  mxfp4_quantize_colwise, mxfp4_dequantize, mx_quantize_rowwise_values, swiglu)
 from .blockwise import (bw_quantize_act_1x128, bw_quantize_weight_128x128,
                         bw_dequantize_act, bw_dequantize_weight, bw_colwise_ld_min,
-                        bw_group_columns, bw_quantize_colwise_128)
+                        bw_group_columns, bw_quantize_colwise_128, pow2_scale)
 from .gemm import (mx_gemm_fwd, mx_gemm_dgrad, mx_gemm_wgrad, bw_gemm_fwd,
                    bw_gemm_dgrad, bw_gemm_wgrad, mxfp4_gemm_fwd, mxfp4_gemm_dgrad, mxfp4_gemm_wgrad, gemm_tolerance, check_gemm, bf16_round_f32)
 
@@ -48,7 +48,7 @@ __all__ = [
     "e4m3_encode_bruteforce", "e8m0_decode", "f32_round",
     "mx_block_exponent", "mx_colwise_ld_min", "mx_dequantize",
     "mx_quantize_colwise", "mx_quantize_rowwise", "mx_group_columns",
-    "bw_quantize_act_1x128", "bw_quantize_weight_128x128",
+    "bw_quantize_act_1x128", "bw_quantize_weight_128x128", "pow2_scale",
     "bw_dequantize_act", "bw_dequantize_weight",
     "mx_gemm_fwd", "mx_gemm_dgrad", "mx_gemm_wgrad", "bw_gemm_fwd",
     "bw_gemm_dgrad", "gemm_tolerance", "check_gemm", "bf16_round_f32",

@@ -11,6 +11,13 @@ elements are q = E4M3(fl32(v / s)) with the division again in float32, then
 rounded to nearest even and saturated at 448 (because s is rounded, the amax
 element can land just above 448).  A weight block's amax covers all
 128 x 128 entries.
+
+Power-of-two mode (pow2=True; the pages fix no scale format beyond fp32, and
+this optional mode is the plainest power-of-two variant): the scale is the
+smallest power of two s with 448 * s >= amax, at least 2^-126 (the smallest
+normal fp32) and 1 for an all-zero tile.  Dividing by it is exact, no element
+exceeds 448, and the fp32 scales stay exact under the GEMM's promotion
+products.
 """
 from __future__ import annotations
 
@@ -21,15 +28,33 @@ from .codecs import e4m3_decode, e4m3_encode
 TILE = 128
 
 
-def _scale_and_quantize(v32: np.ndarray, amax32: np.ndarray):
+def pow2_scale(amax) -> np.ndarray:
+    """Smallest power of two s with 448 * s >= amax, clamped below at 2^-126; 1 where amax = 0.
+    The exponent starts from a guess and is stepped until 448 * 2^e >= amax > 448 * 2^(e-1)
+    (every product is exact in float64)."""
+    a = np.asarray(amax, dtype=np.float64)
+    nz = a > 0
+    e = np.where(nz, np.frexp(np.where(nz, a, 1.0))[1] - 9, 0).astype(np.int64)
+    for _ in range(4):
+        e = e + (nz & (448.0 * np.ldexp(1.0, e) < a))
+        e = e - (nz & (448.0 * np.ldexp(1.0, e - 1) >= a))
+    assert np.all(~nz | ((448.0 * np.ldexp(1.0, e) >= a) & (448.0 * np.ldexp(1.0, e - 1) < a)))
+    e = np.maximum(e, -126)
+    return np.where(nz, np.ldexp(1.0, e), 1.0).astype(np.float32)
+
+
+def _scale_and_quantize(v32: np.ndarray, amax32: np.ndarray, pow2: bool = False):
     """v32, amax32 float32 (amax broadcastable); returns (q, s float32)."""
-    s = (amax32 / np.float32(448.0)).astype(np.float32)      # IEEE fp32 division
-    s = np.where(amax32 == 0, np.float32(1.0), s).astype(np.float32)
-    y = (v32 / s).astype(np.float32)                          # IEEE fp32 division
+    if pow2:
+        s = pow2_scale(amax32)
+    else:
+        s = (amax32 / np.float32(448.0)).astype(np.float32)      # IEEE fp32 division
+        s = np.where(amax32 == 0, np.float32(1.0), s).astype(np.float32)
+    y = (v32 / s).astype(np.float32)                              # IEEE fp32 division
     return e4m3_encode(y.astype(np.float64)), s
 
 
-def bw_quantize_act_1x128(x_bits):
+def bw_quantize_act_1x128(x_bits, pow2: bool = False):
     """bf16 [R, C] -> (q uint8 [R, C], s float32 [R, C/128]), one scale per 1x128 tile."""
     x_bits = np.asarray(x_bits, dtype=np.uint16)
     R, C = x_bits.shape
@@ -37,11 +62,11 @@ def bw_quantize_act_1x128(x_bits):
         raise ValueError("C must be a multiple of 128")
     v = (x_bits.astype(np.uint32) << 16).view(np.float32).reshape(R, C // TILE, TILE)
     amax = np.max(np.abs(v), axis=2, keepdims=True)
-    q, s = _scale_and_quantize(v, amax)
+    q, s = _scale_and_quantize(v, amax, pow2)
     return q.reshape(R, C), s.reshape(R, C // TILE)
 
 
-def bw_quantize_weight_128x128(w_bits):
+def bw_quantize_weight_128x128(w_bits, pow2: bool = False):
     """bf16 [R, C] (R = G*N) -> (q uint8 [R, C], s float32 [R/128, C/128])."""
     w_bits = np.asarray(w_bits, dtype=np.uint16)
     R, C = w_bits.shape
@@ -49,7 +74,7 @@ def bw_quantize_weight_128x128(w_bits):
         raise ValueError("R and C must be multiples of 128")
     v = (w_bits.astype(np.uint32) << 16).view(np.float32).reshape(R // TILE, TILE, C // TILE, TILE)
     amax = np.max(np.abs(v), axis=(1, 3), keepdims=True)
-    q, s = _scale_and_quantize(v, amax)
+    q, s = _scale_and_quantize(v, amax, pow2)
     return q.reshape(R, C), s.reshape(R // TILE, C // TILE)
 
 
@@ -80,7 +105,7 @@ def bw_group_columns(offs):
     return TILE * start[:-1], nb
 
 
-def bw_quantize_colwise_128(x_bits, offs, ld: int):
+def bw_quantize_colwise_128(x_bits, offs, ld: int, pow2: bool = False):
     """bf16 [R, C] quantised in 128-row blocks of one column, restarting at every group's first
     row -- the weight-gradient operands of the blockwise recipe, whose contraction runs over the
     tokens of one expert (reading: the page shows only the forward pass; the backward pass quantises
@@ -107,7 +132,7 @@ def bw_quantize_colwise_128(x_bits, offs, ld: int):
             z = min(a + TILE, r1)
             v = (x_bits[a:z].astype(np.uint32) << 16).view(np.float32)     # [n, C]
             amax = np.max(np.abs(v), axis=0, keepdims=True)
-            q, sc = _scale_and_quantize(v, amax)
+            q, sc = _scale_and_quantize(v, amax, pow2)
             c = int(col0[g]) + TILE * b
             qT[:, c:c + (z - a)] = q.T
             sT[:, c // TILE] = sc[0]
