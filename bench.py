@@ -387,7 +387,8 @@ def swiglu_leg(m, torch, lay, dev_in, steps=10):
 
 def blockwise_leg(m, torch, steps=5, sample_rows=256):
     """DeepSeek-style blockwise FP8 (1x128 activation tiles, 128x128 weight blocks, 128-token blocks
-    for the weight gradient, fp32 scales, promotion every 128) against MXFP8 on the same
+    for the weight gradient, fp32 scales, promotion every 128), also in its power-of-two scale mode,
+    against MXFP8 on the same
     DeepSeek-V3-16B expert-layer tensors: forward, dgrad and wgrad, each recipe with its own
     quantisers.  Accuracy: relative Frobenius error of each recipe's fp32 Y, dX (sampled rows) and dW
     (two experts, sampled n and k) against fp64 products of the original bf16 tensors."""
@@ -401,24 +402,30 @@ def blockwise_leg(m, torch, steps=5, sample_rows=256):
         offs = to_device(torch, lay.offs)
         f = 2.0 * M * N * K
         rec = {}
-        # blockwise
-        bq = {}
+        # blockwise, with fp32 scales amax / 448 and in the power-of-two scale mode
         ldb = m.fp8bw_colwise_ld_min(M, G)
-        ops_bw = [
-            Op("quant_x", "quant", lambda: bq.update(x=m.fp8bw_quantize_act_1x128(x)), M * K * QUANT_BYTES_PER_ELEM, ""),
-            Op("quant_w", "quant", lambda: bq.update(w=m.fp8bw_quantize_weight_128x128(w, transposed=True)),
-               G * N * K * (QUANT_BYTES_PER_ELEM + 1), ""),
-            Op("fwd", "gemm", lambda: bq.update(y=m.fp8bw_grouped_gemm_fwd(*bq["x"], *bq["w"][:2], offs, N, "f32")), f, ""),
-            Op("quant_dy", "quant", lambda: bq.update(dy=m.fp8bw_quantize_act_1x128(dy)), M * N * QUANT_BYTES_PER_ELEM, ""),
-            Op("dgrad", "gemm", lambda: bq.update(dx=m.fp8bw_grouped_gemm_dgrad(*bq["dy"], bq["w"][2], bq["w"][1], offs, K,
-                                                                                 "f32")), f, ""),
-            Op("quant_dy_col", "quant", lambda: bq.update(dyc=m.fp8bw_quantize_colwise_128(dy, offs, ld=ldb)),
-               M * N * QUANT_BYTES_PER_ELEM, ""),
-            Op("quant_x_col", "quant", lambda: bq.update(xc=m.fp8bw_quantize_colwise_128(x, offs, ld=ldb)),
-               M * K * QUANT_BYTES_PER_ELEM, ""),
-            Op("wgrad", "gemm", lambda: bq.update(dw=m.fp8bw_grouped_gemm_wgrad(*bq["dyc"], *bq["xc"], offs, M, "f32")),
-               f, ""),
-        ]
+
+        def bw_ops(bq, p2):
+            return [
+                Op("quant_x", "quant", lambda: bq.update(x=m.fp8bw_quantize_act_1x128(x, pow2=p2)),
+                   M * K * QUANT_BYTES_PER_ELEM, ""),
+                Op("quant_w", "quant", lambda: bq.update(w=m.fp8bw_quantize_weight_128x128(w, transposed=True, pow2=p2)),
+                   G * N * K * (QUANT_BYTES_PER_ELEM + 1), ""),
+                Op("fwd", "gemm", lambda: bq.update(y=m.fp8bw_grouped_gemm_fwd(*bq["x"], *bq["w"][:2], offs, N, "f32")),
+                   f, ""),
+                Op("quant_dy", "quant", lambda: bq.update(dy=m.fp8bw_quantize_act_1x128(dy, pow2=p2)),
+                   M * N * QUANT_BYTES_PER_ELEM, ""),
+                Op("dgrad", "gemm", lambda: bq.update(dx=m.fp8bw_grouped_gemm_dgrad(*bq["dy"], bq["w"][2], bq["w"][1], offs,
+                                                                                     K, "f32")), f, ""),
+                Op("quant_dy_col", "quant", lambda: bq.update(dyc=m.fp8bw_quantize_colwise_128(dy, offs, ld=ldb, pow2=p2)),
+                   M * N * QUANT_BYTES_PER_ELEM, ""),
+                Op("quant_x_col", "quant", lambda: bq.update(xc=m.fp8bw_quantize_colwise_128(x, offs, ld=ldb, pow2=p2)),
+                   M * K * QUANT_BYTES_PER_ELEM, ""),
+                Op("wgrad", "gemm", lambda: bq.update(dw=m.fp8bw_grouped_gemm_wgrad(*bq["dyc"], *bq["xc"], offs, M,
+                                                                                     "f32")), f, ""),
+            ]
+        bq, bq2 = {}, {}
+        ops_bw, ops_bw2 = bw_ops(bq, False), bw_ops(bq2, True)
         mq = {}
         ld = G * N
         ldm = m.mx_colwise_ld_min(M, G)
@@ -436,7 +443,7 @@ def blockwise_leg(m, torch, steps=5, sample_rows=256):
             Op("wgrad", "gemm", lambda: mq.update(dw=m.mx_grouped_gemm_wgrad(*mq["dyc"], *mq["xc"], offs, M, "f32")),
                f, ""),
         ]
-        for name, ops_ in (("blockwise", ops_bw), ("mxfp8", ops_mx)):
+        for name, ops_ in (("blockwise", ops_bw), ("blockwise_pow2", ops_bw2), ("mxfp8", ops_mx)):
             ms = time_ops(torch, ops_, steps, 1)
             gm = sum(float(np.mean(o.ms)) for o in ops_ if o.kind == "gemm")
             rec[name] = {"ms_fwd_bwd_with_quant": round(ms, 4),
@@ -449,7 +456,7 @@ def blockwise_leg(m, torch, steps=5, sample_rows=256):
         wf = lay.w.reshape(G, N, K)
         y_ref = np.stack([xb[i] @ bf16_to_f64(wf[g]).T for i, g in enumerate(grp)])
         dx_ref = np.stack([dyb[i] @ bf16_to_f64(wf[g]) for i, g in enumerate(grp)])
-        for name, q in (("blockwise", bq), ("mxfp8", mq)):
+        for name, q in (("blockwise", bq), ("blockwise_pow2", bq2), ("mxfp8", mq)):
             yg = q["y"][torch.from_numpy(rows).cuda()].double().cpu().numpy()
             dxg = q["dx"][torch.from_numpy(rows).cuda()].double().cpu().numpy()
             rec[name]["rel_fro_err_y"] = float(np.linalg.norm(yg - y_ref) / np.linalg.norm(y_ref))
@@ -459,7 +466,7 @@ def blockwise_leg(m, torch, steps=5, sample_rows=256):
         gs = [int(np.argmax(sizes)), int(rng.choice(np.flatnonzero(sizes > 0)))]
         n_idx = np.sort(rng.choice(N, 64, replace=False))
         k_idx = np.sort(rng.choice(K, 64, replace=False))
-        for name, q in (("blockwise", bq), ("mxfp8", mq)):
+        for name, q in (("blockwise", bq), ("blockwise_pow2", bq2), ("mxfp8", mq)):
             num = den = 0.0
             for g in gs:
                 r0, r1 = int(lay.offs[g]), int(lay.offs[g + 1])
@@ -469,7 +476,7 @@ def blockwise_leg(m, torch, steps=5, sample_rows=256):
                 den += float(np.sum(ref ** 2))
             rec[name]["rel_fro_err_dw"] = float(np.sqrt(num / den))
         out["layers"][lay.name] = rec
-        del x, w, dy, bq, mq, ops_bw, ops_mx
+        del x, w, dy, bq, bq2, mq, ops_bw, ops_bw2, ops_mx
         torch.cuda.empty_cache()
     return out
 

@@ -265,6 +265,20 @@ mxmoe_status fp8bw_quantize_colwise_128(const void* x_bf16, int64_t R, int64_t C
                                         const int32_t* offs, int32_t G,
                                         uint8_t* qT, float* sT, int64_t ld, void* stream);
 
+/* Power-of-two scale mode of the three blockwise quantisers (aifind.ru DeepSeek-V3 article, section
+ * "Low-precision training: FP8 Framework" fixes the 1x128 / 128x128 tiles and fp32 scales only; this
+ * optional mode is a reading): each tile's scale is the smallest power of two s with 448 s >= amax,
+ * at least 2^-126, and 1 for an all-zero tile; codes E4M3(v / s) (an exact division), so no element
+ * saturates.  Same arguments, layouts, validation and errors as the functions above; the outputs
+ * feed the same blockwise GEMMs. */
+mxmoe_status fp8bw_quantize_act_1x128_pow2(const void* x_bf16, int64_t R, int64_t C,
+                                           uint8_t* q, float* s, void* stream);
+mxmoe_status fp8bw_quantize_weight_128x128_pow2(const void* w_bf16, int64_t R, int64_t C,
+                                                uint8_t* q, float* s, uint8_t* qT, void* stream);
+mxmoe_status fp8bw_quantize_colwise_128_pow2(const void* x_bf16, int64_t R, int64_t C,
+                                             const int32_t* offs, int32_t G,
+                                             uint8_t* qT, float* sT, int64_t ld, void* stream);
+
 /* fp8bw_grouped_gemm_wgrad: dW[g, n, k] = sum_b sdyT[n, c_g/128 + b] sxT[k, c_g/128 + b] *
  *                                         sum_{j in block b} qdyT[n, j] qxT[k, j]
  * over expert g's 128-token blocks b (each block's FP8 partial promoted with its two

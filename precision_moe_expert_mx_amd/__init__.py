@@ -62,6 +62,9 @@ _SIGS = {
     "mxfp4_grouped_gemm_wgrad": (ctypes.c_int, [_p, _p, _p, _p, _i64, _p, _i32, _i64, _i64, _i64, _p, ctypes.c_int,
                                                 _p]),
     "fp8bw_quantize_colwise_128": (ctypes.c_int, [_p, _i64, _i64, _p, _i32, _p, _p, _i64, _p]),
+    "fp8bw_quantize_act_1x128_pow2": (ctypes.c_int, [_p, _i64, _i64, _p, _p, _p]),
+    "fp8bw_quantize_weight_128x128_pow2": (ctypes.c_int, [_p, _i64, _i64, _p, _p, _p, _p]),
+    "fp8bw_quantize_colwise_128_pow2": (ctypes.c_int, [_p, _i64, _i64, _p, _i32, _p, _p, _i64, _p]),
     "fp8bw_grouped_gemm_wgrad": (ctypes.c_int, [_p, _p, _p, _p, _i64, _p, _i32, _i64, _i64, _i64, _p, ctypes.c_int,
                                                 _p]),
     "mxmoe_check_offsets": (ctypes.c_int, [_p, _i32, _i64, _p]),
@@ -328,20 +331,22 @@ def mxfp4_grouped_gemm_wgrad(qdyT, sdyT, qxT, sxT, offs, M: int, out_dtype: str 
 
 
 # ---------------------------------------------------------------- blockwise FP8
-def fp8bw_quantize_act_1x128(x, q=None, s=None, stream=None):
+def fp8bw_quantize_act_1x128(x, q=None, s=None, stream=None, pow2: bool = False):
+    """x bf16 [R, C] -> (q [R, C], s f32 [R, C/128]); pow2 selects the power-of-two scale mode."""
     torch = _torch()
     x = _bf16_bits(x)
     R, C = x.shape
     q = _empty((R, C), torch.uint8, x) if q is None else q
     s = _empty((R, C // 128), torch.float32, x) if s is None else s
-    _check("fp8bw_quantize_act_1x128", lib().fp8bw_quantize_act_1x128(_ptr(x), R, C, _ptr(q), _ptr(s),
-                                                                      _stream_handle(stream)))
+    fn = "fp8bw_quantize_act_1x128" + ("_pow2" if pow2 else "")
+    _check(fn, getattr(lib(), fn)(_ptr(x), R, C, _ptr(q), _ptr(s), _stream_handle(stream)))
     return q, s
 
 
-def fp8bw_quantize_weight_128x128(w, q=None, s=None, qT=None, transposed: bool = False, stream=None):
+def fp8bw_quantize_weight_128x128(w, q=None, s=None, qT=None, transposed: bool = False, stream=None,
+                                  pow2: bool = False):
     """w bf16 [R, C] -> (q [R, C], s f32 [R/128, C/128]) or, with transposed=True (or qT given),
-    (q, s, qT [C, R]) where qT is the dgrad operand."""
+    (q, s, qT [C, R]) where qT is the dgrad operand; pow2 selects the power-of-two scale mode."""
     torch = _torch()
     w = _bf16_bits(w)
     R, C = w.shape
@@ -349,8 +354,8 @@ def fp8bw_quantize_weight_128x128(w, q=None, s=None, qT=None, transposed: bool =
     s = _empty((R // 128, C // 128), torch.float32, w) if s is None else s
     if transposed and qT is None:
         qT = _empty((C, R), torch.uint8, w)
-    _check("fp8bw_quantize_weight_128x128", lib().fp8bw_quantize_weight_128x128(_ptr(w), R, C, _ptr(q), _ptr(s),
-                                                                                _ptr(qT), _stream_handle(stream)))
+    fn = "fp8bw_quantize_weight_128x128" + ("_pow2" if pow2 else "")
+    _check(fn, getattr(lib(), fn)(_ptr(w), R, C, _ptr(q), _ptr(s), _ptr(qT), _stream_handle(stream)))
     return (q, s) if qT is None else (q, s, qT)
 
 
@@ -382,8 +387,10 @@ def fp8bw_colwise_ld_min(M: int, G: int) -> int:
     return int(lib().fp8bw_colwise_ld_min(M, G))
 
 
-def fp8bw_quantize_colwise_128(x, offs=None, G: int = 1, ld: Optional[int] = None, qT=None, sT=None, stream=None):
-    """x bf16 [R, C] -> (qT uint8 [C, ld], sT float32 [C, ld/128]): 128-row blocks restarting per group."""
+def fp8bw_quantize_colwise_128(x, offs=None, G: int = 1, ld: Optional[int] = None, qT=None, sT=None, stream=None,
+                               pow2: bool = False):
+    """x bf16 [R, C] -> (qT uint8 [C, ld], sT float32 [C, ld/128]): 128-row blocks restarting per group;
+    pow2 selects the power-of-two scale mode."""
     torch = _torch()
     x = _bf16_bits(x)
     R, C = x.shape
@@ -393,8 +400,8 @@ def fp8bw_quantize_colwise_128(x, offs=None, G: int = 1, ld: Optional[int] = Non
         ld = fp8bw_colwise_ld_min(R, G) if offs is not None else 128 * ((R + 127) // 128)
     qT = _empty((C, ld), torch.uint8, x) if qT is None else qT
     sT = _empty((C, ld // 128), torch.float32, x) if sT is None else sT
-    _check("fp8bw_quantize_colwise_128", lib().fp8bw_quantize_colwise_128(_ptr(x), R, C, _ptr(offs), G, _ptr(qT),
-                                                                          _ptr(sT), ld, _stream_handle(stream)))
+    fn = "fp8bw_quantize_colwise_128" + ("_pow2" if pow2 else "")
+    _check(fn, getattr(lib(), fn)(_ptr(x), R, C, _ptr(offs), G, _ptr(qT), _ptr(sT), ld, _stream_handle(stream)))
     return qT, sT
 
 

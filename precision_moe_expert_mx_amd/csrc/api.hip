@@ -307,20 +307,27 @@ mxmoe_status mxfp4_grouped_gemm_wgrad(const uint8_t* qdyT, const uint8_t* sdyT, 
   return mx_gemm_common(kWgrad, fn, qdyT, sdyT, qxT, sxT, ld, offs, G, M, N, K, dw, (int)dwdt, stream, true);
 }
 
-mxmoe_status fp8bw_quantize_act_1x128(const void* x, int64_t R, int64_t C, uint8_t* q, float* s, void* stream) {
-  const char* fn = "fp8bw_quantize_act_1x128";
+static mxmoe_status bw_act_impl(const char* fn, const void* x, int64_t R, int64_t C, uint8_t* q, float* s, bool pow2,
+                                void* stream) {
   if (R < 0 || C <= 0 || C % 128) return fail(MXMOE_ERR_SHAPE, "%s: need R >= 0, C > 0, C %% 128 == 0", fn);
   if (R == 0) return ok();
   TRY(check_ptr(fn, "x", x, 16));
   TRY(check_ptr(fn, "q", q, 16));
   TRY(check_ptr(fn, "s", s, 4));
   TRY(check_device());
-  return launched(launch_bw_act((const uint16_t*)x, R, C, q, s, (hipStream_t)stream), fn);
+  return launched(launch_bw_act((const uint16_t*)x, R, C, q, s, pow2, (hipStream_t)stream), fn);
 }
 
-mxmoe_status fp8bw_quantize_weight_128x128(const void* w, int64_t R, int64_t C, uint8_t* q, float* s, uint8_t* qT,
-                                           void* stream) {
-  const char* fn = "fp8bw_quantize_weight_128x128";
+mxmoe_status fp8bw_quantize_act_1x128(const void* x, int64_t R, int64_t C, uint8_t* q, float* s, void* stream) {
+  return bw_act_impl("fp8bw_quantize_act_1x128", x, R, C, q, s, false, stream);
+}
+
+mxmoe_status fp8bw_quantize_act_1x128_pow2(const void* x, int64_t R, int64_t C, uint8_t* q, float* s, void* stream) {
+  return bw_act_impl("fp8bw_quantize_act_1x128_pow2", x, R, C, q, s, true, stream);
+}
+
+static mxmoe_status bw_weight_impl(const char* fn, const void* w, int64_t R, int64_t C, uint8_t* q, float* s,
+                                   uint8_t* qT, bool pow2, void* stream) {
   if (R < 0 || C <= 0 || R % 128 || C % 128)
     return fail(MXMOE_ERR_SHAPE, "%s: need R %% 128 == 0, C > 0, C %% 128 == 0", fn);
   if (R / 128 > 65535 || C / 128 > INT32_MAX) return fail(MXMOE_ERR_SHAPE, "%s: too many blocks", fn);
@@ -330,7 +337,17 @@ mxmoe_status fp8bw_quantize_weight_128x128(const void* w, int64_t R, int64_t C, 
   TRY(check_ptr(fn, "s", s, 4));
   if (qT) TRY(check_ptr(fn, "qT", qT, 16));
   TRY(check_device());
-  return launched(launch_bw_weight((const uint16_t*)w, R, C, q, s, qT, (hipStream_t)stream), fn);
+  return launched(launch_bw_weight((const uint16_t*)w, R, C, q, s, qT, pow2, (hipStream_t)stream), fn);
+}
+
+mxmoe_status fp8bw_quantize_weight_128x128(const void* w, int64_t R, int64_t C, uint8_t* q, float* s, uint8_t* qT,
+                                           void* stream) {
+  return bw_weight_impl("fp8bw_quantize_weight_128x128", w, R, C, q, s, qT, false, stream);
+}
+
+mxmoe_status fp8bw_quantize_weight_128x128_pow2(const void* w, int64_t R, int64_t C, uint8_t* q, float* s, uint8_t* qT,
+                                                void* stream) {
+  return bw_weight_impl("fp8bw_quantize_weight_128x128_pow2", w, R, C, q, s, qT, true, stream);
 }
 
 int64_t fp8bw_colwise_ld_min(int64_t M, int32_t G) {
@@ -338,9 +355,8 @@ int64_t fp8bw_colwise_ld_min(int64_t M, int32_t G) {
   return 128 * ((M + 127 * (int64_t)G + 127) / 128);
 }
 
-mxmoe_status fp8bw_quantize_colwise_128(const void* x, int64_t R, int64_t C, const int32_t* offs, int32_t G,
-                                        uint8_t* qT, float* sT, int64_t ld, void* stream) {
-  const char* fn = "fp8bw_quantize_colwise_128";
+static mxmoe_status bw_colwise_impl(const char* fn, const void* x, int64_t R, int64_t C, const int32_t* offs,
+                                    int32_t G, uint8_t* qT, float* sT, int64_t ld, bool pow2, void* stream) {
   if (R < 0 || C <= 0 || C % 128) return fail(MXMOE_ERR_SHAPE, "%s: need R >= 0, C > 0, C %% 128 == 0 (R=%lld C=%lld)",
                                              fn, (long long)R, (long long)C);
   if (R > INT32_MAX) return fail(MXMOE_ERR_SHAPE, "%s: R too large", fn);
@@ -354,7 +370,17 @@ mxmoe_status fp8bw_quantize_colwise_128(const void* x, int64_t R, int64_t C, con
   TRY(check_ptr(fn, "qT", qT, 16));
   TRY(check_ptr(fn, "sT", sT, 4));
   TRY(check_device());
-  return launched(launch_bw_colwise((const uint16_t*)x, R, C, offs, G, qT, sT, ld, (hipStream_t)stream), fn);
+  return launched(launch_bw_colwise((const uint16_t*)x, R, C, offs, G, qT, sT, ld, pow2, (hipStream_t)stream), fn);
+}
+
+mxmoe_status fp8bw_quantize_colwise_128(const void* x, int64_t R, int64_t C, const int32_t* offs, int32_t G,
+                                        uint8_t* qT, float* sT, int64_t ld, void* stream) {
+  return bw_colwise_impl("fp8bw_quantize_colwise_128", x, R, C, offs, G, qT, sT, ld, false, stream);
+}
+
+mxmoe_status fp8bw_quantize_colwise_128_pow2(const void* x, int64_t R, int64_t C, const int32_t* offs, int32_t G,
+                                             uint8_t* qT, float* sT, int64_t ld, void* stream) {
+  return bw_colwise_impl("fp8bw_quantize_colwise_128_pow2", x, R, C, offs, G, qT, sT, ld, true, stream);
 }
 
 static mxmoe_status bw_gemm_common(int mode, const char* fn, const uint8_t* a, const float* sa, const uint8_t* b,

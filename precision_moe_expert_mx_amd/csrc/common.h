@@ -170,9 +170,9 @@ hipError_t launch_mx_dual(const uint16_t* x, int64_t R, int64_t C, const int32_t
                           const int32_t* offs, int32_t G, uint8_t* q, uint8_t* s, uint8_t* qT, uint8_t* sT, int64_t ld,
                           hipStream_t st);
 hipError_t launch_bw_colwise(const uint16_t* x, int64_t R, int64_t C, const int32_t* offs, int32_t G, uint8_t* qT,
-                             float* sT, int64_t ld, hipStream_t st);
-hipError_t launch_bw_act(const uint16_t* x, int64_t R, int64_t C, uint8_t* q, float* s, hipStream_t st);
-hipError_t launch_bw_weight(const uint16_t* w, int64_t R, int64_t C, uint8_t* q, float* s, uint8_t* qT,
+                             float* sT, int64_t ld, bool pow2, hipStream_t st);
+hipError_t launch_bw_act(const uint16_t* x, int64_t R, int64_t C, uint8_t* q, float* s, bool pow2, hipStream_t st);
+hipError_t launch_bw_weight(const uint16_t* w, int64_t R, int64_t C, uint8_t* q, float* s, uint8_t* qT, bool pow2,
                             hipStream_t st);
 
 enum GemmMode { kFwd = 0, kDgrad = 1, kWgrad = 2 };

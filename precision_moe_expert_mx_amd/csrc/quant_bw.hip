@@ -3,6 +3,11 @@
 // "Low-precision training: FP8 Framework").  Scale s = fl32(amax / 448) by IEEE division (1 for an
 // all-zero tile); elements E4M3(fl32(v / s)), nearest even.  |v / s| <= 448 (1 + 2^-23)^2 < 464,
 // so the hardware conversion (which rounds to nearest even) never overflows and no clamp is needed.
+//
+// Power-of-two mode (POW2): the scale is instead the smallest power of two s with 448 s >= amax, at
+// least 2^-126 (1 for an all-zero tile).  From the bf16 magnitude bits of amax (exponent field E,
+// mantissa m): amax / 448 = ((1 + m/128) / 1.75) 2^(E - 135), so e = E - 135, plus 1 when m > 96
+// (significand above 1.75); subnormal amax falls below the clamp.  Dividing by s is exact.
 #include "common.h"
 
 namespace mxmoe {
@@ -32,12 +37,18 @@ __device__ __forceinline__ uint32_t magmax8(const uint4& v) {
   return max(a, b);
 }
 
+template <bool POW2>
 __device__ __forceinline__ float bw_scale_from_amax_bits(uint32_t m) {
+  if (POW2) {
+    const int e = max((int)(m >> 7) - 135 + ((m & 0x7Fu) > 96u ? 1 : 0), -126);
+    return m == 0 ? 1.0f : __uint_as_float((uint32_t)(e + 127) << 23);
+  }
   float amax = __uint_as_float(m << 16);
   return m == 0 ? 1.0f : __fdiv_rn(amax, 448.0f);
 }
 
 // 1x128 activation tiles: 16 lanes per tile (16 bytes each), reduced with xor shuffles inside the 16.
+template <bool POW2>
 __global__ __launch_bounds__(256) void bw_act_kernel(const uint4* __restrict__ x, int64_t nchunks,
                                                      uint2* __restrict__ q, float* __restrict__ s) {
   int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -45,7 +56,7 @@ __global__ __launch_bounds__(256) void bw_act_kernel(const uint4* __restrict__ x
   uint32_t m = magmax8(v);
 #pragma unroll
   for (int d = 1; d < 16; d <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, d, 64));
-  float sc = bw_scale_from_amax_bits(m);
+  float sc = bw_scale_from_amax_bits<POW2>(m);
   if (i < nchunks) {
     q[i] = bw_convert8(v, sc);
     if ((threadIdx.x & 15) == 0) s[i >> 4] = sc;
@@ -58,6 +69,7 @@ __global__ __launch_bounds__(256) void bw_act_kernel(const uint4* __restrict__ x
 // the operand layout of the dgrad GEMM, which contracts over the rows.
 constexpr int kBwTPitch = 128 + 16;     // LDS bytes per transposed row (padded against bank conflicts)
 
+template <bool POW2>
 __global__ __launch_bounds__(256) void bw_weight_kernel(const uint16_t* __restrict__ w, int64_t R, int64_t C,
                                                         uint8_t* __restrict__ q, float* __restrict__ s,
                                                         uint8_t* __restrict__ qT) {
@@ -79,7 +91,7 @@ __global__ __launch_bounds__(256) void bw_weight_kernel(const uint16_t* __restri
   if ((t & 63) == 0) red[t >> 6] = m;
   __syncthreads();
   m = max(max(red[0], red[1]), max(red[2], red[3]));
-  float sc = bw_scale_from_amax_bits(m);
+  float sc = bw_scale_from_amax_bits<POW2>(m);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int rr = r + 16 * i;
@@ -107,18 +119,25 @@ __global__ __launch_bounds__(256) void bw_weight_kernel(const uint16_t* __restri
   }
 }
 
-hipError_t launch_bw_act(const uint16_t* x, int64_t R, int64_t C, uint8_t* q, float* s, hipStream_t st) {
+hipError_t launch_bw_act(const uint16_t* x, int64_t R, int64_t C, uint8_t* q, float* s, bool pow2, hipStream_t st) {
   int64_t nchunks = R * C / 8;
   if (nchunks == 0) return hipSuccess;
-  hipLaunchKernelGGL(bw_act_kernel, dim3((unsigned)((nchunks + 255) / 256)), dim3(256), 0, st,
-                     (const uint4*)x, nchunks, (uint2*)q, s);
+  const dim3 grid((unsigned)((nchunks + 255) / 256));
+  if (pow2)
+    hipLaunchKernelGGL(bw_act_kernel<true>, grid, dim3(256), 0, st, (const uint4*)x, nchunks, (uint2*)q, s);
+  else
+    hipLaunchKernelGGL(bw_act_kernel<false>, grid, dim3(256), 0, st, (const uint4*)x, nchunks, (uint2*)q, s);
   return hipGetLastError();
 }
 
-hipError_t launch_bw_weight(const uint16_t* w, int64_t R, int64_t C, uint8_t* q, float* s, uint8_t* qT, hipStream_t st) {
+hipError_t launch_bw_weight(const uint16_t* w, int64_t R, int64_t C, uint8_t* q, float* s, uint8_t* qT, bool pow2,
+                            hipStream_t st) {
   if (R == 0 || C == 0) return hipSuccess;
-  hipLaunchKernelGGL(bw_weight_kernel, dim3((unsigned)(C / 128), (unsigned)(R / 128)), dim3(256), 0, st, w, R, C, q, s,
-                     qT);
+  const dim3 grid((unsigned)(C / 128), (unsigned)(R / 128));
+  if (pow2)
+    hipLaunchKernelGGL(bw_weight_kernel<true>, grid, dim3(256), 0, st, w, R, C, q, s, qT);
+  else
+    hipLaunchKernelGGL(bw_weight_kernel<false>, grid, dim3(256), 0, st, w, R, C, q, s, qT);
   return hipGetLastError();
 }
 
@@ -138,6 +157,7 @@ hipError_t launch_bw_weight(const uint16_t* w, int64_t R, int64_t C, uint8_t* q,
 constexpr int kBwColPitch = 128 + 16;   // LDS bytes per output (qT) row, padded against bank conflicts
 constexpr int kBwMaxGroupsLds = 1024;
 
+template <bool POW2>
 __global__ __launch_bounds__(256) void bw_colwise_kernel(const uint16_t* __restrict__ x, int64_t R, int64_t C,
                                                          const int32_t* __restrict__ offs, int G,
                                                          uint8_t* __restrict__ qT, float* __restrict__ sT,
@@ -186,7 +206,7 @@ __global__ __launch_bounds__(256) void bw_colwise_kernel(const uint16_t* __restr
     a0 = max(a0, red[k][cp] & 0xFFFFu);
     a1 = max(a1, red[k][cp] >> 16);
   }
-  const float s0 = bw_scale_from_amax_bits(a0), s1 = bw_scale_from_amax_bits(a1);
+  const float s0 = bw_scale_from_amax_bits<POW2>(a0), s1 = bw_scale_from_amax_bits<POW2>(a1);
   uint32_t o0[8], o1[8];
 #pragma unroll
   for (int d = 0; d < 8; ++d) {
@@ -219,12 +239,16 @@ __global__ __launch_bounds__(256) void bw_colwise_kernel(const uint16_t* __restr
 }
 
 hipError_t launch_bw_colwise(const uint16_t* x, int64_t R, int64_t C, const int32_t* offs, int32_t G, uint8_t* qT,
-                             float* sT, int64_t ld, hipStream_t st) {
+                             float* sT, int64_t ld, bool pow2, hipStream_t st) {
   const int64_t nwg = (ld / 128) * (C / 128);
   if (nwg == 0) return hipSuccess;
   if (nwg > 0x7FFFFFFF) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(bw_colwise_kernel, dim3((unsigned)nwg), dim3(256), 0, st, x, R, C, offs, offs ? G : 1, qT, sT,
-                     ld);
+  if (pow2)
+    hipLaunchKernelGGL(bw_colwise_kernel<true>, dim3((unsigned)nwg), dim3(256), 0, st, x, R, C, offs, offs ? G : 1, qT,
+                       sT, ld);
+  else
+    hipLaunchKernelGGL(bw_colwise_kernel<false>, dim3((unsigned)nwg), dim3(256), 0, st, x, R, C, offs, offs ? G : 1, qT,
+                       sT, ld);
   return hipGetLastError();
 }
 

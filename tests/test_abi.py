@@ -78,6 +78,10 @@ def test_quantiser_argument_errors():
     assert _status(L, "fp8bw_quantize_colwise_128", A16, 100, 128, A16, 4, A16, A16, 600, None)[0] == 3
     assert _status(L, "fp8bw_quantize_colwise_128", A16, 100, 128, A16, 4, A16, A16, 512, None)[0] == 2
     assert _status(L, "fp8bw_quantize_colwise_128", A16, 200, 128, None, 0, A16, A16, 128, None)[0] == 2   # one group
+    # the power-of-two mode validates the same way
+    assert _status(L, "fp8bw_quantize_act_1x128_pow2", A16, 4, 96, A16, A16, None)[0] == 2
+    assert _status(L, "fp8bw_quantize_weight_128x128_pow2", A16, 128, 128, A16, A16, BAD, None)[0] == 3
+    assert _status(L, "fp8bw_quantize_colwise_128_pow2", A16, 100, 128, A16, 4, A16, A16, 512, None)[0] == 2
 
 
 def test_gemm_argument_errors():
