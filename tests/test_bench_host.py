@@ -1,0 +1,72 @@
+"""Host-side logic of bench.py (no GPU): the one-GPU guard, and the per-launch traffic summaries built
+from rocprofv3 counter CSVs (dispatch order -> op names, calibration on the 1 GiB copy, source hashes)."""
+import csv
+import json
+import os
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, cwd=ROOT, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+
+
+def _write_csv(path, counter, rows):
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+        w.writeheader()
+        for i, (name, value) in enumerate(rows):
+            # a counter summed over two hardware instances, as rocprofv3 reports per-block values
+            w.writerow({"Dispatch_Id": i + 1, "Kernel_Name": name, "Counter_Name": counter, "Counter_Value": value / 2})
+            w.writerow({"Dispatch_Id": i + 1, "Kernel_Name": name, "Counter_Name": counter, "Counter_Value": value / 2})
+
+
+def test_pmc_summary_maps_dispatches_and_calibrates(tmp_path, monkeypatch):
+    gemm = "void mxmoe::(anonymous namespace)::mx_grouped_gemm_kernel<0, 0, true, false, false>(mxmoe::GemmArgs)"
+    quant = "void mxmoe::mx_colwise_kernel<true, false, true, false>(...)"
+    copy = "__amd_rocclr_copyBuffer"
+    # step order of one layer: quant x, quant w, fwd, quant dy, dgrad, wgrad; two layers
+    order = [quant, quant, gemm, quant, gemm, gemm] * 2
+    fetch_kib = 2 * (1 << 20)            # the 1 GiB copy reads as 2 GiB: factor 1/2
+    write_kib = 1 << 20
+    fetch = [(copy, 8.0), (copy, fetch_kib)] + [(n, 1000.0 * (i + 1)) for i, n in enumerate(order)]
+    write = [(copy, 4.0), (copy, write_kib)] + [(n, 10.0 * (i + 1)) for i, n in enumerate(order)]
+    fcsv, wcsv = tmp_path / "f.csv", tmp_path / "w.csv"
+    _write_csv(fcsv, "FETCH_SIZE", fetch)
+    _write_csv(wcsv, "WRITE_SIZE", write)
+    gfile, qfile = tmp_path / "gemm.txt", tmp_path / "quant.txt"
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(gfile))
+    monkeypatch.setattr(bench, "QUANT_TRAFFIC_FILE", str(qfile))
+    bench.pmc_summary(str(fcsv), str(wcsv), ["cmd a", "cmd b"])
+    g = json.loads(gfile.read_text().splitlines()[-1])
+    q = json.loads(qfile.read_text().splitlines()[-1])
+    assert g["source_sha256"] == bench.gemm_source_hash() and q["source_sha256"] == bench.quant_source_hash()
+    assert abs(g["calibration"]["FETCH_SIZE"] - 0.5) < 1e-12 and g["calibration"]["WRITE_SIZE"] == 1.0
+    # dispatch k of `order` (1-based) read 1000 k KiB fetched and 10 k KiB written
+    want = {}
+    gi = qi = 0
+    for k, n in enumerate(order, start=1):
+        name = bench.GEMM_NAMES[gi] if n == gemm else bench.QUANT_NAMES[qi]
+        if n == gemm:
+            gi += 1
+        else:
+            qi += 1
+        want[name] = (1000.0 * k * 1024 * 0.5, 10.0 * k * 1024)
+    for name in bench.GEMM_NAMES:
+        assert g["fetch"][name] == round(want[name][0]) and g["write"][name] == round(want[name][1])
+        assert g["ops"][name] == round(want[name][0] + want[name][1])
+    for name in bench.QUANT_NAMES:
+        assert q["ops"][name] == round(want[name][0] + want[name][1])
+    assert "cmd a" in gfile.read_text() and "cmd b" in qfile.read_text()
+    # the summaries are read back while the kernel sources are unchanged, and ignored otherwise
+    assert bench.read_traffic(str(gfile)) == g["ops"]
+    assert bench.read_traffic(str(qfile), bench.quant_source_hash()) == q["ops"]
+    assert bench.read_traffic(str(qfile), "0" * 16) is None
