@@ -21,6 +21,39 @@ typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 // full-rate block-scaled FP8 MFMA (sums truncated per 8-element run, see gemm.hip).
 enum GemmFeed { kFeedPrecise = 0, kFeedFast = 1 };
 
+// ---- memory and lane helpers ---------------------------------------------------------------------
+// Non-temporal 16-byte loads and 8 / 4-byte stores for streaming kernels (every byte touched once).
+typedef uint32_t v4u_ __attribute__((ext_vector_type(4)));
+typedef uint32_t v2u_ __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint4 load16_nt(const uint4* p) {
+  const v4u_ v = __builtin_nontemporal_load((const v4u_*)p);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ void store8_nt(uint2* p, uint2 v) { __builtin_nontemporal_store(v2u_{v.x, v.y}, (v2u_*)p); }
+__device__ __forceinline__ void store4_nt(uint32_t* p, uint32_t v) { __builtin_nontemporal_store(v, p); }
+
+__device__ __forceinline__ uint32_t quad_max(uint32_t m) {
+  // quad_perm [1,0,3,2] then [2,3,0,1]: every lane of the quad ends with the quad's maximum
+  m = max(m, (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0xB1, 0xF, 0xF, false));
+  m = max(m, (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0x4E, 0xF, 0xF, false));
+  return m;
+}
+
+// Maximum over each group of 8 lanes: quad permutes, then the half-row mirror (lane i of an 8-lane
+// group with lane 7 - i, in the other quad).  bound_ctrl with an old value of 0 (the identity of an
+// unsigned max) lets each permute fold into the max as one DPP instruction.
+__device__ __forceinline__ uint32_t oct_max(uint32_t m) {
+  m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0xB1, 0xF, 0xF, true));
+  m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x4E, 0xF, 0xF, true));
+  return max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x141, 0xF, 0xF, true));
+}
+
+// Maximum over each row of 16 lanes: the 8-lane maximum, then the row mirror (lane i with 15 - i).
+__device__ __forceinline__ uint32_t hex_max(uint32_t m) {
+  m = oct_max(m);
+  return max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x140, 0xF, 0xF, true));
+}
+
 // ---- MX scale helpers (E8M0 shared exponent of a 32-block) -------------------------------------
 // The magnitude bits of a finite bf16 value order like the value itself, so amax is an integer max
 // over (bits & 0x7FFF).  floor(log2 v) of that magnitude: exponent field - 127 for normals, and for

@@ -7,7 +7,16 @@
 // Power-of-two mode (POW2): the scale is instead the smallest power of two s with 448 s >= amax, at
 // least 2^-126 (1 for an all-zero tile).  From the bf16 magnitude bits of amax (exponent field E,
 // mantissa m): amax / 448 = ((1 + m/128) / 1.75) 2^(E - 135), so e = E - 135, plus 1 when m > 96
-// (significand above 1.75); subnormal amax falls below the clamp.  Dividing by s is exact.
+// (significand above 1.75); subnormal amax falls below the clamp.  Dividing by s is exact, so it is a
+// multiplication by 2^-e.
+//
+// fl32(v / s) without a division per element: with y = fl32(1 / s), formed once per tile,
+//   q0 = fl32(v y),  r = v - s q0 (exact, one FMA),  q = fl32(q0 + r y) (one FMA)
+// is the correctly rounded quotient (Markstein's division correction: y within half an ulp of 1/s,
+// q0 within an ulp of v/s) as long as the remainder does not underflow.  Checked on the host for every
+// bf16 amax >= 2^-59 and every bf16 v with |v| <= amax, both signs, with IEEE and with flushed
+// denormals: the E4M3 codes equal those of the IEEE quotient.  v = -0 yields +0 through the FMAs, so
+// the sign of v is put back.  Tiles with a smaller amax divide per element.
 #include "common.h"
 
 namespace mxmoe {
@@ -21,14 +30,72 @@ __device__ __forceinline__ uint32_t cvt4_f32_e4m3(float a, float b, float c, flo
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-// Quantise 8 bf16 (one uint4) with scale s -> 8 bytes.
-__device__ __forceinline__ uint2 bw_convert8(const uint4& v, float s) {
+// A tile's scale s and what its elements are divided with: y = 1 / s (exact in the power-of-two
+// mode, fl32(1 / s) otherwise) and whether the tile's amax admits the FMA correction.
+struct BwScale {
+  float s, y;
+  bool fma;
+};
+constexpr uint32_t kBwFmaMinAmax = 68u << 7;   // bf16 bits of 2^-59
+
+template <bool POW2>
+__device__ __forceinline__ BwScale bw_scale(uint32_t m) {
+  BwScale r;
+  if (POW2) {
+    const int e = max((int)(m >> 7) - 135 + ((m & 0x7Fu) > 96u ? 1 : 0), -126);
+    r.s = m == 0 ? 1.0f : __uint_as_float((uint32_t)(e + 127) << 23);
+    r.y = m == 0 ? 1.0f : __uint_as_float((uint32_t)(127 - e) << 23);
+    r.fma = true;
+  } else {
+    r.s = m == 0 ? 1.0f : __fdiv_rn(__uint_as_float(m << 16), 448.0f);
+    r.fma = m >= kBwFmaMinAmax;
+    r.y = r.fma ? __fdiv_rn(1.0f, r.s) : 0.0f;
+  }
+  return r;
+}
+
+// fl32(v / s) for an element v of the tile (see the header).
+template <bool POW2>
+__device__ __forceinline__ float bw_quot(float v, const BwScale& sc) {
+  if (POW2) return v * sc.y;
+  const float q0 = v * sc.y;
+  const float r = __builtin_fmaf(-sc.s, q0, v);
+  return __builtin_copysignf(__builtin_fmaf(r, sc.y, q0), v);
+}
+
+// Quantise 8 bf16 (one uint4) of one tile -> 8 bytes.
+template <bool POW2>
+__device__ __forceinline__ uint2 bw_convert8(const uint4& v, const BwScale& sc) {
   uint2 o;
-  o.x = cvt4_f32_e4m3(__fdiv_rn(bf16_lo(v.x), s), __fdiv_rn(bf16_hi(v.x), s),
-                      __fdiv_rn(bf16_lo(v.y), s), __fdiv_rn(bf16_hi(v.y), s));
-  o.y = cvt4_f32_e4m3(__fdiv_rn(bf16_lo(v.z), s), __fdiv_rn(bf16_hi(v.z), s),
-                      __fdiv_rn(bf16_lo(v.w), s), __fdiv_rn(bf16_hi(v.w), s));
+  if (POW2 || sc.fma) {
+    o.x = cvt4_f32_e4m3(bw_quot<POW2>(bf16_lo(v.x), sc), bw_quot<POW2>(bf16_hi(v.x), sc),
+                        bw_quot<POW2>(bf16_lo(v.y), sc), bw_quot<POW2>(bf16_hi(v.y), sc));
+    o.y = cvt4_f32_e4m3(bw_quot<POW2>(bf16_lo(v.z), sc), bw_quot<POW2>(bf16_hi(v.z), sc),
+                        bw_quot<POW2>(bf16_lo(v.w), sc), bw_quot<POW2>(bf16_hi(v.w), sc));
+  } else {
+    const float s = sc.s;
+    o.x = cvt4_f32_e4m3(__fdiv_rn(bf16_lo(v.x), s), __fdiv_rn(bf16_hi(v.x), s),
+                        __fdiv_rn(bf16_lo(v.y), s), __fdiv_rn(bf16_hi(v.y), s));
+    o.y = cvt4_f32_e4m3(__fdiv_rn(bf16_lo(v.z), s), __fdiv_rn(bf16_hi(v.z), s),
+                        __fdiv_rn(bf16_lo(v.w), s), __fdiv_rn(bf16_hi(v.w), s));
+  }
   return o;
+}
+
+// Four elements of one column (bf16 in the low or high half of each dword) of one tile -> 4 codes.
+template <bool POW2, bool HI>
+__device__ __forceinline__ uint32_t bw_convert4_col(const uint32_t* w, const BwScale& sc) {
+  float f[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) f[k] = HI ? bf16_hi(w[k]) : bf16_lo(w[k]);
+  if (POW2 || sc.fma) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) f[k] = bw_quot<POW2>(f[k], sc);
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) f[k] = __fdiv_rn(f[k], sc.s);
+  }
+  return cvt4_f32_e4m3(f[0], f[1], f[2], f[3]);
 }
 
 __device__ __forceinline__ uint32_t magmax8(const uint4& v) {
@@ -37,29 +104,32 @@ __device__ __forceinline__ uint32_t magmax8(const uint4& v) {
   return max(a, b);
 }
 
-template <bool POW2>
-__device__ __forceinline__ float bw_scale_from_amax_bits(uint32_t m) {
-  if (POW2) {
-    const int e = max((int)(m >> 7) - 135 + ((m & 0x7Fu) > 96u ? 1 : 0), -126);
-    return m == 0 ? 1.0f : __uint_as_float((uint32_t)(e + 127) << 23);
-  }
-  float amax = __uint_as_float(m << 16);
-  return m == 0 ? 1.0f : __fdiv_rn(amax, 448.0f);
-}
+// 1x128 activation tiles: 16 lanes per tile (16 bytes each, one DPP row), amax reduced by DPP within
+// the row.  A workgroup of 512 lanes covers 2 x 512 consecutive 16-byte chunks with non-temporal loads
+// and stores (every byte is touched once), the launch shape of the MX row-wise quantiser.
+constexpr int kBwActThreads = 512;
+constexpr int kBwActUnroll = 2;
 
-// 1x128 activation tiles: 16 lanes per tile (16 bytes each), reduced with xor shuffles inside the 16.
 template <bool POW2>
-__global__ __launch_bounds__(256) void bw_act_kernel(const uint4* __restrict__ x, int64_t nchunks,
-                                                     uint2* __restrict__ q, float* __restrict__ s) {
-  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  uint4 v = i < nchunks ? x[i] : make_uint4(0, 0, 0, 0);
-  uint32_t m = magmax8(v);
+__global__ __launch_bounds__(kBwActThreads) void bw_act_kernel(const uint4* __restrict__ x, int64_t nchunks,
+                                                               uint2* __restrict__ q, float* __restrict__ s) {
+  const int64_t base = (int64_t)blockIdx.x * (kBwActThreads * kBwActUnroll) + threadIdx.x;
+  uint4 v[kBwActUnroll];
 #pragma unroll
-  for (int d = 1; d < 16; d <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, d, 64));
-  float sc = bw_scale_from_amax_bits<POW2>(m);
-  if (i < nchunks) {
-    q[i] = bw_convert8(v, sc);
-    if ((threadIdx.x & 15) == 0) s[i >> 4] = sc;
+  for (int j = 0; j < kBwActUnroll; ++j) {
+    const int64_t i = base + (int64_t)j * kBwActThreads;
+    v[j] = i < nchunks ? load16_nt(x + i) : make_uint4(0, 0, 0, 0);
+  }
+#pragma unroll
+  for (int j = 0; j < kBwActUnroll; ++j) {
+    const int64_t i = base + (int64_t)j * kBwActThreads;
+    // nchunks is a multiple of 16 and rows are 16-aligned, so a tile is wholly in or out of range
+    const BwScale sc = bw_scale<POW2>(hex_max(magmax8(v[j])));
+    const uint2 o = bw_convert8<POW2>(v[j], sc);
+    if (i < nchunks) {
+      store8_nt((uint2*)q + i, o);
+      if ((threadIdx.x & 15) == 0) s[i >> 4] = sc.s;
+    }
   }
 }
 
@@ -91,12 +161,12 @@ __global__ __launch_bounds__(256) void bw_weight_kernel(const uint16_t* __restri
   if ((t & 63) == 0) red[t >> 6] = m;
   __syncthreads();
   m = max(max(red[0], red[1]), max(red[2], red[3]));
-  float sc = bw_scale_from_amax_bits<POW2>(m);
+  const BwScale sc = bw_scale<POW2>(m);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int rr = r + 16 * i;
     const int64_t row = br * 128 + rr;
-    const uint2 o = bw_convert8(v[i], sc);
+    const uint2 o = bw_convert8<POW2>(v[i], sc);
     *(uint2*)(q + row * C + bcn * 128 + ch * 8) = o;
     if (qT) {
       // element (row rr, column 8 ch + b) of the block goes to transposed row 8 ch + b, column rr
@@ -105,7 +175,7 @@ __global__ __launch_bounds__(256) void bw_weight_kernel(const uint16_t* __restri
       for (int b = 0; b < 8; ++b) tile[(8 * ch + b) * kBwTPitch + rr] = (uint8_t)(wd[b >> 2] >> (8 * (b & 3)));
     }
   }
-  if (t == 0) s[br * (C / 128) + bcn] = sc;
+  if (t == 0) s[br * (C / 128) + bcn] = sc.s;
   if (qT) {
     __syncthreads();
     // transposed row k (= block column) holds the block's 128 rows: 8 lanes x 16 bytes per row
@@ -122,11 +192,14 @@ __global__ __launch_bounds__(256) void bw_weight_kernel(const uint16_t* __restri
 hipError_t launch_bw_act(const uint16_t* x, int64_t R, int64_t C, uint8_t* q, float* s, bool pow2, hipStream_t st) {
   int64_t nchunks = R * C / 8;
   if (nchunks == 0) return hipSuccess;
-  const dim3 grid((unsigned)((nchunks + 255) / 256));
+  const int64_t per = (int64_t)kBwActThreads * kBwActUnroll;
+  const int64_t blocks = (nchunks + per - 1) / per;
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)blocks);
   if (pow2)
-    hipLaunchKernelGGL(bw_act_kernel<true>, grid, dim3(256), 0, st, (const uint4*)x, nchunks, (uint2*)q, s);
+    hipLaunchKernelGGL(bw_act_kernel<true>, grid, dim3(kBwActThreads), 0, st, (const uint4*)x, nchunks, (uint2*)q, s);
   else
-    hipLaunchKernelGGL(bw_act_kernel<false>, grid, dim3(256), 0, st, (const uint4*)x, nchunks, (uint2*)q, s);
+    hipLaunchKernelGGL(bw_act_kernel<false>, grid, dim3(kBwActThreads), 0, st, (const uint4*)x, nchunks, (uint2*)q, s);
   return hipGetLastError();
 }
 
@@ -206,14 +279,13 @@ __global__ __launch_bounds__(256) void bw_colwise_kernel(const uint16_t* __restr
     a0 = max(a0, red[k][cp] & 0xFFFFu);
     a1 = max(a1, red[k][cp] >> 16);
   }
-  const float s0 = bw_scale_from_amax_bits<POW2>(a0), s1 = bw_scale_from_amax_bits<POW2>(a1);
+  const BwScale sc0 = bw_scale<POW2>(a0), sc1 = bw_scale<POW2>(a1);
+  const float s0 = sc0.s, s1 = sc1.s;
   uint32_t o0[8], o1[8];
 #pragma unroll
   for (int d = 0; d < 8; ++d) {
-    o0[d] = cvt4_f32_e4m3(__fdiv_rn(bf16_lo(w[4 * d]), s0), __fdiv_rn(bf16_lo(w[4 * d + 1]), s0),
-                          __fdiv_rn(bf16_lo(w[4 * d + 2]), s0), __fdiv_rn(bf16_lo(w[4 * d + 3]), s0));
-    o1[d] = cvt4_f32_e4m3(__fdiv_rn(bf16_hi(w[4 * d]), s1), __fdiv_rn(bf16_hi(w[4 * d + 1]), s1),
-                          __fdiv_rn(bf16_hi(w[4 * d + 2]), s1), __fdiv_rn(bf16_hi(w[4 * d + 3]), s1));
+    o0[d] = bw_convert4_col<POW2, false>(w + 4 * d, sc0);
+    o1[d] = bw_convert4_col<POW2, true>(w + 4 * d, sc1);
   }
   uint4* d0 = (uint4*)(outq + (2 * cp) * kBwColPitch + 32 * qq);
   uint4* d1 = (uint4*)(outq + (2 * cp + 1) * kBwColPitch + 32 * qq);

@@ -21,14 +21,6 @@ namespace mxmoe {
 constexpr int kRowThreads = 512;
 constexpr int kRowUnroll = 2;
 
-typedef uint32_t v4u_ __attribute__((ext_vector_type(4)));
-typedef uint32_t v2u_ __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ uint4 load16_nt(const uint4* p) {
-  const v4u_ v = __builtin_nontemporal_load((const v4u_*)p);
-  return make_uint4(v[0], v[1], v[2], v[3]);
-}
-__device__ __forceinline__ void store8_nt(uint2* p, uint2 v) { __builtin_nontemporal_store(v2u_{v.x, v.y}, (v2u_*)p); }
-__device__ __forceinline__ void store4_nt(uint32_t* p, uint32_t v) { __builtin_nontemporal_store(v, p); }
 // Column-wise output stores: non-temporal in the dual-layout launch (it writes as many bytes as it
 // reads), ordinary in the column-wise launch (measured faster there).
 template <bool NT>
@@ -42,12 +34,6 @@ __device__ __forceinline__ void store4_col(uint32_t* p, uint32_t v) {
   else *p = v;
 }
 
-__device__ __forceinline__ uint32_t quad_max(uint32_t m) {
-  // quad_perm [1,0,3,2] then [2,3,0,1]: every lane of the quad ends with the quad's maximum
-  m = max(m, (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0xB1, 0xF, 0xF, false));
-  m = max(m, (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0x4E, 0xF, 0xF, false));
-  return m;
-}
 
 __device__ __forceinline__ uint32_t mag_max8(const uint4& v) {
   typedef unsigned short v2us __attribute__((ext_vector_type(2)));
@@ -169,14 +155,6 @@ __device__ __forceinline__ uint32_t mag_max4(uint32_t w0, uint32_t w1) {
   return max((uint32_t)m[0], (uint32_t)m[1]);
 }
 
-// Maximum over each group of 8 lanes: quad permutes, then the half-row mirror (lane i of an 8-lane
-// group with lane 7 - i, in the other quad).  bound_ctrl with an old value of 0 (the identity of an
-// unsigned max) lets each permute fold into the max as one DPP instruction.
-__device__ __forceinline__ uint32_t oct_max(uint32_t m) {
-  m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0xB1, 0xF, 0xF, true));
-  m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x4E, 0xF, 0xF, true));
-  return max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x141, 0xF, 0xF, true));
-}
 
 typedef uint32_t ColRows __attribute__((ext_vector_type(kColLaneCols / 2)));   // the lane's columns of one row
 
