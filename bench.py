@@ -71,13 +71,15 @@ def build_layer_ops(m, torch, lay, dev_in, fast=False, fused=True):
     x, w, dy, offs = dev_in
     d = x.device
     u8 = torch.uint8
-    ld = m.mx_colwise_ld_min(M, G)
+    # recommended row pitches of the column-wise copies (the minimum, off pitches that write slowly)
+    ld = m.mx_colwise_ld(M, G)
+    ldw = m.mx_colwise_ld(G * N)
     b = dict(
         qx=torch.empty((M, K), dtype=u8, device=d), sx=torch.empty((M, K // 32), dtype=u8, device=d),
         qw=torch.empty((G * N, K), dtype=u8, device=d), sw=torch.empty((G * N, K // 32), dtype=u8, device=d),
         y=torch.empty((M, N), dtype=torch.bfloat16, device=d),
         qdy=torch.empty((M, N), dtype=u8, device=d), sdy=torch.empty((M, N // 32), dtype=u8, device=d),
-        qwT=torch.empty((K, G * N), dtype=u8, device=d), swT=torch.empty((K, G * N // 32), dtype=u8, device=d),
+        qwT=torch.empty((K, ldw), dtype=u8, device=d), swT=torch.empty((K, ldw // 32), dtype=u8, device=d),
         dx=torch.empty((M, K), dtype=torch.bfloat16, device=d),
         qdyT=torch.empty((N, ld), dtype=u8, device=d), sdyT=torch.empty((N, ld // 32), dtype=u8, device=d),
         qxT=torch.empty((K, ld), dtype=u8, device=d), sxT=torch.empty((K, ld // 32), dtype=u8, device=d),
@@ -103,7 +105,7 @@ def build_layer_ops(m, torch, lay, dev_in, fast=False, fused=True):
                lambda: m.mx_quantize_dual(x, offs, ld=ld, q=b["qx"], s=b["sx"], qT=b["qxT"], sT=b["sxT"]),
                M * K * DUAL_BYTES_PER_ELEM, "mx_colwise_kernel<true, false>"),
             Op(f"{n}.quant_w_dual", "quant",
-               lambda: m.mx_quantize_dual(w2, None, ld=G * N, q=b["qw"], s=b["sw"], qT=b["qwT"], sT=b["swT"]),
+               lambda: m.mx_quantize_dual(w2, None, ld=ldw, q=b["qw"], s=b["sw"], qT=b["qwT"], sT=b["swT"]),
                G * N * K * DUAL_BYTES_PER_ELEM, "mx_colwise_kernel<true, false>"),
             fwd,
             Op(f"{n}.quant_dy_dual", "quant",
@@ -122,7 +124,7 @@ def build_layer_ops(m, torch, lay, dev_in, fast=False, fused=True):
             Op(f"{n}.quant_dy_row", "quant", lambda: m.mx_quantize_rowwise(dy, b["qdy"], b["sdy"]),
                M * N * QUANT_BYTES_PER_ELEM, "mx_rowwise_kernel"),
             Op(f"{n}.quant_w_col", "quant",
-               lambda: m.mx_quantize_colwise(w2, None, ld=G * N, qT=b["qwT"], sT=b["swT"]),
+               lambda: m.mx_quantize_colwise(w2, None, ld=ldw, qT=b["qwT"], sT=b["swT"]),
                G * N * K * QUANT_BYTES_PER_ELEM, "mx_colwise_kernel<false, false>"),
             dgrad,
             Op(f"{n}.quant_dy_col", "quant", lambda: m.mx_quantize_colwise(dy, offs, ld=ld, qT=b["qdyT"], sT=b["sdyT"]),
@@ -427,8 +429,8 @@ def blockwise_leg(m, torch, steps=5, sample_rows=256):
         bq, bq2 = {}, {}
         ops_bw, ops_bw2 = bw_ops(bq, False), bw_ops(bq2, True)
         mq = {}
-        ld = G * N
-        ldm = m.mx_colwise_ld_min(M, G)
+        ld = m.mx_colwise_ld(G * N)
+        ldm = m.mx_colwise_ld(M, G)
         ops_mx = [
             Op("quant_x", "quant", lambda: mq.update(x=m.mx_quantize_rowwise(x)), M * K * QUANT_BYTES_PER_ELEM, ""),
             Op("quant_w", "quant", lambda: mq.update(w=m.mx_quantize_rowwise(w)), G * N * K * QUANT_BYTES_PER_ELEM, ""),

@@ -16,7 +16,7 @@ from typing import Optional, Tuple
 
 __all__ = [
     "LIB_PATH", "MxMoeError", "lib", "abi_version", "FEED_FP8",
-    "mx_colwise_ld_min", "mx_quantize_rowwise", "mx_quantize_colwise", "mx_quantize_dual",
+    "mx_colwise_ld_min", "mxmoe_pitch", "mx_colwise_ld", "mx_quantize_rowwise", "mx_quantize_colwise", "mx_quantize_dual",
     "mx_grouped_gemm_fwd", "mx_grouped_gemm_dgrad", "mx_grouped_gemm_wgrad", "mx_grouped_gemm_fwd_swiglu",
     "fp8bw_quantize_act_1x128", "fp8bw_quantize_weight_128x128",
     "fp8bw_grouped_gemm_fwd", "fp8bw_grouped_gemm_dgrad", "mxmoe_check_offsets",
@@ -42,6 +42,7 @@ _SIGS = {
     "mxmoe_abi_version": (ctypes.c_int, []),
     "mxmoe_last_error": (ctypes.c_char_p, []),
     "mx_colwise_ld_min": (_i64, [_i64, _i32]),
+    "mxmoe_pitch": (_i64, [_i64]),
     "mx_quantize_rowwise": (ctypes.c_int, [_p, _i64, _i64, _p, _p, _p]),
     "mx_quantize_colwise": (ctypes.c_int, [_p, _i64, _i64, _p, _i32, _p, _p, _i64, _p]),
     "mx_quantize_dual": (ctypes.c_int, [_p, _i64, _i64, _p, _i64, _p, _i32, _p, _p, _p, _p, _i64, _p]),
@@ -107,6 +108,18 @@ def abi_version() -> int:
 
 def mx_colwise_ld_min(M: int, G: int) -> int:
     return lib().mx_colwise_ld_min(int(M), int(G))
+
+
+def mxmoe_pitch(min_ld: int) -> int:
+    """The recommended row pitch >= min_ld for a column-wise output (avoids slow pitches)."""
+    return lib().mxmoe_pitch(int(min_ld))
+
+
+def mx_colwise_ld(M: int, G: Optional[int] = None) -> int:
+    """Default leading dimension of a column-wise MX output of R = M rows: the recommended pitch for G
+    groups (routing offsets), or for one group of M rows when G is None (a weight viewed as [G*N, K])."""
+    need = mx_colwise_ld_min(M, G) if G is not None else 32 * ((int(M) + 31) // 32)
+    return mxmoe_pitch(need)
 
 
 # ---------------------------------------------------------------- torch plumbing
@@ -175,7 +188,7 @@ def mx_quantize_colwise(x, offs=None, G: int = 1, ld: Optional[int] = None, qT=N
     if offs is not None:
         G = offs.numel() - 1
     if ld is None:
-        ld = mx_colwise_ld_min(R, G) if offs is not None else 32 * ((R + 31) // 32)
+        ld = mx_colwise_ld(R, G if offs is not None else None)
     qT = _empty((C, ld), torch.uint8, x) if qT is None else qT
     sT = _empty((C, ld // 32), torch.uint8, x) if sT is None else sT
     _check("mx_quantize_colwise", lib().mx_quantize_colwise(_ptr(x), R, C, _ptr(offs), G, _ptr(qT), _ptr(sT), ld,
@@ -196,7 +209,7 @@ def mx_quantize_dual(x, offs=None, G: int = 1, ld: Optional[int] = None, row_idx
     if offs is not None:
         G = offs.numel() - 1
     if ld is None:
-        ld = mx_colwise_ld_min(R, G) if offs is not None else 32 * ((R + 31) // 32)
+        ld = mx_colwise_ld(R, G if offs is not None else None)
     q = _empty((R, C), torch.uint8, x) if q is None else q
     s = _empty((R, C // 32), torch.uint8, x) if s is None else s
     qT = _empty((C, ld), torch.uint8, x) if qT is None else qT

@@ -104,6 +104,24 @@ int64_t mx_colwise_ld_min(int64_t M, int32_t G) {
   return 32 * ((M + 31 * (int64_t)G + 31) / 32);
 }
 
+// A pitch 2^p + 2^(p-k) with k in {7, 8, 9}: p is the position of the highest set bit, and the rest is
+// one bit k places below it.
+static bool slow_pitch(int64_t ld) {
+  if (ld <= 0) return false;
+  int p = 63 - __builtin_clzll((unsigned long long)ld);
+  const int64_t rest = ld - ((int64_t)1 << p);
+  for (int k = 7; k <= 9; ++k)
+    if (p >= k && rest == ((int64_t)1 << (p - k))) return true;
+  return false;
+}
+
+int64_t mxmoe_pitch(int64_t min_ld) {
+  if (min_ld < 0) return -1;
+  int64_t ld = min_ld;
+  while (slow_pitch(ld)) ld += 1024;
+  return ld;
+}
+
 mxmoe_status mx_quantize_rowwise(const void* x, int64_t R, int64_t C, uint8_t* q, uint8_t* s, void* stream) {
   const char* fn = "mx_quantize_rowwise";
   if (R < 0 || C <= 0 || C % 32) return fail(MXMOE_ERR_SHAPE, "%s: need R >= 0, C > 0, C %% 32 == 0 (R=%lld C=%lld)",

@@ -4,6 +4,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -43,6 +44,28 @@ def test_host_helpers():
     assert [m.fp8bw_colwise_ld_min(M, G) for M, G in ((1024, 4), (49152, 64), (65536, 8))] == \
         [1536, 57344, 66560]
     assert m.fp8bw_colwise_ld_min(-1, 4) == -1 and m.fp8bw_colwise_ld_min(10, 0) == -1
+
+
+def test_recommended_pitch():
+    m, L = _lib()
+    slow = {(1 << p) + (1 << (p - k)) for p in range(7, 40) for k in (7, 8, 9) if p >= k}
+    # the expert-shard minimum 2^16 + 2^8 and the slow weight pitch 2^15 + 2^7 move up by 1 KiB
+    assert m.mxmoe_pitch(65792) == 65792 + 1024
+    assert m.mxmoe_pitch(32896) == 32896 + 1024
+    # the other configs' minima and powers of two are kept
+    for ld in (1152, 51136, 33280, 32768, 57344, 131072, 180224, 65536):
+        assert m.mxmoe_pitch(ld) == ld
+    assert m.mxmoe_pitch(-1) == -1 and m.mxmoe_pitch(0) == 0
+    rng = np.random.default_rng(5)
+    cands = sorted(slow) + [int(v) for v in rng.integers(0, 1 << 24, 2000) * 32]
+    for ld in cands:
+        got = m.mxmoe_pitch(ld)
+        want = ld
+        while want in slow:
+            want += 1024
+        assert got == want, (ld, got, want)
+    assert m.mx_colwise_ld(65536, 8) == 66816 and m.mx_colwise_ld(49152, 64) == 51136
+    assert m.mx_colwise_ld(32768) == 32768
 
 
 A16 = 0x10000      # fake, 16-byte aligned device addresses: never dereferenced on error paths

@@ -65,14 +65,16 @@ def run_layer(m, L, dt="f32", rows=None, wgrad_groups=None, n_idx=None, k_idx=No
         worst["fwd"] = _check(got, ref, bnd, dt, "fwd", rel)
     if "dgrad" in check:
         qdy, sdy = m.mx_quantize_rowwise(dy)
-        qwT, swT = m.mx_quantize_colwise(w, None, ld=L.G * L.N)
+        # the row pitches the benchmark uses (the recommended ones, >= the minimum)
+        qwT, swT = m.mx_quantize_colwise(w, None, ld=m.mx_colwise_ld(L.G * L.N))
         dx = m.mx_grouped_gemm_dgrad(qdy, sdy, qwT, swT, offs_d, L.K, dt, fast=fast)
         hq = [host(t) for t in (qdy, sdy, qwT, swT)]
         ref, bnd = oracle.mx_gemm_dgrad(*hq, L.offs, L.N, L.K, rows=rows)
         got = _gpu_out(dx)[rows] if rows is not None else _gpu_out(dx)
         worst["dgrad"] = _check(got, ref, bnd, dt, "dgrad", rel)
     if "wgrad" in check:
-        ld = oracle.mx_colwise_ld_min(L.M, L.G)
+        ld = m.mx_colwise_ld(L.M, L.G)
+        assert ld >= oracle.mx_colwise_ld_min(L.M, L.G)
         qdyT, sdyT = m.mx_quantize_colwise(dy, offs_d, ld=ld)
         qxT, sxT = m.mx_quantize_colwise(x, offs_d, ld=ld)
         dw = m.mx_grouped_gemm_wgrad(qdyT, sdyT, qxT, sxT, offs_d, L.M, dt, fast=fast)
