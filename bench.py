@@ -387,6 +387,41 @@ def swiglu_leg(m, torch, lay, dev_in, steps=10):
     return out
 
 
+def other_configs_leg(m, torch, steps=5, warmup=2):
+    """The same MXFP8 fwd+bwd step (dual-layout quantisers, grouped GEMMs fwd/dgrad/wgrad, precise feed)
+    on the other two full-size workloads: DeepSeek-V3-16B-shaped layers (64 experts, 49152 routed rows)
+    and Llama-4-Scout-shaped layers (16 experts, 32768 rows, top-1).  Reported beside the headline."""
+    from workloads import make_workload
+    res = {}
+    for wname in ("dsv3_16b", "llama4_scout"):
+        wl = make_workload(wname)
+        ops, keep = [], []
+        for lay in wl.layers:
+            dev_in = (to_device(torch, lay.x), to_device(torch, lay.w), to_device(torch, lay.dy),
+                      to_device(torch, lay.offs))
+            lops, bufs = build_layer_ops(m, torch, lay, dev_in)
+            ops += lops
+            keep.append((dev_in, bufs))
+        ms = time_ops(torch, ops, steps, warmup)
+        gflop = sum(op.work for op in ops if op.kind == "gemm")
+        gemm_ms = sum(float(np.mean(op.ms)) for op in ops if op.kind == "gemm")
+        q_ms = sum(float(np.mean(op.ms)) for op in ops if op.kind == "quant")
+        q_bytes = sum(op.work for op in ops if op.kind == "quant")
+        gt = gflop / (gemm_ms * 1e-3) / 1e12
+        res[wname] = {
+            "layers": {l.name: {"G": l.G, "M": l.M, "N": l.N, "K": l.K} for l in wl.layers},
+            "ms_per_step": round(ms, 4), "tflops": round(gflop / (ms * 1e-3) / 1e12, 1),
+            "gemm_tflops": round(gt, 1), "gemm_frac_of_bf16_peak": round(gt / MFMA_PEAK_TFLOPS["bf16"], 4),
+            "gemm_frac_of_mxfp8_peak": round(gt / MFMA_PEAK_TFLOPS["mxfp8"], 4),
+            "quant_gbps": round(q_bytes / (q_ms * 1e-3) / 1e9, 1),
+            "ops": {op.name: op_summary(op) for op in ops},
+        }
+        log(f"{wname}: {ms:.3f} ms/step, GEMMs {gt:.0f} TFLOP/s")
+        del ops, keep, wl
+        torch.cuda.empty_cache()
+    return res
+
+
 def blockwise_leg(m, torch, steps=5, sample_rows=256):
     """DeepSeek-style blockwise FP8 (1x128 activation tiles, 128x128 weight blocks, 128-token blocks
     for the weight gradient, fp32 scales, promotion every 128), also in its power-of-two scale mode,
@@ -622,6 +657,7 @@ def main():
         del keep, ops
         torch.cuda.empty_cache()
         extra["blockwise_vs_mx"] = blockwise_leg(m, torch)
+        extra["other_configs"] = other_configs_leg(m, torch)
 
     cpu = None
     if not args.no_cpu_baseline:

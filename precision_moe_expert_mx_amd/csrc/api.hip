@@ -118,7 +118,7 @@ static bool slow_pitch(int64_t ld) {
 int64_t mxmoe_pitch(int64_t min_ld) {
   if (min_ld < 0) return -1;
   int64_t ld = min_ld;
-  while (slow_pitch(ld)) ld += 1024;
+  while (slow_pitch(ld) && ld <= INT64_MAX - 1024) ld += 1024;
   return ld;
 }
 

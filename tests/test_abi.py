@@ -56,6 +56,7 @@ def test_recommended_pitch():
     for ld in (1152, 51136, 33280, 32768, 57344, 131072, 180224, 65536):
         assert m.mxmoe_pitch(ld) == ld
     assert m.mxmoe_pitch(-1) == -1 and m.mxmoe_pitch(0) == 0
+    assert m.mxmoe_pitch((1 << 62) + (1 << 54)) >= (1 << 62) + (1 << 54)   # no overflow near the top
     rng = np.random.default_rng(5)
     cands = sorted(slow) + [int(v) for v in rng.integers(0, 1 << 24, 2000) * 32]
     for ld in cands:
