@@ -304,7 +304,7 @@ def mxfp4_leg(m, torch, wl, keep, steps=5, sample_rows=64):
         G, M, N, K = lay.G, lay.M, lay.N, lay.K
         x, w, dy, offs = dev_in
         w2 = w.view(G * N, K)
-        ld = m.mx_colwise_ld_min(M, G)
+        ld = m.mxfp4_colwise_ld(M, G)
         q = {}
         bufs.append(q)
         f = 2.0 * M * N * K

@@ -76,8 +76,9 @@ const char* mxmoe_last_error(void);
  * arithmetic; returns -1 for M < 0 or G < 1. */
 int64_t mx_colwise_ld_min(int64_t M, int32_t G);
 
-/* mxmoe_pitch: the row pitch (bytes of one qT row of E4M3 codes) this library
- * recommends for a column-wise output whose minimum is min_ld: min_ld itself,
+/* mxmoe_pitch: the row pitch (bytes of one qT row: ld for E4M3 codes, ld / 2 for
+ * E2M1) this library recommends for a column-wise output whose minimum is min_ld
+ * bytes: min_ld itself,
  * raised in steps of 1024 while it has the form 2^p + 2^(p-k), k in {7, 8, 9}
  * (the residues modulo 32, 128 and 1024 are kept).  Measured on MI355X, the
  * column-wise and dual-layout quantisers write such pitches 15-25% slower: with

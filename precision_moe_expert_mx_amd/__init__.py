@@ -16,7 +16,7 @@ from typing import Optional, Tuple
 
 __all__ = [
     "LIB_PATH", "MxMoeError", "lib", "abi_version", "FEED_FP8",
-    "mx_colwise_ld_min", "mxmoe_pitch", "mx_colwise_ld", "mx_quantize_rowwise", "mx_quantize_colwise", "mx_quantize_dual",
+    "mx_colwise_ld_min", "mxmoe_pitch", "mx_colwise_ld", "mxfp4_colwise_ld", "mx_quantize_rowwise", "mx_quantize_colwise", "mx_quantize_dual",
     "mx_grouped_gemm_fwd", "mx_grouped_gemm_dgrad", "mx_grouped_gemm_wgrad", "mx_grouped_gemm_fwd_swiglu",
     "fp8bw_quantize_act_1x128", "fp8bw_quantize_weight_128x128",
     "fp8bw_grouped_gemm_fwd", "fp8bw_grouped_gemm_dgrad", "mxmoe_check_offsets",
@@ -113,6 +113,13 @@ def mx_colwise_ld_min(M: int, G: int) -> int:
 def mxmoe_pitch(min_ld: int) -> int:
     """The recommended row pitch >= min_ld for a column-wise output (avoids slow pitches)."""
     return lib().mxmoe_pitch(int(min_ld))
+
+
+def mxfp4_colwise_ld(M: int, G: Optional[int] = None) -> int:
+    """Default leading dimension (elements) of a column-wise MXFP4 output: qT rows hold ld / 2 bytes, so
+    the recommended pitch applies to the byte count."""
+    need = mx_colwise_ld_min(M, G) if G is not None else 32 * ((int(M) + 31) // 32)
+    return 2 * mxmoe_pitch(need // 2)
 
 
 def mx_colwise_ld(M: int, G: Optional[int] = None) -> int:
@@ -298,7 +305,7 @@ def mxfp4_quantize_colwise(x, offs=None, G: int = 1, ld: Optional[int] = None, q
     if offs is not None:
         G = offs.numel() - 1
     if ld is None:
-        ld = mx_colwise_ld_min(R, G) if offs is not None else 32 * ((R + 31) // 32)
+        ld = mxfp4_colwise_ld(R, G if offs is not None else None)
     qT = _empty((C, ld // 2), torch.uint8, x) if qT is None else qT
     sT = _empty((C, ld // 32), torch.uint8, x) if sT is None else sT
     _check("mxfp4_quantize_colwise", lib().mxfp4_quantize_colwise(_ptr(x), R, C, _ptr(offs), G, _ptr(qT), _ptr(sT),

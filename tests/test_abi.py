@@ -67,6 +67,8 @@ def test_recommended_pitch():
         assert got == want, (ld, got, want)
     assert m.mx_colwise_ld(65536, 8) == 66816 and m.mx_colwise_ld(49152, 64) == 51136
     assert m.mx_colwise_ld(32768) == 32768
+    # E2M1 rows hold ld / 2 bytes: the shard's 65792 / 2 = 2^15 + 2^7 bytes is a slow pitch
+    assert m.mxfp4_colwise_ld(65536, 8) == 2 * (32896 + 1024) and m.mxfp4_colwise_ld(49152, 64) == 51136
 
 
 A16 = 0x10000      # fake, 16-byte aligned device addresses: never dereferenced on error paths
