@@ -136,6 +136,8 @@ def build_layer_ops(m, torch, lay, dev_in, fast=False, fused=True):
     for op in ops:
         if op.kind == "gemm":
             op.bytes = gemm_bytes[op.name.split(".")[1]]
+            # the MFMA rate the feed runs at: bf16 for the precise feed, the MXFP8 rate for the fast one
+            op.peak_tflops = MFMA_PEAK_TFLOPS["mxfp8" if fast else "bf16"]
     return ops, b
 
 
@@ -178,6 +180,11 @@ def op_summary(op):
     d = {"ms": round(ms, 4), "ms_min": round(float(np.min(op.ms)), 4)}
     if op.kind == "gemm":
         d["tflops"] = round(op.work / (ms * 1e-3) / 1e12, 1)
+        if getattr(op, "bytes", None) and getattr(op, "peak_tflops", None):
+            # fraction of the op's own roofline: the larger of its time at the MFMA peak and its time at
+            # the HBM peak (algorithmic bytes), over the measured time
+            t_roof = max(op.work / (op.peak_tflops * 1e12), op.bytes / (HBM_PEAK_GBS * 1e9))
+            d["frac_of_op_roofline"] = round(t_roof / (ms * 1e-3), 4)
     else:
         d["gbps"] = round(op.work / (ms * 1e-3) / 1e9, 1)
         d["frac_hbm"] = round(d["gbps"] / HBM_PEAK_GBS, 3)
@@ -254,6 +261,62 @@ def pmc_summary(fetch_csv: str, write_csv: str, cmds) -> None:
                 f.write(f"#   {c}\n")
             f.write(json.dumps(rec) + "\n")
         print(json.dumps(rec))
+
+
+MFMA_FILE = os.path.join(ROOT, "profiles", "gemm_mfma_dsv3_671b_shard.txt")
+MFMA_COUNTERS = ("GRBM_GUI_ACTIVE", "SQ_VALU_MFMA_BUSY_CYCLES", "MfmaUtil")
+N_XCD = 8                                    # GRBM_GUI_ACTIVE is summed over the MI355X's 8 XCDs
+
+
+def mfma_summary(pmc_dir: str, cmds) -> None:
+    """Clock and MFMA use of the six GEMM launches of one step, from one rocprofv3 run of this script
+    with --kernel-trace and --pmc of MFMA_COUNTERS: the shader clock is GRBM_GUI_ACTIVE (summed over the
+    8 XCDs) / 8 over the launch's duration; the achieved rate is set against the bf16 MFMA rate at that
+    clock (1024 flop per clock per SIMD, 1024 SIMDs); MfmaUtil is rocprofv3's own metric,
+    sum(SQ_VALU_MFMA_BUSY_CYCLES) / (max over XCDs of GRBM_GUI_ACTIVE x SIMD count), the busy count being
+    per SIMD."""
+    import csv
+    from workloads import make_workload
+    flops = {}
+    for lay in make_workload("dsv3_671b_shard").layers:
+        for k in ("fwd", "dgrad", "wgrad"):
+            flops[f"{lay.name}.{k}"] = 2.0 * lay.M * lay.N * lay.K
+    per_disp = {}
+    for r in csv.DictReader(open(os.path.join(pmc_dir, "p_counter_collection.csv"))):
+        d = per_disp.setdefault(int(r["Dispatch_Id"]), {"name": r["Kernel_Name"]})
+        d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    dur = {}
+    for r in csv.DictReader(open(os.path.join(pmc_dir, "p_kernel_trace.csv"))):
+        dur[int(r["Dispatch_Id"])] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    gemm = [k for k in sorted(per_disp) if "mx_grouped_gemm" in per_disp[k]["name"]]
+    acc = {}
+    for i, k in enumerate(gemm):
+        acc.setdefault(GEMM_NAMES[i % len(GEMM_NAMES)], []).append((per_disp[k], dur[k]))
+    ops = {}
+    for n in GEMM_NAMES:
+        if n not in acc:
+            continue
+        c = {m_: float(np.mean([d[m_] for d, _ in acc[n]])) for m_ in MFMA_COUNTERS}
+        ns = float(np.mean([t for _, t in acc[n]]))
+        ghz = c["GRBM_GUI_ACTIVE"] / N_XCD / ns
+        tf = flops[n] / (ns * 1e-9) / 1e12
+        rate_at_clock = 1024 * 1024 * ghz * 1e9 / 1e12
+        ops[n] = {"us": round(ns / 1e3, 1), "clock_ghz": round(ghz, 3), "tflops": round(tf, 1),
+                  "bf16_rate_at_clock_tflops": round(rate_at_clock, 1),
+                  "frac_of_rate_at_clock": round(tf / rate_at_clock, 4),
+                  "frac_of_bf16_peak": round(tf / MFMA_PEAK_TFLOPS["bf16"], 4),
+                  "mfma_util": round(c["MfmaUtil"] / 100.0, 4),
+                  "counters": {m_: round(v) for m_, v in c.items()}}
+    rec = {"source_sha256": gemm_source_hash(), "ops": ops}
+    with open(MFMA_FILE, "w") as f:
+        f.write("# Clock and MFMA use of the six grouped-GEMM launches of one step (DeepSeek-V3-671B expert shard,\n")
+        f.write("# precise feed, bf16 MFMA).  clock = GRBM_GUI_ACTIVE / 8 XCDs / duration; frac_of_rate_at_clock =\n")
+        f.write("# achieved TFLOP/s / (1024 flop/clk/SIMD x 1024 SIMDs x clock); mfma_util = rocprofv3 MfmaUtil\n")
+        f.write("# (sum SQ_VALU_MFMA_BUSY_CYCLES / (max-XCD GRBM_GUI_ACTIVE x SIMDs)); commands (repository root):\n")
+        for c_ in cmds:
+            f.write(f"#   {c_}\n")
+        f.write(json.dumps(rec) + "\n")
+    print(json.dumps(rec))
 
 
 # ------------------------------------------------------------------------------------------- CPU oracle
@@ -531,9 +594,18 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle timing")
     ap.add_argument("--no-extra-legs", action="store_true",
                     help="skip the FP8-feed and blockwise legs (reported beside the headline)")
+    ap.add_argument("--mfma-summary", metavar="PMC_DIR",
+                    help="write the GEMM clock / MFMA-use summary from a rocprofv3 --kernel-trace --pmc run of this script")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the GEMM and quantiser traffic summaries from two rocprofv3 counter runs of this script")
     args = ap.parse_args()
+
+    if args.mfma_summary:
+        mfma_summary(args.mfma_summary, [
+            "rocprofv3 --kernel-trace --pmc " + " ".join(MFMA_COUNTERS) + " --output-format csv -d gpurun_out/pmc_mfma -o p "
+            "-- python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-extra-legs",
+            "python3 bench.py --mfma-summary gpurun_out/pmc_mfma"])
+        return
 
     if args.pmc_summary:
         cmds = [f"rocprofv3 --pmc {c} --output-format csv -d gpurun_out/pmc_{c.lower()} -o p -- "

@@ -72,7 +72,7 @@ def test_colwise_ragged_and_weight_layout():
     assert np.array_equal(host(sT), so) and np.array_equal(host(qT), qo)
 
 
-def _fp4_layer_check(m, L, dt, rows=None, groups=None, n_idx=None, k_idx=None):
+def _fp4_layer_check(m, L, dt, rows=None, groups=None, n_idx=None, k_idx=None, extra=0):
     offs = dev(L.offs)
     x, w, dy = dev(L.x), dev(L.w.reshape(-1, L.K)), dev(L.dy)
     worst = {}
@@ -88,7 +88,9 @@ def _fp4_layer_check(m, L, dt, rows=None, groups=None, n_idx=None, k_idx=None):
     ref, bnd = oracle.mxfp4_gemm_dgrad(host(qd), host(sd), host(qwT), host(swT), L.offs, L.N, L.K, rows=rows)
     got = _gpu_out(dx) if rows is None else _gpu_out(dx)[rows]
     worst["dgrad"] = _check(got, ref, bnd, dt, "fp4 dgrad")
-    ld = oracle.mx_colwise_ld_min(L.M, L.G)
+    # the pitch the benchmark uses (padded off slow byte pitches), or the minimum plus `extra` elements
+    ld = m.mxfp4_colwise_ld(L.M, L.G) + extra
+    assert ld >= oracle.mx_colwise_ld_min(L.M, L.G)
     qdT, sdT = m.mxfp4_quantize_colwise(dy, offs, ld=ld)
     qxT, sxT = m.mxfp4_quantize_colwise(x, offs, ld=ld)
     dw = m.mxfp4_grouped_gemm_wgrad(qdT, sdT, qxT, sxT, offs, L.M, dt)
@@ -110,6 +112,9 @@ def test_gemms_ragged_groups():
         L = _rand_layer(rng, sizes, N, K, outliers=0.001)
         for dt in ("f32", "bf16"):
             print("fp4", sizes, dt, _fp4_layer_check(m, L, dt))
+    # a padded leading dimension (2048 elements = 1 KiB of E2M1 codes per qT row)
+    L = _rand_layer(rng, [0, 5, 130, 1, 300], 256, 512, outliers=0.001)
+    print("fp4 padded ld", _fp4_layer_check(m, L, "f32", extra=2048))
 
 
 def test_run_of_mixed_magnitudes_is_exact():
