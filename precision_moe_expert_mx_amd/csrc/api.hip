@@ -182,6 +182,16 @@ mxmoe_status mx_quantize_dual(const void* x, int64_t R, int64_t C, const int32_t
                   fn);
 }
 
+// The GEMM addresses a tile's operand rows as 32-bit byte offsets from the tile's first row: 256 rows
+// (the gated forward: the N weight rows of an expert) of each operand must span less than 4 GiB.
+static mxmoe_status check_strides(const char* fn, const GemmArgs& p, int64_t b_rows) {
+  const int64_t lim = (int64_t)1 << 32;
+  if (256 * p.lda + 256 > lim || b_rows * p.ldb + 256 > lim)
+    return fail(MXMOE_ERR_SHAPE, "%s: operand row stride too large (lda=%lld ldb=%lld bytes): a tile's rows must "
+                "span less than 4 GiB", fn, (long long)p.lda, (long long)p.ldb);
+  return MXMOE_OK;
+}
+
 static mxmoe_status mx_gemm_common(int mode, const char* fn, const uint8_t* a, const uint8_t* sa, const uint8_t* b,
                                    const uint8_t* sb, int64_t ldb_cols, const int32_t* offs, int32_t G, int64_t M,
                                    int64_t N, int64_t K, void* out, int dt, void* stream, bool fp4 = false) {
@@ -210,6 +220,7 @@ static mxmoe_status mx_gemm_common(int mode, const char* fn, const uint8_t* a, c
   } else {
     p.lda = ldb_cols / epb; p.ldsa = ldb_cols / 32; p.ldb = ldb_cols / epb; p.ldsb = ldb_cols / 32;
   }
+  TRY(check_strides(fn, p, 256));
   if (mode != kWgrad && M == 0) return ok();
   TRY(check_device());
   return launched(launch_mx_gemm(mode, p, (hipStream_t)stream), fn);
@@ -242,6 +253,7 @@ mxmoe_status mx_grouped_gemm_fwd_swiglu(const uint8_t* qx, const uint8_t* sx, co
   p.feed = kFeedPrecise;
   p.lda = K; p.ldsa = K / 32; p.ldb = K; p.ldsb = K / 32;
   p.act_q = qh; p.act_s = sh; p.act_dbg = h;
+  TRY(check_strides(fn, p, N));
   if (M == 0) return ok();
   TRY(check_device());
   return launched(launch_mx_gemm(kFwd, p, (hipStream_t)stream), fn);

@@ -16,7 +16,10 @@
 // outputs per wave).  The contraction advances 128 bytes (four MX blocks) per stage.  Operand bytes
 // and scale bytes go global -> LDS by direct-to-LDS loads (no register staging), two stages in LDS:
 // the loads of stage s+1 are issued right after the barrier that publishes stage s, and land while
-// stage s is multiplied.  LDS rows are 128 bytes with 16-byte chunks XOR-swizzled by row.
+// stage s is multiplied (the precise feed issues them after its first 32-block's MFMAs, so that a stage
+// opens with LDS reads, widening and MFMAs).  Each load is a per-tile 32-bit lane offset from a
+// wave-uniform base in scalar registers that advances by the stage, so issuing costs no vector
+// arithmetic.  LDS rows are 128 bytes with 16-byte chunks XOR-swizzled by row.
 //
 // Operand feeds (same tiling and LDS staging):
 //  * precise (default): each lane reads 16 consecutive bytes of one MX block, widens them exactly to
@@ -95,6 +98,12 @@ __device__ __forceinline__ int swz(int r) { return MXMOE_LDS_SWZ(r); }
 __device__ __forceinline__ int lds_off(int r, int c) { return r * BK + ((c ^ swz(r)) << 4); }
 
 __device__ __forceinline__ int cdiv(int64_t a, int b) { return (int)((a + b - 1) / b); }
+
+__device__ __forceinline__ int64_t uniform64(int64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
 
 // Tile list of the launch and this workgroup's tile.  Scratch arrays live at the start of the LDS
 // (before the first operand load overwrites them).  Returns false when the workgroup has no tile.
@@ -213,6 +222,12 @@ __device__ __forceinline__ uint32_t lds_addr(const char* p) { return (uint32_t)(
 __device__ __forceinline__ void dma16(const uint8_t* g, const char* lds_wave_base) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
                :: "s"(__builtin_amdgcn_readfirstlane(lds_addr(lds_wave_base))), "v"(g) : "memory", "m0");
+}
+// The same load addressed as a wave-uniform 64-bit base (scalar registers) plus a 32-bit lane offset:
+// per stage only the base moves (scalar adds), the lane offsets are formed once per tile.
+__device__ __forceinline__ void dma16s(uint32_t off, const uint8_t* base, const char* lds_wave_base) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :: "s"(__builtin_amdgcn_readfirstlane(lds_addr(lds_wave_base))), "v"(off), "s"(base) : "memory", "m0");
 }
 __device__ __forceinline__ void dma4(const uint8_t* g, const char* lds_wave_base) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off"
@@ -349,11 +364,18 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const Tile& t, char*
   // (l%8) ^ swz(row)
   constexpr int ND = kLoadRows / 8;
   const int drow = kLoadRows * w + (lane >> 3);
-  // source addresses are formed at issue time (few VALU operations per load) rather than kept in
-  // registers, which the accumulators need
   auto dchunk = [&](int j) { return (lane & 7) ^ swz(drow + 8 * j); };
-  auto a_src = [&](int j) { return p.a + a_row(drow + 8 * j) * p.lda + a_col0 + 16 * dchunk(j); };
-  auto b_src = [&](int j) { return p.b + b_row(drow + 8 * j) * p.ldb + b_col0 + 16 * dchunk(j); };
+  // operand rows of the tile relative to its first row (rows never decrease with r): a uniform base per
+  // operand and a 32-bit byte offset per lane and load (the host keeps 256 rows, or the gated forward's
+  // N weight rows, of a stride below 4 GiB)
+  const uint8_t* a_base = p.a + a_row(0) * p.lda + a_col0;
+  const uint8_t* b_base = p.b + b_row(0) * p.ldb + b_col0;
+  uint32_t a_off[ND], b_off[ND];
+#pragma unroll
+  for (int j = 0; j < ND; ++j) {
+    a_off[j] = (uint32_t)((a_row(drow + 8 * j) - a_row(0)) * p.lda) + 16 * dchunk(j);
+    b_off[j] = (uint32_t)((b_row(drow + 8 * j) - b_row(0)) * p.ldb) + 16 * dchunk(j);
+  }
   // scale loads: four E8M0 bytes per row and stage, landing as one dword per row (A rows then B
   // rows).  When the four bytes are an aligned dword in memory (forward, dgrad), the 512 rows move
   // as 8 direct-to-LDS dword loads of 64 rows (u < 4: A rows [64u, 64u + 64), else B rows), spread
@@ -421,8 +443,8 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const Tile& t, char*
     for (int j = 0; j < ND; ++j) {
       // wgrad: chunks past the expert's blocks are not loaded (zeroed after landing)
       if (MODE != kWgrad || koff + 16 * dchunk(j) < L) {
-        dma16(a_src(j) + koff, st + (kLoadRows * w + 8 * j) * BK);
-        dma16(b_src(j) + koff, st + kStageA + (kLoadRows * w + 8 * j) * BK);
+        dma16s(a_off[j], a_base + koff, st + (kLoadRows * w + 8 * j) * BK);
+        dma16s(b_off[j], b_base + koff, st + kStageA + (kLoadRows * w + 8 * j) * BK);
       }
     }
     if (SDW) {
@@ -461,13 +483,20 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const Tile& t, char*
   constexpr int CPB = 8 / BPS;                    // 16-byte chunks per block
   for (int ks = 0; ks < nsteps; ++ks) {
     stage_barrier();                               // stage ks landed; stage ks-1 fully read
-    if (ks + 1 < nsteps) {
-      // the staged scale words arrived before the barrier; store them before issuing the next
-      // stage's loads so that no wait on those loads is needed here
-      if (!SDW) put_scales(ks + 1, s_w);
-      issue(ks + 1);
-      if (!SDW && ks + 2 < nsteps) gather_scales(ks + 2, s_w);
-    }
+    // The next stage's loads may go out any time after the barrier (its buffer was last read in stage
+    // ks - 1) and must land by the next barrier.  The precise feed issues them after its first block's
+    // MFMAs, so that a stage opens with LDS reads, widening and MFMAs rather than with the issue.
+    auto next_stage = [&]() {
+      if (ks + 1 < nsteps) {
+        // the staged scale words arrived before the barrier; store them before issuing the next
+        // stage's loads so that no wait on those loads is needed here
+        if (!SDW) put_scales(ks + 1, s_w);
+        issue(ks + 1);
+        if (!SDW && ks + 2 < nsteps) gather_scales(ks + 2, s_w);
+      }
+    };
+    constexpr bool kLateIssue = FEED == kFeedPrecise;
+    if constexpr (!kLateIssue) next_stage();
     char* st = lds + (ks & 1) * kStage;
     const uint32_t* SA = (const uint32_t*)(lds + 2 * kStage + (ks & 1) * kSStage);
     const uint32_t* SB = SA + BM;
@@ -520,6 +549,7 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const Tile& t, char*
 #pragma unroll
           for (int j = 0; j < NJ; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bhi[j], ahi[i], acc[i][j], 0, 0, 0);
+        if (kLateIssue && bb == 0) next_stage();
       }
     } else if constexpr (FP4) {
       // two k-steps of 128 E2M1 elements: lane group fg feeds block 4 ks2 + fg (16 bytes, the upper
@@ -622,6 +652,15 @@ __global__ __launch_bounds__(NT, 1) void mx_grouped_gemm_kernel(GemmArgs p) {
   __shared__ __attribute__((aligned(16))) char lds[kLds];
   Tile t;
   if (!decode_tile<MODE>(p, lds, t)) return;     // uniform across the workgroup
+  // the tile's fields are the same in every lane: say so, so that everything derived from them (operand
+  // bases, loop bounds) lives in scalar registers
+  t.g = __builtin_amdgcn_readfirstlane(t.g);
+  t.mt = __builtin_amdgcn_readfirstlane(t.mt);
+  t.nt = __builtin_amdgcn_readfirstlane(t.nt);
+  t.rows = __builtin_amdgcn_readfirstlane(t.rows);
+  t.nblk = __builtin_amdgcn_readfirstlane(t.nblk);
+  t.row0 = uniform64(t.row0);
+  t.col0 = uniform64(t.col0);
   __syncthreads();                               // scheduler scratch is reused for operands
   run_tile<MODE, FEED, SDW, FP4, ACT>(p, t, lds);
 }

@@ -132,6 +132,12 @@ def test_gemm_argument_errors():
     # wgrad: ld < mx_colwise_ld_min
     st, msg = _status(L, "mx_grouped_gemm_wgrad", A16, A16, A16b, A16b, 1024, A16, 4, 1024, 512, 256, A16, 0, None)
     assert st == 2 and "ld" in msg
+    # operand rows too long for the 32-bit offsets of a 256-row tile (K = 2^25 bytes per row)
+    a = list(ok_args); a[8] = 1 << 25
+    st, msg = _status(L, "mx_grouped_gemm_fwd", *a)
+    assert st == 2 and "stride" in msg
+    st, msg = _status(L, "mx_grouped_gemm_wgrad", A16, A16, A16b, A16b, 1 << 25, A16, 4, 1024, 512, 256, A16, 0, None)
+    assert st == 2 and "stride" in msg
     # blockwise
     a = list(ok_args); a[8] = 200
     assert _status(L, "fp8bw_grouped_gemm_fwd", *a)[0] == 2
