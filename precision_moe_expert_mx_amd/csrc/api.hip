@@ -183,12 +183,13 @@ mxmoe_status mx_quantize_dual(const void* x, int64_t R, int64_t C, const int32_t
 }
 
 // The GEMM addresses a tile's operand rows as 32-bit byte offsets from the tile's first row: 256 rows
-// (the gated forward: the N weight rows of an expert) of each operand must span less than 4 GiB.
+// (the gated forward: the N weight rows of an expert) of each operand must span less than 2 GiB, so that
+// an offset is the same read as signed or unsigned.
 static mxmoe_status check_strides(const char* fn, const GemmArgs& p, int64_t b_rows) {
-  const int64_t lim = (int64_t)1 << 32;
+  const int64_t lim = (int64_t)1 << 31;
   if (256 * p.lda + 256 > lim || b_rows * p.ldb + 256 > lim)
     return fail(MXMOE_ERR_SHAPE, "%s: operand row stride too large (lda=%lld ldb=%lld bytes): a tile's rows must "
-                "span less than 4 GiB", fn, (long long)p.lda, (long long)p.ldb);
+                "span less than 2 GiB", fn, (long long)p.lda, (long long)p.ldb);
   return MXMOE_OK;
 }
 

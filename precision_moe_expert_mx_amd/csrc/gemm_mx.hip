@@ -366,8 +366,8 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const Tile& t, char*
   const int drow = kLoadRows * w + (lane >> 3);
   auto dchunk = [&](int j) { return (lane & 7) ^ swz(drow + 8 * j); };
   // operand rows of the tile relative to its first row (rows never decrease with r): a uniform base per
-  // operand and a 32-bit byte offset per lane and load (the host keeps 256 rows, or the gated forward's
-  // N weight rows, of a stride below 4 GiB)
+  // operand and a 32-bit byte offset per lane and load (the host keeps the span of 256 rows, or of the
+  // gated forward's N weight rows, below 2 GiB)
   const uint8_t* a_base = p.a + a_row(0) * p.lda + a_col0;
   const uint8_t* b_base = p.b + b_row(0) * p.ldb + b_col0;
   uint32_t a_off[ND], b_off[ND];
