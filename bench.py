@@ -276,11 +276,11 @@ def mfma_summary(pmc_dir: str, cmds) -> None:
     sum(SQ_VALU_MFMA_BUSY_CYCLES) / (max over XCDs of GRBM_GUI_ACTIVE x SIMD count), the busy count being
     per SIMD."""
     import csv
-    from workloads import make_workload
+    from workloads import layer_shapes
     flops = {}
-    for lay in make_workload("dsv3_671b_shard").layers:
+    for name, M, N, K in layer_shapes("dsv3_671b_shard"):
         for k in ("fwd", "dgrad", "wgrad"):
-            flops[f"{lay.name}.{k}"] = 2.0 * lay.M * lay.N * lay.K
+            flops[f"{name}.{k}"] = 2.0 * M * N * K
     per_disp = {}
     for r in csv.DictReader(open(os.path.join(pmc_dir, "p_counter_collection.csv"))):
         d = per_disp.setdefault(int(r["Dispatch_Id"]), {"name": r["Kernel_Name"]})

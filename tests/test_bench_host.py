@@ -70,3 +70,53 @@ def test_pmc_summary_maps_dispatches_and_calibrates(tmp_path, monkeypatch):
     assert bench.read_traffic(str(gfile)) == g["ops"]
     assert bench.read_traffic(str(qfile), bench.quant_source_hash()) == q["ops"]
     assert bench.read_traffic(str(qfile), "0" * 16) is None
+
+
+def test_layer_shapes_match_the_workloads():
+    import numpy as np
+    import workloads as W
+    tiny = W.make_workload("tiny").layers[0]
+    assert W.layer_shapes("tiny") == [(tiny.name, tiny.M, tiny.N, tiny.K)]
+    # the routed-row counts of the large workloads, from their (cheap) group-size draws
+    assert int(np.sum(W._sizes_zipf_shard(np.random.default_rng(103)))) == W.layer_shapes("dsv3_671b_shard")[0][1]
+    assert int(np.sum(W._sizes_top6(np.random.default_rng(102)))) == W.layer_shapes("dsv3_16b")[0][1]
+    assert int(np.sum(W._sizes_dirichlet(np.random.default_rng(104)))) == W.layer_shapes("llama4_scout")[0][1]
+
+
+def test_mfma_summary_clock_and_utilisation(tmp_path, monkeypatch):
+    gemm = "void mxmoe::(anonymous namespace)::mx_grouped_gemm_kernel<0, 0, true, false, false>(mxmoe::GemmArgs)"
+    quant = "void mxmoe::mx_colwise_kernel<true, false, true, false>(...)"
+    order = [quant, quant, gemm, quant, gemm, gemm] * 2
+    ns = {}
+    with open(tmp_path / "p_counter_collection.csv", "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+        w.writeheader()
+        for i, n in enumerate(order, start=1):
+            ns[i] = 1_000_000 * i                                 # launch i lasts i ms
+            # 2 GHz on every XCD: 8 x 2e6 i cycles summed over the XCDs; MfmaUtil 50 + i %
+            for c, v in (("GRBM_GUI_ACTIVE", 8 * 2.0 * ns[i]), ("SQ_VALU_MFMA_BUSY_CYCLES", 1e6 * i),
+                         ("MfmaUtil", 50.0 + i)):
+                w.writerow({"Dispatch_Id": i, "Kernel_Name": n, "Counter_Name": c, "Counter_Value": v})
+    with open(tmp_path / "p_kernel_trace.csv", "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Dispatch_Id", "Start_Timestamp", "End_Timestamp"])
+        w.writeheader()
+        for i in ns:
+            w.writerow({"Dispatch_Id": i, "Start_Timestamp": 10 * ns[i], "End_Timestamp": 11 * ns[i]})
+    out = tmp_path / "mfma.txt"
+    monkeypatch.setattr(bench, "MFMA_FILE", str(out))
+    bench.mfma_summary(str(tmp_path), ["cmd"])
+    rec = json.loads(out.read_text().splitlines()[-1])
+    gemm_disp = [i for i, n in enumerate(order, start=1) if n == gemm]
+    shapes = {f"{l}.{k}": 2.0 * M * N * K for l, M, N, K in bench_shapes() for k in ("fwd", "dgrad", "wgrad")}
+    for name, i in zip(bench.GEMM_NAMES, gemm_disp):
+        o = rec["ops"][name]
+        assert o["clock_ghz"] == 2.0 and o["us"] == round(ns[i] / 1e3, 1)
+        assert o["mfma_util"] == round((50.0 + i) / 100, 4)
+        tf = shapes[name] / (ns[i] * 1e-9) / 1e12
+        assert abs(o["tflops"] - round(tf, 1)) < 1e-9
+        assert abs(o["frac_of_rate_at_clock"] - round(tf / (1024 * 1024 * 2.0e9 / 1e12), 4)) < 1e-9
+
+
+def bench_shapes():
+    from workloads import layer_shapes
+    return layer_shapes("dsv3_671b_shard")

@@ -33,7 +33,7 @@ from __future__ import annotations
 import os
 from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field
-from typing import Dict, List, Optional
+from typing import Dict, List, Optional, Tuple
 
 import numpy as np
 
@@ -219,6 +219,21 @@ def random_offsets(rng, M: int, G: int, empty_frac: float = 0.25) -> np.ndarray:
         w[0] = 1.0
     sizes = rng.multinomial(M, w / w.sum())
     return routing_offsets(sizes)
+
+
+# (layer, routed rows M, N, K) of each workload, as make_workload builds them (no data generated)
+_SHAPES: Dict[str, List[Tuple[str, int, int, int]]] = {
+    "tiny": [("single", 1024, 512, 256)],
+    "dsv3_16b": [("gate_up", 49152, 2816, 2048), ("down", 49152, 2048, 1408)],
+    "dsv3_671b_shard": [("gate_up", 65536, 4096, 7168), ("down", 65536, 7168, 2048)],
+    "llama4_scout": [("gate_up", 32768, 16384, 5120), ("down", 32768, 5120, 8192)],
+}
+_SHAPES["dsv3_16b_blockwise"] = _SHAPES["dsv3_16b"]
+
+
+def layer_shapes(name: str) -> List[Tuple[str, int, int, int]]:
+    """(layer, M, N, K) of a named workload's layers without generating its tensors."""
+    return list(_SHAPES[name])
 
 
 def make_workload(name: str, layers: Optional[List[str]] = None) -> Workload:
