@@ -488,11 +488,13 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const Tile& t, char*
     // MFMAs, so that a stage opens with LDS reads, widening and MFMAs rather than with the issue.
     auto next_stage = [&]() {
       if (ks + 1 < nsteps) {
-        // the staged scale words arrived before the barrier; store them before issuing the next
-        // stage's loads so that no wait on those loads is needed here
+        // The staged scale words arrived before the barrier.  They are stored, and the next words
+        // gathered, before the stage's operand loads go out: a wait the compiler places for those
+        // registers counts only its own loads, while the hardware counter would also hold the operand
+        // loads issued after them, and waiting on it there stalls on the next stage's data.
         if (!SDW) put_scales(ks + 1, s_w);
-        issue(ks + 1);
         if (!SDW && ks + 2 < nsteps) gather_scales(ks + 2, s_w);
+        issue(ks + 1);
       }
     };
     constexpr bool kLateIssue = FEED == kFeedPrecise;
