@@ -78,9 +78,9 @@ int64_t mx_colwise_ld_min(int64_t M, int32_t G);
 
 /* mxmoe_pitch: the row pitch (bytes of one qT row: ld for E4M3 codes, ld / 2 for
  * E2M1) this library recommends for a column-wise output whose minimum is min_ld
- * bytes: min_ld itself,
- * raised in steps of 1024 while it has the form 2^p + 2^(p-k), k in {7, 8, 9}
- * (the residues modulo 32, 128 and 1024 are kept).  Measured on MI355X, the
+ * bytes: min_ld rounded up to a multiple of 128 (the weight-gradient GEMM then
+ * reads the scale rows, ld / 32 bytes, as aligned words straight into LDS), then
+ * raised in steps of 1024 while it has the form 2^p + 2^(p-k), k in {7, 8, 9}.  Measured on MI355X, the
  * column-wise and dual-layout quantisers write such pitches 15-25% slower: with
  * the DeepSeek-V3-671B expert shard's minimum 65792 = 2^16 + 2^8 the dual launch
  * runs at 4.2 TB/s, at 5.1 TB/s with 65792 + 1024, and the weight-gradient GEMM

@@ -117,7 +117,8 @@ static bool slow_pitch(int64_t ld) {
 
 int64_t mxmoe_pitch(int64_t min_ld) {
   if (min_ld < 0) return -1;
-  int64_t ld = min_ld;
+  if (min_ld > INT64_MAX - 2048) return min_ld;
+  int64_t ld = (min_ld + 127) / 128 * 128;      // scale rows of ld / 32 bytes are then aligned dwords
   while (slow_pitch(ld) && ld <= INT64_MAX - 1024) ld += 1024;
   return ld;
 }

@@ -330,7 +330,13 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const Tile& t, char*
   // E2M1: two elements per byte, so a 128-byte stage holds eight 32-blocks
   constexpr int EPB = FP4 ? 2 : 1;            // elements per byte
   constexpr int SPS = FP4 ? 8 : 4;            // scale bytes per row and stage
-  constexpr int kSStage = FP4 ? kScaleStage4 : kScaleStage;
+  // Weight gradient with direct-to-LDS scale loads (scale rows of aligned dwords): an expert's blocks
+  // start at an arbitrary block of the column-wise layout, so a stage's four scale bytes of a row begin
+  // sh = (first block) mod 4 bytes into an aligned dword, the same sh for every row of the tile (all
+  // belong to one expert).  Two dword planes per row are loaded and recombined by sh.
+  constexpr bool SHIFT = MODE == kWgrad && SDW;
+  static_assert(!SHIFT || (FEED == kFeedPrecise && !FP4), "shifted scale planes: E4M3 precise feed");
+  constexpr int kSStage = (FP4 || SHIFT) ? kScaleStage4 : kScaleStage;
 
   // ---- operand geometry (contraction offsets in bytes; scale offsets in 32-blocks) ------------
   int64_t L;
@@ -379,12 +385,14 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const Tile& t, char*
   // scale loads: four E8M0 bytes per row and stage, landing as one dword per row (A rows then B
   // rows).  When the four bytes are an aligned dword in memory (forward, dgrad), the 512 rows move
   // as 8 direct-to-LDS dword loads of 64 rows (u < 4: A rows [64u, 64u + 64), else B rows), spread
-  // over the waves.  Otherwise (wgrad: experts start at arbitrary 32-blocks) thread t gathers rows
+  // over the waves; the weight gradient does the same with two planes when its scale rows are aligned
+  // (SHIFT above).  Otherwise (wgrad: experts start at arbitrary 32-blocks) thread t gathers rows
   // q = t + NT j (q < 256: A row q, else B row q - 256) into registers one stage ahead and stores
   // the dwords to LDS.
   const uint8_t* sa = (const uint8_t*)p.sa;
   const uint8_t* sb = (const uint8_t*)p.sb;
   const int64_t sa_col0 = a_el0 / 32, sb_col0 = b_el0 / 32;
+  const int sh = SHIFT ? (int)(sa_col0 & 3) : 0;          // wgrad: sa_col0 == sb_col0
   constexpr int NS = SDW ? kScaleLoads : kScaleRows;
   const uint8_t* s_src[NS];
 #pragma unroll
@@ -393,7 +401,7 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const Tile& t, char*
     if (SDW) q = 64 * (kScaleLoads * w + j) + lane;
     else q = tid + NT * j;
     const int r = q & 255;
-    s_src[j] = q < 256 ? sa + a_row(r) * p.ldsa + sa_col0 : sb + b_row(r) * p.ldsb + sb_col0;
+    s_src[j] = (q < 256 ? sa + a_row(r) * p.ldsa + sa_col0 : sb + b_row(r) * p.ldsb + sb_col0) - sh;
   }
   // Scale bytes [SPS ks, SPS ks + nv) of a row (nv < SPS only in the last wgrad stage; the rest read
   // as 0) land as SPS / 4 dwords, dword d of every row in plane d of the stage's scale area.  Register
@@ -447,7 +455,17 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const Tile& t, char*
         dma16s(b_off[j], b_base + koff, st + kStageA + (kLoadRows * w + 8 * j) * BK);
       }
     }
-    if (SDW) {
+    if constexpr (SHIFT) {
+      // the aligned dword holding the stage's first scale byte, and the next one only when the stage's
+      // valid bytes reach into it (so no load passes the expert's bytes of the row)
+      const int nv = min(SPS, t.nblk - SPS * ks);
+#pragma unroll
+      for (int j = 0; j < NS; ++j) dma4(s_src[j] + SPS * ks, ss + 256 * (kScaleLoads * w + j));
+      if (sh + nv > 4) {
+#pragma unroll
+        for (int j = 0; j < NS; ++j) dma4(s_src[j] + SPS * ks + 4, ss + 2048 + 256 * (kScaleLoads * w + j));
+      }
+    } else if (SDW) {
 #pragma unroll
       for (int j = 0; j < NS; ++j)
 #pragma unroll
@@ -518,10 +536,27 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const Tile& t, char*
     if constexpr (FEED == kFeedPrecise) {
       const int lr = lane & 31, h = lane >> 5;
       uint32_t sa_w[NI], sb_w[NJ];
+      if constexpr (SHIFT) {
+        // the stage's four bytes from the two planes; bytes past the expert's last block (last stage)
+        // are masked to 0 (their operand chunks are zero, and a stale 0xFF would read as NaN)
+        const int nv = min(4, t.nblk - 4 * ks);
+        const uint32_t keep = nv >= 4 ? 0xFFFFFFFFu : ((1u << (8 * nv)) - 1u);
 #pragma unroll
-      for (int i = 0; i < NI; ++i) sa_w[i] = SA[WM * wm + 32 * i + lr];
+        for (int i = 0; i < NI; ++i) {
+          const int r = WM * wm + 32 * i + lr;
+          sa_w[i] = __builtin_amdgcn_alignbyte(SA[512 + r], SA[r], (uint32_t)sh) & keep;
+        }
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) sb_w[j] = SB[WN * wn + 32 * j + lr];
+        for (int j = 0; j < NJ; ++j) {
+          const int r = WN * wn + 32 * j + lr;
+          sb_w[j] = __builtin_amdgcn_alignbyte(SB[512 + r], SB[r], (uint32_t)sh) & keep;
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < NI; ++i) sa_w[i] = SA[WM * wm + 32 * i + lr];
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) sb_w[j] = SB[WN * wn + 32 * j + lr];
+      }
 #pragma unroll
       for (int bb = 0; bb < 4; ++bb) {
         v8bf alo[NI], ahi[NI], blo[NJ], bhi[NJ];
@@ -704,6 +739,9 @@ hipError_t launch_mx_gemm(int mode, const GemmArgs& args, hipStream_t st) {
   } else if (mode == kFwd) launch_mode<kFwd, true>(p, g, st);
   else if (mode == kDgrad && p.scale_dword) launch_mode<kDgrad, true>(p, g, st);
   else if (mode == kDgrad) launch_mode<kDgrad, false>(p, g, st);
+  else if (!p.fp4 && p.feed == kFeedPrecise && p.ldsa % 4 == 0 && p.ldsb % 4 == 0)
+    // scale rows of aligned dwords (a row pitch that is a multiple of 128): direct-to-LDS scale loads
+    hipLaunchKernelGGL((mx_grouped_gemm_kernel<kWgrad, kFeedPrecise, true>), g, dim3(NT), 0, st, p);
   else launch_mode<kWgrad, false>(p, g, st);
   return hipGetLastError();
 }

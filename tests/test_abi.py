@@ -52,23 +52,24 @@ def test_recommended_pitch():
     # the expert-shard minimum 2^16 + 2^8 and the slow weight pitch 2^15 + 2^7 move up by 1 KiB
     assert m.mxmoe_pitch(65792) == 65792 + 1024
     assert m.mxmoe_pitch(32896) == 32896 + 1024
-    # the other configs' minima and powers of two are kept
-    for ld in (1152, 51136, 33280, 32768, 57344, 131072, 180224, 65536):
+    # the other configs' minima and powers of two are kept, rounded up to a multiple of 128
+    for ld in (1152, 33280, 32768, 57344, 131072, 180224, 65536):
         assert m.mxmoe_pitch(ld) == ld
+    assert m.mxmoe_pitch(51136) == 51200 and m.mxmoe_pitch(1088) == 1152
     assert m.mxmoe_pitch(-1) == -1 and m.mxmoe_pitch(0) == 0
     assert m.mxmoe_pitch((1 << 62) + (1 << 54)) >= (1 << 62) + (1 << 54)   # no overflow near the top
     rng = np.random.default_rng(5)
     cands = sorted(slow) + [int(v) for v in rng.integers(0, 1 << 24, 2000) * 32]
     for ld in cands:
         got = m.mxmoe_pitch(ld)
-        want = ld
+        want = (ld + 127) // 128 * 128
         while want in slow:
             want += 1024
         assert got == want, (ld, got, want)
-    assert m.mx_colwise_ld(65536, 8) == 66816 and m.mx_colwise_ld(49152, 64) == 51136
+    assert m.mx_colwise_ld(65536, 8) == 66816 and m.mx_colwise_ld(49152, 64) == 51200
     assert m.mx_colwise_ld(32768) == 32768
     # E2M1 rows hold ld / 2 bytes: the shard's 65792 / 2 = 2^15 + 2^7 bytes is a slow pitch
-    assert m.mxfp4_colwise_ld(65536, 8) == 2 * (32896 + 1024) and m.mxfp4_colwise_ld(49152, 64) == 51136
+    assert m.mxfp4_colwise_ld(65536, 8) == 2 * (32896 + 1024) and m.mxfp4_colwise_ld(49152, 64) == 51200
 
 
 A16 = 0x10000      # fake, 16-byte aligned device addresses: never dereferenced on error paths

@@ -115,6 +115,30 @@ def test_ragged_groups_long_contractions():
     print(run_layer(m, L, check=("fwd", "dgrad")))
 
 
+def test_wgrad_scale_rows_both_paths():
+    """The weight gradient reads its scale rows through registers (row pitch not a multiple of 128) or
+    straight into LDS as two aligned word planes recombined by the expert's first block mod 4 (pitch a
+    multiple of 128).  Experts start at blocks of every residue mod 4, end in partial stages, and some
+    stages' scale bytes cross into the second word; both paths must match the oracle."""
+    m = require_gpu()
+    rng = np.random.default_rng(39)
+    # 32-blocks per expert 0, 3, 2, 4, 7, 1, 5, 2, 6: first blocks 0, 0, 3, 5, 9, 16, 17, 22, 24
+    sizes = [0, 70, 40, 128, 200, 5, 150, 33, 180]
+    L = _rand_layer(rng, sizes, 256, 384, outliers=0.002)
+    offs_d = dev(L.offs)
+    x, dy = dev(L.x), dev(L.dy)
+    ld_min = oracle.mx_colwise_ld_min(L.M, L.G)
+    assert ld_min % 128 != 0
+    for ld in (ld_min, m.mxmoe_pitch(ld_min)):
+        qdyT, sdyT = m.mx_quantize_colwise(dy, offs_d, ld=ld)
+        qxT, sxT = m.mx_quantize_colwise(x, offs_d, ld=ld)
+        hq = [host(t) for t in (qdyT, sdyT, qxT, sxT)]
+        ref, bnd = oracle.mx_gemm_wgrad(*hq, L.offs, L.N, L.K)
+        for dt in ("f32", "bf16"):
+            dw = m.mx_grouped_gemm_wgrad(qdyT, sdyT, qxT, sxT, offs_d, L.M, dt)
+            print("wgrad ld", ld, dt, _check(_gpu_out(dw), ref, bnd, dt, f"wgrad ld={ld} {dt}"))
+
+
 def test_wgrad_mixed_expert_sizes():
     """Experts of very different sizes in one launch (wgrad contraction length varies per expert)."""
     m = require_gpu()
