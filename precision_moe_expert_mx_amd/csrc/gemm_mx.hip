@@ -335,7 +335,7 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const Tile& t, char*
   // sh = (first block) mod 4 bytes into an aligned dword, the same sh for every row of the tile (all
   // belong to one expert).  Two dword planes per row are loaded and recombined by sh.
   constexpr bool SHIFT = MODE == kWgrad && SDW;
-  static_assert(!SHIFT || (FEED == kFeedPrecise && !FP4), "shifted scale planes: E4M3 precise feed");
+  static_assert(!SHIFT || !FP4, "shifted scale planes: E4M3 operands");
   constexpr int kSStage = (FP4 || SHIFT) ? kScaleStage4 : kScaleStage;
 
   // ---- operand geometry (contraction offsets in bytes; scale offsets in 32-blocks) ------------
@@ -520,6 +520,14 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const Tile& t, char*
     char* st = lds + (ks & 1) * kStage;
     const uint32_t* SA = (const uint32_t*)(lds + 2 * kStage + (ks & 1) * kSStage);
     const uint32_t* SB = SA + BM;
+    // the stage's scale word of operand row r; with SHIFT, recombined from the two planes, and the bytes
+    // past the expert's last block (last stage) masked to 0: their operand chunks are zero, and a stale
+    // 0xFF would read as NaN
+    const uint32_t keep = SHIFT && t.nblk - SPS * ks < 4 ? ((1u << (8 * (t.nblk - SPS * ks))) - 1u) : 0xFFFFFFFFu;
+    auto sword = [&](const uint32_t* S, int r) -> uint32_t {
+      if constexpr (SHIFT) return __builtin_amdgcn_alignbyte(S[512 + r], S[r], (uint32_t)sh) & keep;
+      else return S[r];
+    };
     if (MODE == kWgrad && ks == nsteps - 1 && (t.nblk % BPS)) {
       // the last stage holds fewer blocks: zero the unloaded chunks of every row (their scale bytes
       // were gathered as 0)
@@ -536,27 +544,10 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const Tile& t, char*
     if constexpr (FEED == kFeedPrecise) {
       const int lr = lane & 31, h = lane >> 5;
       uint32_t sa_w[NI], sb_w[NJ];
-      if constexpr (SHIFT) {
-        // the stage's four bytes from the two planes; bytes past the expert's last block (last stage)
-        // are masked to 0 (their operand chunks are zero, and a stale 0xFF would read as NaN)
-        const int nv = min(4, t.nblk - 4 * ks);
-        const uint32_t keep = nv >= 4 ? 0xFFFFFFFFu : ((1u << (8 * nv)) - 1u);
 #pragma unroll
-        for (int i = 0; i < NI; ++i) {
-          const int r = WM * wm + 32 * i + lr;
-          sa_w[i] = __builtin_amdgcn_alignbyte(SA[512 + r], SA[r], (uint32_t)sh) & keep;
-        }
+      for (int i = 0; i < NI; ++i) sa_w[i] = sword(SA, WM * wm + 32 * i + lr);
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-          const int r = WN * wn + 32 * j + lr;
-          sb_w[j] = __builtin_amdgcn_alignbyte(SB[512 + r], SB[r], (uint32_t)sh) & keep;
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < NI; ++i) sa_w[i] = SA[WM * wm + 32 * i + lr];
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) sb_w[j] = SB[WN * wn + 32 * j + lr];
-      }
+      for (int j = 0; j < NJ; ++j) sb_w[j] = sword(SB, WN * wn + 32 * j + lr);
 #pragma unroll
       for (int bb = 0; bb < 4; ++bb) {
         v8bf alo[NI], ahi[NI], blo[NJ], bhi[NJ];
@@ -624,7 +615,7 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const Tile& t, char*
         const v4i lo = *(const v4i*)(B + lds_off(r, fg));
         const v4i hi = *(const v4i*)(B + lds_off(r, 4 + fg));
         bf[j] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        sbv[j] = (int)((SB[r] >> (8 * fg)) & 0xFFu);
+        sbv[j] = (int)((sword(SB, r) >> (8 * fg)) & 0xFFu);
       }
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
@@ -632,7 +623,7 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const Tile& t, char*
         const v4i lo = *(const v4i*)(A + lds_off(r, fg));
         const v4i hi = *(const v4i*)(A + lds_off(r, 4 + fg));
         const v8i af = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        const int sav = (int)((SA[r] >> (8 * fg)) & 0xFFu);
+        const int sav = (int)((sword(SA, r) >> (8 * fg)) & 0xFFu);
 #pragma unroll
         for (int j = 0; j < NJ; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[j], af, acc[i][j], 0, 0, 0, sbv[j], 0, sav);
@@ -740,7 +731,9 @@ hipError_t launch_mx_gemm(int mode, const GemmArgs& args, hipStream_t st) {
   else if (mode == kDgrad && p.scale_dword) launch_mode<kDgrad, true>(p, g, st);
   else if (mode == kDgrad) launch_mode<kDgrad, false>(p, g, st);
   else if (!p.fp4 && p.feed == kFeedPrecise && p.ldsa % 4 == 0 && p.ldsb % 4 == 0)
-    // scale rows of aligned dwords (a row pitch that is a multiple of 128): direct-to-LDS scale loads
+    // scale rows of aligned dwords (a row pitch that is a multiple of 128): direct-to-LDS scale loads.
+    // The fast feed keeps the register path: its loop is bound by LDS reads, and the second plane
+    // measured slower there.
     hipLaunchKernelGGL((mx_grouped_gemm_kernel<kWgrad, kFeedPrecise, true>), g, dim3(NT), 0, st, p);
   else launch_mode<kWgrad, false>(p, g, st);
   return hipGetLastError();

@@ -137,6 +137,9 @@ def test_wgrad_scale_rows_both_paths():
         for dt in ("f32", "bf16"):
             dw = m.mx_grouped_gemm_wgrad(qdyT, sdyT, qxT, sxT, offs_d, L.M, dt)
             print("wgrad ld", ld, dt, _check(_gpu_out(dw), ref, bnd, dt, f"wgrad ld={ld} {dt}"))
+        # the full-rate FP8 feed (register path at both pitches; its own tolerance)
+        dw = m.mx_grouped_gemm_wgrad(qdyT, sdyT, qxT, sxT, offs_d, L.M, "f32", fast=True)
+        print("wgrad fast ld", ld, _check(_gpu_out(dw), ref, bnd, "f32", f"fast wgrad ld={ld}", rel=FAST_REL))
 
 
 def test_wgrad_mixed_expert_sizes():
