@@ -141,11 +141,14 @@ def test_quantisers_full_size_sampled():
     rows = np.concatenate([[0, lay.M - 1], rng.choice(lay.M, 300, replace=False)])
     qo, so = oracle.mx_quantize_rowwise(lay.x[rows])
     assert np.array_equal(host(q[rows]), qo) and np.array_equal(host(s[rows]), so)
-    ld = oracle.mx_colwise_ld_min(lay.M, lay.G)
-    qT, sT = m.mx_quantize_colwise(x, dev(lay.offs), ld=ld)
     cols = np.concatenate([[0, lay.K - 1], rng.choice(lay.K, 40, replace=False)])
-    qo, so = oracle.mx_quantize_colwise(np.ascontiguousarray(lay.x[:, cols]), lay.offs, ld)
-    assert np.array_equal(host(qT[cols]), qo) and np.array_equal(host(sT[cols]), so)
+    # the minimum row pitch and the recommended one the benchmark uses
+    ld_min = oracle.mx_colwise_ld_min(lay.M, lay.G)
+    for ld in (ld_min, m.mx_colwise_ld(lay.M, lay.G)):
+        qT, sT = m.mx_quantize_colwise(x, dev(lay.offs), ld=ld)
+        qo, so = oracle.mx_quantize_colwise(np.ascontiguousarray(lay.x[:, cols]), lay.offs, ld)
+        assert np.array_equal(host(qT[cols]), qo) and np.array_equal(host(sT[cols]), so)
+        del qT, sT
 
 
 def _dual_equal(m, x, offs, ld, row_idx=None):
@@ -219,14 +222,17 @@ def test_dual_full_size_sampled():
     m = require_gpu()
     lay = make_workload("dsv3_671b_shard", layers=["gate_up"]).layers[0]
     rng = np.random.default_rng(28)
-    ld = oracle.mx_colwise_ld_min(lay.M, lay.G)
-    q, s, qT, sT = m.mx_quantize_dual(dev(lay.x), dev(lay.offs), ld=ld)
     rows = np.concatenate([[0, lay.M - 1], rng.choice(lay.M, 300, replace=False)])
-    qo, so = oracle.mx_quantize_rowwise(lay.x[rows])
-    assert np.array_equal(host(q[rows]), qo) and np.array_equal(host(s[rows]), so)
     cols = np.concatenate([[0, lay.K - 1], rng.choice(lay.K, 40, replace=False)])
-    qo, so = oracle.mx_quantize_colwise(np.ascontiguousarray(lay.x[:, cols]), lay.offs, ld)
-    assert np.array_equal(host(qT[cols]), qo) and np.array_equal(host(sT[cols]), so)
+    qro, sro = oracle.mx_quantize_rowwise(lay.x[rows])
+    x = dev(lay.x)
+    # the minimum row pitch and the recommended one the benchmark uses
+    for ld in (oracle.mx_colwise_ld_min(lay.M, lay.G), m.mx_colwise_ld(lay.M, lay.G)):
+        q, s, qT, sT = m.mx_quantize_dual(x, dev(lay.offs), ld=ld)
+        assert np.array_equal(host(q[rows]), qro) and np.array_equal(host(s[rows]), sro)
+        qo, so = oracle.mx_quantize_colwise(np.ascontiguousarray(lay.x[:, cols]), lay.offs, ld)
+        assert np.array_equal(host(qT[cols]), qo) and np.array_equal(host(sT[cols]), so)
+        del q, s, qT, sT
 
 
 def test_blockwise_colwise_ragged_groups():
