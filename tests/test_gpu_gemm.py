@@ -142,6 +142,25 @@ def test_wgrad_scale_rows_both_paths():
         print("wgrad fast ld", ld, _check(_gpu_out(dw), ref, bnd, "f32", f"fast wgrad ld={ld}", rel=FAST_REL))
 
 
+def test_dgrad_padded_weight_pitch():
+    """dgrad reads the column-wise weight copy at any row pitch ldw >= G*N: a pitch whose scale rows are
+    aligned words (direct-to-LDS scale loads) and one whose are not (register-staged scale words)."""
+    m = require_gpu()
+    rng = np.random.default_rng(40)
+    L = _rand_layer(rng, [0, 5, 130, 1, 300], 256, 384, outliers=0.002)
+    offs_d = dev(L.offs)
+    qdy, sdy = m.mx_quantize_rowwise(dev(L.dy))
+    w = dev(L.w)
+    for extra in (384, 32):
+        ldw = L.G * L.N + extra
+        qwT, swT = m.mx_quantize_colwise(w, None, ld=ldw)
+        hq = [host(t) for t in (qdy, sdy, qwT, swT)]
+        ref, bnd = oracle.mx_gemm_dgrad(*hq, L.offs, L.N, L.K)
+        for dt in ("f32", "bf16"):
+            dx = m.mx_grouped_gemm_dgrad(qdy, sdy, qwT, swT, offs_d, L.K, dt)
+            print("dgrad ldw", ldw, dt, _check(_gpu_out(dx), ref, bnd, dt, f"dgrad ldw={ldw} {dt}"))
+
+
 def test_wgrad_mixed_expert_sizes():
     """Experts of very different sizes in one launch (wgrad contraction length varies per expert)."""
     m = require_gpu()
