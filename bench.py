@@ -319,6 +319,49 @@ def mfma_summary(pmc_dir: str, cmds) -> None:
     print(json.dumps(rec))
 
 
+STATS_FILE = os.path.join(ROOT, "profiles", "kernel_stats_dsv3_671b_shard.md")
+STATS_CMD = ("rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof5 -o bench -- "
+             "python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-extra-legs")
+
+
+def stats_summary(prof_dir: str) -> None:
+    """Markdown summary of a rocprofv3 --kernel-trace --stats run of this script (STATS_CMD): the
+    statistics table and, from the kernel trace, each kernel's launches grouped by grid size with their
+    register and LDS use and mean and minimum durations."""
+    import csv
+    import re
+    from collections import defaultdict
+
+    def short(n):
+        n = re.sub(r"^void ", "", n)
+        n = re.sub(r"\(anonymous namespace\)::", "", n)
+        return re.sub(r"\(.*\)$", "", n)
+
+    out = ["# Kernel statistics: DeepSeek-V3-671B expert shard, fwd+bwd step (precise feed)", "",
+           "Commands (from the repository root, one MI355X):", "", "```", STATS_CMD,
+           f"python3 bench.py --stats-summary {prof_dir}", "```", "",
+           "## rocprofv3 kernel statistics (all launches)", "",
+           "| Name | Calls | TotalDurationNs | AverageNs | Percentage | MinNs | MaxNs | StdDev |",
+           "|---|---|---|---|---|---|---|---|"]
+    for r in csv.DictReader(open(os.path.join(prof_dir, "bench_kernel_stats.csv"))):
+        out.append("| " + " | ".join([short(r["Name"])] + [r[k] for k in ("Calls", "TotalDurationNs", "AverageNs",
+                                                                           "Percentage", "MinNs", "MaxNs", "StdDev")]) + " |")
+    out += ["", "## Per kernel and grid size (from the kernel trace)", "",
+            "| kernel | grid (work-items) | VGPR | AGPR | LDS B | scratch B | calls | avg µs | min µs |",
+            "|---|---|---|---|---|---|---|---|---|"]
+    groups, meta = defaultdict(list), {}
+    for r in csv.DictReader(open(os.path.join(prof_dir, "bench_kernel_trace.csv"))):
+        k = (short(r["Kernel_Name"]), int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"]))
+        groups[k].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        meta[k] = (r["VGPR_Count"], r["Accum_VGPR_Count"], r["LDS_Block_Size"], r["Scratch_Size"])
+    for k in sorted(groups):
+        v = groups[k]
+        out.append(f"| `{k[0]}` | {k[1]} | " + " | ".join(meta[k]) + f" | {len(v)} | {sum(v) / len(v):.1f} | {min(v):.1f} |")
+    with open(STATS_FILE, "w") as f:
+        f.write("\n".join(out) + "\n")
+    print("\n".join(out))
+
+
 # ------------------------------------------------------------------------------------------- CPU oracle
 def cpu_baseline(lay, rows_per_expert=2048):
     """The oracle, as it stands, on a bounded sample: the largest expert's weights and its first
@@ -594,11 +637,17 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle timing")
     ap.add_argument("--no-extra-legs", action="store_true",
                     help="skip the FP8-feed and blockwise legs (reported beside the headline)")
+    ap.add_argument("--stats-summary", metavar="PROF_DIR",
+                    help="write the kernel-statistics summary from a rocprofv3 --kernel-trace --stats run of this script")
     ap.add_argument("--mfma-summary", metavar="PMC_DIR",
                     help="write the GEMM clock / MFMA-use summary from a rocprofv3 --kernel-trace --pmc run of this script")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the GEMM and quantiser traffic summaries from two rocprofv3 counter runs of this script")
     args = ap.parse_args()
+
+    if args.stats_summary:
+        stats_summary(args.stats_summary)
+        return
 
     if args.mfma_summary:
         mfma_summary(args.mfma_summary, [

@@ -120,3 +120,29 @@ def test_mfma_summary_clock_and_utilisation(tmp_path, monkeypatch):
 def bench_shapes():
     from workloads import layer_shapes
     return layer_shapes("dsv3_671b_shard")
+
+
+def test_stats_summary_groups_launches_by_grid(tmp_path, monkeypatch):
+    name = "void mxmoe::(anonymous namespace)::mx_grouped_gemm_kernel<2, 0, true, false, false>(mxmoe::GemmArgs)"
+    with open(tmp_path / "bench_kernel_stats.csv", "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Name", "Calls", "TotalDurationNs", "AverageNs", "Percentage", "MinNs", "MaxNs", "StdDev"])
+        w.writerow([name, 3, 600, 200, 100.0, 100, 300, 81.6])
+    fields = ["Kernel_Name", "Start_Timestamp", "End_Timestamp", "Grid_Size_X", "Grid_Size_Y", "Grid_Size_Z",
+              "VGPR_Count", "Accum_VGPR_Count", "LDS_Block_Size", "Scratch_Size"]
+    with open(tmp_path / "bench_kernel_trace.csv", "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=fields)
+        w.writeheader()
+        for start, end, grid in ((0, 1000, 512), (5000, 8000, 1024), (9000, 14000, 1024)):
+            w.writerow({"Kernel_Name": name, "Start_Timestamp": start, "End_Timestamp": end, "Grid_Size_X": grid,
+                        "Grid_Size_Y": 1, "Grid_Size_Z": 1, "VGPR_Count": 112, "Accum_VGPR_Count": 0,
+                        "LDS_Block_Size": 139264, "Scratch_Size": 0})
+    out = tmp_path / "stats.md"
+    monkeypatch.setattr(bench, "STATS_FILE", str(out))
+    bench.stats_summary(str(tmp_path))
+    text = out.read_text()
+    assert bench.STATS_CMD in text and "mxmoe::mx_grouped_gemm_kernel<2, 0, true, false, false>" in text
+    rows = [l for l in text.splitlines() if l.startswith("| `")]
+    # grid 512: one launch of 1 us; grid 1024: two launches of 3 and 5 us
+    assert rows[0].endswith("| 512 | 112 | 0 | 139264 | 0 | 1 | 1.0 | 1.0 |")
+    assert rows[1].endswith("| 1024 | 112 | 0 | 139264 | 0 | 2 | 4.0 | 3.0 |")
