@@ -80,12 +80,12 @@ int64_t mx_colwise_ld_min(int64_t M, int32_t G);
  * E2M1) this library recommends for a column-wise output whose minimum is min_ld
  * bytes: min_ld rounded up to a multiple of 128 (the weight-gradient GEMM then
  * reads the scale rows, ld / 32 bytes, as aligned words straight into LDS), then
- * raised in steps of 1024 while it has the form 2^p + 2^(p-k), k in {7, 8, 9}.  Measured on MI355X, the
- * column-wise and dual-layout quantisers write such pitches 15-25% slower: with
- * the DeepSeek-V3-671B expert shard's minimum 65792 = 2^16 + 2^8 the dual launch
- * runs at 4.2 TB/s, at 5.1 TB/s with 65792 + 1024, and the weight-gradient GEMM
- * that reads the copies gains 2%.  A performance hint only: any ld >= the
- * minimum is valid.  Pure host arithmetic; returns -1 for min_ld < 0. */
+ * raised in steps of 1024 while it has the form 2^p + 2^(p-k), k in {7, 8, 9}.
+ * Measured on MI355X, the column-wise and dual-layout quantisers write such
+ * pitches 15-25% slower: with the DeepSeek-V3-671B expert shard's minimum
+ * 65792 = 2^16 + 2^8 the dual launch runs at 4.2 TB/s, at 5.1 TB/s with
+ * 65792 + 1024.  A performance hint only: any ld >= the minimum is valid.  Pure
+ * host arithmetic; returns -1 for min_ld < 0. */
 int64_t mxmoe_pitch(int64_t min_ld);
 
 /* ---------------------------------------------------------------- MX quantise
@@ -133,7 +133,10 @@ mxmoe_status mx_quantize_dual(const void* x_bf16, int64_t R, int64_t C,
  * Each routine computes, for every expert g in ONE launch, a matrix product
  * over the expert's real rows, from MX operands (value = E4M3 * 2^(E8M0-127)),
  * accumulating in fp32 and writing fp32 or bf16 (round-to-nearest-even).
- * Shapes: N % 128 == 0 and K % 128 == 0.  1 <= G <= 1024.
+ * Shapes: N % 128 == 0 and K % 128 == 0.  1 <= G <= 1024.  A tile addresses
+ * its operand rows as 32-bit offsets: a row stride (K, N or the leading
+ * dimension, in bytes) at which 256 rows span 2 GiB or more is refused with
+ * MXMOE_ERR_SHAPE.
  * Operand feed and accuracy:
  *  - default (precise): each 32-block is widened exactly to bf16 with its scale
  *    folded in and multiplied on the bf16 MFMA, whose sums are fp32-accurate:
@@ -181,7 +184,9 @@ mxmoe_status mx_grouped_gemm_dgrad(const uint8_t* qdy, const uint8_t* sdy,
  *        varies per expert; dW_g = 0 for an empty expert, written)
  *        qdyT/sdyT = mx_quantize_colwise(dY [M, N], offs, ld);
  *        qxT/sxT   = mx_quantize_colwise(X  [M, K], offs, ld) with the same ld;
- *        dw [G, N, K] (dwdt). */
+ *        dw [G, N, K] (dwdt).  With ld % 128 == 0 (as mxmoe_pitch returns) the
+ *        scale rows are aligned words and the precise feed loads them straight
+ *        into LDS; other ld stage them through registers (slower, same result). */
 mxmoe_status mx_grouped_gemm_wgrad(const uint8_t* qdyT, const uint8_t* sdyT,
                                    const uint8_t* qxT, const uint8_t* sxT, int64_t ld,
                                    const int32_t* offs, int32_t G, int64_t M, int64_t N, int64_t K,
