@@ -72,7 +72,8 @@ constexpr int kStageA = BM * BK;                 // 32 KiB
 constexpr int kStage = kStageA + BN * BK;        // 64 KiB
 constexpr int kScaleStage = (BM + BN) * 4;       // four E8M0 bytes per operand row (E4M3)
 constexpr int kScaleStage4 = (BM + BN) * 8;      // eight E8M0 bytes per operand row (E2M1), two dword planes
-constexpr int kLds = 2 * kStage + 2 * kScaleStage4;
+constexpr int kScaleStage6 = (BM + BN) * 12;     // three dword planes (E2M1 wgrad, scale bytes at a byte offset)
+constexpr int kLds = 2 * kStage + 2 * kScaleStage6;
 constexpr int kMaxG = 1024;
 constexpr int kXcd = 8;
 constexpr int kChunk = 8;
@@ -335,8 +336,7 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const Tile& t, char*
   // sh = (first block) mod 4 bytes into an aligned dword, the same sh for every row of the tile (all
   // belong to one expert).  Two dword planes per row are loaded and recombined by sh.
   constexpr bool SHIFT = MODE == kWgrad && SDW;
-  static_assert(!SHIFT || !FP4, "shifted scale planes: E4M3 operands");
-  constexpr int kSStage = (FP4 || SHIFT) ? kScaleStage4 : kScaleStage;
+  constexpr int kSStage = SHIFT ? (FP4 ? kScaleStage6 : kScaleStage4) : (FP4 ? kScaleStage4 : kScaleStage);
 
   // ---- operand geometry (contraction offsets in bytes; scale offsets in 32-blocks) ------------
   int64_t L;
@@ -456,14 +456,15 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const Tile& t, char*
       }
     }
     if constexpr (SHIFT) {
-      // the aligned dword holding the stage's first scale byte, and the next one only when the stage's
-      // valid bytes reach into it (so no load passes the expert's bytes of the row)
+      // the aligned dword holding the stage's first scale byte, and each following one only when the
+      // stage's valid bytes reach into it (so no load passes the expert's bytes of the row)
       const int nv = min(SPS, t.nblk - SPS * ks);
 #pragma unroll
-      for (int j = 0; j < NS; ++j) dma4(s_src[j] + SPS * ks, ss + 256 * (kScaleLoads * w + j));
-      if (sh + nv > 4) {
+      for (int d = 0; d <= SPS / 4; ++d) {
+        if (d == 0 || sh + nv > 4 * d) {
 #pragma unroll
-        for (int j = 0; j < NS; ++j) dma4(s_src[j] + SPS * ks + 4, ss + 2048 + 256 * (kScaleLoads * w + j));
+          for (int j = 0; j < NS; ++j) dma4(s_src[j] + SPS * ks + 4 * d, ss + 2048 * d + 256 * (kScaleLoads * w + j));
+        }
       }
     } else if (SDW) {
 #pragma unroll
@@ -523,10 +524,15 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const Tile& t, char*
     // the stage's scale word of operand row r; with SHIFT, recombined from the two planes, and the bytes
     // past the expert's last block (last stage) masked to 0: their operand chunks are zero, and a stale
     // 0xFF would read as NaN
-    const uint32_t keep = SHIFT && t.nblk - SPS * ks < 4 ? ((1u << (8 * (t.nblk - SPS * ks))) - 1u) : 0xFFFFFFFFu;
-    auto sword = [&](const uint32_t* S, int r) -> uint32_t {
-      if constexpr (SHIFT) return __builtin_amdgcn_alignbyte(S[512 + r], S[r], (uint32_t)sh) & keep;
-      else return S[r];
+    const int nv_s = min(SPS, t.nblk - SPS * ks);
+    auto sword = [&](const uint32_t* S, int r, int word = 0) -> uint32_t {
+      if constexpr (SHIFT) {
+        const int k = nv_s - 4 * word;                // valid bytes of this word
+        const uint32_t keep = k >= 4 ? 0xFFFFFFFFu : (k <= 0 ? 0u : (1u << (8 * k)) - 1u);
+        return __builtin_amdgcn_alignbyte(S[512 * (word + 1) + r], S[512 * word + r], (uint32_t)sh) & keep;
+      } else {
+        return S[512 * word + r];
+      }
     };
     if (MODE == kWgrad && ks == nsteps - 1 && (t.nblk % BPS)) {
       // the last stage holds fewer blocks: zero the unloaded chunks of every row (their scale bytes
@@ -592,14 +598,14 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const Tile& t, char*
           const int r = WN * wn + 16 * j + fr;
           const v4i c = *(const v4i*)(B + lds_off(r, 4 * ks2 + fg));
           bf[j] = v8i{c[0], c[1], c[2], c[3], 0, 0, 0, 0};
-          sbv[j] = (int)((SB[512 * ks2 + r] >> (8 * fg)) & 0xFFu);
+          sbv[j] = (int)((sword(SB, r, ks2) >> (8 * fg)) & 0xFFu);
         }
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
           const int r = WM * wm + 16 * i + fr;
           const v4i c = *(const v4i*)(A + lds_off(r, 4 * ks2 + fg));
           const v8i af = v8i{c[0], c[1], c[2], c[3], 0, 0, 0, 0};
-          const int sav = (int)((SA[512 * ks2 + r] >> (8 * fg)) & 0xFFu);
+          const int sav = (int)((sword(SA, r, ks2) >> (8 * fg)) & 0xFFu);
 #pragma unroll
           for (int j = 0; j < NJ; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[j], af, acc[i][j], 4, 4, 0, sbv[j], 0, sav);
@@ -730,6 +736,9 @@ hipError_t launch_mx_gemm(int mode, const GemmArgs& args, hipStream_t st) {
   } else if (mode == kFwd) launch_mode<kFwd, true>(p, g, st);
   else if (mode == kDgrad && p.scale_dword) launch_mode<kDgrad, true>(p, g, st);
   else if (mode == kDgrad) launch_mode<kDgrad, false>(p, g, st);
+  else if (p.fp4 && p.ldsa % 4 == 0 && p.ldsb % 4 == 0)
+    // E2M1 with scale rows of aligned dwords: three planes straight into LDS
+    hipLaunchKernelGGL((mx_grouped_gemm_kernel<kWgrad, kFeedFast, true, true>), g, dim3(NT), 0, st, p);
   else if (!p.fp4 && p.feed == kFeedPrecise && p.ldsa % 4 == 0 && p.ldsb % 4 == 0)
     // scale rows of aligned dwords (a row pitch that is a multiple of 128): direct-to-LDS scale loads.
     // The fast feed keeps the register path: its loop is bound by LDS reads, and the second plane

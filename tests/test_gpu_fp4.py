@@ -117,6 +117,27 @@ def test_gemms_ragged_groups():
     print("fp4 padded ld", _fp4_layer_check(m, L, "f32", extra=2048))
 
 
+def test_wgrad_scale_rows_both_paths():
+    """MXFP4 weight gradient with its scale rows staged through registers (ld / 32 not a multiple of 4)
+    and straight into LDS as up to three aligned word planes (ld a multiple of 128): experts start at
+    blocks of every residue mod 4, with stages of 1 to 8 valid blocks, some needing the third plane."""
+    m = require_gpu()
+    rng = np.random.default_rng(43)
+    sizes = [0, 70, 300, 40, 128, 200, 5, 150, 33, 180]
+    L = _rand_layer(rng, sizes, 256, 512, outliers=0.002)
+    offs = dev(L.offs)
+    x, dy = dev(L.x), dev(L.dy)
+    ld_min = oracle.mx_colwise_ld_min(L.M, L.G)
+    assert (ld_min // 32) % 4 != 0
+    for ld in (ld_min, m.mxfp4_colwise_ld(L.M, L.G)):
+        qdT, sdT = m.mxfp4_quantize_colwise(dy, offs, ld=ld)
+        qxT, sxT = m.mxfp4_quantize_colwise(x, offs, ld=ld)
+        ref, bnd = oracle.mxfp4_gemm_wgrad(host(qdT), host(sdT), host(qxT), host(sxT), L.offs, L.N, L.K)
+        for dt in ("f32", "bf16"):
+            dw = m.mxfp4_grouped_gemm_wgrad(qdT, sdT, qxT, sxT, offs, L.M, dt)
+            print("fp4 wgrad ld", ld, dt, _check(_gpu_out(dw), ref, bnd, dt, f"fp4 wgrad ld={ld} {dt}"))
+
+
 def test_run_of_mixed_magnitudes_is_exact():
     """Products 36 and 0.25 (6 x 6 and 0.5 x 0.5) side by side in every 32-block, and blocks whose
     scales differ by up to 2^+-4: all terms are multiples of 2^-6 below 2^18, so every partial sum is
