@@ -72,8 +72,7 @@ constexpr int kStageA = BM * BK;                 // 32 KiB
 constexpr int kStage = kStageA + BN * BK;        // 64 KiB
 constexpr int kScaleStage = (BM + BN) * 4;       // four E8M0 bytes per operand row (E4M3)
 constexpr int kScaleStage4 = (BM + BN) * 8;      // eight E8M0 bytes per operand row (E2M1), two dword planes
-constexpr int kScaleStage6 = (BM + BN) * 12;     // three dword planes (E2M1 wgrad, scale bytes at a byte offset)
-constexpr int kLds = 2 * kStage + 2 * kScaleStage6;
+constexpr int kLds = 2 * kStage + 2 * kScaleStage4;
 constexpr int kMaxG = 1024;
 constexpr int kXcd = 8;
 constexpr int kChunk = 8;
@@ -332,20 +331,26 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const Tile& t, char*
   constexpr int EPB = FP4 ? 2 : 1;            // elements per byte
   constexpr int SPS = FP4 ? 8 : 4;            // scale bytes per row and stage
   // Weight gradient with direct-to-LDS scale loads (scale rows of aligned dwords): an expert's blocks
-  // start at an arbitrary block of the column-wise layout, so a stage's four scale bytes of a row begin
-  // sh = (first block) mod 4 bytes into an aligned dword, the same sh for every row of the tile (all
-  // belong to one expert).  Two dword planes per row are loaded and recombined by sh.
-  constexpr bool SHIFT = MODE == kWgrad && SDW;
-  constexpr int kSStage = SHIFT ? (FP4 ? kScaleStage6 : kScaleStage4) : (FP4 ? kScaleStage4 : kScaleStage);
+  // start at an arbitrary block of the column-wise layout.  Its contraction starts f = (first block)
+  // mod 4 blocks earlier, at a block whose scale byte opens an aligned dword (the same f for every row
+  // of the tile: all belong to one expert), so every stage's scale bytes are whole dwords.  The f
+  // leading blocks of the first stage are not loaded: their operand chunks are zeroed and their scale
+  // bytes masked to 0, so they add exact zeros.
+  constexpr bool ALIGNED_START = MODE == kWgrad && SDW;
+  static_assert(!(ALIGNED_START && FP4), "the E2M1 weight gradient gathers its scale rows in registers");
+  constexpr int kSStage = FP4 ? kScaleStage4 : kScaleStage;
 
   // ---- operand geometry (contraction offsets in bytes; scale offsets in 32-blocks) ------------
+  const int f = ALIGNED_START && t.nblk > 0 ? (int)((t.col0 / 32) & 3) : 0;   // leading blocks
+  const int nblk_e = t.nblk + f;                                                // wgrad: blocks looped over
   int64_t L;
   if (MODE == kFwd) L = p.K / EPB;
   else if (MODE == kDgrad) L = p.N / EPB;
-  else L = 32 / EPB * (int64_t)t.nblk;
+  else L = 32 / EPB * (int64_t)nblk_e;
   const int nsteps = (int)((L + BK - 1) / BK);
-  const int64_t a_el0 = MODE == kWgrad ? t.col0 : 0;     // first contraction element
-  const int64_t b_el0 = MODE == kWgrad ? t.col0 : (MODE == kDgrad ? (int64_t)t.g * p.N : 0);
+  const int64_t L0 = 32 / EPB * f;                        // bytes of the leading blocks (first stage)
+  const int64_t a_el0 = MODE == kWgrad ? t.col0 - 32 * f : 0;     // first contraction element
+  const int64_t b_el0 = MODE == kWgrad ? t.col0 - 32 * f : (MODE == kDgrad ? (int64_t)t.g * p.N : 0);
   const int64_t a_col0 = a_el0 / EPB, b_col0 = b_el0 / EPB;
   const int64_t a_rows_lim = MODE == kWgrad ? p.N : 0;     // wgrad: A rows are n
   const int64_t b_rows_lim = MODE == kFwd ? p.N : p.K;
@@ -385,14 +390,13 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const Tile& t, char*
   // scale loads: four E8M0 bytes per row and stage, landing as one dword per row (A rows then B
   // rows).  When the four bytes are an aligned dword in memory (forward, dgrad), the 512 rows move
   // as 8 direct-to-LDS dword loads of 64 rows (u < 4: A rows [64u, 64u + 64), else B rows), spread
-  // over the waves; the weight gradient does the same with two planes when its scale rows are aligned
-  // (SHIFT above).  Otherwise (wgrad: experts start at arbitrary 32-blocks) thread t gathers rows
+  // over the waves; the weight gradient does the same when its scale rows are aligned
+  // (ALIGNED_START above).  Otherwise (wgrad: experts start at arbitrary 32-blocks) thread t gathers rows
   // q = t + NT j (q < 256: A row q, else B row q - 256) into registers one stage ahead and stores
   // the dwords to LDS.
   const uint8_t* sa = (const uint8_t*)p.sa;
   const uint8_t* sb = (const uint8_t*)p.sb;
   const int64_t sa_col0 = a_el0 / 32, sb_col0 = b_el0 / 32;
-  const int sh = SHIFT ? (int)(sa_col0 & 3) : 0;          // wgrad: sa_col0 == sb_col0
   constexpr int NS = SDW ? kScaleLoads : kScaleRows;
   const uint8_t* s_src[NS];
 #pragma unroll
@@ -401,7 +405,7 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const Tile& t, char*
     if (SDW) q = 64 * (kScaleLoads * w + j) + lane;
     else q = tid + NT * j;
     const int r = q & 255;
-    s_src[j] = (q < 256 ? sa + a_row(r) * p.ldsa + sa_col0 : sb + b_row(r) * p.ldsb + sb_col0) - sh;
+    s_src[j] = q < 256 ? sa + a_row(r) * p.ldsa + sa_col0 : sb + b_row(r) * p.ldsb + sb_col0;
   }
   // Scale bytes [SPS ks, SPS ks + nv) of a row (nv < SPS only in the last wgrad stage; the rest read
   // as 0) land as SPS / 4 dwords, dword d of every row in plane d of the stage's scale area.  Register
@@ -411,7 +415,7 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const Tile& t, char*
   // between the loads of a stage.
   constexpr int P = SPS / 4;                  // dword planes
   auto scale_geom = [&](int j, int ks, int& nv, int& sh) -> const uint32_t* {
-    nv = MODE == kWgrad ? min(SPS, t.nblk - SPS * ks) : SPS;
+    nv = MODE == kWgrad ? min(SPS, nblk_e - SPS * ks) : SPS;
     const uintptr_t ai = (uintptr_t)(s_src[j] + SPS * ks);
     sh = (int)(ai & 3);
     return (const uint32_t*)(ai & ~(uintptr_t)3);
@@ -447,21 +451,25 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const Tile& t, char*
     char* st = lds + (ks & 1) * kStage;
     char* ss = lds + 2 * kStage + (ks & 1) * kSStage;
     const int64_t koff = (int64_t)ks * BK;
+    // wgrad: chunks outside the expert's blocks, bytes [lim_lo, lim_hi) of the stage's rows, are not
+    // loaded (zeroed after landing)
+    const int lim_hi = (int)min(L - koff, (int64_t)BK);
+    const int lim_lo = ks == 0 ? (int)L0 : 0;
 #pragma unroll
     for (int j = 0; j < ND; ++j) {
-      // wgrad: chunks past the expert's blocks are not loaded (zeroed after landing)
-      if (MODE != kWgrad || koff + 16 * dchunk(j) < L) {
+      const int c = 16 * dchunk(j);
+      if (MODE != kWgrad || (c < lim_hi && c >= lim_lo)) {
         dma16s(a_off[j], a_base + koff, st + (kLoadRows * w + 8 * j) * BK);
         dma16s(b_off[j], b_base + koff, st + kStageA + (kLoadRows * w + 8 * j) * BK);
       }
     }
-    if constexpr (SHIFT) {
-      // the aligned dword holding the stage's first scale byte, and each following one only when the
-      // stage's valid bytes reach into it (so no load passes the expert's bytes of the row)
-      const int nv = min(SPS, t.nblk - SPS * ks);
+    if constexpr (ALIGNED_START) {
+      // the stage's first scale dword, and the second (E2M1) only when the stage's blocks reach into
+      // it (so no load passes the expert's bytes of the row)
+      const int nv = min(SPS, nblk_e - SPS * ks);
 #pragma unroll
-      for (int d = 0; d <= SPS / 4; ++d) {
-        if (d == 0 || sh + nv > 4 * d) {
+      for (int d = 0; d < SPS / 4; ++d) {
+        if (d == 0 || nv > 4 * d) {
 #pragma unroll
           for (int j = 0; j < NS; ++j) dma4(s_src[j] + SPS * ks + 4 * d, ss + 2048 * d + 256 * (kScaleLoads * w + j));
         }
@@ -521,26 +529,32 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const Tile& t, char*
     char* st = lds + (ks & 1) * kStage;
     const uint32_t* SA = (const uint32_t*)(lds + 2 * kStage + (ks & 1) * kSStage);
     const uint32_t* SB = SA + BM;
-    // the stage's scale word of operand row r; with SHIFT, recombined from the two planes, and the bytes
-    // past the expert's last block (last stage) masked to 0: their operand chunks are zero, and a stale
-    // 0xFF would read as NaN
-    const int nv_s = min(SPS, t.nblk - SPS * ks);
+    // the stage's blocks [lo_b, hi_b) belong to the expert: the leading blocks (first stage) and those
+    // past its last block (last stage) were not loaded
+    const int lo_b = ks == 0 ? f : 0;
+    const int hi_b = MODE == kWgrad ? min(SPS, nblk_e - SPS * ks) : SPS;
+    // the stage's scale word of operand row r; with ALIGNED_START, the bytes of blocks outside
+    // [lo_b, hi_b) masked to 0: their operand chunks are zero, and a stale 0xFF would read as NaN
+    uint32_t keep[SPS / 4];                       // wave-uniform byte masks of the stage's scale words
+#pragma unroll
+    for (int d = 0; d < SPS / 4; ++d) {
+      auto low = [](int k) { return k >= 4 ? 0xFFFFFFFFu : (k <= 0 ? 0u : (1u << (8 * k)) - 1u); };
+      keep[d] = __builtin_amdgcn_readfirstlane(low(hi_b - 4 * d) & ~low(lo_b - 4 * d));
+    }
     auto sword = [&](const uint32_t* S, int r, int word = 0) -> uint32_t {
-      if constexpr (SHIFT) {
-        const int k = nv_s - 4 * word;                // valid bytes of this word
-        const uint32_t keep = k >= 4 ? 0xFFFFFFFFu : (k <= 0 ? 0u : (1u << (8 * k)) - 1u);
-        return __builtin_amdgcn_alignbyte(S[512 * (word + 1) + r], S[512 * word + r], (uint32_t)sh) & keep;
+      if constexpr (ALIGNED_START) {
+        return S[512 * word + r] & keep[word];
       } else {
         return S[512 * word + r];
       }
     };
-    if (MODE == kWgrad && ks == nsteps - 1 && (t.nblk % BPS)) {
-      // the last stage holds fewer blocks: zero the unloaded chunks of every row (their scale bytes
-      // were gathered as 0)
+    if (MODE == kWgrad && (lo_b > 0 || hi_b < BPS)) {
+      // zero the unloaded chunks of every row (the register path gathered their scale bytes as 0)
       for (int q = tid; q < BM + BN; q += NT) {
         const int r = q & 255;
         char* row = st + (q < BM ? 0 : kStageA) + r * BK;
-        for (int c = CPB * (t.nblk % BPS); c < 8; ++c) *(uint4*)(row + ((c ^ swz(r)) << 4)) = make_uint4(0, 0, 0, 0);
+        for (int c = 0; c < 8; ++c)
+          if (c < CPB * lo_b || c >= CPB * hi_b) *(uint4*)(row + ((c ^ swz(r)) << 4)) = make_uint4(0, 0, 0, 0);
       }
       stage_barrier();
     }
@@ -736,14 +750,12 @@ hipError_t launch_mx_gemm(int mode, const GemmArgs& args, hipStream_t st) {
   } else if (mode == kFwd) launch_mode<kFwd, true>(p, g, st);
   else if (mode == kDgrad && p.scale_dword) launch_mode<kDgrad, true>(p, g, st);
   else if (mode == kDgrad) launch_mode<kDgrad, false>(p, g, st);
-  else if (p.fp4 && p.ldsa % 4 == 0 && p.ldsb % 4 == 0)
-    // E2M1 with scale rows of aligned dwords: three planes straight into LDS
-    hipLaunchKernelGGL((mx_grouped_gemm_kernel<kWgrad, kFeedFast, true, true>), g, dim3(NT), 0, st, p);
-  else if (!p.fp4 && p.feed == kFeedPrecise && p.ldsa % 4 == 0 && p.ldsb % 4 == 0)
-    // scale rows of aligned dwords (a row pitch that is a multiple of 128): direct-to-LDS scale loads.
-    // The fast feed keeps the register path: its loop is bound by LDS reads, and the second plane
-    // measured slower there.
+  else if (!p.fp4 && p.ldsa % 4 == 0 && p.ldsb % 4 == 0 && p.feed == kFeedPrecise)
+    // E4M3 scale rows of aligned dwords (a row pitch that is a multiple of 128): direct-to-LDS scale
+    // loads from an aligned-down start
     hipLaunchKernelGGL((mx_grouped_gemm_kernel<kWgrad, kFeedPrecise, true>), g, dim3(NT), 0, st, p);
+  else if (!p.fp4 && p.ldsa % 4 == 0 && p.ldsb % 4 == 0)
+    hipLaunchKernelGGL((mx_grouped_gemm_kernel<kWgrad, kFeedFast, true>), g, dim3(NT), 0, st, p);
   else launch_mode<kWgrad, false>(p, g, st);
   return hipGetLastError();
 }

@@ -118,9 +118,9 @@ def test_gemms_ragged_groups():
 
 
 def test_wgrad_scale_rows_both_paths():
-    """MXFP4 weight gradient with its scale rows staged through registers (ld / 32 not a multiple of 4)
-    and straight into LDS as up to three aligned word planes (ld a multiple of 128): experts start at
-    blocks of every residue mod 4, with stages of 1 to 8 valid blocks, some needing the third plane."""
+    """MXFP4 weight gradient at a scale pitch of unaligned rows (ld / 32 not a multiple of 4) and at the
+    recommended pitch (aligned rows): experts start at blocks of every residue mod 4, with stages of 1
+    to 8 valid blocks."""
     m = require_gpu()
     rng = np.random.default_rng(43)
     sizes = [0, 70, 300, 40, 128, 200, 5, 150, 33, 180]
