@@ -117,9 +117,10 @@ def test_ragged_groups_long_contractions():
 
 def test_wgrad_scale_rows_both_paths():
     """The weight gradient reads its scale rows through registers (row pitch not a multiple of 128) or
-    straight into LDS as two aligned word planes recombined by the expert's first block mod 4 (pitch a
-    multiple of 128).  Experts start at blocks of every residue mod 4, end in partial stages, and some
-    stages' scale bytes cross into the second word; both paths must match the oracle."""
+    straight into LDS as aligned words from the aligned-down block before the expert's first (pitch a
+    multiple of 128; the leading blocks are not loaded and must add nothing).  Experts start at blocks
+    of every residue mod 4 and end in partial stages, some in the stage they start in; both paths must
+    match the oracle."""
     m = require_gpu()
     rng = np.random.default_rng(39)
     # 32-blocks per expert 0, 3, 2, 4, 7, 1, 5, 2, 6: first blocks 0, 0, 3, 5, 9, 16, 17, 22, 24
@@ -137,7 +138,7 @@ def test_wgrad_scale_rows_both_paths():
         for dt in ("f32", "bf16"):
             dw = m.mx_grouped_gemm_wgrad(qdyT, sdyT, qxT, sxT, offs_d, L.M, dt)
             print("wgrad ld", ld, dt, _check(_gpu_out(dw), ref, bnd, dt, f"wgrad ld={ld} {dt}"))
-        # the full-rate FP8 feed (register path at both pitches; its own tolerance)
+        # the full-rate FP8 feed (the same two scale paths; its own tolerance)
         dw = m.mx_grouped_gemm_wgrad(qdyT, sdyT, qxT, sxT, offs_d, L.M, "f32", fast=True)
         print("wgrad fast ld", ld, _check(_gpu_out(dw), ref, bnd, "f32", f"fast wgrad ld={ld}", rel=FAST_REL))
 
