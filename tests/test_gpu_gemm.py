@@ -123,8 +123,10 @@ def test_wgrad_scale_rows_both_paths():
     match the oracle."""
     m = require_gpu()
     rng = np.random.default_rng(39)
-    # 32-blocks per expert 0, 3, 2, 4, 7, 1, 5, 2, 6: first blocks 0, 0, 3, 5, 9, 16, 17, 22, 24
-    sizes = [0, 70, 40, 128, 200, 5, 150, 33, 180]
+    # 32-blocks per expert 0, 3, 2, 4, 7, 1, 5, 2, 6, 1, 1, 3: first blocks 0, 0, 3, 5, 9, 16, 17, 22,
+    # 24, 30, 31, 32.  The one-block experts at 30 and 31 each fill one stage's block 2 or 3 of 4 at the
+    # aligned pitch: the first has leading and trailing blocks outside it, the second leading ones.
+    sizes = [0, 70, 40, 128, 200, 5, 150, 33, 180, 20, 32, 90]
     L = _rand_layer(rng, sizes, 256, 384, outliers=0.002)
     offs_d = dev(L.offs)
     x, dy = dev(L.x), dev(L.dy)
