@@ -26,13 +26,15 @@ docstring of the function that applies them.  Element and scale encodings
 follow the OCP Microscaling Formats (MX) v1.0 specification (E4M3 "FN":
 bias 7, max 448, no infinities; E8M0: bias 127, 0xFF = NaN).
 
-Parity pins: every function is checked against closed forms, a library
-routine (torch's CPU float8 cast), brute force or invariants in
-``tests/test_oracle_*.py``.  Nothing here is "parity unpinned".
+Parity pins: every exported function is checked against closed forms, a
+library routine (torch's CPU float8 cast and float32 division), brute force,
+dense products of the dequantised operands or invariants in
+``tests/test_oracle_*.py``; the scale rule ``mx_block_exponent`` is pinned
+through the quantisers' exhaustive bf16 sweeps.
 """
 from .codecs import (E2M1_MAX, e2m1_decode, e2m1_encode, e2m1_encode_bruteforce, fp4_pack, fp4_unpack,
                      E4M3_MAX, bf16_bits_to_f64, e4m3_decode, e4m3_encode,
-                     e4m3_encode_bruteforce, e8m0_decode, f32_round)
+                     e4m3_encode_bruteforce, e8m0_decode)
 from .mx import (mx_block_exponent, mx_colwise_ld_min, mx_dequantize,
                  mx_quantize_colwise, mx_quantize_rowwise, mx_group_columns,
                  mx_gather_rows, mx_quantize_dual, mxfp4_quantize_rowwise,
@@ -41,15 +43,15 @@ from .blockwise import (bw_quantize_act_1x128, bw_quantize_weight_128x128,
                         bw_dequantize_act, bw_dequantize_weight, bw_colwise_ld_min,
                         bw_group_columns, bw_quantize_colwise_128, pow2_scale)
 from .gemm import (mx_gemm_fwd, mx_gemm_dgrad, mx_gemm_wgrad, bw_gemm_fwd,
-                   bw_gemm_dgrad, bw_gemm_wgrad, mxfp4_gemm_fwd, mxfp4_gemm_dgrad, mxfp4_gemm_wgrad, gemm_tolerance, check_gemm, bf16_round_f32)
+                   bw_gemm_dgrad, bw_gemm_wgrad, mxfp4_gemm_fwd, mxfp4_gemm_dgrad, mxfp4_gemm_wgrad, gemm_tolerance, check_gemm)
 
 __all__ = [
     "E4M3_MAX", "bf16_bits_to_f64", "e4m3_decode", "e4m3_encode",
-    "e4m3_encode_bruteforce", "e8m0_decode", "f32_round",
+    "e4m3_encode_bruteforce", "e8m0_decode",
     "mx_block_exponent", "mx_colwise_ld_min", "mx_dequantize",
     "mx_quantize_colwise", "mx_quantize_rowwise", "mx_group_columns",
     "bw_quantize_act_1x128", "bw_quantize_weight_128x128", "pow2_scale",
     "bw_dequantize_act", "bw_dequantize_weight",
     "mx_gemm_fwd", "mx_gemm_dgrad", "mx_gemm_wgrad", "bw_gemm_fwd",
-    "bw_gemm_dgrad", "gemm_tolerance", "check_gemm", "bf16_round_f32",
+    "bw_gemm_dgrad", "gemm_tolerance", "check_gemm",
 ]

@@ -19,11 +19,6 @@ def bf16_bits_to_f64(bits) -> np.ndarray:
     return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
-def f32_round(x) -> np.ndarray:
-    """Round to the nearest float32 (ties to even) and return it as float64."""
-    return np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float64)
-
-
 def e4m3_decode(codes) -> np.ndarray:
     """Value of E4M3-FN codes.
 

@@ -274,9 +274,3 @@ def check_gemm(got, ref, bound, out_dtype: str = "f32", rel: float = REL_TOL):
     r = float(ratio.reshape(-1)[worst]) if ratio.size else 0.0
     return bool(r <= 1.0), r, worst
 
-
-def bf16_round_f32(x) -> np.ndarray:
-    """float32 -> bfloat16 (nearest even), returned as float64 values."""
-    u = np.asarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
-    return r.astype(np.uint32).view(np.float32).astype(np.float64)

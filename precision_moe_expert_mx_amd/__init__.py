@@ -15,7 +15,7 @@ import os
 from typing import Optional, Tuple
 
 __all__ = [
-    "LIB_PATH", "MxMoeError", "lib", "abi_version", "FEED_FP8",
+    "LIB_PATH", "MxMoeError", "lib", "abi_version",
     "mx_colwise_ld_min", "mxmoe_pitch", "mx_colwise_ld", "mxfp4_colwise_ld",
     "mx_quantize_rowwise", "mx_quantize_colwise", "mx_quantize_dual",
     "mx_grouped_gemm_fwd", "mx_grouped_gemm_dgrad", "mx_grouped_gemm_wgrad", "mx_grouped_gemm_fwd_swiglu",
@@ -30,7 +30,6 @@ __all__ = [
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmxmoe.so")
 
 MXMOE_F32, MXMOE_BF16 = 0, 1
-FEED_FP8 = 0x100          # OR-ed into a GEMM's output dtype: full-rate FP8 MFMA feed
 _STATUS = {0: "OK", 1: "ERR_NULL", 2: "ERR_SHAPE", 3: "ERR_ALIGN", 4: "ERR_DTYPE", 5: "ERR_OFFSETS",
            6: "ERR_HIP", 7: "ERR_UNSUPPORTED"}
 
@@ -71,6 +70,10 @@ _SIGS = {
                                                 _p]),
     "mxmoe_check_offsets": (ctypes.c_int, [_p, _i32, _i64, _p]),
 }
+# the full-rate FP8 operand feed: the same arguments as the precise entry points
+for _n in ("mx_grouped_gemm_fwd", "mx_grouped_gemm_dgrad", "mx_grouped_gemm_wgrad", "fp8bw_grouped_gemm_fwd",
+           "fp8bw_grouped_gemm_dgrad", "fp8bw_grouped_gemm_wgrad"):
+    _SIGS[_n + "_fp8feed"] = _SIGS[_n]
 EXPORTED_SYMBOLS = tuple(_SIGS)
 
 
@@ -166,14 +169,23 @@ def _empty(shape, dtype, like):
     return _torch().empty(shape, dtype=dtype, device=like.device)
 
 
-def _out_dtype(dt: str, fast: bool = False):
+def _out_dtype(dt: str):
     torch = _torch()
-    flag = FEED_FP8 if fast else 0
     if dt == "f32":
-        return torch.float32, MXMOE_F32 | flag
+        return torch.float32, MXMOE_F32
     if dt == "bf16":
-        return torch.bfloat16, MXMOE_BF16 | flag
+        return torch.bfloat16, MXMOE_BF16
     raise ValueError(dt)
+
+
+def _gemm(name: str, fast: bool):
+    """The entry point of a GEMM: the precise feed, or its full-rate FP8 feed (`name`_fp8feed)."""
+    return (name + "_fp8feed" if fast else name), getattr(lib(), name + "_fp8feed" if fast else name)
+
+
+def _call(entry, *args):
+    name, f = entry
+    return name, f(*args)
 
 
 # ---------------------------------------------------------------- MX quantisers
@@ -232,9 +244,9 @@ def mx_grouped_gemm_fwd(qx, sx, qw, sw, offs, N: int, out_dtype: str = "f32", y=
     """Y [M, N] = per-expert X_g W_g^T from row-wise MX operands (qw: [G*N, K])."""
     M, K = qx.shape
     G = offs.numel() - 1
-    tdt, cdt = _out_dtype(out_dtype, fast)
+    tdt, cdt = _out_dtype(out_dtype)
     y = _empty((M, N), tdt, qx) if y is None else y
-    _check("mx_grouped_gemm_fwd", lib().mx_grouped_gemm_fwd(_ptr(qx), _ptr(sx), _ptr(qw), _ptr(sw), _ptr(offs), G, M,
+    _check(*_call(_gemm("mx_grouped_gemm_fwd", fast), _ptr(qx), _ptr(sx), _ptr(qw), _ptr(sw), _ptr(offs), G, M,
                                                             N, K, _ptr(y), cdt, _stream_handle(stream)))
     return y
 
@@ -264,9 +276,9 @@ def mx_grouped_gemm_dgrad(qdy, sdy, qwT, swT, offs, K: int, out_dtype: str = "f3
     M, N = qdy.shape
     G = offs.numel() - 1
     ldw = qwT.shape[1]
-    tdt, cdt = _out_dtype(out_dtype, fast)
+    tdt, cdt = _out_dtype(out_dtype)
     dx = _empty((M, K), tdt, qdy) if dx is None else dx
-    _check("mx_grouped_gemm_dgrad", lib().mx_grouped_gemm_dgrad(_ptr(qdy), _ptr(sdy), _ptr(qwT), _ptr(swT), ldw,
+    _check(*_call(_gemm("mx_grouped_gemm_dgrad", fast), _ptr(qdy), _ptr(sdy), _ptr(qwT), _ptr(swT), ldw,
                                                                 _ptr(offs), G, M, N, K, _ptr(dx), cdt,
                                                                 _stream_handle(stream)))
     return dx
@@ -277,9 +289,9 @@ def mx_grouped_gemm_wgrad(qdyT, sdyT, qxT, sxT, offs, M: int, out_dtype: str = "
     N, ld = qdyT.shape
     K = qxT.shape[0]
     G = offs.numel() - 1
-    tdt, cdt = _out_dtype(out_dtype, fast)
+    tdt, cdt = _out_dtype(out_dtype)
     dw = _empty((G, N, K), tdt, qdyT) if dw is None else dw
-    _check("mx_grouped_gemm_wgrad", lib().mx_grouped_gemm_wgrad(_ptr(qdyT), _ptr(sdyT), _ptr(qxT), _ptr(sxT), ld,
+    _check(*_call(_gemm("mx_grouped_gemm_wgrad", fast), _ptr(qdyT), _ptr(sdyT), _ptr(qxT), _ptr(sxT), ld,
                                                                 _ptr(offs), G, M, N, K, _ptr(dw), cdt,
                                                                 _stream_handle(stream)))
     return dw
@@ -383,9 +395,9 @@ def fp8bw_quantize_weight_128x128(w, q=None, s=None, qT=None, transposed: bool =
 def fp8bw_grouped_gemm_fwd(qx, sx, qw, sw, offs, N: int, out_dtype: str = "f32", y=None, stream=None, fast: bool = False):
     M, K = qx.shape
     G = offs.numel() - 1
-    tdt, cdt = _out_dtype(out_dtype, fast)
+    tdt, cdt = _out_dtype(out_dtype)
     y = _empty((M, N), tdt, qx) if y is None else y
-    _check("fp8bw_grouped_gemm_fwd", lib().fp8bw_grouped_gemm_fwd(_ptr(qx), _ptr(sx), _ptr(qw), _ptr(sw), _ptr(offs),
+    _check(*_call(_gemm("fp8bw_grouped_gemm_fwd", fast), _ptr(qx), _ptr(sx), _ptr(qw), _ptr(sw), _ptr(offs),
                                                                   G, M, N, K, _ptr(y), cdt, _stream_handle(stream)))
     return y
 
@@ -395,9 +407,9 @@ def fp8bw_grouped_gemm_dgrad(qdy, sdy, qwT, sw, offs, K: int, out_dtype: str = "
     """dX [M, K] from blockwise dY (1x128 along N) and the transposed weight copy qwT [K, G*N]."""
     M, N = qdy.shape
     G = offs.numel() - 1
-    tdt, cdt = _out_dtype(out_dtype, fast)
+    tdt, cdt = _out_dtype(out_dtype)
     dx = _empty((M, K), tdt, qdy) if dx is None else dx
-    _check("fp8bw_grouped_gemm_dgrad", lib().fp8bw_grouped_gemm_dgrad(_ptr(qdy), _ptr(sdy), _ptr(qwT), _ptr(sw),
+    _check(*_call(_gemm("fp8bw_grouped_gemm_dgrad", fast), _ptr(qdy), _ptr(sdy), _ptr(qwT), _ptr(sw),
                                                                       _ptr(offs), G, M, N, K, _ptr(dx), cdt,
                                                                       _stream_handle(stream)))
     return dx
@@ -432,9 +444,9 @@ def fp8bw_grouped_gemm_wgrad(qdyT, sdyT, qxT, sxT, offs, M: int, out_dtype: str 
     N, ld = qdyT.shape
     K = qxT.shape[0]
     G = offs.numel() - 1
-    tdt, cdt = _out_dtype(out_dtype, fast)
+    tdt, cdt = _out_dtype(out_dtype)
     dw = _empty((G, N, K), tdt, qdyT) if dw is None else dw
-    _check("fp8bw_grouped_gemm_wgrad", lib().fp8bw_grouped_gemm_wgrad(_ptr(qdyT), _ptr(sdyT), _ptr(qxT), _ptr(sxT), ld,
+    _check(*_call(_gemm("fp8bw_grouped_gemm_wgrad", fast), _ptr(qdyT), _ptr(sdyT), _ptr(qxT), _ptr(sxT), ld,
                                                                       _ptr(offs), G, M, N, K, _ptr(dw), cdt,
                                                                       _stream_handle(stream)))
     return dw

@@ -70,8 +70,7 @@ mxmoe_status check_gemm_common(const char* fn, const int32_t* offs, int32_t G, i
   if (N % 128 || K % 128) return fail(MXMOE_ERR_SHAPE, "%s: N and K must be multiples of 128 (N=%lld K=%lld)", fn,
                                       (long long)N, (long long)K);
   if (M > INT32_MAX) return fail(MXMOE_ERR_SHAPE, "%s: M too large", fn);
-  const int base = dt & ~MXMOE_FEED_FP8;
-  if (base != MXMOE_F32 && base != MXMOE_BF16) return fail(MXMOE_ERR_DTYPE, "%s: unknown output dtype %d", fn, dt);
+  if (dt != MXMOE_F32 && dt != MXMOE_BF16) return fail(MXMOE_ERR_DTYPE, "%s: unknown output dtype %d", fn, dt);
   if (!offs) return fail(MXMOE_ERR_NULL, "%s: offs is NULL", fn);
   if (!out) return fail(MXMOE_ERR_NULL, "%s: output is NULL", fn);
   if (!aligned(offs, 4)) return fail(MXMOE_ERR_ALIGN, "%s: offs not 4-byte aligned", fn);
@@ -196,7 +195,8 @@ static mxmoe_status check_strides(const char* fn, const GemmArgs& p, int64_t b_r
 
 static mxmoe_status mx_gemm_common(int mode, const char* fn, const uint8_t* a, const uint8_t* sa, const uint8_t* b,
                                    const uint8_t* sb, int64_t ldb_cols, const int32_t* offs, int32_t G, int64_t M,
-                                   int64_t N, int64_t K, void* out, int dt, void* stream, bool fp4 = false) {
+                                   int64_t N, int64_t K, void* out, int dt, void* stream, int feed,
+                                   bool fp4 = false) {
   TRY(check_gemm_common(fn, offs, G, M, N, K, out, dt));
   if (fp4 && (N % 256 || K % 256))
     return fail(MXMOE_ERR_SHAPE, "%s: MXFP4 needs N and K multiples of 256 (N=%lld K=%lld)", fn, (long long)N,
@@ -209,12 +209,11 @@ static mxmoe_status mx_gemm_common(int mode, const char* fn, const uint8_t* a, c
   memset(&p, 0, sizeof p);
   p.a = a; p.sa = sa; p.b = b; p.sb = sb; p.offs = offs; p.out = out;
   p.M = M; p.N = N; p.K = K; p.G = G;
-  p.out_bf16 = (dt & ~MXMOE_FEED_FP8) == MXMOE_BF16;
-  p.feed = (dt & MXMOE_FEED_FP8) ? kFeedFast : kFeedPrecise;
+  p.out_bf16 = dt == MXMOE_BF16;
+  p.feed = feed;
   // operand leading dimensions in bytes (E2M1: two elements per byte), scale ones in blocks
   const int epb = fp4 ? 2 : 1;
   p.fp4 = fp4;
-  if (fp4) p.feed = kFeedFast;
   if (mode == kFwd) {
     p.lda = K / epb; p.ldsa = K / 32; p.ldb = K / epb; p.ldsb = K / 32;
   } else if (mode == kDgrad) {
@@ -231,7 +230,15 @@ static mxmoe_status mx_gemm_common(int mode, const char* fn, const uint8_t* a, c
 mxmoe_status mx_grouped_gemm_fwd(const uint8_t* qx, const uint8_t* sx, const uint8_t* qw, const uint8_t* sw,
                                  const int32_t* offs, int32_t G, int64_t M, int64_t N, int64_t K, void* y,
                                  mxmoe_dtype ydt, void* stream) {
-  return mx_gemm_common(kFwd, "mx_grouped_gemm_fwd", qx, sx, qw, sw, 0, offs, G, M, N, K, y, (int)ydt, stream);
+  return mx_gemm_common(kFwd, "mx_grouped_gemm_fwd", qx, sx, qw, sw, 0, offs, G, M, N, K, y, (int)ydt, stream,
+                        kFeedPrecise);
+}
+
+mxmoe_status mx_grouped_gemm_fwd_fp8feed(const uint8_t* qx, const uint8_t* sx, const uint8_t* qw, const uint8_t* sw,
+                                         const int32_t* offs, int32_t G, int64_t M, int64_t N, int64_t K, void* y,
+                                         mxmoe_dtype ydt, void* stream) {
+  return mx_gemm_common(kFwd, "mx_grouped_gemm_fwd_fp8feed", qx, sx, qw, sw, 0, offs, G, M, N, K, y, (int)ydt,
+                        stream, kFeedFast);
 }
 
 mxmoe_status mx_grouped_gemm_fwd_swiglu(const uint8_t* qx, const uint8_t* sx, const uint8_t* qw, const uint8_t* sw,
@@ -261,24 +268,50 @@ mxmoe_status mx_grouped_gemm_fwd_swiglu(const uint8_t* qx, const uint8_t* sx, co
   return launched(launch_mx_gemm(kFwd, p, (hipStream_t)stream), fn);
 }
 
-mxmoe_status mx_grouped_gemm_dgrad(const uint8_t* qdy, const uint8_t* sdy, const uint8_t* qwT, const uint8_t* swT,
-                                   int64_t ldw, const int32_t* offs, int32_t G, int64_t M, int64_t N, int64_t K,
-                                   void* dx, mxmoe_dtype dxdt, void* stream) {
-  const char* fn = "mx_grouped_gemm_dgrad";
+static mxmoe_status mx_dgrad_impl(const char* fn, int feed, const uint8_t* qdy, const uint8_t* sdy,
+                                  const uint8_t* qwT, const uint8_t* swT, int64_t ldw, const int32_t* offs, int32_t G,
+                                  int64_t M, int64_t N, int64_t K, void* dx, mxmoe_dtype dxdt, void* stream) {
   if (ldw % 32 || ldw < (int64_t)G * N)
     return fail(MXMOE_ERR_SHAPE, "%s: ldw=%lld must be a multiple of 32 and >= G*N=%lld", fn, (long long)ldw,
                 (long long)G * N);
-  return mx_gemm_common(kDgrad, fn, qdy, sdy, qwT, swT, ldw, offs, G, M, N, K, dx, (int)dxdt, stream);
+  return mx_gemm_common(kDgrad, fn, qdy, sdy, qwT, swT, ldw, offs, G, M, N, K, dx, (int)dxdt, stream, feed);
+}
+
+mxmoe_status mx_grouped_gemm_dgrad(const uint8_t* qdy, const uint8_t* sdy, const uint8_t* qwT, const uint8_t* swT,
+                                   int64_t ldw, const int32_t* offs, int32_t G, int64_t M, int64_t N, int64_t K,
+                                   void* dx, mxmoe_dtype dxdt, void* stream) {
+  return mx_dgrad_impl("mx_grouped_gemm_dgrad", kFeedPrecise, qdy, sdy, qwT, swT, ldw, offs, G, M, N, K, dx, dxdt,
+                       stream);
+}
+
+mxmoe_status mx_grouped_gemm_dgrad_fp8feed(const uint8_t* qdy, const uint8_t* sdy, const uint8_t* qwT,
+                                           const uint8_t* swT, int64_t ldw, const int32_t* offs, int32_t G, int64_t M,
+                                           int64_t N, int64_t K, void* dx, mxmoe_dtype dxdt, void* stream) {
+  return mx_dgrad_impl("mx_grouped_gemm_dgrad_fp8feed", kFeedFast, qdy, sdy, qwT, swT, ldw, offs, G, M, N, K, dx,
+                       dxdt, stream);
+}
+
+static mxmoe_status mx_wgrad_impl(const char* fn, int feed, const uint8_t* qdyT, const uint8_t* sdyT,
+                                  const uint8_t* qxT, const uint8_t* sxT, int64_t ld, const int32_t* offs, int32_t G,
+                                  int64_t M, int64_t N, int64_t K, void* dw, mxmoe_dtype dwdt, void* stream) {
+  if (G >= 1 && M >= 0 && (ld % 32 || ld < mx_colwise_ld_min(M, G)))
+    return fail(MXMOE_ERR_SHAPE, "%s: ld=%lld must be a multiple of 32 and >= mx_colwise_ld_min(M, G)=%lld", fn,
+                (long long)ld, (long long)mx_colwise_ld_min(M, G));
+  return mx_gemm_common(kWgrad, fn, qdyT, sdyT, qxT, sxT, ld, offs, G, M, N, K, dw, (int)dwdt, stream, feed);
 }
 
 mxmoe_status mx_grouped_gemm_wgrad(const uint8_t* qdyT, const uint8_t* sdyT, const uint8_t* qxT, const uint8_t* sxT,
                                    int64_t ld, const int32_t* offs, int32_t G, int64_t M, int64_t N, int64_t K,
                                    void* dw, mxmoe_dtype dwdt, void* stream) {
-  const char* fn = "mx_grouped_gemm_wgrad";
-  if (G >= 1 && M >= 0 && (ld % 32 || ld < mx_colwise_ld_min(M, G)))
-    return fail(MXMOE_ERR_SHAPE, "%s: ld=%lld must be a multiple of 32 and >= mx_colwise_ld_min(M, G)=%lld", fn,
-                (long long)ld, (long long)mx_colwise_ld_min(M, G));
-  return mx_gemm_common(kWgrad, fn, qdyT, sdyT, qxT, sxT, ld, offs, G, M, N, K, dw, (int)dwdt, stream);
+  return mx_wgrad_impl("mx_grouped_gemm_wgrad", kFeedPrecise, qdyT, sdyT, qxT, sxT, ld, offs, G, M, N, K, dw, dwdt,
+                       stream);
+}
+
+mxmoe_status mx_grouped_gemm_wgrad_fp8feed(const uint8_t* qdyT, const uint8_t* sdyT, const uint8_t* qxT,
+                                           const uint8_t* sxT, int64_t ld, const int32_t* offs, int32_t G, int64_t M,
+                                           int64_t N, int64_t K, void* dw, mxmoe_dtype dwdt, void* stream) {
+  return mx_wgrad_impl("mx_grouped_gemm_wgrad_fp8feed", kFeedFast, qdyT, sdyT, qxT, sxT, ld, offs, G, M, N, K, dw,
+                       dwdt, stream);
 }
 
 mxmoe_status mxfp4_quantize_rowwise(const void* x, int64_t R, int64_t C, uint8_t* q, uint8_t* s, void* stream) {
@@ -316,7 +349,7 @@ mxmoe_status mxfp4_grouped_gemm_fwd(const uint8_t* qx, const uint8_t* sx, const 
                                     const int32_t* offs, int32_t G, int64_t M, int64_t N, int64_t K, void* y,
                                     mxmoe_dtype ydt, void* stream) {
   return mx_gemm_common(kFwd, "mxfp4_grouped_gemm_fwd", qx, sx, qw, sw, 0, offs, G, M, N, K, y, (int)ydt, stream,
-                        true);
+                        kFeedFast, true);
 }
 
 mxmoe_status mxfp4_grouped_gemm_dgrad(const uint8_t* qdy, const uint8_t* sdy, const uint8_t* qwT, const uint8_t* swT,
@@ -326,7 +359,8 @@ mxmoe_status mxfp4_grouped_gemm_dgrad(const uint8_t* qdy, const uint8_t* sdy, co
   if (ldw % 32 || ldw < (int64_t)G * N)
     return fail(MXMOE_ERR_SHAPE, "%s: ldw=%lld must be a multiple of 32 and >= G*N=%lld", fn, (long long)ldw,
                 (long long)G * N);
-  return mx_gemm_common(kDgrad, fn, qdy, sdy, qwT, swT, ldw, offs, G, M, N, K, dx, (int)dxdt, stream, true);
+  return mx_gemm_common(kDgrad, fn, qdy, sdy, qwT, swT, ldw, offs, G, M, N, K, dx, (int)dxdt, stream, kFeedFast,
+                        true);
 }
 
 mxmoe_status mxfp4_grouped_gemm_wgrad(const uint8_t* qdyT, const uint8_t* sdyT, const uint8_t* qxT,
@@ -336,7 +370,8 @@ mxmoe_status mxfp4_grouped_gemm_wgrad(const uint8_t* qdyT, const uint8_t* sdyT, 
   if (G >= 1 && M >= 0 && (ld % 32 || ld < mx_colwise_ld_min(M, G)))
     return fail(MXMOE_ERR_SHAPE, "%s: ld=%lld must be a multiple of 32 and >= mx_colwise_ld_min(M, G)=%lld", fn,
                 (long long)ld, (long long)mx_colwise_ld_min(M, G));
-  return mx_gemm_common(kWgrad, fn, qdyT, sdyT, qxT, sxT, ld, offs, G, M, N, K, dw, (int)dwdt, stream, true);
+  return mx_gemm_common(kWgrad, fn, qdyT, sdyT, qxT, sxT, ld, offs, G, M, N, K, dw, (int)dwdt, stream, kFeedFast,
+                        true);
 }
 
 static mxmoe_status bw_act_impl(const char* fn, const void* x, int64_t R, int64_t C, uint8_t* q, float* s, bool pow2,
@@ -415,9 +450,9 @@ mxmoe_status fp8bw_quantize_colwise_128_pow2(const void* x, int64_t R, int64_t C
   return bw_colwise_impl("fp8bw_quantize_colwise_128_pow2", x, R, C, offs, G, qT, sT, ld, true, stream);
 }
 
-static mxmoe_status bw_gemm_common(int mode, const char* fn, const uint8_t* a, const float* sa, const uint8_t* b,
-                                   const float* sb, const int32_t* offs, int32_t G, int64_t M, int64_t N, int64_t K,
-                                   void* out, int dt, void* stream, int64_t ld = 0) {
+static mxmoe_status bw_gemm_common(int mode, const char* fn, int feed, const uint8_t* a, const float* sa,
+                                   const uint8_t* b, const float* sb, const int32_t* offs, int32_t G, int64_t M,
+                                   int64_t N, int64_t K, void* out, int dt, void* stream, int64_t ld = 0) {
   TRY(check_gemm_common(fn, offs, G, M, N, K, out, dt));
   TRY(check_ptr(fn, "A operand", a, 16));
   TRY(check_ptr(fn, "A scales", sa, 4));
@@ -427,8 +462,8 @@ static mxmoe_status bw_gemm_common(int mode, const char* fn, const uint8_t* a, c
   memset(&p, 0, sizeof p);
   p.a = a; p.sa = sa; p.b = b; p.sb = sb; p.offs = offs; p.out = out;
   p.M = M; p.N = N; p.K = K; p.G = G;
-  p.out_bf16 = (dt & ~MXMOE_FEED_FP8) == MXMOE_BF16;
-  p.feed = (dt & MXMOE_FEED_FP8) ? kFeedFast : kFeedPrecise;
+  p.out_bf16 = dt == MXMOE_BF16;
+  p.feed = feed;
   if (mode == kFwd) {
     p.lda = K; p.ldsa = K / 128; p.ldb = K; p.ldsb = K / 128;
   } else if (mode == kDgrad) {
@@ -446,24 +481,52 @@ static mxmoe_status bw_gemm_common(int mode, const char* fn, const uint8_t* a, c
 mxmoe_status fp8bw_grouped_gemm_fwd(const uint8_t* qx, const float* sx, const uint8_t* qw, const float* sw,
                                     const int32_t* offs, int32_t G, int64_t M, int64_t N, int64_t K, void* y,
                                     mxmoe_dtype ydt, void* stream) {
-  return bw_gemm_common(kFwd, "fp8bw_grouped_gemm_fwd", qx, sx, qw, sw, offs, G, M, N, K, y, (int)ydt, stream);
+  return bw_gemm_common(kFwd, "fp8bw_grouped_gemm_fwd", kFeedPrecise, qx, sx, qw, sw, offs, G, M, N, K, y, (int)ydt,
+                        stream);
+}
+
+mxmoe_status fp8bw_grouped_gemm_fwd_fp8feed(const uint8_t* qx, const float* sx, const uint8_t* qw, const float* sw,
+                                            const int32_t* offs, int32_t G, int64_t M, int64_t N, int64_t K, void* y,
+                                            mxmoe_dtype ydt, void* stream) {
+  return bw_gemm_common(kFwd, "fp8bw_grouped_gemm_fwd_fp8feed", kFeedFast, qx, sx, qw, sw, offs, G, M, N, K, y,
+                        (int)ydt, stream);
+}
+
+static mxmoe_status bw_wgrad_impl(const char* fn, int feed, const uint8_t* qdyT, const float* sdyT, const uint8_t* qxT,
+                                  const float* sxT, int64_t ld, const int32_t* offs, int32_t G, int64_t M, int64_t N,
+                                  int64_t K, void* dw, mxmoe_dtype dwdt, void* stream) {
+  if (G >= 1 && M >= 0 && (ld % 128 || ld < fp8bw_colwise_ld_min(M, G)))
+    return fail(MXMOE_ERR_SHAPE, "%s: ld=%lld must be a multiple of 128 and >= fp8bw_colwise_ld_min(M, G)=%lld", fn,
+                (long long)ld, (long long)fp8bw_colwise_ld_min(M, G));
+  return bw_gemm_common(kWgrad, fn, feed, qdyT, sdyT, qxT, sxT, offs, G, M, N, K, dw, (int)dwdt, stream, ld);
 }
 
 mxmoe_status fp8bw_grouped_gemm_wgrad(const uint8_t* qdyT, const float* sdyT, const uint8_t* qxT, const float* sxT,
                                       int64_t ld, const int32_t* offs, int32_t G, int64_t M, int64_t N, int64_t K,
                                       void* dw, mxmoe_dtype dwdt, void* stream) {
-  const char* fn = "fp8bw_grouped_gemm_wgrad";
-  if (G >= 1 && M >= 0 && (ld % 128 || ld < fp8bw_colwise_ld_min(M, G)))
-    return fail(MXMOE_ERR_SHAPE, "%s: ld=%lld must be a multiple of 128 and >= fp8bw_colwise_ld_min(M, G)=%lld", fn,
-                (long long)ld, (long long)fp8bw_colwise_ld_min(M, G));
-  return bw_gemm_common(kWgrad, fn, qdyT, sdyT, qxT, sxT, offs, G, M, N, K, dw, (int)dwdt, stream, ld);
+  return bw_wgrad_impl("fp8bw_grouped_gemm_wgrad", kFeedPrecise, qdyT, sdyT, qxT, sxT, ld, offs, G, M, N, K, dw, dwdt,
+                       stream);
+}
+
+mxmoe_status fp8bw_grouped_gemm_wgrad_fp8feed(const uint8_t* qdyT, const float* sdyT, const uint8_t* qxT,
+                                              const float* sxT, int64_t ld, const int32_t* offs, int32_t G, int64_t M,
+                                              int64_t N, int64_t K, void* dw, mxmoe_dtype dwdt, void* stream) {
+  return bw_wgrad_impl("fp8bw_grouped_gemm_wgrad_fp8feed", kFeedFast, qdyT, sdyT, qxT, sxT, ld, offs, G, M, N, K, dw,
+                       dwdt, stream);
 }
 
 mxmoe_status fp8bw_grouped_gemm_dgrad(const uint8_t* qdy, const float* sdy, const uint8_t* qwT, const float* sw,
                                       const int32_t* offs, int32_t G, int64_t M, int64_t N, int64_t K, void* dx,
                                       mxmoe_dtype dxdt, void* stream) {
-  return bw_gemm_common(kDgrad, "fp8bw_grouped_gemm_dgrad", qdy, sdy, qwT, sw, offs, G, M, N, K, dx, (int)dxdt,
-                        stream);
+  return bw_gemm_common(kDgrad, "fp8bw_grouped_gemm_dgrad", kFeedPrecise, qdy, sdy, qwT, sw, offs, G, M, N, K, dx,
+                        (int)dxdt, stream);
+}
+
+mxmoe_status fp8bw_grouped_gemm_dgrad_fp8feed(const uint8_t* qdy, const float* sdy, const uint8_t* qwT,
+                                              const float* sw, const int32_t* offs, int32_t G, int64_t M, int64_t N,
+                                              int64_t K, void* dx, mxmoe_dtype dxdt, void* stream) {
+  return bw_gemm_common(kDgrad, "fp8bw_grouped_gemm_dgrad_fp8feed", kFeedFast, qdy, sdy, qwT, sw, offs, G, M, N, K,
+                        dx, (int)dxdt, stream);
 }
 
 mxmoe_status mxmoe_check_offsets(const int32_t* offs, int32_t G, int64_t M, void* stream) {

@@ -18,7 +18,7 @@ typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
 // GEMM operand feeds: bf16-widened operands on the bf16 MFMA (fp32-accurate sums), or the
-// full-rate block-scaled FP8 MFMA (sums truncated per 8-element run, see gemm.hip).
+// full-rate block-scaled FP8 MFMA (sums truncated per 8-element run, see gemm_mx.hip).
 enum GemmFeed { kFeedPrecise = 0, kFeedFast = 1 };
 
 // ---- memory and lane helpers ---------------------------------------------------------------------

@@ -1,35 +1,37 @@
-// Dropless grouped GEMM for MoE experts on gfx950 block-scaled FP8 MFMA.
+// Blockwise-FP8 dropless grouped GEMM for MoE experts on gfx950 (the DeepSeek-V3 fine-grained recipe).
 //
-// All experts run in one launch, each on its real number of rows (iitak.ru, "NVIDIA sped up
-// training of mixture-of-experts models on JAX tenfold": no capacity padding, no dropped tokens).
-// The work of every expert is cut into 128x128 output tiles; the launch enumerates the tiles of
-// all experts from the device-resident group offsets, so an expert with no rows contributes no
-// tile (forward / dgrad) and one with a handful of rows contributes one partial tile.
+// aifind.ru, "DeepSeek-V3: a revolutionary high-performance language model with low training cost", section
+// "Low-precision training: FP8 Framework", captions (a) and (b): activations carry an fp32 scale per 1x128
+// tile, weights per 128x128 block, and the FP8 products are summed over each 128-element slice of the
+// contraction before that partial is promoted, i.e. multiplied by its two scales and added to a
+// full-precision accumulator.  All experts run in one launch, each on its real number of rows (iitak.ru,
+// "NVIDIA sped up training of mixture-of-experts models on JAX tenfold": no capacity padding, no dropped
+// tokens): the launch enumerates the 128x128 output tiles of all experts from the device-resident group
+// offsets, so an expert with no rows contributes no tile (forward / dgrad) and one with a handful of rows
+// one partial tile.
 //
-// Generic form computed by one workgroup (tile (mt, nt) of expert g):
-//   out[i, j] = sum_t A[row_a(i), col0_a + t] * B[row_b(j), col0_b + t],   t < L_g
-// with per-32 E8M0 scales (MX) or per-128 fp32 scales (blockwise), where
-//   forward: A = X rows of expert g, B = W_g rows, L = K            (Y = X W^T)
-//   dgrad:   A = dY rows of expert g, B = column-wise W (rows = k, columns gN..gN+N), L = N
-//   wgrad:   A = column-wise dY (rows = n), B = column-wise X (rows = k), both from column c_g,
-//            L = 128 ceil(m_g / 128) (pads are zero); blockwise only: 128-token blocks restarting at
-//            each expert, an fp32 scale per (row, block) on both operands, promoted per block
+// Generic form computed by one workgroup (tile (mt, nt) of expert g), promoted per 128-slice kb:
+//   out[i, j] = sum_kb sA(i, kb) sB(j, kb) sum_{t in kb} A[row_a(i), col0_a + t] * B[row_b(j), col0_b + t]
+// where
+//   forward: A = X rows of expert g, B = W_g rows, sA = the 1x128 tile scale, sB = the 128x128 block scale
+//   dgrad:   A = dY rows of expert g (1x128 tiles along N), B = the transposed weight copy (rows k,
+//            columns gN..gN+N), sB = the forward block scale read transposed
+//   wgrad:   A = column-wise dY (rows n), B = column-wise X (rows k), both from column c_g, 128-token
+//            blocks restarting at each expert with an fp32 scale per (row, block) on both operands
 //
-// Main loop: BK = 128 contraction bytes per step; global -> registers (prefetch of the next step)
-// -> LDS (16-byte chunks XOR-swizzled by row) -> MFMA operands.  Each of the four waves owns a
-// 64x64 quarter of the tile as 4x4 v_mfma_scale_f32_16x16x128_f8f6f4 (fp32 accumulators).
-//
-// MFMA operand layout (measured on gfx950): lane l feeds row/column (l % 16); its 32 operand bytes
-// are contraction elements [16 g, 16 g + 16) and [64 + 16 g, 64 + 16 g + 16) with g = l / 16, i.e.
-// 16-byte chunks g and 4 + g of the 128-byte row; its scale byte is the E8M0 of 32-block g.
+// Main loop: BK = 128 contraction bytes (one promotion slice) per step; global -> registers (prefetch of
+// the next step) -> LDS (16-byte chunks XOR-swizzled by row) -> MFMA operands.  Each of the four waves
+// owns a 64x64 quarter of the tile as 4x4 16x16 fragments, with an fp32 partial and an fp32 accumulator
+// per fragment.
 //
 // Two operand feeds (same tiling, same LDS staging of the FP8 bytes):
-//  * precise (default): each 32-block is widened to bf16 with its E8M0 scale folded in (exact) and
-//    multiplied on v_mfma_f32_16x16x32_bf16, whose sums are fp32-accurate;
-//  * fast (opt-in): v_mfma_scale_f32_16x16x128_f8f6f4 at twice the rate.  Measured on gfx950, it
-//    truncates the products of each run of 8 consecutive operand bytes to a 14-bit window below the
-//    run's largest product, so its error is bounded by about 7 * 2^-13 times the largest product of
-//    each run rather than by fp32 rounding.
+//  * precise (default): each 32-element piece is widened exactly to bf16 and multiplied on
+//    v_mfma_f32_16x16x32_bf16, whose sums are fp32-accurate;
+//  * full-rate FP8: v_mfma_scale_f32_16x16x128_f8f6f4 (unit scales) at twice the rate.  Lane l feeds
+//    row l % 16 with 16-byte chunks g and 4 + g of the 128-byte row (g = l / 16).  Measured on gfx950,
+//    it truncates the products of each run of 8 consecutive operand bytes toward zero below a 2^-13
+//    window of the run's largest product, so its error is bounded by about 7 * 2^-13 times the largest
+//    product of each run rather than by fp32 rounding.
 #include "common.h"
 
 namespace mxmoe {
@@ -43,7 +45,7 @@ struct TileInfo {
   int mt, nt;     // tile coordinates inside the expert
   int64_t row0;   // first global row of A for this expert (forward / dgrad)
   int rows;       // valid rows of this tile (forward / dgrad)
-  int nblk;       // wgrad: number of contraction blocks (32 rows MX, 128 rows blockwise)
+  int nblk;       // wgrad: number of 128-token contraction blocks
   int64_t col0;   // wgrad: first column of the expert in the column-wise layout
   bool valid;
 };
@@ -129,7 +131,7 @@ __device__ TileInfo decode_tile(int mode, int wblk, const GemmArgs& p, int32_t* 
 __device__ __forceinline__ int lds_off(int r, int c) { return r * BK + ((c ^ (r & 7)) << 4); }
 
 // Eight E4M3 bytes -> eight bf16 multiplied by the power of two whose exponent field is that of
-// `scale` (the E8M0 byte shifted into a float's exponent); exact for every product of the GEMMs.
+// `scale` (1.0 here: the fp32 scales are applied at promotion); exact.
 __device__ __forceinline__ v8bf widen8(uint2 w, float scale) {
   const v2bf a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, scale, false);
   const v2bf b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, scale, true);
@@ -138,7 +140,7 @@ __device__ __forceinline__ v8bf widen8(uint2 w, float scale) {
   return v8bf{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
-template <int MODE, bool BW, int FEED>
+template <int MODE, int FEED>
 __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const TileInfo& ti, uint8_t* ldsA, uint8_t* ldsB,
                                           uint32_t* ldsSA, uint32_t* ldsSB) {
   const int tid = threadIdx.x;
@@ -149,7 +151,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const TileInfo& ti,
   // A rows: forward/dgrad -> token rows (clamped to the expert's last row); wgrad -> n rows
   // B rows: forward -> gN + j; dgrad -> k rows of W^c (column offset gN); wgrad -> k rows (col c_g)
   int64_t a_col0 = 0, b_col0 = 0;
-  constexpr int WBLK = BW ? 128 : 32;   // wgrad contraction block
+  constexpr int WBLK = 128;   // wgrad contraction block (128 tokens)
   int64_t L;   // contraction length in bytes (multiple of 128 for forward/dgrad)
   if (MODE == kFwd) L = p.K;
   else if (MODE == kDgrad) L = p.N;
@@ -194,7 +196,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const TileInfo& ti,
     else s_row = (int64_t)ti.nt * BN + s_r;
   }
   const int64_t s_ld = s_is_a ? p.ldsa : p.ldsb;
-  const int64_t s_col0 = (s_is_a ? a_col0 : b_col0) / (BW ? 128 : 32);
+  const int64_t s_col0 = (s_is_a ? a_col0 : b_col0) / 128;
 
   uint4 ra[4], rb[4];
   uint32_t rs = 0;
@@ -208,21 +210,9 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const TileInfo& ti,
       ra[j] = ok ? *(const uint4*)(a_ptr[j] + koff) : make_uint4(0, 0, 0, 0);
       rb[j] = ok ? *(const uint4*)(b_ptr[j] + koff) : make_uint4(0, 0, 0, 0);
     }
-    if (BW) {
-      // A row scales; wgrad also B row scales (forward / dgrad read the B block scale per tile)
-      const float* sp = (const float*)(s_is_a ? p.sa : p.sb);
-      if (s_is_a || MODE == kWgrad) rs = __float_as_uint(sp[s_row * s_ld + s_col0 + ks]);
-    } else {
-      const uint8_t* sp = (const uint8_t*)(s_is_a ? p.sa : p.sb) + s_row * s_ld + s_col0 + (int64_t)ks * 4;
-      uint32_t v = 0;
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        bool ok = true;
-        if (MODE == kWgrad) ok = (int64_t)ks * 4 + b < nblk;
-        if (ok) v |= (uint32_t)sp[b] << (8 * b);
-      }
-      rs = v;
-    }
+    // A row scales; wgrad also B row scales (forward / dgrad read the B block scale per tile)
+    const float* sp = (const float*)(s_is_a ? p.sa : p.sb);
+    if (s_is_a || MODE == kWgrad) rs = __float_as_uint(sp[s_row * s_ld + s_col0 + ks]);
   };
   auto store_step = [&]() {
 #pragma unroll
@@ -232,7 +222,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const TileInfo& ti,
       *(uint4*)(ldsB + lds_off(r, ld_ch)) = rb[j];
     }
     if (s_is_a) ldsSA[s_r] = rs;
-    else if (!BW || MODE == kWgrad) ldsSB[s_r] = rs;
+    else if (MODE == kWgrad) ldsSB[s_r] = rs;
   };
 
   v4f acc[4][4];
@@ -251,7 +241,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const TileInfo& ti,
     // blockwise: fp32 weight-block scale of this step (one per 128x128 block)
     float sbw = 1.f;
     float rsc[4][4], csc[4];
-    if (BW) {
+    {
       const float* sw = (const float*)p.sb;
       if (MODE == kFwd) sbw = sw[(((int64_t)ti.g * p.N + (int64_t)ti.nt * BN) / 128) * p.ldsb + ks];
       else if (MODE == kDgrad) sbw = sw[(((int64_t)ti.g * p.N) / 128 + ks) * p.ldsb + ti.nt];
@@ -267,16 +257,14 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const TileInfo& ti,
     }
 
     if (FEED == kFeedPrecise) {
-      // four bf16 MFMAs of K = 32 per step, one per 32-block: lane group fg supplies bytes
-      // [8 fg, 8 fg + 8) of the block, widened to bf16 with the block's E8M0 scale folded in
-      // (exact), so every product is exact and the MFMA sums them at fp32 precision
+      // four bf16 MFMAs of K = 32 per step: lane group fg supplies bytes [8 fg, 8 fg + 8) of each
+      // 32-element piece, widened exactly to bf16, so every product is exact and the MFMA sums them at
+      // fp32 precision into the slice's partial
       v4f part[4][4];
-      if (BW) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) part[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-      }
+        for (int j = 0; j < 4; ++j) part[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
         v8bf af[4], bfr[4];
@@ -284,38 +272,32 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const TileInfo& ti,
         for (int i = 0; i < 4; ++i) {
           const int r = wm * 64 + i * 16 + fr;
           const uint2 w = *(const uint2*)(ldsA + lds_off(r, 2 * kb + (fg >> 1)) + 8 * (fg & 1));
-          const float sc = BW ? 1.0f : __uint_as_float(((ldsSA[r] >> (8 * kb)) & 0xFFu) << 23);
-          af[i] = widen8(w, sc);
+          af[i] = widen8(w, 1.0f);
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int r = wn * 64 + j * 16 + fr;
           const uint2 w = *(const uint2*)(ldsB + lds_off(r, 2 * kb + (fg >> 1)) + 8 * (fg & 1));
-          const float sc = BW ? 1.0f : __uint_as_float(((ldsSB[r] >> (8 * kb)) & 0xFFu) << 23);
-          bfr[j] = widen8(w, sc);
+          bfr[j] = widen8(w, 1.0f);
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            if (BW) part[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], part[i][j], 0, 0, 0);
-            else acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-          }
-      }
-      if (BW) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
           for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const float f = MODE == kWgrad ? rsc[i][q] * csc[j] : rsc[i][q];
-              acc[i][j][q] = __builtin_fmaf(part[i][j][q], f, acc[i][j][q]);
-            }
+            part[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], part[i][j], 0, 0, 0);
       }
+      // promotion of the slice's partial with its two fp32 scales
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float f = MODE == kWgrad ? rsc[i][q] * csc[j] : rsc[i][q];
+            acc[i][j][q] = __builtin_fmaf(part[i][j][q], f, acc[i][j][q]);
+          }
     } else {
-      // full-rate block-scaled FP8 MFMA, K = 128 per instruction
-      int sa[4], sb[4];
+      // full-rate FP8 MFMA (unit scales), K = 128 per instruction: one unscaled partial per slice
       v8i af[4], bf[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -323,7 +305,6 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const TileInfo& ti,
         v4i lo = *(const v4i*)(ldsA + lds_off(r, fg));
         v4i hi = *(const v4i*)(ldsA + lds_off(r, 4 + fg));
         af[i] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        sa[i] = BW ? 127 : (int)((ldsSA[r] >> (8 * fg)) & 0xFFu);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -331,30 +312,20 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const TileInfo& ti,
         v4i lo = *(const v4i*)(ldsB + lds_off(r, fg));
         v4i hi = *(const v4i*)(ldsB + lds_off(r, 4 + fg));
         bf[i] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        sb[i] = BW ? 127 : (int)((ldsSB[r] >> (8 * fg)) & 0xFFu);
       }
-      if (BW) {
-        // promotion: unscaled partial over this 128-slice, then fp32 FMA with the two scales
+      // promotion: unscaled partial over this 128-slice, then fp32 FMA with the two scales
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const v4f part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[i], bf[j], v4f{0.f, 0.f, 0.f, 0.f},
-                                                                              0, 0, 0, 127, 0, 127);
+        for (int j = 0; j < 4; ++j) {
+          const v4f part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[i], bf[j], v4f{0.f, 0.f, 0.f, 0.f},
+                                                                            0, 0, 0, 127, 0, 127);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const float f = MODE == kWgrad ? rsc[i][q] * csc[j] : rsc[i][q];
-              acc[i][j][q] = __builtin_fmaf(part[q], f, acc[i][j][q]);
-            }
+          for (int q = 0; q < 4; ++q) {
+            const float f = MODE == kWgrad ? rsc[i][q] * csc[j] : rsc[i][q];
+            acc[i][j][q] = __builtin_fmaf(part[q], f, acc[i][j][q]);
           }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[i], bf[j], acc[i][j], 0, 0, 0, sa[i], 0,
-                                                                         sb[j]);
-      }
+        }
     }
     __syncthreads();
   }
@@ -382,7 +353,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const TileInfo& ti,
       }
 }
 
-template <int MODE, bool BW, int FEED>
+template <int MODE, int FEED>
 __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_kernel(GemmArgs p) {
   __shared__ int32_t pre[kMaxGroups + 1];
   __shared__ int64_t rowstart[kMaxGroups + 1];
@@ -390,9 +361,9 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_kernel(GemmArgs p) {
   __shared__ __attribute__((aligned(16))) uint8_t ldsB[BN * BK];
   __shared__ uint32_t ldsSA[BM];
   __shared__ uint32_t ldsSB[BN];
-  const TileInfo ti = decode_tile(MODE, BW ? 128 : 32, p, pre, rowstart);
+  const TileInfo ti = decode_tile(MODE, 128, p, pre, rowstart);
   if (!ti.valid) return;   // uniform across the workgroup
-  gemm_tile<MODE, BW, FEED>(p, ti, ldsA, ldsB, ldsSA, ldsSB);
+  gemm_tile<MODE, FEED>(p, ti, ldsA, ldsB, ldsSA, ldsSB);
 }
 
 static int64_t tile_upper_bound(int mode, const GemmArgs& p) {
@@ -401,19 +372,19 @@ static int64_t tile_upper_bound(int mode, const GemmArgs& p) {
   return ((p.M + BM - 1) / BM + p.G) * ntc;   // sum_g ceil(m_g/BM) <= ceil(M/BM) + G
 }
 
-template <int MODE, bool BW>
+template <int MODE>
 static void launch_feed(const GemmArgs& p, dim3 grid, dim3 block, hipStream_t st) {
-  if (p.feed == kFeedFast) hipLaunchKernelGGL((grouped_gemm_kernel<MODE, BW, kFeedFast>), grid, block, 0, st, p);
-  else hipLaunchKernelGGL((grouped_gemm_kernel<MODE, BW, kFeedPrecise>), grid, block, 0, st, p);
+  if (p.feed == kFeedFast) hipLaunchKernelGGL((grouped_gemm_kernel<MODE, kFeedFast>), grid, block, 0, st, p);
+  else hipLaunchKernelGGL((grouped_gemm_kernel<MODE, kFeedPrecise>), grid, block, 0, st, p);
 }
 
 hipError_t launch_bw_gemm(int mode, const GemmArgs& p, hipStream_t st) {
   const int64_t tiles = tile_upper_bound(mode, p);
   if (tiles == 0) return hipSuccess;
   dim3 grid((unsigned)tiles), block(kThreads);
-  if (mode == kFwd) launch_feed<kFwd, true>(p, grid, block, st);
-  else if (mode == kDgrad) launch_feed<kDgrad, true>(p, grid, block, st);
-  else launch_feed<kWgrad, true>(p, grid, block, st);
+  if (mode == kFwd) launch_feed<kFwd>(p, grid, block, st);
+  else if (mode == kDgrad) launch_feed<kDgrad>(p, grid, block, st);
+  else launch_feed<kWgrad>(p, grid, block, st);
   return hipGetLastError();
 }
 

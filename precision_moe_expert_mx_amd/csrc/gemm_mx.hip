@@ -556,7 +556,9 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const Tile& t, char*
         for (int c = 0; c < 8; ++c)
           if (c < CPB * lo_b || c >= CPB * hi_b) *(uint4*)(row + ((c ^ swz(r)) << 4)) = make_uint4(0, 0, 0, 0);
       }
-      stage_barrier();
+      // the zeros are visible to every wave: this stage's own loads landed before the stage's barrier,
+      // and the next stage's (possibly in flight) go to the other buffer, so only LDS stores are waited on
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     }
     const char* A = st;
     const char* B = st + kStageA;

@@ -38,3 +38,21 @@ def random_bf16(rng, shape, std=1.0, outlier_frac=0.0, outlier_mult=100.0):
         idx = rng.choice(x.size, int(outlier_frac * x.size) or 1, replace=False)
         x.reshape(-1)[idx] *= np.float32(outlier_mult)
     return f32_to_bf16_bits(x)
+
+
+def same_bytes(got, ref, what):
+    """Quantiser outputs of the GPU (codes, scales, ...) equal the oracle's, element by element."""
+    for i, (g, r) in enumerate(zip(got, ref)):
+        g, r = np.asarray(g), np.asarray(r)
+        assert g.shape == r.shape and np.array_equal(g, r), f"{what}: output {i} differs from the oracle's quantisation"
+
+
+def check_rows(n, idx=None, seed=0, cap=256):
+    """Operand rows whose bytes are compared with the oracle's quantisation before they feed an oracle
+    GEMM: the given ones, else all up to `cap`, else `cap` seeded ones including the first and last."""
+    if idx is not None:
+        return np.asarray(idx, np.int64)
+    if n <= cap:
+        return np.arange(n)
+    rng = np.random.default_rng(seed)
+    return np.unique(np.concatenate([[0, n - 1], rng.choice(n, cap - 2, replace=False)]))

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
     m, L = _lib()
     for name in _declared():
         assert hasattr(L, name), name
-    assert m.abi_version() == 1
+    assert m.abi_version() == 2
 
 
 def test_host_helpers():
@@ -148,6 +148,31 @@ def test_gemm_argument_errors():
     assert st == 2 and "ld" in msg
     assert _status(L, "fp8bw_grouped_gemm_wgrad", A16, A16, A16b, A16b, 1408, A16, 4, 1024, 512, 256, A16, 0,
                    None)[0] == 2
+
+
+def test_fp8_feed_entry_points_validate_like_the_precise_ones():
+    """The full-rate FP8 feed has entry points of its own (same arguments); the output dtype argument
+    takes exactly MXMOE_F32 or MXMOE_BF16 (no feed bits)."""
+    _, L = _lib()
+    ok_args = (A16, A16, A16b, A16b, A16, 4, 1024, 512, 256, A16, 0, None)
+    for fn in ("mx_grouped_gemm_fwd", "mx_grouped_gemm_fwd_fp8feed", "fp8bw_grouped_gemm_fwd",
+               "fp8bw_grouped_gemm_fwd_fp8feed"):
+        for dt in (0x100, 0x101, 2, -1):
+            a = list(ok_args); a[10] = dt
+            st, msg = _status(L, fn, *a)
+            assert st == 4 and fn in msg, (fn, dt, msg)
+        a = list(ok_args); a[7] = 500
+        assert _status(L, fn, *a)[0] == 2
+        a = list(ok_args); a[6] = 0
+        assert _status(L, fn, *a) == (0, "")
+    for fn in ("mx_grouped_gemm_dgrad_fp8feed", "mx_grouped_gemm_wgrad_fp8feed"):
+        st, msg = _status(L, fn, A16, A16, A16b, A16b, 1024, A16, 4, 1024, 512, 256, A16, 0, None)
+        assert st == 2 and fn in msg
+    st, msg = _status(L, "fp8bw_grouped_gemm_wgrad_fp8feed", A16, A16, A16b, A16b, 1184, A16, 4, 1024, 512, 256, A16,
+                      0, None)
+    assert st == 2 and "fp8feed" in msg
+    a = list(ok_args); a[8] = 200
+    assert _status(L, "fp8bw_grouped_gemm_dgrad_fp8feed", *a)[0] == 2
 
 
 def test_binding_refuses_cpu_tensors():

@@ -6,7 +6,7 @@ import pytest
 import torch
 
 import oracle
-from gpu_util import dev, host, random_bf16, require_gpu
+from gpu_util import dev, host, random_bf16, require_gpu, same_bytes
 from workloads import f32_to_bf16_bits, routing_offsets
 
 pytestmark = pytest.mark.gpu
@@ -81,11 +81,15 @@ def test_gemms_on_power_of_two_operands():
         od = dev(offs)
         qx, sx = m.fp8bw_quantize_act_1x128(dev(x), pow2=True)
         qw, sw, qwT = m.fp8bw_quantize_weight_128x128(dev(w), transposed=True, pow2=True)
+        same_bytes((host(qx), host(sx)), oracle.bw_quantize_act_1x128(x, pow2=True), "pow2 X")
+        wq = oracle.bw_quantize_weight_128x128(w, pow2=True)
+        same_bytes((host(qw), host(sw), host(qwT)), (wq[0], wq[1], wq[0].T), "pow2 W")
         y = m.fp8bw_grouped_gemm_fwd(qx, sx, qw, sw, od, N)
         ref, bnd = oracle.bw_gemm_fwd(host(qx), host(sx), host(qw), host(sw), offs, N)
         ok, worst, _ = oracle.check_gemm(host(y), ref, bnd, "f32")
         assert ok, f"fwd worst err/tol {worst}"
         qd, sd = m.fp8bw_quantize_act_1x128(dev(dy), pow2=True)
+        same_bytes((host(qd), host(sd)), oracle.bw_quantize_act_1x128(dy, pow2=True), "pow2 dY")
         dx = m.fp8bw_grouped_gemm_dgrad(qd, sd, qwT, sw, od, K)
         ref, bnd = oracle.bw_gemm_dgrad(host(qd), host(sd), host(qw), host(sw), offs, N, K)
         ok, worst, _ = oracle.check_gemm(host(dx), ref, bnd, "f32")
@@ -93,6 +97,8 @@ def test_gemms_on_power_of_two_operands():
         ld = oracle.bw_colwise_ld_min(M, G)
         qdT, sdT = m.fp8bw_quantize_colwise_128(dev(dy), od, ld=ld, pow2=True)
         qxT, sxT = m.fp8bw_quantize_colwise_128(dev(x), od, ld=ld, pow2=True)
+        same_bytes((host(qdT), host(sdT)), oracle.bw_quantize_colwise_128(dy, offs, ld, pow2=True), "pow2 dY 128-token")
+        same_bytes((host(qxT), host(sxT)), oracle.bw_quantize_colwise_128(x, offs, ld, pow2=True), "pow2 X 128-token")
         dw = m.fp8bw_grouped_gemm_wgrad(qdT, sdT, qxT, sxT, od, M, "f32")
         ref, bnd = oracle.bw_gemm_wgrad(host(qdT), host(sdT), host(qxT), host(sxT), offs, N, K)
         ok, worst, _ = oracle.check_gemm(host(dw), ref, bnd, "f32")

@@ -6,7 +6,7 @@ import pytest
 import torch
 
 import oracle
-from gpu_util import dev, host, random_bf16, require_gpu
+from gpu_util import check_rows, dev, host, random_bf16, require_gpu, same_bytes
 from test_gpu_gemm import _check, _gpu_out, _rand_layer
 from workloads import f32_to_bf16_bits, make_workload
 
@@ -74,16 +74,25 @@ def test_colwise_ragged_and_weight_layout():
 
 def _fp4_layer_check(m, L, dt, rows=None, groups=None, n_idx=None, k_idx=None, extra=0):
     offs = dev(L.offs)
-    x, w, dy = dev(L.x), dev(L.w.reshape(-1, L.K)), dev(L.dy)
+    w2 = L.w.reshape(-1, L.K)
+    x, w, dy = dev(L.x), dev(w2), dev(L.dy)
     worst = {}
+    r_chk = check_rows(L.M, rows, cap=1 << 30)
+    w_chk = check_rows(L.G * L.N, seed=73)
     qx, sx = m.mxfp4_quantize_rowwise(x)
     qw, sw = m.mxfp4_quantize_rowwise(w)
+    same_bytes((host(qx)[r_chk], host(sx)[r_chk]), oracle.mxfp4_quantize_rowwise(L.x[r_chk]), "E2M1 X row-wise")
+    same_bytes((host(qw)[w_chk], host(sw)[w_chk]), oracle.mxfp4_quantize_rowwise(w2[w_chk]), "E2M1 W row-wise")
     y = m.mxfp4_grouped_gemm_fwd(qx, sx, qw, sw, offs, L.N, dt)
     ref, bnd = oracle.mxfp4_gemm_fwd(host(qx), host(sx), host(qw), host(sw), L.offs, L.N, rows=rows)
     got = _gpu_out(y) if rows is None else _gpu_out(y)[rows]
     worst["fwd"] = _check(got, ref, bnd, dt, "fp4 fwd")
     qd, sd = m.mxfp4_quantize_rowwise(dy)
     qwT, swT = m.mxfp4_quantize_colwise(w, None, ld=L.G * L.N)
+    k_chk = check_rows(L.K, seed=74, cap=32)
+    same_bytes((host(qd)[r_chk], host(sd)[r_chk]), oracle.mxfp4_quantize_rowwise(L.dy[r_chk]), "E2M1 dY row-wise")
+    same_bytes((host(qwT)[k_chk], host(swT)[k_chk]), oracle.mxfp4_quantize_colwise(w2[:, k_chk], None, L.G * L.N),
+               "E2M1 W column-wise")
     dx = m.mxfp4_grouped_gemm_dgrad(qd, sd, qwT, swT, offs, L.K, dt)
     ref, bnd = oracle.mxfp4_gemm_dgrad(host(qd), host(sd), host(qwT), host(swT), L.offs, L.N, L.K, rows=rows)
     got = _gpu_out(dx) if rows is None else _gpu_out(dx)[rows]
@@ -94,6 +103,11 @@ def _fp4_layer_check(m, L, dt, rows=None, groups=None, n_idx=None, k_idx=None, e
     qdT, sdT = m.mxfp4_quantize_colwise(dy, offs, ld=ld)
     qxT, sxT = m.mxfp4_quantize_colwise(x, offs, ld=ld)
     dw = m.mxfp4_grouped_gemm_wgrad(qdT, sdT, qxT, sxT, offs, L.M, dt)
+    n_chk, k_chk = check_rows(L.N, n_idx, cap=1 << 30), check_rows(L.K, k_idx, cap=1 << 30)
+    same_bytes((host(qdT)[n_chk], host(sdT)[n_chk]), oracle.mxfp4_quantize_colwise(L.dy[:, n_chk], L.offs, ld),
+               "E2M1 dY column-wise")
+    same_bytes((host(qxT)[k_chk], host(sxT)[k_chk]), oracle.mxfp4_quantize_colwise(L.x[:, k_chk], L.offs, ld),
+               "E2M1 X column-wise")
     ref, bnd = oracle.mxfp4_gemm_wgrad(host(qdT), host(sdT), host(qxT), host(sxT), L.offs, L.N, L.K,
                                        groups=groups, n_idx=n_idx, k_idx=k_idx)
     got = _gpu_out(dw)
@@ -117,10 +131,10 @@ def test_gemms_ragged_groups():
     print("fp4 padded ld", _fp4_layer_check(m, L, "f32", extra=2048))
 
 
-def test_wgrad_scale_rows_both_paths():
-    """MXFP4 weight gradient at a scale pitch of unaligned rows (ld / 32 not a multiple of 4) and at the
-    recommended pitch (aligned rows): experts start at blocks of every residue mod 4, with stages of 1
-    to 8 valid blocks."""
+def test_wgrad_at_two_scale_pitches():
+    """MXFP4 weight gradient (its scale rows are always gathered through registers) at a scale pitch of
+    unaligned rows (ld / 32 not a multiple of 4) and at the recommended pitch (aligned rows): experts
+    start at blocks of every residue mod 4, with stages of 1 to 8 valid blocks."""
     m = require_gpu()
     rng = np.random.default_rng(43)
     sizes = [0, 70, 300, 40, 128, 200, 5, 150, 33, 180]
@@ -132,6 +146,8 @@ def test_wgrad_scale_rows_both_paths():
     for ld in (ld_min, m.mxfp4_colwise_ld(L.M, L.G)):
         qdT, sdT = m.mxfp4_quantize_colwise(dy, offs, ld=ld)
         qxT, sxT = m.mxfp4_quantize_colwise(x, offs, ld=ld)
+        same_bytes((host(qdT), host(sdT)), oracle.mxfp4_quantize_colwise(L.dy, L.offs, ld), "E2M1 dY column-wise")
+        same_bytes((host(qxT), host(sxT)), oracle.mxfp4_quantize_colwise(L.x, L.offs, ld), "E2M1 X column-wise")
         ref, bnd = oracle.mxfp4_gemm_wgrad(host(qdT), host(sdT), host(qxT), host(sxT), L.offs, L.N, L.K)
         for dt in ("f32", "bf16"):
             dw = m.mxfp4_grouped_gemm_wgrad(qdT, sdT, qxT, sxT, offs, L.M, dt)
@@ -154,6 +170,8 @@ def test_run_of_mixed_magnitudes_is_exact():
     w = f32_to_bf16_bits(wv.astype(np.float32))
     qx, sx = m.mxfp4_quantize_rowwise(dev(x))
     qw, sw = m.mxfp4_quantize_rowwise(dev(w))
+    same_bytes((host(qx), host(sx)), oracle.mxfp4_quantize_rowwise(x), "E2M1 X row-wise")
+    same_bytes((host(qw), host(sw)), oracle.mxfp4_quantize_rowwise(w), "E2M1 W row-wise")
     y = m.mxfp4_grouped_gemm_fwd(qx, sx, qw, sw, dev(offs), N, "f32")
     ref, _ = oracle.mxfp4_gemm_fwd(host(qx), host(sx), host(qw), host(sw), offs, N)
     assert np.array_equal(_gpu_out(y), ref)

@@ -5,7 +5,7 @@ import pytest
 import torch
 
 import oracle
-from gpu_util import dev, host, random_bf16, require_gpu
+from gpu_util import check_rows, dev, host, random_bf16, require_gpu, same_bytes
 from workloads import make_workload, random_offsets, routing_offsets
 
 pytestmark = pytest.mark.gpu
@@ -49,26 +49,36 @@ def _gpu_out(t):
 
 def run_layer(m, L, dt="f32", rows=None, wgrad_groups=None, n_idx=None, k_idx=None, check=("fwd", "dgrad", "wgrad"),
               fast=False):
-    """Quantise on the GPU (bit-exactness is covered elsewhere), run the GEMMs, compare with the oracle
-    evaluated on the GPU's own quantised operands (copied back)."""
+    """Quantise on the GPU, run the GEMMs, compare with the oracle evaluated on the GPU's quantised
+    operands (copied back).  Those bytes are first compared with the oracle's own quantisation of the
+    bf16 inputs: every activation row (column-wise: every n / k row) the sampled outputs read, and a
+    sample of the weight rows."""
     offs_d = dev(L.offs)
     x, w, dy = dev(L.x), dev(L.w), dev(L.dy)
     rel = FAST_REL if fast else oracle.gemm.REL_TOL
+    r_chk = np.arange(L.M) if rows is None else np.asarray(rows, np.int64)
     worst = {}
     if "fwd" in check:
         qx, sx = m.mx_quantize_rowwise(x)
         qw, sw = m.mx_quantize_rowwise(w)
         y = m.mx_grouped_gemm_fwd(qx, sx, qw, sw, offs_d, L.N, dt, fast=fast)
         hq = [host(t) for t in (qx, sx, qw, sw)]
+        same_bytes((hq[0][r_chk], hq[1][r_chk]), oracle.mx_quantize_rowwise(L.x[r_chk]), "X row-wise")
+        w_chk = check_rows(L.G * L.N, None, 70)
+        same_bytes((hq[2][w_chk], hq[3][w_chk]), oracle.mx_quantize_rowwise(L.w[w_chk]), "W row-wise")
         ref, bnd = oracle.mx_gemm_fwd(*hq, L.offs, L.N, rows=rows)
         got = _gpu_out(y)[rows] if rows is not None else _gpu_out(y)
         worst["fwd"] = _check(got, ref, bnd, dt, "fwd", rel)
     if "dgrad" in check:
         qdy, sdy = m.mx_quantize_rowwise(dy)
         # the row pitches the benchmark uses (the recommended ones, >= the minimum)
-        qwT, swT = m.mx_quantize_colwise(w, None, ld=m.mx_colwise_ld(L.G * L.N))
+        ldw = m.mx_colwise_ld(L.G * L.N)
+        qwT, swT = m.mx_quantize_colwise(w, None, ld=ldw)
         dx = m.mx_grouped_gemm_dgrad(qdy, sdy, qwT, swT, offs_d, L.K, dt, fast=fast)
         hq = [host(t) for t in (qdy, sdy, qwT, swT)]
+        same_bytes((hq[0][r_chk], hq[1][r_chk]), oracle.mx_quantize_rowwise(L.dy[r_chk]), "dY row-wise")
+        k_chk = check_rows(L.K, None, 71, cap=32)
+        same_bytes((hq[2][k_chk], hq[3][k_chk]), oracle.mx_quantize_colwise(L.w[:, k_chk], None, ldw), "W column-wise")
         ref, bnd = oracle.mx_gemm_dgrad(*hq, L.offs, L.N, L.K, rows=rows)
         got = _gpu_out(dx)[rows] if rows is not None else _gpu_out(dx)
         worst["dgrad"] = _check(got, ref, bnd, dt, "dgrad", rel)
@@ -79,6 +89,10 @@ def run_layer(m, L, dt="f32", rows=None, wgrad_groups=None, n_idx=None, k_idx=No
         qxT, sxT = m.mx_quantize_colwise(x, offs_d, ld=ld)
         dw = m.mx_grouped_gemm_wgrad(qdyT, sdyT, qxT, sxT, offs_d, L.M, dt, fast=fast)
         hq = [host(t) for t in (qdyT, sdyT, qxT, sxT)]
+        n_chk = np.arange(L.N) if n_idx is None else np.asarray(n_idx)
+        k_chk = np.arange(L.K) if k_idx is None else np.asarray(k_idx)
+        same_bytes((hq[0][n_chk], hq[1][n_chk]), oracle.mx_quantize_colwise(L.dy[:, n_chk], L.offs, ld), "dY column-wise")
+        same_bytes((hq[2][k_chk], hq[3][k_chk]), oracle.mx_quantize_colwise(L.x[:, k_chk], L.offs, ld), "X column-wise")
         ref, bnd = oracle.mx_gemm_wgrad(*hq, L.offs, L.N, L.K, groups=wgrad_groups, n_idx=n_idx, k_idx=k_idx)
         got = _gpu_out(dw)
         if wgrad_groups is not None:
@@ -136,6 +150,8 @@ def test_wgrad_scale_rows_both_paths():
         qdyT, sdyT = m.mx_quantize_colwise(dy, offs_d, ld=ld)
         qxT, sxT = m.mx_quantize_colwise(x, offs_d, ld=ld)
         hq = [host(t) for t in (qdyT, sdyT, qxT, sxT)]
+        same_bytes(hq[:2], oracle.mx_quantize_colwise(L.dy, L.offs, ld), f"dY column-wise ld={ld}")
+        same_bytes(hq[2:], oracle.mx_quantize_colwise(L.x, L.offs, ld), f"X column-wise ld={ld}")
         ref, bnd = oracle.mx_gemm_wgrad(*hq, L.offs, L.N, L.K)
         for dt in ("f32", "bf16"):
             dw = m.mx_grouped_gemm_wgrad(qdyT, sdyT, qxT, sxT, offs_d, L.M, dt)
@@ -158,6 +174,8 @@ def test_dgrad_padded_weight_pitch():
         ldw = L.G * L.N + extra
         qwT, swT = m.mx_quantize_colwise(w, None, ld=ldw)
         hq = [host(t) for t in (qdy, sdy, qwT, swT)]
+        same_bytes(hq[:2], oracle.mx_quantize_rowwise(L.dy), "dY row-wise")
+        same_bytes(hq[2:], oracle.mx_quantize_colwise(L.w, None, ldw), f"W column-wise ldw={ldw}")
         ref, bnd = oracle.mx_gemm_dgrad(*hq, L.offs, L.N, L.K)
         for dt in ("f32", "bf16"):
             dx = m.mx_grouped_gemm_dgrad(qdy, sdy, qwT, swT, offs_d, L.K, dt)
@@ -247,10 +265,14 @@ def test_blockwise_gemms():
         offs = dev(L.offs)
         qx, sx = m.fp8bw_quantize_act_1x128(dev(L.x))
         qw, sw, qwT = m.fp8bw_quantize_weight_128x128(dev(L.w), transposed=True)
+        same_bytes((host(qx), host(sx)), oracle.bw_quantize_act_1x128(L.x), "bw X 1x128")
+        wq = oracle.bw_quantize_weight_128x128(L.w)
+        same_bytes((host(qw), host(sw), host(qwT)), (wq[0], wq[1], wq[0].T), "bw W 128x128")
         y = m.fp8bw_grouped_gemm_fwd(qx, sx, qw, sw, offs, N)
         ref, bnd = oracle.bw_gemm_fwd(host(qx), host(sx), host(qw), host(sw), L.offs, N)
         print("bw fwd", _check(_gpu_out(y), ref, bnd, "f32", "bw fwd"))
         qd, sd = m.fp8bw_quantize_act_1x128(dev(L.dy))
+        same_bytes((host(qd), host(sd)), oracle.bw_quantize_act_1x128(L.dy), "bw dY 1x128")
         dx = m.fp8bw_grouped_gemm_dgrad(qd, sd, qwT, sw, offs, K)
         ref, bnd = oracle.bw_gemm_dgrad(host(qd), host(sd), host(qw), host(sw), L.offs, N, K)
         print("bw dgrad", _check(_gpu_out(dx), ref, bnd, "f32", "bw dgrad"))
@@ -265,12 +287,20 @@ def test_blockwise_full_size_sampled():
         offs_d = dev(lay.offs)
         rows = np.unique(rng.choice(lay.M, 64, replace=False))
         qx, sx = m.fp8bw_quantize_act_1x128(dev(lay.x))
-        qw, sw, qwT = m.fp8bw_quantize_weight_128x128(dev(lay.w.reshape(-1, lay.K)), transposed=True)
+        w2 = lay.w.reshape(-1, lay.K)
+        qw, sw, qwT = m.fp8bw_quantize_weight_128x128(dev(w2), transposed=True)
         y = m.fp8bw_grouped_gemm_fwd(qx, sx, qw, sw, offs_d, lay.N)
         hqw, hsw = host(qw), host(sw)
+        same_bytes((host(qx)[rows], host(sx)[rows]), oracle.bw_quantize_act_1x128(lay.x[rows]), "bw X 1x128")
+        hqwT = host(qwT)
+        for band in rng.choice(w2.shape[0] // 128, 4, replace=False):       # sampled 128-row weight bands
+            r = slice(128 * band, 128 * band + 128)
+            wq = oracle.bw_quantize_weight_128x128(w2[r])
+            same_bytes((hqw[r], hsw[band:band + 1], hqwT[:, r]), (wq[0], wq[1], wq[0].T), "bw W 128x128")
         ref, bnd = oracle.bw_gemm_fwd(host(qx), host(sx), hqw, hsw, lay.offs, lay.N, rows=rows)
         print(lay.name, "bw fwd", _check(_gpu_out(y)[rows], ref, bnd, "f32", "bw fwd"))
         qd, sd = m.fp8bw_quantize_act_1x128(dev(lay.dy))
+        same_bytes((host(qd)[rows], host(sd)[rows]), oracle.bw_quantize_act_1x128(lay.dy[rows]), "bw dY 1x128")
         dx = m.fp8bw_grouped_gemm_dgrad(qd, sd, qwT, sw, offs_d, lay.K)
         ref, bnd = oracle.bw_gemm_dgrad(host(qd), host(sd), hqw, hsw, lay.offs, lay.N, lay.K, rows=rows)
         print(lay.name, "bw dgrad", _check(_gpu_out(dx)[rows], ref, bnd, "f32", "bw dgrad"))
@@ -338,6 +368,10 @@ def _bw_wgrad_case(m, L, dt, groups=None, n_idx=None, k_idx=None):
     qd, sd = m.fp8bw_quantize_colwise_128(dev(L.dy), offs, ld=ld)
     qx, sx = m.fp8bw_quantize_colwise_128(dev(L.x), offs, ld=ld)
     dw = m.fp8bw_grouped_gemm_wgrad(qd, sd, qx, sx, offs, L.M, dt)
+    n_chk = check_rows(L.N, n_idx)
+    k_chk = check_rows(L.K, k_idx)
+    same_bytes((host(qd)[n_chk], host(sd)[n_chk]), oracle.bw_quantize_colwise_128(L.dy[:, n_chk], L.offs, ld), "bw dY 128-token")
+    same_bytes((host(qx)[k_chk], host(sx)[k_chk]), oracle.bw_quantize_colwise_128(L.x[:, k_chk], L.offs, ld), "bw X 128-token")
     ref, bnd = oracle.bw_gemm_wgrad(host(qd), host(sd), host(qx), host(sx), L.offs, L.N, L.K,
                                     groups=groups, n_idx=n_idx, k_idx=k_idx)
     got = _gpu_out(dw)
@@ -385,7 +419,12 @@ def _swiglu_case(m, L, rows=None):
     qw, sw = m.mx_quantize_rowwise(dev(L.w))
     y, qh, sh, h = m.mx_grouped_gemm_fwd_swiglu(qx, sx, qw, sw, offs, L.N, with_h=True)
     H = L.N // 2
-    ref, bnd = oracle.mx_gemm_fwd(host(qx), host(sx), host(qw), host(sw), L.offs, L.N, rows=rows)
+    hq = [host(t) for t in (qx, sx, qw, sw)]
+    r_chk = np.arange(L.M) if rows is None else np.asarray(rows, np.int64)
+    same_bytes((hq[0][r_chk], hq[1][r_chk]), oracle.mx_quantize_rowwise(L.x[r_chk]), "X row-wise")
+    w_chk = check_rows(L.G * L.N, None, 72)
+    same_bytes((hq[2][w_chk], hq[3][w_chk]), oracle.mx_quantize_rowwise(L.w[w_chk]), "W row-wise")
+    ref, bnd = oracle.mx_gemm_fwd(*hq, L.offs, L.N, rows=rows)
     sel = slice(None) if rows is None else rows
     worst_y = _check(_gpu_out(y)[sel], ref, bnd, "bf16", "swiglu y")
     hg = host(h)[sel].astype(np.float64)
