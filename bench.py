@@ -3,11 +3,13 @@
 One step is the whole path, forward and backward, of both expert linear layers
 (gate+up and down) of the DeepSeek-V3-671B one-GPU expert shard: 8 local
 experts, 65536 routed rows with Zipf(1.2)-skewed group sizes (one expert with
-17 rows), hidden 7168, gate+up N=4096, down N=7168.  Per layer:
+17 rows), hidden 7168, gate+up N=4096, down N=7168.  In training order:
 
-    MX quantise X row-wise, W row-wise        -> grouped GEMM forward  (Y bf16)
-    MX quantise dY row-wise, W column-wise    -> grouped GEMM dgrad    (dX bf16)
-    MX quantise dY, X column-wise per expert  -> grouped GEMM wgrad    (dW fp32)
+    gate+up: X, W -> both MX layouts (one launch each)
+             grouped GEMM forward, SwiGLU and MX quantisation of H (both layouts) in its epilogue
+    down:    W -> both layouts; grouped GEMM forward on H
+             dY -> both layouts; grouped GEMM dgrad (dH bf16); grouped GEMM wgrad on H column-wise
+    gate+up: dY -> both layouts; grouped GEMM dgrad (dX bf16); grouped GEMM wgrad (dW fp32)
 
 `value` = algorithmic GEMM flops of the step (2*M*N*K per GEMM, real rows only)
 divided by the wall time of the whole step, quantisers included, inputs
@@ -139,6 +141,37 @@ def build_layer_ops(m, torch, lay, dev_in, fast=False, fused=True):
             # the MFMA rate the feed runs at: bf16 for the precise feed, the MXFP8 rate for the fast one
             op.peak_tflops = MFMA_PEAK_TFLOPS["mxfp8" if fast else "bf16"]
     return ops, b
+
+
+def build_step_ops(m, torch, layers, dev_ins):
+    """The expert MLP's step in training order, with both fused sides: per layer, X, W and dY each get
+    both MX layouts from one dual-layout launch; the gate+up forward applies SwiGLU in its epilogue and
+    writes H row-wise and column-wise, which the down layer's forward and weight gradient consume (no
+    quantiser launch for H, H never in HBM in a wider format).  The two layers share the routing.
+
+    Order: gate+up X, W; gate+up forward (+ H); down W; down forward; down dY; down dgrad; down wgrad;
+    gate+up dY; gate+up dgrad; gate+up wgrad.  The dY of each layer is the workload's synthetic
+    gradient (the activation's backward is not part of this path)."""
+    gu, dn = layers
+    assert gu.name == "gate_up" and dn.name == "down" and dn.K == gu.N // 2 and np.array_equal(gu.offs, dn.offs)
+    gu_ops, gb = build_layer_ops(m, torch, gu, dev_ins[0])
+    dn_ops, db = build_layer_ops(m, torch, dn, dev_ins[1])
+    by = {op.name: op for op in gu_ops + dn_ops}
+    G, M, N, K = gu.G, gu.M, gu.N, gu.K
+    offs = dev_ins[0][3]
+    H = N // 2
+    mxb = 1.0 + 1.0 / 32.0
+    fused = Op("gate_up.fwd_swiglu", "gemm",
+               lambda: m.mx_grouped_gemm_fwd_swiglu(gb["qx"], gb["sx"], gb["qw"], gb["sw"], offs, N, y=gb["y"],
+                                                    qh=db["qx"], sh=db["sx"], qhT=db["qxT"], shT=db["sxT"]),
+               2.0 * M * N * K, "grouped_gemm fwd + SwiGLU + MX(H) both layouts")
+    fused.bytes = (M * K + G * N * K) * mxb + M * N * 2 + 2 * M * H * mxb
+    fused.peak_tflops = MFMA_PEAK_TFLOPS["bf16"]
+    order = ["gate_up.quant_x_dual", "gate_up.quant_w_dual", None, "down.quant_w_dual", "down.fwd",
+             "down.quant_dy_dual", "down.dgrad", "down.wgrad", "gate_up.quant_dy_dual", "gate_up.dgrad",
+             "gate_up.wgrad"]
+    ops = [fused if n is None else by[n] for n in order]
+    return ops, (gb, db)
 
 
 def to_device(torch, a: np.ndarray):
@@ -524,13 +557,9 @@ def other_configs_leg(m, torch, steps=5, warmup=2):
     res = {}
     for wname in ("dsv3_16b", "llama4_scout"):
         wl = make_workload(wname)
-        ops, keep = [], []
-        for lay in wl.layers:
-            dev_in = (to_device(torch, lay.x), to_device(torch, lay.w), to_device(torch, lay.dy),
-                      to_device(torch, lay.offs))
-            lops, bufs = build_layer_ops(m, torch, lay, dev_in)
-            ops += lops
-            keep.append((dev_in, bufs))
+        dev_ins = [(to_device(torch, lay.x), to_device(torch, lay.w), to_device(torch, lay.dy),
+                    to_device(torch, lay.offs)) for lay in wl.layers]
+        ops, keep = build_step_ops(m, torch, wl.layers, dev_ins)
         ms = time_ops(torch, ops, steps, warmup)
         gflop = sum(op.work for op in ops if op.kind == "gemm")
         gemm_ms = sum(float(np.mean(op.ms)) for op in ops if op.kind == "gemm")
@@ -546,7 +575,7 @@ def other_configs_leg(m, torch, steps=5, warmup=2):
             "ops": {op.name: op_summary(op) for op in ops},
         }
         log(f"{wname}: {ms:.3f} ms/step, GEMMs {gt:.0f} TFLOP/s")
-        del ops, keep, wl
+        del ops, keep, wl, dev_ins
         torch.cuda.empty_cache()
     return res
 
@@ -721,14 +750,10 @@ def main():
     copy_gbps = 2 * 5 * (1 << 30) / (e0.elapsed_time(e1) * 1e-3) / 1e9
     del cal, cal2
 
-    ops = []
-    keep = []
-    for lay in wl.layers:
-        dev_in = (to_device(torch, lay.x), to_device(torch, lay.w), to_device(torch, lay.dy),
-                  to_device(torch, lay.offs))
-        lops, bufs = build_layer_ops(m, torch, lay, dev_in)
-        ops += lops
-        keep.append((dev_in, bufs))
+    dev_ins = [(to_device(torch, lay.x), to_device(torch, lay.w), to_device(torch, lay.dy),
+                to_device(torch, lay.offs)) for lay in wl.layers]
+    ops, step_bufs = build_step_ops(m, torch, wl.layers, dev_ins)
+    keep = list(zip(dev_ins, step_bufs))
     torch.cuda.synchronize()
     log(f"inputs resident; {torch.cuda.memory_allocated() / 2**30:.1f} GiB allocated")
 
@@ -829,7 +854,9 @@ def main():
         "config": {"workload": wname, "experts": wl.layers[0].G, "routed_rows": wl.layers[0].M,
                    "group_sizes": [int(s) for s in wl.layers[0].sizes],
                    "layers": {l.name: {"N": l.N, "K": l.K} for l in wl.layers},
-                   "step": "per layer: X, W, dY each quantised to both MX layouts in one launch + grouped GEMM fwd/dgrad/wgrad"},
+                   "step": "expert MLP fwd+bwd: per layer X, W, dY each quantised to both MX layouts in one launch; "
+                           "gate+up forward with SwiGLU and H quantised to both layouts in its epilogue, consumed by "
+                           "the down layer; grouped GEMM fwd/dgrad/wgrad of both layers"},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "quant_roofline": quant_roofline,

@@ -158,12 +158,19 @@ mxmoe_status mx_grouped_gemm_fwd(const uint8_t* qx, const uint8_t* sx,
  *      row-wise (the forward operand of the down GEMM) without H
  *      ever reaching memory in a wider format (a reading: the pages name no activation; SwiGLU is
  *      the gated unit of the DeepSeek-V3 / Llama-4 expert MLPs);
- *   h  f32 [M, H] or NULL: H as formed before quantisation (for checking).
- * Precise feed; N % 256 == 0; qx/sx, qw/sw and offs as for mx_grouped_gemm_fwd. */
+ *   h  f32 [M, H] or NULL: H as formed before quantisation (for checking);
+ *   qhT [H, ldh], shT [H, ldh/32], or both NULL: the same fp32 H MX-quantised column-wise, the
+ *      weight-gradient operand of the down GEMM, in the layout of mx_quantize_colwise with the
+ *      routing offsets (32-row blocks restarting at each expert, pads and the tail 0x00); ldh % 32
+ *      == 0 and ldh >= mx_colwise_ld_min(M, G).  Both copies of H leave the epilogue, so H never
+ *      reaches memory in a wider format and is not read back to be quantised.
+ * Precise feed; N % 256 == 0; qx/sx, qw/sw and offs as for mx_grouped_gemm_fwd.  M == 0 is a no-op
+ * (nothing is written). */
 mxmoe_status mx_grouped_gemm_fwd_swiglu(const uint8_t* qx, const uint8_t* sx,
                                         const uint8_t* qw, const uint8_t* sw,
                                         const int32_t* offs, int32_t G, int64_t M, int64_t N, int64_t K,
-                                        void* y, uint8_t* qh, uint8_t* sh, float* h, void* stream);
+                                        void* y, uint8_t* qh, uint8_t* sh, float* h,
+                                        uint8_t* qhT, uint8_t* shT, int64_t ldh, void* stream);
 
 /* dgrad: dX[r, k] = sum_n dY[r, n] W[g*N + n, k]        for r in group g
  *        qdy/sdy = mx_quantize_rowwise(dY [M, N]);
@@ -189,7 +196,7 @@ mxmoe_status mx_grouped_gemm_wgrad(const uint8_t* qdyT, const uint8_t* sdyT,
 /* ---------------------------------------------------------------- full-rate FP8 operand feed
  * The same three products, arguments, layouts, validation and errors as
  * mx_grouped_gemm_fwd / _dgrad / _wgrad, computed on the block-scaled FP8 MFMA
- * (v_mfma_scale_f32_16x16x128_f8f6f4, E8M0 scales applied by the instruction) at
+ * (v_mfma_scale_f32_32x32x64_f8f6f4, E8M0 scales applied by the instruction) at
  * twice the bf16 rate.  Its sums are not fp32-accurate.  Measured on gfx950 (the
  * 16x16x128 and 32x32x64 block-scaled forms and the older FP8 MFMAs alike): the
  * products of each run of 8 consecutive contraction elements held in one lane's

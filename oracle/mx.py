@@ -227,6 +227,36 @@ def mx_quantize_rowwise_values(v):
     return q.reshape(R, C), s.reshape(R, C // BLOCK)
 
 
+def mx_quantize_colwise_values(v, offs, ld: int):
+    """MX-quantise exact real values (float64 [R, C], e.g. float32 results widened) column-wise in the
+    layout of mx_quantize_colwise: blocks of 32 rows of one column restarting at every group's first
+    row, group g at columns [c_g, c_g + m_g), a short last block's amax over its real rows, pads, the
+    tail and scale bytes of no block 0x00.  The same block rule as mx_quantize_colwise, whose input is
+    bf16 bit patterns."""
+    v = np.asarray(v, dtype=np.float64)
+    if not np.all(np.isfinite(v)):
+        raise ValueError("non-finite input is outside the contract")
+    R, C = v.shape
+    offs = np.asarray(offs, dtype=np.int64)
+    if offs[0] != 0 or offs[-1] != R or np.any(np.diff(offs) < 0):
+        raise ValueError("bad offsets")
+    if ld % BLOCK or ld < mx_colwise_ld_min(R, len(offs) - 1):
+        raise ValueError("bad ld")
+    qT = np.zeros((C, ld), dtype=np.uint8)
+    sT = np.zeros((C, ld // BLOCK), dtype=np.uint8)
+    col0, nb = mx_group_columns(offs)
+    for g in range(len(offs) - 1):
+        r0, r1 = int(offs[g]), int(offs[g + 1])
+        for b in range(int(nb[g])):
+            a = r0 + BLOCK * b
+            z = min(a + BLOCK, r1)
+            q, s = _quantize_blocks(v[a:z, :], axis=0)
+            c = int(col0[g]) + BLOCK * b
+            qT[:, c:c + (z - a)] = q.T
+            sT[:, c // BLOCK] = s[0]
+    return qT, sT
+
+
 def swiglu(gate, up):
     """Gated activation of an expert's gate+up output: silu(gate) * up, silu(z) = z / (1 + e^-z).
 

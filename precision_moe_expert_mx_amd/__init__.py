@@ -47,7 +47,8 @@ _SIGS = {
     "mx_quantize_colwise": (ctypes.c_int, [_p, _i64, _i64, _p, _i32, _p, _p, _i64, _p]),
     "mx_quantize_dual": (ctypes.c_int, [_p, _i64, _i64, _p, _i64, _p, _i32, _p, _p, _p, _p, _i64, _p]),
     "mx_grouped_gemm_fwd": (ctypes.c_int, [_p, _p, _p, _p, _p, _i32, _i64, _i64, _i64, _p, ctypes.c_int, _p]),
-    "mx_grouped_gemm_fwd_swiglu": (ctypes.c_int, [_p, _p, _p, _p, _p, _i32, _i64, _i64, _i64, _p, _p, _p, _p, _p]),
+    "mx_grouped_gemm_fwd_swiglu": (ctypes.c_int, [_p, _p, _p, _p, _p, _i32, _i64, _i64, _i64, _p, _p, _p, _p, _p, _p,
+                                                  _i64, _p]),
     "mx_grouped_gemm_dgrad": (ctypes.c_int, [_p, _p, _p, _p, _i64, _p, _i32, _i64, _i64, _i64, _p, ctypes.c_int, _p]),
     "mx_grouped_gemm_wgrad": (ctypes.c_int, [_p, _p, _p, _p, _i64, _p, _i32, _i64, _i64, _i64, _p, ctypes.c_int, _p]),
     "fp8bw_quantize_act_1x128": (ctypes.c_int, [_p, _i64, _i64, _p, _p, _p]),
@@ -252,10 +253,12 @@ def mx_grouped_gemm_fwd(qx, sx, qw, sw, offs, N: int, out_dtype: str = "f32", y=
 
 
 def mx_grouped_gemm_fwd_swiglu(qx, sx, qw, sw, offs, N: int, y=None, qh=None, sh=None, h=None,
-                               with_h: bool = False, stream=None):
+                               with_h: bool = False, colwise: bool = False, ldh: Optional[int] = None, qhT=None,
+                               shT=None, stream=None):
     """Forward of the gate+up GEMM (W rows: gate then up of each expert, N = 2H) with SwiGLU and the
-    row-wise MX quantisation of H in the epilogue.  Returns (y bf16 [M, N], qh [M, H], sh [M, H/32])
-    and, with with_h (or h given), H in fp32 [M, H] as a fourth item."""
+    MX quantisation of H in the epilogue.  Returns (y bf16 [M, N], qh [M, H], sh [M, H/32]); with
+    colwise (or qhT given) also H column-wise (qhT [H, ldh], shT [H, ldh/32], ldh by default the
+    recommended pitch for the routing offsets); with with_h (or h given) H in fp32 [M, H] last."""
     torch = _torch()
     M, K = qx.shape
     G = offs.numel() - 1
@@ -265,10 +268,18 @@ def mx_grouped_gemm_fwd_swiglu(qx, sx, qw, sw, offs, N: int, y=None, qh=None, sh
     sh = _empty((M, H // 32), torch.uint8, qx) if sh is None else sh
     if with_h and h is None:
         h = _empty((M, H), torch.float32, qx)
+    if colwise or qhT is not None:
+        if qhT is not None:
+            ldh = qhT.shape[1]
+        elif ldh is None:
+            ldh = mx_colwise_ld(M, G)
+        qhT = _empty((H, ldh), torch.uint8, qx) if qhT is None else qhT
+        shT = _empty((H, ldh // 32), torch.uint8, qx) if shT is None else shT
     _check("mx_grouped_gemm_fwd_swiglu", lib().mx_grouped_gemm_fwd_swiglu(
         _ptr(qx), _ptr(sx), _ptr(qw), _ptr(sw), _ptr(offs), G, M, N, K, _ptr(y), _ptr(qh), _ptr(sh), _ptr(h),
-        _stream_handle(stream)))
-    return (y, qh, sh) if h is None else (y, qh, sh, h)
+        _ptr(qhT), _ptr(shT), int(ldh or 0), _stream_handle(stream)))
+    out = (y, qh, sh) + ((qhT, shT) if qhT is not None else ())
+    return out if h is None else out + (h,)
 
 
 def mx_grouped_gemm_dgrad(qdy, sdy, qwT, swT, offs, K: int, out_dtype: str = "f32", dx=None, stream=None, fast: bool = False):

@@ -243,7 +243,8 @@ mxmoe_status mx_grouped_gemm_fwd_fp8feed(const uint8_t* qx, const uint8_t* sx, c
 
 mxmoe_status mx_grouped_gemm_fwd_swiglu(const uint8_t* qx, const uint8_t* sx, const uint8_t* qw, const uint8_t* sw,
                                         const int32_t* offs, int32_t G, int64_t M, int64_t N, int64_t K, void* y,
-                                        uint8_t* qh, uint8_t* sh, float* h, void* stream) {
+                                        uint8_t* qh, uint8_t* sh, float* h, uint8_t* qhT, uint8_t* shT, int64_t ldh,
+                                        void* stream) {
   const char* fn = "mx_grouped_gemm_fwd_swiglu";
   TRY(check_gemm_common(fn, offs, G, M, N, K, y, MXMOE_BF16));
   if (N % 256) return fail(MXMOE_ERR_SHAPE, "%s: N = 2H must be a multiple of 256 (N=%lld)", fn, (long long)N);
@@ -254,6 +255,13 @@ mxmoe_status mx_grouped_gemm_fwd_swiglu(const uint8_t* qx, const uint8_t* sx, co
   TRY(check_ptr(fn, "qh", qh, 16));
   TRY(check_ptr(fn, "sh", sh, 4));
   if (h && !aligned(h, 16)) return fail(MXMOE_ERR_ALIGN, "%s: h not 16-byte aligned", fn);
+  if ((qhT == nullptr) != (shT == nullptr)) return fail(MXMOE_ERR_NULL, "%s: qhT and shT go together", fn);
+  if (qhT) {
+    TRY(check_ptr(fn, "qhT", qhT, 16));
+    if (ldh % 32 || ldh < mx_colwise_ld_min(M, G))
+      return fail(MXMOE_ERR_SHAPE, "%s: ldh=%lld must be a multiple of 32 and >= mx_colwise_ld_min(M, G)=%lld", fn,
+                  (long long)ldh, (long long)mx_colwise_ld_min(M, G));
+  }
   GemmArgs p;
   memset(&p, 0, sizeof p);
   p.a = qx; p.sa = sx; p.b = qw; p.sb = sw; p.offs = offs; p.out = y;
@@ -262,6 +270,7 @@ mxmoe_status mx_grouped_gemm_fwd_swiglu(const uint8_t* qx, const uint8_t* sx, co
   p.feed = kFeedPrecise;
   p.lda = K; p.ldsa = K / 32; p.ldb = K; p.ldsb = K / 32;
   p.act_q = qh; p.act_s = sh; p.act_dbg = h;
+  p.act_qT = qhT; p.act_sT = shT; p.act_ld = ldh;
   TRY(check_strides(fn, p, N));
   if (M == 0) return ok();
   TRY(check_device());

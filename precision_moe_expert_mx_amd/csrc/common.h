@@ -231,6 +231,11 @@ struct GemmArgs {
   uint8_t* act_q;
   uint8_t* act_s;
   float* act_dbg;
+  // and, when act_qT is not NULL, H MX-quantised column-wise (32-row blocks restarting at each expert,
+  // the layout of mx_quantize_colwise) into act_qT [H, act_ld] / act_sT [H, act_ld / 32]
+  uint8_t* act_qT;
+  uint8_t* act_sT;
+  int64_t act_ld;
 };
 
 hipError_t launch_mx_gemm(int mode, const GemmArgs& a, hipStream_t st);

@@ -26,10 +26,9 @@
 //    bf16 with the block's power-of-two scale folded in (v_cvt_scalef32_pk_bf16_fp8), and feeds two
 //    v_mfma_f32_32x32x16_bf16; every product is exact and the MFMA sums at fp32 precision.  A and B
 //    use the same assignment of contraction elements to MFMA k-slots, so the sum is unchanged.
-//  * fast (opt-in): v_mfma_scale_f32_16x16x128_f8f6f4 at twice the bf16 rate, scales applied by the
-//    instruction.  Lane l feeds row l % 16, 16-byte chunks g and 4 + g of the 128-byte row
-//    (g = l / 16) and the E8M0 byte of block g.  Its sums are truncated per run of products (see
-//    include/mxmoe.h).
+//  * fast (opt-in, the *_fp8feed entry points): v_mfma_scale_f32_32x32x64_f8f6f4 at twice the bf16
+//    rate, scales applied by the instruction, two k-steps per stage (lane layout at the loop).  Its
+//    sums are truncated per run of 8 products (see include/mxmoe.h).
 //
 // MXFP4 (E2M1 codes two per byte, E8M0 per 32): the same tiling with 128 bytes = 256 elements
 // (eight blocks) per stage on the fast feed only, two v_mfma_scale_f32_16x16x128_f8f6f4 k-steps per
@@ -88,8 +87,9 @@ struct Tile {
   int g, mt, nt;
   int64_t row0;   // forward / dgrad: first A row of the tile
   int rows;       // forward / dgrad: valid A rows (1..256)
-  int64_t col0;   // wgrad: first column of the expert in the column-wise layout
+  int64_t col0;   // wgrad, gated forward: first column of the expert in the column-wise layout
   int nblk;       // wgrad: 32-blocks in the expert's contraction
+  int64_t col_end;  // gated forward: columns of the column-wise layout holding blocks (32 x all blocks)
 };
 
 // LDS rows of 128 bytes; 16-byte chunk c of row r sits at chunk position c ^ swz(r), so that the
@@ -107,7 +107,9 @@ __device__ __forceinline__ int64_t uniform64(int64_t v) {
 
 // Tile list of the launch and this workgroup's tile.  Scratch arrays live at the start of the LDS
 // (before the first operand load overwrites them).  Returns false when the workgroup has no tile.
-template <int MODE>
+// CB: also the first 32-block of each expert in the column-wise layout (wgrad; the gated forward's
+// column-wise H).
+template <int MODE, bool CB>
 __device__ bool decode_tile(const GemmArgs& p, char* lds, Tile& t) {
   int32_t* s_rs = (int32_t*)lds;             // clamped offsets [G+1]
   int32_t* s_pre = s_rs + (kMaxG + 1);       // tile prefix over the processing order [G+1]
@@ -135,7 +137,7 @@ __device__ bool decode_tile(const GemmArgs& p, char* lds, Tile& t) {
   const int ntc = cdiv(MODE == kFwd ? p.N : p.K, BN);
   const int mtc_w = cdiv(p.N, BM);
   const int lane = tid & 63;
-  if (tid < 64 || (MODE == kWgrad && tid < 128)) {
+  if (tid < 64 || (CB && tid < 128)) {
     const bool tiles = tid < 64;
     int carry = 0;
     for (int base = 0; base < G; base += 64) {
@@ -187,7 +189,8 @@ __device__ bool decode_tile(const GemmArgs& p, char* lds, Tile& t) {
   t.nt = r / gsz;
   t.row0 = s_rs[g] + (int64_t)t.mt * BM;
   t.rows = (int)min((int64_t)BM, (int64_t)s_rs[g + 1] - t.row0);
-  t.col0 = 32 * (int64_t)s_cb[g];
+  t.col0 = CB ? 32 * (int64_t)s_cb[g] : 0;
+  t.col_end = CB ? 32 * (int64_t)s_cb[G] : 0;
   t.nblk = cdiv(m_g, 32);
   if (MODE == kWgrad) {
     // offsets that are not monotone could place an expert past the leading dimension: clip (lda is
@@ -245,6 +248,9 @@ __device__ __forceinline__ void stage_barrier() {
 // wave writes its pre-activations as bf16 to Y (gate at column u, up at H + u); the up waves hand
 // their fp32 values to the gate waves through LDS, which form H = silu(gate) * up in fp32 and
 // MX-quantise it row-wise: a row's 32-column block is one fragment, split between lanes l and l ^ 32.
+// With a column-wise output the gate waves put H back into LDS in place of the up values, and all
+// waves then quantise the tile's 256 rows x 128 hidden units in 32-row blocks down each column (the
+// tile's rows start at a multiple of 256 inside its expert, so its blocks are the expert's blocks).
 template <typename Acc>
 __device__ __forceinline__ void act_epilogue(const GemmArgs& p, const Tile& t, char* lds, Acc (&acc)[WM / 32][WN / 32]) {
   constexpr int NI = WM / 32, NJ = WN / 32;
@@ -254,6 +260,7 @@ __device__ __forceinline__ void act_epilogue(const GemmArgs& p, const Tile& t, c
   const int wm = w / kWavesN, wn = w % kWavesN;
   const int64_t H = p.N / 2;
   const bool up_wave = wn >= kWavesN / 2;
+  const bool colwise = p.act_qT != nullptr;       // uniform: a kernel argument
   const int ucol0 = WN * (wn % (kWavesN / 2)) + 4 * (lane / 32);    // tile-local hidden column of fragment 0
   const int64_t hcol0 = (int64_t)t.nt * (BN / 2) + ucol0;          // global hidden column
   const int row_lim = t.rows;
@@ -281,43 +288,96 @@ __device__ __forceinline__ void act_epilogue(const GemmArgs& p, const Tile& t, c
       }
   }
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  if (up_wave) return;
+  if (up_wave && !colwise) return;
 
+  if (!up_wave) {
 #pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    const int r = lrow + 32 * i;
-    const int64_t grow = t.row0 + r;
+    for (int i = 0; i < NI; ++i) {
+      const int r = lrow + 32 * i;
+      const int64_t grow = t.row0 + r;
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      float h[16];
-      uint32_t amax = 0;
+      for (int j = 0; j < NJ; ++j) {
+        float h[16];
+        uint32_t amax = 0;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float4 u = *(const float4*)(up + r * kUpPitch + ucol0 + 32 * j + 8 * q);
-        const float uu[4] = {u.x, u.y, u.z, u.w};
+        for (int q = 0; q < 4; ++q) {
+          float* uptr = up + r * kUpPitch + ucol0 + 32 * j + 8 * q;
+          const float4 u = *(const float4*)uptr;
+          const float uu[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const float g = acc[i][j][4 * q + k];
-          // silu with the hardware exponential and reciprocal (a few ulp; g -> -inf gives -0)
-          h[4 * q + k] = g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * uu[k];
-          amax = max(amax, __float_as_uint(h[4 * q + k]) & 0x7FFFFFFFu);
+          for (int k = 0; k < 4; ++k) {
+            const float g = acc[i][j][4 * q + k];
+            // silu with the hardware exponential and reciprocal (a few ulp; g -> -inf gives -0)
+            h[4 * q + k] = g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * uu[k];
+            amax = max(amax, __float_as_uint(h[4 * q + k]) & 0x7FFFFFFFu);
+          }
+          // the lane read these four up values itself: H replaces them in place
+          if (colwise) *(float4*)uptr = make_float4(h[4 * q], h[4 * q + 1], h[4 * q + 2], h[4 * q + 3]);
         }
-      }
-      amax = max(amax, (uint32_t)__shfl_xor((int)amax, 32, 64));
-      // shared exponent of the block: floor(log2 amax) - 8 from the fp32 exponent field, clamped
-      const int e = max((int)(amax >> 23) - 135, -127);
-      const float sc = __uint_as_float((uint32_t)(e + 127) << 23);
-      const float lim = __uint_as_float(((uint32_t)(e + 135) << 23) | 0x600000u);   // 448 * 2^e
-      if (r >= row_lim) continue;
-      const int64_t hc = hcol0 + 32 * j;
+        amax = max(amax, (uint32_t)__shfl_xor((int)amax, 32, 64));
+        // shared exponent of the block: floor(log2 amax) - 8 from the fp32 exponent field, clamped
+        const int e = max((int)(amax >> 23) - 135, -127);
+        const float sc = __uint_as_float((uint32_t)(e + 127) << 23);
+        const float lim = __uint_as_float(((uint32_t)(e + 135) << 23) | 0x600000u);   // 448 * 2^e
+        if (r >= row_lim) continue;
+        const int64_t hc = hcol0 + 32 * j;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const uint32_t code = cvt4_f32_e4m3_scaled(h[4 * q], h[4 * q + 1], h[4 * q + 2], h[4 * q + 3], lim, sc);
-        *(uint32_t*)(p.act_q + grow * H + hc + 8 * q) = code;
-        if (p.act_dbg)
-          *(float4*)(p.act_dbg + grow * H + hc + 8 * q) = make_float4(h[4 * q], h[4 * q + 1], h[4 * q + 2], h[4 * q + 3]);
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t code = cvt4_f32_e4m3_scaled(h[4 * q], h[4 * q + 1], h[4 * q + 2], h[4 * q + 3], lim, sc);
+          *(uint32_t*)(p.act_q + grow * H + hc + 8 * q) = code;
+          if (p.act_dbg)
+            *(float4*)(p.act_dbg + grow * H + hc + 8 * q) = make_float4(h[4 * q], h[4 * q + 1], h[4 * q + 2], h[4 * q + 3]);
+        }
+        if (lane < 32) p.act_s[grow * (H / 32) + (hc - 4 * (lane / 32)) / 32] = (uint8_t)(e + 127);
       }
-      if (lane < 32) p.act_s[grow * (H / 32) + (hc - 4 * (lane / 32)) / 32] = (uint8_t)(e + 127);
+    }
+  }
+  if (!colwise) return;
+
+  // column-wise H: item it = (hidden column c, 32-row block b) of the tile; blocks at or past the
+  // expert's end within this tile hold no rows of it (the next expert's columns) and are skipped,
+  // rows past its end inside its last block are pads (zero codes)
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  const int64_t ldq = p.act_ld;
+  const int64_t tcol = t.col0 + (int64_t)t.mt * BM;               // the tile's first column of qT
+  const int nb_tile = (row_lim + 31) / 32;
+  for (int it = tid; it < (BN / 2) * (BM / 32); it += NT) {
+    const int c = it % (BN / 2), b = it / (BN / 2);
+    // (with offsets that are not monotone an expert's blocks could lie past the leading dimension)
+    if (b >= nb_tile || tcol + 32 * b + 32 > ldq) continue;
+    float v[32];
+    uint32_t amax = 0;
+#pragma unroll
+    for (int r = 0; r < 32; ++r) {
+      const int row = 32 * b + r;
+      v[r] = row < row_lim ? up[row * kUpPitch + c] : 0.f;
+      amax = max(amax, __float_as_uint(v[r]) & 0x7FFFFFFFu);
+    }
+    const int e = max((int)(amax >> 23) - 135, -127);
+    const float sc = __uint_as_float((uint32_t)(e + 127) << 23);
+    const float lim = __uint_as_float(((uint32_t)(e + 135) << 23) | 0x600000u);
+    uint32_t code[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) code[q] = cvt4_f32_e4m3_scaled(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3], lim, sc);
+    const int64_t u = (int64_t)t.nt * (BN / 2) + c;                // hidden unit: row of qT
+    uint4* dst = (uint4*)(p.act_qT + u * ldq + tcol + 32 * b);
+    dst[0] = make_uint4(code[0], code[1], code[2], code[3]);
+    dst[1] = make_uint4(code[4], code[5], code[6], code[7]);
+    p.act_sT[u * (ldq / 32) + tcol / 32 + b] = (uint8_t)(e + 127);
+  }
+  // the tile holding the last routed row zeroes the tail of its 128 rows of qT and sT: the columns past
+  // the last expert's blocks
+  if (t.row0 + t.rows == p.M) {
+    const int64_t tail = ldq - t.col_end;                           // a multiple of 32
+    const int64_t chunks = tail / 16;
+    for (int64_t k = tid; k < (BN / 2) * chunks; k += NT) {
+      const int64_t u = (int64_t)t.nt * (BN / 2) + k / chunks;
+      *(uint4*)(p.act_qT + u * ldq + t.col_end + 16 * (k % chunks)) = make_uint4(0, 0, 0, 0);
+    }
+    const int64_t stail = tail / 32;
+    for (int64_t k = tid; k < (BN / 2) * stail; k += NT) {
+      const int64_t u = (int64_t)t.nt * (BN / 2) + k / stail;
+      p.act_sT[u * (ldq / 32) + t.col_end / 32 + k % stail] = 0;
     }
   }
 }
@@ -485,9 +545,10 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const Tile& t, char*
 
   // ---- accumulators ----------------------------------------------------------------------------
   const int wm = w / kWavesN, wn = w % kWavesN;
-  constexpr int NI = FEED == kFeedPrecise ? WM / 32 : WM / 16;   // A fragments (32 or 16 rows)
-  constexpr int NJ = FEED == kFeedPrecise ? WN / 32 : WN / 16;   // B fragments
-  constexpr int NR = FEED == kFeedPrecise ? 16 : 4;     // accumulator registers per fragment pair
+  constexpr int FR = FP4 ? 16 : 32;                       // fragment rows / columns (E2M1: 16x16x128)
+  constexpr int NI = WM / FR;                            // A fragments
+  constexpr int NJ = WN / FR;                            // B fragments
+  constexpr int NR = FR * FR / 64;                       // accumulator registers per fragment pair
   typedef float vacc __attribute__((ext_vector_type(NR)));
   vacc acc[NI][NJ];
 #pragma unroll
@@ -628,27 +689,34 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const Tile& t, char*
         }
       }
     } else {
-      const int fr = lane & 15, fg = lane >> 4;
-      v8i bf[NJ];
-      int sbv[NJ];
+      // E4M3 on v_mfma_scale_f32_32x32x64_f8f6f4, two k-steps of 64 bytes per stage.  Lane l feeds row
+      // l % 32 with the 16-byte chunks 4 ks2 + h and 4 ks2 + 2 + h of the 128-byte row (h = l / 32); the
+      // scale operand of half h applies to the stage's block 2 ks2 + h, i.e. to chunks 4 ks2 + 2h and
+      // 4 ks2 + 2h + 1, which lanes of both halves hold (measured on gfx950).
+      const int lr = lane & 31, h = lane >> 5;
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        const int r = WN * wn + 16 * j + fr;
-        const v4i lo = *(const v4i*)(B + lds_off(r, fg));
-        const v4i hi = *(const v4i*)(B + lds_off(r, 4 + fg));
-        bf[j] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        sbv[j] = (int)((sword(SB, r) >> (8 * fg)) & 0xFFu);
-      }
+      for (int ks2 = 0; ks2 < 2; ++ks2) {
+        v8i bf[NJ];
+        int sbv[NJ];
 #pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        const int r = WM * wm + 16 * i + fr;
-        const v4i lo = *(const v4i*)(A + lds_off(r, fg));
-        const v4i hi = *(const v4i*)(A + lds_off(r, 4 + fg));
-        const v8i af = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        const int sav = (int)((sword(SA, r) >> (8 * fg)) & 0xFFu);
+        for (int j = 0; j < NJ; ++j) {
+          const int r = WN * wn + 32 * j + lr;
+          const v4i lo = *(const v4i*)(B + lds_off(r, 4 * ks2 + h));
+          const v4i hi = *(const v4i*)(B + lds_off(r, 4 * ks2 + 2 + h));
+          bf[j] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          sbv[j] = (int)((sword(SB, r) >> (8 * (2 * ks2 + h))) & 0xFFu);
+        }
 #pragma unroll
-        for (int j = 0; j < NJ; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[j], af, acc[i][j], 0, 0, 0, sbv[j], 0, sav);
+        for (int i = 0; i < NI; ++i) {
+          const int r = WM * wm + 32 * i + lr;
+          const v4i lo = *(const v4i*)(A + lds_off(r, 4 * ks2 + h));
+          const v4i hi = *(const v4i*)(A + lds_off(r, 4 * ks2 + 2 + h));
+          const v8i af = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          const int sav = (int)((sword(SA, r) >> (8 * (2 * ks2 + h))) & 0xFFu);
+#pragma unroll
+          for (int j = 0; j < NJ; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf[j], af, acc[i][j], 0, 0, 0, sbv[j], 0, sav);
+        }
       }
     }
   }
@@ -669,7 +737,7 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const Tile& t, char*
   const int row_lim = (int)min((int64_t)BM, MODE == kWgrad ? p.N - (int64_t)t.mt * BM : (int64_t)t.rows);
   const int col_lim = (int)min((int64_t)BN, nout - (int64_t)t.nt * BN);
   const int64_t out_row0 = MODE == kWgrad ? (int64_t)t.g * p.N + (int64_t)t.mt * BM : t.row0;
-  constexpr int FI = FEED == kFeedPrecise ? 32 : 16;     // fragment rows / columns
+  constexpr int FI = FR;                                 // fragment rows / columns
   const int lrow = WM * wm + lane % FI;
   const int lcol = WN * wn + 4 * (lane / FI);
   const int64_t base = (out_row0 + lrow) * nout + (int64_t)t.nt * BN + lcol;
@@ -701,7 +769,7 @@ template <int MODE, int FEED, bool SDW, bool FP4 = false, bool ACT = false>
 __global__ __launch_bounds__(NT, 1) void mx_grouped_gemm_kernel(GemmArgs p) {
   __shared__ __attribute__((aligned(16))) char lds[kLds];
   Tile t;
-  if (!decode_tile<MODE>(p, lds, t)) return;     // uniform across the workgroup
+  if (!decode_tile<MODE, MODE == kWgrad || ACT>(p, lds, t)) return;     // uniform across the workgroup
   // the tile's fields are the same in every lane: say so, so that everything derived from them (operand
   // bases, loop bounds) lives in scalar registers
   t.g = __builtin_amdgcn_readfirstlane(t.g);
@@ -711,6 +779,7 @@ __global__ __launch_bounds__(NT, 1) void mx_grouped_gemm_kernel(GemmArgs p) {
   t.nblk = __builtin_amdgcn_readfirstlane(t.nblk);
   t.row0 = uniform64(t.row0);
   t.col0 = uniform64(t.col0);
+  t.col_end = uniform64(t.col_end);
   __syncthreads();                               // scheduler scratch is reused for operands
   run_tile<MODE, FEED, SDW, FP4, ACT>(p, t, lds);
 }

@@ -276,3 +276,41 @@ def test_quantise_values_matches_bf16_path():
     v[0, 0] = 3.0 * 2.0 ** 20                       # amax with exponent field 127 + 21
     q, s = mx_quantize_rowwise_values(v)
     assert s[0, 0] == 127 + 21 - 8
+
+
+def test_colwise_values_matches_bf16_path_and_rowwise_rule():
+    """The column-wise value quantiser: on bf16-representable inputs it equals the (separately pinned)
+    bf16-pattern column-wise quantiser byte for byte, pads and tail included; on float32 values each
+    group's 32-row blocks equal the row-wise value quantiser applied to the group's rows transposed and
+    zero-padded to a multiple of 32 (zeros neither raise an amax nor change a code); an element whose
+    float32 value is not a bf16 value is quantised from its own value (brute-force nearest code)."""
+    from oracle import e4m3_encode_bruteforce, mx_group_columns, mx_quantize_colwise_values, mx_quantize_rowwise_values
+    rng = np.random.default_rng(9)
+    sizes, C = [0, 5, 70, 1, 32, 0, 41], 64
+    offs = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
+    M, G = int(offs[-1]), len(sizes)
+    ld = mx_colwise_ld_min(M, G) + 64
+    x = f32_to_bf16_bits((rng.standard_normal((M, C)) * np.where(rng.random((M, C)) < 0.02, 100, 1)).astype(np.float32))
+    q1, s1 = mx_quantize_colwise(x, offs, ld)
+    q2, s2 = mx_quantize_colwise_values(bf16_bits_to_f64(x), offs, ld)
+    assert np.array_equal(q1, q2) and np.array_equal(s1, s2)
+    v = (rng.standard_normal((M, C)) * np.exp2(rng.integers(-20, 20, (M, C)))).astype(np.float32).astype(np.float64)
+    qT, sT = mx_quantize_colwise_values(v, offs, ld)
+    col0, nb = mx_group_columns(offs)
+    used = np.zeros(ld, bool)
+    for g in range(G):
+        m = sizes[g]
+        if m == 0:
+            continue
+        pad = np.zeros((32 * int(nb[g]), C))
+        pad[:m] = v[offs[g]:offs[g + 1]]
+        qr, sr = mx_quantize_rowwise_values(pad.T)                  # [C, 32 nb]
+        c0 = int(col0[g])
+        assert np.array_equal(qT[:, c0:c0 + m], qr[:, :m])
+        assert np.array_equal(sT[:, c0 // 32:c0 // 32 + int(nb[g])], sr)
+        used[c0:c0 + m] = True
+        # one element per group against the brute-force encoder of its scaled value
+        k = int(rng.integers(0, C))
+        e = int(sr[k, 0]) - 127
+        assert qT[k, c0] == e4m3_encode_bruteforce(np.ldexp(pad[0, k], -e))[0]
+    assert not qT[:, ~used].any() and not sT[:, int(np.sum(nb)):].any()
