@@ -301,8 +301,7 @@ __device__ __forceinline__ void act_epilogue(const GemmArgs& p, const Tile& t, c
         uint32_t amax = 0;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          float* uptr = up + r * kUpPitch + ucol0 + 32 * j + 8 * q;
-          const float4 u = *(const float4*)uptr;
+          const float4 u = *(const float4*)(up + r * kUpPitch + ucol0 + 32 * j + 8 * q);
           const float uu[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
           for (int k = 0; k < 4; ++k) {
@@ -310,9 +309,8 @@ __device__ __forceinline__ void act_epilogue(const GemmArgs& p, const Tile& t, c
             // silu with the hardware exponential and reciprocal (a few ulp; g -> -inf gives -0)
             h[4 * q + k] = g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * uu[k];
             amax = max(amax, __float_as_uint(h[4 * q + k]) & 0x7FFFFFFFu);
+            acc[i][j][4 * q + k] = h[4 * q + k];     // H replaces the gate value (Y is written)
           }
-          // the lane read these four up values itself: H replaces them in place
-          if (colwise) *(float4*)uptr = make_float4(h[4 * q], h[4 * q + 1], h[4 * q + 2], h[4 * q + 3]);
         }
         amax = max(amax, (uint32_t)__shfl_xor((int)amax, 32, 64));
         // shared exponent of the block: floor(log2 amax) - 8 from the fp32 exponent field, clamped
@@ -334,36 +332,54 @@ __device__ __forceinline__ void act_epilogue(const GemmArgs& p, const Tile& t, c
   }
   if (!colwise) return;
 
-  // column-wise H: item it = (hidden column c, 32-row block b) of the tile; blocks at or past the
-  // expert's end within this tile hold no rows of it (the next expert's columns) and are skipped,
-  // rows past its end inside its last block are pads (zero codes)
+  // Column-wise H.  H goes to LDS transposed, column c of the tile at hT + c * kTPitch with its 256
+  // rows contiguous (every up value has been read: one more barrier first).  Then 16 lanes take one
+  // hidden column: at step m lane k reads the column's 16-byte chunk 16 m + k (rows 4 (16 m + k) .. + 3),
+  // so 32-row block b = 2 m + k / 8 is held by 8 lanes, whose amax meets by DPP, and the 16 lanes store
+  // 64 consecutive code bytes of the column's qT row.  Blocks at or past the expert's end within this
+  // tile hold no rows of it (the next expert's columns) and are skipped; rows past its end inside its
+  // last block are pads (zero codes).
+  constexpr int kTPitch = BM + 8;                 // the two lane halves of a transposed store: disjoint banks
+  static_assert((BN / 2) * kTPitch * 4 <= kLds, "transposed H must fit in LDS");
+  float* hT = (float*)lds;
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  if (!up_wave) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int k = 0; k < 4; ++k) hT[(ucol0 + 32 * j + 8 * q + k) * kTPitch + lrow + 32 * i] = acc[i][j][4 * q + k];
+  }
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   const int64_t ldq = p.act_ld;
   const int64_t tcol = t.col0 + (int64_t)t.mt * BM;               // the tile's first column of qT
   const int nb_tile = (row_lim + 31) / 32;
-  for (int it = tid; it < (BN / 2) * (BM / 32); it += NT) {
-    const int c = it % (BN / 2), b = it / (BN / 2);
-    // (with offsets that are not monotone an expert's blocks could lie past the leading dimension)
-    if (b >= nb_tile || tcol + 32 * b + 32 > ldq) continue;
-    float v[32];
-    uint32_t amax = 0;
+  const int k16 = lane & 15;
+  for (int cb = 4 * w + (lane >> 4); cb < BN / 2; cb += 4 * kWaves) {
+    const int64_t u = (int64_t)t.nt * (BN / 2) + cb;              // hidden unit: row of qT
 #pragma unroll
-    for (int r = 0; r < 32; ++r) {
-      const int row = 32 * b + r;
-      v[r] = row < row_lim ? up[row * kUpPitch + c] : 0.f;
-      amax = max(amax, __float_as_uint(v[r]) & 0x7FFFFFFFu);
+    for (int m = 0; m < 4; ++m) {
+      const int row0 = 4 * (16 * m + k16);
+      const float4 x = *(const float4*)(hT + cb * kTPitch + row0);
+      const float v0 = row0 < row_lim ? x.x : 0.f, v1 = row0 + 1 < row_lim ? x.y : 0.f;
+      const float v2 = row0 + 2 < row_lim ? x.z : 0.f, v3 = row0 + 3 < row_lim ? x.w : 0.f;
+      uint32_t amax = max(max(__float_as_uint(v0) & 0x7FFFFFFFu, __float_as_uint(v1) & 0x7FFFFFFFu),
+                          max(__float_as_uint(v2) & 0x7FFFFFFFu, __float_as_uint(v3) & 0x7FFFFFFFu));
+      amax = oct_max(amax);
+      const int e = max((int)(amax >> 23) - 135, -127);
+      const float sc = __uint_as_float((uint32_t)(e + 127) << 23);
+      const float lim = __uint_as_float(((uint32_t)(e + 135) << 23) | 0x600000u);
+      const uint32_t code = cvt4_f32_e4m3_scaled(v0, v1, v2, v3, lim, sc);
+      const int b = 2 * m + (k16 >> 3);
+      // (with offsets that are not monotone an expert's blocks could lie past the leading dimension)
+      if (b < nb_tile && tcol + 32 * b + 32 <= ldq) {
+        *(uint32_t*)(p.act_qT + u * ldq + tcol + row0) = code;
+        if ((k16 & 7) == 0) p.act_sT[u * (ldq / 32) + tcol / 32 + b] = (uint8_t)(e + 127);
+      }
     }
-    const int e = max((int)(amax >> 23) - 135, -127);
-    const float sc = __uint_as_float((uint32_t)(e + 127) << 23);
-    const float lim = __uint_as_float(((uint32_t)(e + 135) << 23) | 0x600000u);
-    uint32_t code[8];
-#pragma unroll
-    for (int q = 0; q < 8; ++q) code[q] = cvt4_f32_e4m3_scaled(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3], lim, sc);
-    const int64_t u = (int64_t)t.nt * (BN / 2) + c;                // hidden unit: row of qT
-    uint4* dst = (uint4*)(p.act_qT + u * ldq + tcol + 32 * b);
-    dst[0] = make_uint4(code[0], code[1], code[2], code[3]);
-    dst[1] = make_uint4(code[4], code[5], code[6], code[7]);
-    p.act_sT[u * (ldq / 32) + tcol / 32 + b] = (uint8_t)(e + 127);
   }
   // the tile holding the last routed row zeroes the tail of its 128 rows of qT and sT: the columns past
   // the last expert's blocks
@@ -521,6 +537,11 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const Tile& t, char*
       if (MODE != kWgrad || (c < lim_hi && c >= lim_lo)) {
         dma16s(a_off[j], a_base + koff, st + (kLoadRows * w + 8 * j) * BK);
         dma16s(b_off[j], b_base + koff, st + kStageA + (kLoadRows * w + 8 * j) * BK);
+      } else {
+        // a chunk outside the expert's blocks: zeros where the load would have landed (the buffer is
+        // free when a stage is issued, and the barrier that publishes the stage waits for LDS stores)
+        *(uint4*)(st + (kLoadRows * w + 8 * j) * BK + 16 * lane) = make_uint4(0, 0, 0, 0);
+        *(uint4*)(st + kStageA + (kLoadRows * w + 8 * j) * BK + 16 * lane) = make_uint4(0, 0, 0, 0);
       }
     }
     if constexpr (ALIGNED_START) {
@@ -568,62 +589,52 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const Tile& t, char*
     }
   }
   constexpr int BPS = SPS;                        // 32-blocks per stage
-  constexpr int CPB = 8 / BPS;                    // 16-byte chunks per block
-  for (int ks = 0; ks < nsteps; ++ks) {
-    stage_barrier();                               // stage ks landed; stage ks-1 fully read
-    // The next stage's loads may go out any time after the barrier (its buffer was last read in stage
-    // ks - 1) and must land by the next barrier.  The precise feed issues them after its first block's
-    // MFMAs, so that a stage opens with LDS reads, widening and MFMAs rather than with the issue.
-    auto next_stage = [&]() {
-      if (ks + 1 < nsteps) {
-        // The staged scale words arrived before the barrier.  They are stored, and the next words
-        // gathered, before the stage's operand loads go out: a wait the compiler places for those
-        // registers counts only its own loads, while the hardware counter would also hold the operand
-        // loads issued after them, and waiting on it there stalls on the next stage's data.
-        if (!SDW) put_scales(ks + 1, s_w);
-        if (!SDW && ks + 2 < nsteps) gather_scales(ks + 2, s_w);
-        issue(ks + 1);
-      }
-    };
-    constexpr bool kLateIssue = FEED == kFeedPrecise;
-    if constexpr (!kLateIssue) next_stage();
-    char* st = lds + (ks & 1) * kStage;
-    const uint32_t* SA = (const uint32_t*)(lds + 2 * kStage + (ks & 1) * kSStage);
-    const uint32_t* SB = SA + BM;
-    // the stage's blocks [lo_b, hi_b) belong to the expert: the leading blocks (first stage) and those
-    // past its last block (last stage) were not loaded
+  // The stage's blocks [lo_b, hi_b) belong to the expert: the leading blocks (first stage) and those past
+  // its last block (last stage) were not loaded (their chunks were zeroed at issue).  With ALIGNED_START
+  // the scale bytes of the other blocks are masked to 0 (a stale 0xFF would read as NaN): keep[] holds
+  // the wave-uniform byte masks of the stage's scale words.
+  auto stage_keep = [&](int ks, uint32_t (&keep)[SPS / 4]) {
     const int lo_b = ks == 0 ? f : 0;
     const int hi_b = MODE == kWgrad ? min(SPS, nblk_e - SPS * ks) : SPS;
-    // the stage's scale word of operand row r; with ALIGNED_START, the bytes of blocks outside
-    // [lo_b, hi_b) masked to 0: their operand chunks are zero, and a stale 0xFF would read as NaN
-    uint32_t keep[SPS / 4];                       // wave-uniform byte masks of the stage's scale words
 #pragma unroll
     for (int d = 0; d < SPS / 4; ++d) {
       auto low = [](int k) { return k >= 4 ? 0xFFFFFFFFu : (k <= 0 ? 0u : (1u << (8 * k)) - 1u); };
       keep[d] = __builtin_amdgcn_readfirstlane(low(hi_b - 4 * d) & ~low(lo_b - 4 * d));
     }
-    auto sword = [&](const uint32_t* S, int r, int word = 0) -> uint32_t {
-      if constexpr (ALIGNED_START) {
-        return S[512 * word + r] & keep[word];
-      } else {
-        return S[512 * word + r];
-      }
-    };
-    if (MODE == kWgrad && (lo_b > 0 || hi_b < BPS)) {
-      // zero the unloaded chunks of every row (the register path gathered their scale bytes as 0)
-      for (int q = tid; q < BM + BN; q += NT) {
-        const int r = q & 255;
-        char* row = st + (q < BM ? 0 : kStageA) + r * BK;
-        for (int c = 0; c < 8; ++c)
-          if (c < CPB * lo_b || c >= CPB * hi_b) *(uint4*)(row + ((c ^ swz(r)) << 4)) = make_uint4(0, 0, 0, 0);
-      }
-      // the zeros are visible to every wave: this stage's own loads landed before the stage's barrier,
-      // and the next stage's (possibly in flight) go to the other buffer, so only LDS stores are waited on
-      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  };
+  auto sword_k = [&](const uint32_t* S, int r, const uint32_t (&keep)[SPS / 4], int word = 0) -> uint32_t {
+    if constexpr (ALIGNED_START) {
+      return S[512 * word + r] & keep[word];
+    } else {
+      return S[512 * word + r];
     }
-    const char* A = st;
-    const char* B = st + kStageA;
+  };
+  // Loads of stage s into buffer s % 2, which no wave reads any more.  Register-staged scale words: those
+  // of stage s arrived earlier; they are stored, and stage s + 1's gathered, before the operand loads go
+  // out (a wait the compiler places for those registers counts only its own loads, while the hardware
+  // counter would also hold the operand loads issued after them).
+  auto stage_out = [&](int s) {
+    if (!SDW) put_scales(s, s_w);
+    if (!SDW && s + 1 < nsteps) gather_scales(s + 1, s_w);
+    issue(s);
+  };
 
+  for (int ks = 0; ks < nsteps; ++ks) {
+    stage_barrier();                               // stage ks landed; stage ks-1 fully read
+    // The next stage's loads may go out any time after the barrier (its buffer was last read in stage
+    // ks - 1) and must land by the next barrier.  The precise feed issues them after its first block's
+    // MFMAs, so that a stage opens with LDS reads, widening and MFMAs rather than with the issue.  (A
+    // software-pipelined precise loop, with the next block's LDS reads issued before the current
+    // block's MFMAs and the stage barrier moved before the last block's MFMAs, measured 4-7% slower.)
+    constexpr bool kLateIssue = FEED == kFeedPrecise;
+    if (!kLateIssue && ks + 1 < nsteps) stage_out(ks + 1);
+    const char* A = lds + (ks & 1) * kStage;
+    const char* B = A + kStageA;
+    const uint32_t* SA = (const uint32_t*)(lds + 2 * kStage + (ks & 1) * kSStage);
+    const uint32_t* SB = SA + BM;
+    uint32_t keep[SPS / 4];
+    stage_keep(ks, keep);
+    auto sword = [&](const uint32_t* S, int r, int word = 0) -> uint32_t { return sword_k(S, r, keep, word); };
     if constexpr (FEED == kFeedPrecise) {
       const int lr = lane & 31, h = lane >> 5;
       uint32_t sa_w[NI], sb_w[NJ];
@@ -660,7 +671,7 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const Tile& t, char*
 #pragma unroll
           for (int j = 0; j < NJ; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bhi[j], ahi[i], acc[i][j], 0, 0, 0);
-        if (kLateIssue && bb == 0) next_stage();
+        if (kLateIssue && bb == 0 && ks + 1 < nsteps) stage_out(ks + 1);
       }
     } else if constexpr (FP4) {
       // two k-steps of 128 E2M1 elements: lane group fg feeds block 4 ks2 + fg (16 bytes, the upper
