@@ -6,385 +6,306 @@
 // contraction before that partial is promoted, i.e. multiplied by its two scales and added to a
 // full-precision accumulator.  All experts run in one launch, each on its real number of rows (iitak.ru,
 // "NVIDIA sped up training of mixture-of-experts models on JAX tenfold": no capacity padding, no dropped
-// tokens): the launch enumerates the 128x128 output tiles of all experts from the device-resident group
-// offsets, so an expert with no rows contributes no tile (forward / dgrad) and one with a handful of rows
-// one partial tile.
+// tokens).
 //
 // Generic form computed by one workgroup (tile (mt, nt) of expert g), promoted per 128-slice kb:
 //   out[i, j] = sum_kb sA(i, kb) sB(j, kb) sum_{t in kb} A[row_a(i), col0_a + t] * B[row_b(j), col0_b + t]
 // where
-//   forward: A = X rows of expert g, B = W_g rows, sA = the 1x128 tile scale, sB = the 128x128 block scale
+//   forward: A = X rows of expert g, B = W_g rows; sA = the 1x128 tile scale, sB = the 128x128 block scale
+//            (one per tile and slice: a tile's 128 B rows are one weight block row)
 //   dgrad:   A = dY rows of expert g (1x128 tiles along N), B = the transposed weight copy (rows k,
-//            columns gN..gN+N), sB = the forward block scale read transposed
+//            columns gN..gN+N); sB = the forward block scale of (n-slice kb, k-block nt)
 //   wgrad:   A = column-wise dY (rows n), B = column-wise X (rows k), both from column c_g, 128-token
-//            blocks restarting at each expert with an fp32 scale per (row, block) on both operands
+//            blocks restarting at each expert; sA, sB the row scales of each block (sB per output column)
 //
-// Main loop: BK = 128 contraction bytes (one promotion slice) per step; global -> registers (prefetch of
-// the next step) -> LDS (16-byte chunks XOR-swizzled by row) -> MFMA operands.  Each of the four waves
-// owns a 64x64 quarter of the tile as 4x4 16x16 fragments, with an fp32 partial and an fp32 accumulator
-// per fragment.
+// The MX kernel's design with a 256 x 128 tile: 8 waves of 64 x 64 outputs (4 along A rows x 2 along B
+// rows), so each wave keeps an fp32 partial beside its accumulators (64 + 64 registers).  A stage is one
+// promotion slice (128 contraction bytes); operand rows and fp32 row scales move global -> LDS by
+// direct-to-LDS loads from a wave-uniform base and per-tile 32-bit lane offsets, two stages in LDS with
+// one barrier per stage, the next stage's loads issued after the first 32 elements' MFMAs.  LDS rows
+// of 128 bytes with 16-byte chunks XOR-swizzled by row.  The tile list comes from the device-resident
+// offsets (grouped_tile.h): ceil(m_g / 256) x (N_out / 128) tiles per expert for forward / dgrad (none
+// for an empty expert), every (n, k) tile of every expert for wgrad, largest expert first.
 //
-// Two operand feeds (same tiling, same LDS staging of the FP8 bytes):
-//  * precise (default): each 32-element piece is widened exactly to bf16 and multiplied on
-//    v_mfma_f32_16x16x32_bf16, whose sums are fp32-accurate;
-//  * full-rate FP8: v_mfma_scale_f32_16x16x128_f8f6f4 (unit scales) at twice the rate.  Lane l feeds
-//    row l % 16 with 16-byte chunks g and 4 + g of the 128-byte row (g = l / 16).  Measured on gfx950,
-//    it truncates the products of each run of 8 consecutive operand bytes toward zero below a 2^-13
-//    window of the run's largest product, so its error is bounded by about 7 * 2^-13 times the largest
-//    product of each run rather than by fp32 rounding.
-#include "common.h"
+// Operand feeds:
+//  * precise (default): each lane widens 16 E4M3 bytes exactly to bf16 and feeds two
+//    v_mfma_f32_32x32x16_bf16 per 32 elements, whose sums are fp32-accurate;
+//  * full-rate FP8: v_mfma_scale_f32_32x32x64_f8f6f4 with unit E8M0 scales, two k-steps per slice (lane
+//    l: row l % 32, chunks 4 s + h and 4 s + 2 + h, h = l / 32).  Measured on gfx950, it truncates the
+//    products of each run of 8 consecutive operand bytes toward zero to a 2^-13 window of the run's
+//    largest product, so its error is bounded by about 7 * 2^-13 times the largest product of each run.
+#include "grouped_tile.h"
 
 namespace mxmoe {
+namespace {
 
-constexpr int BM = 128, BN = 128, BK = 128;
-constexpr int kThreads = 256;
-constexpr int kMaxGroups = 1024;
+constexpr int BM = 256;                          // A rows per tile
+constexpr int BN = 128;                          // B rows per tile (output columns)
+constexpr int BK = 128;                          // contraction bytes per stage: one promotion slice
+constexpr int kWavesM = 4, kWavesN = 2, kWaves = kWavesM * kWavesN;
+constexpr int NT = 64 * kWaves;
+constexpr int WM = BM / kWavesM, WN = BN / kWavesN;          // 64 x 64 outputs per wave
+constexpr int NI = WM / 32, NJ = WN / 32;                    // 32 x 32 fragments
+constexpr int kRowsA = BM / kWaves, kRowsB = BN / kWaves;    // operand rows each wave loads per stage
+constexpr int NDA = kRowsA / 8, NDB = kRowsB / 8;            // 1 KiB loads (8 rows) per wave and stage
+constexpr int kStageA = BM * BK;                             // 32 KiB
+constexpr int kStage = kStageA + BN * BK;                    // 48 KiB
+constexpr int kScaleA = 0, kScaleB = 4 * BM, kScaleBlk = 4 * (BM + BN);   // byte offsets in a scale stage
+constexpr int kScaleStage = 4 * (BM + BN) + 16;
+constexpr int kLds = 2 * kStage + 2 * kScaleStage;
+static_assert(4 * (kMaxG + 1) * 4 <= kStage, "scheduler scratch must fit in the first stage");
 
-struct TileInfo {
-  int g;          // expert
-  int mt, nt;     // tile coordinates inside the expert
-  int64_t row0;   // first global row of A for this expert (forward / dgrad)
-  int rows;       // valid rows of this tile (forward / dgrad)
-  int nblk;       // wgrad: number of 128-token contraction blocks
-  int64_t col0;   // wgrad: first column of the expert in the column-wise layout
-  bool valid;
-};
+typedef float v16f __attribute__((ext_vector_type(16)));
 
-// Tiles are enumerated expert by expert; inside an expert the output-column tile runs fastest so
-// that consecutive workgroups share A rows.  Wave 0 computes the per-expert tile counts and their
-// prefix sums in LDS, then every thread binary-searches its tile.
-__device__ TileInfo decode_tile(int mode, int wblk, const GemmArgs& p, int32_t* pre, int64_t* rowstart) {
-  const int G = p.G;
-  const int64_t M = p.M;
-  const int nt_count = (int)((mode == kFwd ? p.N : p.K) / BN);
-  if (threadIdx.x < 64) {
-    const int lane = threadIdx.x;
-    int32_t carry = 0;
-    for (int g0 = 0; g0 <= G; g0 += 64) {
-      int g = g0 + lane;
-      int32_t cnt = 0;
-      int64_t o0 = 0;
-      if (g <= G) {
-        o0 = clamp_off(p.offs[g], M);
-        rowstart[g] = o0;
-      }
-      if (g < G) {
-        int64_t o1 = clamp_off(p.offs[g + 1], M);
-        int64_t m = o1 > o0 ? o1 - o0 : 0;
-        if (mode == kWgrad) cnt = (int32_t)((m + wblk - 1) / wblk);   // contraction blocks (prefix -> c_g)
-        else cnt = (int32_t)((m + BM - 1) / BM) * nt_count;
-      }
-      int32_t incl = cnt;
-#pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        int32_t t = __shfl_up(incl, d, 64);
-        if (lane >= d) incl += t;
-      }
-      if (g <= G) pre[g] = carry + incl - cnt;
-      carry += __shfl(incl, 63, 64);
-    }
-  }
-  __syncthreads();
-  TileInfo ti;
-  ti.valid = false;
-  ti.nblk = 0;
-  ti.col0 = 0;
-  ti.rows = 0;
-  ti.row0 = 0;
-  const int64_t t = blockIdx.x;
-  if (mode == kWgrad) {
-    const int per_g = (int)(p.N / BM) * (int)(p.K / BN);
-    const int g = (int)(t / per_g);
-    if (g >= G) return ti;
-    const int lt = (int)(t % per_g);
-    const int ntc = (int)(p.K / BN);
-    ti.g = g;
-    ti.mt = lt / ntc;
-    ti.nt = lt % ntc;
-    ti.col0 = (int64_t)wblk * pre[g];
-    int64_t o0 = rowstart[g], o1 = rowstart[g + 1];
-    ti.nblk = o1 > o0 ? (int)((o1 - o0 + wblk - 1) / wblk) : 0;
-    ti.row0 = o0;
-    ti.rows = (int)(o1 > o0 ? o1 - o0 : 0);   // contraction length m_g
-    ti.valid = true;
-    return ti;
-  }
-  if (t >= pre[G]) return ti;
-  int lo = 0, hi = G - 1;
-  while (lo < hi) {
-    int mid = (lo + hi + 1) >> 1;
-    if (pre[mid] <= t) lo = mid; else hi = mid - 1;
-  }
-  const int g = lo;
-  const int lt = (int)(t - pre[g]);
-  ti.g = g;
-  ti.mt = lt / nt_count;
-  ti.nt = lt % nt_count;
-  ti.row0 = rowstart[g] + (int64_t)ti.mt * BM;
-  int64_t left = rowstart[g + 1] - ti.row0;
-  ti.rows = (int)(left < BM ? left : BM);
-  ti.valid = ti.rows > 0;
-  return ti;
-}
-
-// LDS byte offset of 16-byte chunk c of tile row r (8 chunks per 128-byte row).
-__device__ __forceinline__ int lds_off(int r, int c) { return r * BK + ((c ^ (r & 7)) << 4); }
-
-// Eight E4M3 bytes -> eight bf16 multiplied by the power of two whose exponent field is that of
-// `scale` (1.0 here: the fp32 scales are applied at promotion); exact.
-__device__ __forceinline__ v8bf widen8(uint2 w, float scale) {
-  const v2bf a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, scale, false);
-  const v2bf b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, scale, true);
-  const v2bf c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, scale, false);
-  const v2bf d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, scale, true);
-  return v8bf{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
-}
+__device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
+__device__ __forceinline__ int lds_off(int r, int c) { return r * BK + ((c ^ swz(r)) << 4); }
 
 template <int MODE, int FEED>
-__device__ __forceinline__ void gemm_tile(const GemmArgs& p, const TileInfo& ti, uint8_t* ldsA, uint8_t* ldsB,
-                                          uint32_t* ldsSA, uint32_t* ldsSB) {
+__device__ __forceinline__ void bw_tile(const GemmArgs& p, const GroupTile& t, char* lds) {
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int lane = tid & 63, w = tid >> 6;
+  const int wm = w / kWavesN, wn = w % kWavesN;
+  const int lr = lane & 31, h = lane >> 5;
 
-  // ---- per-tile operand geometry ------------------------------------------------------------
-  // A rows: forward/dgrad -> token rows (clamped to the expert's last row); wgrad -> n rows
-  // B rows: forward -> gN + j; dgrad -> k rows of W^c (column offset gN); wgrad -> k rows (col c_g)
-  int64_t a_col0 = 0, b_col0 = 0;
-  constexpr int WBLK = 128;   // wgrad contraction block (128 tokens)
-  int64_t L;   // contraction length in bytes (multiple of 128 for forward/dgrad)
+  // ---- geometry (contraction offsets in bytes) ------------------------------------------------
+  int64_t L;
   if (MODE == kFwd) L = p.K;
   else if (MODE == kDgrad) L = p.N;
-  else L = (int64_t)WBLK * ti.nblk;
-  if (MODE == kDgrad) b_col0 = (int64_t)ti.g * p.N;
-  int nblk = ti.nblk;
-  if (MODE == kWgrad) {
-    a_col0 = ti.col0;
-    b_col0 = ti.col0;
-    // offsets that are not monotone could place an expert past the leading dimension: clip
-    const int64_t room = p.lda > a_col0 ? (p.lda - a_col0) / WBLK : 0;
-    if (nblk > room) nblk = (int)room;
-    L = (int64_t)WBLK * nblk;
-  }
-  const int nsteps = (int)((L + BK - 1) / BK);
+  else L = (int64_t)BK * t.nblk;                 // whole 128-token blocks (pad columns hold zero codes)
+  const int nsteps = (int)(L / BK);
+  const int64_t a_col0 = MODE == kWgrad ? t.col0 : 0;
+  const int64_t b_col0 = MODE == kWgrad ? t.col0 : (MODE == kDgrad ? (int64_t)t.g * p.N : 0);
+  auto a_row = [&](int r) -> int64_t {
+    if (MODE == kWgrad) return min((int64_t)t.mt * BM + r, p.N - 1);
+    return t.row0 + min(r, t.rows - 1);
+  };
+  auto b_row = [&](int r) -> int64_t {
+    const int64_t n = min((int64_t)t.nt * BN + r, (MODE == kFwd ? p.N : p.K) - 1);
+    return MODE == kFwd ? (int64_t)t.g * p.N + n : n;
+  };
 
-  // global load assignment: chunk id c = tid + 256 j (j = 0..3): row c / 8, chunk c % 8
-  const int ld_row = tid >> 3, ld_ch = tid & 7;
-  const uint8_t* a_ptr[4];
-  const uint8_t* b_ptr[4];
+  // operand loads: wave w moves A rows [kRowsA w, +kRowsA) and B rows [kRowsB w, +kRowsB), 8 rows per
+  // instruction; lane l lands in row (base + l / 8) at chunk position l % 8, which holds logical chunk
+  // (l % 8) ^ swz(row)
+  const int drow_a = kRowsA * w + (lane >> 3), drow_b = kRowsB * w + (lane >> 3);
+  const uint8_t* a_base = p.a + a_row(0) * p.lda + a_col0;
+  const uint8_t* b_base = p.b + b_row(0) * p.ldb + b_col0;
+  uint32_t a_off[NDA], b_off[NDB];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    int r = ld_row + 32 * j;
-    int64_t arow;
-    if (MODE == kWgrad) arow = (int64_t)ti.mt * BM + r;
-    else arow = ti.row0 + (r < ti.rows ? r : ti.rows - 1);
-    a_ptr[j] = p.a + arow * p.lda + a_col0 + ld_ch * 16;
-    int64_t brow;
-    if (MODE == kFwd) brow = (int64_t)ti.g * p.N + (int64_t)ti.nt * BN + r;
-    else brow = (int64_t)ti.nt * BN + r;
-    b_ptr[j] = p.b + brow * p.ldb + b_col0 + ld_ch * 16;
+  for (int j = 0; j < NDA; ++j)
+    a_off[j] = (uint32_t)((a_row(drow_a + 8 * j) - a_row(0)) * p.lda) + 16 * ((lane & 7) ^ swz(drow_a + 8 * j));
+#pragma unroll
+  for (int j = 0; j < NDB; ++j)
+    b_off[j] = (uint32_t)((b_row(drow_b + 8 * j) - b_row(0)) * p.ldb) + 16 * ((lane & 7) ^ swz(drow_b + 8 * j));
+  // fp32 scales, one dword per stage: waves 0-3 load the A row scales of rows [64 w, 64 w + 64); for wgrad
+  // waves 4-5 the B row scales of rows [64 (w - 4), +64); for forward / dgrad lane 0 of wave 4 the tile's
+  // block scale.  Each lands at its row's dword of the stage's scale area.
+  const float* sa = (const float*)p.sa;
+  const float* sb = (const float*)p.sb;
+  const float* s_src = nullptr;
+  int s_dst = -1;
+  if (w < 4) {
+    s_src = sa + a_row(64 * w + lane) * p.ldsa + a_col0 / BK;
+    s_dst = kScaleA + 256 * w;
+  } else if (MODE == kWgrad && w < 6) {
+    s_src = sb + b_row(64 * (w - 4) + lane) * p.ldsb + b_col0 / BK;
+    s_dst = kScaleB + 256 * (w - 4);
+  } else if (MODE != kWgrad && w == 4) {
+    // forward: block (gN + 128 nt) / 128 of the weight rows, slice ks; dgrad: block row gN / 128 + ks
+    // (the n-slice), column nt (the tile's k block)
+    if (MODE == kFwd) s_src = sb + (((int64_t)t.g * p.N) / BN + t.nt) * p.ldsb;
+    else s_src = sb + (((int64_t)t.g * p.N) / BK) * p.ldsb + t.nt;
+    s_dst = kScaleBlk;
   }
-  // scale rows: threads 0..127 -> A row tid, 128..255 -> B row tid-128
-  const bool s_is_a = tid < 128;
-  const int s_r = tid & 127;
-  int64_t s_row;
-  if (s_is_a) {
-    if (MODE == kWgrad) s_row = (int64_t)ti.mt * BM + s_r;
-    else s_row = ti.row0 + (s_r < ti.rows ? s_r : ti.rows - 1);
-  } else {
-    if (MODE == kFwd) s_row = (int64_t)ti.g * p.N + (int64_t)ti.nt * BN + s_r;
-    else s_row = (int64_t)ti.nt * BN + s_r;
-  }
-  const int64_t s_ld = s_is_a ? p.ldsa : p.ldsb;
-  const int64_t s_col0 = (s_is_a ? a_col0 : b_col0) / 128;
+  const int64_t s_step = MODE == kDgrad && w == 4 ? p.ldsb : 1;   // floats between the stages' scales
 
-  uint4 ra[4], rb[4];
-  uint32_t rs = 0;
-
-  auto load_step = [&](int ks) {
+  auto issue = [&](int ks) {
+    char* st = lds + (ks & 1) * kStage;
+    char* ss = lds + 2 * kStage + (ks & 1) * kScaleStage;
     const int64_t koff = (int64_t)ks * BK;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      bool ok = true;
-      if (MODE == kWgrad) ok = (koff + ld_ch * 16) < L;     // chunk inside the expert's blocks
-      ra[j] = ok ? *(const uint4*)(a_ptr[j] + koff) : make_uint4(0, 0, 0, 0);
-      rb[j] = ok ? *(const uint4*)(b_ptr[j] + koff) : make_uint4(0, 0, 0, 0);
-    }
-    // A row scales; wgrad also B row scales (forward / dgrad read the B block scale per tile)
-    const float* sp = (const float*)(s_is_a ? p.sa : p.sb);
-    if (s_is_a || MODE == kWgrad) rs = __float_as_uint(sp[s_row * s_ld + s_col0 + ks]);
-  };
-  auto store_step = [&]() {
+    for (int j = 0; j < NDA; ++j) dma16s(a_off[j], a_base + koff, st + (kRowsA * w + 8 * j) * BK);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      int r = ld_row + 32 * j;
-      *(uint4*)(ldsA + lds_off(r, ld_ch)) = ra[j];
-      *(uint4*)(ldsB + lds_off(r, ld_ch)) = rb[j];
+    for (int j = 0; j < NDB; ++j) dma16s(b_off[j], b_base + koff, st + kStageA + (kRowsB * w + 8 * j) * BK);
+    if (s_dst >= 0) {
+      if (MODE == kWgrad || w < 4) dma4((const uint8_t*)(s_src + ks), ss + s_dst);
+      else if (lane == 0) dma4((const uint8_t*)(s_src + ks * s_step), ss + s_dst);
     }
-    if (s_is_a) ldsSA[s_r] = rs;
-    else if (MODE == kWgrad) ldsSB[s_r] = rs;
   };
 
-  v4f acc[4][4];
+  // ---- accumulators and the promoted partials -----------------------------------------------
+  v16f acc[NI][NJ], part[NI][NJ];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < NI; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  const int fr = lane & 15, fg = lane >> 4;
-  if (nsteps > 0) load_step(0);
+  if (nsteps > 0) issue(0);
   for (int ks = 0; ks < nsteps; ++ks) {
-    store_step();
-    __syncthreads();
-    if (ks + 1 < nsteps) load_step(ks + 1);
-
-    // blockwise: fp32 weight-block scale of this step (one per 128x128 block)
-    float sbw = 1.f;
-    float rsc[4][4], csc[4];
-    {
-      const float* sw = (const float*)p.sb;
-      if (MODE == kFwd) sbw = sw[(((int64_t)ti.g * p.N + (int64_t)ti.nt * BN) / 128) * p.ldsb + ks];
-      else if (MODE == kDgrad) sbw = sw[(((int64_t)ti.g * p.N) / 128 + ks) * p.ldsb + ti.nt];
-      // promotion factors of the lane's four output rows per A fragment (times the weight-block scale)
+    stage_barrier();                               // stage ks landed; stage ks-1 fully read
+    constexpr bool kLateIssue = FEED == kFeedPrecise;
+    if (!kLateIssue && ks + 1 < nsteps) issue(ks + 1);
+    const char* A = lds + (ks & 1) * kStage;
+    const char* B = A + kStageA;
+    const v16f zero = {};                          // the slice's first MFMAs start from 0 (no zeroing pass)
+    if constexpr (FEED == kFeedPrecise) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int bb = 0; bb < 4; ++bb) {
+        v8bf alo[NI], ahi[NI], blo[NJ], bhi[NJ];
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          rsc[i][q] = __uint_as_float(ldsSA[wm * 64 + i * 16 + 4 * fg + q]) * sbw;
-      // wgrad: the lane's output column of each B fragment has its own scale (the X row scale)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) csc[j] = MODE == kWgrad ? __uint_as_float(ldsSB[wn * 64 + j * 16 + fr]) : 1.f;
-    }
-
-    if (FEED == kFeedPrecise) {
-      // four bf16 MFMAs of K = 32 per step: lane group fg supplies bytes [8 fg, 8 fg + 8) of each
-      // 32-element piece, widened exactly to bf16, so every product is exact and the MFMA sums them at
-      // fp32 precision into the slice's partial
-      v4f part[4][4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) part[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        v8bf af[4], bfr[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = wm * 64 + i * 16 + fr;
-          const uint2 w = *(const uint2*)(ldsA + lds_off(r, 2 * kb + (fg >> 1)) + 8 * (fg & 1));
-          af[i] = widen8(w, 1.0f);
+        for (int i = 0; i < NI; ++i) {
+          const uint4 v = *(const uint4*)(A + lds_off(WM * wm + 32 * i + lr, 2 * bb + h));
+          alo[i] = widen8(v.x, v.y, 1.0f);
+          ahi[i] = widen8(v.z, v.w, 1.0f);
         }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int r = wn * 64 + j * 16 + fr;
-          const uint2 w = *(const uint2*)(ldsB + lds_off(r, 2 * kb + (fg >> 1)) + 8 * (fg & 1));
-          bfr[j] = widen8(w, 1.0f);
+        for (int j = 0; j < NJ; ++j) {
+          const uint4 v = *(const uint4*)(B + lds_off(WN * wn + 32 * j + lr, 2 * bb + h));
+          blo[j] = widen8(v.x, v.y, 1.0f);
+          bhi[j] = widen8(v.z, v.w, 1.0f);
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < NI; ++i)
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
-            part[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], part[i][j], 0, 0, 0);
+          for (int j = 0; j < NJ; ++j)
+            part[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(blo[j], alo[i], bb == 0 ? zero : part[i][j], 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < NI; ++i)
+#pragma unroll
+          for (int j = 0; j < NJ; ++j)
+            part[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bhi[j], ahi[i], part[i][j], 0, 0, 0);
+        if (kLateIssue && bb == 0 && ks + 1 < nsteps) issue(ks + 1);
       }
-      // promotion of the slice's partial with its two fp32 scales
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const float f = MODE == kWgrad ? rsc[i][q] * csc[j] : rsc[i][q];
-            acc[i][j][q] = __builtin_fmaf(part[i][j][q], f, acc[i][j][q]);
-          }
     } else {
-      // full-rate FP8 MFMA (unit scales), K = 128 per instruction: one unscaled partial per slice
-      v8i af[4], bf[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = wm * 64 + i * 16 + fr;
-        v4i lo = *(const v4i*)(ldsA + lds_off(r, fg));
-        v4i hi = *(const v4i*)(ldsA + lds_off(r, 4 + fg));
-        af[i] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      }
+      for (int ks2 = 0; ks2 < 2; ++ks2) {
+        v8i bf[NJ];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = wn * 64 + i * 16 + fr;
-        v4i lo = *(const v4i*)(ldsB + lds_off(r, fg));
-        v4i hi = *(const v4i*)(ldsB + lds_off(r, 4 + fg));
-        bf[i] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      }
-      // promotion: unscaled partial over this 128-slice, then fp32 FMA with the two scales
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const v4f part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[i], bf[j], v4f{0.f, 0.f, 0.f, 0.f},
-                                                                            0, 0, 0, 127, 0, 127);
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const float f = MODE == kWgrad ? rsc[i][q] * csc[j] : rsc[i][q];
-            acc[i][j][q] = __builtin_fmaf(part[q], f, acc[i][j][q]);
-          }
+        for (int j = 0; j < NJ; ++j) {
+          const int r = WN * wn + 32 * j + lr;
+          const v4i lo = *(const v4i*)(B + lds_off(r, 4 * ks2 + h));
+          const v4i hi = *(const v4i*)(B + lds_off(r, 4 * ks2 + 2 + h));
+          bf[j] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         }
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+          const int r = WM * wm + 32 * i + lr;
+          const v4i lo = *(const v4i*)(A + lds_off(r, 4 * ks2 + h));
+          const v4i hi = *(const v4i*)(A + lds_off(r, 4 * ks2 + 2 + h));
+          const v8i af = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+#pragma unroll
+          for (int j = 0; j < NJ; ++j)
+            part[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf[j], af, ks2 == 0 ? zero : part[i][j], 0, 0,
+                                                                          0, 127, 0, 127);
+        }
+      }
     }
-    __syncthreads();
+    // promotion.  The MFMAs take the B fragment first, so lane l holds output row (A row) l % 32 of each
+    // fragment, and per group of four registers four consecutive output columns 8q + 4h .. + 3.
+    const char* S = lds + 2 * kStage + (ks & 1) * kScaleStage;
+    float fa[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) fa[i] = *(const float*)(S + kScaleA + 4 * (WM * wm + 32 * i + lr));
+    if constexpr (MODE == kWgrad) {
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float4 cb = *(const float4*)(S + kScaleB + 4 * (WN * wn + 32 * j + 8 * q + 4 * h));
+          const float cbv[4] = {cb.x, cb.y, cb.z, cb.w};
+#pragma unroll
+          for (int i = 0; i < NI; ++i)
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+              acc[i][j][4 * q + k] = __builtin_fmaf(part[i][j][4 * q + k], fa[i] * cbv[k], acc[i][j][4 * q + k]);
+        }
+    } else {
+      const float fb = *(const float*)(S + kScaleBlk);
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const float fi = fa[i] * fb;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[i][j][r] = __builtin_fmaf(part[i][j][r], fi, acc[i][j][r]);
+      }
+    }
   }
 
-  // ---- epilogue: lane holds rows 4*(l/16)+q of each 16x16 sub-tile, column l%16 --------------
-  const int64_t nout = (MODE == kFwd) ? p.N : p.K;
+  // ---- epilogue: 8-byte (bf16) or 16-byte (fp32) pieces, one base address per lane -------------
+  const int64_t nout = MODE == kFwd ? p.N : p.K;
+  const int row_lim = (int)min((int64_t)BM, MODE == kWgrad ? p.N - (int64_t)t.mt * BM : (int64_t)t.rows);
+  const int col_lim = (int)min((int64_t)BN, nout - (int64_t)t.nt * BN);
+  const int64_t out_row0 = MODE == kWgrad ? (int64_t)t.g * p.N + (int64_t)t.mt * BM : t.row0;
+  const int lrow = WM * wm + lr;
+  const int lcol = WN * wn + 4 * h;
+  const int64_t base = (out_row0 + lrow) * nout + (int64_t)t.nt * BN + lcol;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < NI; ++i) {
+    if (lrow + 32 * i >= row_lim) continue;
+    const int64_t rbase = base + (int64_t)(32 * i) * nout;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int r = wm * 64 + i * 16 + 4 * fg + q;
-        const int c = wn * 64 + j * 16 + fr;
-        int64_t idx;
-        if (MODE == kWgrad) {
-          idx = ((int64_t)ti.g * p.N + (int64_t)ti.mt * BM + r) * p.K + (int64_t)ti.nt * BN + c;
+        const int co = 32 * j + 8 * q;
+        if (lcol + co >= col_lim) continue;
+        const int64_t idx = rbase + co;
+        const float v0 = acc[i][j][4 * q], v1 = acc[i][j][4 * q + 1];
+        const float v2 = acc[i][j][4 * q + 2], v3 = acc[i][j][4 * q + 3];
+        if (p.out_bf16) {
+          const uint2 wv = make_uint2(f32_to_bf16_bits(v0) | (f32_to_bf16_bits(v1) << 16),
+                                      f32_to_bf16_bits(v2) | (f32_to_bf16_bits(v3) << 16));
+          *(uint2*)((uint16_t*)p.out + idx) = wv;
         } else {
-          if (r >= ti.rows) continue;
-          idx = (ti.row0 + r) * nout + (int64_t)ti.nt * BN + c;
+          *(float4*)((float*)p.out + idx) = make_float4(v0, v1, v2, v3);
         }
-        const float v = acc[i][j][q];
-        if (p.out_bf16) ((uint16_t*)p.out)[idx] = (uint16_t)f32_to_bf16_bits(v);
-        else ((float*)p.out)[idx] = v;
       }
+  }
 }
 
 template <int MODE, int FEED>
-__global__ __launch_bounds__(kThreads, 2) void grouped_gemm_kernel(GemmArgs p) {
-  __shared__ int32_t pre[kMaxGroups + 1];
-  __shared__ int64_t rowstart[kMaxGroups + 1];
-  __shared__ __attribute__((aligned(16))) uint8_t ldsA[BM * BK];
-  __shared__ __attribute__((aligned(16))) uint8_t ldsB[BN * BK];
-  __shared__ uint32_t ldsSA[BM];
-  __shared__ uint32_t ldsSB[BN];
-  const TileInfo ti = decode_tile(MODE, 128, p, pre, rowstart);
-  if (!ti.valid) return;   // uniform across the workgroup
-  gemm_tile<MODE, FEED>(p, ti, ldsA, ldsB, ldsSA, ldsSB);
+__global__ __launch_bounds__(NT, 1) void bw_grouped_gemm_kernel(GemmArgs p) {
+  __shared__ __attribute__((aligned(16))) char lds[kLds];
+  GroupTile t;
+  if (!decode_grouped_tile<MODE, MODE == kWgrad, BM, BN, NT, BK>(p, lds, t)) return;   // uniform
+  t.g = __builtin_amdgcn_readfirstlane(t.g);
+  t.mt = __builtin_amdgcn_readfirstlane(t.mt);
+  t.nt = __builtin_amdgcn_readfirstlane(t.nt);
+  t.rows = __builtin_amdgcn_readfirstlane(t.rows);
+  t.nblk = __builtin_amdgcn_readfirstlane(t.nblk);
+  t.row0 = uniform64(t.row0);
+  t.col0 = uniform64(t.col0);
+  __syncthreads();                               // scheduler scratch is reused for operands
+  bw_tile<MODE, FEED>(p, t, lds);
 }
 
-static int64_t tile_upper_bound(int mode, const GemmArgs& p) {
-  if (mode == kWgrad) return (int64_t)p.G * (p.N / BM) * (p.K / BN);
-  const int64_t ntc = (mode == kFwd ? p.N : p.K) / BN;
-  return ((p.M + BM - 1) / BM + p.G) * ntc;   // sum_g ceil(m_g/BM) <= ceil(M/BM) + G
+int64_t bw_tile_count_bound(int mode, const GemmArgs& p) {
+  if (mode == kWgrad) return (int64_t)p.G * ((p.N + BM - 1) / BM) * ((p.K + BN - 1) / BN);
+  const int64_t ntc = ((mode == kFwd ? p.N : p.K) + BN - 1) / BN;
+  return ((p.M + BM - 1) / BM + p.G) * ntc;     // sum_g ceil(m_g / BM) <= ceil(M / BM) + G
 }
 
 template <int MODE>
-static void launch_feed(const GemmArgs& p, dim3 grid, dim3 block, hipStream_t st) {
-  if (p.feed == kFeedFast) hipLaunchKernelGGL((grouped_gemm_kernel<MODE, kFeedFast>), grid, block, 0, st, p);
-  else hipLaunchKernelGGL((grouped_gemm_kernel<MODE, kFeedPrecise>), grid, block, 0, st, p);
+void bw_launch_mode(const GemmArgs& p, dim3 grid, hipStream_t st) {
+  if (p.feed == kFeedFast) hipLaunchKernelGGL((bw_grouped_gemm_kernel<MODE, kFeedFast>), grid, dim3(NT), 0, st, p);
+  else hipLaunchKernelGGL((bw_grouped_gemm_kernel<MODE, kFeedPrecise>), grid, dim3(NT), 0, st, p);
 }
 
+}  // namespace
+
 hipError_t launch_bw_gemm(int mode, const GemmArgs& p, hipStream_t st) {
-  const int64_t tiles = tile_upper_bound(mode, p);
+  const int64_t tiles = bw_tile_count_bound(mode, p);
   if (tiles == 0) return hipSuccess;
-  dim3 grid((unsigned)tiles), block(kThreads);
-  if (mode == kFwd) launch_feed<kFwd>(p, grid, block, st);
-  else if (mode == kDgrad) launch_feed<kDgrad>(p, grid, block, st);
-  else launch_feed<kWgrad>(p, grid, block, st);
+  const int64_t per = (int64_t)kXcd * kChunk;
+  const int64_t grid = (tiles + per - 1) / per * per;
+  if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const dim3 g((unsigned)grid);
+  if (mode == kFwd) bw_launch_mode<kFwd>(p, g, st);
+  else if (mode == kDgrad) bw_launch_mode<kDgrad>(p, g, st);
+  else bw_launch_mode<kWgrad>(p, g, st);
   return hipGetLastError();
 }
 

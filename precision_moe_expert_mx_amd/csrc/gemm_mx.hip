@@ -43,10 +43,12 @@
 // (zeros for an empty one), experts taken largest first.  Inside an expert tiles are rasterised in
 // columns of four A tiles; consecutive chunks of 8 tiles go to the same XCD (workgroups are
 // dispatched round-robin over the 8 XCDs) so that tiles sharing operands share an L2.
-#include "common.h"
+#include "grouped_tile.h"
 
 namespace mxmoe {
 namespace {
+
+using Tile = GroupTile;
 
 #ifndef MXMOE_WAVES_M
 #define MXMOE_WAVES_M 2
@@ -72,176 +74,17 @@ constexpr int kStage = kStageA + BN * BK;        // 64 KiB
 constexpr int kScaleStage = (BM + BN) * 4;       // four E8M0 bytes per operand row (E4M3)
 constexpr int kScaleStage4 = (BM + BN) * 8;      // eight E8M0 bytes per operand row (E2M1), two dword planes
 constexpr int kLds = 2 * kStage + 2 * kScaleStage4;
-constexpr int kMaxG = 1024;
-constexpr int kXcd = 8;
-constexpr int kChunk = 8;
-constexpr int kGroupM = 4;
-constexpr int kLptMaxG = 256;                    // wgrad orders experts by size up to this G
 #ifndef MXMOE_LDS_SWZ
 #define MXMOE_LDS_SWZ(r) (((r) >> 1) & 7)
 #endif
 
 typedef float v16f __attribute__((ext_vector_type(16)));
 
-struct Tile {
-  int g, mt, nt;
-  int64_t row0;   // forward / dgrad: first A row of the tile
-  int rows;       // forward / dgrad: valid A rows (1..256)
-  int64_t col0;   // wgrad, gated forward: first column of the expert in the column-wise layout
-  int nblk;       // wgrad: 32-blocks in the expert's contraction
-  int64_t col_end;  // gated forward: columns of the column-wise layout holding blocks (32 x all blocks)
-};
 
 // LDS rows of 128 bytes; 16-byte chunk c of row r sits at chunk position c ^ swz(r), so that the
 // lanes of one 16-byte LDS read (consecutive rows, same logical chunk) hit distinct banks.
 __device__ __forceinline__ int swz(int r) { return MXMOE_LDS_SWZ(r); }
 __device__ __forceinline__ int lds_off(int r, int c) { return r * BK + ((c ^ swz(r)) << 4); }
-
-__device__ __forceinline__ int cdiv(int64_t a, int b) { return (int)((a + b - 1) / b); }
-
-__device__ __forceinline__ int64_t uniform64(int64_t v) {
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
-  return (int64_t)(((uint64_t)hi << 32) | lo);
-}
-
-// Tile list of the launch and this workgroup's tile.  Scratch arrays live at the start of the LDS
-// (before the first operand load overwrites them).  Returns false when the workgroup has no tile.
-// CB: also the first 32-block of each expert in the column-wise layout (wgrad; the gated forward's
-// column-wise H).
-template <int MODE, bool CB>
-__device__ bool decode_tile(const GemmArgs& p, char* lds, Tile& t) {
-  int32_t* s_rs = (int32_t*)lds;             // clamped offsets [G+1]
-  int32_t* s_pre = s_rs + (kMaxG + 1);       // tile prefix over the processing order [G+1]
-  int32_t* s_cb = s_pre + (kMaxG + 1);       // wgrad: first 32-block of each expert [G+1]
-  int32_t* s_ord = s_cb + (kMaxG + 1);       // processing order [G]
-  const int G = p.G;
-  const int tid = threadIdx.x;
-  const int64_t M = p.M;
-  for (int g = tid; g <= G; g += NT) s_rs[g] = (int32_t)clamp_off(p.offs[g], M);
-  __syncthreads();
-  const bool lpt = MODE == kWgrad && G <= kLptMaxG;
-  for (int g = tid; g < G; g += NT) {
-    int pos = g;
-    if (lpt) {
-      const int mg = max(s_rs[g + 1] - s_rs[g], 0);
-      pos = 0;
-      for (int h = 0; h < G; ++h) {
-        const int mh = max(s_rs[h + 1] - s_rs[h], 0);
-        pos += (mh > mg) || (mh == mg && h < g);
-      }
-    }
-    s_ord[pos] = g;
-  }
-  __syncthreads();
-  const int ntc = cdiv(MODE == kFwd ? p.N : p.K, BN);
-  const int mtc_w = cdiv(p.N, BM);
-  const int lane = tid & 63;
-  if (tid < 64 || (CB && tid < 128)) {
-    const bool tiles = tid < 64;
-    int carry = 0;
-    for (int base = 0; base < G; base += 64) {
-      const int q = base + lane;
-      int c = 0;
-      if (q < G) {
-        if (tiles) {
-          const int g = s_ord[q];
-          if (MODE == kWgrad) c = mtc_w * ntc;
-          else c = cdiv(max(s_rs[g + 1] - s_rs[g], 0), BM) * ntc;
-        } else {
-          c = cdiv(max(s_rs[q + 1] - s_rs[q], 0), 32);
-        }
-      }
-      int incl = c;
-#pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        const int v = __shfl_up(incl, d, 64);
-        if (lane >= d) incl += v;
-      }
-      if (q < G) (tiles ? s_pre : s_cb)[q] = carry + incl - c;
-      carry += __shfl(incl, 63, 64);
-    }
-    if (lane == 0) (tiles ? s_pre : s_cb)[G] = carry;
-  }
-  __syncthreads();
-
-  // workgroup -> logical tile: chunks of kChunk consecutive tiles per XCD visit
-  const int b = blockIdx.x;
-  const int x = b % kXcd, q = b / kXcd;
-  const int lt_all = ((q / kChunk) * kXcd + x) * kChunk + (q % kChunk);
-  if (lt_all >= s_pre[G]) return false;
-  int lo = 0, hi = G - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (s_pre[mid] <= lt_all) lo = mid; else hi = mid - 1;
-  }
-  const int g = s_ord[lo];
-  const int lt = lt_all - s_pre[lo];
-  const int m_g = max(s_rs[g + 1] - s_rs[g], 0);
-  const int mtc = MODE == kWgrad ? mtc_w : cdiv(m_g, BM);
-  const int span = kGroupM * ntc;
-  const int sg = lt / span;
-  const int fm = sg * kGroupM;
-  const int gsz = min(mtc - fm, kGroupM);
-  const int r = lt - sg * span;
-  t.g = g;
-  t.mt = fm + r % gsz;
-  t.nt = r / gsz;
-  t.row0 = s_rs[g] + (int64_t)t.mt * BM;
-  t.rows = (int)min((int64_t)BM, (int64_t)s_rs[g + 1] - t.row0);
-  t.col0 = CB ? 32 * (int64_t)s_cb[g] : 0;
-  t.col_end = CB ? 32 * (int64_t)s_cb[G] : 0;
-  t.nblk = cdiv(m_g, 32);
-  if (MODE == kWgrad) {
-    // offsets that are not monotone could place an expert past the leading dimension: clip (lda is
-    // in bytes; an E2M1 block is 16 bytes)
-    const int64_t ld_el = p.fp4 ? 2 * p.lda : p.lda;
-    const int64_t room = ld_el > t.col0 ? (ld_el - t.col0) / 32 : 0;
-    if (t.nblk > room) t.nblk = (int)room;
-  }
-  return true;
-}
-
-// Eight E4M3 bytes -> eight bf16 multiplied by 2^(e-127), e the E8M0 byte whose bits sit in the
-// exponent field of `scale`; exact for every product the GEMMs form.
-__device__ __forceinline__ v8bf widen8(uint32_t w0, uint32_t w1, float scale) {
-  const v2bf a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, scale, false);
-  const v2bf b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, scale, true);
-  const v2bf c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, scale, false);
-  const v2bf d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, scale, true);
-  return v8bf{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
-}
-
-__device__ __forceinline__ float e8m0_as_scale(uint32_t word, int b) {
-  return __uint_as_float(((word >> (8 * b)) & 0xFFu) << 23);
-}
-
-// Direct global -> LDS loads.  Lane l writes its bytes at LDS address m0 + size * l, m0 being the
-// wave-uniform base.  Issued from inline assembly so that the compiler does not treat them as LDS
-// stores it must wait for before every later LDS read: the kernel orders them itself (stage_barrier).
-// Nothing else in these kernels uses m0.
-__device__ __forceinline__ uint32_t lds_addr(const char* p) { return (uint32_t)(uintptr_t)p; }
-
-__device__ __forceinline__ void dma16(const uint8_t* g, const char* lds_wave_base) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
-               :: "s"(__builtin_amdgcn_readfirstlane(lds_addr(lds_wave_base))), "v"(g) : "memory", "m0");
-}
-// The same load addressed as a wave-uniform 64-bit base (scalar registers) plus a 32-bit lane offset:
-// per stage only the base moves (scalar adds), the lane offsets are formed once per tile.
-__device__ __forceinline__ void dma16s(uint32_t off, const uint8_t* base, const char* lds_wave_base) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
-               :: "s"(__builtin_amdgcn_readfirstlane(lds_addr(lds_wave_base))), "v"(off), "s"(base) : "memory", "m0");
-}
-__device__ __forceinline__ void dma4(const uint8_t* g, const char* lds_wave_base) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off"
-               :: "s"(__builtin_amdgcn_readfirstlane(lds_addr(lds_wave_base))), "v"(g) : "memory", "m0");
-}
-
-// Wait for this wave's outstanding loads and LDS operations, then the workgroup barrier.  The memory
-// clobber keeps the compiler from moving LDS accesses across it.
-__device__ __forceinline__ void stage_barrier() {
-  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
 
 // Gated forward epilogue (precise feed, 32x32 fragments, 8 waves 2 x 4).  Waves wn = 0, 1 hold the
 // gate columns of the tile's 128 hidden units, waves 2, 3 the up columns of the same units.  Every
@@ -528,7 +371,7 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const Tile& t, char*
     char* ss = lds + 2 * kStage + (ks & 1) * kSStage;
     const int64_t koff = (int64_t)ks * BK;
     // wgrad: chunks outside the expert's blocks, bytes [lim_lo, lim_hi) of the stage's rows, are not
-    // loaded (zeroed after landing)
+    // loaded (zeroed where they would have landed)
     const int lim_hi = (int)min(L - koff, (int64_t)BK);
     const int lim_lo = ks == 0 ? (int)L0 : 0;
 #pragma unroll
@@ -780,7 +623,7 @@ template <int MODE, int FEED, bool SDW, bool FP4 = false, bool ACT = false>
 __global__ __launch_bounds__(NT, 1) void mx_grouped_gemm_kernel(GemmArgs p) {
   __shared__ __attribute__((aligned(16))) char lds[kLds];
   Tile t;
-  if (!decode_tile<MODE, MODE == kWgrad || ACT>(p, lds, t)) return;     // uniform across the workgroup
+  if (!decode_grouped_tile<MODE, MODE == kWgrad || ACT, BM, BN, NT, 32>(p, lds, t)) return;     // uniform across the workgroup
   // the tile's fields are the same in every lane: say so, so that everything derived from them (operand
   // bases, loop bounds) lives in scalar registers
   t.g = __builtin_amdgcn_readfirstlane(t.g);

@@ -281,6 +281,36 @@ def test_blockwise_gemms():
         print("bw dgrad", _check(_gpu_out(dx), ref, bnd, "f32", "bw dgrad"))
 
 
+def test_blockwise_fp8_feed():
+    """The blockwise GEMMs on the full-rate FP8 feed (each slice's partial from the block-scaled MFMA
+    with unit scales, then promoted) against the oracle within that feed's bound; ragged experts."""
+    m = require_gpu()
+    rng = np.random.default_rng(48)
+    L = _rand_layer(rng, [0, 5, 130, 1, 300], 256, 384, w_std=0.02, outliers=0.001)
+    offs = dev(L.offs)
+    qx, sx = m.fp8bw_quantize_act_1x128(dev(L.x))
+    qw, sw, qwT = m.fp8bw_quantize_weight_128x128(dev(L.w), transposed=True)
+    same_bytes((host(qx), host(sx)), oracle.bw_quantize_act_1x128(L.x), "bw X 1x128")
+    wq = oracle.bw_quantize_weight_128x128(L.w)
+    same_bytes((host(qw), host(sw), host(qwT)), (wq[0], wq[1], wq[0].T), "bw W 128x128")
+    y = m.fp8bw_grouped_gemm_fwd(qx, sx, qw, sw, offs, L.N, fast=True)
+    ref, bnd = oracle.bw_gemm_fwd(host(qx), host(sx), host(qw), host(sw), L.offs, L.N)
+    print("bw fast fwd", _check(_gpu_out(y), ref, bnd, "f32", "bw fast fwd", rel=FAST_REL))
+    qd, sd = m.fp8bw_quantize_act_1x128(dev(L.dy))
+    same_bytes((host(qd), host(sd)), oracle.bw_quantize_act_1x128(L.dy), "bw dY 1x128")
+    dx = m.fp8bw_grouped_gemm_dgrad(qd, sd, qwT, sw, offs, L.K, fast=True)
+    ref, bnd = oracle.bw_gemm_dgrad(host(qd), host(sd), host(qw), host(sw), L.offs, L.N, L.K)
+    print("bw fast dgrad", _check(_gpu_out(dx), ref, bnd, "f32", "bw fast dgrad", rel=FAST_REL))
+    ld = oracle.bw_colwise_ld_min(L.M, L.G)
+    qdT, sdT = m.fp8bw_quantize_colwise_128(dev(L.dy), offs, ld=ld)
+    qxT, sxT = m.fp8bw_quantize_colwise_128(dev(L.x), offs, ld=ld)
+    same_bytes((host(qdT), host(sdT)), oracle.bw_quantize_colwise_128(L.dy, L.offs, ld), "bw dY 128-token")
+    same_bytes((host(qxT), host(sxT)), oracle.bw_quantize_colwise_128(L.x, L.offs, ld), "bw X 128-token")
+    dw = m.fp8bw_grouped_gemm_wgrad(qdT, sdT, qxT, sxT, offs, L.M, "f32", fast=True)
+    ref, bnd = oracle.bw_gemm_wgrad(host(qdT), host(sdT), host(qxT), host(sxT), L.offs, L.N, L.K)
+    print("bw fast wgrad", _check(_gpu_out(dw), ref, bnd, "f32", "bw fast wgrad", rel=FAST_REL))
+
+
 def test_blockwise_full_size_sampled():
     """The blockwise recipe on the DeepSeek-V3-16B layer tensors (sampled rows)."""
     m = require_gpu()
