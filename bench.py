@@ -40,7 +40,7 @@ MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "mxfp8": 5000.0, "mxfp4": 10100.0}
 QUANT_BYTES_PER_ELEM = 2.0 + 1.0 + 1.0 / 32.0   # bf16 in, E4M3 out, one E8M0 per 32
 DUAL_BYTES_PER_ELEM = 2.0 + 2.0 * (1.0 + 1.0 / 32.0)   # bf16 in once, both MX layouts out
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_traffic_dsv3_671b_shard.txt")
-GEMM_SOURCES = [os.path.join(ROOT, "precision_moe_expert_mx_amd", "csrc", f) for f in ("gemm_mx.hip", "common.h")]
+GEMM_SOURCES = [os.path.join(ROOT, "precision_moe_expert_mx_amd", "csrc", f) for f in ("gemm_mx.hip", "grouped_tile.h", "common.h")]
 
 
 def log(*a):
@@ -167,10 +167,8 @@ def build_step_ops(m, torch, layers, dev_ins):
                2.0 * M * N * K, "grouped_gemm fwd + SwiGLU + MX(H) both layouts")
     fused.bytes = (M * K + G * N * K) * mxb + M * N * 2 + 2 * M * H * mxb
     fused.peak_tflops = MFMA_PEAK_TFLOPS["bf16"]
-    order = ["gate_up.quant_x_dual", "gate_up.quant_w_dual", None, "down.quant_w_dual", "down.fwd",
-             "down.quant_dy_dual", "down.dgrad", "down.wgrad", "gate_up.quant_dy_dual", "gate_up.dgrad",
-             "gate_up.wgrad"]
-    ops = [fused if n is None else by[n] for n in order]
+    by[fused.name] = fused
+    ops = [by[n] for n in STEP_ORDER]
     return ops, (gb, db)
 
 
@@ -230,8 +228,12 @@ def op_summary(op):
 # covers and is ignored once they change.
 QUANT_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "quant_traffic_dsv3_671b_shard.txt")
 QUANT_SOURCES = [os.path.join(ROOT, "precision_moe_expert_mx_amd", "csrc", f) for f in ("quant_mx.hip", "common.h")]
-GEMM_NAMES = [f"{l}.{k}" for l in ("gate_up", "down") for k in ("fwd", "dgrad", "wgrad")]
-QUANT_NAMES = [f"{l}.quant_{t}_dual" for l in ("gate_up", "down") for t in ("x", "w", "dy")]
+# the step's launches in order (build_step_ops): the profile summaries map kernel dispatches to these
+STEP_ORDER = ["gate_up.quant_x_dual", "gate_up.quant_w_dual", "gate_up.fwd_swiglu", "down.quant_w_dual", "down.fwd",
+              "down.quant_dy_dual", "down.dgrad", "down.wgrad", "gate_up.quant_dy_dual", "gate_up.dgrad",
+              "gate_up.wgrad"]
+GEMM_NAMES = [n for n in STEP_ORDER if "quant" not in n]
+QUANT_NAMES = [n for n in STEP_ORDER if "quant" in n]
 
 
 def quant_source_hash() -> str:
@@ -258,8 +260,8 @@ def read_traffic(path=TRAFFIC_FILE, src_hash=None):
 
 
 def pmc_summary(fetch_csv: str, write_csv: str, cmds) -> None:
-    """Per-launch HBM bytes of the six GEMM launches and the six dual-layout quantiser launches of a
-    step from two rocprofv3 counter runs of this script (FETCH_SIZE, then WRITE_SIZE, KiB per
+    """Per-launch HBM bytes of the GEMM launches and the dual-layout quantiser launches of a step
+    (STEP_ORDER) from two rocprofv3 counter runs of this script (FETCH_SIZE, then WRITE_SIZE, KiB per
     dispatch), each scaled by what the same counter reads for the 1 GiB device copy the script
     performs before timing."""
     import csv
@@ -288,7 +290,7 @@ def pmc_summary(fetch_csv: str, write_csv: str, cmds) -> None:
                "fetch": {n: round(float(np.mean(c["FETCH_SIZE"]))) for n, c in sel.items()},
                "write": {n: round(float(np.mean(c["WRITE_SIZE"]))) for n, c in sel.items()}}
         with open(path, "w") as f:
-            f.write(f"# HBM traffic per launch of the six {what} launches of one step (DeepSeek-V3-671B expert shard)\n")
+            f.write(f"# HBM traffic per launch of the {len(names)} {what} launches of one step (DeepSeek-V3-671B expert shard)\n")
             f.write("# bytes = counter KiB * 1024 * (2^30 / counter KiB of the 1 GiB device copy); commands (repository root):\n")
             for c in cmds:
                 f.write(f"#   {c}\n")
@@ -312,7 +314,7 @@ def mfma_summary(pmc_dir: str, cmds) -> None:
     from workloads import layer_shapes
     flops = {}
     for name, M, N, K in layer_shapes("dsv3_671b_shard"):
-        for k in ("fwd", "dgrad", "wgrad"):
+        for k in ("fwd", "fwd_swiglu", "dgrad", "wgrad"):
             flops[f"{name}.{k}"] = 2.0 * M * N * K
     per_disp = {}
     for r in csv.DictReader(open(os.path.join(pmc_dir, "p_counter_collection.csv"))):

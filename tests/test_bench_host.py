@@ -33,8 +33,9 @@ def test_pmc_summary_maps_dispatches_and_calibrates(tmp_path, monkeypatch):
     gemm = "void mxmoe::(anonymous namespace)::mx_grouped_gemm_kernel<0, 0, true, false, false>(mxmoe::GemmArgs)"
     quant = "void mxmoe::mx_colwise_kernel<true, false, true, false>(...)"
     copy = "__amd_rocclr_copyBuffer"
-    # step order of one layer: quant x, quant w, fwd, quant dy, dgrad, wgrad; two layers
-    order = [quant, quant, gemm, quant, gemm, gemm] * 2
+    # the step's launch order (bench.STEP_ORDER): quantisers and GEMMs of both layers interleaved
+    order = [quant if "quant" in n else gemm for n in bench.STEP_ORDER]
+    assert len(order) == 11 and order.count(gemm) == 6
     fetch_kib = 2 * (1 << 20)            # the 1 GiB copy reads as 2 GiB: factor 1/2
     write_kib = 1 << 20
     fetch = [(copy, 8.0), (copy, fetch_kib)] + [(n, 1000.0 * (i + 1)) for i, n in enumerate(order)]
@@ -86,7 +87,7 @@ def test_layer_shapes_match_the_workloads():
 def test_mfma_summary_clock_and_utilisation(tmp_path, monkeypatch):
     gemm = "void mxmoe::(anonymous namespace)::mx_grouped_gemm_kernel<0, 0, true, false, false>(mxmoe::GemmArgs)"
     quant = "void mxmoe::mx_colwise_kernel<true, false, true, false>(...)"
-    order = [quant, quant, gemm, quant, gemm, gemm] * 2
+    order = [quant if "quant" in n else gemm for n in bench.STEP_ORDER] * 2
     ns = {}
     with open(tmp_path / "p_counter_collection.csv", "w", newline="") as f:
         w = csv.DictWriter(f, fieldnames=["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
@@ -107,12 +108,17 @@ def test_mfma_summary_clock_and_utilisation(tmp_path, monkeypatch):
     bench.mfma_summary(str(tmp_path), ["cmd"])
     rec = json.loads(out.read_text().splitlines()[-1])
     gemm_disp = [i for i, n in enumerate(order, start=1) if n == gemm]
-    shapes = {f"{l}.{k}": 2.0 * M * N * K for l, M, N, K in bench_shapes() for k in ("fwd", "dgrad", "wgrad")}
-    for name, i in zip(bench.GEMM_NAMES, gemm_disp):
+    shapes = {f"{l}.{k}": 2.0 * M * N * K for l, M, N, K in bench_shapes()
+              for k in ("fwd", "fwd_swiglu", "dgrad", "wgrad")}
+    assert len(gemm_disp) == 2 * len(bench.GEMM_NAMES)
+    for j, name in enumerate(bench.GEMM_NAMES):
+        # two steps: each op's figures are the mean over its two launches
+        i, i2 = gemm_disp[j], gemm_disp[j + len(bench.GEMM_NAMES)]
         o = rec["ops"][name]
-        assert o["clock_ghz"] == 2.0 and o["us"] == round(ns[i] / 1e3, 1)
-        assert o["mfma_util"] == round((50.0 + i) / 100, 4)
-        tf = shapes[name] / (ns[i] * 1e-9) / 1e12
+        t = (ns[i] + ns[i2]) / 2
+        assert abs(o["clock_ghz"] - 2.0) < 1e-9 and o["us"] == round(t / 1e3, 1)
+        assert o["mfma_util"] == round((50.0 + (i + i2) / 2) / 100, 4)
+        tf = shapes[name] / (t * 1e-9) / 1e12
         assert abs(o["tflops"] - round(tf, 1)) < 1e-9
         assert abs(o["frac_of_rate_at_clock"] - round(tf / (1024 * 1024 * 2.0e9 / 1e12), 4)) < 1e-9
 
