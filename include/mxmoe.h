@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define MXMOE_ABI_VERSION 2
+#define MXMOE_ABI_VERSION 3
 
 typedef enum {
   MXMOE_OK = 0,
@@ -217,6 +217,56 @@ mxmoe_status mx_grouped_gemm_wgrad_fp8feed(const uint8_t* qdyT, const uint8_t* s
                                            const uint8_t* qxT, const uint8_t* sxT, int64_t ld,
                                            const int32_t* offs, int32_t G, int64_t M, int64_t N, int64_t K,
                                            void* dw, mxmoe_dtype dwdt, void* stream);
+
+/* ---------------------------------------------------------------- 128-byte tiled column-wise layout
+ * A layout option for the column-wise E4M3 copies (an addition of this library: the pages fix what a
+ * column-wise copy holds, not how it is laid out).  The bytes of a copy qT [C, ld] (row c = column c
+ * of the source, byte j = group-blocked position j, as mx_quantize_colwise defines them) are stored as
+ * ld / 128 tiles of C x 128 bytes:
+ *     byte (c, j)  at  (j / 128) * C * 128 + c * 128 + (j % 128),      ld % 128 == 0,
+ * so one 128-byte slice of the contraction for all C rows is one contiguous block of memory: the
+ * quantiser writes whole tiles, and the GEMMs load a 128-byte stage of a row from one place.  The
+ * buffer has the same size (C * ld bytes); the scales sT [C, ld/32] keep their row-major layout.
+ * Each entry point below takes exactly the arguments, and validates them as, its row-major namesake,
+ * with ld (ldh, ldw) % 128 == 0 required in addition (MXMOE_ERR_ALIGN for the quantisers,
+ * MXMOE_ERR_SHAPE for the GEMMs); results are the same bytes / values permuted as above:
+ *   mx_quantize_colwise_tiled, mx_quantize_dual_tiled   qT in the tiled layout (q, s, sT unchanged);
+ *   mx_grouped_gemm_fwd_swiglu_tiled                    qhT tiled ([ldh/128][H][128]); qhT and shT
+ *                                                       are required;
+ *   mx_grouped_gemm_dgrad_tiled[_fp8feed]               qwT tiled ([ldw/128][K][128]);
+ *   mx_grouped_gemm_wgrad_tiled[_fp8feed]               qdyT and qxT tiled ([ld/128][N][128],
+ *                                                       [ld/128][K][128]).
+ * The GEMM results are bit-identical to the row-major entry points on the same data (the same
+ * products are summed in the same order). */
+mxmoe_status mx_quantize_colwise_tiled(const void* x_bf16, int64_t R, int64_t C,
+                                       const int32_t* offs, int32_t G,
+                                       uint8_t* qT, uint8_t* sT, int64_t ld, void* stream);
+mxmoe_status mx_quantize_dual_tiled(const void* x_bf16, int64_t R, int64_t C,
+                                    const int32_t* row_idx, int64_t R_src,
+                                    const int32_t* offs, int32_t G,
+                                    uint8_t* q, uint8_t* s,
+                                    uint8_t* qT, uint8_t* sT, int64_t ld, void* stream);
+mxmoe_status mx_grouped_gemm_fwd_swiglu_tiled(const uint8_t* qx, const uint8_t* sx,
+                                              const uint8_t* qw, const uint8_t* sw,
+                                              const int32_t* offs, int32_t G, int64_t M, int64_t N,
+                                              int64_t K, void* y, uint8_t* qh, uint8_t* sh, float* h,
+                                              uint8_t* qhT, uint8_t* shT, int64_t ldh, void* stream);
+mxmoe_status mx_grouped_gemm_dgrad_tiled(const uint8_t* qdy, const uint8_t* sdy,
+                                         const uint8_t* qwT, const uint8_t* swT, int64_t ldw,
+                                         const int32_t* offs, int32_t G, int64_t M, int64_t N, int64_t K,
+                                         void* dx, mxmoe_dtype dxdt, void* stream);
+mxmoe_status mx_grouped_gemm_dgrad_tiled_fp8feed(const uint8_t* qdy, const uint8_t* sdy,
+                                                 const uint8_t* qwT, const uint8_t* swT, int64_t ldw,
+                                                 const int32_t* offs, int32_t G, int64_t M, int64_t N,
+                                                 int64_t K, void* dx, mxmoe_dtype dxdt, void* stream);
+mxmoe_status mx_grouped_gemm_wgrad_tiled(const uint8_t* qdyT, const uint8_t* sdyT,
+                                         const uint8_t* qxT, const uint8_t* sxT, int64_t ld,
+                                         const int32_t* offs, int32_t G, int64_t M, int64_t N, int64_t K,
+                                         void* dw, mxmoe_dtype dwdt, void* stream);
+mxmoe_status mx_grouped_gemm_wgrad_tiled_fp8feed(const uint8_t* qdyT, const uint8_t* sdyT,
+                                                 const uint8_t* qxT, const uint8_t* sxT, int64_t ld,
+                                                 const int32_t* offs, int32_t G, int64_t M, int64_t N,
+                                                 int64_t K, void* dw, mxmoe_dtype dwdt, void* stream);
 
 /* ---------------------------------------------------------------- MXFP4
  * The MX scheme with E2M1 elements (OCP MX v1.0 "MXFP4": sign, 2 exponent bits,

@@ -257,6 +257,25 @@ def mx_quantize_colwise_values(v, offs, ld: int):
     return qT, sT
 
 
+TILE = 128
+
+
+def mx_colwise_tiled(qT):
+    """A column-wise copy qT [C, ld] in the library's 128-byte tiled layout (a layout option of the
+    library, not something the pages define; the permutation is the library's stated contract): tile t
+    holds columns [128 t, 128 t + 128) of every row, row c of the tile being bytes 128 t .. 128 t + 127
+    of qT's row c, so byte (c, j) lands at flat position (j // 128) * C * 128 + c * 128 + j % 128.
+    Returns [ld // 128, C, 128] of the same dtype; ld % 128 == 0."""
+    qT = np.asarray(qT)
+    C, ld = qT.shape
+    if ld % TILE:
+        raise ValueError("the tiled layout needs ld % 128 == 0")
+    out = np.empty((ld // TILE, C, TILE), dtype=qT.dtype)
+    for t in range(ld // TILE):
+        out[t] = qT[:, TILE * t:TILE * (t + 1)]
+    return out
+
+
 def swiglu(gate, up):
     """Gated activation of an expert's gate+up output: silu(gate) * up, silu(z) = z / (1 + e^-z).
 

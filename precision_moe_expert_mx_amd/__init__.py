@@ -19,6 +19,8 @@ __all__ = [
     "mx_colwise_ld_min", "mxmoe_pitch", "mx_colwise_ld", "mxfp4_colwise_ld",
     "mx_quantize_rowwise", "mx_quantize_colwise", "mx_quantize_dual",
     "mx_grouped_gemm_fwd", "mx_grouped_gemm_dgrad", "mx_grouped_gemm_wgrad", "mx_grouped_gemm_fwd_swiglu",
+    "mx_quantize_colwise_tiled", "mx_quantize_dual_tiled", "mx_grouped_gemm_fwd_swiglu_tiled",
+    "mx_grouped_gemm_dgrad_tiled", "mx_grouped_gemm_wgrad_tiled",
     "fp8bw_quantize_act_1x128", "fp8bw_quantize_weight_128x128",
     "fp8bw_grouped_gemm_fwd", "fp8bw_grouped_gemm_dgrad", "mxmoe_check_offsets",
     "fp8bw_colwise_ld_min", "fp8bw_quantize_colwise_128", "fp8bw_grouped_gemm_wgrad",
@@ -71,9 +73,14 @@ _SIGS = {
                                                 _p]),
     "mxmoe_check_offsets": (ctypes.c_int, [_p, _i32, _i64, _p]),
 }
+# the 128-byte tiled column-wise layout: the same arguments as the row-major entry points
+for _n in ("mx_quantize_colwise", "mx_quantize_dual", "mx_grouped_gemm_fwd_swiglu", "mx_grouped_gemm_dgrad",
+           "mx_grouped_gemm_wgrad"):
+    _SIGS[_n + "_tiled"] = _SIGS[_n]
 # the full-rate FP8 operand feed: the same arguments as the precise entry points
 for _n in ("mx_grouped_gemm_fwd", "mx_grouped_gemm_dgrad", "mx_grouped_gemm_wgrad", "fp8bw_grouped_gemm_fwd",
-           "fp8bw_grouped_gemm_dgrad", "fp8bw_grouped_gemm_wgrad"):
+           "fp8bw_grouped_gemm_dgrad", "fp8bw_grouped_gemm_wgrad", "mx_grouped_gemm_dgrad_tiled",
+           "mx_grouped_gemm_wgrad_tiled"):
     _SIGS[_n + "_fp8feed"] = _SIGS[_n]
 EXPORTED_SYMBOLS = tuple(_SIGS)
 
@@ -201,8 +208,13 @@ def mx_quantize_rowwise(x, q=None, s=None, stream=None) -> Tuple[object, object]
     return q, s
 
 
-def mx_quantize_colwise(x, offs=None, G: int = 1, ld: Optional[int] = None, qT=None, sT=None, stream=None):
-    """x bf16 [R, C] -> (qT uint8 [C, ld], sT uint8 [C, ld/32]); offs int32 [G+1] device or None."""
+def _colwise_out(C, ld, tiled, like):
+    """A column-wise code buffer: [C, ld] row-major, or [ld / 128, C, 128] in the tiled layout."""
+    torch = _torch()
+    return _empty((ld // 128, C, 128) if tiled else (C, ld), torch.uint8, like)
+
+
+def _colwise(name, tiled, x, offs, G, ld, qT, sT, stream):
     torch = _torch()
     x = _bf16_bits(x)
     R, C = x.shape
@@ -210,19 +222,23 @@ def mx_quantize_colwise(x, offs=None, G: int = 1, ld: Optional[int] = None, qT=N
         G = offs.numel() - 1
     if ld is None:
         ld = mx_colwise_ld(R, G if offs is not None else None)
-    qT = _empty((C, ld), torch.uint8, x) if qT is None else qT
+    qT = _colwise_out(C, ld, tiled, x) if qT is None else qT
     sT = _empty((C, ld // 32), torch.uint8, x) if sT is None else sT
-    _check("mx_quantize_colwise", lib().mx_quantize_colwise(_ptr(x), R, C, _ptr(offs), G, _ptr(qT), _ptr(sT), ld,
-                                                            _stream_handle(stream)))
+    _check(name, getattr(lib(), name)(_ptr(x), R, C, _ptr(offs), G, _ptr(qT), _ptr(sT), ld, _stream_handle(stream)))
     return qT, sT
 
 
-def mx_quantize_dual(x, offs=None, G: int = 1, ld: Optional[int] = None, row_idx=None, q=None, s=None, qT=None,
-                     sT=None, stream=None):
-    """Row-wise and column-wise MX layouts from one read of x.
+def mx_quantize_colwise(x, offs=None, G: int = 1, ld: Optional[int] = None, qT=None, sT=None, stream=None):
+    """x bf16 [R, C] -> (qT uint8 [C, ld], sT uint8 [C, ld/32]); offs int32 [G+1] device or None."""
+    return _colwise("mx_quantize_colwise", False, x, offs, G, ld, qT, sT, stream)
 
-    x bf16 [R_src, C]; row_idx int32 [R] (routed row r reads x[row_idx[r]]) or None (R = R_src).
-    Returns (q [R, C], s [R, C/32], qT [C, ld], sT [C, ld/32]), all uint8."""
+
+def mx_quantize_colwise_tiled(x, offs=None, G: int = 1, ld: Optional[int] = None, qT=None, sT=None, stream=None):
+    """As mx_quantize_colwise with qT in the 128-byte tiled layout: qT uint8 [ld/128, C, 128]."""
+    return _colwise("mx_quantize_colwise_tiled", True, x, offs, G, ld, qT, sT, stream)
+
+
+def _dual(name, tiled, x, offs, G, ld, row_idx, q, s, qT, sT, stream):
     torch = _torch()
     x = _bf16_bits(x)
     R_src, C = x.shape
@@ -233,11 +249,26 @@ def mx_quantize_dual(x, offs=None, G: int = 1, ld: Optional[int] = None, row_idx
         ld = mx_colwise_ld(R, G if offs is not None else None)
     q = _empty((R, C), torch.uint8, x) if q is None else q
     s = _empty((R, C // 32), torch.uint8, x) if s is None else s
-    qT = _empty((C, ld), torch.uint8, x) if qT is None else qT
+    qT = _colwise_out(C, ld, tiled, x) if qT is None else qT
     sT = _empty((C, ld // 32), torch.uint8, x) if sT is None else sT
-    _check("mx_quantize_dual", lib().mx_quantize_dual(_ptr(x), R, C, _ptr(row_idx), R_src, _ptr(offs), G, _ptr(q),
-                                                      _ptr(s), _ptr(qT), _ptr(sT), ld, _stream_handle(stream)))
+    _check(name, getattr(lib(), name)(_ptr(x), R, C, _ptr(row_idx), R_src, _ptr(offs), G, _ptr(q), _ptr(s), _ptr(qT),
+                                      _ptr(sT), ld, _stream_handle(stream)))
     return q, s, qT, sT
+
+
+def mx_quantize_dual(x, offs=None, G: int = 1, ld: Optional[int] = None, row_idx=None, q=None, s=None, qT=None,
+                     sT=None, stream=None):
+    """Row-wise and column-wise MX layouts from one read of x.
+
+    x bf16 [R_src, C]; row_idx int32 [R] (routed row r reads x[row_idx[r]]) or None (R = R_src).
+    Returns (q [R, C], s [R, C/32], qT [C, ld], sT [C, ld/32]), all uint8."""
+    return _dual("mx_quantize_dual", False, x, offs, G, ld, row_idx, q, s, qT, sT, stream)
+
+
+def mx_quantize_dual_tiled(x, offs=None, G: int = 1, ld: Optional[int] = None, row_idx=None, q=None, s=None,
+                           qT=None, sT=None, stream=None):
+    """As mx_quantize_dual with qT in the 128-byte tiled layout: qT uint8 [ld/128, C, 128]."""
+    return _dual("mx_quantize_dual_tiled", True, x, offs, G, ld, row_idx, q, s, qT, sT, stream)
 
 
 # ---------------------------------------------------------------- MX grouped GEMMs
@@ -252,13 +283,7 @@ def mx_grouped_gemm_fwd(qx, sx, qw, sw, offs, N: int, out_dtype: str = "f32", y=
     return y
 
 
-def mx_grouped_gemm_fwd_swiglu(qx, sx, qw, sw, offs, N: int, y=None, qh=None, sh=None, h=None,
-                               with_h: bool = False, colwise: bool = False, ldh: Optional[int] = None, qhT=None,
-                               shT=None, stream=None):
-    """Forward of the gate+up GEMM (W rows: gate then up of each expert, N = 2H) with SwiGLU and the
-    MX quantisation of H in the epilogue.  Returns (y bf16 [M, N], qh [M, H], sh [M, H/32]); with
-    colwise (or qhT given) also H column-wise (qhT [H, ldh], shT [H, ldh/32], ldh by default the
-    recommended pitch for the routing offsets); with with_h (or h given) H in fp32 [M, H] last."""
+def _swiglu(name, tiled, qx, sx, qw, sw, offs, N, y, qh, sh, h, with_h, colwise, ldh, qhT, shT, stream):
     torch = _torch()
     M, K = qx.shape
     G = offs.numel() - 1
@@ -268,43 +293,83 @@ def mx_grouped_gemm_fwd_swiglu(qx, sx, qw, sw, offs, N: int, y=None, qh=None, sh
     sh = _empty((M, H // 32), torch.uint8, qx) if sh is None else sh
     if with_h and h is None:
         h = _empty((M, H), torch.float32, qx)
-    if colwise or qhT is not None:
+    if colwise or tiled or qhT is not None:
         if qhT is not None:
-            ldh = qhT.shape[1]
+            ldh = qhT.shape[0] * 128 if tiled else qhT.shape[1]
         elif ldh is None:
             ldh = mx_colwise_ld(M, G)
-        qhT = _empty((H, ldh), torch.uint8, qx) if qhT is None else qhT
+        qhT = _colwise_out(H, ldh, tiled, qx) if qhT is None else qhT
         shT = _empty((H, ldh // 32), torch.uint8, qx) if shT is None else shT
-    _check("mx_grouped_gemm_fwd_swiglu", lib().mx_grouped_gemm_fwd_swiglu(
+    _check(name, getattr(lib(), name)(
         _ptr(qx), _ptr(sx), _ptr(qw), _ptr(sw), _ptr(offs), G, M, N, K, _ptr(y), _ptr(qh), _ptr(sh), _ptr(h),
         _ptr(qhT), _ptr(shT), int(ldh or 0), _stream_handle(stream)))
     out = (y, qh, sh) + ((qhT, shT) if qhT is not None else ())
     return out if h is None else out + (h,)
 
 
+def mx_grouped_gemm_fwd_swiglu(qx, sx, qw, sw, offs, N: int, y=None, qh=None, sh=None, h=None,
+                               with_h: bool = False, colwise: bool = False, ldh: Optional[int] = None, qhT=None,
+                               shT=None, stream=None):
+    """Forward of the gate+up GEMM (W rows: gate then up of each expert, N = 2H) with SwiGLU and the
+    MX quantisation of H in the epilogue.  Returns (y bf16 [M, N], qh [M, H], sh [M, H/32]); with
+    colwise (or qhT given) also H column-wise (qhT [H, ldh], shT [H, ldh/32], ldh by default the
+    recommended pitch for the routing offsets); with with_h (or h given) H in fp32 [M, H] last."""
+    return _swiglu("mx_grouped_gemm_fwd_swiglu", False, qx, sx, qw, sw, offs, N, y, qh, sh, h, with_h, colwise, ldh,
+                   qhT, shT, stream)
+
+
+def mx_grouped_gemm_fwd_swiglu_tiled(qx, sx, qw, sw, offs, N: int, y=None, qh=None, sh=None, h=None,
+                                     with_h: bool = False, ldh: Optional[int] = None, qhT=None, shT=None,
+                                     stream=None):
+    """As mx_grouped_gemm_fwd_swiglu, always with H column-wise, qhT in the 128-byte tiled layout
+    ([ldh/128, H, 128]).  Returns (y, qh, sh, qhT, shT[, h])."""
+    return _swiglu("mx_grouped_gemm_fwd_swiglu_tiled", True, qx, sx, qw, sw, offs, N, y, qh, sh, h, with_h, True,
+                   ldh, qhT, shT, stream)
+
+
 def mx_grouped_gemm_dgrad(qdy, sdy, qwT, swT, offs, K: int, out_dtype: str = "f32", dx=None, stream=None, fast: bool = False):
     """dX [M, K] = per-expert dY_g W_g from row-wise dY and column-wise W ([K, ldw])."""
+    return _dgrad("mx_grouped_gemm_dgrad", qwT.shape[1], qdy, sdy, qwT, swT, offs, K, out_dtype, dx, stream, fast)
+
+
+def mx_grouped_gemm_dgrad_tiled(qdy, sdy, qwT, swT, offs, K: int, out_dtype: str = "f32", dx=None, stream=None,
+                                fast: bool = False):
+    """As mx_grouped_gemm_dgrad with qwT in the 128-byte tiled layout ([ldw/128, K, 128])."""
+    return _dgrad("mx_grouped_gemm_dgrad_tiled", qwT.shape[0] * 128, qdy, sdy, qwT, swT, offs, K, out_dtype, dx,
+                  stream, fast)
+
+
+def _dgrad(name, ldw, qdy, sdy, qwT, swT, offs, K, out_dtype, dx, stream, fast):
     M, N = qdy.shape
     G = offs.numel() - 1
-    ldw = qwT.shape[1]
     tdt, cdt = _out_dtype(out_dtype)
     dx = _empty((M, K), tdt, qdy) if dx is None else dx
-    _check(*_call(_gemm("mx_grouped_gemm_dgrad", fast), _ptr(qdy), _ptr(sdy), _ptr(qwT), _ptr(swT), ldw,
-                                                                _ptr(offs), G, M, N, K, _ptr(dx), cdt,
-                                                                _stream_handle(stream)))
+    _check(*_call(_gemm(name, fast), _ptr(qdy), _ptr(sdy), _ptr(qwT), _ptr(swT), ldw, _ptr(offs), G, M, N, K,
+                  _ptr(dx), cdt, _stream_handle(stream)))
     return dx
 
 
 def mx_grouped_gemm_wgrad(qdyT, sdyT, qxT, sxT, offs, M: int, out_dtype: str = "f32", dw=None, stream=None, fast: bool = False):
     """dW [G, N, K] = per-expert dY_g^T X_g from column-wise dY ([N, ld]) and X ([K, ld])."""
     N, ld = qdyT.shape
-    K = qxT.shape[0]
+    return _wgrad("mx_grouped_gemm_wgrad", N, ld, qxT.shape[0], qdyT, sdyT, qxT, sxT, offs, M, out_dtype, dw, stream,
+                  fast)
+
+
+def mx_grouped_gemm_wgrad_tiled(qdyT, sdyT, qxT, sxT, offs, M: int, out_dtype: str = "f32", dw=None, stream=None,
+                                fast: bool = False):
+    """As mx_grouped_gemm_wgrad with qdyT / qxT in the 128-byte tiled layout ([ld/128, N, 128],
+    [ld/128, K, 128])."""
+    return _wgrad("mx_grouped_gemm_wgrad_tiled", qdyT.shape[1], qdyT.shape[0] * 128, qxT.shape[1], qdyT, sdyT, qxT,
+                  sxT, offs, M, out_dtype, dw, stream, fast)
+
+
+def _wgrad(name, N, ld, K, qdyT, sdyT, qxT, sxT, offs, M, out_dtype, dw, stream, fast):
     G = offs.numel() - 1
     tdt, cdt = _out_dtype(out_dtype)
     dw = _empty((G, N, K), tdt, qdyT) if dw is None else dw
-    _check(*_call(_gemm("mx_grouped_gemm_wgrad", fast), _ptr(qdyT), _ptr(sdyT), _ptr(qxT), _ptr(sxT), ld,
-                                                                _ptr(offs), G, M, N, K, _ptr(dw), cdt,
-                                                                _stream_handle(stream)))
+    _check(*_call(_gemm(name, fast), _ptr(qdyT), _ptr(sdyT), _ptr(qxT), _ptr(sxT), ld, _ptr(offs), G, M, N, K,
+                  _ptr(dw), cdt, _stream_handle(stream)))
     return dw
 
 

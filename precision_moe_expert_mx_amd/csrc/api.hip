@@ -134,15 +134,16 @@ mxmoe_status mx_quantize_rowwise(const void* x, int64_t R, int64_t C, uint8_t* q
   return launched(launch_mx_rowwise((const uint16_t*)x, R, C, q, s, (hipStream_t)stream), fn);
 }
 
-mxmoe_status mx_quantize_colwise(const void* x, int64_t R, int64_t C, const int32_t* offs, int32_t G, uint8_t* qT,
-                                 uint8_t* sT, int64_t ld, void* stream) {
-  const char* fn = "mx_quantize_colwise";
+static mxmoe_status colwise_impl(const char* fn, const void* x, int64_t R, int64_t C, const int32_t* offs, int32_t G,
+                                 uint8_t* qT, uint8_t* sT, int64_t ld, bool tiled, void* stream) {
   if (R < 0 || C <= 0 || C % 32) return fail(MXMOE_ERR_SHAPE, "%s: need R >= 0, C > 0, C %% 32 == 0 (R=%lld C=%lld)",
                                             fn, (long long)R, (long long)C);
   if (R > INT32_MAX) return fail(MXMOE_ERR_SHAPE, "%s: R too large", fn);
   if (offs && (G < 1 || G > kMaxG)) return fail(MXMOE_ERR_SHAPE, "%s: G = %d outside [1, %d]", fn, (int)G, (int)kMaxG);
   if (ld <= 0 || ld % 32) return fail(MXMOE_ERR_ALIGN, "%s: ld must be a positive multiple of 32 (ld=%lld)", fn,
                                       (long long)ld);
+  if (tiled && ld % 128)
+    return fail(MXMOE_ERR_ALIGN, "%s: the tiled layout needs ld %% 128 == 0 (ld=%lld)", fn, (long long)ld);
   const int64_t need = offs ? mx_colwise_ld_min(R, G) : 32 * ((R + 31) / 32);
   if (ld < need) return fail(MXMOE_ERR_SHAPE, "%s: ld=%lld < required %lld", fn, (long long)ld, (long long)need);
   if (R > 0) TRY(check_ptr(fn, "x", x, 16));
@@ -150,19 +151,30 @@ mxmoe_status mx_quantize_colwise(const void* x, int64_t R, int64_t C, const int3
   TRY(check_ptr(fn, "qT", qT, 16));
   TRY(check_ptr(fn, "sT", sT, 4));
   TRY(check_device());
-  return launched(launch_mx_colwise((const uint16_t*)x, R, C, offs, G, qT, sT, ld, (hipStream_t)stream), fn);
+  return launched(launch_mx_colwise((const uint16_t*)x, R, C, offs, G, qT, sT, ld, tiled, (hipStream_t)stream), fn);
 }
 
-mxmoe_status mx_quantize_dual(const void* x, int64_t R, int64_t C, const int32_t* row_idx, int64_t R_src,
-                              const int32_t* offs, int32_t G, uint8_t* q, uint8_t* s, uint8_t* qT, uint8_t* sT,
-                              int64_t ld, void* stream) {
-  const char* fn = "mx_quantize_dual";
+mxmoe_status mx_quantize_colwise(const void* x, int64_t R, int64_t C, const int32_t* offs, int32_t G, uint8_t* qT,
+                                 uint8_t* sT, int64_t ld, void* stream) {
+  return colwise_impl("mx_quantize_colwise", x, R, C, offs, G, qT, sT, ld, false, stream);
+}
+
+mxmoe_status mx_quantize_colwise_tiled(const void* x, int64_t R, int64_t C, const int32_t* offs, int32_t G,
+                                       uint8_t* qT, uint8_t* sT, int64_t ld, void* stream) {
+  return colwise_impl("mx_quantize_colwise_tiled", x, R, C, offs, G, qT, sT, ld, true, stream);
+}
+
+static mxmoe_status dual_impl(const char* fn, const void* x, int64_t R, int64_t C, const int32_t* row_idx,
+                              int64_t R_src, const int32_t* offs, int32_t G, uint8_t* q, uint8_t* s, uint8_t* qT,
+                              uint8_t* sT, int64_t ld, bool tiled, void* stream) {
   if (R < 0 || C <= 0 || C % 32) return fail(MXMOE_ERR_SHAPE, "%s: need R >= 0, C > 0, C %% 32 == 0 (R=%lld C=%lld)",
                                             fn, (long long)R, (long long)C);
   if (R > INT32_MAX) return fail(MXMOE_ERR_SHAPE, "%s: R too large", fn);
   if (offs && (G < 1 || G > kMaxG)) return fail(MXMOE_ERR_SHAPE, "%s: G = %d outside [1, %d]", fn, (int)G, (int)kMaxG);
   if (ld <= 0 || ld % 32) return fail(MXMOE_ERR_ALIGN, "%s: ld must be a positive multiple of 32 (ld=%lld)", fn,
                                       (long long)ld);
+  if (tiled && ld % 128)
+    return fail(MXMOE_ERR_ALIGN, "%s: the tiled layout needs ld %% 128 == 0 (ld=%lld)", fn, (long long)ld);
   const int64_t need = offs ? mx_colwise_ld_min(R, G) : 32 * ((R + 31) / 32);
   if (ld < need) return fail(MXMOE_ERR_SHAPE, "%s: ld=%lld < required %lld", fn, (long long)ld, (long long)need);
   if (row_idx && R > 0 && R_src < 1)
@@ -178,8 +190,20 @@ mxmoe_status mx_quantize_dual(const void* x, int64_t R, int64_t C, const int32_t
   TRY(check_ptr(fn, "sT", sT, 4));
   TRY(check_device());
   return launched(launch_mx_dual((const uint16_t*)x, R, C, R > 0 ? row_idx : nullptr, row_idx ? R_src : R, offs, G, q,
-                                 s, qT, sT, ld, (hipStream_t)stream),
+                                 s, qT, sT, ld, tiled, (hipStream_t)stream),
                   fn);
+}
+
+mxmoe_status mx_quantize_dual(const void* x, int64_t R, int64_t C, const int32_t* row_idx, int64_t R_src,
+                              const int32_t* offs, int32_t G, uint8_t* q, uint8_t* s, uint8_t* qT, uint8_t* sT,
+                              int64_t ld, void* stream) {
+  return dual_impl("mx_quantize_dual", x, R, C, row_idx, R_src, offs, G, q, s, qT, sT, ld, false, stream);
+}
+
+mxmoe_status mx_quantize_dual_tiled(const void* x, int64_t R, int64_t C, const int32_t* row_idx, int64_t R_src,
+                                    const int32_t* offs, int32_t G, uint8_t* q, uint8_t* s, uint8_t* qT, uint8_t* sT,
+                                    int64_t ld, void* stream) {
+  return dual_impl("mx_quantize_dual_tiled", x, R, C, row_idx, R_src, offs, G, q, s, qT, sT, ld, true, stream);
 }
 
 // The GEMM addresses a tile's operand rows as 32-bit byte offsets from the tile's first row: 256 rows
@@ -196,7 +220,7 @@ static mxmoe_status check_strides(const char* fn, const GemmArgs& p, int64_t b_r
 static mxmoe_status mx_gemm_common(int mode, const char* fn, const uint8_t* a, const uint8_t* sa, const uint8_t* b,
                                    const uint8_t* sb, int64_t ldb_cols, const int32_t* offs, int32_t G, int64_t M,
                                    int64_t N, int64_t K, void* out, int dt, void* stream, int feed,
-                                   bool fp4 = false) {
+                                   bool fp4 = false, bool tiled = false) {
   TRY(check_gemm_common(fn, offs, G, M, N, K, out, dt));
   if (fp4 && (N % 256 || K % 256))
     return fail(MXMOE_ERR_SHAPE, "%s: MXFP4 needs N and K multiples of 256 (N=%lld K=%lld)", fn, (long long)N,
@@ -221,6 +245,14 @@ static mxmoe_status mx_gemm_common(int mode, const char* fn, const uint8_t* a, c
   } else {
     p.lda = ldb_cols / epb; p.ldsa = ldb_cols / 32; p.ldb = ldb_cols / epb; p.ldsb = ldb_cols / 32;
   }
+  p.a_kstride = p.b_kstride = 128;
+  if (tiled) {
+    // column-wise operands in the 128-byte tiled layout: rows 128 bytes apart, chunks rows * 128 apart
+    if (mode == kWgrad) {
+      p.lda = 128; p.a_kstride = 128 * N;
+    }
+    p.ldb = 128; p.b_kstride = 128 * K;
+  }
   TRY(check_strides(fn, p, 256));
   if (mode != kWgrad && M == 0) return ok();
   TRY(check_device());
@@ -241,11 +273,10 @@ mxmoe_status mx_grouped_gemm_fwd_fp8feed(const uint8_t* qx, const uint8_t* sx, c
                         stream, kFeedFast);
 }
 
-mxmoe_status mx_grouped_gemm_fwd_swiglu(const uint8_t* qx, const uint8_t* sx, const uint8_t* qw, const uint8_t* sw,
-                                        const int32_t* offs, int32_t G, int64_t M, int64_t N, int64_t K, void* y,
-                                        uint8_t* qh, uint8_t* sh, float* h, uint8_t* qhT, uint8_t* shT, int64_t ldh,
-                                        void* stream) {
-  const char* fn = "mx_grouped_gemm_fwd_swiglu";
+static mxmoe_status swiglu_impl(const char* fn, const uint8_t* qx, const uint8_t* sx, const uint8_t* qw,
+                                const uint8_t* sw, const int32_t* offs, int32_t G, int64_t M, int64_t N, int64_t K,
+                                void* y, uint8_t* qh, uint8_t* sh, float* h, uint8_t* qhT, uint8_t* shT, int64_t ldh,
+                                bool tiled, void* stream) {
   TRY(check_gemm_common(fn, offs, G, M, N, K, y, MXMOE_BF16));
   if (N % 256) return fail(MXMOE_ERR_SHAPE, "%s: N = 2H must be a multiple of 256 (N=%lld)", fn, (long long)N);
   TRY(check_ptr(fn, "A operand", qx, 16));
@@ -258,9 +289,11 @@ mxmoe_status mx_grouped_gemm_fwd_swiglu(const uint8_t* qx, const uint8_t* sx, co
   if ((qhT == nullptr) != (shT == nullptr)) return fail(MXMOE_ERR_NULL, "%s: qhT and shT go together", fn);
   if (qhT) {
     TRY(check_ptr(fn, "qhT", qhT, 16));
-    if (ldh % 32 || ldh < mx_colwise_ld_min(M, G))
-      return fail(MXMOE_ERR_SHAPE, "%s: ldh=%lld must be a multiple of 32 and >= mx_colwise_ld_min(M, G)=%lld", fn,
-                  (long long)ldh, (long long)mx_colwise_ld_min(M, G));
+    if (ldh % (tiled ? 128 : 32) || ldh < mx_colwise_ld_min(M, G))
+      return fail(MXMOE_ERR_SHAPE, "%s: ldh=%lld must be a multiple of %d and >= mx_colwise_ld_min(M, G)=%lld", fn,
+                  (long long)ldh, tiled ? 128 : 32, (long long)mx_colwise_ld_min(M, G));
+  } else if (tiled) {
+    return fail(MXMOE_ERR_NULL, "%s: the tiled variant writes H column-wise: qhT and shT are required", fn);
   }
   GemmArgs p;
   memset(&p, 0, sizeof p);
@@ -271,19 +304,39 @@ mxmoe_status mx_grouped_gemm_fwd_swiglu(const uint8_t* qx, const uint8_t* sx, co
   p.lda = K; p.ldsa = K / 32; p.ldb = K; p.ldsb = K / 32;
   p.act_q = qh; p.act_s = sh; p.act_dbg = h;
   p.act_qT = qhT; p.act_sT = shT; p.act_ld = ldh;
+  p.act_tiled = tiled;
+  p.a_kstride = p.b_kstride = 128;
   TRY(check_strides(fn, p, N));
   if (M == 0) return ok();
   TRY(check_device());
   return launched(launch_mx_gemm(kFwd, p, (hipStream_t)stream), fn);
 }
 
+mxmoe_status mx_grouped_gemm_fwd_swiglu(const uint8_t* qx, const uint8_t* sx, const uint8_t* qw, const uint8_t* sw,
+                                        const int32_t* offs, int32_t G, int64_t M, int64_t N, int64_t K, void* y,
+                                        uint8_t* qh, uint8_t* sh, float* h, uint8_t* qhT, uint8_t* shT, int64_t ldh,
+                                        void* stream) {
+  return swiglu_impl("mx_grouped_gemm_fwd_swiglu", qx, sx, qw, sw, offs, G, M, N, K, y, qh, sh, h, qhT, shT, ldh,
+                     false, stream);
+}
+
+mxmoe_status mx_grouped_gemm_fwd_swiglu_tiled(const uint8_t* qx, const uint8_t* sx, const uint8_t* qw,
+                                              const uint8_t* sw, const int32_t* offs, int32_t G, int64_t M, int64_t N,
+                                              int64_t K, void* y, uint8_t* qh, uint8_t* sh, float* h, uint8_t* qhT,
+                                              uint8_t* shT, int64_t ldh, void* stream) {
+  return swiglu_impl("mx_grouped_gemm_fwd_swiglu_tiled", qx, sx, qw, sw, offs, G, M, N, K, y, qh, sh, h, qhT, shT, ldh,
+                     true, stream);
+}
+
 static mxmoe_status mx_dgrad_impl(const char* fn, int feed, const uint8_t* qdy, const uint8_t* sdy,
                                   const uint8_t* qwT, const uint8_t* swT, int64_t ldw, const int32_t* offs, int32_t G,
-                                  int64_t M, int64_t N, int64_t K, void* dx, mxmoe_dtype dxdt, void* stream) {
-  if (ldw % 32 || ldw < (int64_t)G * N)
-    return fail(MXMOE_ERR_SHAPE, "%s: ldw=%lld must be a multiple of 32 and >= G*N=%lld", fn, (long long)ldw,
-                (long long)G * N);
-  return mx_gemm_common(kDgrad, fn, qdy, sdy, qwT, swT, ldw, offs, G, M, N, K, dx, (int)dxdt, stream, feed);
+                                  int64_t M, int64_t N, int64_t K, void* dx, mxmoe_dtype dxdt, void* stream,
+                                  bool tiled = false) {
+  if (ldw % (tiled ? 128 : 32) || ldw < (int64_t)G * N)
+    return fail(MXMOE_ERR_SHAPE, "%s: ldw=%lld must be a multiple of %d and >= G*N=%lld", fn, (long long)ldw,
+                tiled ? 128 : 32, (long long)G * N);
+  return mx_gemm_common(kDgrad, fn, qdy, sdy, qwT, swT, ldw, offs, G, M, N, K, dx, (int)dxdt, stream, feed, false,
+                        tiled);
 }
 
 mxmoe_status mx_grouped_gemm_dgrad(const uint8_t* qdy, const uint8_t* sdy, const uint8_t* qwT, const uint8_t* swT,
@@ -300,13 +353,30 @@ mxmoe_status mx_grouped_gemm_dgrad_fp8feed(const uint8_t* qdy, const uint8_t* sd
                        dxdt, stream);
 }
 
+mxmoe_status mx_grouped_gemm_dgrad_tiled(const uint8_t* qdy, const uint8_t* sdy, const uint8_t* qwT, const uint8_t* swT,
+                                         int64_t ldw, const int32_t* offs, int32_t G, int64_t M, int64_t N, int64_t K,
+                                         void* dx, mxmoe_dtype dxdt, void* stream) {
+  return mx_dgrad_impl("mx_grouped_gemm_dgrad_tiled", kFeedPrecise, qdy, sdy, qwT, swT, ldw, offs, G, M, N, K, dx,
+                       dxdt, stream, true);
+}
+
+mxmoe_status mx_grouped_gemm_dgrad_tiled_fp8feed(const uint8_t* qdy, const uint8_t* sdy, const uint8_t* qwT,
+                                                 const uint8_t* swT, int64_t ldw, const int32_t* offs, int32_t G,
+                                                 int64_t M, int64_t N, int64_t K, void* dx, mxmoe_dtype dxdt,
+                                                 void* stream) {
+  return mx_dgrad_impl("mx_grouped_gemm_dgrad_tiled_fp8feed", kFeedFast, qdy, sdy, qwT, swT, ldw, offs, G, M, N, K,
+                       dx, dxdt, stream, true);
+}
+
 static mxmoe_status mx_wgrad_impl(const char* fn, int feed, const uint8_t* qdyT, const uint8_t* sdyT,
                                   const uint8_t* qxT, const uint8_t* sxT, int64_t ld, const int32_t* offs, int32_t G,
-                                  int64_t M, int64_t N, int64_t K, void* dw, mxmoe_dtype dwdt, void* stream) {
-  if (G >= 1 && M >= 0 && (ld % 32 || ld < mx_colwise_ld_min(M, G)))
-    return fail(MXMOE_ERR_SHAPE, "%s: ld=%lld must be a multiple of 32 and >= mx_colwise_ld_min(M, G)=%lld", fn,
-                (long long)ld, (long long)mx_colwise_ld_min(M, G));
-  return mx_gemm_common(kWgrad, fn, qdyT, sdyT, qxT, sxT, ld, offs, G, M, N, K, dw, (int)dwdt, stream, feed);
+                                  int64_t M, int64_t N, int64_t K, void* dw, mxmoe_dtype dwdt, void* stream,
+                                  bool tiled = false) {
+  if (G >= 1 && M >= 0 && (ld % (tiled ? 128 : 32) || ld < mx_colwise_ld_min(M, G)))
+    return fail(MXMOE_ERR_SHAPE, "%s: ld=%lld must be a multiple of %d and >= mx_colwise_ld_min(M, G)=%lld", fn,
+                (long long)ld, tiled ? 128 : 32, (long long)mx_colwise_ld_min(M, G));
+  return mx_gemm_common(kWgrad, fn, qdyT, sdyT, qxT, sxT, ld, offs, G, M, N, K, dw, (int)dwdt, stream, feed, false,
+                        tiled);
 }
 
 mxmoe_status mx_grouped_gemm_wgrad(const uint8_t* qdyT, const uint8_t* sdyT, const uint8_t* qxT, const uint8_t* sxT,
@@ -321,6 +391,21 @@ mxmoe_status mx_grouped_gemm_wgrad_fp8feed(const uint8_t* qdyT, const uint8_t* s
                                            int64_t N, int64_t K, void* dw, mxmoe_dtype dwdt, void* stream) {
   return mx_wgrad_impl("mx_grouped_gemm_wgrad_fp8feed", kFeedFast, qdyT, sdyT, qxT, sxT, ld, offs, G, M, N, K, dw,
                        dwdt, stream);
+}
+
+mxmoe_status mx_grouped_gemm_wgrad_tiled(const uint8_t* qdyT, const uint8_t* sdyT, const uint8_t* qxT,
+                                         const uint8_t* sxT, int64_t ld, const int32_t* offs, int32_t G, int64_t M,
+                                         int64_t N, int64_t K, void* dw, mxmoe_dtype dwdt, void* stream) {
+  return mx_wgrad_impl("mx_grouped_gemm_wgrad_tiled", kFeedPrecise, qdyT, sdyT, qxT, sxT, ld, offs, G, M, N, K, dw,
+                       dwdt, stream, true);
+}
+
+mxmoe_status mx_grouped_gemm_wgrad_tiled_fp8feed(const uint8_t* qdyT, const uint8_t* sdyT, const uint8_t* qxT,
+                                                 const uint8_t* sxT, int64_t ld, const int32_t* offs, int32_t G,
+                                                 int64_t M, int64_t N, int64_t K, void* dw, mxmoe_dtype dwdt,
+                                                 void* stream) {
+  return mx_wgrad_impl("mx_grouped_gemm_wgrad_tiled_fp8feed", kFeedFast, qdyT, sdyT, qxT, sxT, ld, offs, G, M, N, K,
+                       dw, dwdt, stream, true);
 }
 
 mxmoe_status mxfp4_quantize_rowwise(const void* x, int64_t R, int64_t C, uint8_t* q, uint8_t* s, void* stream) {

@@ -194,14 +194,15 @@ __device__ __forceinline__ void block_rows(int bc, int nbc, int G, const int32_t
 
 // ---- internal launchers (defined in the .hip files; arguments already validated) ---------------
 hipError_t launch_mx_rowwise(const uint16_t* x, int64_t R, int64_t C, uint8_t* q, uint8_t* s, hipStream_t st);
+// tiled: qT in the 128-byte tiled layout, [ld / 128][C][128] (ld % 128 == 0)
 hipError_t launch_mx_colwise(const uint16_t* x, int64_t R, int64_t C, const int32_t* offs, int32_t G,
-                             uint8_t* qT, uint8_t* sT, int64_t ld, hipStream_t st);
+                             uint8_t* qT, uint8_t* sT, int64_t ld, bool tiled, hipStream_t st);
 hipError_t launch_mxfp4_rowwise(const uint16_t* x, int64_t R, int64_t C, uint8_t* q, uint8_t* s, hipStream_t st);
 hipError_t launch_mxfp4_colwise(const uint16_t* x, int64_t R, int64_t C, const int32_t* offs, int32_t G,
                                 uint8_t* qT, uint8_t* sT, int64_t ld, hipStream_t st);
 hipError_t launch_mx_dual(const uint16_t* x, int64_t R, int64_t C, const int32_t* row_idx, int64_t Rsrc,
                           const int32_t* offs, int32_t G, uint8_t* q, uint8_t* s, uint8_t* qT, uint8_t* sT, int64_t ld,
-                          hipStream_t st);
+                          bool tiled, hipStream_t st);
 hipError_t launch_bw_colwise(const uint16_t* x, int64_t R, int64_t C, const int32_t* offs, int32_t G, uint8_t* qT,
                              float* sT, int64_t ld, bool pow2, hipStream_t st);
 hipError_t launch_bw_act(const uint16_t* x, int64_t R, int64_t C, uint8_t* q, float* s, bool pow2, hipStream_t st);
@@ -219,6 +220,9 @@ struct GemmArgs {
   void* out;
   int64_t lda, ldsa;  // A row stride in bytes / scale row stride in elements
   int64_t ldb, ldsb;
+  // MX: bytes between consecutive 128-byte contraction chunks of an operand row: 128 in the row-major
+  // layouts, rows * 128 in the 128-byte tiled column-wise layout (whose row stride is then 128)
+  int64_t a_kstride, b_kstride;
   int64_t M, N, K;    // problem sizes as in the ABI
   int32_t G;
   int32_t out_bf16;
@@ -236,6 +240,7 @@ struct GemmArgs {
   uint8_t* act_qT;
   uint8_t* act_sT;
   int64_t act_ld;
+  int32_t act_tiled;    // act_qT in the 128-byte tiled layout ([act_ld / 128][H][128])
 };
 
 hipError_t launch_mx_gemm(int mode, const GemmArgs& a, hipStream_t st);

@@ -198,6 +198,10 @@ __device__ __forceinline__ void act_epilogue(const GemmArgs& p, const Tile& t, c
   }
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   const int64_t ldq = p.act_ld;
+  // byte of qT row u, column j: row-major [H, ldq], or tiled [ldq / 128][H][128]
+  auto qt_at = [&](int64_t u, int64_t j) -> int64_t {
+    return p.act_tiled ? (j >> 7) * (H * 128) + u * 128 + (j & 127) : u * ldq + j;
+  };
   const int64_t tcol = t.col0 + (int64_t)t.mt * BM;               // the tile's first column of qT
   const int nb_tile = (row_lim + 31) / 32;
   const int k16 = lane & 15;
@@ -219,7 +223,7 @@ __device__ __forceinline__ void act_epilogue(const GemmArgs& p, const Tile& t, c
       const int b = 2 * m + (k16 >> 3);
       // (with offsets that are not monotone an expert's blocks could lie past the leading dimension)
       if (b < nb_tile && tcol + 32 * b + 32 <= ldq) {
-        *(uint32_t*)(p.act_qT + u * ldq + tcol + row0) = code;
+        *(uint32_t*)(p.act_qT + qt_at(u, tcol + row0)) = code;
         if ((k16 & 7) == 0) p.act_sT[u * (ldq / 32) + tcol / 32 + b] = (uint8_t)(e + 127);
       }
     }
@@ -231,7 +235,7 @@ __device__ __forceinline__ void act_epilogue(const GemmArgs& p, const Tile& t, c
     const int64_t chunks = tail / 16;
     for (int64_t k = tid; k < (BN / 2) * chunks; k += NT) {
       const int64_t u = (int64_t)t.nt * (BN / 2) + k / chunks;
-      *(uint4*)(p.act_qT + u * ldq + t.col_end + 16 * (k % chunks)) = make_uint4(0, 0, 0, 0);
+      *(uint4*)(p.act_qT + qt_at(u, t.col_end + 16 * (k % chunks))) = make_uint4(0, 0, 0, 0);
     }
     const int64_t stail = tail / 32;
     for (int64_t k = tid; k < (BN / 2) * stail; k += NT) {
@@ -298,8 +302,11 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const Tile& t, char*
   // operand rows of the tile relative to its first row (rows never decrease with r): a uniform base per
   // operand and a 32-bit byte offset per lane and load (the host keeps the span of 256 rows, or of the
   // gated forward's N weight rows, below 2 GiB)
-  const uint8_t* a_base = p.a + a_row(0) * p.lda + a_col0;
-  const uint8_t* b_base = p.b + b_row(0) * p.ldb + b_col0;
+  // (contraction byte k of a row sits at chunk k / 128, byte k % 128: chunks are a_kstride / b_kstride
+  // bytes apart, 128 in the row-major layouts; the tiled column-wise layout starts every expert's
+  // contraction, and so a_col0 / b_col0, at a multiple of 128)
+  const uint8_t* a_base = p.a + a_row(0) * p.lda + (a_col0 >> 7) * p.a_kstride + (a_col0 & 127);
+  const uint8_t* b_base = p.b + b_row(0) * p.ldb + (b_col0 >> 7) * p.b_kstride + (b_col0 & 127);
   uint32_t a_off[ND], b_off[ND];
 #pragma unroll
   for (int j = 0; j < ND; ++j) {
@@ -370,6 +377,7 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const Tile& t, char*
     char* st = lds + (ks & 1) * kStage;
     char* ss = lds + 2 * kStage + (ks & 1) * kSStage;
     const int64_t koff = (int64_t)ks * BK;
+    const int64_t koff_a = (int64_t)ks * p.a_kstride, koff_b = (int64_t)ks * p.b_kstride;
     // wgrad: chunks outside the expert's blocks, bytes [lim_lo, lim_hi) of the stage's rows, are not
     // loaded (zeroed where they would have landed)
     const int lim_hi = (int)min(L - koff, (int64_t)BK);
@@ -378,8 +386,8 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const Tile& t, char*
     for (int j = 0; j < ND; ++j) {
       const int c = 16 * dchunk(j);
       if (MODE != kWgrad || (c < lim_hi && c >= lim_lo)) {
-        dma16s(a_off[j], a_base + koff, st + (kLoadRows * w + 8 * j) * BK);
-        dma16s(b_off[j], b_base + koff, st + kStageA + (kLoadRows * w + 8 * j) * BK);
+        dma16s(a_off[j], a_base + koff_a, st + (kLoadRows * w + 8 * j) * BK);
+        dma16s(b_off[j], b_base + koff_b, st + kStageA + (kLoadRows * w + 8 * j) * BK);
       } else {
         // a chunk outside the expert's blocks: zeros where the load would have landed (the buffer is
         // free when a stage is issued, and the barrier that publishes the stage waits for LDS stores)
@@ -431,7 +439,6 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const Tile& t, char*
       if (nsteps > 1) gather_scales(1, s_w);
     }
   }
-  constexpr int BPS = SPS;                        // 32-blocks per stage
   // The stage's blocks [lo_b, hi_b) belong to the expert: the leading blocks (first stage) and those past
   // its last block (last stage) were not loaded (their chunks were zeroed at issue).  With ALIGNED_START
   // the scale bytes of the other blocks are masked to 0 (a stale 0xFF would read as NaN): keep[] holds
@@ -660,6 +667,8 @@ void launch_mode(const GemmArgs& p, dim3 grid, hipStream_t st) {
 
 hipError_t launch_mx_gemm(int mode, const GemmArgs& args, hipStream_t st) {
   GemmArgs p = args;
+  if (p.a_kstride == 0) p.a_kstride = BK;        // row-major operands
+  if (p.b_kstride == 0) p.b_kstride = BK;
   const int64_t tiles = tile_count_bound(mode, p);
   if (tiles == 0) return hipSuccess;
   const int64_t per = (int64_t)kXcd * kChunk;

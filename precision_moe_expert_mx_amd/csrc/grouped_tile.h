@@ -118,9 +118,10 @@ __device__ bool decode_grouped_tile(const GemmArgs& p, char* lds, GroupTile& t) 
   t.col_end = CB ? CBLK * (int64_t)s_cb[G] : 0;
   t.nblk = cdiv(m_g, CBLK);
   if (MODE == kWgrad) {
-    // offsets that are not monotone could place an expert past the leading dimension: clip (lda is
-    // in bytes; an E2M1 block is 16 bytes)
-    const int64_t ld_el = p.fp4 ? 2 * p.lda : p.lda;
+    // offsets that are not monotone could place an expert past the leading dimension: clip.  The
+    // leading dimension in elements comes from the scale rows (one scale per CBLK elements): the
+    // operand row stride is not it in the tiled layout (128) nor for E2M1 (two elements per byte).
+    const int64_t ld_el = (int64_t)CBLK * p.ldsa;
     const int64_t room = ld_el > t.col0 ? (ld_el - t.col0) / CBLK : 0;
     if (t.nblk > room) t.nblk = (int)room;
   }

@@ -198,7 +198,7 @@ __device__ __forceinline__ void col_load(const ColArgs& a, int r0, int n, ColRow
 
 // Convert the workgroup's 4 blocks (this wave's: rows r0 .. r0 + n of block-column bc0 + w) and write
 // them out.
-template <bool ROW, bool FULLWIN, bool FP4>
+template <bool ROW, bool FULLWIN, bool FP4, bool TILED>
 __device__ __forceinline__ void col_group(const ColArgs& a, int r0, int n, int bc0, ColRows (&v)[32],
                                           uint8_t* outq, uint8_t* outs, uint8_t* rsc, const int32_t* g_r0,
                                           const int32_t* g_n) {
@@ -287,7 +287,8 @@ __device__ __forceinline__ void col_group(const ColArgs& a, int r0, int n, int b
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
   // write out: output row cbase + rr holds kBlkBytes kColBlk bytes from block-column bc0 (fewer at the
-  // right edge of ld), 16 bytes per lane
+  // right edge of ld), 16 bytes per lane.  Tiled layout ([ld / 128][C][128], E4M3): those 128 bytes are
+  // row rr of tile bc0 / 4, so the workgroup's output is one contiguous run of 128 kColCols bytes.
   constexpr int kPieces = kColBlk * kBlkBytes / 16;                // 16-byte pieces per output row
   constexpr int kPiecesPerBlk = kBlkBytes / 16;
   const int64_t nbc = a.ld / 32;
@@ -300,13 +301,23 @@ __device__ __forceinline__ void col_group(const ColArgs& a, int r0, int n, int b
     const int64_t c = a.cbase + rr;
     if ((FULLWIN || c < a.C) && (piece / kPiecesPerBlk) < nb) {
       const uint4 val = *(const uint4*)(outq + rr * kPitch + 16 * piece);
-      store16_col<ROW>((uint4*)(a.qT + c * row_bytes + (int64_t)bc0 * kBlkBytes + 16 * piece), val);
+      const int64_t off = TILED ? (int64_t)(bc0 / kColBlk) * a.C * (kColBlk * kBlkBytes) + c * (kColBlk * kBlkBytes)
+                                : c * row_bytes + (int64_t)bc0 * kBlkBytes;
+      store16_col<ROW>((uint4*)(a.qT + off + 16 * piece), val);
     }
   }
-  for (int idx = a.t; idx < kColCols * kColBlk; idx += kColThreads) {
-    const int rr = idx / kColBlk, bb = idx % kColBlk;
-    const int64_t c = a.cbase + rr;
-    if ((FULLWIN || c < a.C) && bb < nb) a.sT[c * nbc + bc0 + bb] = outs[idx];
+  if (nb == kColBlk && (nbc & 3) == 0) {
+    // the 4 scale bytes of a column are one aligned dword of its sT row
+    for (int rr = a.t; rr < kColCols; rr += kColThreads) {
+      const int64_t c = a.cbase + rr;
+      if (FULLWIN || c < a.C) *(uint32_t*)(a.sT + c * nbc + bc0) = *(const uint32_t*)(outs + rr * kColBlk);
+    }
+  } else {
+    for (int idx = a.t; idx < kColCols * kColBlk; idx += kColThreads) {
+      const int rr = idx / kColBlk, bb = idx % kColBlk;
+      const int64_t c = a.cbase + rr;
+      if ((FULLWIN || c < a.C) && bb < nb) a.sT[c * nbc + bc0 + bb] = outs[idx];
+    }
   }
   if constexpr (ROW) {
     // row-wise scales: the window's (up to) 8 bytes of each row of the 4 blocks, one lane per row
@@ -335,7 +346,7 @@ __device__ __forceinline__ void col_group(const ColArgs& a, int r0, int n, int b
 // reads; each routed row lies in exactly one block-column, so it is written once.  GATHER: routed
 // row r is read from source row row_idx[r] (clamped into [0, Rsrc)).  FULLWIN: C % 256 == 0, so every
 // window lies inside the tensor.
-template <bool ROW, bool GATHER, bool FULLWIN, bool FP4>
+template <bool ROW, bool GATHER, bool FULLWIN, bool FP4, bool TILED>
 __global__ __launch_bounds__(kColThreads) void mx_colwise_kernel(const uint16_t* __restrict__ x, int64_t R, int64_t C,
                                                                  const int32_t* __restrict__ offs, int G,
                                                                  uint8_t* __restrict__ qT, uint8_t* __restrict__ sT,
@@ -349,7 +360,7 @@ __global__ __launch_bounds__(kColThreads) void mx_colwise_kernel(const uint16_t*
   int32_t* starts = (int32_t*)outq;
   int32_t* rows0 = starts + (kMaxGroupsLds + 1);
   __shared__ int32_t blk_r0[kColBlk], blk_n[kColBlk];
-  __shared__ uint8_t outs[kColCols * kColBlk];
+  __shared__ __attribute__((aligned(16))) uint8_t outs[kColCols * kColBlk];
   __shared__ __attribute__((aligned(8))) uint8_t rsc[ROW ? kColBlk * 32 * kRowBlks : 8];
 
   const int nbc = (int)(ld / 32);
@@ -397,32 +408,38 @@ __global__ __launch_bounds__(kColThreads) void mx_colwise_kernel(const uint16_t*
   const int n = __builtin_amdgcn_readfirstlane(blk_n[a.w]);
   ColRows v[32];
   col_load<GATHER, FULLWIN>(a, r0, n, v);
-  col_group<ROW, FULLWIN, FP4>(a, r0, n, bc0, v, outq, outs, rsc, blk_r0, blk_n);
+  col_group<ROW, FULLWIN, FP4, TILED>(a, r0, n, bc0, v, outq, outs, rsc, blk_r0, blk_n);
 }
 
 static int64_t colwise_grid(int64_t C, int64_t ld) {
   return ((ld / 32 + kColBlk - 1) / kColBlk) * ((C + kColCols - 1) / kColCols);
 }
 
-template <bool ROW, bool GATHER, bool FP4 = false>
+template <bool ROW, bool GATHER, bool FP4 = false, bool TILED = false>
 static void launch_col(bool fullwin, int64_t nwg, hipStream_t st, const uint16_t* x, int64_t R, int64_t C,
                        const int32_t* offs, int32_t G, uint8_t* qT, uint8_t* sT, int64_t ld, uint8_t* q, uint8_t* s,
                        const int32_t* row_idx, int64_t Rsrc) {
+  static_assert(!(TILED && FP4), "the tiled layout holds E4M3 codes");
   if (fullwin)
-    hipLaunchKernelGGL((mx_colwise_kernel<ROW, GATHER, true, FP4>), dim3((unsigned)nwg), dim3(kColThreads), 0, st, x, R,
-                       C, offs, G, qT, sT, ld, q, s, row_idx, Rsrc);
+    hipLaunchKernelGGL((mx_colwise_kernel<ROW, GATHER, true, FP4, TILED>), dim3((unsigned)nwg), dim3(kColThreads), 0,
+                       st, x, R, C, offs, G, qT, sT, ld, q, s, row_idx, Rsrc);
   else
-    hipLaunchKernelGGL((mx_colwise_kernel<ROW, GATHER, false, FP4>), dim3((unsigned)nwg), dim3(kColThreads), 0, st, x,
-                       R, C, offs, G, qT, sT, ld, q, s, row_idx, Rsrc);
+    hipLaunchKernelGGL((mx_colwise_kernel<ROW, GATHER, false, FP4, TILED>), dim3((unsigned)nwg), dim3(kColThreads), 0,
+                       st, x, R, C, offs, G, qT, sT, ld, q, s, row_idx, Rsrc);
 }
 
 hipError_t launch_mx_colwise(const uint16_t* x, int64_t R, int64_t C, const int32_t* offs, int32_t G,
-                             uint8_t* qT, uint8_t* sT, int64_t ld, hipStream_t st) {
+                             uint8_t* qT, uint8_t* sT, int64_t ld, bool tiled, hipStream_t st) {
   if (C == 0 || ld == 0) return hipSuccess;
+  if (tiled && ld % 128) return hipErrorInvalidValue;
   const int64_t nwg = colwise_grid(C, ld);
   if (nwg > 0x7FFFFFFF) return hipErrorInvalidValue;
-  launch_col<false, false>(C % kColCols == 0, nwg, st, x, R, C, offs, offs ? G : 1, qT, sT, ld, nullptr, nullptr,
-                           nullptr, (int64_t)0);
+  if (tiled)
+    launch_col<false, false, false, true>(C % kColCols == 0, nwg, st, x, R, C, offs, offs ? G : 1, qT, sT, ld, nullptr,
+                                          nullptr, nullptr, (int64_t)0);
+  else
+    launch_col<false, false>(C % kColCols == 0, nwg, st, x, R, C, offs, offs ? G : 1, qT, sT, ld, nullptr, nullptr,
+                             nullptr, (int64_t)0);
   return hipGetLastError();
 }
 
@@ -438,14 +455,17 @@ hipError_t launch_mxfp4_colwise(const uint16_t* x, int64_t R, int64_t C, const i
 
 hipError_t launch_mx_dual(const uint16_t* x, int64_t R, int64_t C, const int32_t* row_idx, int64_t Rsrc,
                           const int32_t* offs, int32_t G, uint8_t* q, uint8_t* s, uint8_t* qT, uint8_t* sT, int64_t ld,
-                          hipStream_t st) {
+                          bool tiled, hipStream_t st) {
   if (C == 0 || ld == 0) return hipSuccess;
+  if (tiled && ld % 128) return hipErrorInvalidValue;
   const int64_t nwg = colwise_grid(C, ld);
   if (nwg > 0x7FFFFFFF) return hipErrorInvalidValue;
-  if (row_idx)
-    launch_col<true, true>(C % kColCols == 0, nwg, st, x, R, C, offs, offs ? G : 1, qT, sT, ld, q, s, row_idx, Rsrc);
-  else
-    launch_col<true, false>(C % kColCols == 0, nwg, st, x, R, C, offs, offs ? G : 1, qT, sT, ld, q, s, nullptr, R);
+  const bool fw = C % kColCols == 0;
+  const int32_t g = offs ? G : 1;
+  if (row_idx && tiled) launch_col<true, true, false, true>(fw, nwg, st, x, R, C, offs, g, qT, sT, ld, q, s, row_idx, Rsrc);
+  else if (row_idx) launch_col<true, true>(fw, nwg, st, x, R, C, offs, g, qT, sT, ld, q, s, row_idx, Rsrc);
+  else if (tiled) launch_col<true, false, false, true>(fw, nwg, st, x, R, C, offs, g, qT, sT, ld, q, s, nullptr, R);
+  else launch_col<true, false>(fw, nwg, st, x, R, C, offs, g, qT, sT, ld, q, s, nullptr, R);
   return hipGetLastError();
 }
 

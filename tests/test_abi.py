@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
     m, L = _lib()
     for name in _declared():
         assert hasattr(L, name), name
-    assert m.abi_version() == 2
+    assert m.abi_version() == 3
 
 
 def test_host_helpers():
@@ -173,6 +173,35 @@ def test_fp8_feed_entry_points_validate_like_the_precise_ones():
     assert st == 2 and "fp8feed" in msg
     a = list(ok_args); a[8] = 200
     assert _status(L, "fp8bw_grouped_gemm_dgrad_fp8feed", *a)[0] == 2
+
+
+def test_tiled_entry_points_need_a_pitch_multiple_of_128():
+    """The 128-byte tiled column-wise layout: the same validation as the row-major entry points plus
+    ld % 128 == 0 (quantisers: MXMOE_ERR_ALIGN; GEMMs: MXMOE_ERR_SHAPE); the gated forward's tiled
+    variant always writes H column-wise."""
+    _, L = _lib()
+    # R = 1000 rows in 4 groups: minimum ld 1120; 1184 is a multiple of 32 but not of 128
+    for fn, args in (("mx_quantize_colwise_tiled", (A16, 1000, 64, A16, 4, A16, A16, 1184, None)),
+                     ("mx_quantize_dual_tiled", (A16, 1000, 64, None, 0, A16, 4, A16, A16, A16b, A16b, 1184, None))):
+        st, msg = _status(L, fn, *args)
+        assert st == 3 and fn in msg and "128" in msg, (fn, st, msg)
+    assert _status(L, "mx_quantize_colwise_tiled", A16, 100, 64, A16, 4, A16, A16, 96, None)[0] == 3
+    assert _status(L, "mx_quantize_colwise_tiled", A16, 1000, 64, A16, 4, A16, A16, 1024, None)[0] == 2   # < 1120
+    assert _status(L, "mx_quantize_colwise_tiled", A16, 100, 64, A16, 4, None, A16, 256, None)[0] == 1
+    for fn in ("mx_grouped_gemm_dgrad_tiled", "mx_grouped_gemm_dgrad_tiled_fp8feed"):
+        # G * N = 2048: ldw 2080 is a multiple of 32, not of 128
+        st, msg = _status(L, fn, A16, A16, A16b, A16b, 2080, A16, 4, 1024, 512, 256, A16, 0, None)
+        assert st == 2 and fn in msg and "128" in msg, (fn, msg)
+    for fn in ("mx_grouped_gemm_wgrad_tiled", "mx_grouped_gemm_wgrad_tiled_fp8feed"):
+        # mx_colwise_ld_min(1024, 4) = 1152; 1184 is above it but not a multiple of 128
+        st, msg = _status(L, fn, A16, A16, A16b, A16b, 1184, A16, 4, 1024, 512, 256, A16, 0, None)
+        assert st == 2 and fn in msg and "128" in msg, (fn, msg)
+        assert _status(L, fn, A16, A16, A16b, A16b, 1024, A16, 4, 1024, 512, 256, A16, 0, None)[0] == 2
+    sw = (A16, A16, A16b, A16b, A16, 4, 1024, 512, 256, A16, A16, A16)
+    st, msg = _status(L, "mx_grouped_gemm_fwd_swiglu_tiled", *sw, None, None, None, 1152, None)
+    assert st == 1 and "qhT" in msg
+    st, msg = _status(L, "mx_grouped_gemm_fwd_swiglu_tiled", *sw, None, A16b, A16b, 1184, None)
+    assert st == 2 and "128" in msg
 
 
 def test_binding_refuses_cpu_tensors():

@@ -5,6 +5,7 @@ import json
 import os
 
 import numpy as np
+import pytest
 
 from oracle import (bf16_bits_to_f64, e4m3_decode, e4m3_encode_bruteforce, mx_colwise_ld_min,
                     mx_dequantize, mx_quantize_colwise, mx_quantize_rowwise, mx_group_columns)
@@ -314,3 +315,28 @@ def test_colwise_values_matches_bf16_path_and_rowwise_rule():
         e = int(sr[k, 0]) - 127
         assert qT[k, c0] == e4m3_encode_bruteforce(np.ldexp(pad[0, k], -e))[0]
     assert not qT[:, ~used].any() and not sT[:, int(np.sum(nb)):].any()
+
+
+def test_colwise_tiled_is_the_stated_permutation():
+    """The 128-byte tiled layout (library contract): byte (c, j) of qT [C, ld] at flat position
+    (j // 128) * C * 128 + c * 128 + j % 128.  Checked element by element by that formula, as a bijection
+    onto the buffer, and on a case small enough to write out."""
+    from oracle import mx_colwise_tiled
+    rng = np.random.default_rng(71)
+    for C, ld in ((3, 128), (5, 384), (32, 256)):
+        qT = rng.integers(0, 256, size=(C, ld), dtype=np.uint8)
+        t = mx_colwise_tiled(qT)
+        assert t.shape == (ld // 128, C, 128) and t.dtype == np.uint8
+        flat = t.reshape(-1)
+        pos = np.empty((C, ld), dtype=np.int64)
+        for c in range(C):
+            for j in range(ld):
+                pos[c, j] = (j // 128) * C * 128 + c * 128 + j % 128
+                assert flat[pos[c, j]] == qT[c, j]
+        assert np.array_equal(np.sort(pos.reshape(-1)), np.arange(C * ld))
+    # 2 rows, 256 bytes: tile 0 = row 0 bytes 0..127 then row 1 bytes 0..127; tile 1 = bytes 128..255
+    qT = np.arange(512, dtype=np.int64).reshape(2, 256)
+    want = np.concatenate([np.arange(0, 128), np.arange(256, 384), np.arange(128, 256), np.arange(384, 512)])
+    assert np.array_equal(mx_colwise_tiled(qT).reshape(-1), want)
+    with pytest.raises(ValueError):
+        mx_colwise_tiled(np.zeros((2, 96), dtype=np.uint8))
