@@ -39,6 +39,11 @@ HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "mxfp8": 5000.0, "mxfp4": 10100.0}
 QUANT_BYTES_PER_ELEM = 2.0 + 1.0 + 1.0 / 32.0   # bf16 in, E4M3 out, one E8M0 per 32
 DUAL_BYTES_PER_ELEM = 2.0 + 2.0 * (1.0 + 1.0 / 32.0)   # bf16 in once, both MX layouts out
+# the workload the step runs on (the DeepSeek-V3-671B one-GPU expert shard unless --workload says
+# otherwise; the profile summaries are named for it)
+WORKLOAD = "dsv3_671b_shard"
+WORKLOAD_TITLE = {"dsv3_671b_shard": "DeepSeek-V3-671B expert shard", "dsv3_16b": "DeepSeek-V3-16B layers",
+                  "llama4_scout": "Llama-4-Scout layers"}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_traffic_dsv3_671b_shard.txt")
 GEMM_SOURCES = [os.path.join(ROOT, "precision_moe_expert_mx_amd", "csrc", f) for f in ("gemm_mx.hip", "grouped_tile.h", "common.h")]
 
@@ -303,7 +308,8 @@ def pmc_summary(fetch_csv: str, write_csv: str, cmds) -> None:
                "fetch": {n: round(float(np.mean(c["FETCH_SIZE"]))) for n, c in sel.items()},
                "write": {n: round(float(np.mean(c["WRITE_SIZE"]))) for n, c in sel.items()}}
         with open(path, "w") as f:
-            f.write(f"# HBM traffic per launch of the {len(names)} {what} launches of one step (DeepSeek-V3-671B expert shard)\n")
+            f.write(f"# HBM traffic per launch of the {len(names)} {what} launches of one step "
+                    f"({WORKLOAD_TITLE[WORKLOAD]})\n")
             f.write("# bytes = counter KiB * 1024 * (2^30 / counter KiB of the 1 GiB device copy); commands (repository root):\n")
             for c in cmds:
                 f.write(f"#   {c}\n")
@@ -326,7 +332,7 @@ def mfma_summary(pmc_dir: str, cmds) -> None:
     import csv
     from workloads import layer_shapes
     flops = {}
-    for name, M, N, K in layer_shapes("dsv3_671b_shard"):
+    for name, M, N, K in layer_shapes(WORKLOAD):
         for k in ("fwd", "fwd_swiglu", "dgrad", "wgrad"):
             flops[f"{name}.{k}"] = 2.0 * M * N * K
     per_disp = {}
@@ -357,7 +363,7 @@ def mfma_summary(pmc_dir: str, cmds) -> None:
                   "counters": {m_: round(v) for m_, v in c.items()}}
     rec = {"source_sha256": gemm_source_hash(), "ops": ops}
     with open(MFMA_FILE, "w") as f:
-        f.write("# Clock and MFMA use of the six grouped-GEMM launches of one step (DeepSeek-V3-671B expert shard,\n")
+        f.write(f"# Clock and MFMA use of the six grouped-GEMM launches of one step ({WORKLOAD_TITLE[WORKLOAD]},\n")
         f.write("# precise feed, bf16 MFMA).  clock = GRBM_GUI_ACTIVE / 8 XCDs / duration; frac_of_rate_at_clock =\n")
         f.write("# achieved TFLOP/s / (1024 flop/clk/SIMD x 1024 SIMDs x clock); mfma_util = rocprofv3 MfmaUtil\n")
         f.write("# (sum SQ_VALU_MFMA_BUSY_CYCLES / (max-XCD GRBM_GUI_ACTIVE x SIMDs)); commands (repository root):\n")
@@ -370,6 +376,20 @@ def mfma_summary(pmc_dir: str, cmds) -> None:
 STATS_FILE = os.path.join(ROOT, "profiles", "kernel_stats_dsv3_671b_shard.md")
 STATS_CMD = ("rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof5 -o bench -- "
              "python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-extra-legs")
+
+
+def set_workload(wname: str) -> None:
+    """Run on `wname`: the profile summaries and their commands are named for it."""
+    global WORKLOAD, TRAFFIC_FILE, QUANT_TRAFFIC_FILE, MFMA_FILE, STATS_FILE, STATS_CMD
+    if wname == WORKLOAD:
+        return
+    WORKLOAD = wname
+    prof = os.path.join(ROOT, "profiles")
+    TRAFFIC_FILE = os.path.join(prof, f"gemm_traffic_{wname}.txt")
+    QUANT_TRAFFIC_FILE = os.path.join(prof, f"quant_traffic_{wname}.txt")
+    MFMA_FILE = os.path.join(prof, f"gemm_mfma_{wname}.txt")
+    STATS_FILE = os.path.join(prof, f"kernel_stats_{wname}.md")
+    STATS_CMD = STATS_CMD.replace("gpurun_out/prof5 ", f"gpurun_out/prof5_{wname} ") + f" --workload {wname}"
 
 
 def stats_summary(prof_dir: str) -> None:
@@ -385,9 +405,10 @@ def stats_summary(prof_dir: str) -> None:
         n = re.sub(r"\(anonymous namespace\)::", "", n)
         return re.sub(r"\(.*\)$", "", n)
 
-    out = ["# Kernel statistics: DeepSeek-V3-671B expert shard, fwd+bwd step (precise feed)", "",
+    out = [f"# Kernel statistics: {WORKLOAD_TITLE[WORKLOAD]}, fwd+bwd step (precise feed)", "",
            "Commands (from the repository root, one MI355X):", "", "```", STATS_CMD,
-           f"python3 bench.py --stats-summary {prof_dir}", "```", "",
+           f"python3 bench.py --stats-summary {prof_dir}"
+           + ("" if WORKLOAD == "dsv3_671b_shard" else f" --workload {WORKLOAD}"), "```", "",
            "## rocprofv3 kernel statistics (all launches)", "",
            "| Name | Calls | TotalDurationNs | AverageNs | Percentage | MinNs | MaxNs | StdDev |",
            "|---|---|---|---|---|---|---|---|"]
@@ -710,25 +731,30 @@ def main():
                     help="write the GEMM clock / MFMA-use summary from a rocprofv3 --kernel-trace --pmc run of this script")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the GEMM and quantiser traffic summaries from two rocprofv3 counter runs of this script")
+    ap.add_argument("--workload", default=WORKLOAD, choices=sorted(WORKLOAD_TITLE),
+                    help="run the step on another workload (for its profiles; the headline is the default)")
     args = ap.parse_args()
+    set_workload(args.workload)
 
     if args.stats_summary:
         stats_summary(args.stats_summary)
         return
 
+    # (another workload: its own output folders and the --workload argument in every command)
+    wl_arg, sfx = ("", "") if WORKLOAD == "dsv3_671b_shard" else (f" --workload {WORKLOAD}", f"_{WORKLOAD}")
     if args.mfma_summary:
         mfma_summary(args.mfma_summary, [
-            "rocprofv3 --kernel-trace --pmc " + " ".join(MFMA_COUNTERS) + " --output-format csv -d gpurun_out/pmc_mfma -o p "
-            "-- python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-extra-legs",
-            "python3 bench.py --mfma-summary gpurun_out/pmc_mfma"])
+            "rocprofv3 --kernel-trace --pmc " + " ".join(MFMA_COUNTERS) + f" --output-format csv -d gpurun_out/pmc_mfma{sfx} "
+            "-o p -- python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-extra-legs" + wl_arg,
+            f"python3 bench.py --mfma-summary gpurun_out/pmc_mfma{sfx}{wl_arg}"])
         return
 
     if args.pmc_summary:
-        cmds = [f"rocprofv3 --pmc {c} --output-format csv -d gpurun_out/pmc_{c.lower()} -o p -- "
-                "python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-extra-legs"
+        cmds = [f"rocprofv3 --pmc {c} --output-format csv -d gpurun_out/pmc_{c.lower()}{sfx} -o p -- "
+                "python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-extra-legs" + wl_arg
                 for c in ("FETCH_SIZE", "WRITE_SIZE")]
-        cmds.append("python3 bench.py --pmc-summary gpurun_out/pmc_fetch_size/p_counter_collection.csv "
-                    "gpurun_out/pmc_write_size/p_counter_collection.csv")
+        cmds.append(f"python3 bench.py --pmc-summary gpurun_out/pmc_fetch_size{sfx}/p_counter_collection.csv "
+                    f"gpurun_out/pmc_write_size{sfx}/p_counter_collection.csv{wl_arg}")
         pmc_summary(args.pmc_summary[0], args.pmc_summary[1], cmds)
         return
 
@@ -745,7 +771,7 @@ def main():
     m.lib()                                    # raises if the HIP library is not built
 
     from workloads import make_workload
-    wname = "dsv3_671b_shard"
+    wname = WORKLOAD
     t = time.perf_counter()
     wl = make_workload(wname)
     log(f"workload {wname} generated in {time.perf_counter() - t:.1f} s")
@@ -786,7 +812,7 @@ def main():
     dom = max((op for op in ops if op.kind == "gemm"), key=lambda o: float(np.mean(o.ms)))
     dom_ms = float(np.mean(dom.ms))
     achieved = dom.work / (dom_ms * 1e-3) / 1e12
-    traffic = read_traffic()
+    traffic = read_traffic(TRAFFIC_FILE)
     # against the dense MXFP8 MFMA peak that the metric names; the precise feed runs on the bf16 MFMA,
     # whose peak (half of it) is its own ceiling, reported beside it
     roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_PEAK_TFLOPS["mxfp8"],
