@@ -234,36 +234,15 @@ __device__ __forceinline__ void bw_tile(const GemmArgs& p, const GroupTile& t, c
     }
   }
 
-  // ---- epilogue: 8-byte (bf16) or 16-byte (fp32) pieces, one base address per lane -------------
+  // ---- epilogue: through LDS, 32 rows of each wave at a time, whole row pieces (store_tile_rows) ----
   const int64_t nout = MODE == kFwd ? p.N : p.K;
   const int row_lim = (int)min((int64_t)BM, MODE == kWgrad ? p.N - (int64_t)t.mt * BM : (int64_t)t.rows);
   const int col_lim = (int)min((int64_t)BN, nout - (int64_t)t.nt * BN);
   const int64_t out_row0 = MODE == kWgrad ? (int64_t)t.g * p.N + (int64_t)t.mt * BM : t.row0;
-  const int lrow = WM * wm + lr;
-  const int lcol = WN * wn + 4 * h;
-  const int64_t base = (out_row0 + lrow) * nout + (int64_t)t.nt * BN + lcol;
-#pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    if (lrow + 32 * i >= row_lim) continue;
-    const int64_t rbase = base + (int64_t)(32 * i) * nout;
-#pragma unroll
-    for (int j = 0; j < NJ; ++j)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int co = 32 * j + 8 * q;
-        if (lcol + co >= col_lim) continue;
-        const int64_t idx = rbase + co;
-        const float v0 = acc[i][j][4 * q], v1 = acc[i][j][4 * q + 1];
-        const float v2 = acc[i][j][4 * q + 2], v3 = acc[i][j][4 * q + 3];
-        if (p.out_bf16) {
-          const uint2 wv = make_uint2(f32_to_bf16_bits(v0) | (f32_to_bf16_bits(v1) << 16),
-                                      f32_to_bf16_bits(v2) | (f32_to_bf16_bits(v3) << 16));
-          *(uint2*)((uint16_t*)p.out + idx) = wv;
-        } else {
-          *(float4*)((float*)p.out + idx) = make_float4(v0, v1, v2, v3);
-        }
-      }
-  }
+  static_assert(kWaves * 32 * (128 * NJ + 16) <= kLds, "staged epilogue must fit in LDS");
+  stage_barrier();                                 // every wave is done with the stages
+  store_tile_rows<NI, NJ, 1>(acc, lds + w * 32 * (128 * NJ + 16), p.out_bf16, p.out, out_row0, nout,
+                             (int64_t)t.nt * BN, WM * wm, WN * wn, row_lim, col_lim);
 }
 
 template <int MODE, int FEED>

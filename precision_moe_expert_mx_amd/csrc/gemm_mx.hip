@@ -603,54 +603,13 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const Tile& t, char*
   const int lcol = WN * wn + 4 * (lane / FI);
   const int64_t base = (out_row0 + lrow) * nout + (int64_t)t.nt * BN + lcol;
   if constexpr (FR == 32 && NI % 2 == 0) {
-    // E4M3 (32x32 fragments), through LDS: each wave stages 64 of its rows (two fragment rows) in a
-    // region of its own, then stores them as whole row pieces (16 bytes per lane; 4 rows x 256 bytes
-    // of fp32 or 8 rows x 128 bytes of bf16 per instruction) instead of 32 rows x 32 (16) bytes per
-    // instruction straight from the accumulators (measured: the expert-shard step -1.4%, the
-    // DeepSeek-V3-16B step -3%).  The stages are free once every wave has passed the barrier; a
-    // wave's own LDS accesses stay in order, so its two passes and the write / read of a pass need no
-    // barrier.
-    constexpr int kPitch32 = 4 * WN + 16, kPitch16 = 2 * WN + 16;     // bytes per staged row
-    static_assert(kWaves * 64 * kPitch32 <= kLds, "staged epilogue must fit in LDS");
+    // E4M3 (32x32 fragments): through LDS, 64 rows of each wave at a time (store_tile_rows; measured:
+    // the expert-shard step -1.4%, the DeepSeek-V3-16B step -3% against stores straight from the
+    // accumulators).  Every wave is done with the stages once it has passed the barrier.
+    static_assert(kWaves * 64 * (128 * NJ + 16) <= kLds, "staged epilogue must fit in LDS");
     stage_barrier();
-    const bool bf = p.out_bf16;
-    const int pitch = bf ? kPitch16 : kPitch32;
-    char* reg = lds + w * 64 * kPitch32;
-    const int h = lane / FI;
-#pragma unroll
-    for (int pass = 0; pass < NI / 2; ++pass) {
-#pragma unroll
-      for (int ii = 0; ii < 2; ++ii) {
-        const int i = 2 * pass + ii;
-        const int r = lane % FI + FI * ii;
-#pragma unroll
-        for (int j = 0; j < NJ; ++j)
-#pragma unroll
-          for (int q = 0; q < NR / 4; ++q) {
-            const int c = FI * j + 8 * q + 4 * h;
-            const float v0 = acc[i][j][4 * q], v1 = acc[i][j][4 * q + 1];
-            const float v2 = acc[i][j][4 * q + 2], v3 = acc[i][j][4 * q + 3];
-            if (bf)
-              *(uint2*)(reg + r * kPitch16 + 2 * c) = make_uint2(f32_to_bf16_bits(v0) | (f32_to_bf16_bits(v1) << 16),
-                                                                 f32_to_bf16_bits(v2) | (f32_to_bf16_bits(v3) << 16));
-            else
-              *(float4*)(reg + r * kPitch32 + 4 * c) = make_float4(v0, v1, v2, v3);
-          }
-      }
-      // 64 rows x (4 WN or 2 WN) bytes, 16 bytes per lane: chunk k = lane + 64 m of the pass
-      const int cpr = bf ? (2 * WN / 16) : (4 * WN / 16);           // 16-byte chunks per row
-      const int nchunk = 64 * cpr;
-      for (int k = lane; k < nchunk; k += 64) {
-        const int r = k / cpr, ch = k % cpr;
-        const int trow = WM * wm + 64 * pass + r;                  // tile row
-        const int tcol = WN * wn + ch * (bf ? 8 : 4);              // tile column of the chunk's first element
-        if (trow >= row_lim || tcol >= col_lim) continue;
-        const uint4 v = *(const uint4*)(reg + r * pitch + 16 * ch);
-        const int64_t idx = (out_row0 + trow) * nout + (int64_t)t.nt * BN + tcol;
-        if (bf) *(uint4*)((uint16_t*)p.out + idx) = v;
-        else *(uint4*)((float*)p.out + idx) = v;
-      }
-    }
+    store_tile_rows<NI, NJ, 2>(acc, lds + w * 64 * (128 * NJ + 16), p.out_bf16, p.out, out_row0, nout,
+                               (int64_t)t.nt * BN, WM * wm, WN * wn, row_lim, col_lim);
     return;
   }
 #pragma unroll

@@ -128,6 +128,58 @@ __device__ bool decode_grouped_tile(const GemmArgs& p, char* lds, GroupTile& t) 
   return true;
 }
 
+// Store a wave's accumulator tile as whole row pieces.  The tile is NI x NJ fragments of 32 x 32 in
+// the layout of an MFMA that takes the B fragment first: lane l holds tile row 32 i + l % 32 and, per
+// group q of four registers, columns 32 j + 8 q + 4 (l / 32) .. + 3.  RPP fragment rows (32 RPP rows) at
+// a time go to the wave's own LDS region `reg` (>= 32 RPP (128 NJ + 16) bytes, 16-byte aligned), as fp32
+// or bf16, and leave 16 bytes per lane: an instruction writes 4 rows x 128 NJ bytes (fp32) or 8 rows x
+// 64 NJ bytes (bf16), where stores straight from the accumulators write 32 rows x 16 or 32 bytes.
+// Output element (tile row r, tile column c) is out[(out_row0 + r0 + r) * nout + col0 + c0 + c]; rows at
+// or past row_lim and column groups at or past col_lim are not written (col_lim a multiple of 8).  The
+// region must be free (the caller's barrier); a wave's own LDS accesses stay in order, so the passes
+// and the write and read of a pass need no barrier.
+template <int NI, int NJ, int RPP, typename Acc>
+__device__ __forceinline__ void store_tile_rows(const Acc (&acc)[NI][NJ], char* reg, bool bf16, void* out,
+                                                int64_t out_row0, int64_t nout, int64_t col0, int r0, int c0,
+                                                int row_lim, int col_lim) {
+  static_assert(NI % RPP == 0, "passes of RPP fragment rows");
+  constexpr int kPitch32 = 128 * NJ + 16, kPitch16 = 64 * NJ + 16;    // bytes per staged row
+  const int lane = threadIdx.x & 63, h = lane >> 5;
+  const int pitch = bf16 ? kPitch16 : kPitch32;
+#pragma unroll
+  for (int pass = 0; pass < NI / RPP; ++pass) {
+#pragma unroll
+    for (int ii = 0; ii < RPP; ++ii) {
+      const int i = RPP * pass + ii;
+      const int r = (lane & 31) + 32 * ii;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int c = 32 * j + 8 * q + 4 * h;
+          const float v0 = acc[i][j][4 * q], v1 = acc[i][j][4 * q + 1];
+          const float v2 = acc[i][j][4 * q + 2], v3 = acc[i][j][4 * q + 3];
+          if (bf16)
+            *(uint2*)(reg + r * kPitch16 + 2 * c) = make_uint2(f32_to_bf16_bits(v0) | (f32_to_bf16_bits(v1) << 16),
+                                                               f32_to_bf16_bits(v2) | (f32_to_bf16_bits(v3) << 16));
+          else
+            *(float4*)(reg + r * kPitch32 + 4 * c) = make_float4(v0, v1, v2, v3);
+        }
+    }
+    const int cpr = bf16 ? 4 * NJ : 8 * NJ;                        // 16-byte chunks per staged row
+    for (int k = lane; k < 32 * RPP * cpr; k += 64) {
+      const int r = k / cpr, ch = k % cpr;
+      const int tr = r0 + 32 * RPP * pass + r;                     // tile row
+      const int tc = c0 + ch * (bf16 ? 8 : 4);                     // tile column of the chunk's first element
+      if (tr >= row_lim || tc >= col_lim) continue;
+      const uint4 v = *(const uint4*)(reg + r * pitch + 16 * ch);
+      const int64_t idx = (out_row0 + tr) * nout + col0 + tc;
+      if (bf16) *(uint4*)((uint16_t*)out + idx) = v;
+      else *(uint4*)((float*)out + idx) = v;
+    }
+  }
+}
+
 // Eight E4M3 bytes -> eight bf16 multiplied by 2^(e-127), e the E8M0 byte whose bits sit in the
 // exponent field of `scale`; exact for every product the GEMMs form.
 __device__ __forceinline__ v8bf widen8(uint32_t w0, uint32_t w1, float scale) {
