@@ -110,25 +110,28 @@ __device__ __forceinline__ void act_epilogue(const GemmArgs& p, const Tile& t, c
   const int lrow = WM * wm + lane % 32;
   float* up = (float*)lds;
 
-  // pre-activations (bf16) and the up values to LDS
+  // pre-activations (bf16) as whole row pieces through LDS (store_tile_rows): gate waves at columns
+  // [128 nt, +128) of Y, up waves at H + the same
   stage_barrier();                                  // every wave is done with the last stage
+  static_assert(kWaves * 64 * (128 * NJ + 16) <= kLds, "staged Y must fit in LDS");
+  store_tile_rows<NI, NJ, 2>(acc, lds + w * 64 * (128 * NJ + 16), true, p.out, t.row0, p.N,
+                             (up_wave ? H : 0) + (int64_t)t.nt * (BN / 2), WM * wm, WN * (wn % (kWavesN / 2)),
+                             row_lim, BN);
+  // the up values to LDS once every wave is done with its staged rows
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  if (up_wave) {
 #pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    const int r = lrow + 32 * i;
+    for (int i = 0; i < NI; ++i) {
+      const int r = lrow + 32 * i;
 #pragma unroll
-    for (int j = 0; j < NJ; ++j)
+      for (int j = 0; j < NJ; ++j)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int c = ucol0 + 32 * j + 8 * q;
-        const float v0 = acc[i][j][4 * q], v1 = acc[i][j][4 * q + 1], v2 = acc[i][j][4 * q + 2], v3 = acc[i][j][4 * q + 3];
-        if (up_wave) *(float4*)(up + r * kUpPitch + c) = make_float4(v0, v1, v2, v3);
-        if (r < row_lim) {
-          const int64_t yc = (up_wave ? H : 0) + (int64_t)t.nt * (BN / 2) + c;
-          const uint2 wv = make_uint2(f32_to_bf16_bits(v0) | (f32_to_bf16_bits(v1) << 16),
-                                      f32_to_bf16_bits(v2) | (f32_to_bf16_bits(v3) << 16));
-          *(uint2*)((uint16_t*)p.out + (t.row0 + r) * p.N + yc) = wv;
+        for (int q = 0; q < 4; ++q) {
+          const int c = ucol0 + 32 * j + 8 * q;
+          *(float4*)(up + r * kUpPitch + c) =
+              make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
         }
-      }
+    }
   }
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   if (up_wave && !colwise) return;
