@@ -153,7 +153,7 @@ __global__ __launch_bounds__(256) void bw_weight_kernel(const uint16_t* __restri
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     int64_t row = br * 128 + r + 16 * i;
-    v[i] = *(const uint4*)(w + row * C + bcn * 128 + ch * 8);
+    v[i] = load16_nt((const uint4*)(w + row * C + bcn * 128 + ch * 8));                     // read once
     m = max(m, magmax8(v[i]));
   }
 #pragma unroll
@@ -267,7 +267,7 @@ __global__ __launch_bounds__(256) void bw_colwise_kernel(const uint16_t* __restr
   const uint16_t* src = x + ((int64_t)r0 + 32 * qq) * C + cbase + 2 * cp;
 #pragma unroll
   for (int r = 0; r < 32; ++r) {
-    w[r] = r < nq ? *(const uint32_t*)(src + (int64_t)r * C) : 0u;
+    w[r] = r < nq ? __builtin_nontemporal_load((const uint32_t*)(src + (int64_t)r * C)) : 0u;   // read once
     m0 = max(m0, w[r] & 0x7FFFu);
     m1 = max(m1, (w[r] >> 16) & 0x7FFFu);
   }
