@@ -339,6 +339,31 @@ mxmoe_status fp8bw_grouped_gemm_dgrad(const uint8_t* qdy, const float* sdy,
                                       const int32_t* offs, int32_t G, int64_t M, int64_t N, int64_t K,
                                       void* dx, mxmoe_dtype dxdt, void* stream);
 
+/* fp8bw_grouped_gemm_fwd_pow2 / fp8bw_grouped_gemm_dgrad_pow2: the same products (arguments, layouts
+ * and errors as fp8bw_grouped_gemm_fwd / _dgrad) for scales that are powers of two, as the _pow2
+ * quantisers write them.  Such a scale is exactly representable as an E8M0 byte, so each 128-slice
+ * is multiplied exactly with its scales folded into the operands and summed in the fp32 accumulator
+ * across the whole contraction (the MX kernel): the promoted sum of the recipe and this sum differ
+ * only in fp32 rounding order, within the same |err| <= 1e-5 * sum |a b| bound.  A scale that is not
+ * a power of two is read as the power of two of its exponent (a wrong result, not an error: the
+ * scales are device data).  The _fp8feed forms use the block-scaled FP8 MFMA. */
+mxmoe_status fp8bw_grouped_gemm_fwd_pow2(const uint8_t* qx, const float* sx,
+                                         const uint8_t* qw, const float* sw,
+                                         const int32_t* offs, int32_t G, int64_t M, int64_t N, int64_t K,
+                                         void* y, mxmoe_dtype ydt, void* stream);
+mxmoe_status fp8bw_grouped_gemm_dgrad_pow2(const uint8_t* qdy, const float* sdy,
+                                           const uint8_t* qwT, const float* sw,
+                                           const int32_t* offs, int32_t G, int64_t M, int64_t N, int64_t K,
+                                           void* dx, mxmoe_dtype dxdt, void* stream);
+mxmoe_status fp8bw_grouped_gemm_fwd_pow2_fp8feed(const uint8_t* qx, const float* sx,
+                                                 const uint8_t* qw, const float* sw,
+                                                 const int32_t* offs, int32_t G, int64_t M, int64_t N, int64_t K,
+                                                 void* y, mxmoe_dtype ydt, void* stream);
+mxmoe_status fp8bw_grouped_gemm_dgrad_pow2_fp8feed(const uint8_t* qdy, const float* sdy,
+                                                   const uint8_t* qwT, const float* sw,
+                                                   const int32_t* offs, int32_t G, int64_t M, int64_t N, int64_t K,
+                                                   void* dx, mxmoe_dtype dxdt, void* stream);
+
 /* Full-rate FP8 operand feed of the blockwise GEMMs (arguments as above; accuracy as the MX
  * *_fp8feed routines, each 128-slice partial truncated per run of products before its promotion). */
 mxmoe_status fp8bw_grouped_gemm_fwd_fp8feed(const uint8_t* qx, const float* sx,

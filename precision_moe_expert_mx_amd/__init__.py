@@ -23,6 +23,7 @@ __all__ = [
     "mx_grouped_gemm_dgrad_tiled", "mx_grouped_gemm_wgrad_tiled",
     "fp8bw_quantize_act_1x128", "fp8bw_quantize_weight_128x128",
     "fp8bw_grouped_gemm_fwd", "fp8bw_grouped_gemm_dgrad", "mxmoe_check_offsets",
+    "fp8bw_grouped_gemm_fwd_pow2", "fp8bw_grouped_gemm_dgrad_pow2",
     "fp8bw_colwise_ld_min", "fp8bw_quantize_colwise_128", "fp8bw_grouped_gemm_wgrad",
     "mxfp4_quantize_rowwise", "mxfp4_quantize_colwise", "mxfp4_grouped_gemm_fwd", "mxfp4_grouped_gemm_dgrad",
     "mxfp4_grouped_gemm_wgrad",
@@ -77,8 +78,11 @@ _SIGS = {
 for _n in ("mx_quantize_colwise", "mx_quantize_dual", "mx_grouped_gemm_fwd_swiglu", "mx_grouped_gemm_dgrad",
            "mx_grouped_gemm_wgrad"):
     _SIGS[_n + "_tiled"] = _SIGS[_n]
+# blockwise forward / dgrad for power-of-two scales (on the MX kernel): the same arguments
+_SIGS["fp8bw_grouped_gemm_fwd_pow2"] = _SIGS["fp8bw_grouped_gemm_fwd"]
+_SIGS["fp8bw_grouped_gemm_dgrad_pow2"] = _SIGS["fp8bw_grouped_gemm_dgrad"]
 # the full-rate FP8 operand feed: the same arguments as the precise entry points
-for _n in ("mx_grouped_gemm_fwd", "mx_grouped_gemm_dgrad", "mx_grouped_gemm_wgrad", "fp8bw_grouped_gemm_fwd",
+for _n in ("fp8bw_grouped_gemm_fwd_pow2", "fp8bw_grouped_gemm_dgrad_pow2", "mx_grouped_gemm_fwd", "mx_grouped_gemm_dgrad", "mx_grouped_gemm_wgrad", "fp8bw_grouped_gemm_fwd",
            "fp8bw_grouped_gemm_dgrad", "fp8bw_grouped_gemm_wgrad", "mx_grouped_gemm_dgrad_tiled",
            "mx_grouped_gemm_wgrad_tiled"):
     _SIGS[_n + "_fp8feed"] = _SIGS[_n]
@@ -468,27 +472,47 @@ def fp8bw_quantize_weight_128x128(w, q=None, s=None, qT=None, transposed: bool =
     return (q, s) if qT is None else (q, s, qT)
 
 
-def fp8bw_grouped_gemm_fwd(qx, sx, qw, sw, offs, N: int, out_dtype: str = "f32", y=None, stream=None, fast: bool = False):
+def _bw_fwd(name, qx, sx, qw, sw, offs, N, out_dtype, y, stream, fast):
     M, K = qx.shape
     G = offs.numel() - 1
     tdt, cdt = _out_dtype(out_dtype)
     y = _empty((M, N), tdt, qx) if y is None else y
-    _check(*_call(_gemm("fp8bw_grouped_gemm_fwd", fast), _ptr(qx), _ptr(sx), _ptr(qw), _ptr(sw), _ptr(offs),
-                                                                  G, M, N, K, _ptr(y), cdt, _stream_handle(stream)))
+    _check(*_call(_gemm(name, fast), _ptr(qx), _ptr(sx), _ptr(qw), _ptr(sw), _ptr(offs), G, M, N, K, _ptr(y), cdt,
+                  _stream_handle(stream)))
     return y
+
+
+def _bw_dgrad(name, qdy, sdy, qwT, sw, offs, K, out_dtype, dx, stream, fast):
+    M, N = qdy.shape
+    G = offs.numel() - 1
+    tdt, cdt = _out_dtype(out_dtype)
+    dx = _empty((M, K), tdt, qdy) if dx is None else dx
+    _check(*_call(_gemm(name, fast), _ptr(qdy), _ptr(sdy), _ptr(qwT), _ptr(sw), _ptr(offs), G, M, N, K, _ptr(dx),
+                  cdt, _stream_handle(stream)))
+    return dx
+
+
+def fp8bw_grouped_gemm_fwd(qx, sx, qw, sw, offs, N: int, out_dtype: str = "f32", y=None, stream=None, fast: bool = False):
+    """Y [M, N] from blockwise X (1x128 tiles) and W (128x128 blocks), promoted per 128-slice."""
+    return _bw_fwd("fp8bw_grouped_gemm_fwd", qx, sx, qw, sw, offs, N, out_dtype, y, stream, fast)
 
 
 def fp8bw_grouped_gemm_dgrad(qdy, sdy, qwT, sw, offs, K: int, out_dtype: str = "f32", dx=None, stream=None,
                              fast: bool = False):
     """dX [M, K] from blockwise dY (1x128 along N) and the transposed weight copy qwT [K, G*N]."""
-    M, N = qdy.shape
-    G = offs.numel() - 1
-    tdt, cdt = _out_dtype(out_dtype)
-    dx = _empty((M, K), tdt, qdy) if dx is None else dx
-    _check(*_call(_gemm("fp8bw_grouped_gemm_dgrad", fast), _ptr(qdy), _ptr(sdy), _ptr(qwT), _ptr(sw),
-                                                                      _ptr(offs), G, M, N, K, _ptr(dx), cdt,
-                                                                      _stream_handle(stream)))
-    return dx
+    return _bw_dgrad("fp8bw_grouped_gemm_dgrad", qdy, sdy, qwT, sw, offs, K, out_dtype, dx, stream, fast)
+
+
+def fp8bw_grouped_gemm_fwd_pow2(qx, sx, qw, sw, offs, N: int, out_dtype: str = "f32", y=None, stream=None,
+                                fast: bool = False):
+    """fp8bw_grouped_gemm_fwd for power-of-two scales (the _pow2 quantisers' output), on the MX kernel."""
+    return _bw_fwd("fp8bw_grouped_gemm_fwd_pow2", qx, sx, qw, sw, offs, N, out_dtype, y, stream, fast)
+
+
+def fp8bw_grouped_gemm_dgrad_pow2(qdy, sdy, qwT, sw, offs, K: int, out_dtype: str = "f32", dx=None, stream=None,
+                                  fast: bool = False):
+    """fp8bw_grouped_gemm_dgrad for power-of-two scales (the _pow2 quantisers' output), on the MX kernel."""
+    return _bw_dgrad("fp8bw_grouped_gemm_dgrad_pow2", qdy, sdy, qwT, sw, offs, K, out_dtype, dx, stream, fast)
 
 
 def fp8bw_colwise_ld_min(M: int, G: int) -> int:

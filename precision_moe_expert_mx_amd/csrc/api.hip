@@ -586,6 +586,64 @@ mxmoe_status fp8bw_grouped_gemm_fwd_fp8feed(const uint8_t* qx, const float* sx, 
                         (int)ydt, stream);
 }
 
+// Blockwise forward / dgrad with power-of-two scales on the MX kernel (the scale's exponent byte is its
+// E8M0 form): fp32 scale rows are K/32 (A: L/32) bytes long, so the MX kernel's byte strides apply.
+static mxmoe_status bw_pow2_common(int mode, const char* fn, int feed, const uint8_t* a, const float* sa,
+                                   const uint8_t* b, const float* sb, const int32_t* offs, int32_t G, int64_t M,
+                                   int64_t N, int64_t K, void* out, int dt, void* stream) {
+  TRY(check_gemm_common(fn, offs, G, M, N, K, out, dt));
+  TRY(check_ptr(fn, "A operand", a, 16));
+  TRY(check_ptr(fn, "A scales", sa, 4));
+  TRY(check_ptr(fn, "B operand", b, 16));
+  TRY(check_ptr(fn, "B scales", sb, 4));
+  GemmArgs p;
+  memset(&p, 0, sizeof p);
+  p.a = a; p.sa = sa; p.b = b; p.sb = sb; p.offs = offs; p.out = out;
+  p.M = M; p.N = N; p.K = K; p.G = G;
+  p.out_bf16 = dt == MXMOE_BF16;
+  p.feed = feed;
+  p.bw_pow2 = 1;
+  p.a_kstride = p.b_kstride = 128;
+  if (mode == kFwd) {
+    p.lda = K; p.ldsa = K / 32; p.ldb = K; p.ldsb = K / 32;
+  } else {
+    // B is the transposed weight copy [K, G*N]; its block scales keep the forward layout
+    p.lda = N; p.ldsa = N / 32; p.ldb = (int64_t)G * N; p.ldsb = K / 32;
+  }
+  TRY(check_strides(fn, p, 256));
+  if (M == 0) return ok();
+  TRY(check_device());
+  return launched(launch_mx_gemm(mode, p, (hipStream_t)stream), fn);
+}
+
+mxmoe_status fp8bw_grouped_gemm_fwd_pow2(const uint8_t* qx, const float* sx, const uint8_t* qw, const float* sw,
+                                         const int32_t* offs, int32_t G, int64_t M, int64_t N, int64_t K, void* y,
+                                         mxmoe_dtype ydt, void* stream) {
+  return bw_pow2_common(kFwd, "fp8bw_grouped_gemm_fwd_pow2", kFeedPrecise, qx, sx, qw, sw, offs, G, M, N, K, y,
+                        (int)ydt, stream);
+}
+
+mxmoe_status fp8bw_grouped_gemm_fwd_pow2_fp8feed(const uint8_t* qx, const float* sx, const uint8_t* qw,
+                                                 const float* sw, const int32_t* offs, int32_t G, int64_t M,
+                                                 int64_t N, int64_t K, void* y, mxmoe_dtype ydt, void* stream) {
+  return bw_pow2_common(kFwd, "fp8bw_grouped_gemm_fwd_pow2_fp8feed", kFeedFast, qx, sx, qw, sw, offs, G, M, N, K, y,
+                        (int)ydt, stream);
+}
+
+mxmoe_status fp8bw_grouped_gemm_dgrad_pow2(const uint8_t* qdy, const float* sdy, const uint8_t* qwT,
+                                           const float* sw, const int32_t* offs, int32_t G, int64_t M, int64_t N,
+                                           int64_t K, void* dx, mxmoe_dtype dxdt, void* stream) {
+  return bw_pow2_common(kDgrad, "fp8bw_grouped_gemm_dgrad_pow2", kFeedPrecise, qdy, sdy, qwT, sw, offs, G, M, N, K,
+                        dx, (int)dxdt, stream);
+}
+
+mxmoe_status fp8bw_grouped_gemm_dgrad_pow2_fp8feed(const uint8_t* qdy, const float* sdy, const uint8_t* qwT,
+                                                   const float* sw, const int32_t* offs, int32_t G, int64_t M,
+                                                   int64_t N, int64_t K, void* dx, mxmoe_dtype dxdt, void* stream) {
+  return bw_pow2_common(kDgrad, "fp8bw_grouped_gemm_dgrad_pow2_fp8feed", kFeedFast, qdy, sdy, qwT, sw, offs, G, M, N,
+                        K, dx, (int)dxdt, stream);
+}
+
 static mxmoe_status bw_wgrad_impl(const char* fn, int feed, const uint8_t* qdyT, const float* sdyT, const uint8_t* qxT,
                                   const float* sxT, int64_t ld, const int32_t* offs, int32_t G, int64_t M, int64_t N,
                                   int64_t K, void* dw, mxmoe_dtype dwdt, void* stream) {

@@ -229,6 +229,7 @@ struct GemmArgs {
   int32_t feed;       // GemmFeed
   int32_t scale_dword;  // MX: every row's scale bytes of a stage form aligned dwords
   int32_t fp4;          // MX operands are E2M1 (two per byte; leading dimensions in bytes)
+  int32_t bw_pow2;      // MX kernel on blockwise operands whose fp32 scales are powers of two (fwd, dgrad)
   // forward with the gated activation in the epilogue: out = Y bf16 [M, 2H] (gate | up), plus
   // H = silu(gate) * up MX-quantised row-wise into act_q [M, H] / act_s [M, H/32], and H in fp32 into
   // act_dbg [M, H] when not NULL

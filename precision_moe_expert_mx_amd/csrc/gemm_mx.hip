@@ -248,7 +248,11 @@ __device__ __forceinline__ void act_epilogue(const GemmArgs& p, const Tile& t, c
   }
 }
 
-template <int MODE, int FEED, bool SDW, bool FP4, bool ACT>
+// BWP2: blockwise operands with power-of-two fp32 scales (forward, dgrad; the SDW path): one fp32 per
+// row and 128-element stage for A (1x128 tiles), per 128x128 block for B.  Such a scale is exactly the
+// E8M0 scale 2^(exponent field - 127), so its exponent byte, repeated for the stage's four 32-blocks,
+// takes the place of the MX scale word and the stage multiplies exactly as an MX stage.
+template <int MODE, int FEED, bool SDW, bool FP4, bool ACT, bool BWP2 = false>
 __device__ __forceinline__ void run_tile(const GemmArgs& p, const Tile& t, char* lds) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
@@ -335,6 +339,20 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const Tile& t, char*
     else q = tid + NT * j;
     const int r = q & 255;
     s_src[j] = q < 256 ? sa + a_row(r) * p.ldsa + sa_col0 : sb + b_row(r) * p.ldsb + sb_col0;
+    if (BWP2 && q >= 256) {
+      // fp32 block scales [G N / 128, K / 128]: row stride ldsb = K / 32 bytes.  Forward: block row
+      // (g N + n) / 128, one fp32 per stage.  Dgrad (B rows k, the stages run over n): block column
+      // k / 128, block row g N / 128 + stage.
+      if (MODE == kFwd) s_src[j] = sb + (b_row(r) >> 7) * p.ldsb;
+      else s_src[j] = sb + (((int64_t)t.g * p.N) >> 7) * p.ldsb + (b_row(r) >> 7) * 4;
+    }
+  }
+  // bytes between the scales of consecutive stages (BWP2 dgrad B: one block row of scales)
+  int64_t s_step[NS];
+#pragma unroll
+  for (int j = 0; j < NS; ++j) {
+    const bool b_rows = (SDW ? 64 * (kScaleLoads * w + j) : tid + NT * j) >= 256;
+    s_step[j] = BWP2 && MODE == kDgrad && b_rows ? p.ldsb : SPS;
   }
   // Scale bytes [SPS ks, SPS ks + nv) of a row (nv < SPS only in the last wgrad stage; the rest read
   // as 0) land as SPS / 4 dwords, dword d of every row in plane d of the stage's scale area.  Register
@@ -414,7 +432,7 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const Tile& t, char*
       for (int j = 0; j < NS; ++j)
 #pragma unroll
         for (int d = 0; d < P; ++d)
-          dma4(s_src[j] + SPS * ks + 4 * d, ss + 2048 * d + 256 * (kScaleLoads * w + j));
+          dma4(s_src[j] + s_step[j] * ks + 4 * d, ss + 2048 * d + 256 * (kScaleLoads * w + j));
     }
   };
 
@@ -456,7 +474,9 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const Tile& t, char*
     }
   };
   auto sword_k = [&](const uint32_t* S, int r, const uint32_t (&keep)[SPS / 4], int word = 0) -> uint32_t {
-    if constexpr (ALIGNED_START) {
+    if constexpr (BWP2) {
+      return ((S[r] >> 23) & 0xFFu) * 0x01010101u;      // the power of two's exponent byte, 4 blocks
+    } else if constexpr (ALIGNED_START) {
       return S[512 * word + r] & keep[word];
     } else {
       return S[512 * word + r];
@@ -639,7 +659,7 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const Tile& t, char*
   }
 }
 
-template <int MODE, int FEED, bool SDW, bool FP4 = false, bool ACT = false>
+template <int MODE, int FEED, bool SDW, bool FP4 = false, bool ACT = false, bool BWP2 = false>
 __global__ __launch_bounds__(NT, 1) void mx_grouped_gemm_kernel(GemmArgs p) {
   __shared__ __attribute__((aligned(16))) char lds[kLds];
   Tile t;
@@ -655,7 +675,7 @@ __global__ __launch_bounds__(NT, 1) void mx_grouped_gemm_kernel(GemmArgs p) {
   t.col0 = uniform64(t.col0);
   t.col_end = uniform64(t.col_end);
   __syncthreads();                               // scheduler scratch is reused for operands
-  run_tile<MODE, FEED, SDW, FP4, ACT>(p, t, lds);
+  run_tile<MODE, FEED, SDW, FP4, ACT, BWP2>(p, t, lds);
 }
 
 static_assert(4 * (kMaxG + 1) * 4 <= kStage, "scheduler scratch must fit in the first stage");
@@ -691,6 +711,19 @@ hipError_t launch_mx_gemm(int mode, const GemmArgs& args, hipStream_t st) {
   // a multiple of 4 bytes (wgrad expert columns start at arbitrary 32-blocks)
   p.scale_dword = mode != kWgrad && p.ldsa % 4 == 0 && p.ldsb % 4 == 0 && (p.N / 32) % 4 == 0;
   const dim3 g((unsigned)grid);
+  if (p.bw_pow2) {
+    // blockwise operands with power-of-two scales (forward, dgrad): scale rows of aligned dwords
+    if (!p.scale_dword || mode == kWgrad || p.fp4 || p.act_q) return hipErrorInvalidValue;
+    if (mode == kFwd && p.feed == kFeedFast)
+      hipLaunchKernelGGL((mx_grouped_gemm_kernel<kFwd, kFeedFast, true, false, false, true>), g, dim3(NT), 0, st, p);
+    else if (mode == kFwd)
+      hipLaunchKernelGGL((mx_grouped_gemm_kernel<kFwd, kFeedPrecise, true, false, false, true>), g, dim3(NT), 0, st, p);
+    else if (p.feed == kFeedFast)
+      hipLaunchKernelGGL((mx_grouped_gemm_kernel<kDgrad, kFeedFast, true, false, false, true>), g, dim3(NT), 0, st, p);
+    else
+      hipLaunchKernelGGL((mx_grouped_gemm_kernel<kDgrad, kFeedPrecise, true, false, false, true>), g, dim3(NT), 0, st, p);
+    return hipGetLastError();
+  }
   if (mode == kFwd && p.act_q) {
     if (!p.scale_dword) return hipErrorInvalidValue;
     hipLaunchKernelGGL((mx_grouped_gemm_kernel<kFwd, kFeedPrecise, true, false, true>), g, dim3(NT), 0, st, p);

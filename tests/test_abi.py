@@ -204,6 +204,22 @@ def test_tiled_entry_points_need_a_pitch_multiple_of_128():
     assert st == 2 and "128" in msg
 
 
+def test_pow2_blockwise_entry_points_validate_like_the_blockwise_ones():
+    _, L = _lib()
+    ok_args = (A16, A16, A16b, A16b, A16, 4, 1024, 512, 256, A16, 0, None)
+    for fn in ("fp8bw_grouped_gemm_fwd_pow2", "fp8bw_grouped_gemm_fwd_pow2_fp8feed", "fp8bw_grouped_gemm_dgrad_pow2",
+               "fp8bw_grouped_gemm_dgrad_pow2_fp8feed"):
+        a = list(ok_args); a[7] = 500                 # N not a multiple of 128
+        st, msg = _status(L, fn, *a)
+        assert st == 2 and fn in msg, (fn, msg)
+        a = list(ok_args); a[10] = 0x101               # output dtype
+        assert _status(L, fn, *a)[0] == 4
+        a = list(ok_args); a[3] = BAD                  # B scales not 4-byte aligned
+        assert _status(L, fn, *a)[0] == 3
+        a = list(ok_args); a[6] = 0                    # M == 0: no-op
+        assert _status(L, fn, *a) == (0, "")
+
+
 def test_binding_refuses_cpu_tensors():
     m, _ = _lib()
     import torch

@@ -104,3 +104,43 @@ def test_gemms_on_power_of_two_operands():
         ok, worst, _ = oracle.check_gemm(host(dw), ref, bnd, "f32")
         assert ok, f"wgrad worst err/tol {worst}"
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("fast", [False, True])
+def test_pow2_forward_and_dgrad_on_the_mx_kernel(fast):
+    """fp8bw_grouped_gemm_fwd_pow2 / _dgrad_pow2: power-of-two blockwise scales folded into the operands
+    on the MX kernel, against the oracle's promoted blockwise products (within 1e-5 sum|ab|; the FP8
+    feed within its 2^-10 bound), on ragged experts (empty, 1, 17, 129 rows) and both output dtypes."""
+    m = require_gpu()
+    rng = np.random.default_rng(64)
+    rel = 2.0 ** -10 if fast else oracle.gemm.REL_TOL
+    for sizes, N, K in (([0, 5, 130, 1, 60], 256, 1024), ([129, 0, 17], 128, 256),
+                        ([700, 0, 129, 1, 513, 64], 384, 768)):
+        offs = routing_offsets(sizes)
+        M, G = int(offs[-1]), len(sizes)
+        x = random_bf16(rng, (M, K), outlier_frac=0.001, outlier_mult=1000.0)
+        w = random_bf16(rng, (G * N, K), std=0.02, outlier_frac=0.001)
+        dy = random_bf16(rng, (M, N), outlier_frac=0.001)
+        od = dev(offs)
+        qx, sx = m.fp8bw_quantize_act_1x128(dev(x), pow2=True)
+        qw, sw, qwT = m.fp8bw_quantize_weight_128x128(dev(w), transposed=True, pow2=True)
+        qd, sd = m.fp8bw_quantize_act_1x128(dev(dy), pow2=True)
+        xq = oracle.bw_quantize_act_1x128(x, pow2=True)
+        wq = oracle.bw_quantize_weight_128x128(w, pow2=True)
+        dq = oracle.bw_quantize_act_1x128(dy, pow2=True)
+        same_bytes((host(qx), host(sx), host(qw), host(sw), host(qwT), host(qd), host(sd)),
+                   (xq[0], xq[1], wq[0], wq[1], wq[0].T, dq[0], dq[1]), "pow2 operands")
+        for dt in ("f32", "bf16"):
+            y = m.fp8bw_grouped_gemm_fwd_pow2(qx, sx, qw, sw, od, N, dt, fast=fast)
+            ref, bnd = oracle.bw_gemm_fwd(xq[0], xq[1], wq[0], wq[1], offs, N)
+            got = host(y)
+            got = (got.astype(np.uint32) << 16).view(np.float32) if dt == "bf16" else got
+            ok, worst, _ = oracle.check_gemm(got, ref, bnd, dt, rel=rel)
+            assert ok, f"fwd_pow2 {sizes} {dt}: worst err/tol {worst:.3g}"
+            dx = m.fp8bw_grouped_gemm_dgrad_pow2(qd, sd, qwT, sw, od, K, dt, fast=fast)
+            ref, bnd = oracle.bw_gemm_dgrad(dq[0], dq[1], wq[0], wq[1], offs, N, K)
+            got = host(dx)
+            got = (got.astype(np.uint32) << 16).view(np.float32) if dt == "bf16" else got
+            ok, worst, _ = oracle.check_gemm(got, ref, bnd, dt, rel=rel)
+            assert ok, f"dgrad_pow2 {sizes} {dt}: worst err/tol {worst:.3g}"
+        torch.cuda.synchronize()
