@@ -619,7 +619,7 @@ def other_configs_leg(m, torch, steps=5, warmup=2):
 def blockwise_leg(m, torch, steps=5, sample_rows=256):
     """DeepSeek-style blockwise FP8 (1x128 activation tiles, 128x128 weight blocks, 128-token blocks
     for the weight gradient, fp32 scales, promotion every 128), also in its power-of-two scale mode
-    (forward and dgrad on the MX kernel, the scales folded into the operands), against MXFP8 on the same
+    (its GEMMs on the MX kernel, the scales folded into the operands), against MXFP8 on the same
     DeepSeek-V3-16B expert-layer tensors: forward, dgrad and wgrad, each recipe with its own
     quantisers.  Accuracy: relative Frobenius error of each recipe's fp32 Y, dX (sampled rows) and dW
     (two experts, sampled n and k) against fp64 products of the original bf16 tensors."""
@@ -642,7 +642,7 @@ def blockwise_leg(m, torch, steps=5, sample_rows=256):
                    M * K * QUANT_BYTES_PER_ELEM, ""),
                 Op("quant_w", "quant", lambda: bq.update(w=m.fp8bw_quantize_weight_128x128(w, transposed=True, pow2=p2)),
                    G * N * K * (QUANT_BYTES_PER_ELEM + 1), ""),
-                # power-of-two scales: forward and dgrad on the MX kernel (the _pow2 entry points)
+                # power-of-two scales: the GEMMs on the MX kernel (the _pow2 entry points)
                 Op("fwd", "gemm", lambda: bq.update(y=(m.fp8bw_grouped_gemm_fwd_pow2 if p2 else m.fp8bw_grouped_gemm_fwd)(
                     *bq["x"], *bq["w"][:2], offs, N, "f32")), f, ""),
                 Op("quant_dy", "quant", lambda: bq.update(dy=m.fp8bw_quantize_act_1x128(dy, pow2=p2)),
@@ -653,8 +653,8 @@ def blockwise_leg(m, torch, steps=5, sample_rows=256):
                    M * N * QUANT_BYTES_PER_ELEM, ""),
                 Op("quant_x_col", "quant", lambda: bq.update(xc=m.fp8bw_quantize_colwise_128(x, offs, ld=ldb, pow2=p2)),
                    M * K * QUANT_BYTES_PER_ELEM, ""),
-                Op("wgrad", "gemm", lambda: bq.update(dw=m.fp8bw_grouped_gemm_wgrad(*bq["dyc"], *bq["xc"], offs, M,
-                                                                                     "f32")), f, ""),
+                Op("wgrad", "gemm", lambda: bq.update(dw=(m.fp8bw_grouped_gemm_wgrad_pow2 if p2 else m.fp8bw_grouped_gemm_wgrad)(
+                    *bq["dyc"], *bq["xc"], offs, M, "f32")), f, ""),
             ]
         bq, bq2 = {}, {}
         ops_bw, ops_bw2 = bw_ops(bq, False), bw_ops(bq2, True)

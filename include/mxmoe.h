@@ -363,6 +363,16 @@ mxmoe_status fp8bw_grouped_gemm_dgrad_pow2_fp8feed(const uint8_t* qdy, const flo
                                                    const uint8_t* qwT, const float* sw,
                                                    const int32_t* offs, int32_t G, int64_t M, int64_t N, int64_t K,
                                                    void* dx, mxmoe_dtype dxdt, void* stream);
+/* fp8bw_grouped_gemm_wgrad_pow2[_fp8feed]: fp8bw_grouped_gemm_wgrad (arguments, layouts and errors as
+ * declared below) for power-of-two scales, on the same footing as the two above. */
+mxmoe_status fp8bw_grouped_gemm_wgrad_pow2(const uint8_t* qdyT, const float* sdyT,
+                                           const uint8_t* qxT, const float* sxT, int64_t ld,
+                                           const int32_t* offs, int32_t G, int64_t M, int64_t N, int64_t K,
+                                           void* dw, mxmoe_dtype dwdt, void* stream);
+mxmoe_status fp8bw_grouped_gemm_wgrad_pow2_fp8feed(const uint8_t* qdyT, const float* sdyT,
+                                                   const uint8_t* qxT, const float* sxT, int64_t ld,
+                                                   const int32_t* offs, int32_t G, int64_t M, int64_t N,
+                                                   int64_t K, void* dw, mxmoe_dtype dwdt, void* stream);
 
 /* Full-rate FP8 operand feed of the blockwise GEMMs (arguments as above; accuracy as the MX
  * *_fp8feed routines, each 128-slice partial truncated per run of products before its promotion). */

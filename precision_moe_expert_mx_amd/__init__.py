@@ -23,7 +23,7 @@ __all__ = [
     "mx_grouped_gemm_dgrad_tiled", "mx_grouped_gemm_wgrad_tiled",
     "fp8bw_quantize_act_1x128", "fp8bw_quantize_weight_128x128",
     "fp8bw_grouped_gemm_fwd", "fp8bw_grouped_gemm_dgrad", "mxmoe_check_offsets",
-    "fp8bw_grouped_gemm_fwd_pow2", "fp8bw_grouped_gemm_dgrad_pow2",
+    "fp8bw_grouped_gemm_fwd_pow2", "fp8bw_grouped_gemm_dgrad_pow2", "fp8bw_grouped_gemm_wgrad_pow2",
     "fp8bw_colwise_ld_min", "fp8bw_quantize_colwise_128", "fp8bw_grouped_gemm_wgrad",
     "mxfp4_quantize_rowwise", "mxfp4_quantize_colwise", "mxfp4_grouped_gemm_fwd", "mxfp4_grouped_gemm_dgrad",
     "mxfp4_grouped_gemm_wgrad",
@@ -81,8 +81,9 @@ for _n in ("mx_quantize_colwise", "mx_quantize_dual", "mx_grouped_gemm_fwd_swigl
 # blockwise forward / dgrad for power-of-two scales (on the MX kernel): the same arguments
 _SIGS["fp8bw_grouped_gemm_fwd_pow2"] = _SIGS["fp8bw_grouped_gemm_fwd"]
 _SIGS["fp8bw_grouped_gemm_dgrad_pow2"] = _SIGS["fp8bw_grouped_gemm_dgrad"]
+_SIGS["fp8bw_grouped_gemm_wgrad_pow2"] = _SIGS["fp8bw_grouped_gemm_wgrad"]
 # the full-rate FP8 operand feed: the same arguments as the precise entry points
-for _n in ("fp8bw_grouped_gemm_fwd_pow2", "fp8bw_grouped_gemm_dgrad_pow2", "mx_grouped_gemm_fwd", "mx_grouped_gemm_dgrad", "mx_grouped_gemm_wgrad", "fp8bw_grouped_gemm_fwd",
+for _n in ("fp8bw_grouped_gemm_fwd_pow2", "fp8bw_grouped_gemm_dgrad_pow2", "fp8bw_grouped_gemm_wgrad_pow2", "mx_grouped_gemm_fwd", "mx_grouped_gemm_dgrad", "mx_grouped_gemm_wgrad", "fp8bw_grouped_gemm_fwd",
            "fp8bw_grouped_gemm_dgrad", "fp8bw_grouped_gemm_wgrad", "mx_grouped_gemm_dgrad_tiled",
            "mx_grouped_gemm_wgrad_tiled"):
     _SIGS[_n + "_fp8feed"] = _SIGS[_n]
@@ -538,18 +539,27 @@ def fp8bw_quantize_colwise_128(x, offs=None, G: int = 1, ld: Optional[int] = Non
     return qT, sT
 
 
-def fp8bw_grouped_gemm_wgrad(qdyT, sdyT, qxT, sxT, offs, M: int, out_dtype: str = "f32", dw=None, stream=None,
-                             fast: bool = False):
-    """dW [G, N, K] from the column-wise blockwise copies of dY [N, ld] and X [K, ld]."""
+def _bw_wgrad(name, qdyT, sdyT, qxT, sxT, offs, M, out_dtype, dw, stream, fast):
     N, ld = qdyT.shape
     K = qxT.shape[0]
     G = offs.numel() - 1
     tdt, cdt = _out_dtype(out_dtype)
     dw = _empty((G, N, K), tdt, qdyT) if dw is None else dw
-    _check(*_call(_gemm("fp8bw_grouped_gemm_wgrad", fast), _ptr(qdyT), _ptr(sdyT), _ptr(qxT), _ptr(sxT), ld,
-                                                                      _ptr(offs), G, M, N, K, _ptr(dw), cdt,
-                                                                      _stream_handle(stream)))
+    _check(*_call(_gemm(name, fast), _ptr(qdyT), _ptr(sdyT), _ptr(qxT), _ptr(sxT), ld, _ptr(offs), G, M, N, K,
+                  _ptr(dw), cdt, _stream_handle(stream)))
     return dw
+
+
+def fp8bw_grouped_gemm_wgrad(qdyT, sdyT, qxT, sxT, offs, M: int, out_dtype: str = "f32", dw=None, stream=None,
+                             fast: bool = False):
+    """dW [G, N, K] from the column-wise blockwise copies of dY [N, ld] and X [K, ld]."""
+    return _bw_wgrad("fp8bw_grouped_gemm_wgrad", qdyT, sdyT, qxT, sxT, offs, M, out_dtype, dw, stream, fast)
+
+
+def fp8bw_grouped_gemm_wgrad_pow2(qdyT, sdyT, qxT, sxT, offs, M: int, out_dtype: str = "f32", dw=None, stream=None,
+                                  fast: bool = False):
+    """fp8bw_grouped_gemm_wgrad for power-of-two scales (the _pow2 quantisers' output), on the MX kernel."""
+    return _bw_wgrad("fp8bw_grouped_gemm_wgrad_pow2", qdyT, sdyT, qxT, sxT, offs, M, out_dtype, dw, stream, fast)
 
 
 def mxmoe_check_offsets(offs, M: int, stream=None) -> None:

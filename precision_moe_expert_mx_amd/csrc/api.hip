@@ -644,6 +644,48 @@ mxmoe_status fp8bw_grouped_gemm_dgrad_pow2_fp8feed(const uint8_t* qdy, const flo
                         K, dx, (int)dxdt, stream);
 }
 
+static mxmoe_status fp8bw_grouped_gemm_wgrad_pow2_impl(const char* fn, int feed, const uint8_t* qdyT, const float* sdyT,
+                                                const uint8_t* qxT, const float* sxT, int64_t ld, const int32_t* offs,
+                                                int32_t G, int64_t M, int64_t N, int64_t K, void* dw, int dt,
+                                                void* stream) {
+  if (G >= 1 && M >= 0 && (ld % 128 || ld < fp8bw_colwise_ld_min(M, G)))
+    return fail(MXMOE_ERR_SHAPE, "%s: ld=%lld must be a multiple of 128 and >= fp8bw_colwise_ld_min(M, G)=%lld", fn,
+                (long long)ld, (long long)fp8bw_colwise_ld_min(M, G));
+  TRY(check_gemm_common(fn, offs, G, M, N, K, dw, dt));
+  TRY(check_ptr(fn, "A operand", qdyT, 16));
+  TRY(check_ptr(fn, "A scales", sdyT, 4));
+  TRY(check_ptr(fn, "B operand", qxT, 16));
+  TRY(check_ptr(fn, "B scales", sxT, 4));
+  GemmArgs p;
+  memset(&p, 0, sizeof p);
+  p.a = qdyT; p.sa = sdyT; p.b = qxT; p.sb = sxT; p.offs = offs; p.out = dw;
+  p.M = M; p.N = N; p.K = K; p.G = G;
+  p.out_bf16 = dt == MXMOE_BF16;
+  p.feed = feed;
+  p.bw_pow2 = 1;
+  p.a_kstride = p.b_kstride = 128;
+  // fp32 scale rows of ld / 128 floats = ld / 32 bytes, the MX kernel's byte stride
+  p.lda = ld; p.ldsa = ld / 32; p.ldb = ld; p.ldsb = ld / 32;
+  TRY(check_strides(fn, p, 256));
+  TRY(check_device());
+  return launched(launch_mx_gemm(kWgrad, p, (hipStream_t)stream), fn);
+}
+
+mxmoe_status fp8bw_grouped_gemm_wgrad_pow2(const uint8_t* qdyT, const float* sdyT, const uint8_t* qxT,
+                                           const float* sxT, int64_t ld, const int32_t* offs, int32_t G, int64_t M,
+                                           int64_t N, int64_t K, void* dw, mxmoe_dtype dwdt, void* stream) {
+  return fp8bw_grouped_gemm_wgrad_pow2_impl("fp8bw_grouped_gemm_wgrad_pow2", kFeedPrecise, qdyT, sdyT, qxT, sxT, ld,
+                                            offs, G, M, N, K, dw, (int)dwdt, stream);
+}
+
+mxmoe_status fp8bw_grouped_gemm_wgrad_pow2_fp8feed(const uint8_t* qdyT, const float* sdyT, const uint8_t* qxT,
+                                                   const float* sxT, int64_t ld, const int32_t* offs, int32_t G,
+                                                   int64_t M, int64_t N, int64_t K, void* dw, mxmoe_dtype dwdt,
+                                                   void* stream) {
+  return fp8bw_grouped_gemm_wgrad_pow2_impl("fp8bw_grouped_gemm_wgrad_pow2_fp8feed", kFeedFast, qdyT, sdyT, qxT, sxT,
+                                            ld, offs, G, M, N, K, dw, (int)dwdt, stream);
+}
+
 static mxmoe_status bw_wgrad_impl(const char* fn, int feed, const uint8_t* qdyT, const float* sdyT, const uint8_t* qxT,
                                   const float* sxT, int64_t ld, const int32_t* offs, int32_t G, int64_t M, int64_t N,
                                   int64_t K, void* dw, mxmoe_dtype dwdt, void* stream) {

@@ -248,10 +248,12 @@ __device__ __forceinline__ void act_epilogue(const GemmArgs& p, const Tile& t, c
   }
 }
 
-// BWP2: blockwise operands with power-of-two fp32 scales (forward, dgrad; the SDW path): one fp32 per
-// row and 128-element stage for A (1x128 tiles), per 128x128 block for B.  Such a scale is exactly the
-// E8M0 scale 2^(exponent field - 127), so its exponent byte, repeated for the stage's four 32-blocks,
-// takes the place of the MX scale word and the stage multiplies exactly as an MX stage.
+// BWP2: blockwise operands with power-of-two fp32 scales (the SDW path): one fp32 per row and
+// 128-element stage for A (1x128 tiles) and for both wgrad operands (128-token blocks), per 128x128
+// block for the forward / dgrad B.  Such a scale is exactly the E8M0 scale 2^(exponent field - 127),
+// so its exponent byte, repeated for the stage's four 32-blocks, takes the place of the MX scale word
+// and the stage multiplies exactly as an MX stage.  The wgrad tile list counts 128-token blocks
+// (experts start on a 128-column boundary of the blockwise layout).
 template <int MODE, int FEED, bool SDW, bool FP4, bool ACT, bool BWP2 = false>
 __device__ __forceinline__ void run_tile(const GemmArgs& p, const Tile& t, char* lds) {
   const int tid = threadIdx.x;
@@ -272,7 +274,8 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const Tile& t, char*
 
   // ---- operand geometry (contraction offsets in bytes; scale offsets in 32-blocks) ------------
   const int f = ALIGNED_START && t.nblk > 0 ? (int)((t.col0 / 32) & 3) : 0;   // leading blocks
-  const int nblk_e = t.nblk + f;                                                // wgrad: blocks looped over
+  // wgrad: 32-blocks looped over (BWP2: the tile list counts 128-token blocks, and f == 0)
+  const int nblk_e = (BWP2 ? 4 : 1) * t.nblk + f;
   int64_t L;
   if (MODE == kFwd) L = p.K / EPB;
   else if (MODE == kDgrad) L = p.N / EPB;
@@ -339,7 +342,7 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const Tile& t, char*
     else q = tid + NT * j;
     const int r = q & 255;
     s_src[j] = q < 256 ? sa + a_row(r) * p.ldsa + sa_col0 : sb + b_row(r) * p.ldsb + sb_col0;
-    if (BWP2 && q >= 256) {
+    if (BWP2 && MODE != kWgrad && q >= 256) {
       // fp32 block scales [G N / 128, K / 128]: row stride ldsb = K / 32 bytes.  Forward: block row
       // (g N + n) / 128, one fp32 per stage.  Dgrad (B rows k, the stages run over n): block column
       // k / 128, block row g N / 128 + stage.
@@ -663,7 +666,8 @@ template <int MODE, int FEED, bool SDW, bool FP4 = false, bool ACT = false, bool
 __global__ __launch_bounds__(NT, 1) void mx_grouped_gemm_kernel(GemmArgs p) {
   __shared__ __attribute__((aligned(16))) char lds[kLds];
   Tile t;
-  if (!decode_grouped_tile<MODE, MODE == kWgrad || ACT, BM, BN, NT, 32>(p, lds, t)) return;     // uniform across the workgroup
+  // (the blockwise power-of-two wgrad lays experts out in 128-token blocks)
+  if (!decode_grouped_tile<MODE, MODE == kWgrad || ACT, BM, BN, NT, BWP2 ? 128 : 32>(p, lds, t)) return;
   // the tile's fields are the same in every lane: say so, so that everything derived from them (operand
   // bases, loop bounds) lives in scalar registers
   t.g = __builtin_amdgcn_readfirstlane(t.g);
@@ -712,9 +716,13 @@ hipError_t launch_mx_gemm(int mode, const GemmArgs& args, hipStream_t st) {
   p.scale_dword = mode != kWgrad && p.ldsa % 4 == 0 && p.ldsb % 4 == 0 && (p.N / 32) % 4 == 0;
   const dim3 g((unsigned)grid);
   if (p.bw_pow2) {
-    // blockwise operands with power-of-two scales (forward, dgrad): scale rows of aligned dwords
-    if (!p.scale_dword || mode == kWgrad || p.fp4 || p.act_q) return hipErrorInvalidValue;
-    if (mode == kFwd && p.feed == kFeedFast)
+    // blockwise operands with power-of-two scales: scale rows of aligned dwords
+    if (p.fp4 || p.act_q || p.ldsa % 4 || p.ldsb % 4 || (mode != kWgrad && !p.scale_dword)) return hipErrorInvalidValue;
+    if (mode == kWgrad && p.feed == kFeedFast)
+      hipLaunchKernelGGL((mx_grouped_gemm_kernel<kWgrad, kFeedFast, true, false, false, true>), g, dim3(NT), 0, st, p);
+    else if (mode == kWgrad)
+      hipLaunchKernelGGL((mx_grouped_gemm_kernel<kWgrad, kFeedPrecise, true, false, false, true>), g, dim3(NT), 0, st, p);
+    else if (mode == kFwd && p.feed == kFeedFast)
       hipLaunchKernelGGL((mx_grouped_gemm_kernel<kFwd, kFeedFast, true, false, false, true>), g, dim3(NT), 0, st, p);
     else if (mode == kFwd)
       hipLaunchKernelGGL((mx_grouped_gemm_kernel<kFwd, kFeedPrecise, true, false, false, true>), g, dim3(NT), 0, st, p);

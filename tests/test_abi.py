@@ -218,6 +218,12 @@ def test_pow2_blockwise_entry_points_validate_like_the_blockwise_ones():
         assert _status(L, fn, *a)[0] == 3
         a = list(ok_args); a[6] = 0                    # M == 0: no-op
         assert _status(L, fn, *a) == (0, "")
+    for fn in ("fp8bw_grouped_gemm_wgrad_pow2", "fp8bw_grouped_gemm_wgrad_pow2_fp8feed"):
+        # fp8bw_colwise_ld_min(1024, 4) = 1536: 1568 is not a multiple of 128, 1408 is too small
+        st, msg = _status(L, fn, A16, A16, A16b, A16b, 1568, A16, 4, 1024, 512, 256, A16, 0, None)
+        assert st == 2 and fn in msg and "128" in msg, (fn, msg)
+        assert _status(L, fn, A16, A16, A16b, A16b, 1408, A16, 4, 1024, 512, 256, A16, 0, None)[0] == 2
+        assert _status(L, fn, A16, A16, A16b, BAD, 1536, A16, 4, 1024, 512, 256, A16, 0, None)[0] == 3
 
 
 def test_binding_refuses_cpu_tensors():

@@ -107,10 +107,11 @@ def test_gemms_on_power_of_two_operands():
 
 
 @pytest.mark.parametrize("fast", [False, True])
-def test_pow2_forward_and_dgrad_on_the_mx_kernel(fast):
-    """fp8bw_grouped_gemm_fwd_pow2 / _dgrad_pow2: power-of-two blockwise scales folded into the operands
+def test_pow2_gemms_on_the_mx_kernel(fast):
+    """fp8bw_grouped_gemm_{fwd,dgrad,wgrad}_pow2: power-of-two blockwise scales folded into the operands
     on the MX kernel, against the oracle's promoted blockwise products (within 1e-5 sum|ab|; the FP8
-    feed within its 2^-10 bound), on ragged experts (empty, 1, 17, 129 rows) and both output dtypes."""
+    feed within its 2^-10 bound), on ragged experts (empty, 1, 17, 129 rows) and both output dtypes;
+    the weight gradient also with a padded leading dimension (empty experts give zeros)."""
     m = require_gpu()
     rng = np.random.default_rng(64)
     rel = 2.0 ** -10 if fast else oracle.gemm.REL_TOL
@@ -143,4 +144,16 @@ def test_pow2_forward_and_dgrad_on_the_mx_kernel(fast):
             got = (got.astype(np.uint32) << 16).view(np.float32) if dt == "bf16" else got
             ok, worst, _ = oracle.check_gemm(got, ref, bnd, dt, rel=rel)
             assert ok, f"dgrad_pow2 {sizes} {dt}: worst err/tol {worst:.3g}"
+        for extra in (0, 256):
+            ld = oracle.bw_colwise_ld_min(M, G) + extra
+            qdT, sdT = m.fp8bw_quantize_colwise_128(dev(dy), od, ld=ld, pow2=True)
+            qxT, sxT = m.fp8bw_quantize_colwise_128(dev(x), od, ld=ld, pow2=True)
+            cd = oracle.bw_quantize_colwise_128(dy, offs, ld, pow2=True)
+            cx = oracle.bw_quantize_colwise_128(x, offs, ld, pow2=True)
+            same_bytes((host(qdT), host(sdT), host(qxT), host(sxT)), (cd[0], cd[1], cx[0], cx[1]), "pow2 128-token")
+            dw = torch.full((G, N, K), float("nan"), dtype=torch.float32, device="cuda")
+            m.fp8bw_grouped_gemm_wgrad_pow2(qdT, sdT, qxT, sxT, od, M, "f32", dw=dw, fast=fast)
+            ref, bnd = oracle.bw_gemm_wgrad(cd[0], cd[1], cx[0], cx[1], offs, N, K)
+            ok, worst, _ = oracle.check_gemm(host(dw), ref, bnd, "f32", rel=rel)
+            assert ok, f"wgrad_pow2 {sizes} ld {ld}: worst err/tol {worst:.3g}"
         torch.cuda.synchronize()
