@@ -311,32 +311,54 @@ def test_blockwise_fp8_feed():
     print("bw fast wgrad", _check(_gpu_out(dw), ref, bnd, "f32", "bw fast wgrad", rel=FAST_REL))
 
 
-def test_blockwise_full_size_sampled():
-    """The blockwise recipe on the DeepSeek-V3-16B layer tensors (sampled rows)."""
+@pytest.mark.parametrize("pow2", [False, True])
+def test_blockwise_full_size_sampled(pow2):
+    """The blockwise recipe on the DeepSeek-V3-16B layer tensors (sampled rows); with power-of-two
+    scales through the _pow2 GEMMs (the MX kernel), whose weight gradient is also sampled (two experts,
+    sampled n and k)."""
     m = require_gpu()
     wl = make_workload("dsv3_16b_blockwise")
     rng = np.random.default_rng(37)
+    fwd = m.fp8bw_grouped_gemm_fwd_pow2 if pow2 else m.fp8bw_grouped_gemm_fwd
+    dgrad = m.fp8bw_grouped_gemm_dgrad_pow2 if pow2 else m.fp8bw_grouped_gemm_dgrad
     for lay in wl.layers:
         offs_d = dev(lay.offs)
         rows = np.unique(rng.choice(lay.M, 64, replace=False))
-        qx, sx = m.fp8bw_quantize_act_1x128(dev(lay.x))
+        qx, sx = m.fp8bw_quantize_act_1x128(dev(lay.x), pow2=pow2)
         w2 = lay.w.reshape(-1, lay.K)
-        qw, sw, qwT = m.fp8bw_quantize_weight_128x128(dev(w2), transposed=True)
-        y = m.fp8bw_grouped_gemm_fwd(qx, sx, qw, sw, offs_d, lay.N)
+        qw, sw, qwT = m.fp8bw_quantize_weight_128x128(dev(w2), transposed=True, pow2=pow2)
+        y = fwd(qx, sx, qw, sw, offs_d, lay.N)
         hqw, hsw = host(qw), host(sw)
-        same_bytes((host(qx)[rows], host(sx)[rows]), oracle.bw_quantize_act_1x128(lay.x[rows]), "bw X 1x128")
+        same_bytes((host(qx)[rows], host(sx)[rows]), oracle.bw_quantize_act_1x128(lay.x[rows], pow2=pow2), "bw X 1x128")
         hqwT = host(qwT)
         for band in rng.choice(w2.shape[0] // 128, 4, replace=False):       # sampled 128-row weight bands
             r = slice(128 * band, 128 * band + 128)
-            wq = oracle.bw_quantize_weight_128x128(w2[r])
+            wq = oracle.bw_quantize_weight_128x128(w2[r], pow2=pow2)
             same_bytes((hqw[r], hsw[band:band + 1], hqwT[:, r]), (wq[0], wq[1], wq[0].T), "bw W 128x128")
         ref, bnd = oracle.bw_gemm_fwd(host(qx), host(sx), hqw, hsw, lay.offs, lay.N, rows=rows)
         print(lay.name, "bw fwd", _check(_gpu_out(y)[rows], ref, bnd, "f32", "bw fwd"))
-        qd, sd = m.fp8bw_quantize_act_1x128(dev(lay.dy))
-        same_bytes((host(qd)[rows], host(sd)[rows]), oracle.bw_quantize_act_1x128(lay.dy[rows]), "bw dY 1x128")
-        dx = m.fp8bw_grouped_gemm_dgrad(qd, sd, qwT, sw, offs_d, lay.K)
+        qd, sd = m.fp8bw_quantize_act_1x128(dev(lay.dy), pow2=pow2)
+        same_bytes((host(qd)[rows], host(sd)[rows]), oracle.bw_quantize_act_1x128(lay.dy[rows], pow2=pow2), "bw dY 1x128")
+        dx = dgrad(qd, sd, qwT, sw, offs_d, lay.K)
         ref, bnd = oracle.bw_gemm_dgrad(host(qd), host(sd), hqw, hsw, lay.offs, lay.N, lay.K, rows=rows)
         print(lay.name, "bw dgrad", _check(_gpu_out(dx)[rows], ref, bnd, "f32", "bw dgrad"))
+        if pow2:
+            ld = m.fp8bw_colwise_ld_min(lay.M, lay.G)
+            qdT, sdT = m.fp8bw_quantize_colwise_128(dev(lay.dy), offs_d, ld=ld, pow2=True)
+            qxT, sxT = m.fp8bw_quantize_colwise_128(dev(lay.x), offs_d, ld=ld, pow2=True)
+            dw = m.fp8bw_grouped_gemm_wgrad_pow2(qdT, sdT, qxT, sxT, offs_d, lay.M, "f32")
+            sizes = np.diff(lay.offs.astype(np.int64))
+            groups = [int(np.argmax(sizes)), int(rng.choice(np.flatnonzero(sizes > 0)))]
+            n_idx = np.sort(rng.choice(lay.N, 24, replace=False))
+            k_idx = np.sort(rng.choice(lay.K, 24, replace=False))
+            hd = (host(qdT), host(sdT), host(qxT), host(sxT))
+            same_bytes((hd[0][n_idx], hd[1][n_idx]), oracle.bw_quantize_colwise_128(lay.dy[:, n_idx], lay.offs, ld, pow2=True),
+                       "bw dY 128-token")
+            same_bytes((hd[2][k_idx], hd[3][k_idx]), oracle.bw_quantize_colwise_128(lay.x[:, k_idx], lay.offs, ld, pow2=True),
+                       "bw X 128-token")
+            ref, bnd = oracle.bw_gemm_wgrad(*hd, lay.offs, lay.N, lay.K, groups=groups, n_idx=n_idx, k_idx=k_idx)
+            got = _gpu_out(dw)[np.asarray(groups)][:, n_idx][:, :, k_idx]
+            print(lay.name, "bw wgrad", _check(got, ref, bnd, "f32", "bw wgrad"))
         torch.cuda.empty_cache()
 
 
