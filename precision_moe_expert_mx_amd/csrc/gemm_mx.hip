@@ -19,7 +19,10 @@
 // stage s is multiplied (the precise feed issues them after its first 32-block's MFMAs, so that a stage
 // opens with LDS reads, widening and MFMAs).  Each load is a per-tile 32-bit lane offset from a
 // wave-uniform base in scalar registers that advances by the stage, so issuing costs no vector
-// arithmetic.  LDS rows are 128 bytes with 16-byte chunks XOR-swizzled by row.
+// arithmetic.  LDS rows are 128 bytes with 16-byte chunks XOR-swizzled by row.  A column-wise operand
+// may be in the 128-byte tiled layout (a stage of a row is then one 128-byte piece of tile ks; the
+// stage advance is the operand's chunk stride).  The output tile leaves through LDS as whole row
+// pieces (store_tile_rows).
 //
 // Operand feeds (same tiling and LDS staging):
 //  * precise (default): each lane reads 16 consecutive bytes of one MX block, widens them exactly to
