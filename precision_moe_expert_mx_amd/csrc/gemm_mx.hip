@@ -53,17 +53,11 @@ namespace {
 
 using Tile = GroupTile;
 
-#ifndef MXMOE_WAVES_M
-#define MXMOE_WAVES_M 2
-#endif
-#ifndef MXMOE_WAVES_N
-#define MXMOE_WAVES_N 4
-#endif
 constexpr int BM = 256;                          // A rows per tile
 constexpr int BN = 256;                          // B rows per tile (output columns)
 constexpr int BK = 128;                          // contraction elements (bytes) per stage
-constexpr int kWavesM = MXMOE_WAVES_M;           // waves along the A rows of the tile
-constexpr int kWavesN = MXMOE_WAVES_N;           // waves along the B rows
+constexpr int kWavesM = 2;                       // waves along the A rows of the tile
+constexpr int kWavesN = 4;                       // waves along the B rows
 constexpr int kWaves = kWavesM * kWavesN;
 constexpr int NT = 64 * kWaves;                  // threads per workgroup
 constexpr int WM = BM / kWavesM;                 // outputs per wave along A rows
@@ -77,16 +71,13 @@ constexpr int kStage = kStageA + BN * BK;        // 64 KiB
 constexpr int kScaleStage = (BM + BN) * 4;       // four E8M0 bytes per operand row (E4M3)
 constexpr int kScaleStage4 = (BM + BN) * 8;      // eight E8M0 bytes per operand row (E2M1), two dword planes
 constexpr int kLds = 2 * kStage + 2 * kScaleStage4;
-#ifndef MXMOE_LDS_SWZ
-#define MXMOE_LDS_SWZ(r) (((r) >> 1) & 7)
-#endif
 
 typedef float v16f __attribute__((ext_vector_type(16)));
 
 
 // LDS rows of 128 bytes; 16-byte chunk c of row r sits at chunk position c ^ swz(r), so that the
 // lanes of one 16-byte LDS read (consecutive rows, same logical chunk) hit distinct banks.
-__device__ __forceinline__ int swz(int r) { return MXMOE_LDS_SWZ(r); }
+__device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
 __device__ __forceinline__ int lds_off(int r, int c) { return r * BK + ((c ^ swz(r)) << 4); }
 
 // Gated forward epilogue (precise feed, 32x32 fragments, 8 waves 2 x 4).  Waves wn = 0, 1 hold the
