@@ -15,14 +15,14 @@
 // Tiling: 256 x 256 output tile per workgroup of 8 waves (2 along A rows x 4 along B rows, 128 x 64
 // outputs per wave).  The contraction advances 128 bytes (four MX blocks) per stage.  Operand bytes
 // and scale bytes go global -> LDS by direct-to-LDS loads (no register staging), two stages in LDS:
-// the loads of stage s+1 are issued right after the barrier that publishes stage s, and land while
-// stage s is multiplied (the precise feed issues them after its first 32-block's MFMAs, so that a stage
-// opens with LDS reads, widening and MFMAs).  Each load is a per-tile 32-bit lane offset from a
-// wave-uniform base in scalar registers that advances by the stage, so issuing costs no vector
-// arithmetic.  LDS rows are 128 bytes with 16-byte chunks XOR-swizzled by row.  A column-wise operand
-// may be in the 128-byte tiled layout (a stage of a row is then one 128-byte piece of tile ks; the
-// stage advance is the operand's chunk stride).  The output tile leaves through LDS as whole row
-// pieces (store_tile_rows).
+// the loads of stage s+1 are issued early in stage s, after the barrier that publishes it, and land
+// while stage s is multiplied (the precise feed issues them after its first 32-block's MFMAs, the FP8
+// feed inside its first MFMA group, so that a stage opens with LDS reads).  Each load is a per-tile
+// 32-bit lane offset from a wave-uniform base in scalar registers that advances by the stage, so
+// issuing costs no vector arithmetic.  LDS rows are 128 bytes with 16-byte chunks XOR-swizzled by
+// row.  A column-wise operand may be in the 128-byte tiled layout (a stage of a row is then one
+// 128-byte piece of tile ks; the stage advance is the operand's chunk stride).  The output tile leaves
+// through LDS as whole row pieces (store_tile_rows).
 //
 // Operand feeds (same tiling and LDS staging):
 //  * precise (default): each lane reads 16 consecutive bytes of one MX block, widens them exactly to
@@ -391,28 +391,29 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const Tile& t, char*
     }
   };
 
-  auto issue = [&](int ks) {
+  // Loads of stage ks into buffer ks % 2 (which no wave reads any more): issue_rows moves chunk row j of
+  // both operands (the FP8 loop issues them inside its first MFMA group), issue_scales the stage's
+  // scale bytes.
+  auto issue_rows = [&](int ks, int j) {
     char* st = lds + (ks & 1) * kStage;
-    char* ss = lds + 2 * kStage + (ks & 1) * kSStage;
-    const int64_t koff = (int64_t)ks * BK;
-    const int64_t koff_a = (int64_t)ks * p.a_kstride, koff_b = (int64_t)ks * p.b_kstride;
     // wgrad: chunks outside the expert's blocks, bytes [lim_lo, lim_hi) of the stage's rows, are not
     // loaded (zeroed where they would have landed)
+    const int64_t koff = (int64_t)ks * BK;
     const int lim_hi = (int)min(L - koff, (int64_t)BK);
     const int lim_lo = ks == 0 ? (int)L0 : 0;
-#pragma unroll
-    for (int j = 0; j < ND; ++j) {
-      const int c = 16 * dchunk(j);
-      if (MODE != kWgrad || (c < lim_hi && c >= lim_lo)) {
-        dma16s(a_off[j], a_base + koff_a, st + (kLoadRows * w + 8 * j) * BK);
-        dma16s(b_off[j], b_base + koff_b, st + kStageA + (kLoadRows * w + 8 * j) * BK);
-      } else {
-        // a chunk outside the expert's blocks: zeros where the load would have landed (the buffer is
-        // free when a stage is issued, and the barrier that publishes the stage waits for LDS stores)
-        *(uint4*)(st + (kLoadRows * w + 8 * j) * BK + 16 * lane) = make_uint4(0, 0, 0, 0);
-        *(uint4*)(st + kStageA + (kLoadRows * w + 8 * j) * BK + 16 * lane) = make_uint4(0, 0, 0, 0);
-      }
+    const int c = 16 * dchunk(j);
+    if (MODE != kWgrad || (c < lim_hi && c >= lim_lo)) {
+      dma16s(a_off[j], a_base + (int64_t)ks * p.a_kstride, st + (kLoadRows * w + 8 * j) * BK);
+      dma16s(b_off[j], b_base + (int64_t)ks * p.b_kstride, st + kStageA + (kLoadRows * w + 8 * j) * BK);
+    } else {
+      // a chunk outside the expert's blocks: zeros where the load would have landed (the buffer is
+      // free when a stage is issued, and the barrier that publishes the stage waits for LDS stores)
+      *(uint4*)(st + (kLoadRows * w + 8 * j) * BK + 16 * lane) = make_uint4(0, 0, 0, 0);
+      *(uint4*)(st + kStageA + (kLoadRows * w + 8 * j) * BK + 16 * lane) = make_uint4(0, 0, 0, 0);
     }
+  };
+  auto issue_scales = [&](int ks) {
+    char* ss = lds + 2 * kStage + (ks & 1) * kSStage;
     if constexpr (ALIGNED_START) {
       // the stage's first scale dword, and the second (E2M1) only when the stage's blocks reach into
       // it (so no load passes the expert's bytes of the row)
@@ -450,7 +451,9 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const Tile& t, char*
 
   uint32_t s_w[NS][P + 1];                       // register-staged scale words of the next stage
   if (nsteps > 0) {
-    issue(0);
+#pragma unroll
+    for (int j = 0; j < ND; ++j) issue_rows(0, j);
+    issue_scales(0);
     if (!SDW) {
       gather_scales(0, s_w);
       put_scales(0, s_w);
@@ -483,21 +486,34 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const Tile& t, char*
   // of stage s arrived earlier; they are stored, and stage s + 1's gathered, before the operand loads go
   // out (a wait the compiler places for those registers counts only its own loads, while the hardware
   // counter would also hold the operand loads issued after them).
-  auto stage_out = [&](int s) {
+  auto stage_out = [&](int s, bool rows) {
     if (!SDW) put_scales(s, s_w);
     if (!SDW && s + 1 < nsteps) gather_scales(s + 1, s_w);
-    issue(s);
+    if (rows) {
+#pragma unroll
+      for (int j = 0; j < ND; ++j) issue_rows(s, j);
+    }
+    issue_scales(s);
   };
 
   for (int ks = 0; ks < nsteps; ++ks) {
     stage_barrier();                               // stage ks landed; stage ks-1 fully read
     // The next stage's loads may go out any time after the barrier (its buffer was last read in stage
     // ks - 1) and must land by the next barrier.  The precise feed issues them after its first block's
-    // MFMAs, so that a stage opens with LDS reads, widening and MFMAs rather than with the issue.  (A
-    // software-pipelined precise loop, with the next block's LDS reads issued before the current
-    // block's MFMAs and the stage barrier moved before the last block's MFMAs, measured 4-7% slower.)
-    constexpr bool kLateIssue = FEED == kFeedPrecise;
-    if (!kLateIssue && ks + 1 < nsteps) stage_out(ks + 1);
+    // MFMAs, so that a stage opens with LDS reads, widening and MFMAs rather than with the issue.  The
+    // FP8 feed issues its scale loads at the top and its operand loads inside its first MFMA group,
+    // after that group's LDS reads: a stage then opens with LDS reads rather than with eight loads
+    // (fast-feed GEMMs of the expert shard 3-6% faster for forward and dgrad, wgrad within 1%).
+    // Measured and dropped: spreading the precise feed's loads over its blocks, one chunk row per
+    // group of MFMAs or two per block (4-9% slower; a probe of the bare loop had shown 4% more MFMA
+    // issue per clock), and a software-pipelined precise loop, with the next block's LDS reads issued
+    // before the current block's MFMAs and the stage barrier moved before the last block's MFMAs
+    // (4-7% slower).
+    const bool more = ks + 1 < nsteps;
+    constexpr bool kFastTop = FP4;
+    if constexpr (FEED != kFeedPrecise) {
+      if (more) stage_out(ks + 1, kFastTop);
+    }
     const char* A = lds + (ks & 1) * kStage;
     const char* B = A + kStageA;
     const uint32_t* SA = (const uint32_t*)(lds + 2 * kStage + (ks & 1) * kSStage);
@@ -541,7 +557,7 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const Tile& t, char*
 #pragma unroll
           for (int j = 0; j < NJ; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bhi[j], ahi[i], acc[i][j], 0, 0, 0);
-        if (kLateIssue && bb == 0 && ks + 1 < nsteps) stage_out(ks + 1);
+        if (more && bb == 0) stage_out(ks + 1, true);
       }
     } else if constexpr (FP4) {
       // two k-steps of 128 E2M1 elements: lane group fg feeds block 4 ks2 + fg (16 bytes, the upper
@@ -594,6 +610,10 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const Tile& t, char*
           const v4i hi = *(const v4i*)(A + lds_off(r, 4 * ks2 + 2 + h));
           const v8i af = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
           const int sav = (int)((sword(SA, r) >> (8 * (2 * ks2 + h))) & 0xFFu);
+          if (!kFastTop && more && ks2 == 0 && i == 0) {
+#pragma unroll
+            for (int q = 0; q < ND; ++q) issue_rows(ks + 1, q);
+          }
 #pragma unroll
           for (int j = 0; j < NJ; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf[j], af, acc[i][j], 0, 0, 0, sbv[j], 0, sav);
