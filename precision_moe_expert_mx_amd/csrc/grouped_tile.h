@@ -46,17 +46,25 @@ __device__ bool decode_grouped_tile(const GemmArgs& p, char* lds, GroupTile& t) 
   for (int g = tid; g <= G; g += TNT) s_rs[g] = (int32_t)clamp_off(p.offs[g], M);
   __syncthreads();
   const bool lpt = MODE == kWgrad && G <= kLptMaxG;
-  for (int g = tid; g < G; g += TNT) {
-    int pos = g;
-    if (lpt) {
+  if (lpt) {
+    // the rank of expert g, largest first (ties by index): eight consecutive lanes count the experts
+    // h = part, part + 8, ... that go before g, and their counts are summed across the eight lanes
+    static_assert(TNT % 64 == 0, "whole waves");
+    for (int idx = tid; idx < 8 * G; idx += TNT) {
+      const int g = idx >> 3, part = idx & 7;
       const int mg = max(s_rs[g + 1] - s_rs[g], 0);
-      pos = 0;
-      for (int h = 0; h < G; ++h) {
+      int pos = 0;
+      for (int h = part; h < G; h += 8) {
         const int mh = max(s_rs[h + 1] - s_rs[h], 0);
         pos += (mh > mg) || (mh == mg && h < g);
       }
+      pos += __shfl_xor(pos, 1, 64);
+      pos += __shfl_xor(pos, 2, 64);
+      pos += __shfl_xor(pos, 4, 64);
+      if (part == 0) s_ord[pos] = g;
     }
-    s_ord[pos] = g;
+  } else {
+    for (int g = tid; g < G; g += TNT) s_ord[g] = g;
   }
   __syncthreads();
   const int ntc = cdiv(MODE == kFwd ? p.N : p.K, TBN);
@@ -138,15 +146,18 @@ __device__ bool decode_grouped_tile(const GemmArgs& p, char* lds, GroupTile& t) 
 // Output element (tile row r, tile column c) is out[(out_row0 + r0 + r) * nout + col0 + c0 + c]; rows at
 // or past row_lim and column groups at or past col_lim are not written (col_lim a multiple of 8).  The
 // region must be free (the caller's barrier); a wave's own LDS accesses stay in order, so the passes
-// and the write and read of a pass need no barrier.
-template <int NI, int NJ, int RPP, typename Acc>
-__device__ __forceinline__ void store_tile_rows(const Acc (&acc)[NI][NJ], char* reg, bool bf16, void* out,
-                                                int64_t out_row0, int64_t nout, int64_t col0, int r0, int c0,
-                                                int row_lim, int col_lim) {
+// and the write and read of a pass need no barrier.  A pass reads all its pieces from LDS before it
+// stores any (unrolled), so the LDS latency is paid once per pass rather than once per piece.
+template <int NI, int NJ, int RPP, bool BF16, typename Acc>
+__device__ __forceinline__ void store_tile_rows_as(const Acc (&acc)[NI][NJ], char* reg, void* out, int64_t out_row0,
+                                                   int64_t nout, int64_t col0, int r0, int c0, int row_lim,
+                                                   int col_lim) {
   static_assert(NI % RPP == 0, "passes of RPP fragment rows");
-  constexpr int kPitch32 = 128 * NJ + 16, kPitch16 = 64 * NJ + 16;    // bytes per staged row
+  constexpr int kPitch = BF16 ? 64 * NJ + 16 : 128 * NJ + 16;    // bytes per staged row
+  constexpr int kCpr = BF16 ? 4 * NJ : 8 * NJ;                    // 16-byte pieces per staged row
+  constexpr int kPieces = 32 * RPP * kCpr / 64;                   // pieces per lane and pass
+  static_assert(32 * RPP * kCpr % 64 == 0, "whole pieces per lane");
   const int lane = threadIdx.x & 63, h = lane >> 5;
-  const int pitch = bf16 ? kPitch16 : kPitch32;
 #pragma unroll
   for (int pass = 0; pass < NI / RPP; ++pass) {
 #pragma unroll
@@ -160,25 +171,39 @@ __device__ __forceinline__ void store_tile_rows(const Acc (&acc)[NI][NJ], char* 
           const int c = 32 * j + 8 * q + 4 * h;
           const float v0 = acc[i][j][4 * q], v1 = acc[i][j][4 * q + 1];
           const float v2 = acc[i][j][4 * q + 2], v3 = acc[i][j][4 * q + 3];
-          if (bf16)
-            *(uint2*)(reg + r * kPitch16 + 2 * c) = make_uint2(f32_to_bf16_bits(v0) | (f32_to_bf16_bits(v1) << 16),
-                                                               f32_to_bf16_bits(v2) | (f32_to_bf16_bits(v3) << 16));
+          if constexpr (BF16)
+            *(uint2*)(reg + r * kPitch + 2 * c) = make_uint2(f32_to_bf16_bits(v0) | (f32_to_bf16_bits(v1) << 16),
+                                                             f32_to_bf16_bits(v2) | (f32_to_bf16_bits(v3) << 16));
           else
-            *(float4*)(reg + r * kPitch32 + 4 * c) = make_float4(v0, v1, v2, v3);
+            *(float4*)(reg + r * kPitch + 4 * c) = make_float4(v0, v1, v2, v3);
         }
     }
-    const int cpr = bf16 ? 4 * NJ : 8 * NJ;                        // 16-byte chunks per staged row
-    for (int k = lane; k < 32 * RPP * cpr; k += 64) {
-      const int r = k / cpr, ch = k % cpr;
-      const int tr = r0 + 32 * RPP * pass + r;                     // tile row
-      const int tc = c0 + ch * (bf16 ? 8 : 4);                     // tile column of the chunk's first element
+    uint4 v[kPieces];
+#pragma unroll
+    for (int it = 0; it < kPieces; ++it) {
+      const int k = lane + 64 * it;
+      v[it] = *(const uint4*)(reg + (k / kCpr) * kPitch + 16 * (k % kCpr));
+    }
+#pragma unroll
+    for (int it = 0; it < kPieces; ++it) {
+      const int k = lane + 64 * it;
+      const int tr = r0 + 32 * RPP * pass + k / kCpr;               // tile row
+      const int tc = c0 + (k % kCpr) * (BF16 ? 8 : 4);             // tile column of the piece's first element
       if (tr >= row_lim || tc >= col_lim) continue;
-      const uint4 v = *(const uint4*)(reg + r * pitch + 16 * ch);
       const int64_t idx = (out_row0 + tr) * nout + col0 + tc;
-      if (bf16) *(uint4*)((uint16_t*)out + idx) = v;
-      else *(uint4*)((float*)out + idx) = v;
+      if constexpr (BF16) *(uint4*)((uint16_t*)out + idx) = v[it];
+      else *(uint4*)((float*)out + idx) = v[it];
     }
   }
+}
+
+// The same with the output type chosen at run time (a kernel argument: uniform).
+template <int NI, int NJ, int RPP, typename Acc>
+__device__ __forceinline__ void store_tile_rows(const Acc (&acc)[NI][NJ], char* reg, bool bf16, void* out,
+                                                int64_t out_row0, int64_t nout, int64_t col0, int r0, int c0,
+                                                int row_lim, int col_lim) {
+  if (bf16) store_tile_rows_as<NI, NJ, RPP, true>(acc, reg, out, out_row0, nout, col0, r0, c0, row_lim, col_lim);
+  else store_tile_rows_as<NI, NJ, RPP, false>(acc, reg, out, out_row0, nout, col0, r0, c0, row_lim, col_lim);
 }
 
 // Eight E4M3 bytes -> eight bf16 multiplied by 2^(e-127), e the E8M0 byte whose bits sit in the
