@@ -89,12 +89,12 @@ def build_layer_ops(m, torch, lay, dev_in, fast=False, fused=True, tiled=False):
         y=torch.empty((M, N), dtype=torch.bfloat16, device=d),
         qdy=torch.empty((M, N), dtype=u8, device=d), sdy=torch.empty((M, N // 32), dtype=u8, device=d),
         qwT=torch.empty((ldw // 128, K, 128) if tiled else (K, ldw), dtype=u8, device=d),
-        swT=torch.empty((K, ldw // 32), dtype=u8, device=d),
+        swT=torch.empty((ldw // 128, K, 4) if tiled else (K, ldw // 32), dtype=u8, device=d),
         dx=torch.empty((M, K), dtype=torch.bfloat16, device=d),
         qdyT=torch.empty((ld // 128, N, 128) if tiled else (N, ld), dtype=u8, device=d),
-        sdyT=torch.empty((N, ld // 32), dtype=u8, device=d),
+        sdyT=torch.empty((ld // 128, N, 4) if tiled else (N, ld // 32), dtype=u8, device=d),
         qxT=torch.empty((ld // 128, K, 128) if tiled else (K, ld), dtype=u8, device=d),
-        sxT=torch.empty((K, ld // 32), dtype=u8, device=d),
+        sxT=torch.empty((ld // 128, K, 4) if tiled else (K, ld // 32), dtype=u8, device=d),
         dw=torch.empty((G, N, K), dtype=torch.float32, device=d),
     )
     w2 = w.view(G * N, K)

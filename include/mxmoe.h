@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define MXMOE_ABI_VERSION 3
+#define MXMOE_ABI_VERSION 4
 
 typedef enum {
   MXMOE_OK = 0,
@@ -226,16 +226,21 @@ mxmoe_status mx_grouped_gemm_wgrad_fp8feed(const uint8_t* qdyT, const uint8_t* s
  *     byte (c, j)  at  (j / 128) * C * 128 + c * 128 + (j % 128),      ld % 128 == 0,
  * so one 128-byte slice of the contraction for all C rows is one contiguous block of memory: the
  * quantiser writes whole tiles, and the GEMMs load a 128-byte stage of a row from one place.  The
- * buffer has the same size (C * ld bytes); the scales sT [C, ld/32] keep their row-major layout.
+ * scales sT [C, ld/32] of such a copy are tiled the same way, four bytes (the scales of one 128-byte
+ * slice) per row and tile:
+ *     scale byte (c, b)  at  (b / 4) * C * 4 + c * 4 + (b % 4),
+ * so a quantiser workgroup writes its scale bytes as one contiguous run rather than one dword per
+ * row.  Both buffers keep their sizes (C * ld and C * ld / 32 bytes).
  * Each entry point below takes exactly the arguments, and validates them as, its row-major namesake,
  * with ld (ldh, ldw) % 128 == 0 required in addition (MXMOE_ERR_ALIGN for the quantisers,
  * MXMOE_ERR_SHAPE for the GEMMs); results are the same bytes / values permuted as above:
- *   mx_quantize_colwise_tiled, mx_quantize_dual_tiled   qT in the tiled layout (q, s, sT unchanged);
- *   mx_grouped_gemm_fwd_swiglu_tiled                    qhT tiled ([ldh/128][H][128]); qhT and shT
- *                                                       are required;
- *   mx_grouped_gemm_dgrad_tiled[_fp8feed]               qwT tiled ([ldw/128][K][128]);
- *   mx_grouped_gemm_wgrad_tiled[_fp8feed]               qdyT and qxT tiled ([ld/128][N][128],
- *                                                       [ld/128][K][128]).
+ *   mx_quantize_colwise_tiled, mx_quantize_dual_tiled   qT, sT in the tiled layout (q, s unchanged);
+ *   mx_grouped_gemm_fwd_swiglu_tiled                    qhT, shT tiled ([ldh/128][H][128],
+ *                                                       [ldh/128][H][4]); qhT and shT are required;
+ *   mx_grouped_gemm_dgrad_tiled[_fp8feed]               qwT, swT tiled ([ldw/128][K][128], [.][K][4]);
+ *   mx_grouped_gemm_wgrad_tiled[_fp8feed]               qdyT, sdyT and qxT, sxT tiled
+ *                                                       ([ld/128][N][128], [.][N][4]; [ld/128][K][128],
+ *                                                       [.][K][4]).
  * The GEMM results are bit-identical to the row-major entry points on the same data (the same
  * products are summed in the same order). */
 mxmoe_status mx_quantize_colwise_tiled(const void* x_bf16, int64_t R, int64_t C,

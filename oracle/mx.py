@@ -276,6 +276,22 @@ def mx_colwise_tiled(qT):
     return out
 
 
+def mx_colwise_scales_tiled(sT):
+    """The scales sT [C, ld / 32] of a column-wise copy in the same tiled layout (the library's stated
+    contract, as above): tile t holds the scale bytes of code tile t, i.e. blocks [4 t, 4 t + 4) of
+    every row, so scale byte (c, b) lands at flat position (b // 4) * C * 4 + c * 4 + b % 4.
+    Returns [ld // 128, C, 4]; ld % 128 == 0."""
+    sT = np.asarray(sT)
+    C, nb = sT.shape
+    per = TILE // 32                       # blocks (scale bytes) per 128-byte code tile
+    if nb % per:
+        raise ValueError("the tiled layout needs ld % 128 == 0")
+    out = np.empty((nb // per, C, per), dtype=sT.dtype)
+    for t in range(nb // per):
+        out[t] = sT[:, per * t:per * (t + 1)]
+    return out
+
+
 def swiglu(gate, up):
     """Gated activation of an expert's gate+up output: silu(gate) * up, silu(z) = z / (1 + e^-z).
 

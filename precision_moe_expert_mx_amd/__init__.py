@@ -219,6 +219,12 @@ def _colwise_out(C, ld, tiled, like):
     return _empty((ld // 128, C, 128) if tiled else (C, ld), torch.uint8, like)
 
 
+def _colwise_scales_out(C, ld, tiled, like):
+    """Its scale buffer: [C, ld / 32] row-major, or [ld / 128, C, 4] in the tiled layout."""
+    torch = _torch()
+    return _empty((ld // 128, C, 4) if tiled else (C, ld // 32), torch.uint8, like)
+
+
 def _colwise(name, tiled, x, offs, G, ld, qT, sT, stream):
     torch = _torch()
     x = _bf16_bits(x)
@@ -228,7 +234,7 @@ def _colwise(name, tiled, x, offs, G, ld, qT, sT, stream):
     if ld is None:
         ld = mx_colwise_ld(R, G if offs is not None else None)
     qT = _colwise_out(C, ld, tiled, x) if qT is None else qT
-    sT = _empty((C, ld // 32), torch.uint8, x) if sT is None else sT
+    sT = _colwise_scales_out(C, ld, tiled, x) if sT is None else sT
     _check(name, getattr(lib(), name)(_ptr(x), R, C, _ptr(offs), G, _ptr(qT), _ptr(sT), ld, _stream_handle(stream)))
     return qT, sT
 
@@ -239,7 +245,7 @@ def mx_quantize_colwise(x, offs=None, G: int = 1, ld: Optional[int] = None, qT=N
 
 
 def mx_quantize_colwise_tiled(x, offs=None, G: int = 1, ld: Optional[int] = None, qT=None, sT=None, stream=None):
-    """As mx_quantize_colwise with qT in the 128-byte tiled layout: qT uint8 [ld/128, C, 128]."""
+    """As mx_quantize_colwise in the 128-byte tiled layout: qT uint8 [ld/128, C, 128], sT [ld/128, C, 4]."""
     return _colwise("mx_quantize_colwise_tiled", True, x, offs, G, ld, qT, sT, stream)
 
 
@@ -255,7 +261,7 @@ def _dual(name, tiled, x, offs, G, ld, row_idx, q, s, qT, sT, stream):
     q = _empty((R, C), torch.uint8, x) if q is None else q
     s = _empty((R, C // 32), torch.uint8, x) if s is None else s
     qT = _colwise_out(C, ld, tiled, x) if qT is None else qT
-    sT = _empty((C, ld // 32), torch.uint8, x) if sT is None else sT
+    sT = _colwise_scales_out(C, ld, tiled, x) if sT is None else sT
     _check(name, getattr(lib(), name)(_ptr(x), R, C, _ptr(row_idx), R_src, _ptr(offs), G, _ptr(q), _ptr(s), _ptr(qT),
                                       _ptr(sT), ld, _stream_handle(stream)))
     return q, s, qT, sT
@@ -272,7 +278,7 @@ def mx_quantize_dual(x, offs=None, G: int = 1, ld: Optional[int] = None, row_idx
 
 def mx_quantize_dual_tiled(x, offs=None, G: int = 1, ld: Optional[int] = None, row_idx=None, q=None, s=None,
                            qT=None, sT=None, stream=None):
-    """As mx_quantize_dual with qT in the 128-byte tiled layout: qT uint8 [ld/128, C, 128]."""
+    """As mx_quantize_dual with qT, sT in the 128-byte tiled layout: [ld/128, C, 128], [ld/128, C, 4]."""
     return _dual("mx_quantize_dual_tiled", True, x, offs, G, ld, row_idx, q, s, qT, sT, stream)
 
 
@@ -304,7 +310,7 @@ def _swiglu(name, tiled, qx, sx, qw, sw, offs, N, y, qh, sh, h, with_h, colwise,
         elif ldh is None:
             ldh = mx_colwise_ld(M, G)
         qhT = _colwise_out(H, ldh, tiled, qx) if qhT is None else qhT
-        shT = _empty((H, ldh // 32), torch.uint8, qx) if shT is None else shT
+        shT = _colwise_scales_out(H, ldh, tiled, qx) if shT is None else shT
     _check(name, getattr(lib(), name)(
         _ptr(qx), _ptr(sx), _ptr(qw), _ptr(sw), _ptr(offs), G, M, N, K, _ptr(y), _ptr(qh), _ptr(sh), _ptr(h),
         _ptr(qhT), _ptr(shT), int(ldh or 0), _stream_handle(stream)))
@@ -326,8 +332,8 @@ def mx_grouped_gemm_fwd_swiglu(qx, sx, qw, sw, offs, N: int, y=None, qh=None, sh
 def mx_grouped_gemm_fwd_swiglu_tiled(qx, sx, qw, sw, offs, N: int, y=None, qh=None, sh=None, h=None,
                                      with_h: bool = False, ldh: Optional[int] = None, qhT=None, shT=None,
                                      stream=None):
-    """As mx_grouped_gemm_fwd_swiglu, always with H column-wise, qhT in the 128-byte tiled layout
-    ([ldh/128, H, 128]).  Returns (y, qh, sh, qhT, shT[, h])."""
+    """As mx_grouped_gemm_fwd_swiglu, always with H column-wise, qhT and shT in the 128-byte tiled
+    layout ([ldh/128, H, 128], [ldh/128, H, 4]).  Returns (y, qh, sh, qhT, shT[, h])."""
     return _swiglu("mx_grouped_gemm_fwd_swiglu_tiled", True, qx, sx, qw, sw, offs, N, y, qh, sh, h, with_h, True,
                    ldh, qhT, shT, stream)
 
@@ -339,7 +345,8 @@ def mx_grouped_gemm_dgrad(qdy, sdy, qwT, swT, offs, K: int, out_dtype: str = "f3
 
 def mx_grouped_gemm_dgrad_tiled(qdy, sdy, qwT, swT, offs, K: int, out_dtype: str = "f32", dx=None, stream=None,
                                 fast: bool = False):
-    """As mx_grouped_gemm_dgrad with qwT in the 128-byte tiled layout ([ldw/128, K, 128])."""
+    """As mx_grouped_gemm_dgrad with qwT, swT in the 128-byte tiled layout ([ldw/128, K, 128],
+    [ldw/128, K, 4])."""
     return _dgrad("mx_grouped_gemm_dgrad_tiled", qwT.shape[0] * 128, qdy, sdy, qwT, swT, offs, K, out_dtype, dx,
                   stream, fast)
 
@@ -363,8 +370,8 @@ def mx_grouped_gemm_wgrad(qdyT, sdyT, qxT, sxT, offs, M: int, out_dtype: str = "
 
 def mx_grouped_gemm_wgrad_tiled(qdyT, sdyT, qxT, sxT, offs, M: int, out_dtype: str = "f32", dw=None, stream=None,
                                 fast: bool = False):
-    """As mx_grouped_gemm_wgrad with qdyT / qxT in the 128-byte tiled layout ([ld/128, N, 128],
-    [ld/128, K, 128])."""
+    """As mx_grouped_gemm_wgrad with qdyT, sdyT / qxT, sxT in the 128-byte tiled layout
+    ([ld/128, N, 128], [ld/128, N, 4] / [ld/128, K, 128], [ld/128, K, 4])."""
     return _wgrad("mx_grouped_gemm_wgrad_tiled", qdyT.shape[1], qdyT.shape[0] * 128, qxT.shape[1], qdyT, sdyT, qxT,
                   sxT, offs, M, out_dtype, dw, stream, fast)
 

@@ -246,12 +246,17 @@ static mxmoe_status mx_gemm_common(int mode, const char* fn, const uint8_t* a, c
     p.lda = ldb_cols / epb; p.ldsa = ldb_cols / 32; p.ldb = ldb_cols / epb; p.ldsb = ldb_cols / 32;
   }
   p.a_kstride = p.b_kstride = 128;
+  p.sa_gstride = p.sb_gstride = 4;
+  if (mode == kWgrad) p.ld_cols = ldb_cols;
   if (tiled) {
-    // column-wise operands in the 128-byte tiled layout: rows 128 bytes apart, chunks rows * 128 apart
+    // column-wise operands in the 128-byte tiled layout: rows 128 bytes apart, chunks rows * 128 apart;
+    // their scales [ld / 128][rows][4]: rows 4 bytes apart, 4-byte groups rows * 4 apart
     if (mode == kWgrad) {
       p.lda = 128; p.a_kstride = 128 * N;
+      p.ldsa = 4; p.sa_gstride = 4 * N;
     }
     p.ldb = 128; p.b_kstride = 128 * K;
+    p.ldsb = 4; p.sb_gstride = 4 * K;
   }
   TRY(check_strides(fn, p, 256));
   if (mode != kWgrad && M == 0) return ok();
@@ -566,6 +571,7 @@ static mxmoe_status bw_gemm_common(int mode, const char* fn, int feed, const uin
   } else {
     // wgrad: both operands column-wise with leading dimension ld, one fp32 scale per 128 columns
     p.lda = ld; p.ldsa = ld / 128; p.ldb = ld; p.ldsb = ld / 128;
+    p.ld_cols = ld;
   }
   if (mode != kWgrad && M == 0) return ok();
   TRY(check_device());
@@ -666,6 +672,7 @@ static mxmoe_status fp8bw_grouped_gemm_wgrad_pow2_impl(const char* fn, int feed,
   p.a_kstride = p.b_kstride = 128;
   // fp32 scale rows of ld / 128 floats = ld / 32 bytes, the MX kernel's byte stride
   p.lda = ld; p.ldsa = ld / 32; p.ldb = ld; p.ldsb = ld / 32;
+  p.ld_cols = ld;
   TRY(check_strides(fn, p, 256));
   TRY(check_device());
   return launched(launch_mx_gemm(kWgrad, p, (hipStream_t)stream), fn);

@@ -218,11 +218,17 @@ struct GemmArgs {
   const void* sb;     // B scales
   const int32_t* offs;
   void* out;
-  int64_t lda, ldsa;  // A row stride in bytes / scale row stride in elements
+  int64_t lda, ldsa;  // A row stride in bytes / scale row stride in scale elements
   int64_t ldb, ldsb;
   // MX: bytes between consecutive 128-byte contraction chunks of an operand row: 128 in the row-major
   // layouts, rows * 128 in the 128-byte tiled column-wise layout (whose row stride is then 128)
   int64_t a_kstride, b_kstride;
+  // MX: bytes between consecutive 4-byte groups of a row's scale bytes (the scales of one 128-element
+  // chunk): 4 in the row-major layouts, rows * 4 in the tiled column-wise layout (whose scale row
+  // stride ldsa / ldsb is then 4)
+  int64_t sa_gstride, sb_gstride;
+  // wgrad: leading dimension of the column-wise copies in elements (the expert clip)
+  int64_t ld_cols;
   int64_t M, N, K;    // problem sizes as in the ABI
   int32_t G;
   int32_t out_bf16;

@@ -199,6 +199,10 @@ __device__ __forceinline__ void act_epilogue(const GemmArgs& p, const Tile& t, c
   auto qt_at = [&](int64_t u, int64_t j) -> int64_t {
     return p.act_tiled ? (j >> 7) * (H * 128) + u * 128 + (j & 127) : u * ldq + j;
   };
+  // scale byte of qT row u, block b: row-major [H, ldq / 32], or tiled [ldq / 128][H][4]
+  auto st_at = [&](int64_t u, int64_t b) -> int64_t {
+    return p.act_tiled ? (b >> 2) * (H * 4) + u * 4 + (b & 3) : u * (ldq / 32) + b;
+  };
   const int64_t tcol = t.col0 + (int64_t)t.mt * BM;               // the tile's first column of qT
   const int nb_tile = (row_lim + 31) / 32;
   const int k16 = lane & 15;
@@ -221,7 +225,7 @@ __device__ __forceinline__ void act_epilogue(const GemmArgs& p, const Tile& t, c
       // (with offsets that are not monotone an expert's blocks could lie past the leading dimension)
       if (b < nb_tile && tcol + 32 * b + 32 <= ldq) {
         *(uint32_t*)(p.act_qT + qt_at(u, tcol + row0)) = code;
-        if ((k16 & 7) == 0) p.act_sT[u * (ldq / 32) + tcol / 32 + b] = (uint8_t)(e + 127);
+        if ((k16 & 7) == 0) p.act_sT[st_at(u, tcol / 32 + b)] = (uint8_t)(e + 127);
       }
     }
   }
@@ -237,7 +241,7 @@ __device__ __forceinline__ void act_epilogue(const GemmArgs& p, const Tile& t, c
     const int64_t stail = tail / 32;
     for (int64_t k = tid; k < (BN / 2) * stail; k += NT) {
       const int64_t u = (int64_t)t.nt * (BN / 2) + k / stail;
-      p.act_sT[u * (ldq / 32) + t.col_end / 32 + k % stail] = 0;
+      p.act_sT[st_at(u, t.col_end / 32 + k % stail)] = 0;
     }
   }
 }
@@ -324,6 +328,9 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const Tile& t, char*
   // (ALIGNED_START above).  Otherwise (wgrad: experts start at arbitrary 32-blocks) thread t gathers rows
   // q = t + NT j (q < 256: A row q, else B row q - 256) into registers one stage ahead and stores
   // the dwords to LDS.
+  // A row's scale bytes sit in groups of four (one 128-element chunk), sa_gstride / sb_gstride bytes
+  // apart: 4 in the row-major layouts (a plain row), rows * 4 in the tiled column-wise layout, where a
+  // chunk's groups of all rows form one block ([ld / 128][rows][4]; only with aligned dwords).
   const uint8_t* sa = (const uint8_t*)p.sa;
   const uint8_t* sb = (const uint8_t*)p.sb;
   const int64_t sa_col0 = a_el0 / 32, sb_col0 = b_el0 / 32;
@@ -335,7 +342,8 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const Tile& t, char*
     if (SDW) q = 64 * (kScaleLoads * w + j) + lane;
     else q = tid + NT * j;
     const int r = q & 255;
-    s_src[j] = q < 256 ? sa + a_row(r) * p.ldsa + sa_col0 : sb + b_row(r) * p.ldsb + sb_col0;
+    s_src[j] = q < 256 ? sa + a_row(r) * p.ldsa + (sa_col0 >> 2) * p.sa_gstride + (sa_col0 & 3)
+                       : sb + b_row(r) * p.ldsb + (sb_col0 >> 2) * p.sb_gstride + (sb_col0 & 3);
     if (BWP2 && MODE != kWgrad && q >= 256) {
       // fp32 block scales [G N / 128, K / 128]: row stride ldsb = K / 32 bytes.  Forward: block row
       // (g N + n) / 128, one fp32 per stage.  Dgrad (B rows k, the stages run over n): block column
@@ -344,12 +352,14 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const Tile& t, char*
       else s_src[j] = sb + (((int64_t)t.g * p.N) >> 7) * p.ldsb + (b_row(r) >> 7) * 4;
     }
   }
-  // bytes between the scales of consecutive stages (BWP2 dgrad B: one block row of scales)
-  int64_t s_step[NS];
+  // bytes between a row's scale groups (direct-to-LDS paths: 64 rows of one operand per load) and
+  // between the scales of consecutive stages (BWP2 dgrad B: one block row of scales)
+  int64_t s_gs[NS], s_step[NS];
 #pragma unroll
   for (int j = 0; j < NS; ++j) {
     const bool b_rows = (SDW ? 64 * (kScaleLoads * w + j) : tid + NT * j) >= 256;
-    s_step[j] = BWP2 && MODE == kDgrad && b_rows ? p.ldsb : SPS;
+    s_gs[j] = b_rows ? p.sb_gstride : p.sa_gstride;
+    s_step[j] = BWP2 && MODE == kDgrad && b_rows ? p.ldsb : (SPS / 4) * s_gs[j];
   }
   // Scale bytes [SPS ks, SPS ks + nv) of a row (nv < SPS only in the last wgrad stage; the rest read
   // as 0) land as SPS / 4 dwords, dword d of every row in plane d of the stage's scale area.  Register
@@ -422,7 +432,8 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const Tile& t, char*
       for (int d = 0; d < SPS / 4; ++d) {
         if (d == 0 || nv > 4 * d) {
 #pragma unroll
-          for (int j = 0; j < NS; ++j) dma4(s_src[j] + SPS * ks + 4 * d, ss + 2048 * d + 256 * (kScaleLoads * w + j));
+          for (int j = 0; j < NS; ++j)
+            dma4(s_src[j] + ((SPS / 4) * ks + d) * s_gs[j], ss + 2048 * d + 256 * (kScaleLoads * w + j));
         }
       }
     } else if (SDW) {
@@ -430,7 +441,7 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const Tile& t, char*
       for (int j = 0; j < NS; ++j)
 #pragma unroll
         for (int d = 0; d < P; ++d)
-          dma4(s_src[j] + s_step[j] * ks + 4 * d, ss + 2048 * d + 256 * (kScaleLoads * w + j));
+          dma4(s_src[j] + s_step[j] * ks + d * s_gs[j], ss + 2048 * d + 256 * (kScaleLoads * w + j));
     }
   };
 
@@ -720,6 +731,11 @@ hipError_t launch_mx_gemm(int mode, const GemmArgs& args, hipStream_t st) {
   GemmArgs p = args;
   if (p.a_kstride == 0) p.a_kstride = BK;        // row-major operands
   if (p.b_kstride == 0) p.b_kstride = BK;
+  if (p.sa_gstride == 0) p.sa_gstride = 4;       // row-major scale rows
+  if (p.sb_gstride == 0) p.sb_gstride = 4;
+  // tiled scale layouts are read only by the direct-to-LDS dword paths (E4M3, scale rows of dwords)
+  const bool tiled_scales = p.sa_gstride != 4 || p.sb_gstride != 4;
+  if (tiled_scales && (p.fp4 || p.bw_pow2 || p.ldsa % 4 || p.ldsb % 4)) return hipErrorInvalidValue;
   const int64_t tiles = tile_count_bound(mode, p);
   if (tiles == 0) return hipSuccess;
   const int64_t per = (int64_t)kXcd * kChunk;
@@ -728,6 +744,7 @@ hipError_t launch_mx_gemm(int mode, const GemmArgs& args, hipStream_t st) {
   // the scale bytes of a row and stage are aligned dwords when every scale row and column offset is
   // a multiple of 4 bytes (wgrad expert columns start at arbitrary 32-blocks)
   p.scale_dword = mode != kWgrad && p.ldsa % 4 == 0 && p.ldsb % 4 == 0 && (p.N / 32) % 4 == 0;
+  if (tiled_scales && mode != kWgrad && !p.scale_dword) return hipErrorInvalidValue;
   const dim3 g((unsigned)grid);
   if (p.bw_pow2) {
     // blockwise operands with power-of-two scales: scale rows of aligned dwords

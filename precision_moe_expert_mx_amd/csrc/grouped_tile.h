@@ -126,11 +126,8 @@ __device__ bool decode_grouped_tile(const GemmArgs& p, char* lds, GroupTile& t) 
   t.col_end = CB ? CBLK * (int64_t)s_cb[G] : 0;
   t.nblk = cdiv(m_g, CBLK);
   if (MODE == kWgrad) {
-    // offsets that are not monotone could place an expert past the leading dimension: clip.  The
-    // leading dimension in elements comes from the scale rows (one scale per CBLK elements; the MX
-    // kernel's power-of-two blockwise mode reads its fp32 scale rows in bytes, 4 per 128 elements):
-    // the operand row stride is not it in the tiled layout (128) nor for E2M1 (two elements per byte).
-    const int64_t ld_el = p.bw_pow2 ? 32 * p.ldsa : (int64_t)CBLK * p.ldsa;
+    // offsets that are not monotone could place an expert past the leading dimension: clip
+    const int64_t ld_el = p.ld_cols;
     const int64_t room = ld_el > t.col0 ? (ld_el - t.col0) / CBLK : 0;
     if (t.nblk > room) t.nblk = (int)room;
   }

@@ -308,11 +308,13 @@ __device__ __forceinline__ void col_group(const ColArgs& a, int r0, int n, int b
       store16_col<ROW>((uint4*)(a.qT + off + 16 * piece), val);
     }
   }
-  if (nb == kColBlk && (nbc & 3) == 0) {
-    // the 4 scale bytes of a column are one aligned dword of its sT row
+  if (TILED || (nb == kColBlk && (nbc & 3) == 0)) {
+    // the 4 scale bytes of a column are one aligned dword of its sT row; tiled layout
+    // ([ld / 128][C][4], ld % 128 == 0, so nb == 4): the workgroup's dwords are one contiguous run
     for (int rr = a.t; rr < kColCols; rr += kColThreads) {
       const int64_t c = a.cbase + rr;
-      if (FULLWIN || c < a.C) *(uint32_t*)(a.sT + c * nbc + bc0) = *(const uint32_t*)(outs + rr * kColBlk);
+      const int64_t off = TILED ? (int64_t)(bc0 / kColBlk) * a.C * kColBlk + c * kColBlk : c * nbc + bc0;
+      if (FULLWIN || c < a.C) *(uint32_t*)(a.sT + off) = *(const uint32_t*)(outs + rr * kColBlk);
     }
   } else {
     for (int idx = a.t; idx < kColCols * kColBlk; idx += kColThreads) {

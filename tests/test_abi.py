@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
     m, L = _lib()
     for name in _declared():
         assert hasattr(L, name), name
-    assert m.abi_version() == 3
+    assert m.abi_version() == 4
 
 
 def test_host_helpers():

@@ -1,7 +1,7 @@
 """The 128-byte tiled column-wise layout on the GPU.
 
 Quantiser outputs are compared byte for byte with the oracle's column-wise quantisation permuted by
-oracle.mx_colwise_tiled (the layout's stated contract); the GEMMs that read tiled operands must give
+oracle.mx_colwise_tiled and oracle.mx_colwise_scales_tiled (the layout's stated contract); the GEMMs that read tiled operands must give
 results bit-identical to the row-major entry points on the same data and lie within the oracle's
 bound; the gated forward's tiled H is compared with the oracle's quantisation of the kernel's H.
 Output buffers are pre-filled with 0xAB so that every byte the contract defines must be written."""
@@ -27,19 +27,24 @@ def _filled(shape, dtype=torch.uint8):
 
 
 def _untile(t):
-    """[ld/128, C, 128] tiled bytes -> the row-major [C, ld] copy."""
+    """[ld/128, C, 128] tiled bytes (or [ld/128, C, 4] tiled scales) -> the row-major [C, ld] copy."""
     a = host(t)
-    T, C, _ = a.shape
-    return np.ascontiguousarray(a.transpose(1, 0, 2).reshape(C, T * 128))
+    T, C, W = a.shape
+    return np.ascontiguousarray(a.transpose(1, 0, 2).reshape(C, T * W))
+
+
+def _tiles(qo, so):
+    """The oracle's row-major column-wise copy in the tiled layout (codes and scales)."""
+    return oracle.mx_colwise_tiled(qo), oracle.mx_colwise_scales_tiled(so)
 
 
 def _colwise_tiled_equal(m, x, offs, ld):
     R, C = x.shape
-    qT, sT = _filled((ld // 128, C, 128)), _filled((C, ld // 32))
+    qT, sT = _filled((ld // 128, C, 128)), _filled((ld // 128, C, 4))
     m.mx_quantize_colwise_tiled(dev(x), None if offs is None else dev(np.asarray(offs, np.int32)), ld=ld, qT=qT,
                                 sT=sT)
     qo, so = oracle.mx_quantize_colwise(x, offs, ld)
-    same_bytes((host(qT), host(sT)), (oracle.mx_colwise_tiled(qo), so), f"tiled column-wise {R}x{C} ld {ld}")
+    same_bytes((host(qT), host(sT)), _tiles(qo, so), f"tiled column-wise {R}x{C} ld {ld}")
 
 
 def test_colwise_tiled_ragged_groups():
@@ -65,11 +70,11 @@ def _dual_tiled_equal(m, x, offs, ld, row_idx=None):
     R = x.shape[0] if row_idx is None else len(row_idx)
     C = x.shape[1]
     q, s = _filled((R, C)), _filled((R, C // 32))
-    qT, sT = _filled((ld // 128, C, 128)), _filled((C, ld // 32))
+    qT, sT = _filled((ld // 128, C, 128)), _filled((ld // 128, C, 4))
     m.mx_quantize_dual_tiled(dev(x), None if offs is None else dev(offs), ld=ld,
                              row_idx=None if row_idx is None else dev(row_idx), q=q, s=s, qT=qT, sT=sT)
     ro = oracle.mx_quantize_dual(x, offs, ld, row_idx)
-    same_bytes((host(q), host(s), host(qT), host(sT)), (ro[0], ro[1], oracle.mx_colwise_tiled(ro[2]), ro[3]),
+    same_bytes((host(q), host(s), host(qT), host(sT)), (ro[0], ro[1]) + _tiles(ro[2], ro[3]),
                f"tiled dual {R}x{C} ld {ld}")
 
 
@@ -111,7 +116,7 @@ def test_dual_tiled_full_size_sampled():
     q, s, qT, sT = m.mx_quantize_dual_tiled(dev(lay.x), dev(lay.offs), ld=ld)
     same_bytes((host(q[rows]), host(s[rows])), oracle.mx_quantize_rowwise(lay.x[rows]), "dual tiled, row-wise")
     qo, so = oracle.mx_quantize_colwise(np.ascontiguousarray(lay.x[:, cols]), lay.offs, ld)
-    same_bytes((_untile(qT[:, cols, :]), host(sT[cols])), (qo, so), "dual tiled, column-wise")
+    same_bytes((_untile(qT[:, cols, :]), _untile(sT[:, cols, :])), (qo, so), "dual tiled, column-wise")
     del q, s, qT, sT
     torch.cuda.empty_cache()
 
@@ -139,12 +144,12 @@ def test_gemms_on_tiled_operands(fast):
         ldw = _ld128(G * N) + 128
         qwT, swT = m.mx_quantize_colwise(dev(w), None, ld=ldw)
         qwTt, swTt = m.mx_quantize_colwise_tiled(dev(w), None, ld=ldw)
-        same_bytes((host(qwTt), host(swTt)), (oracle.mx_colwise_tiled(host(qwT)), host(swT)), "W tiled vs row-major")
+        same_bytes((host(qwTt), host(swTt)), _tiles(host(qwT), host(swT)), "W tiled vs row-major")
         dx = m.mx_grouped_gemm_dgrad(qdy, sdy, qwT, swT, offs_d, K, "f32", fast=fast)
         dxt = m.mx_grouped_gemm_dgrad_tiled(qdy, sdy, qwTt, swTt, offs_d, K, "f32", fast=fast)
         assert torch.equal(dx, dxt), "dgrad: tiled operand gives other bits than the row-major one"
         qo, so = oracle.mx_quantize_colwise(w, None, ldw)
-        same_bytes((host(qwTt), host(swTt)), (oracle.mx_colwise_tiled(qo), so), "W tiled")
+        same_bytes((host(qwTt), host(swTt)), _tiles(qo, so), "W tiled")
         ref, bnd = oracle.mx_gemm_dgrad(*oracle.mx_quantize_rowwise(dy), qo, so, offs, N, K)
         ok, worst, _ = oracle.check_gemm(host(dxt).astype(np.float64), ref, bnd, "f32", rel=rel)
         assert ok, f"dgrad tiled: worst err/tol {worst:.3g}"
@@ -161,8 +166,8 @@ def test_gemms_on_tiled_operands(fast):
             assert torch.equal(dw, dwt), f"wgrad ({dt}): tiled operands give other bits than the row-major ones"
         qa, sa = oracle.mx_quantize_colwise(dy, offs, ld)
         qb, sb = oracle.mx_quantize_colwise(x, offs, ld)
-        same_bytes((host(qdyTt), host(sdyTt), host(qxTt), host(sxTt)),
-                   (oracle.mx_colwise_tiled(qa), sa, oracle.mx_colwise_tiled(qb), sb), "dY, X tiled")
+        same_bytes((host(qdyTt), host(sdyTt), host(qxTt), host(sxTt)), _tiles(qa, sa) + _tiles(qb, sb),
+                   "dY, X tiled")
         ref, bnd = oracle.mx_gemm_wgrad(qa, sa, qb, sb, offs, N, K)
         dw = m.mx_grouped_gemm_wgrad_tiled(qdyTt, sdyTt, qxTt, sxTt, offs_d, M, "f32", fast=fast)
         ok, worst, _ = oracle.check_gemm(host(dw).astype(np.float64), ref, bnd, "f32", rel=rel)
@@ -215,10 +220,10 @@ def test_swiglu_tiled_column_wise_h():
         for extra in (0, 128):
             ldh = m.mx_colwise_ld(M, G) + extra
             y0, qh0, sh0, qhT0, shT0 = m.mx_grouped_gemm_fwd_swiglu(qx, sx, qw, sw, offs_d, N, colwise=True, ldh=ldh)
-            qhT, shT = _filled((ldh // 128, H, 128)), _filled((H, ldh // 32))
+            qhT, shT = _filled((ldh // 128, H, 128)), _filled((ldh // 128, H, 4))
             y, qh, sh, qhT, shT, h = m.mx_grouped_gemm_fwd_swiglu_tiled(qx, sx, qw, sw, offs_d, N, with_h=True,
                                                                         qhT=qhT, shT=shT)
             assert torch.equal(y, y0) and torch.equal(qh, qh0) and torch.equal(sh, sh0)
             qo, so = oracle.mx_quantize_colwise_values(host(h).astype(np.float64), offs, ldh)
-            same_bytes((host(qhT), host(shT)), (oracle.mx_colwise_tiled(qo), so), f"H tiled {sizes} ldh {ldh}")
-            same_bytes((host(qhT),), (oracle.mx_colwise_tiled(host(qhT0)),), "H tiled vs row-major")
+            same_bytes((host(qhT), host(shT)), _tiles(qo, so), f"H tiled {sizes} ldh {ldh}")
+            same_bytes((host(qhT), host(shT)), _tiles(host(qhT0), host(shT0)), "H tiled vs row-major")

@@ -340,3 +340,36 @@ def test_colwise_tiled_is_the_stated_permutation():
     assert np.array_equal(mx_colwise_tiled(qT).reshape(-1), want)
     with pytest.raises(ValueError):
         mx_colwise_tiled(np.zeros((2, 96), dtype=np.uint8))
+
+
+def test_colwise_scales_tiled_is_the_stated_permutation():
+    """The tiled layout's scales (library contract): scale byte (c, b) of sT [C, ld / 32] at flat position
+    (b // 4) * C * 4 + c * 4 + b % 4, the four scale bytes of code tile b // 4 of row c.  Checked element
+    by element by that formula, as a bijection onto the buffer, against the code tiling (the scale of
+    code byte (c, j) sits in the same tile t = j // 128, at row c, slot (j % 128) // 32), and on a case
+    small enough to write out."""
+    from oracle import mx_colwise_tiled, mx_colwise_scales_tiled
+    rng = np.random.default_rng(72)
+    for C, ld in ((3, 128), (5, 384), (32, 256)):
+        sT = rng.integers(0, 256, size=(C, ld // 32), dtype=np.uint8)
+        t = mx_colwise_scales_tiled(sT)
+        assert t.shape == (ld // 128, C, 4) and t.dtype == np.uint8
+        flat = t.reshape(-1)
+        pos = np.empty((C, ld // 32), dtype=np.int64)
+        for c in range(C):
+            for b in range(ld // 32):
+                pos[c, b] = (b // 4) * C * 4 + c * 4 + b % 4
+                assert flat[pos[c, b]] == sT[c, b]
+        assert np.array_equal(np.sort(pos.reshape(-1)), np.arange(C * ld // 32))
+        # code byte (c, j) and its block's scale land in the same tile and row
+        qT = rng.integers(0, 256, size=(C, ld), dtype=np.uint8)
+        qt = mx_colwise_tiled(qT)
+        for c in range(C):
+            for j in range(0, ld, 32):
+                assert qt[j // 128, c, j % 128] == qT[c, j] and t[j // 128, c, (j % 128) // 32] == sT[c, j // 32]
+    # 2 rows, 8 blocks: tile 0 = row 0 blocks 0..3 then row 1 blocks 0..3; tile 1 = blocks 4..7
+    sT = np.arange(16, dtype=np.int64).reshape(2, 8)
+    want = np.array([0, 1, 2, 3, 8, 9, 10, 11, 4, 5, 6, 7, 12, 13, 14, 15])
+    assert np.array_equal(mx_colwise_scales_tiled(sT).reshape(-1), want)
+    with pytest.raises(ValueError):
+        mx_colwise_scales_tiled(np.zeros((2, 3), dtype=np.uint8))
