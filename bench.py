@@ -84,10 +84,13 @@ def build_layer_ops(m, torch, lay, dev_in, fast=False, fused=True, tiled=False):
     ld = m.mx_colwise_ld(M, G)
     ldw = m.mx_colwise_ld(G * N)
     b = dict(
-        qx=torch.empty((M, K), dtype=u8, device=d), sx=torch.empty((M, K // 32), dtype=u8, device=d),
-        qw=torch.empty((G * N, K), dtype=u8, device=d), sw=torch.empty((G * N, K // 32), dtype=u8, device=d),
+        qx=torch.empty((M, K), dtype=u8, device=d),
+        sx=torch.empty((K // 128, M, 4) if tiled else (M, K // 32), dtype=u8, device=d),
+        qw=torch.empty((G * N, K), dtype=u8, device=d),
+        sw=torch.empty((K // 128, G * N, 4) if tiled else (G * N, K // 32), dtype=u8, device=d),
         y=torch.empty((M, N), dtype=torch.bfloat16, device=d),
-        qdy=torch.empty((M, N), dtype=u8, device=d), sdy=torch.empty((M, N // 32), dtype=u8, device=d),
+        qdy=torch.empty((M, N), dtype=u8, device=d),
+        sdy=torch.empty((N // 128, M, 4) if tiled else (M, N // 32), dtype=u8, device=d),
         qwT=torch.empty((ldw // 128, K, 128) if tiled else (K, ldw), dtype=u8, device=d),
         swT=torch.empty((ldw // 128, K, 4) if tiled else (K, ldw // 32), dtype=u8, device=d),
         dx=torch.empty((M, K), dtype=torch.bfloat16, device=d),
@@ -103,8 +106,9 @@ def build_layer_ops(m, torch, lay, dev_in, fast=False, fused=True, tiled=False):
     mxb = 1.0 + 1.0 / 32.0          # E4M3 byte plus its share of an E8M0 scale
     gemm_bytes = {"fwd": (M * K + G * N * K) * mxb + M * N * 2, "dgrad": (M * N + G * N * K) * mxb + M * K * 2,
                   "wgrad": (M * N + M * K) * mxb + G * N * K * 4}
-    fwd = Op(f"{n}.fwd", "gemm", lambda: m.mx_grouped_gemm_fwd(b["qx"], b["sx"], b["qw"], b["sw"], offs, N, "bf16",
-                                                              y=b["y"], fast=fast), f, "grouped_gemm fwd")
+    fw = m.mx_grouped_gemm_fwd_tiled if tiled else m.mx_grouped_gemm_fwd
+    fwd = Op(f"{n}.fwd", "gemm", lambda: fw(b["qx"], b["sx"], b["qw"], b["sw"], offs, N, "bf16", y=b["y"], fast=fast),
+             f, "grouped_gemm fwd")
     dg = m.mx_grouped_gemm_dgrad_tiled if tiled else m.mx_grouped_gemm_dgrad
     wg = m.mx_grouped_gemm_wgrad_tiled if tiled else m.mx_grouped_gemm_wgrad
     dual = m.mx_quantize_dual_tiled if tiled else m.mx_quantize_dual
@@ -440,7 +444,13 @@ def gpu_sample(lay, bufs, rows_per_expert=2048):
     rows = int(min(rows_per_expert, lay.sizes[g]))
     sl = slice(r0, r0 + rows)
     y = bufs["y"][sl].view(__import__("torch").int16).cpu().numpy().view(np.uint16)
-    return {"qx": bufs["qx"][sl].cpu().numpy(), "sx": bufs["sx"][sl].cpu().numpy(), "y_bf16": y}
+    sx = bufs["sx"]
+    if sx.dim() == 3:
+        # tiled scales [K / 128, M, 4] -> the rows' row-major [rows, K / 32]
+        sx = sx[:, sl, :].permute(1, 0, 2).reshape(rows, -1)
+    else:
+        sx = sx[sl]
+    return {"qx": bufs["qx"][sl].cpu().numpy(), "sx": sx.cpu().numpy(), "y_bf16": y}
 
 
 def cpu_baseline(lay, rows_per_expert=2048, gpu=None):

@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define MXMOE_ABI_VERSION 4
+#define MXMOE_ABI_VERSION 5
 
 typedef enum {
   MXMOE_OK = 0,
@@ -225,24 +225,34 @@ mxmoe_status mx_grouped_gemm_wgrad_fp8feed(const uint8_t* qdyT, const uint8_t* s
  * ld / 128 tiles of C x 128 bytes:
  *     byte (c, j)  at  (j / 128) * C * 128 + c * 128 + (j % 128),      ld % 128 == 0,
  * so one 128-byte slice of the contraction for all C rows is one contiguous block of memory: the
- * quantiser writes whole tiles, and the GEMMs load a 128-byte stage of a row from one place.  The
- * scales sT [C, ld/32] of such a copy are tiled the same way, four bytes (the scales of one 128-byte
- * slice) per row and tile:
- *     scale byte (c, b)  at  (b / 4) * C * 4 + c * 4 + (b % 4),
- * so a quantiser workgroup writes its scale bytes as one contiguous run rather than one dword per
- * row.  Both buffers keep their sizes (C * ld and C * ld / 32 bytes).
+ * quantiser writes whole tiles, and the GEMMs load a 128-byte stage of a row from one place.  Every
+ * scale buffer of this family, column-wise sT [C, ld/32] and row-wise s [R, C/32] alike, is tiled the
+ * same way, four bytes (the scales of one 128-element slice) per row and tile:
+ *     scale byte (row, b)  at  (b / 4) * rows * 4 + row * 4 + (b % 4),
+ * i.e. sT as [ld/128][C][4] and s as [C/128][R][4] (C % 128 == 0), so a quantiser workgroup writes
+ * its scale bytes as contiguous runs rather than one piece per row, and a GEMM stage reads the four
+ * scale bytes of its 256 rows as one contiguous 1 KiB.  The codes q of a row-wise copy stay row-major.
+ * Every buffer keeps its size.
  * Each entry point below takes exactly the arguments, and validates them as, its row-major namesake,
- * with ld (ldh, ldw) % 128 == 0 required in addition (MXMOE_ERR_ALIGN for the quantisers,
- * MXMOE_ERR_SHAPE for the GEMMs); results are the same bytes / values permuted as above:
- *   mx_quantize_colwise_tiled, mx_quantize_dual_tiled   qT, sT in the tiled layout (q, s unchanged);
- *   mx_grouped_gemm_fwd_swiglu_tiled                    qhT, shT tiled ([ldh/128][H][128],
+ * with ld (ldh, ldw) % 128 == 0 (MXMOE_ERR_ALIGN for the quantisers, MXMOE_ERR_SHAPE for the GEMMs)
+ * and, for a row-wise copy, C % 128 == 0 (MXMOE_ERR_SHAPE) required in addition; results are the same
+ * bytes / values permuted as above:
+ *   mx_quantize_rowwise_tiled                           s tiled ([C/128][R][4]);
+ *   mx_quantize_colwise_tiled                           qT, sT tiled ([ld/128][C][128], [ld/128][C][4]);
+ *   mx_quantize_dual_tiled                              qT, sT and s tiled;
+ *   mx_grouped_gemm_fwd_tiled[_fp8feed]                 sx, sw tiled ([K/128][M][4], [K/128][G N][4]);
+ *   mx_grouped_gemm_fwd_swiglu_tiled                    sx, sw tiled; sh, qhT, shT written tiled
+ *                                                       ([H/128][M][4], [ldh/128][H][128],
  *                                                       [ldh/128][H][4]); qhT and shT are required;
- *   mx_grouped_gemm_dgrad_tiled[_fp8feed]               qwT, swT tiled ([ldw/128][K][128], [.][K][4]);
+ *   mx_grouped_gemm_dgrad_tiled[_fp8feed]               sdy ([N/128][M][4]), qwT, swT ([ldw/128][K][128],
+ *                                                       [ldw/128][K][4]) tiled;
  *   mx_grouped_gemm_wgrad_tiled[_fp8feed]               qdyT, sdyT and qxT, sxT tiled
  *                                                       ([ld/128][N][128], [.][N][4]; [ld/128][K][128],
  *                                                       [.][K][4]).
  * The GEMM results are bit-identical to the row-major entry points on the same data (the same
  * products are summed in the same order). */
+mxmoe_status mx_quantize_rowwise_tiled(const void* x_bf16, int64_t R, int64_t C,
+                                       uint8_t* q, uint8_t* s, void* stream);
 mxmoe_status mx_quantize_colwise_tiled(const void* x_bf16, int64_t R, int64_t C,
                                        const int32_t* offs, int32_t G,
                                        uint8_t* qT, uint8_t* sT, int64_t ld, void* stream);
@@ -251,6 +261,14 @@ mxmoe_status mx_quantize_dual_tiled(const void* x_bf16, int64_t R, int64_t C,
                                     const int32_t* offs, int32_t G,
                                     uint8_t* q, uint8_t* s,
                                     uint8_t* qT, uint8_t* sT, int64_t ld, void* stream);
+mxmoe_status mx_grouped_gemm_fwd_tiled(const uint8_t* qx, const uint8_t* sx,
+                                       const uint8_t* qw, const uint8_t* sw,
+                                       const int32_t* offs, int32_t G, int64_t M, int64_t N, int64_t K,
+                                       void* y, mxmoe_dtype ydt, void* stream);
+mxmoe_status mx_grouped_gemm_fwd_tiled_fp8feed(const uint8_t* qx, const uint8_t* sx,
+                                               const uint8_t* qw, const uint8_t* sw,
+                                               const int32_t* offs, int32_t G, int64_t M, int64_t N, int64_t K,
+                                               void* y, mxmoe_dtype ydt, void* stream);
 mxmoe_status mx_grouped_gemm_fwd_swiglu_tiled(const uint8_t* qx, const uint8_t* sx,
                                               const uint8_t* qw, const uint8_t* sw,
                                               const int32_t* offs, int32_t G, int64_t M, int64_t N,

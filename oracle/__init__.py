@@ -39,7 +39,7 @@ from .mx import (mx_block_exponent, mx_colwise_ld_min, mx_dequantize,
                  mx_quantize_colwise, mx_quantize_rowwise, mx_group_columns,
                  mx_gather_rows, mx_quantize_dual, mxfp4_quantize_rowwise,
                  mxfp4_quantize_colwise, mxfp4_dequantize, mx_quantize_rowwise_values,
-                 mx_quantize_colwise_values, mx_colwise_tiled, mx_colwise_scales_tiled, swiglu)
+                 mx_quantize_colwise_values, mx_colwise_tiled, mx_scales_tiled, swiglu)
 from .blockwise import (bw_quantize_act_1x128, bw_quantize_weight_128x128,
                         bw_dequantize_act, bw_dequantize_weight, bw_colwise_ld_min,
                         bw_group_columns, bw_quantize_colwise_128, pow2_scale)

@@ -276,19 +276,19 @@ def mx_colwise_tiled(qT):
     return out
 
 
-def mx_colwise_scales_tiled(sT):
-    """The scales sT [C, ld / 32] of a column-wise copy in the same tiled layout (the library's stated
-    contract, as above): tile t holds the scale bytes of code tile t, i.e. blocks [4 t, 4 t + 4) of
-    every row, so scale byte (c, b) lands at flat position (b // 4) * C * 4 + c * 4 + b % 4.
-    Returns [ld // 128, C, 4]; ld % 128 == 0."""
-    sT = np.asarray(sT)
-    C, nb = sT.shape
-    per = TILE // 32                       # blocks (scale bytes) per 128-byte code tile
+def mx_scales_tiled(s):
+    """The scale bytes [rows, nb] of an MX copy (row-wise s [R, C / 32] or column-wise sT [C, ld / 32]) in
+    the library's tiled layout (its stated contract, as above): tile t holds blocks [4 t, 4 t + 4) of
+    every row (the scales of code tile t, one 128-element slice), so scale byte (row, b) lands at flat
+    position (b // 4) * rows * 4 + row * 4 + b % 4.  Returns [nb // 4, rows, 4]; nb % 4 == 0."""
+    s = np.asarray(s)
+    rows, nb = s.shape
+    per = TILE // 32                       # blocks (scale bytes) per 128-element slice
     if nb % per:
-        raise ValueError("the tiled layout needs ld % 128 == 0")
-    out = np.empty((nb // per, C, per), dtype=sT.dtype)
+        raise ValueError("the tiled layout needs a multiple of 128 elements per row")
+    out = np.empty((nb // per, rows, per), dtype=s.dtype)
     for t in range(nb // per):
-        out[t] = sT[:, per * t:per * (t + 1)]
+        out[t] = s[:, per * t:per * (t + 1)]
     return out
 
 

@@ -19,8 +19,8 @@ __all__ = [
     "mx_colwise_ld_min", "mxmoe_pitch", "mx_colwise_ld", "mxfp4_colwise_ld",
     "mx_quantize_rowwise", "mx_quantize_colwise", "mx_quantize_dual",
     "mx_grouped_gemm_fwd", "mx_grouped_gemm_dgrad", "mx_grouped_gemm_wgrad", "mx_grouped_gemm_fwd_swiglu",
-    "mx_quantize_colwise_tiled", "mx_quantize_dual_tiled", "mx_grouped_gemm_fwd_swiglu_tiled",
-    "mx_grouped_gemm_dgrad_tiled", "mx_grouped_gemm_wgrad_tiled",
+    "mx_quantize_rowwise_tiled", "mx_quantize_colwise_tiled", "mx_quantize_dual_tiled", "mx_grouped_gemm_fwd_tiled",
+    "mx_grouped_gemm_fwd_swiglu_tiled", "mx_grouped_gemm_dgrad_tiled", "mx_grouped_gemm_wgrad_tiled",
     "fp8bw_quantize_act_1x128", "fp8bw_quantize_weight_128x128",
     "fp8bw_grouped_gemm_fwd", "fp8bw_grouped_gemm_dgrad", "mxmoe_check_offsets",
     "fp8bw_grouped_gemm_fwd_pow2", "fp8bw_grouped_gemm_dgrad_pow2", "fp8bw_grouped_gemm_wgrad_pow2",
@@ -74,9 +74,9 @@ _SIGS = {
                                                 _p]),
     "mxmoe_check_offsets": (ctypes.c_int, [_p, _i32, _i64, _p]),
 }
-# the 128-byte tiled column-wise layout: the same arguments as the row-major entry points
-for _n in ("mx_quantize_colwise", "mx_quantize_dual", "mx_grouped_gemm_fwd_swiglu", "mx_grouped_gemm_dgrad",
-           "mx_grouped_gemm_wgrad"):
+# the 128-byte tiled layouts: the same arguments as the row-major entry points
+for _n in ("mx_quantize_rowwise", "mx_quantize_colwise", "mx_quantize_dual", "mx_grouped_gemm_fwd",
+           "mx_grouped_gemm_fwd_swiglu", "mx_grouped_gemm_dgrad", "mx_grouped_gemm_wgrad"):
     _SIGS[_n + "_tiled"] = _SIGS[_n]
 # blockwise forward / dgrad for power-of-two scales (on the MX kernel): the same arguments
 _SIGS["fp8bw_grouped_gemm_fwd_pow2"] = _SIGS["fp8bw_grouped_gemm_fwd"]
@@ -84,8 +84,8 @@ _SIGS["fp8bw_grouped_gemm_dgrad_pow2"] = _SIGS["fp8bw_grouped_gemm_dgrad"]
 _SIGS["fp8bw_grouped_gemm_wgrad_pow2"] = _SIGS["fp8bw_grouped_gemm_wgrad"]
 # the full-rate FP8 operand feed: the same arguments as the precise entry points
 for _n in ("fp8bw_grouped_gemm_fwd_pow2", "fp8bw_grouped_gemm_dgrad_pow2", "fp8bw_grouped_gemm_wgrad_pow2", "mx_grouped_gemm_fwd", "mx_grouped_gemm_dgrad", "mx_grouped_gemm_wgrad", "fp8bw_grouped_gemm_fwd",
-           "fp8bw_grouped_gemm_dgrad", "fp8bw_grouped_gemm_wgrad", "mx_grouped_gemm_dgrad_tiled",
-           "mx_grouped_gemm_wgrad_tiled"):
+           "fp8bw_grouped_gemm_dgrad", "fp8bw_grouped_gemm_wgrad", "mx_grouped_gemm_fwd_tiled",
+           "mx_grouped_gemm_dgrad_tiled", "mx_grouped_gemm_wgrad_tiled"):
     _SIGS[_n + "_fp8feed"] = _SIGS[_n]
 EXPORTED_SYMBOLS = tuple(_SIGS)
 
@@ -202,15 +202,30 @@ def _call(entry, *args):
 
 
 # ---------------------------------------------------------------- MX quantisers
-def mx_quantize_rowwise(x, q=None, s=None, stream=None) -> Tuple[object, object]:
-    """x bf16 [R, C] -> (q uint8 [R, C], s uint8 [R, C/32])."""
+def _rowwise_scales_out(R, C, tiled, like):
+    """A row-wise copy's scale buffer: [R, C / 32], or [C / 128, R, 4] in the tiled layout."""
+    torch = _torch()
+    return _empty((C // 128, R, 4) if tiled else (R, C // 32), torch.uint8, like)
+
+
+def _rowwise(name, tiled, x, q, s, stream):
     torch = _torch()
     x = _bf16_bits(x)
     R, C = x.shape
     q = _empty((R, C), torch.uint8, x) if q is None else q
-    s = _empty((R, C // 32), torch.uint8, x) if s is None else s
-    _check("mx_quantize_rowwise", lib().mx_quantize_rowwise(_ptr(x), R, C, _ptr(q), _ptr(s), _stream_handle(stream)))
+    s = _rowwise_scales_out(R, C, tiled, x) if s is None else s
+    _check(name, getattr(lib(), name)(_ptr(x), R, C, _ptr(q), _ptr(s), _stream_handle(stream)))
     return q, s
+
+
+def mx_quantize_rowwise(x, q=None, s=None, stream=None) -> Tuple[object, object]:
+    """x bf16 [R, C] -> (q uint8 [R, C], s uint8 [R, C/32])."""
+    return _rowwise("mx_quantize_rowwise", False, x, q, s, stream)
+
+
+def mx_quantize_rowwise_tiled(x, q=None, s=None, stream=None) -> Tuple[object, object]:
+    """As mx_quantize_rowwise with the scales in the tiled layout: s uint8 [C/128, R, 4] (C % 128 == 0)."""
+    return _rowwise("mx_quantize_rowwise_tiled", True, x, q, s, stream)
 
 
 def _colwise_out(C, ld, tiled, like):
@@ -259,7 +274,7 @@ def _dual(name, tiled, x, offs, G, ld, row_idx, q, s, qT, sT, stream):
     if ld is None:
         ld = mx_colwise_ld(R, G if offs is not None else None)
     q = _empty((R, C), torch.uint8, x) if q is None else q
-    s = _empty((R, C // 32), torch.uint8, x) if s is None else s
+    s = _rowwise_scales_out(R, C, tiled, x) if s is None else s
     qT = _colwise_out(C, ld, tiled, x) if qT is None else qT
     sT = _colwise_scales_out(C, ld, tiled, x) if sT is None else sT
     _check(name, getattr(lib(), name)(_ptr(x), R, C, _ptr(row_idx), R_src, _ptr(offs), G, _ptr(q), _ptr(s), _ptr(qT),
@@ -278,20 +293,31 @@ def mx_quantize_dual(x, offs=None, G: int = 1, ld: Optional[int] = None, row_idx
 
 def mx_quantize_dual_tiled(x, offs=None, G: int = 1, ld: Optional[int] = None, row_idx=None, q=None, s=None,
                            qT=None, sT=None, stream=None):
-    """As mx_quantize_dual with qT, sT in the 128-byte tiled layout: [ld/128, C, 128], [ld/128, C, 4]."""
+    """As mx_quantize_dual in the 128-byte tiled layouts: qT [ld/128, C, 128], sT [ld/128, C, 4] and
+    s [C/128, R, 4] (C % 128 == 0)."""
     return _dual("mx_quantize_dual_tiled", True, x, offs, G, ld, row_idx, q, s, qT, sT, stream)
 
 
 # ---------------------------------------------------------------- MX grouped GEMMs
-def mx_grouped_gemm_fwd(qx, sx, qw, sw, offs, N: int, out_dtype: str = "f32", y=None, stream=None, fast: bool = False):
-    """Y [M, N] = per-expert X_g W_g^T from row-wise MX operands (qw: [G*N, K])."""
+def _fwd(name, qx, sx, qw, sw, offs, N, out_dtype, y, stream, fast):
     M, K = qx.shape
     G = offs.numel() - 1
     tdt, cdt = _out_dtype(out_dtype)
     y = _empty((M, N), tdt, qx) if y is None else y
-    _check(*_call(_gemm("mx_grouped_gemm_fwd", fast), _ptr(qx), _ptr(sx), _ptr(qw), _ptr(sw), _ptr(offs), G, M,
-                                                            N, K, _ptr(y), cdt, _stream_handle(stream)))
+    _check(*_call(_gemm(name, fast), _ptr(qx), _ptr(sx), _ptr(qw), _ptr(sw), _ptr(offs), G, M, N, K, _ptr(y), cdt,
+                  _stream_handle(stream)))
     return y
+
+
+def mx_grouped_gemm_fwd(qx, sx, qw, sw, offs, N: int, out_dtype: str = "f32", y=None, stream=None, fast: bool = False):
+    """Y [M, N] = per-expert X_g W_g^T from row-wise MX operands (qw: [G*N, K])."""
+    return _fwd("mx_grouped_gemm_fwd", qx, sx, qw, sw, offs, N, out_dtype, y, stream, fast)
+
+
+def mx_grouped_gemm_fwd_tiled(qx, sx, qw, sw, offs, N: int, out_dtype: str = "f32", y=None, stream=None,
+                              fast: bool = False):
+    """As mx_grouped_gemm_fwd with the scales in the tiled layout (sx [K/128, M, 4], sw [K/128, G*N, 4])."""
+    return _fwd("mx_grouped_gemm_fwd_tiled", qx, sx, qw, sw, offs, N, out_dtype, y, stream, fast)
 
 
 def _swiglu(name, tiled, qx, sx, qw, sw, offs, N, y, qh, sh, h, with_h, colwise, ldh, qhT, shT, stream):
@@ -301,7 +327,7 @@ def _swiglu(name, tiled, qx, sx, qw, sw, offs, N, y, qh, sh, h, with_h, colwise,
     H = N // 2
     y = _empty((M, N), torch.bfloat16, qx) if y is None else y
     qh = _empty((M, H), torch.uint8, qx) if qh is None else qh
-    sh = _empty((M, H // 32), torch.uint8, qx) if sh is None else sh
+    sh = _rowwise_scales_out(M, H, tiled, qx) if sh is None else sh
     if with_h and h is None:
         h = _empty((M, H), torch.float32, qx)
     if colwise or tiled or qhT is not None:
@@ -332,8 +358,9 @@ def mx_grouped_gemm_fwd_swiglu(qx, sx, qw, sw, offs, N: int, y=None, qh=None, sh
 def mx_grouped_gemm_fwd_swiglu_tiled(qx, sx, qw, sw, offs, N: int, y=None, qh=None, sh=None, h=None,
                                      with_h: bool = False, ldh: Optional[int] = None, qhT=None, shT=None,
                                      stream=None):
-    """As mx_grouped_gemm_fwd_swiglu, always with H column-wise, qhT and shT in the 128-byte tiled
-    layout ([ldh/128, H, 128], [ldh/128, H, 4]).  Returns (y, qh, sh, qhT, shT[, h])."""
+    """As mx_grouped_gemm_fwd_swiglu in the 128-byte tiled layouts: sx [K/128, M, 4] and sw [K/128, G*N, 4]
+    in; sh [H/128, M, 4], qhT [ldh/128, H, 128], shT [ldh/128, H, 4] out (H always column-wise too).
+    Returns (y, qh, sh, qhT, shT[, h])."""
     return _swiglu("mx_grouped_gemm_fwd_swiglu_tiled", True, qx, sx, qw, sw, offs, N, y, qh, sh, h, with_h, True,
                    ldh, qhT, shT, stream)
 
@@ -345,8 +372,8 @@ def mx_grouped_gemm_dgrad(qdy, sdy, qwT, swT, offs, K: int, out_dtype: str = "f3
 
 def mx_grouped_gemm_dgrad_tiled(qdy, sdy, qwT, swT, offs, K: int, out_dtype: str = "f32", dx=None, stream=None,
                                 fast: bool = False):
-    """As mx_grouped_gemm_dgrad with qwT, swT in the 128-byte tiled layout ([ldw/128, K, 128],
-    [ldw/128, K, 4])."""
+    """As mx_grouped_gemm_dgrad in the 128-byte tiled layouts: sdy [N/128, M, 4], qwT [ldw/128, K, 128],
+    swT [ldw/128, K, 4]."""
     return _dgrad("mx_grouped_gemm_dgrad_tiled", qwT.shape[0] * 128, qdy, sdy, qwT, swT, offs, K, out_dtype, dx,
                   stream, fast)
 

@@ -122,16 +122,26 @@ int64_t mxmoe_pitch(int64_t min_ld) {
   return ld;
 }
 
-mxmoe_status mx_quantize_rowwise(const void* x, int64_t R, int64_t C, uint8_t* q, uint8_t* s, void* stream) {
-  const char* fn = "mx_quantize_rowwise";
+static mxmoe_status rowwise_impl(const char* fn, const void* x, int64_t R, int64_t C, uint8_t* q, uint8_t* s,
+                                 bool tiled, void* stream) {
   if (R < 0 || C <= 0 || C % 32) return fail(MXMOE_ERR_SHAPE, "%s: need R >= 0, C > 0, C %% 32 == 0 (R=%lld C=%lld)",
                                             fn, (long long)R, (long long)C);
+  if (tiled && C % 128)
+    return fail(MXMOE_ERR_SHAPE, "%s: the tiled scale layout needs C %% 128 == 0 (C=%lld)", fn, (long long)C);
   if (R == 0) return ok();
   TRY(check_ptr(fn, "x", x, 16));
   TRY(check_ptr(fn, "q", q, 16));
   TRY(check_ptr(fn, "s", s, 4));
   TRY(check_device());
-  return launched(launch_mx_rowwise((const uint16_t*)x, R, C, q, s, (hipStream_t)stream), fn);
+  return launched(launch_mx_rowwise((const uint16_t*)x, R, C, q, s, tiled, (hipStream_t)stream), fn);
+}
+
+mxmoe_status mx_quantize_rowwise(const void* x, int64_t R, int64_t C, uint8_t* q, uint8_t* s, void* stream) {
+  return rowwise_impl("mx_quantize_rowwise", x, R, C, q, s, false, stream);
+}
+
+mxmoe_status mx_quantize_rowwise_tiled(const void* x, int64_t R, int64_t C, uint8_t* q, uint8_t* s, void* stream) {
+  return rowwise_impl("mx_quantize_rowwise_tiled", x, R, C, q, s, true, stream);
 }
 
 static mxmoe_status colwise_impl(const char* fn, const void* x, int64_t R, int64_t C, const int32_t* offs, int32_t G,
@@ -175,6 +185,8 @@ static mxmoe_status dual_impl(const char* fn, const void* x, int64_t R, int64_t 
                                       (long long)ld);
   if (tiled && ld % 128)
     return fail(MXMOE_ERR_ALIGN, "%s: the tiled layout needs ld %% 128 == 0 (ld=%lld)", fn, (long long)ld);
+  if (tiled && C % 128)
+    return fail(MXMOE_ERR_SHAPE, "%s: the tiled scale layout needs C %% 128 == 0 (C=%lld)", fn, (long long)C);
   const int64_t need = offs ? mx_colwise_ld_min(R, G) : 32 * ((R + 31) / 32);
   if (ld < need) return fail(MXMOE_ERR_SHAPE, "%s: ld=%lld < required %lld", fn, (long long)ld, (long long)need);
   if (row_idx && R > 0 && R_src < 1)
@@ -250,13 +262,18 @@ static mxmoe_status mx_gemm_common(int mode, const char* fn, const uint8_t* a, c
   if (mode == kWgrad) p.ld_cols = ldb_cols;
   if (tiled) {
     // column-wise operands in the 128-byte tiled layout: rows 128 bytes apart, chunks rows * 128 apart;
-    // their scales [ld / 128][rows][4]: rows 4 bytes apart, 4-byte groups rows * 4 apart
-    if (mode == kWgrad) {
-      p.lda = 128; p.a_kstride = 128 * N;
-      p.ldsa = 4; p.sa_gstride = 4 * N;
+    // every scale buffer (row-wise and column-wise) [chunks][rows][4]: rows 4 bytes apart, 4-byte groups
+    // rows * 4 apart
+    p.ldsa = 4; p.ldsb = 4;
+    if (mode == kFwd) {
+      p.sa_gstride = 4 * M; p.sb_gstride = 4 * (int64_t)G * N;
+    } else if (mode == kDgrad) {
+      p.sa_gstride = 4 * M;
+      p.ldb = 128; p.b_kstride = 128 * K; p.sb_gstride = 4 * K;
+    } else {
+      p.lda = 128; p.a_kstride = 128 * N; p.sa_gstride = 4 * N;
+      p.ldb = 128; p.b_kstride = 128 * K; p.sb_gstride = 4 * K;
     }
-    p.ldb = 128; p.b_kstride = 128 * K;
-    p.ldsb = 4; p.sb_gstride = 4 * K;
   }
   TRY(check_strides(fn, p, 256));
   if (mode != kWgrad && M == 0) return ok();
@@ -276,6 +293,20 @@ mxmoe_status mx_grouped_gemm_fwd_fp8feed(const uint8_t* qx, const uint8_t* sx, c
                                          mxmoe_dtype ydt, void* stream) {
   return mx_gemm_common(kFwd, "mx_grouped_gemm_fwd_fp8feed", qx, sx, qw, sw, 0, offs, G, M, N, K, y, (int)ydt,
                         stream, kFeedFast);
+}
+
+mxmoe_status mx_grouped_gemm_fwd_tiled(const uint8_t* qx, const uint8_t* sx, const uint8_t* qw, const uint8_t* sw,
+                                       const int32_t* offs, int32_t G, int64_t M, int64_t N, int64_t K, void* y,
+                                       mxmoe_dtype ydt, void* stream) {
+  return mx_gemm_common(kFwd, "mx_grouped_gemm_fwd_tiled", qx, sx, qw, sw, 0, offs, G, M, N, K, y, (int)ydt, stream,
+                        kFeedPrecise, false, true);
+}
+
+mxmoe_status mx_grouped_gemm_fwd_tiled_fp8feed(const uint8_t* qx, const uint8_t* sx, const uint8_t* qw,
+                                               const uint8_t* sw, const int32_t* offs, int32_t G, int64_t M, int64_t N,
+                                               int64_t K, void* y, mxmoe_dtype ydt, void* stream) {
+  return mx_gemm_common(kFwd, "mx_grouped_gemm_fwd_tiled_fp8feed", qx, sx, qw, sw, 0, offs, G, M, N, K, y, (int)ydt,
+                        stream, kFeedFast, false, true);
 }
 
 static mxmoe_status swiglu_impl(const char* fn, const uint8_t* qx, const uint8_t* sx, const uint8_t* qw,
@@ -311,6 +342,12 @@ static mxmoe_status swiglu_impl(const char* fn, const uint8_t* qx, const uint8_t
   p.act_qT = qhT; p.act_sT = shT; p.act_ld = ldh;
   p.act_tiled = tiled;
   p.a_kstride = p.b_kstride = 128;
+  p.sa_gstride = p.sb_gstride = 4;
+  if (tiled) {
+    // row-wise scales of X and W in the tiled layout ([K / 128][M][4], [K / 128][G N][4])
+    p.ldsa = 4; p.sa_gstride = 4 * M;
+    p.ldsb = 4; p.sb_gstride = 4 * (int64_t)G * N;
+  }
   TRY(check_strides(fn, p, N));
   if (M == 0) return ok();
   TRY(check_device());

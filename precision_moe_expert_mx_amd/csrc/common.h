@@ -193,8 +193,10 @@ __device__ __forceinline__ void block_rows(int bc, int nbc, int G, const int32_t
 }
 
 // ---- internal launchers (defined in the .hip files; arguments already validated) ---------------
-hipError_t launch_mx_rowwise(const uint16_t* x, int64_t R, int64_t C, uint8_t* q, uint8_t* s, hipStream_t st);
-// tiled: qT in the 128-byte tiled layout, [ld / 128][C][128] (ld % 128 == 0)
+hipError_t launch_mx_rowwise(const uint16_t* x, int64_t R, int64_t C, uint8_t* q, uint8_t* s, bool tiled,
+                             hipStream_t st);
+// tiled: qT and sT in the 128-byte tiled layout, [ld / 128][C][128] and [ld / 128][C][4] (ld % 128 == 0);
+// for the row-wise copies (launch_mx_rowwise, launch_mx_dual) s as [C / 128][R][4] (C % 128 == 0)
 hipError_t launch_mx_colwise(const uint16_t* x, int64_t R, int64_t C, const int32_t* offs, int32_t G,
                              uint8_t* qT, uint8_t* sT, int64_t ld, bool tiled, hipStream_t st);
 hipError_t launch_mxfp4_rowwise(const uint16_t* x, int64_t R, int64_t C, uint8_t* q, uint8_t* s, hipStream_t st);
@@ -247,7 +249,8 @@ struct GemmArgs {
   uint8_t* act_qT;
   uint8_t* act_sT;
   int64_t act_ld;
-  int32_t act_tiled;    // act_qT in the 128-byte tiled layout ([act_ld / 128][H][128])
+  int32_t act_tiled;    // the tiled layouts: act_qT [act_ld / 128][H][128], act_sT [act_ld / 128][H][4],
+                        // act_s [H / 128][M][4]
 };
 
 hipError_t launch_mx_gemm(int mode, const GemmArgs& a, hipStream_t st);

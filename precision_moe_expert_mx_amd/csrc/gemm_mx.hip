@@ -166,7 +166,12 @@ __device__ __forceinline__ void act_epilogue(const GemmArgs& p, const Tile& t, c
           if (p.act_dbg)
             *(float4*)(p.act_dbg + grow * H + hc + 8 * q) = make_float4(h[4 * q], h[4 * q + 1], h[4 * q + 2], h[4 * q + 3]);
         }
-        if (lane < 32) p.act_s[grow * (H / 32) + (hc - 4 * (lane / 32)) / 32] = (uint8_t)(e + 127);
+        if (lane < 32) {
+          // row-wise scales [M, H / 32], or tiled [H / 128][M][4]
+          const int64_t blk = (hc - 4 * (lane / 32)) / 32;
+          const int64_t off = p.act_tiled ? (blk >> 2) * (p.M * 4) + grow * 4 + (blk & 3) : grow * (H / 32) + blk;
+          p.act_s[off] = (uint8_t)(e + 127);
+        }
       }
     }
   }

@@ -45,8 +45,12 @@ __device__ __forceinline__ uint32_t mag_max8(const uint4& v) {
   return max((uint32_t)m[0], (uint32_t)m[1]);
 }
 
+// TILED: the scales in the tiled layout [C / 128][R][4] (the four scale bytes of a row's 128-element
+// chunk together, the chunk's rows one after another); c32 = C / 32 blocks per row.
+template <bool TILED>
 __global__ __launch_bounds__(kRowThreads) void mx_rowwise_kernel(const uint4* __restrict__ x, int64_t nchunks,
-                                                                  uint2* __restrict__ q, uint8_t* __restrict__ s) {
+                                                                  uint2* __restrict__ q, uint8_t* __restrict__ s,
+                                                                  int64_t R, int64_t c32) {
   const int64_t base = (int64_t)blockIdx.x * (kRowThreads * kRowUnroll) + threadIdx.x;
   uint4 v[kRowUnroll];
 #pragma unroll
@@ -68,18 +72,32 @@ __global__ __launch_bounds__(kRowThreads) void mx_rowwise_kernel(const uint4* __
     o.y = cvt4_e4m3(v[j].z, v[j].w, cl2, sc);
     if (i < nchunks) {
       store8_nt(q + i, o);
-      if ((threadIdx.x & 3) == 0) s[i >> 2] = (uint8_t)(e + 127);
+      if ((threadIdx.x & 3) == 0) {
+        const int64_t blk = i >> 2;
+        int64_t off = blk;
+        if (TILED) {
+          const int64_t r = blk / c32, b = blk - r * c32;
+          off = (b >> 2) * (R * 4) + r * 4 + (b & 3);
+        }
+        s[off] = (uint8_t)(e + 127);
+      }
     }
   }
 }
 
-hipError_t launch_mx_rowwise(const uint16_t* x, int64_t R, int64_t C, uint8_t* q, uint8_t* s, hipStream_t st) {
+hipError_t launch_mx_rowwise(const uint16_t* x, int64_t R, int64_t C, uint8_t* q, uint8_t* s, bool tiled,
+                             hipStream_t st) {
   int64_t nchunks = R * C / 8;
   if (nchunks == 0) return hipSuccess;
+  if (tiled && C % 128) return hipErrorInvalidValue;
   int64_t per = (int64_t)kRowThreads * kRowUnroll;
   int64_t blocks = (nchunks + per - 1) / per;
-  hipLaunchKernelGGL(mx_rowwise_kernel, dim3((unsigned)blocks), dim3(kRowThreads), 0, st,
-                     (const uint4*)x, nchunks, (uint2*)q, s);
+  if (tiled)
+    hipLaunchKernelGGL(mx_rowwise_kernel<true>, dim3((unsigned)blocks), dim3(kRowThreads), 0, st,
+                       (const uint4*)x, nchunks, (uint2*)q, s, R, C / 32);
+  else
+    hipLaunchKernelGGL(mx_rowwise_kernel<false>, dim3((unsigned)blocks), dim3(kRowThreads), 0, st,
+                       (const uint4*)x, nchunks, (uint2*)q, s, R, C / 32);
   return hipGetLastError();
 }
 
@@ -335,11 +353,20 @@ __device__ __forceinline__ void col_group(const ColArgs& a, int r0, int n, int b
         for (int j = 0; j < 4; ++j) lo |= (uint32_t)rsc[(wb * kRowBlks + j) * 32 + r] << (8 * j);
 #pragma unroll
         for (int j = 0; j < 4; ++j) hi |= (uint32_t)rsc[(wb * kRowBlks + 4 + j) * 32 + r] << (8 * j);
-        uint8_t* dst = a.s + ((int64_t)g_r0[wb] + r) * c32 + a.cbase / 32;
-        if (nrb == kRowBlks && ((uintptr_t)dst & 7) == 0) {
-          *(uint2*)dst = make_uint2(lo, hi);
+        const int64_t row = (int64_t)g_r0[wb] + r;
+        if (TILED) {
+          // tiled scales [C / 128][R][4] (C % 128 == 0, so nrb is 4 or 8): one dword per 128-column
+          // chunk, the chunk's rows one after another
+          uint8_t* dst = a.s + (a.cbase / 128) * (a.R * 4) + row * 4;
+          *(uint32_t*)dst = lo;
+          if (nrb > 4) *(uint32_t*)(dst + a.R * 4) = hi;
         } else {
-          for (int j = 0; j < nrb; ++j) dst[j] = (uint8_t)((j < 4 ? lo : hi) >> (8 * (j & 3)));
+          uint8_t* dst = a.s + row * c32 + a.cbase / 32;
+          if (nrb == kRowBlks && ((uintptr_t)dst & 7) == 0) {
+            *(uint2*)dst = make_uint2(lo, hi);
+          } else {
+            for (int j = 0; j < nrb; ++j) dst[j] = (uint8_t)((j < 4 ? lo : hi) >> (8 * (j & 3)));
+          }
         }
       }
     }
@@ -461,7 +488,7 @@ hipError_t launch_mx_dual(const uint16_t* x, int64_t R, int64_t C, const int32_t
                           const int32_t* offs, int32_t G, uint8_t* q, uint8_t* s, uint8_t* qT, uint8_t* sT, int64_t ld,
                           bool tiled, hipStream_t st) {
   if (C == 0 || ld == 0) return hipSuccess;
-  if (tiled && ld % 128) return hipErrorInvalidValue;
+  if (tiled && (ld % 128 || C % 128)) return hipErrorInvalidValue;
   const int64_t nwg = colwise_grid(C, ld);
   if (nwg > 0x7FFFFFFF) return hipErrorInvalidValue;
   const bool fw = C % kColCols == 0;

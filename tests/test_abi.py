@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
     m, L = _lib()
     for name in _declared():
         assert hasattr(L, name), name
-    assert m.abi_version() == 4
+    assert m.abi_version() == 5
 
 
 def test_host_helpers():
@@ -202,6 +202,24 @@ def test_tiled_entry_points_need_a_pitch_multiple_of_128():
     assert st == 1 and "qhT" in msg
     st, msg = _status(L, "mx_grouped_gemm_fwd_swiglu_tiled", *sw, None, A16b, A16b, 1184, None)
     assert st == 2 and "128" in msg
+
+
+def test_tiled_row_wise_scales_need_whole_128_column_slices():
+    """Tiled row-wise scales ([C/128][R][4]): the row-wise and dual tiled quantisers refuse C % 128 != 0
+    (MXMOE_ERR_SHAPE) where their row-major namesakes accept any C % 32 == 0; the tiled forward GEMM
+    validates as mx_grouped_gemm_fwd."""
+    _, L = _lib()
+    st, msg = _status(L, "mx_quantize_rowwise_tiled", A16, 100, 96, A16, A16, None)
+    assert st == 2 and "128" in msg and "mx_quantize_rowwise_tiled" in msg
+    st, msg = _status(L, "mx_quantize_dual_tiled", A16, 1000, 96, None, 0, A16, 4, A16, A16, A16b, A16b, 1152, None)
+    assert st == 2 and "128" in msg
+    assert _status(L, "mx_quantize_rowwise_tiled", A16, 100, 64 + 1, A16, A16, None)[0] == 2
+    assert _status(L, "mx_quantize_rowwise_tiled", A16, 0, 128, None, None, None)[0] == 0    # R == 0: no-op
+    assert _status(L, "mx_quantize_rowwise_tiled", A16, 100, 128, A16, None, None)[0] == 1
+    for fn in ("mx_grouped_gemm_fwd_tiled", "mx_grouped_gemm_fwd_tiled_fp8feed"):
+        st, msg = _status(L, fn, A16, A16, A16b, A16b, A16, 4, 1024, 500, 256, A16, 0, None)   # N % 128
+        assert st == 2 and fn in msg, (fn, msg)
+        assert _status(L, fn, A16, A16, A16b, A16b, None, 4, 1024, 512, 256, A16, 0, None)[0] == 1
 
 
 def test_pow2_blockwise_entry_points_validate_like_the_blockwise_ones():

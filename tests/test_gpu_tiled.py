@@ -1,9 +1,10 @@
-"""The 128-byte tiled column-wise layout on the GPU.
+"""The 128-byte tiled layouts on the GPU (column-wise codes and every scale buffer tiled).
 
-Quantiser outputs are compared byte for byte with the oracle's column-wise quantisation permuted by
-oracle.mx_colwise_tiled and oracle.mx_colwise_scales_tiled (the layout's stated contract); the GEMMs that read tiled operands must give
-results bit-identical to the row-major entry points on the same data and lie within the oracle's
-bound; the gated forward's tiled H is compared with the oracle's quantisation of the kernel's H.
+Quantiser outputs are compared byte for byte with the oracle's quantisation permuted by
+oracle.mx_colwise_tiled and oracle.mx_scales_tiled (the layout's stated contract); the GEMMs that read
+tiled operands must give results bit-identical to the row-major entry points on the same data and lie
+within the oracle's bound; the gated forward's tiled H is compared with the oracle's quantisation of
+the kernel's H.
 Output buffers are pre-filled with 0xAB so that every byte the contract defines must be written."""
 import numpy as np
 import pytest
@@ -35,7 +36,7 @@ def _untile(t):
 
 def _tiles(qo, so):
     """The oracle's row-major column-wise copy in the tiled layout (codes and scales)."""
-    return oracle.mx_colwise_tiled(qo), oracle.mx_colwise_scales_tiled(so)
+    return oracle.mx_colwise_tiled(qo), oracle.mx_scales_tiled(so)
 
 
 def _colwise_tiled_equal(m, x, offs, ld):
@@ -69,13 +70,24 @@ def test_colwise_tiled_ragged_groups():
 def _dual_tiled_equal(m, x, offs, ld, row_idx=None):
     R = x.shape[0] if row_idx is None else len(row_idx)
     C = x.shape[1]
-    q, s = _filled((R, C)), _filled((R, C // 32))
+    q, s = _filled((R, C)), _filled((C // 128, R, 4))
     qT, sT = _filled((ld // 128, C, 128)), _filled((ld // 128, C, 4))
     m.mx_quantize_dual_tiled(dev(x), None if offs is None else dev(offs), ld=ld,
                              row_idx=None if row_idx is None else dev(row_idx), q=q, s=s, qT=qT, sT=sT)
     ro = oracle.mx_quantize_dual(x, offs, ld, row_idx)
-    same_bytes((host(q), host(s), host(qT), host(sT)), (ro[0], ro[1]) + _tiles(ro[2], ro[3]),
+    same_bytes((host(q), host(s), host(qT), host(sT)), (ro[0], oracle.mx_scales_tiled(ro[1])) + _tiles(ro[2], ro[3]),
                f"tiled dual {R}x{C} ld {ld}")
+
+
+def test_rowwise_tiled():
+    m = require_gpu()
+    rng = np.random.default_rng(86)
+    for R, C in ((1, 128), (37, 256), (300, 384), (1000, 1152)):
+        x = random_bf16(rng, (R, C), outlier_frac=0.01, outlier_mult=1000.0)
+        q, s = _filled((R, C)), _filled((C // 128, R, 4))
+        m.mx_quantize_rowwise_tiled(dev(x), q=q, s=s)
+        qo, so = oracle.mx_quantize_rowwise(x)
+        same_bytes((host(q), host(s)), (qo, oracle.mx_scales_tiled(so)), f"tiled row-wise {R}x{C}")
 
 
 def test_dual_tiled_ragged_groups_partial_windows_and_gather():
@@ -84,12 +96,12 @@ def test_dual_tiled_ragged_groups_partial_windows_and_gather():
     sizes = [0, 5, 130, 1, 60, 33, 0]
     offs = routing_offsets(sizes)
     M = int(offs[-1])
-    for C in (32, 96, 288, 512, 1056):
+    for C in (128, 384, 512, 1152):                 # 384 and 1152: a last window of 128 columns
         x = random_bf16(rng, (M, C), outlier_frac=0.01, outlier_mult=1000.0)
         ld = _ld128(oracle.mx_colwise_ld_min(M, len(sizes)))
         _dual_tiled_equal(m, x, offs, ld)
         _dual_tiled_equal(m, x, offs, ld + 128)
-    x = random_bf16(rng, (3 * 128 + 7, 320), std=0.02)
+    x = random_bf16(rng, (3 * 128 + 7, 640), std=0.02)
     _dual_tiled_equal(m, x, None, _ld128(x.shape[0]))
     # routed rows gathered by index (top-2), two indices out of range (clamped)
     T, C, G = 300, 384, 5
@@ -114,7 +126,8 @@ def test_dual_tiled_full_size_sampled():
     ld = m.mx_colwise_ld(lay.M, lay.G)
     assert ld % 128 == 0
     q, s, qT, sT = m.mx_quantize_dual_tiled(dev(lay.x), dev(lay.offs), ld=ld)
-    same_bytes((host(q[rows]), host(s[rows])), oracle.mx_quantize_rowwise(lay.x[rows]), "dual tiled, row-wise")
+    same_bytes((host(q[rows]), _untile(s[:, rows, :])), oracle.mx_quantize_rowwise(lay.x[rows]),
+               "dual tiled, row-wise")
     qo, so = oracle.mx_quantize_colwise(np.ascontiguousarray(lay.x[:, cols]), lay.offs, ld)
     same_bytes((_untile(qT[:, cols, :]), _untile(sT[:, cols, :])), (qo, so), "dual tiled, column-wise")
     del q, s, qT, sT
@@ -130,7 +143,7 @@ def _layer(rng, sizes, N, K):
 
 @pytest.mark.parametrize("fast", [False, True])
 def test_gemms_on_tiled_operands(fast):
-    """dgrad and wgrad from tiled column-wise operands: bit-identical to the row-major entry points, and
+    """fwd, dgrad and wgrad from tiled operands: bit-identical to the row-major entry points, and
     within the oracle's bound on the oracle's own quantisation (the tiled bytes checked first)."""
     m = require_gpu()
     rng = np.random.default_rng(84)
@@ -139,14 +152,30 @@ def test_gemms_on_tiled_operands(fast):
         offs, x, w, dy = _layer(rng, sizes, N, K)
         M, G = int(offs[-1]), len(sizes)
         offs_d = dev(offs)
-        # dgrad: W column-wise [K, ldw] (ldw padded past G*N)
+        # forward: row-wise X and W with tiled scales
+        qx, sx = m.mx_quantize_rowwise(dev(x))
+        qw, sw = m.mx_quantize_rowwise(dev(w))
+        qxt, sxt = m.mx_quantize_rowwise_tiled(dev(x))
+        qwt, swt = m.mx_quantize_rowwise_tiled(dev(w))
+        xo, wo = oracle.mx_quantize_rowwise(x), oracle.mx_quantize_rowwise(w)
+        same_bytes((host(qxt), host(sxt), host(qwt), host(swt)),
+                   (xo[0], oracle.mx_scales_tiled(xo[1]), wo[0], oracle.mx_scales_tiled(wo[1])), "X, W row-wise tiled")
+        y = m.mx_grouped_gemm_fwd(qx, sx, qw, sw, offs_d, N, "f32", fast=fast)
+        yt = m.mx_grouped_gemm_fwd_tiled(qxt, sxt, qwt, swt, offs_d, N, "f32", fast=fast)
+        assert torch.equal(y, yt), "fwd: tiled scales give other bits than the row-major ones"
+        ref, bnd = oracle.mx_gemm_fwd(*xo, *wo, offs, N)
+        ok, worst, _ = oracle.check_gemm(host(yt).astype(np.float64), ref, bnd, "f32", rel=rel)
+        assert ok, f"fwd tiled: worst err/tol {worst:.3g}"
+        # dgrad: dY row-wise (tiled scales), W column-wise [K, ldw] (ldw padded past G*N)
         qdy, sdy = m.mx_quantize_rowwise(dev(dy))
+        qdyr, sdyt = m.mx_quantize_rowwise_tiled(dev(dy))
+        same_bytes((host(qdyr), host(sdyt)), (host(qdy), oracle.mx_scales_tiled(host(sdy))), "dY row-wise tiled")
         ldw = _ld128(G * N) + 128
         qwT, swT = m.mx_quantize_colwise(dev(w), None, ld=ldw)
         qwTt, swTt = m.mx_quantize_colwise_tiled(dev(w), None, ld=ldw)
         same_bytes((host(qwTt), host(swTt)), _tiles(host(qwT), host(swT)), "W tiled vs row-major")
         dx = m.mx_grouped_gemm_dgrad(qdy, sdy, qwT, swT, offs_d, K, "f32", fast=fast)
-        dxt = m.mx_grouped_gemm_dgrad_tiled(qdy, sdy, qwTt, swTt, offs_d, K, "f32", fast=fast)
+        dxt = m.mx_grouped_gemm_dgrad_tiled(qdyr, sdyt, qwTt, swTt, offs_d, K, "f32", fast=fast)
         assert torch.equal(dx, dxt), "dgrad: tiled operand gives other bits than the row-major one"
         qo, so = oracle.mx_quantize_colwise(w, None, ldw)
         same_bytes((host(qwTt), host(swTt)), _tiles(qo, so), "W tiled")
@@ -175,22 +204,31 @@ def test_gemms_on_tiled_operands(fast):
 
 
 def test_gemms_on_tiled_operands_full_size():
-    """DeepSeek-V3-671B shard gate+up dgrad and wgrad at full size: the tiled-operand launches give the
-    row-major launches' bits exactly, on every element."""
+    """DeepSeek-V3-671B shard gate+up fwd, dgrad and wgrad at full size: the tiled-operand launches give
+    the row-major launches' bits exactly, on every element."""
     m = require_gpu()
     lay = make_workload("dsv3_671b_shard", layers=["gate_up"]).layers[0]
     G, M, N, K = lay.G, lay.M, lay.N, lay.K
     offs = dev(lay.offs)
     x, dy, w = dev(lay.x), dev(lay.dy), dev(lay.w.reshape(G * N, K))
+    qx, sx = m.mx_quantize_rowwise(x)
+    qw, sw = m.mx_quantize_rowwise(w)
+    a = m.mx_grouped_gemm_fwd(qx, sx, qw, sw, offs, N, "bf16")
+    _, sxt = m.mx_quantize_rowwise_tiled(x)
+    _, swt = m.mx_quantize_rowwise_tiled(w)
+    b = m.mx_grouped_gemm_fwd_tiled(qx, sxt, qw, swt, offs, N, "bf16")
+    assert torch.equal(a, b), "full-size fwd: tiled and row-major differ"
+    del a, b, qx, sx, qw, sw, sxt, swt
     qdy, sdy = m.mx_quantize_rowwise(dy)
     ldw = m.mx_colwise_ld(G * N)
     qwT, swT = m.mx_quantize_colwise(w, None, ld=ldw)
     a = m.mx_grouped_gemm_dgrad(qdy, sdy, qwT, swT, offs, K, "bf16")
     del qwT
+    _, sdyt = m.mx_quantize_rowwise_tiled(dy)
     qwTt, swTt = m.mx_quantize_colwise_tiled(w, None, ld=ldw)
-    b = m.mx_grouped_gemm_dgrad_tiled(qdy, sdy, qwTt, swTt, offs, K, "bf16")
+    b = m.mx_grouped_gemm_dgrad_tiled(qdy, sdyt, qwTt, swTt, offs, K, "bf16")
     assert torch.equal(a, b), "full-size dgrad: tiled and row-major differ"
-    del a, b, qwTt, swTt, qdy, sdy
+    del a, b, qwTt, swTt, qdy, sdy, sdyt
     ld = m.mx_colwise_ld(M, G)
     _, _, qdyT, sdyT = m.mx_quantize_dual(dy, offs, ld=ld)
     _, _, qxT, sxT = m.mx_quantize_dual(x, offs, ld=ld)
@@ -205,9 +243,10 @@ def test_gemms_on_tiled_operands_full_size():
 
 
 def test_swiglu_tiled_column_wise_h():
-    """The gated forward writing H column-wise in the tiled layout: Y, qh and sh the same bits as the
-    row-major variant; qhT / shT bit-exact against the oracle's column-wise quantisation of the
-    kernel's fp32 H, permuted into tiles (experts of 0, 1, 31, 33, 255, 256, 257 rows; padded ldh)."""
+    """The gated forward in the tiled layouts (tiled scales of X and W in, sh, qhT, shT tiled out): Y, qh
+    and sh the same bits as the row-major variant (sh permuted); qhT / shT bit-exact against the
+    oracle's column-wise quantisation of the kernel's fp32 H, permuted into tiles (experts of 0, 1, 31,
+    33, 255, 256, 257 rows; padded ldh)."""
     m = require_gpu()
     rng = np.random.default_rng(85)
     for sizes, N, K in (([0, 1, 31, 33, 255, 0, 256, 257], 256, 256), ([300], 512, 256)):
@@ -217,13 +256,17 @@ def test_swiglu_tiled_column_wise_h():
         offs_d = dev(offs)
         qx, sx = m.mx_quantize_rowwise(dev(x))
         qw, sw = m.mx_quantize_rowwise(dev(w))
+        _, sxt = m.mx_quantize_rowwise_tiled(dev(x))
+        _, swt = m.mx_quantize_rowwise_tiled(dev(w))
         for extra in (0, 128):
             ldh = m.mx_colwise_ld(M, G) + extra
             y0, qh0, sh0, qhT0, shT0 = m.mx_grouped_gemm_fwd_swiglu(qx, sx, qw, sw, offs_d, N, colwise=True, ldh=ldh)
             qhT, shT = _filled((ldh // 128, H, 128)), _filled((ldh // 128, H, 4))
-            y, qh, sh, qhT, shT, h = m.mx_grouped_gemm_fwd_swiglu_tiled(qx, sx, qw, sw, offs_d, N, with_h=True,
-                                                                        qhT=qhT, shT=shT)
-            assert torch.equal(y, y0) and torch.equal(qh, qh0) and torch.equal(sh, sh0)
+            sh = _filled((H // 128, M, 4))
+            y, qh, sh, qhT, shT, h = m.mx_grouped_gemm_fwd_swiglu_tiled(qx, sxt, qw, swt, offs_d, N, sh=sh,
+                                                                        with_h=True, qhT=qhT, shT=shT)
+            assert torch.equal(y, y0) and torch.equal(qh, qh0)
+            same_bytes((host(sh),), (oracle.mx_scales_tiled(host(sh0)),), "sh tiled vs row-major")
             qo, so = oracle.mx_quantize_colwise_values(host(h).astype(np.float64), offs, ldh)
             same_bytes((host(qhT), host(shT)), _tiles(qo, so), f"H tiled {sizes} ldh {ldh}")
             same_bytes((host(qhT), host(shT)), _tiles(host(qhT0), host(shT0)), "H tiled vs row-major")

@@ -342,17 +342,18 @@ def test_colwise_tiled_is_the_stated_permutation():
         mx_colwise_tiled(np.zeros((2, 96), dtype=np.uint8))
 
 
-def test_colwise_scales_tiled_is_the_stated_permutation():
-    """The tiled layout's scales (library contract): scale byte (c, b) of sT [C, ld / 32] at flat position
-    (b // 4) * C * 4 + c * 4 + b % 4, the four scale bytes of code tile b // 4 of row c.  Checked element
-    by element by that formula, as a bijection onto the buffer, against the code tiling (the scale of
-    code byte (c, j) sits in the same tile t = j // 128, at row c, slot (j % 128) // 32), and on a case
-    small enough to write out."""
-    from oracle import mx_colwise_tiled, mx_colwise_scales_tiled
+def test_scales_tiled_is_the_stated_permutation():
+    """The tiled layout's scales (library contract): scale byte (row, b) of s [rows, nb] at flat position
+    (b // 4) * rows * 4 + row * 4 + b % 4, the four scale bytes of 128-element slice b // 4 of the row.
+    Checked element by element by that formula, as a bijection onto the buffer, against the code tiling
+    of a column-wise copy (the scale of code byte (c, j) sits in the same tile t = j // 128, at row c,
+    slot (j % 128) // 32), for a row-wise copy from the oracle's quantiser (the scale of element (r, k)
+    at tile k // 128, row r, slot (k % 128) // 32), and on a case small enough to write out."""
+    from oracle import mx_colwise_tiled, mx_scales_tiled, mx_quantize_rowwise
     rng = np.random.default_rng(72)
     for C, ld in ((3, 128), (5, 384), (32, 256)):
         sT = rng.integers(0, 256, size=(C, ld // 32), dtype=np.uint8)
-        t = mx_colwise_scales_tiled(sT)
+        t = mx_scales_tiled(sT)
         assert t.shape == (ld // 128, C, 4) and t.dtype == np.uint8
         flat = t.reshape(-1)
         pos = np.empty((C, ld // 32), dtype=np.int64)
@@ -367,9 +368,18 @@ def test_colwise_scales_tiled_is_the_stated_permutation():
         for c in range(C):
             for j in range(0, ld, 32):
                 assert qt[j // 128, c, j % 128] == qT[c, j] and t[j // 128, c, (j % 128) // 32] == sT[c, j // 32]
+    # a row-wise copy: element (r, k)'s scale, the exponent of its block, at tile k // 128
+    x = (rng.standard_normal((5, 256)) * np.exp2(rng.integers(-6, 7, size=(5, 256)))).astype(np.float32)
+    bits = (x.view(np.uint32) >> 16).astype(np.uint16)
+    q, s = mx_quantize_rowwise(bits)
+    ts = mx_scales_tiled(s)
+    assert ts.shape == (2, 5, 4)
+    for r in range(5):
+        for k in range(0, 256, 32):
+            assert ts[k // 128, r, (k % 128) // 32] == s[r, k // 32]
     # 2 rows, 8 blocks: tile 0 = row 0 blocks 0..3 then row 1 blocks 0..3; tile 1 = blocks 4..7
     sT = np.arange(16, dtype=np.int64).reshape(2, 8)
     want = np.array([0, 1, 2, 3, 8, 9, 10, 11, 4, 5, 6, 7, 12, 13, 14, 15])
-    assert np.array_equal(mx_colwise_scales_tiled(sT).reshape(-1), want)
+    assert np.array_equal(mx_scales_tiled(sT).reshape(-1), want)
     with pytest.raises(ValueError):
-        mx_colwise_scales_tiled(np.zeros((2, 3), dtype=np.uint8))
+        mx_scales_tiled(np.zeros((2, 3), dtype=np.uint8))
