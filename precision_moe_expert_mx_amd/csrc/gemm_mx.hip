@@ -452,6 +452,13 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const Tile& t, char*
 
   // ---- accumulators ----------------------------------------------------------------------------
   const int wm = w / kWavesN, wn = w % kWavesN;
+  // A wave whose 128 A rows all lie past the tile's valid rows (the last row tile of an expert with at
+  // most 128 rows left; the last N tile of a weight gradient with N % 256 == 128) skips its LDS reads
+  // and MFMAs: it still moves its share of every stage's loads and meets every barrier, and the other
+  // wave of its column, on the same SIMD, has the matrix core to itself.  Its accumulators stay zero
+  // and its rows are not stored.
+  const int valid_rows = MODE == kWgrad ? (int)min((int64_t)BM, p.N - (int64_t)t.mt * BM) : t.rows;
+  const bool active = __builtin_amdgcn_readfirstlane((int)(WM * wm < valid_rows)) != 0;
   constexpr int FR = FP4 ? 16 : 32;                       // fragment rows / columns (E2M1: 16x16x128)
   constexpr int NI = WM / FR;                            // A fragments
   constexpr int NJ = WN / FR;                            // B fragments
@@ -526,6 +533,10 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const Tile& t, char*
     // before the current block's MFMAs and the stage barrier moved before the last block's MFMAs
     // (4-7% slower).
     const bool more = ks + 1 < nsteps;
+    if (!active) {
+      if (more) stage_out(ks + 1, true);
+      continue;
+    }
     constexpr bool kFastTop = FP4;
     if constexpr (FEED != kFeedPrecise) {
       if (more) stage_out(ks + 1, kFastTop);
