@@ -53,7 +53,7 @@ constexpr int kStage = kStageA + BN * BK;                    // 48 KiB
 constexpr int kScaleA = 0, kScaleB = 4 * BM, kScaleBlk = 4 * (BM + BN);   // byte offsets in a scale stage
 constexpr int kScaleStage = 4 * (BM + BN) + 16;
 constexpr int kLds = 2 * kStage + 2 * kScaleStage;
-static_assert(4 * (kMaxG + 1) * 4 <= kStage, "scheduler scratch must fit in the first stage");
+static_assert(5 * (kMaxG + 1) * 4 <= kStage, "scheduler scratch must fit in the first stage");
 
 typedef float v16f __attribute__((ext_vector_type(16)));
 

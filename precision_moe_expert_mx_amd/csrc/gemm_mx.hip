@@ -708,7 +708,8 @@ __global__ __launch_bounds__(NT, 1) void mx_grouped_gemm_kernel(GemmArgs p) {
   __shared__ __attribute__((aligned(16))) char lds[kLds];
   Tile t;
   // (the blockwise power-of-two wgrad lays experts out in 128-token blocks)
-  if (!decode_grouped_tile<MODE, MODE == kWgrad || ACT, BM, BN, NT, BWP2 ? 128 : 32>(p, lds, t)) return;
+  if (!decode_grouped_tile<MODE, MODE == kWgrad || ACT, BM, BN, NT, BWP2 ? 128 : 32, MODE != kWgrad>(p, lds, t))
+    return;
   // the tile's fields are the same in every lane: say so, so that everything derived from them (operand
   // bases, loop bounds) lives in scalar registers
   t.g = __builtin_amdgcn_readfirstlane(t.g);
@@ -723,7 +724,7 @@ __global__ __launch_bounds__(NT, 1) void mx_grouped_gemm_kernel(GemmArgs p) {
   run_tile<MODE, FEED, SDW, FP4, ACT, BWP2>(p, t, lds);
 }
 
-static_assert(4 * (kMaxG + 1) * 4 <= kStage, "scheduler scratch must fit in the first stage");
+static_assert(5 * (kMaxG + 1) * 4 <= kStage, "scheduler scratch must fit in the first stage");
 
 int64_t tile_count_bound(int mode, const GemmArgs& p) {
   if (mode == kWgrad) return (int64_t)p.G * ((p.N + BM - 1) / BM) * ((p.K + BN - 1) / BN);

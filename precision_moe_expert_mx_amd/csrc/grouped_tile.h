@@ -34,28 +34,40 @@ __device__ __forceinline__ int64_t uniform64(int64_t v) {
 // (before the first operand load overwrites them).  Returns false when the workgroup has no tile.
 // Tiles are TBM A rows x TBN B rows; TNT threads.  CB: also the first CBLK-block of each expert in the
 // column-wise layout (wgrad; the gated forward's column-wise H), whose blocks are CBLK rows.
-template <int MODE, bool CB, int TBM, int TBN, int TNT, int CBLK>
+// PARTIAL_LAST (forward, dgrad): the experts' full row tiles come first, in expert order, and their
+// partial last row tiles after them, the ones with the most rows first (for G <= kLptMaxG), so that
+// the launch's last round holds the tiles with the fewest rows (cheaper where idle waves skip their
+// MFMAs).
+template <int MODE, bool CB, int TBM, int TBN, int TNT, int CBLK, bool PARTIAL_LAST = false>
 __device__ bool decode_grouped_tile(const GemmArgs& p, char* lds, GroupTile& t) {
   int32_t* s_rs = (int32_t*)lds;             // clamped offsets [G+1]
   int32_t* s_pre = s_rs + (kMaxG + 1);       // tile prefix over the processing order [G+1]
   int32_t* s_cb = s_pre + (kMaxG + 1);       // wgrad: first 32-block of each expert [G+1]
-  int32_t* s_ord = s_cb + (kMaxG + 1);       // processing order [G]
+  int32_t* s_ord = s_cb + (kMaxG + 1);       // processing order [G] (PARTIAL_LAST: of the partial tiles)
+  int32_t* s_pre2 = s_ord + kMaxG;           // PARTIAL_LAST: prefix of the partial tiles [G+1]
+  constexpr bool kSplit = PARTIAL_LAST && MODE != kWgrad;
   const int G = p.G;
   const int tid = threadIdx.x;
   const int64_t M = p.M;
   for (int g = tid; g <= G; g += TNT) s_rs[g] = (int32_t)clamp_off(p.offs[g], M);
   __syncthreads();
-  const bool lpt = MODE == kWgrad && G <= kLptMaxG;
+  // wgrad: experts by size; split forward / dgrad: the partial tiles by their rows (m_g mod TBM, 0 for
+  // none); largest first, ties by index
+  const bool lpt = (MODE == kWgrad || kSplit) && G <= kLptMaxG;
+  auto key = [&](int g) {
+    const int m = max(s_rs[g + 1] - s_rs[g], 0);
+    return kSplit ? m % TBM : m;
+  };
   if (lpt) {
-    // the rank of expert g, largest first (ties by index): eight consecutive lanes count the experts
-    // h = part, part + 8, ... that go before g, and their counts are summed across the eight lanes
+    // the rank of expert g: eight consecutive lanes count the experts h = part, part + 8, ... that go
+    // before g, and their counts are summed across the eight lanes
     static_assert(TNT % 64 == 0, "whole waves");
     for (int idx = tid; idx < 8 * G; idx += TNT) {
       const int g = idx >> 3, part = idx & 7;
-      const int mg = max(s_rs[g + 1] - s_rs[g], 0);
+      const int mg = key(g);
       int pos = 0;
       for (int h = part; h < G; h += 8) {
-        const int mh = max(s_rs[h + 1] - s_rs[h], 0);
+        const int mh = key(h);
         pos += (mh > mg) || (mh == mg && h < g);
       }
       pos += __shfl_xor(pos, 1, 64);
@@ -70,19 +82,27 @@ __device__ bool decode_grouped_tile(const GemmArgs& p, char* lds, GroupTile& t) 
   const int ntc = cdiv(MODE == kFwd ? p.N : p.K, TBN);
   const int mtc_w = cdiv(p.N, TBM);
   const int lane = tid & 63;
-  if (tid < 64 || (CB && tid < 128)) {
-    const bool tiles = tid < 64;
+  // prefix sums, one wave each: the tiles (full row tiles when split) over the processing order (expert
+  // order when split), the blocks of each expert (CB), the partial tiles over s_ord (split)
+  const int wv = tid >> 6;
+  const bool cb_wave = CB && wv == 1;
+  const bool p2_wave = kSplit && wv == 2;
+  if (wv == 0 || cb_wave || p2_wave) {
     int carry = 0;
     for (int base = 0; base < G; base += 64) {
       const int q = base + lane;
       int c = 0;
       if (q < G) {
-        if (tiles) {
-          const int g = s_ord[q];
+        if (wv == 0) {
+          const int g = kSplit ? q : s_ord[q];
+          const int mg = max(s_rs[g + 1] - s_rs[g], 0);
           if (MODE == kWgrad) c = mtc_w * ntc;
-          else c = cdiv(max(s_rs[g + 1] - s_rs[g], 0), TBM) * ntc;
-        } else {
+          else c = (kSplit ? mg / TBM : cdiv(mg, TBM)) * ntc;
+        } else if (cb_wave) {
           c = cdiv(max(s_rs[q + 1] - s_rs[q], 0), CBLK);
+        } else {
+          const int g = s_ord[q];
+          c = (max(s_rs[g + 1] - s_rs[g], 0) % TBM ? 1 : 0) * ntc;
         }
       }
       int incl = c;
@@ -91,10 +111,11 @@ __device__ bool decode_grouped_tile(const GemmArgs& p, char* lds, GroupTile& t) 
         const int v = __shfl_up(incl, d, 64);
         if (lane >= d) incl += v;
       }
-      if (q < G) (tiles ? s_pre : s_cb)[q] = carry + incl - c;
+      int32_t* dst = wv == 0 ? s_pre : (cb_wave ? s_cb : s_pre2);
+      if (q < G) dst[q] = carry + incl - c;
       carry += __shfl(incl, 63, 64);
     }
-    if (lane == 0) (tiles ? s_pre : s_cb)[G] = carry;
+    if (lane == 0) (wv == 0 ? s_pre : (cb_wave ? s_cb : s_pre2))[G] = carry;
   }
   __syncthreads();
 
@@ -102,24 +123,43 @@ __device__ bool decode_grouped_tile(const GemmArgs& p, char* lds, GroupTile& t) 
   const int b = blockIdx.x;
   const int x = b % kXcd, q = b / kXcd;
   const int lt_all = ((q / kChunk) * kXcd + x) * kChunk + (q % kChunk);
-  if (lt_all >= s_pre[G]) return false;
-  int lo = 0, hi = G - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (s_pre[mid] <= lt_all) lo = mid; else hi = mid - 1;
+  const int n_full = s_pre[G];
+  if (lt_all >= n_full + (kSplit ? s_pre2[G] : 0)) return false;
+  int g, mt, nt, mtc;
+  if (kSplit && lt_all >= n_full) {
+    // a partial last row tile: expert by the partial-tile prefix, then its column tile
+    const int lt2 = lt_all - n_full;
+    int lo = 0, hi = G - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_pre2[mid] <= lt2) lo = mid; else hi = mid - 1;
+    }
+    g = s_ord[lo];
+    mtc = max(s_rs[g + 1] - s_rs[g], 0) / TBM;      // full row tiles before it
+    mt = mtc;
+    nt = lt2 - s_pre2[lo];
+  } else {
+    int lo = 0, hi = G - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_pre[mid] <= lt_all) lo = mid; else hi = mid - 1;
+    }
+    g = kSplit ? lo : s_ord[lo];
+    const int lt = lt_all - s_pre[lo];
+    const int m_g = max(s_rs[g + 1] - s_rs[g], 0);
+    mtc = MODE == kWgrad ? mtc_w : (kSplit ? m_g / TBM : cdiv(m_g, TBM));
+    const int span = kGroupM * ntc;
+    const int sg = lt / span;
+    const int fm = sg * kGroupM;
+    const int gsz = min(mtc - fm, kGroupM);
+    const int r = lt - sg * span;
+    mt = fm + r % gsz;
+    nt = r / gsz;
   }
-  const int g = s_ord[lo];
-  const int lt = lt_all - s_pre[lo];
   const int m_g = max(s_rs[g + 1] - s_rs[g], 0);
-  const int mtc = MODE == kWgrad ? mtc_w : cdiv(m_g, TBM);
-  const int span = kGroupM * ntc;
-  const int sg = lt / span;
-  const int fm = sg * kGroupM;
-  const int gsz = min(mtc - fm, kGroupM);
-  const int r = lt - sg * span;
   t.g = g;
-  t.mt = fm + r % gsz;
-  t.nt = r / gsz;
+  t.mt = mt;
+  t.nt = nt;
   t.row0 = s_rs[g] + (int64_t)t.mt * TBM;
   t.rows = (int)min((int64_t)TBM, (int64_t)s_rs[g + 1] - t.row0);
   t.col0 = CB ? CBLK * (int64_t)s_cb[g] : 0;
