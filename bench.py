@@ -770,7 +770,7 @@ def main():
         return
 
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); "
               "the expert-parallel split across GPUs is a design, not an implementation", file=sys.stderr)
         sys.exit(2)
 
