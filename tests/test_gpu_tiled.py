@@ -270,3 +270,40 @@ def test_swiglu_tiled_column_wise_h():
             qo, so = oracle.mx_quantize_colwise_values(host(h).astype(np.float64), offs, ldh)
             same_bytes((host(qhT), host(shT)), _tiles(qo, so), f"H tiled {sizes} ldh {ldh}")
             same_bytes((host(qhT), host(shT)), _tiles(host(qhT0), host(shT0)), "H tiled vs row-major")
+
+
+@pytest.mark.parametrize("fast", [False, True])
+def test_tiled_max_expert_count(fast):
+    """1024 experts, most of them empty: the tiled dual quantiser bit-exact against the oracle, and the
+    three GEMMs on tiled operands give the row-major launches' bits (empty experts' dW zero)."""
+    m = require_gpu()
+    rng = np.random.default_rng(87)
+    G, N, K = 1024, 256, 384
+    sizes = np.zeros(G, np.int64)
+    busy = rng.choice(G - 1, 50, replace=False)
+    sizes[busy] = rng.integers(1, 300, busy.size)
+    sizes[G - 1] = 33
+    offs, x, w, dy = _layer(rng, sizes, N, K)
+    M = int(offs[-1])
+    offs_d = dev(offs)
+    ld = m.mx_colwise_ld(M, G)
+    _dual_tiled_equal(m, x, offs, ld)
+    qx, sx, qxT, sxT = m.mx_quantize_dual(dev(x), offs_d, ld=ld)
+    qdy, sdy, qdyT, sdyT = m.mx_quantize_dual(dev(dy), offs_d, ld=ld)
+    _, sxt, qxTt, sxTt = m.mx_quantize_dual_tiled(dev(x), offs_d, ld=ld)
+    _, sdyt, qdyTt, sdyTt = m.mx_quantize_dual_tiled(dev(dy), offs_d, ld=ld)
+    qw, sw = m.mx_quantize_rowwise(dev(w))
+    _, swt = m.mx_quantize_rowwise_tiled(dev(w))
+    ldw = m.mx_colwise_ld(G * N)
+    qwT, swT = m.mx_quantize_colwise(dev(w), None, ld=ldw)
+    qwTt, swTt = m.mx_quantize_colwise_tiled(dev(w), None, ld=ldw)
+    y = m.mx_grouped_gemm_fwd(qx, sx, qw, sw, offs_d, N, "f32", fast=fast)
+    yt = m.mx_grouped_gemm_fwd_tiled(qx, sxt, qw, swt, offs_d, N, "f32", fast=fast)
+    assert torch.equal(y, yt), "fwd: tiled and row-major differ"
+    dx = m.mx_grouped_gemm_dgrad(qdy, sdy, qwT, swT, offs_d, K, "f32", fast=fast)
+    dxt = m.mx_grouped_gemm_dgrad_tiled(qdy, sdyt, qwTt, swTt, offs_d, K, "f32", fast=fast)
+    assert torch.equal(dx, dxt), "dgrad: tiled and row-major differ"
+    dw = m.mx_grouped_gemm_wgrad(qdyT, sdyT, qxT, sxT, offs_d, M, "f32", fast=fast)
+    dwt = m.mx_grouped_gemm_wgrad_tiled(qdyTt, sdyTt, qxTt, sxTt, offs_d, M, "f32", fast=fast)
+    assert torch.equal(dw, dwt), "wgrad: tiled and row-major differ"
+    assert not host(dwt)[sizes == 0].any(), "an empty expert's weight gradient is not zero"
