@@ -82,17 +82,19 @@ __device__ __forceinline__ int lds_off(int r, int c) { return r * BK + ((c ^ swz
 
 // Gated forward epilogue (precise feed, 32x32 fragments, 8 waves 2 x 4).  Waves wn = 0, 1 hold the
 // gate columns of the tile's 128 hidden units, waves 2, 3 the up columns of the same units.  Every
-// wave writes its pre-activations as bf16 to Y (gate at column u, up at H + u); the up waves hand
-// their fp32 values to the gate waves through LDS, which form H = silu(gate) * up in fp32 and
-// MX-quantise it row-wise: a row's 32-column block is one fragment, split between lanes l and l ^ 32.
-// With a column-wise output the gate waves put H back into LDS in place of the up values, and all
-// waves then quantise the tile's 256 rows x 128 hidden units in 32-row blocks down each column (the
+// wave writes its pre-activations as bf16 to Y (gate at column u, up at H + u).  Then each gate wave
+// and the up wave holding the same outputs swap half of their fp32 values through LDS, and each forms
+// H = silu(gate) * up in fp32 for its half of the rows and MX-quantises it row-wise: a row's 32-column
+// block is one fragment, split between lanes l and l ^ 32.  (Waves w and w + 4, the two row halves of
+// one column group, share a SIMD: with the gate waves alone doing this, two SIMDs would sit idle
+// through the exponentials.)  With a column-wise output every wave puts its H transposed into LDS, and
+// all waves then quantise the tile's 256 rows x 128 hidden units in 32-row blocks down each column (the
 // tile's rows start at a multiple of 256 inside its expert, so its blocks are the expert's blocks).
 template <typename Acc>
 __device__ __forceinline__ void act_epilogue(const GemmArgs& p, const Tile& t, char* lds, Acc (&acc)[WM / 32][WN / 32]) {
   constexpr int NI = WM / 32, NJ = WN / 32;
   constexpr int kUpPitch = BN / 2 + 4;            // floats per LDS row (padded against bank conflicts)
-  static_assert(BM * kUpPitch * 4 <= kLds, "up tile must fit in LDS");
+  static_assert(BM * kUpPitch * 4 <= kLds, "exchanged values must fit in LDS");
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int wm = w / kWavesN, wn = w % kWavesN;
   const int64_t H = p.N / 2;
@@ -102,7 +104,6 @@ __device__ __forceinline__ void act_epilogue(const GemmArgs& p, const Tile& t, c
   const int64_t hcol0 = (int64_t)t.nt * (BN / 2) + ucol0;          // global hidden column
   const int row_lim = t.rows;
   const int lrow = WM * wm + lane % 32;
-  float* up = (float*)lds;
 
   // pre-activations (bf16) as whole row pieces through LDS (store_tile_rows): gate waves at columns
   // [128 nt, +128) of Y, up waves at H + the same
@@ -111,74 +112,79 @@ __device__ __forceinline__ void act_epilogue(const GemmArgs& p, const Tile& t, c
   store_tile_rows<NI, NJ, 2>(acc, lds + w * 64 * (128 * NJ + 16), true, p.out, t.row0, p.N,
                              (up_wave ? H : 0) + (int64_t)t.nt * (BN / 2), WM * wm, WN * (wn % (kWavesN / 2)),
                              row_lim, BN);
-  // the up values to LDS once every wave is done with its staged rows
+  // Exchange through LDS, so that every SIMD forms H for half of its rows (a SIMD holds the two row
+  // halves of one column group: both gate waves or both up waves).  Gate waves keep fragment rows
+  // i < NI / 2 and hand over their gate values of i >= NI / 2; up waves keep i >= NI / 2 and hand over
+  // their up values of i < NI / 2.  Both go to xch[r][c] (tile row r, tile-local hidden column c):
+  // the two halves are disjoint.  The region is free once every wave is done with its staged rows.
+  constexpr int kHalf = NI / 2;
+  float* xch = (float*)lds;
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  if (up_wave) {
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int r = lrow + 32 * i;
+  for (int i = 0; i < NI; ++i) {
+    if ((i < kHalf) != up_wave) continue;          // a fragment row this wave keeps
+    const int r = lrow + 32 * i;
 #pragma unroll
-      for (int j = 0; j < NJ; ++j)
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int c = ucol0 + 32 * j + 8 * q;
-          *(float4*)(up + r * kUpPitch + c) =
-              make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
-        }
-    }
+      for (int q = 0; q < 4; ++q) {
+        const int c = ucol0 + 32 * j + 8 * q;
+        *(float4*)(xch + r * kUpPitch + c) =
+            make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+      }
   }
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  if (up_wave && !colwise) return;
 
-  if (!up_wave) {
+  // H = silu(gate) * up for the kept rows, MX-quantised row-wise; H replaces the kept accumulators
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int r = lrow + 32 * i;
-      const int64_t grow = t.row0 + r;
+  for (int i = 0; i < NI; ++i) {
+    if ((i < kHalf) == up_wave) continue;          // a fragment row handed over
+    const int r = lrow + 32 * i;
+    const int64_t grow = t.row0 + r;
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        float h[16];
-        uint32_t amax = 0;
+    for (int j = 0; j < NJ; ++j) {
+      float h[16];
+      uint32_t amax = 0;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float4 u = *(const float4*)(up + r * kUpPitch + ucol0 + 32 * j + 8 * q);
-          const float uu[4] = {u.x, u.y, u.z, u.w};
+      for (int q = 0; q < 4; ++q) {
+        const float4 o = *(const float4*)(xch + r * kUpPitch + ucol0 + 32 * j + 8 * q);
+        const float oo[4] = {o.x, o.y, o.z, o.w};
 #pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            const float g = acc[i][j][4 * q + k];
-            // silu with the hardware exponential and reciprocal (a few ulp; g -> -inf gives -0)
-            h[4 * q + k] = g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * uu[k];
-            amax = max(amax, __float_as_uint(h[4 * q + k]) & 0x7FFFFFFFu);
-            acc[i][j][4 * q + k] = h[4 * q + k];     // H replaces the gate value (Y is written)
-          }
+        for (int k = 0; k < 4; ++k) {
+          const float mine = acc[i][j][4 * q + k];
+          const float g = up_wave ? oo[k] : mine, u = up_wave ? mine : oo[k];
+          // silu with the hardware exponential and reciprocal (a few ulp; g -> -inf gives -0)
+          h[4 * q + k] = g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
+          amax = max(amax, __float_as_uint(h[4 * q + k]) & 0x7FFFFFFFu);
+          acc[i][j][4 * q + k] = h[4 * q + k];
         }
-        amax = max(amax, (uint32_t)__shfl_xor((int)amax, 32, 64));
-        // shared exponent of the block: floor(log2 amax) - 8 from the fp32 exponent field, clamped
-        const int e = max((int)(amax >> 23) - 135, -127);
-        const float sc = __uint_as_float((uint32_t)(e + 127) << 23);
-        const float lim = __uint_as_float(((uint32_t)(e + 135) << 23) | 0x600000u);   // 448 * 2^e
-        if (r >= row_lim) continue;
-        const int64_t hc = hcol0 + 32 * j;
+      }
+      amax = max(amax, (uint32_t)__shfl_xor((int)amax, 32, 64));
+      // shared exponent of the block: floor(log2 amax) - 8 from the fp32 exponent field, clamped
+      const int e = max((int)(amax >> 23) - 135, -127);
+      const float sc = __uint_as_float((uint32_t)(e + 127) << 23);
+      const float lim = __uint_as_float(((uint32_t)(e + 135) << 23) | 0x600000u);   // 448 * 2^e
+      if (r >= row_lim) continue;
+      const int64_t hc = hcol0 + 32 * j;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const uint32_t code = cvt4_f32_e4m3_scaled(h[4 * q], h[4 * q + 1], h[4 * q + 2], h[4 * q + 3], lim, sc);
-          *(uint32_t*)(p.act_q + grow * H + hc + 8 * q) = code;
-          if (p.act_dbg)
-            *(float4*)(p.act_dbg + grow * H + hc + 8 * q) = make_float4(h[4 * q], h[4 * q + 1], h[4 * q + 2], h[4 * q + 3]);
-        }
-        if (lane < 32) {
-          // row-wise scales [M, H / 32], or tiled [H / 128][M][4]
-          const int64_t blk = (hc - 4 * (lane / 32)) / 32;
-          const int64_t off = p.act_tiled ? (blk >> 2) * (p.M * 4) + grow * 4 + (blk & 3) : grow * (H / 32) + blk;
-          p.act_s[off] = (uint8_t)(e + 127);
-        }
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t code = cvt4_f32_e4m3_scaled(h[4 * q], h[4 * q + 1], h[4 * q + 2], h[4 * q + 3], lim, sc);
+        *(uint32_t*)(p.act_q + grow * H + hc + 8 * q) = code;
+        if (p.act_dbg)
+          *(float4*)(p.act_dbg + grow * H + hc + 8 * q) = make_float4(h[4 * q], h[4 * q + 1], h[4 * q + 2], h[4 * q + 3]);
+      }
+      if (lane < 32) {
+        // row-wise scales [M, H / 32], or tiled [H / 128][M][4]
+        const int64_t blk = (hc - 4 * (lane / 32)) / 32;
+        const int64_t off = p.act_tiled ? (blk >> 2) * (p.M * 4) + grow * 4 + (blk & 3) : grow * (H / 32) + blk;
+        p.act_s[off] = (uint8_t)(e + 127);
       }
     }
   }
   if (!colwise) return;
 
   // Column-wise H.  H goes to LDS transposed, column c of the tile at hT + c * kTPitch with its 256
-  // rows contiguous (every up value has been read: one more barrier first).  Then 16 lanes take one
+  // rows contiguous (every exchanged value has been read: one more barrier first).  Then 16 lanes take one
   // hidden column: at step m lane k reads the column's 16-byte chunk 16 m + k (rows 4 (16 m + k) .. + 3),
   // so 32-row block b = 2 m + k / 8 is held by 8 lanes, whose amax meets by DPP, and the 16 lanes store
   // 64 consecutive code bytes of the column's qT row.  Blocks at or past the expert's end within this
@@ -188,15 +194,15 @@ __device__ __forceinline__ void act_epilogue(const GemmArgs& p, const Tile& t, c
   static_assert((BN / 2) * kTPitch * 4 <= kLds, "transposed H must fit in LDS");
   float* hT = (float*)lds;
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  if (!up_wave) {
 #pragma unroll
-    for (int i = 0; i < NI; ++i)
+  for (int i = 0; i < NI; ++i) {
+    if ((i < kHalf) == up_wave) continue;          // H of the rows this wave kept
 #pragma unroll
-      for (int j = 0; j < NJ; ++j)
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
+      for (int q = 0; q < 4; ++q)
 #pragma unroll
-          for (int k = 0; k < 4; ++k) hT[(ucol0 + 32 * j + 8 * q + k) * kTPitch + lrow + 32 * i] = acc[i][j][4 * q + k];
+        for (int k = 0; k < 4; ++k) hT[(ucol0 + 32 * j + 8 * q + k) * kTPitch + lrow + 32 * i] = acc[i][j][4 * q + k];
   }
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   const int64_t ldq = p.act_ld;

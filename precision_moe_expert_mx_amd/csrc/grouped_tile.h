@@ -221,6 +221,10 @@ __device__ __forceinline__ void store_tile_rows_as(const Acc (&acc)[NI][NJ], cha
       const int k = lane + 64 * it;
       v[it] = *(const uint4*)(reg + (k / kCpr) * kPitch + 16 * (k % kCpr));
     }
+    // Left alone, the compiler sinks each read into the row test of its store, which then waits out the
+    // LDS latency once per piece.  An empty asm that takes every piece keeps the reads ahead of the stores.
+#pragma unroll
+    for (int it = 0; it < kPieces; ++it) asm volatile("" : "+v"(v[it].x), "+v"(v[it].y), "+v"(v[it].z), "+v"(v[it].w));
 #pragma unroll
     for (int it = 0; it < kPieces; ++it) {
       const int k = lane + 64 * it;
