@@ -278,7 +278,7 @@ void bw_launch_mode(const GemmArgs& p, dim3 grid, hipStream_t st) {
 hipError_t launch_bw_gemm(int mode, const GemmArgs& p, hipStream_t st) {
   const int64_t tiles = bw_tile_count_bound(mode, p);
   if (tiles == 0) return hipSuccess;
-  const int64_t per = (int64_t)kXcd * kChunk;
+  const int64_t per = (int64_t)kXcd * chunk_tiles(mode);   // whole XCD chunks: every tile has a workgroup
   const int64_t grid = (tiles + per - 1) / per * per;
   if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
   const dim3 g((unsigned)grid);

@@ -765,7 +765,7 @@ hipError_t launch_mx_gemm(int mode, const GemmArgs& args, hipStream_t st) {
   if (tiled_scales && (p.fp4 || p.bw_pow2 || p.ldsa % 4 || p.ldsb % 4)) return hipErrorInvalidValue;
   const int64_t tiles = tile_count_bound(mode, p);
   if (tiles == 0) return hipSuccess;
-  const int64_t per = (int64_t)kXcd * kChunk;
+  const int64_t per = (int64_t)kXcd * chunk_tiles(mode);   // whole XCD chunks: every tile has a workgroup
   const int64_t grid = (tiles + per - 1) / per * per;
   if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
   // the scale bytes of a row and stage are aligned dwords when every scale row and column offset is

@@ -9,8 +9,12 @@ namespace mxmoe {
 
 constexpr int kMaxG = 1024;                      // largest expert count of a launch
 constexpr int kXcd = 8;                          // workgroups go round-robin over the 8 XCDs
-constexpr int kChunk = 8;                        // consecutive tiles one XCD takes per visit
 constexpr int kGroupM = 4;                       // A tiles per raster column inside an expert
+// Consecutive tiles one XCD takes per visit.  Forward and dgrad: 16, so that (with the raster above)
+// the 32 tiles an XCD runs at once span about 8 A and 4 B tiles, 12 operand panels, where chunks of 8
+// gave 16 A and 2 B tiles (18 panels, every A panel fetched by all eight XCDs).  Weight gradient: 8
+// (its largest-expert-first list ran 4% slower with 16).
+constexpr int chunk_tiles(int mode) { return mode == kWgrad ? 8 : 16; }
 constexpr int kLptMaxG = 256;                    // wgrad orders experts by size up to this G
 
 struct GroupTile {
@@ -120,6 +124,7 @@ __device__ bool decode_grouped_tile(const GemmArgs& p, char* lds, GroupTile& t) 
   __syncthreads();
 
   // workgroup -> logical tile: chunks of kChunk consecutive tiles per XCD visit
+  constexpr int kChunk = chunk_tiles(MODE);
   const int b = blockIdx.x;
   const int x = b % kXcd, q = b / kXcd;
   const int lt_all = ((q / kChunk) * kXcd + x) * kChunk + (q % kChunk);
